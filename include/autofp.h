@@ -1,0 +1,213 @@
+/*
+ * autofp.h - C ABI of the AutoFP block-scaled low-bit linear layer on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Source of the method: "AutoEMatic: Runtime-Adaptive Mixed-Precision LLM
+ * Inference via Automatic Exponent-Mantissa Refinement" (arXiv 2611.10165v1),
+ * cited below as [AE] with the section, equation, table or figure.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Memory. Every data pointer is DEVICE memory owned by the caller unless the
+ *    argument says "host". The library never allocates, frees or synchronizes;
+ *    scratch space comes from the caller through (workspace, workspace_bytes),
+ *    sized by autofp_workspace_bytes(). Device pointers need 16-byte alignment.
+ *  - Streams. `stream` is a hipStream_t passed as void* (NULL = the null
+ *    stream). Calls are asynchronous on it; the returned status reports
+ *    argument checks and the launch result only, never kernel completion.
+ *  - Errors. Arguments are checked before anything is launched; on any error
+ *    nothing is launched and no output is written.
+ *  - Shapes. A tensor is [rows x k] row-major with k the reduction dimension;
+ *    k must be a positive multiple of 16 (one NVFP4 group, [AE] App. B.1).
+ *  - Non-finite inputs (inf / NaN) give unspecified results.
+ *  - Thread safety: no global mutable state; concurrent calls on different
+ *    buffers are safe.
+ */
+#ifndef AUTOFP_H
+#define AUTOFP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AUTOFP_OK = 0,
+  AUTOFP_ERR_NULL = 1,               /* a required pointer is NULL                  */
+  AUTOFP_ERR_SHAPE = 2,              /* k % 16 != 0, rows < 1, mismatched shapes    */
+  AUTOFP_ERR_BITS = 3,               /* precision level not in {2, 4, 6}            */
+  AUTOFP_ERR_KIND = 4,               /* weight/activation operand in the wrong slot */
+  AUTOFP_ERR_WORKSPACE = 5,          /* workspace NULL or smaller than required     */
+  AUTOFP_ERR_MISSING_REFINEMENT = 6, /* level 6 without mask/offsets                */
+  AUTOFP_ERR_DTYPE = 7,              /* unsupported dtype code                      */
+  AUTOFP_ERR_ARG = 8,                /* a parameter out of its documented range     */
+  AUTOFP_ERR_HIP = 9                 /* the HIP runtime reported a launch error     */
+} autofp_status;
+
+typedef enum { AUTOFP_F32 = 0, AUTOFP_BF16 = 1 } autofp_dtype;
+typedef enum { AUTOFP_WEIGHT = 0, AUTOFP_ACTIVATION = 1 } autofp_kind;
+
+/* Hyperparameters; autofp_default_params() fills the values of [AE] §5.1
+ * ("Hyperparameters"). */
+typedef struct {
+  double  rho;             /* 0.2   weight refinement budget: floor(rho*k/4) refined subgroups */
+  float   act_nmse_thresh; /* 0.003 activation subgroup NMSE threshold ([AE] §6.4)          */
+  float   c2;              /* 2.0   AutoFP2 scale multiple c ([AE] App. B.4, Eq. 4)          */
+  int32_t top_k;           /* 10    G_E top-K; top_k >= vocab means the whole vocabulary     */
+  float   eps;             /* 1e-6  L_A stability term ([AE] Eq. 1; value not in the paper)  */
+} autofp_params;
+
+/*
+ * One AutoFP tensor ([AE] §4: "E2M1 base values with E4M3 group scales, signed
+ * offsets d stored as one byte per refined subgroup, and refinement masks
+ * stored as 4 bits per group along the K-dimension"; layout of Fig. 23).
+ *
+ *  codes        [rows][k/2]   E2M1 codes s|e1|e0|m, element 2i in the low nibble.
+ *  scales       [rows][k/16]  E4M3 (OCP E4M3FN) group scales B.
+ *  tensor_scale [1]           FP32 tensor scale T ([AE] Eq. 2).
+ *  mask         WEIGHT:     [ceil(k/32)]        one 4-bit mask per group shared by
+ *                                               all rows (M_W, [AE] §3.2);
+ *               ACTIVATION: [rows][ceil(k/32)]  per-row mask M_A.
+ *               Group 2g is the low nibble; bit s of a nibble = subgroup s.
+ *               NULL when the tensor carries no 6-bit refinement.
+ *  offsets      WEIGHT:     [rows][n_refined]   one byte per refined subgroup, in
+ *                                               ascending (group, subgroup) order;
+ *               ACTIVATION: [rows][k/4]         one byte per subgroup (0 where the
+ *                                               subgroup is not refined).
+ *               Byte = four 2-bit two's-complement d, element e of the subgroup
+ *               in bits [2e+1:2e]; value delta = d/8 ([AE] §3.2, fixed step).
+ *  n_refined    WEIGHT only: number of refined subgroups per row (= popcount of
+ *               mask); 0 otherwise.
+ */
+typedef struct {
+  int64_t  rows;
+  int64_t  k;
+  int32_t  kind;        /* autofp_kind */
+  int32_t  n_refined;
+  uint8_t *codes;
+  uint8_t *scales;
+  float   *tensor_scale;
+  uint8_t *mask;
+  uint8_t *offsets;
+} autofp_packed;
+
+/* Operations whose scratch space autofp_workspace_bytes() sizes. */
+typedef enum {
+  AUTOFP_OP_QUANTIZE = 0,     /* rows, k of the input                           */
+  AUTOFP_OP_SELECT_MASK = 1,  /* rows, k of the weight                          */
+  AUTOFP_OP_GEMV = 2,         /* rows = batch (tokens), k                       */
+  AUTOFP_OP_GEMM = 3          /* rows = tokens, k                               */
+} autofp_op;
+
+/* Fills *p with the paper's hyperparameters. Errors: NULL. */
+autofp_status autofp_default_params(autofp_params *p);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *autofp_status_string(autofp_status s);
+
+/* Bytes of each buffer of one packed tensor, written to out_bytes (host):
+ * [0] codes, [1] scales, [2] tensor_scale, [3] mask, [4] offsets.
+ * refine = 0 gives 0 for mask and offsets. For WEIGHT, n_refined is the value
+ * autofp_weight_refined_count() returns. Errors: NULL, SHAPE, KIND, ARG. */
+autofp_status autofp_packed_bytes(int64_t rows, int64_t k, int32_t kind, int32_t refine,
+                                  int32_t n_refined, size_t out_bytes[5]);
+
+/* Number of refined subgroups per weight row: floor(rho * k / 4), at most two
+ * per group ([AE] App. E, Alg. 1: budget rho*K/4, l_j in {0, 1, 2}).
+ * Host only, no GPU work. Errors: NULL, SHAPE, ARG (rho outside [0, 1]). */
+autofp_status autofp_weight_refined_count(int64_t k, const autofp_params *p, int32_t *n_refined);
+
+/* Scratch bytes that operation `op` needs for a [rows x k] operand (host).
+ * Errors: NULL, SHAPE, ARG. */
+autofp_status autofp_workspace_bytes(int32_t op, int64_t rows, int64_t k, size_t *bytes);
+
+/*
+ * Weight mask M_W for a weight w [rows x k] (fp32, device), [AE] §3.2 and
+ * App. E, Alg. 1 (budget allocation) with the identity Hessian:
+ *  1. NVFP4-encode w (as autofp_quantize does) and, per row n, group j and
+ *     subgroup s, the fp64 reduction in squared error from refining it:
+ *       g = sum over the 4 elements of (eb*eb - er*er),
+ *       eb = w - T*B*q, er = w - T*B*(q + d/8);
+ *  2. sum g over rows n = 0..rows-1 in that order (fp64);
+ *  3. refine the top n_refined (group, subgroup) candidates, at most two per
+ *     group, ordered by gain (descending), then group, then subgroup.
+ * Writes mask_out [ceil(k/32)] (device). n_refined comes from
+ * autofp_weight_refined_count(). Errors: NULL, SHAPE, ARG, WORKSPACE, HIP.
+ */
+autofp_status autofp_select_weight_mask(const float *w, int64_t rows, int64_t k,
+                                        const autofp_params *p, uint8_t *mask_out,
+                                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Encode x [out->rows x out->k] (x_dtype F32 or BF16; bf16 is widened exactly)
+ * into AutoFP, [AE] App. B.1 Eqs. 2-3 (NVFP4 base), §3.2 (AutoFP6 offsets):
+ *   T = amax(x) / 2688;  B_j = E4M3(amax(x_j) / (6T));  q_i = E2M1(x_i / (T B_j))
+ * in fp32 with round-to-nearest-even (ties to even), E2M1 saturating at 6,
+ * E4M3 at 448, canonical +0; T is one scalar over the whole call.
+ *  - WEIGHT with out->mask != NULL: out->mask must already hold M_W (from
+ *    autofp_select_weight_mask) and out->n_refined its popcount; writes the
+ *    compacted offsets d = argmin over {-2,-1,0,+1} of |x/(TB) - q - d/8|
+ *    (ties to the smaller |d|).
+ *  - ACTIVATION with refine != 0: writes M_A - subgroups whose NMSE
+ *    ((e0^2+e1^2)+e2^2)+e3^2 > thresh * ((v0^2+v1^2)+v2^2)+v3^2 (fp32, v = x/(TB),
+ *    e = v - q; [AE] §6.4) that are not in exclude_mask (the layer's M_W,
+ *    [ceil(k/32)], may be NULL) - and the dense offsets.
+ * Errors: NULL, SHAPE, KIND, DTYPE, WORKSPACE, MISSING_REFINEMENT, HIP.
+ */
+autofp_status autofp_quantize(const void *x, int32_t x_dtype, int32_t refine,
+                              const uint8_t *exclude_mask, const autofp_params *p,
+                              autofp_packed *out, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/*
+ * Decode-phase linear layer ([AE] §3.1-3.2, §4): for b < x->rows, n < w->rows
+ *   y[b][n] = sum_k What[n][k] * Xhat[b][k]
+ * with the operands at precision level `bits`:
+ *   2: W as AutoFP2 digits c*T*B*Q, X as NVFP4 (W2A4);
+ *   4: both NVFP4 T*B*q;
+ *   6: W refined on M_W, X refined on M_A: T*B*(q + d/8) (W6A6).
+ * Products are exact and accumulated in fp32. y is [x->rows x w->rows]
+ * row-major, y_dtype F32 or BF16 (round to nearest even).
+ * If bits_dev != NULL the level is read on the device when the kernels run
+ * (graph-capturable, no host read); `bits` is then ignored but a level-6 call
+ * must be allowed by the operands (both carry refinement).
+ * Best for x->rows <= 64; larger batches run in slices of 64 tokens.
+ * Errors: NULL, SHAPE, KIND, BITS, MISSING_REFINEMENT, DTYPE, WORKSPACE, HIP.
+ */
+autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_t bits,
+                          const int32_t *bits_dev, void *y, int32_t y_dtype,
+                          const autofp_params *p, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
+ * Prefill-phase linear layer: the same result as autofp_gemv for any number of
+ * tokens, tiled for the matrix cores. Same arguments and errors.
+ */
+autofp_status autofp_gemm(const autofp_packed *w, const autofp_packed *x, int32_t bits,
+                          const int32_t *bits_dev, void *y, int32_t y_dtype,
+                          const autofp_params *p, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
+ * The two runtime-policy signals ([AE] §3.1):
+ *  - entropy_out[b] = G_E of logits row b: softmax over the top_k largest
+ *    logits, H = -sum p ln p, divided by ln(top_k) (ln(vocab) when
+ *    top_k >= vocab). logits [batch x vocab] fp32. top_k must be 1..32 or
+ *    >= vocab.
+ *  - update_out[b] = L_A = ||h_cur[b] - h_prev[b]||_2 / (||h_prev[b]||_2 + eps)
+ *    ([AE] Eq. 1); h_prev, h_cur [batch x hidden] in h_dtype (F32 or BF16).
+ * Either signal is skipped when its output pointer is NULL (its inputs may
+ * then be NULL too). Errors: NULL, SHAPE, DTYPE, ARG, HIP.
+ */
+autofp_status autofp_policy_signals(const float *logits, int64_t batch, int64_t vocab,
+                                    const void *h_prev, const void *h_cur, int32_t h_dtype,
+                                    int64_t hidden, const autofp_params *p,
+                                    float *entropy_out, float *update_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AUTOFP_H */

@@ -179,7 +179,7 @@ class NVFP4:
     s: np.ndarray        # [rows, K/16] fp32 T * B as rounded for the division
 
 
-def nvfp4_quantize(x):
+def nvfp4_quantize(x, tensor_amax=None):
     """NVFP4 quantization, [AE] App. B.1, Eqs. 2-3, evaluated in fp32.
 
         T   = amax(X) / (6*448)
@@ -190,13 +190,19 @@ def nvfp4_quantize(x):
     first, each rounded to fp32: ``sixT = 6*T``; ``b = a_j / sixT``;
     ``s = T * B``; ``v = x / s``. When 6T or s is zero the group encodes to
     zeros (B = 0, all codes +0).
+
+    ``tensor_amax`` replaces amax(X) when ``x`` holds only some rows of a
+    larger tensor (the per-tensor scale is a property of the whole tensor).
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
     if x.ndim != 2 or x.shape[1] % GROUP:
         raise ValueError("x must be [rows, K] with K a multiple of 16")
     rows, K = x.shape
     G = K // GROUP
-    amax = np.max(np.abs(x)) if x.size else np.float32(0)
+    if tensor_amax is None:
+        amax = np.max(np.abs(x)) if x.size else np.float32(0)
+    else:
+        amax = np.float32(tensor_amax)
     T = np.float32(amax) / np.float32(6 * 448)
     six_t = np.float32(6.0) * T
     a = np.max(np.abs(x.reshape(rows, G, GROUP)), axis=2) if x.size else np.zeros((rows, G), np.float32)
@@ -383,14 +389,14 @@ def _mask_bits_of(packed_mask, G):
 # Public quantizers producing the packed format
 # ----------------------------------------------------------------------------
 
-def quantize_activation(x, refine=False, exclude_mask=None, thresh=0.003):
+def quantize_activation(x, refine=False, exclude_mask=None, thresh=0.003, tensor_amax=None):
     """Encode activations X [B, K] (fp32, or bf16 widened exactly by the caller)
     to AutoFP: NVFP4 base with one per-tensor scale over the whole call
     ([AE] App. B.1; reading: one T over all rows of the call), plus, when
     ``refine``, the activation mask (excluding the packed weight mask
     ``exclude_mask`` [K/32]) and dense offsets [B, K/4] (one byte per subgroup,
     0x00 where not refined)."""
-    base = nvfp4_quantize(x)
+    base = nvfp4_quantize(x, tensor_amax)
     rows, K = base.codes.shape
     out = dict(codes=pack_nibbles(base.codes), scales=base.scales.copy(), T=base.T,
                q=base.codes, rows=rows, k=K)
@@ -404,12 +410,12 @@ def quantize_activation(x, refine=False, exclude_mask=None, thresh=0.003):
     return out
 
 
-def quantize_weight(w, mask=None):
+def quantize_weight(w, mask=None, tensor_amax=None):
     """Encode a weight W [N, K] (fp32): NVFP4 base; with a packed weight mask
     [K/32] also the compacted offsets [N, R]: for every row, one byte per
     refined subgroup in ascending (group, subgroup) order ([AE] §4: "signed
     offsets d stored as one byte per refined subgroup"; Fig. 23)."""
-    base = nvfp4_quantize(w)
+    base = nvfp4_quantize(w, tensor_amax)
     N, K = base.codes.shape
     out = dict(codes=pack_nibbles(base.codes), scales=base.scales.copy(), T=base.T,
                q=base.codes, rows=N, k=K)

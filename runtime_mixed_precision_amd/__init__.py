@@ -1,0 +1,238 @@
+"""AutoFP block-scaled low-bit linear layer on MI355X (gfx950).
+
+Thin PyTorch-facing binding over the C ABI of ``include/autofp.h``
+(``libautofp.so``): it allocates device buffers with torch, marshals pointers
+and sizes, and calls the library on torch's current stream. Every step of the
+computation runs in the library's HIP kernels; if the library is missing the
+calls raise ``NativeLibraryError``.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _native as N
+from ._native import AutofpError, NativeLibraryError, Params  # noqa: F401
+
+__all__ = [
+    "AutoFPTensor", "default_params", "packed_bytes", "weight_refined_count", "workspace_bytes",
+    "select_weight_mask", "quantize", "quantize_weight", "quantize_activation",
+    "gemv", "gemm", "policy_signals", "AutofpError", "NativeLibraryError",
+]
+
+_DT = {torch.float32: N.F32, torch.bfloat16: N.BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dev_check(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous CUDA (HIP) tensors")
+
+
+def default_params(**overrides) -> Params:
+    p = Params()
+    N.check(N.lib().autofp_default_params(C.byref(p)), "autofp_default_params")
+    for k, v in overrides.items():
+        setattr(p, k, v)
+    return p
+
+
+def packed_bytes(rows, k, kind, refine=False, n_refined=0):
+    out = (C.c_size_t * 5)()
+    N.check(N.lib().autofp_packed_bytes(rows, k, kind, int(bool(refine)), n_refined, out),
+            "autofp_packed_bytes")
+    return list(out)
+
+
+def weight_refined_count(k, params=None) -> int:
+    p = params or default_params()
+    n = C.c_int32()
+    N.check(N.lib().autofp_weight_refined_count(k, C.byref(p), C.byref(n)),
+            "autofp_weight_refined_count")
+    return int(n.value)
+
+
+def workspace_bytes(op, rows, k) -> int:
+    b = C.c_size_t()
+    N.check(N.lib().autofp_workspace_bytes(op, rows, k, C.byref(b)), "autofp_workspace_bytes")
+    return int(b.value)
+
+
+def _workspace(op, rows, k, device):
+    return torch.empty(max(workspace_bytes(op, rows, k), 16), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class AutoFPTensor:
+    """Device buffers of one packed AutoFP tensor (layout of include/autofp.h)."""
+    rows: int
+    k: int
+    kind: int
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tensor_scale: torch.Tensor
+    mask: Optional[torch.Tensor] = None
+    offsets: Optional[torch.Tensor] = None
+    n_refined: int = 0
+
+    def struct(self) -> N.Packed:
+        return N.Packed(self.rows, self.k, self.kind, self.n_refined, _ptr(self.codes),
+                        _ptr(self.scales), _ptr(self.tensor_scale), _ptr(self.mask),
+                        _ptr(self.offsets))
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in
+                   (self.codes, self.scales, self.tensor_scale, self.mask, self.offsets)
+                   if t is not None)
+
+    def to_host(self) -> dict:
+        """Host copy in the packed-format dictionary layout used by the tests."""
+        d = dict(codes=self.codes.cpu().numpy(), scales=self.scales.cpu().numpy(),
+                 T=self.tensor_scale.cpu().numpy()[0], rows=self.rows, k=self.k)
+        if self.mask is not None:
+            d["mask"] = self.mask.cpu().numpy()
+        if self.offsets is not None:
+            d["offsets"] = self.offsets.cpu().numpy()
+        if self.kind == N.WEIGHT:
+            d["n_refined"] = self.n_refined
+        return d
+
+
+def _alloc_packed(rows, k, kind, refine, n_refined, device):
+    nb = packed_bytes(rows, k, kind, refine, n_refined)
+
+    def buf(n, shape):
+        return torch.zeros(shape, dtype=torch.uint8, device=device) if n else None
+
+    mb = (k + 31) // 32
+    codes = torch.empty(rows, k // 2, dtype=torch.uint8, device=device)
+    scales = torch.empty(rows, k // 16, dtype=torch.uint8, device=device)
+    ts = torch.empty(1, dtype=torch.float32, device=device)
+    if kind == N.WEIGHT:
+        mask = buf(nb[3], (mb,))
+        offs = buf(nb[4], (rows, n_refined))
+        if refine and n_refined == 0:
+            offs = torch.zeros(rows, 1, dtype=torch.uint8, device=device)
+    else:
+        mask = buf(nb[3], (rows, mb))
+        offs = buf(nb[4], (rows, k // 4))
+    return AutoFPTensor(rows, k, kind, codes, scales, ts, mask, offs, n_refined if kind == N.WEIGHT else 0)
+
+
+def select_weight_mask(w: torch.Tensor, params=None, stream=None):
+    """Weight mask M_W (device uint8 [ceil(k/32)]) and its refined-subgroup count."""
+    _dev_check(w)
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise ValueError("weight must be a 2-D float32 tensor")
+    p = params or default_params()
+    rows, k = w.shape
+    mask = torch.zeros((k + 31) // 32, dtype=torch.uint8, device=w.device)
+    ws = _workspace(N.OP_SELECT_MASK, rows, k, w.device)
+    N.check(N.lib().autofp_select_weight_mask(_ptr(w), rows, k, C.byref(p), _ptr(mask), _ptr(ws),
+                                              ws.numel(), _stream(stream)), "autofp_select_weight_mask")
+    return mask, weight_refined_count(k, p)
+
+
+def quantize(x: torch.Tensor, kind: int, refine=False, exclude_mask=None, weight_mask=None,
+             n_refined=0, params=None, stream=None) -> AutoFPTensor:
+    """Encode a [rows x k] fp32/bf16 tensor to AutoFP (autofp_quantize)."""
+    _dev_check(x, exclude_mask, weight_mask)
+    if x.dim() != 2 or x.dtype not in _DT:
+        raise ValueError("x must be a 2-D float32 or bfloat16 tensor")
+    rows, k = x.shape
+    p = params or default_params()
+    if kind == N.WEIGHT:
+        out = _alloc_packed(rows, k, kind, weight_mask is not None, n_refined, x.device)
+        if weight_mask is not None:
+            out.mask = weight_mask
+    else:
+        out = _alloc_packed(rows, k, kind, refine, 0, x.device)
+    ws = _workspace(N.OP_QUANTIZE, rows, k, x.device)
+    st = out.struct()
+    N.check(N.lib().autofp_quantize(_ptr(x), _DT[x.dtype], int(bool(refine)), _ptr(exclude_mask),
+                                    C.byref(p), C.byref(st), _ptr(ws), ws.numel(), _stream(stream)),
+            "autofp_quantize")
+    return out
+
+
+def quantize_weight(w: torch.Tensor, refine=True, params=None, stream=None) -> AutoFPTensor:
+    """Offline weight packing: M_W selection (when ``refine``) and encode."""
+    if refine:
+        mask, nref = select_weight_mask(w, params, stream)
+        return quantize(w, N.WEIGHT, refine=True, weight_mask=mask, n_refined=nref, params=params,
+                        stream=stream)
+    return quantize(w, N.WEIGHT, params=params, stream=stream)
+
+
+def quantize_activation(x: torch.Tensor, refine=False, exclude_mask=None, params=None,
+                        stream=None) -> AutoFPTensor:
+    return quantize(x, N.ACTIVATION, refine=refine, exclude_mask=exclude_mask, params=params,
+                    stream=stream)
+
+
+def _linear(fn, name, w, x, bits, bits_dev, out_dtype, params, workspace, out, stream):
+    _dev_check(bits_dev)
+    p = params or default_params()
+    op = N.OP_GEMV if name == "autofp_gemv" else N.OP_GEMM
+    if out is None:
+        out = torch.empty(x.rows, w.rows, dtype=out_dtype, device=w.codes.device)
+    if workspace is None:
+        workspace = _workspace(op, x.rows, x.k, w.codes.device)
+    ws_, xs_ = w.struct(), x.struct()
+    N.check(fn(C.byref(ws_), C.byref(xs_), int(bits), _ptr(bits_dev), _ptr(out), _DT[out.dtype],
+               C.byref(p), _ptr(workspace), workspace.numel(), _stream(stream)), name)
+    return out
+
+
+def gemv(w: AutoFPTensor, x: AutoFPTensor, bits=4, bits_dev=None, out_dtype=torch.float32,
+         params=None, workspace=None, out=None, stream=None) -> torch.Tensor:
+    """y = Xhat . What^T at level ``bits`` (decode path, autofp_gemv)."""
+    return _linear(N.lib().autofp_gemv, "autofp_gemv", w, x, bits, bits_dev, out_dtype, params,
+                   workspace, out, stream)
+
+
+def gemm(w: AutoFPTensor, x: AutoFPTensor, bits=4, bits_dev=None, out_dtype=torch.float32,
+         params=None, workspace=None, out=None, stream=None) -> torch.Tensor:
+    """y = Xhat . What^T at level ``bits`` (prefill path, autofp_gemm)."""
+    return _linear(N.lib().autofp_gemm, "autofp_gemm", w, x, bits, bits_dev, out_dtype, params,
+                   workspace, out, stream)
+
+
+def policy_signals(logits=None, h_prev=None, h_cur=None, params=None, stream=None):
+    """(G_E per row or None, L_A per row or None) via autofp_policy_signals."""
+    _dev_check(logits, h_prev, h_cur)
+    p = params or default_params()
+    ent = upd = None
+    batch = vocab = hidden = 0
+    hdt = N.F32
+    if logits is not None:
+        if logits.dtype != torch.float32 or logits.dim() != 2:
+            raise ValueError("logits must be 2-D float32")
+        batch, vocab = logits.shape
+        ent = torch.empty(batch, dtype=torch.float32, device=logits.device)
+    if h_prev is not None:
+        if h_prev.shape != h_cur.shape or h_prev.dtype != h_cur.dtype or h_prev.dim() != 2:
+            raise ValueError("h_prev and h_cur must be matching 2-D tensors")
+        if logits is not None and h_prev.shape[0] != batch:
+            raise ValueError("logits and hidden states need the same batch")
+        batch, hidden = h_prev.shape
+        hdt = _DT[h_prev.dtype]
+        upd = torch.empty(batch, dtype=torch.float32, device=h_prev.device)
+    N.check(N.lib().autofp_policy_signals(_ptr(logits), batch, vocab, _ptr(h_prev), _ptr(h_cur), hdt,
+                                          hidden, C.byref(p), _ptr(ent), _ptr(upd), _stream(stream)),
+            "autofp_policy_signals")
+    return ent, upd

@@ -1,0 +1,127 @@
+// Device-side helpers of the AutoFP kernels for gfx950: element/scale codecs,
+// packed-operand conversions and wave reductions.
+//
+// Formats ("AutoEMatic: Runtime-Adaptive Mixed-Precision LLM Inference via
+// Automatic Exponent-Mantissa Refinement", arXiv 2611.10165v1, App. B,
+// Tables 5-6):
+//   E2M1 element  s|e1|e0|m, bias 1, magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}
+//   E4M3 scale    OCP E4M3FN, bias 7, subnormals m * 2^-9, max 448
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace afp {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// Scalar codecs (encode side; exact IEEE fp32, no contraction)
+// ---------------------------------------------------------------------------
+
+// E4M3 value of a scale code; the sign bit is ignored (scales are magnitudes).
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+  code &= 0x7F;
+  const uint32_t e = code >> 3, m = code & 7;
+  if (e == 0) return (float)m * 0.001953125f;        // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Nearest E4M3 code to b >= 0 (round half to even), saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_encode(float b) {
+  if (!(b < 448.0f)) return 0x7Eu;
+  if (b < 0.015625f) {                                 // below 2^-6: step 2^-9
+    return (uint32_t)rintf(b * 512.0f);                // 0..8 (8 = code of 2^-6)
+  }
+  uint32_t u = __float_as_uint(b);
+  u += 0x7FFFFu + ((u >> 20) & 1u);                    // round mantissa to 3 bits, ties even
+  const uint32_t code = (u >> 20) - (120u << 3);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// E2M1 magnitude index of |v| with round half to even: the decision points are
+// the midpoints 0.25 .. 5; a tie goes to the even index (mantissa bit 0).
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+  const float a = fabsf(v);
+  const uint32_t i = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return i ? (i | ((__float_as_uint(v) >> 28) & 8u)) : 0u;   // canonical +0
+}
+
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const float mag = e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : 0.5f * (float)m;
+  return (c & 8u) ? -mag : mag;
+}
+
+// Signed offset for a residual r = v - q: argmin over d in {-2,-1,0,1} of
+// |r - d/8|, ties to the smaller |d|. Returned as its 2-bit two's-complement code.
+__device__ __forceinline__ uint32_t offset_code(float r) {
+  const int d = (r > 0.0625f) ? 1 : (r >= -0.0625f) ? 0 : (r >= -0.1875f) ? -1 : -2;
+  return (uint32_t)d & 3u;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);   // quiet NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Packed-operand conversions (compute side)
+// ---------------------------------------------------------------------------
+
+// Eight E2M1 codes of one dword (element 2i in the low nibble of byte i) to
+// eight fp16 values, via the gfx950 fp4 converts with unit scale (exact).
+__device__ __forceinline__ half8v fp4x8_to_half8(uint32_t w) {
+  const half2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  const half2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  const half2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  const half2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  return half8v{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// AutoFP2 digit codes from eight E2M1 codes: keep the sign, magnitude bits
+// {e1 AND e0, e1 XOR e0} placed as the E2M1 codes of 2 (0b100) and 1 (0b010).
+__device__ __forceinline__ uint32_t autofp2_codes(uint32_t w) {
+  const uint32_t e1 = (w >> 2) & 0x11111111u;
+  const uint32_t e0 = (w >> 1) & 0x11111111u;
+  return (w & 0x88888888u) | ((e1 & e0) << 2) | ((e1 ^ e0) << 1);
+}
+
+// fp16 offsets of one offset byte: d_e / 8 for elements e = 0..3.
+__device__ __forceinline__ void offsets_to_half4(uint32_t byte, half2v &lo, half2v &hi) {
+  auto dv = [](uint32_t c) -> _Float16 {
+    const int d = (int)(c & 3u) - (int)((c & 2u) << 1);   // sign-extend 2 bits
+    return (_Float16)((float)d * 0.125f);
+  };
+  lo = half2v{dv(byte), dv(byte >> 2)};
+  hi = half2v{dv(byte >> 4), dv(byte >> 6)};
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions (64-wide wavefronts)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace afp

@@ -1,0 +1,94 @@
+// Host-side launchers shared by the translation units of libautofp (internal;
+// the public interface is include/autofp.h). Each returns the hipError_t of
+// its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "autofp.h"
+
+namespace afp {
+
+constexpr int kGroup = 16;      // elements per NVFP4 group
+constexpr int kAmaxBlocks = 1024;   // max partial-max blocks of the tensor-scale pass
+
+inline int64_t mask_bytes(int64_t k) { return (k + 31) / 32; }
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// ---- encode.hip ----
+// Partial |x| maxima: writes n_partial floats to partial.
+hipError_t launch_amax_partial(const void *x, int dtype, int64_t n, float *partial, int n_partial,
+                               hipStream_t s);
+int amax_partial_count(int64_t n);
+
+// Exclusive prefix of popcounts over the mask bytes: prefix[i] = refined
+// subgroups in bytes [0, i); prefix has nbytes + 1 entries.
+hipError_t launch_mask_prefix(const uint8_t *mask, int64_t nbytes, int32_t *prefix, hipStream_t s);
+
+struct EncodeArgs {
+  const void *x;
+  int dtype;
+  int64_t rows, k;
+  const float *partial;        // amax partials
+  int n_partial;
+  uint8_t *codes, *scales;
+  float *tensor_scale;
+  // activation refinement (dense offsets)
+  int act_refine;
+  const uint8_t *exclude_mask;  // [mask_bytes(k)] or null
+  float thresh;
+  uint8_t *act_mask;            // [rows][mask_bytes(k)]
+  uint8_t *act_offsets;         // [rows][k/4]
+  // weight refinement (compacted offsets)
+  const uint8_t *w_mask;        // [mask_bytes(k)] or null
+  const int32_t *w_prefix;      // mask prefix table
+  int32_t n_refined;
+  uint8_t *w_offsets;           // [rows][n_refined]
+};
+hipError_t launch_encode(const EncodeArgs &a, hipStream_t s);
+
+// Weight-mask selection ([AE] App. E, Alg. 1 allocation with H = I).
+hipError_t launch_select_mask(const float *w, int64_t rows, int64_t k, int32_t budget,
+                              const float *partial, int n_partial, double *row_gain,
+                              double *col_gain, uint8_t *mask_out, hipStream_t s);
+
+// ---- gemv.hip ----
+struct LinearArgs {
+  // weight operand
+  const uint8_t *w_codes, *w_scales, *w_mask, *w_offsets;
+  const float *w_T;
+  int32_t n_refined;
+  int64_t n;                    // weight rows (outputs)
+  // activation operand
+  const uint8_t *x_codes, *x_scales, *x_offsets;
+  const float *x_T;
+  int64_t b;                    // tokens
+  int64_t k;
+  // level
+  int32_t bits;
+  const int32_t *bits_dev;
+  float c2;
+  // output
+  void *y;
+  int y_dtype;
+  // scratch
+  _Float16 *xh;                 // dequantized activations [b][kpad]
+  int64_t kpad;
+  int32_t *prefix;              // weight-mask prefix table (GEMM)
+};
+int64_t xh_kpad(int64_t k);
+hipError_t launch_act_dequant(const LinearArgs &a, hipStream_t s);
+hipError_t launch_gemv(const LinearArgs &a, hipStream_t s);
+
+// ---- gemm.hip ----
+hipError_t launch_gemm(const LinearArgs &a, hipStream_t s);
+
+// ---- signals.hip ----
+hipError_t launch_entropy(const float *logits, int64_t batch, int64_t vocab, int top_k,
+                          float *out, hipStream_t s);
+hipError_t launch_update_norm(const void *h_prev, const void *h_cur, int dtype, int64_t batch,
+                              int64_t hidden, float eps, float *out, hipStream_t s);
+
+}  // namespace afp

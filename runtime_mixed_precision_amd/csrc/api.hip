@@ -1,0 +1,334 @@
+// C ABI of libautofp (declared in include/autofp.h): argument checks,
+// workspace carving and kernel dispatch. No allocation, no synchronization.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "afp_launch.h"
+#include "autofp.h"
+
+using namespace afp;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (((uintptr_t)p) & 15u) == 0; }
+
+bool valid_k(int64_t k) { return k >= 16 && (k % 16) == 0; }
+
+autofp_status from_hip(hipError_t e) { return e == hipSuccess ? AUTOFP_OK : AUTOFP_ERR_HIP; }
+
+autofp_params params_or_default(const autofp_params *p) {
+  autofp_params d;
+  autofp_default_params(&d);
+  return p ? *p : d;
+}
+
+int32_t refined_budget(int64_t k, double rho) {
+  double r = floor(rho * (double)k / 4.0);
+  const double cap = 2.0 * (double)(k / 16);
+  if (r > cap) r = cap;
+  if (r < 0) r = 0;
+  return (int32_t)r;
+}
+
+// workspace pieces
+size_t ws_quantize(int64_t rows, int64_t k) {
+  (void)rows;
+  return align_up(sizeof(float) * kAmaxBlocks) + align_up(sizeof(int32_t) * (mask_bytes(k) + 1));
+}
+
+size_t ws_select(int64_t rows, int64_t k) {
+  const size_t ncol = (size_t)(k / 4), ng = (size_t)(k / 16);
+  return align_up(sizeof(float) * kAmaxBlocks) + align_up(sizeof(double) * (size_t)rows * ncol) +
+         align_up(sizeof(double) * (ncol + 2 * ng) + sizeof(int32_t) * 4 * ng);
+}
+
+size_t ws_linear(int64_t tokens, int64_t k) {
+  return align_up(sizeof(_Float16) * (size_t)tokens * (size_t)xh_kpad(k)) +
+         align_up(sizeof(int32_t) * (mask_bytes(k) + 1));
+}
+
+autofp_status check_packed(const autofp_packed *t, int32_t kind) {
+  if (!t) return AUTOFP_ERR_NULL;
+  if (t->kind != kind) return AUTOFP_ERR_KIND;
+  if (t->rows < 1 || !valid_k(t->k)) return AUTOFP_ERR_SHAPE;
+  if (!t->codes || !t->scales || !t->tensor_scale) return AUTOFP_ERR_NULL;
+  if (!aligned16(t->codes) || !aligned16(t->scales) || !aligned16(t->tensor_scale) ||
+      (t->mask && !aligned16(t->mask)) || (t->offsets && !aligned16(t->offsets)))
+    return AUTOFP_ERR_ARG;
+  if (kind == AUTOFP_WEIGHT && (t->n_refined < 0 || t->n_refined > 2 * (t->k / 16)))
+    return AUTOFP_ERR_ARG;
+  return AUTOFP_OK;
+}
+
+bool has_refinement(const autofp_packed *w, const autofp_packed *x) {
+  const bool w_ok = w->mask != nullptr && (w->n_refined == 0 || w->offsets != nullptr);
+  const bool x_ok = x->offsets != nullptr;
+  return w_ok && x_ok;
+}
+
+autofp_status linear_common(const autofp_packed *w, const autofp_packed *x, int32_t bits,
+                            const int32_t *bits_dev, void *y, int32_t y_dtype,
+                            const autofp_params *p, void *ws, size_t ws_bytes, LinearArgs &a) {
+  autofp_status st = check_packed(w, AUTOFP_WEIGHT);
+  if (st != AUTOFP_OK) return st;
+  st = check_packed(x, AUTOFP_ACTIVATION);
+  if (st != AUTOFP_OK) return st;
+  if (w->k != x->k) return AUTOFP_ERR_SHAPE;
+  if (!y) return AUTOFP_ERR_NULL;
+  if (!aligned16(y)) return AUTOFP_ERR_ARG;
+  if (y_dtype != AUTOFP_F32 && y_dtype != AUTOFP_BF16) return AUTOFP_ERR_DTYPE;
+  if (!bits_dev && bits != 2 && bits != 4 && bits != 6) return AUTOFP_ERR_BITS;
+  if ((bits_dev || bits == 6) && !has_refinement(w, x)) return AUTOFP_ERR_MISSING_REFINEMENT;
+  const size_t need = ws_linear(x->rows, x->k);
+  if (!ws || ws_bytes < need) return AUTOFP_ERR_WORKSPACE;
+  if (!aligned16(ws)) return AUTOFP_ERR_ARG;
+  const autofp_params pp = params_or_default(p);
+  a.w_codes = w->codes;
+  a.w_scales = w->scales;
+  a.w_mask = w->mask;
+  a.w_offsets = w->offsets;
+  a.w_T = w->tensor_scale;
+  a.n_refined = w->n_refined;
+  a.n = w->rows;
+  a.x_codes = x->codes;
+  a.x_scales = x->scales;
+  a.x_offsets = x->offsets;
+  a.x_T = x->tensor_scale;
+  a.b = x->rows;
+  a.k = x->k;
+  a.bits = bits;
+  a.bits_dev = bits_dev;
+  a.c2 = pp.c2;
+  a.y = y;
+  a.y_dtype = y_dtype;
+  a.kpad = xh_kpad(x->k);
+  a.xh = (_Float16 *)ws;
+  a.prefix = (int32_t *)((char *)ws + align_up(sizeof(_Float16) * (size_t)x->rows * (size_t)a.kpad));
+  return AUTOFP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+autofp_status autofp_default_params(autofp_params *p) {
+  if (!p) return AUTOFP_ERR_NULL;
+  p->rho = 0.2;
+  p->act_nmse_thresh = 0.003f;
+  p->c2 = 2.0f;
+  p->top_k = 10;
+  p->eps = 1e-6f;
+  return AUTOFP_OK;
+}
+
+const char *autofp_status_string(autofp_status s) {
+  switch (s) {
+    case AUTOFP_OK: return "ok";
+    case AUTOFP_ERR_NULL: return "null pointer";
+    case AUTOFP_ERR_SHAPE: return "bad shape (k must be a positive multiple of 16)";
+    case AUTOFP_ERR_BITS: return "precision level not in {2, 4, 6}";
+    case AUTOFP_ERR_KIND: return "operand kind mismatch";
+    case AUTOFP_ERR_WORKSPACE: return "workspace missing or too small";
+    case AUTOFP_ERR_MISSING_REFINEMENT: return "level 6 needs masks and offsets";
+    case AUTOFP_ERR_DTYPE: return "unsupported dtype";
+    case AUTOFP_ERR_ARG: return "argument out of range or misaligned";
+    case AUTOFP_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+autofp_status autofp_packed_bytes(int64_t rows, int64_t k, int32_t kind, int32_t refine,
+                                  int32_t n_refined, size_t out_bytes[5]) {
+  if (!out_bytes) return AUTOFP_ERR_NULL;
+  if (rows < 1 || !valid_k(k)) return AUTOFP_ERR_SHAPE;
+  if (kind != AUTOFP_WEIGHT && kind != AUTOFP_ACTIVATION) return AUTOFP_ERR_KIND;
+  if (n_refined < 0 || n_refined > 2 * (k / 16)) return AUTOFP_ERR_ARG;
+  out_bytes[0] = (size_t)(rows * (k / 2));
+  out_bytes[1] = (size_t)(rows * (k / 16));
+  out_bytes[2] = sizeof(float);
+  out_bytes[3] = 0;
+  out_bytes[4] = 0;
+  if (refine) {
+    if (kind == AUTOFP_WEIGHT) {
+      out_bytes[3] = (size_t)mask_bytes(k);
+      out_bytes[4] = (size_t)rows * (size_t)n_refined;
+    } else {
+      out_bytes[3] = (size_t)(rows * mask_bytes(k));
+      out_bytes[4] = (size_t)(rows * (k / 4));
+    }
+  }
+  return AUTOFP_OK;
+}
+
+autofp_status autofp_weight_refined_count(int64_t k, const autofp_params *p, int32_t *n_refined) {
+  if (!p || !n_refined) return AUTOFP_ERR_NULL;
+  if (!valid_k(k)) return AUTOFP_ERR_SHAPE;
+  if (!(p->rho >= 0.0 && p->rho <= 1.0)) return AUTOFP_ERR_ARG;
+  *n_refined = refined_budget(k, p->rho);
+  return AUTOFP_OK;
+}
+
+autofp_status autofp_workspace_bytes(int32_t op, int64_t rows, int64_t k, size_t *bytes) {
+  if (!bytes) return AUTOFP_ERR_NULL;
+  if (rows < 1 || !valid_k(k)) return AUTOFP_ERR_SHAPE;
+  switch (op) {
+    case AUTOFP_OP_QUANTIZE: *bytes = ws_quantize(rows, k); return AUTOFP_OK;
+    case AUTOFP_OP_SELECT_MASK:
+      if (k > 65536) return AUTOFP_ERR_SHAPE;
+      *bytes = ws_select(rows, k);
+      return AUTOFP_OK;
+    case AUTOFP_OP_GEMV:
+    case AUTOFP_OP_GEMM: *bytes = ws_linear(rows, k); return AUTOFP_OK;
+    default: return AUTOFP_ERR_ARG;
+  }
+}
+
+autofp_status autofp_select_weight_mask(const float *w, int64_t rows, int64_t k,
+                                        const autofp_params *p, uint8_t *mask_out, void *workspace,
+                                        size_t workspace_bytes, void *stream) {
+  if (!w || !p || !mask_out) return AUTOFP_ERR_NULL;
+  if (rows < 1 || !valid_k(k) || k > 65536) return AUTOFP_ERR_SHAPE;
+  if (!(p->rho >= 0.0 && p->rho <= 1.0)) return AUTOFP_ERR_ARG;
+  if (!aligned16(w) || !aligned16(mask_out)) return AUTOFP_ERR_ARG;
+  if (!workspace || workspace_bytes < ws_select(rows, k)) return AUTOFP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return AUTOFP_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  float *partial = (float *)ws;
+  ws += align_up(sizeof(float) * kAmaxBlocks);
+  double *row_gain = (double *)ws;
+  ws += align_up(sizeof(double) * (size_t)rows * (size_t)(k / 4));
+  double *col_gain = (double *)ws;
+  const int np = amax_partial_count(rows * k);
+  hipError_t e = launch_amax_partial(w, AUTOFP_F32, rows * k, partial, np, s);
+  if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  e = launch_select_mask(w, rows, k, refined_budget(k, p->rho), partial, np, row_gain, col_gain,
+                         mask_out, s);
+  return from_hip(e);
+}
+
+autofp_status autofp_quantize(const void *x, int32_t x_dtype, int32_t refine,
+                              const uint8_t *exclude_mask, const autofp_params *p,
+                              autofp_packed *out, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  if (!x || !out) return AUTOFP_ERR_NULL;
+  if (x_dtype != AUTOFP_F32 && x_dtype != AUTOFP_BF16) return AUTOFP_ERR_DTYPE;
+  if (out->kind != AUTOFP_WEIGHT && out->kind != AUTOFP_ACTIVATION) return AUTOFP_ERR_KIND;
+  if (out->rows < 1 || !valid_k(out->k)) return AUTOFP_ERR_SHAPE;
+  if (!out->codes || !out->scales || !out->tensor_scale) return AUTOFP_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out->codes) || !aligned16(out->scales) ||
+      !aligned16(out->tensor_scale) || (out->mask && !aligned16(out->mask)) ||
+      (out->offsets && !aligned16(out->offsets)) || (exclude_mask && !aligned16(exclude_mask)))
+    return AUTOFP_ERR_ARG;
+  const autofp_params pp = params_or_default(p);
+  const bool act_refine = out->kind == AUTOFP_ACTIVATION && refine;
+  const bool w_refine = out->kind == AUTOFP_WEIGHT && out->mask != nullptr;
+  if (act_refine && (!out->mask || !out->offsets)) return AUTOFP_ERR_MISSING_REFINEMENT;
+  if (out->kind == AUTOFP_WEIGHT && refine && !out->mask) return AUTOFP_ERR_MISSING_REFINEMENT;
+  if (w_refine) {
+    if (out->n_refined < 0 || out->n_refined > 2 * (out->k / 16)) return AUTOFP_ERR_ARG;
+    if (out->n_refined > 0 && !out->offsets) return AUTOFP_ERR_MISSING_REFINEMENT;
+  }
+  if (!workspace || workspace_bytes < ws_quantize(out->rows, out->k)) return AUTOFP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return AUTOFP_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  float *partial = (float *)workspace;
+  int32_t *prefix = (int32_t *)((char *)workspace + align_up(sizeof(float) * kAmaxBlocks));
+  const int64_t n = out->rows * out->k;
+  const int np = amax_partial_count(n);
+  hipError_t e = launch_amax_partial(x, x_dtype, n, partial, np, s);
+  if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  if (w_refine) {
+    e = launch_mask_prefix(out->mask, mask_bytes(out->k), prefix, s);
+    if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  }
+  EncodeArgs a{};
+  a.x = x;
+  a.dtype = x_dtype;
+  a.rows = out->rows;
+  a.k = out->k;
+  a.partial = partial;
+  a.n_partial = np;
+  a.codes = out->codes;
+  a.scales = out->scales;
+  a.tensor_scale = out->tensor_scale;
+  a.act_refine = act_refine ? 1 : 0;
+  a.exclude_mask = act_refine ? exclude_mask : nullptr;
+  a.thresh = pp.act_nmse_thresh;
+  a.act_mask = act_refine ? out->mask : nullptr;
+  a.act_offsets = act_refine ? out->offsets : nullptr;
+  a.w_mask = w_refine ? out->mask : nullptr;
+  a.w_prefix = prefix;
+  a.n_refined = out->n_refined;
+  a.w_offsets = out->offsets;
+  return from_hip(launch_encode(a, s));
+}
+
+autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_t bits,
+                          const int32_t *bits_dev, void *y, int32_t y_dtype,
+                          const autofp_params *p, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  LinearArgs a{};
+  const autofp_status st =
+      linear_common(w, x, bits, bits_dev, y, y_dtype, p, workspace, workspace_bytes, a);
+  if (st != AUTOFP_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_act_dequant(a, s);
+  if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  return from_hip(launch_gemv(a, s));
+}
+
+autofp_status autofp_gemm(const autofp_packed *w, const autofp_packed *x, int32_t bits,
+                          const int32_t *bits_dev, void *y, int32_t y_dtype,
+                          const autofp_params *p, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  LinearArgs a{};
+  const autofp_status st =
+      linear_common(w, x, bits, bits_dev, y, y_dtype, p, workspace, workspace_bytes, a);
+  if (st != AUTOFP_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_act_dequant(a, s);
+  if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  if (w->mask && (bits_dev || bits == 6)) {
+    e = launch_mask_prefix(w->mask, mask_bytes(w->k), a.prefix, s);
+    if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  }
+  return from_hip(launch_gemm(a, s));
+}
+
+autofp_status autofp_policy_signals(const float *logits, int64_t batch, int64_t vocab,
+                                    const void *h_prev, const void *h_cur, int32_t h_dtype,
+                                    int64_t hidden, const autofp_params *p, float *entropy_out,
+                                    float *update_out, void *stream) {
+  const autofp_params pp = params_or_default(p);
+  if (!entropy_out && !update_out) return AUTOFP_ERR_NULL;
+  if (batch < 1) return AUTOFP_ERR_SHAPE;
+  if (entropy_out) {
+    if (!logits) return AUTOFP_ERR_NULL;
+    if (vocab < 1) return AUTOFP_ERR_SHAPE;
+    if (pp.top_k < 1 || (pp.top_k > 32 && pp.top_k < vocab)) return AUTOFP_ERR_ARG;
+    if (!aligned16(logits)) return AUTOFP_ERR_ARG;
+  }
+  if (update_out) {
+    if (!h_prev || !h_cur) return AUTOFP_ERR_NULL;
+    if (hidden < 1) return AUTOFP_ERR_SHAPE;
+    if (h_dtype != AUTOFP_F32 && h_dtype != AUTOFP_BF16) return AUTOFP_ERR_DTYPE;
+    if (!(pp.eps >= 0.0f)) return AUTOFP_ERR_ARG;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (entropy_out) {
+    const hipError_t e = launch_entropy(logits, batch, vocab, pp.top_k, entropy_out, s);
+    if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  }
+  if (update_out) {
+    const hipError_t e = launch_update_norm(h_prev, h_cur, h_dtype, batch, hidden, pp.eps, update_out, s);
+    if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  }
+  return AUTOFP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,482 @@
+// AutoFP encode kernels for gfx950: per-tensor scale, NVFP4 base, AutoFP6
+// offsets and masks, and the offline weight-mask selection.
+//
+// "AutoEMatic: Runtime-Adaptive Mixed-Precision LLM Inference via Automatic
+// Exponent-Mantissa Refinement" (arXiv 2611.10165v1):
+//   App. B.1, Eqs. 2-3   T = amax(X)/(6*448), B_j = E4M3(amax(X_j)/(6T)),
+//                        q_i = E2M1(x_i/(T B_j)), round to nearest, ties to even
+//   §3.2                 signed offsets d in {-2,-1,0,+1}, delta = d/8,
+//                        4-bit subgroup masks, weight mask shared by all rows
+//   §6.4, §5.1           activation subgroups refined when NMSE > 0.003,
+//                        excluding the weight mask
+//   App. E, Alg. 1       weight refinement budget rho*K/4, greedy allocation
+//
+// Every fp32 step is IEEE-rounded in the order written (no contraction), so
+// the codes are a deterministic function of the input.
+#include <hip/hip_runtime.h>
+
+#include "afp_device.h"
+#include "afp_launch.h"
+
+namespace afp {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float load_elem(const void *x, int dtype, int64_t i) {
+  return dtype == AUTOFP_BF16 ? bf16_to_f32(((const uint16_t *)x)[i]) : ((const float *)x)[i];
+}
+
+// ---------------------------------------------------------------------------
+// Tensor scale: partial maxima, then every encode block folds them (no atomics,
+// no zero-initialised scratch, identical T in every block).
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void amax_partial_kernel(const void *__restrict__ x,
+                                                                int dtype, int64_t n,
+                                                                float *__restrict__ partial) {
+  float m = 0.0f;
+  const int64_t n8 = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < n8; u += stride) {
+    if (dtype == AUTOFP_BF16) {
+      const uint4 p = ((const uint4 *)x)[u];
+      const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m = fmaxf(m, fabsf(__uint_as_float(w[j] << 16)));
+        m = fmaxf(m, fabsf(__uint_as_float(w[j] & 0xFFFF0000u)));
+      }
+    } else {
+      const float4 a = ((const float4 *)x)[2 * u];
+      const float4 b = ((const float4 *)x)[2 * u + 1];
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+    }
+  }
+  if (blockIdx.x == 0) {
+    for (int64_t i = n8 * 8 + threadIdx.x; i < n; i += kThreads) m = fmaxf(m, fabsf(load_elem(x, dtype, i)));
+  }
+  m = wave_max(m);
+  __shared__ float red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[w]);
+    partial[blockIdx.x] = r;
+  }
+}
+
+// max over the partials, computed by a whole block
+__device__ float fold_partials(const float *partial, int n_partial) {
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n_partial; i += blockDim.x) m = fmaxf(m, partial[i]);
+  m = wave_max(m);
+  __shared__ float red[16];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Mask prefix (exclusive popcount scan over the packed weight-mask bytes)
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(1024) void mask_prefix_kernel(const uint8_t *__restrict__ mask,
+                                                           int64_t nbytes,
+                                                           int32_t *__restrict__ prefix) {
+  const int t = threadIdx.x;
+  const int64_t per = (nbytes + 1023) / 1024;
+  const int64_t b0 = t * per;
+  int32_t local = 0;
+  for (int64_t i = b0; i < b0 + per && i < nbytes; ++i) local += __popc((uint32_t)mask[i]);
+  __shared__ int32_t sc[1024];
+  sc[t] = local;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t v = (t >= off) ? sc[t - off] : 0;
+    __syncthreads();
+    sc[t] += v;
+    __syncthreads();
+  }
+  int32_t run = sc[t] - local;   // exclusive
+  for (int64_t i = b0; i < b0 + per && i < nbytes; ++i) {
+    prefix[i] = run;
+    run += __popc((uint32_t)mask[i]);
+  }
+  if (t == 1023) prefix[nbytes] = sc[1023];
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 base of two consecutive groups (32 elements), shared by the encoder
+// and the weight-gain kernel.
+// ---------------------------------------------------------------------------
+
+struct PairEnc {
+  float v[32];        // normalized values x / (T B)
+  uint32_t q[32];     // E2M1 codes
+  uint32_t B[2];      // E4M3 scale codes
+};
+
+__device__ __forceinline__ void encode_pair(const float *xv, int ng, float T, float sixT,
+                                            PairEnc &e) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    if (g < ng) {
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xv[16 * g + i]));
+      const float b = sixT > 0.0f ? a / sixT : 0.0f;
+      const uint32_t B = e4m3_encode(b);
+      const float s = T * e4m3_value(B);
+      e.B[g] = B;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float v = (s != 0.0f) ? xv[16 * g + i] / s : 0.0f;
+        e.v[16 * g + i] = v;
+        e.q[16 * g + i] = e2m1_encode(v);
+      }
+    } else {
+      e.B[g] = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        e.v[16 * g + i] = 0.0f;
+        e.q[16 * g + i] = 0;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void load_pair(const void *x, int dtype, int64_t base, int nel,
+                                          bool vec_ok, float *xv) {
+  if (vec_ok && nel == 32) {
+    if (dtype == AUTOFP_BF16) {
+      const uint4 *p = (const uint4 *)((const uint16_t *)x + base);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 w = p[c];
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xv[8 * c + 2 * j] = __uint_as_float(ww[j] << 16);
+          xv[8 * c + 2 * j + 1] = __uint_as_float(ww[j] & 0xFFFF0000u);
+        }
+      }
+    } else {
+      const float4 *p = (const float4 *)((const float *)x + base);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float4 w = p[c];
+        xv[4 * c] = w.x;
+        xv[4 * c + 1] = w.y;
+        xv[4 * c + 2] = w.z;
+        xv[4 * c + 3] = w.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) xv[i] = (i < nel) ? load_elem(x, dtype, base + i) : 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Encoder: one thread per 32 elements (two groups) of one row.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
+#pragma clang fp contract(off)
+  const float amax = fold_partials(a.partial, a.n_partial);
+  const float T = amax / 2688.0f;
+  const float sixT = 6.0f * T;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.tensor_scale = T;
+
+  const int64_t P2 = (a.k + 31) / 32;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= a.rows * P2) return;
+  const int64_t row = idx / P2;
+  const int64_t pr = idx - row * P2;
+  const int64_t k0 = pr * 32;
+  const int nel = (int)((a.k - k0) < 32 ? (a.k - k0) : 32);
+  const int ng = nel / 16;
+  const bool vec_ok = (a.k % 32) == 0;
+
+  float xv[32];
+  load_pair(a.x, a.dtype, row * a.k + k0, nel, vec_ok, xv);
+  PairEnc e;
+  encode_pair(xv, ng, T, sixT, e);
+
+  // codes: element 2i in the low nibble of byte i
+  uint32_t cw[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc |= e.q[8 * w + j] << (4 * j);
+    cw[w] = acc;
+  }
+  uint8_t *cdst = a.codes + row * (a.k / 2) + k0 / 2;
+  uint8_t *sdst = a.scales + row * (a.k / 16) + k0 / 16;
+  if (vec_ok) {
+    *(uint4 *)cdst = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+    *(uint16_t *)sdst = (uint16_t)(e.B[0] | (e.B[1] << 8));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < nel / 2) cdst[i] = (uint8_t)(cw[i >> 2] >> (8 * (i & 3)));
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      if (g < ng) sdst[g] = (uint8_t)e.B[g];
+  }
+
+  const bool want_act = a.act_refine != 0;
+  const bool want_w = a.w_mask != nullptr;
+  if (!want_act && !want_w) return;
+
+  // per-subgroup offset bytes (d = argmin |r - d/8|, r = v - q, exact in fp32)
+  uint32_t ob[8];
+#pragma unroll
+  for (int sg = 0; sg < 8; ++sg) {
+    uint32_t byte = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int el = 4 * sg + i;
+      const float r = e.v[el] - e2m1_value(e.q[el]);
+      byte |= offset_code(r) << (2 * i);
+    }
+    ob[sg] = byte;
+  }
+
+  if (want_act) {
+    const uint32_t ex = a.exclude_mask ? (uint32_t)a.exclude_mask[pr] : 0u;
+    uint32_t mbits = 0;
+#pragma unroll
+    for (int sg = 0; sg < 8; ++sg) {
+      float num = 0.0f, den = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int el = 4 * sg + i;
+        const float r = e.v[el] - e2m1_value(e.q[el]);
+        const float rr = r * r;
+        const float vv = e.v[el] * e.v[el];
+        num = (i == 0) ? rr : num + rr;
+        den = (i == 0) ? vv : den + vv;
+      }
+      const float thr = a.thresh * den;
+      const bool refine = (4 * sg < nel) && den > 0.0f && num > thr && !((ex >> sg) & 1u);
+      if (refine) mbits |= 1u << sg;
+      else ob[sg] = 0;
+    }
+    a.act_mask[row * P2 + pr] = (uint8_t)mbits;
+    uint8_t *odst = a.act_offsets + row * (a.k / 4) + k0 / 4;
+    if (vec_ok) {
+      *(uint2 *)odst = make_uint2(ob[0] | (ob[1] << 8) | (ob[2] << 16) | (ob[3] << 24),
+                                  ob[4] | (ob[5] << 8) | (ob[6] << 16) | (ob[7] << 24));
+    } else {
+#pragma unroll
+      for (int sg = 0; sg < 8; ++sg)
+        if (sg < nel / 4) odst[sg] = (uint8_t)ob[sg];
+    }
+  }
+  if (want_w) {
+    const uint32_t mb = a.w_mask[pr];
+    int32_t pos = a.w_prefix[pr];
+    uint8_t *odst = a.w_offsets + row * (int64_t)a.n_refined;
+#pragma unroll
+    for (int sg = 0; sg < 8; ++sg) {
+      if ((mb >> sg) & 1u) odst[pos++] = (uint8_t)ob[sg];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Weight-mask selection ([AE] App. E, Alg. 1 allocation, identity Hessian)
+// ---------------------------------------------------------------------------
+
+// Per row and subgroup: g = sum_e (eb^2 - er^2) in fp64, eb = w - TB q,
+// er = w - TB (q + d/8), TB = T * B exactly.
+__global__ __launch_bounds__(kThreads) void weight_gain_kernel(const float *__restrict__ w,
+                                                               int64_t rows, int64_t k,
+                                                               const float *partial, int n_partial,
+                                                               double *__restrict__ row_gain) {
+#pragma clang fp contract(off)
+  const float amax = fold_partials(partial, n_partial);
+  const float T = amax / 2688.0f;
+  const float sixT = 6.0f * T;
+  const int64_t P2 = (k + 31) / 32;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= rows * P2) return;
+  const int64_t row = idx / P2;
+  const int64_t pr = idx - row * P2;
+  const int64_t k0 = pr * 32;
+  const int nel = (int)((k - k0) < 32 ? (k - k0) : 32);
+  float xv[32];
+  load_pair(w, AUTOFP_F32, row * k + k0, nel, (k % 32) == 0, xv);
+  PairEnc e;
+  encode_pair(xv, nel / 16, T, sixT, e);
+  double *dst = row_gain + row * (k / 4) + k0 / 4;
+#pragma unroll
+  for (int sg = 0; sg < 8; ++sg) {
+    if (sg >= nel / 4) break;
+    const double tb = (double)T * (double)e4m3_value(e.B[sg >> 2]);
+    double g = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int el = 4 * sg + i;
+      const double q = (double)e2m1_value(e.q[el]);
+      const uint32_t dc = offset_code(e.v[el] - e2m1_value(e.q[el]));
+      const double d = (double)((int)dc - (int)((dc & 2u) << 1));
+      const double x = (double)xv[el];
+      const double eb = x - tb * q;
+      const double er = x - tb * (q + d / 8.0);
+      const double ge = eb * eb - er * er;
+      g = (i == 0) ? ge : g + ge;
+    }
+    dst[sg] = g;
+  }
+}
+
+// Column sums over rows in row order (fp64).
+__global__ __launch_bounds__(kThreads) void gain_colsum_kernel(const double *__restrict__ row_gain,
+                                                               int64_t rows, int64_t ncol,
+                                                               double *__restrict__ col_gain) {
+#pragma clang fp contract(off)
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= ncol) return;
+  double acc = 0.0;
+  for (int64_t n = 0; n < rows; ++n) acc = acc + row_gain[n * ncol + c];
+  col_gain[c] = acc;
+}
+
+// The two best subgroups of each group (gain descending, then subgroup).
+__global__ __launch_bounds__(kThreads) void gain_candidates_kernel(const double *__restrict__ col_gain,
+                                                                   int64_t ngroups,
+                                                                   double *__restrict__ cgain,
+                                                                   int32_t *__restrict__ csg) {
+  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (j >= ngroups) return;
+  double g[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) g[s] = col_gain[4 * j + s];
+  int best = 0;
+  for (int s = 1; s < 4; ++s)
+    if (g[s] > g[best]) best = s;
+  int second = best == 0 ? 1 : 0;
+  for (int s = 0; s < 4; ++s)
+    if (s != best && g[s] > g[second]) second = s;
+  // equal gains rank the lower subgroup first
+  for (int s = 0; s < 4; ++s)
+    if (s != best && g[s] == g[second] && s < second) second = s;
+  cgain[2 * j] = g[best];
+  csg[2 * j] = best;
+  cgain[2 * j + 1] = g[second];
+  csg[2 * j + 1] = second;
+}
+
+// rank(c) = number of candidates ordered before c by (gain desc, group, subgroup);
+// selected iff rank < budget.
+__global__ __launch_bounds__(kThreads) void gain_rank_kernel(const double *__restrict__ cgain,
+                                                             const int32_t *__restrict__ csg,
+                                                             int64_t ncand, int32_t budget,
+                                                             int32_t *__restrict__ selected) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const bool live = c < ncand;
+  const double gc = live ? cgain[c] : 0.0;
+  const int64_t jc = c >> 1;
+  const int32_t sc = live ? csg[c] : 0;
+  __shared__ double tg[kThreads];
+  __shared__ int32_t ts[kThreads];
+  int64_t rank = 0;
+  for (int64_t t0 = 0; t0 < ncand; t0 += kThreads) {
+    const int64_t t = t0 + threadIdx.x;
+    tg[threadIdx.x] = t < ncand ? cgain[t] : 0.0;
+    ts[threadIdx.x] = t < ncand ? csg[t] : 0;
+    __syncthreads();
+    const int64_t lim = (ncand - t0) < kThreads ? (ncand - t0) : kThreads;
+    for (int64_t i = 0; i < lim; ++i) {
+      const double g = tg[i];
+      const int64_t j = (t0 + i) >> 1;
+      const int32_t s = ts[i];
+      const bool before = (g > gc) || (g == gc && (j < jc || (j == jc && s < sc)));
+      rank += before ? 1 : 0;
+    }
+    __syncthreads();
+  }
+  if (live) selected[c] = rank < budget ? 1 : 0;
+}
+
+__global__ __launch_bounds__(kThreads) void mask_write_kernel(const int32_t *__restrict__ csg,
+                                                              const int32_t *__restrict__ selected,
+                                                              int64_t ngroups,
+                                                              uint8_t *__restrict__ mask) {
+  const int64_t pb = (int64_t)blockIdx.x * kThreads + threadIdx.x;   // mask byte
+  if (pb >= (ngroups + 1) / 2) return;
+  uint32_t byte = 0;
+  for (int h = 0; h < 2; ++h) {
+    const int64_t j = 2 * pb + h;
+    if (j >= ngroups) break;
+    uint32_t nib = 0;
+    for (int c = 0; c < 2; ++c)
+      if (selected[2 * j + c]) nib |= 1u << csg[2 * j + c];
+    byte |= nib << (4 * h);
+  }
+  mask[pb] = (uint8_t)byte;
+}
+
+inline unsigned grid_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
+
+}  // namespace
+
+int amax_partial_count(int64_t n) {
+  const int64_t per_block = (int64_t)kThreads * 8 * 4;
+  int64_t b = (n + per_block - 1) / per_block;
+  if (b < 1) b = 1;
+  if (b > kAmaxBlocks) b = kAmaxBlocks;
+  return (int)b;
+}
+
+hipError_t launch_amax_partial(const void *x, int dtype, int64_t n, float *partial, int n_partial,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(amax_partial_kernel, dim3(n_partial), dim3(kThreads), 0, s, x, dtype, n, partial);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_prefix(const uint8_t *mask, int64_t nbytes, int32_t *prefix, hipStream_t s) {
+  hipLaunchKernelGGL(mask_prefix_kernel, dim3(1), dim3(1024), 0, s, mask, nbytes, prefix);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode(const EncodeArgs &a, hipStream_t s) {
+  const int64_t threads = a.rows * ((a.k + 31) / 32);
+  hipLaunchKernelGGL(encode_kernel, dim3(grid_for(threads, kThreads)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_mask(const float *w, int64_t rows, int64_t k, int32_t budget,
+                              const float *partial, int n_partial, double *row_gain,
+                              double *col_gain, uint8_t *mask_out, hipStream_t s) {
+  const int64_t P2 = (k + 31) / 32;
+  const int64_t ncol = k / 4;
+  const int64_t ngroups = k / 16;
+  double *cgain = col_gain + ncol;
+  int32_t *csg = (int32_t *)(cgain + 2 * ngroups);
+  int32_t *sel = csg + 2 * ngroups;
+  hipLaunchKernelGGL(weight_gain_kernel, dim3(grid_for(rows * P2, kThreads)), dim3(kThreads), 0, s,
+                     w, rows, k, partial, n_partial, row_gain);
+  hipLaunchKernelGGL(gain_colsum_kernel, dim3(grid_for(ncol, kThreads)), dim3(kThreads), 0, s,
+                     row_gain, rows, ncol, col_gain);
+  hipLaunchKernelGGL(gain_candidates_kernel, dim3(grid_for(ngroups, kThreads)), dim3(kThreads), 0, s,
+                     col_gain, ngroups, cgain, csg);
+  hipLaunchKernelGGL(gain_rank_kernel, dim3(grid_for(2 * ngroups, kThreads)), dim3(kThreads), 0, s,
+                     cgain, csg, 2 * ngroups, budget, sel);
+  hipLaunchKernelGGL(mask_write_kernel, dim3(grid_for((ngroups + 1) / 2, kThreads)), dim3(kThreads),
+                     0, s, csg, sel, ngroups, mask_out);
+  return hipGetLastError();
+}
+
+}  // namespace afp

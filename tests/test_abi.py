@@ -1,0 +1,146 @@
+"""The C ABI library loads, exports every declared symbol and rejects bad
+arguments before launching anything (CPU only: no kernel runs here)."""
+
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "autofp.h")
+LIB = os.path.join(ROOT, "runtime_mixed_precision_amd", "libautofp.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libautofp.so not built")
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(autofp_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_operations():
+    names = declared()
+    for op in ("autofp_quantize", "autofp_gemv", "autofp_gemm", "autofp_policy_signals"):
+        assert op in names
+
+
+def test_every_declared_symbol_is_exported():
+    from runtime_mixed_precision_amd import _native as N
+    L = N.lib()
+    for name in declared():
+        assert hasattr(L, name), name
+    assert sorted(N.EXPORTS) == declared()
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (autofp_\w+)", out))
+    assert set(declared()) <= exported
+    assert exported <= set(declared())          # nothing undocumented is exported
+
+
+@pytest.fixture(scope="module")
+def N():
+    from runtime_mixed_precision_amd import _native
+    _native.lib()
+    return _native
+
+
+def params(N):
+    p = N.Params()
+    assert N.lib().autofp_default_params(C.byref(p)) == 0
+    return p
+
+
+def test_default_params_are_the_papers(N):
+    p = params(N)
+    assert p.rho == pytest.approx(0.2) and p.act_nmse_thresh == pytest.approx(0.003)
+    assert p.c2 == 2.0 and p.top_k == 10
+    assert N.lib().autofp_default_params(None) == 1
+
+
+def test_sizes(N):
+    L = N.lib()
+    out = (C.c_size_t * 5)()
+    assert L.autofp_packed_bytes(16, 256, N.ACTIVATION, 1, 0, out) == 0
+    assert list(out) == [16 * 128, 16 * 16, 4, 16 * 8, 16 * 64]
+    assert L.autofp_packed_bytes(256, 4096, N.WEIGHT, 1, 204, out) == 0
+    assert list(out) == [256 * 2048, 256 * 256, 4, 128, 256 * 204]
+    assert L.autofp_packed_bytes(16, 250, N.WEIGHT, 0, 0, out) == 2
+    n = C.c_int32()
+    p = params(N)
+    for k, want in ((4096, 204), (14336, 716), (256, 12), (16, 0)):
+        assert L.autofp_weight_refined_count(k, C.byref(p), C.byref(n)) == 0
+        assert n.value == want
+    p.rho = 1.0                        # capped at two refined subgroups per group
+    assert L.autofp_weight_refined_count(256, C.byref(p), C.byref(n)) == 0 and n.value == 32
+    p.rho = 1.5
+    assert L.autofp_weight_refined_count(256, C.byref(p), C.byref(n)) == 8
+    b = C.c_size_t()
+    for op in (N.OP_QUANTIZE, N.OP_SELECT_MASK, N.OP_GEMV, N.OP_GEMM):
+        assert L.autofp_workspace_bytes(op, 64, 4096, C.byref(b)) == 0 and b.value > 0
+    assert L.autofp_workspace_bytes(9, 64, 4096, C.byref(b)) == 8
+    assert L.autofp_workspace_bytes(N.OP_GEMV, 0, 4096, C.byref(b)) == 2
+    assert L.autofp_status_string(5) == b"workspace missing or too small"
+
+
+FAKE = 0x10000    # aligned, never dereferenced: every call below fails its checks first
+
+
+def packed(N, kind, rows=4, k=64, refine=False, n_refined=0):
+    p = N.Packed(rows, k, kind, n_refined, FAKE, FAKE, FAKE, None, None)
+    if refine:
+        p.mask = FAKE
+        p.offsets = FAKE
+    return p
+
+
+def test_quantize_rejects_bad_arguments(N):
+    L = N.lib()
+    p = params(N)
+    ws = C.c_void_p(FAKE)
+    q = lambda x, dt, ref, out, wsz=1 << 20: L.autofp_quantize(x, dt, ref, None, C.byref(p), out, ws, wsz, None)
+    good = packed(N, N.ACTIVATION)
+    assert q(None, N.F32, 0, C.byref(good)) == 1
+    assert q(FAKE, N.F32, 0, None) == 1
+    assert q(FAKE, 7, 0, C.byref(good)) == 7
+    bad = packed(N, N.ACTIVATION, k=40)
+    assert q(FAKE, N.F32, 0, C.byref(bad)) == 2
+    bad = packed(N, 5)
+    assert q(FAKE, N.F32, 0, C.byref(bad)) == 4
+    assert q(FAKE, N.F32, 1, C.byref(good)) == 6          # refine without mask/offsets
+    assert q(FAKE + 4, N.F32, 0, C.byref(good)) == 8      # misaligned input
+    assert q(FAKE, N.F32, 0, C.byref(good), 8) == 5       # workspace too small
+
+
+def test_linear_rejects_bad_arguments(N):
+    L = N.lib()
+    p = params(N)
+    for fn in (L.autofp_gemv, L.autofp_gemm):
+        w = packed(N, N.WEIGHT, rows=8, k=64)
+        x = packed(N, N.ACTIVATION, rows=2, k=64)
+        call = lambda w_, x_, bits, y=FAKE, ws=1 << 20, bd=None: fn(
+            C.byref(w_), C.byref(x_), bits, bd, y, N.F32, C.byref(p), FAKE, ws, None)
+        assert call(w, x, 3) == 3                         # level not in {2,4,6}
+        assert call(x, w, 4) == 4                         # swapped operands
+        assert call(w, x, 6) == 6                         # level 6 without refinement
+        assert call(w, x, 4, bd=FAKE) == 6                # device level needs refinement
+        assert call(w, x, 4, y=None) == 1
+        assert call(w, x, 4, ws=16) == 5
+        x2 = packed(N, N.ACTIVATION, rows=2, k=128)
+        assert call(w, x2, 4) == 2                        # K mismatch
+        wbad = packed(N, N.WEIGHT, rows=8, k=64, refine=True, n_refined=99)
+        assert call(wbad, x, 4) == 8                      # n_refined beyond 2 per group
+
+
+def test_signals_reject_bad_arguments(N):
+    L = N.lib()
+    p = params(N)
+    sig = lambda *a: L.autofp_policy_signals(*a, None)
+    assert sig(FAKE, 1, 100, None, None, N.F32, 0, C.byref(p), None, None) == 1
+    assert sig(None, 1, 100, None, None, N.F32, 0, C.byref(p), FAKE, None) == 1
+    p.top_k = 40
+    assert sig(FAKE, 1, 100, None, None, N.F32, 0, C.byref(p), FAKE, None) == 8
+    p.top_k = 10
+    assert sig(None, 1, 0, FAKE, FAKE, 3, 64, C.byref(p), None, FAKE) == 7
+    assert sig(None, 0, 0, FAKE, FAKE, N.F32, 64, C.byref(p), None, FAKE) == 2

@@ -1,0 +1,193 @@
+"""GPU parity of the AutoFP decode GEMV and prefill GEMM against the fp64
+oracle product of the decoded operands.
+
+Tolerance: the products are exact and only the fp32 accumulation rounds, so
+every output must satisfy |y - y_ref| <= 1e-3 * max(|y_ref|, 0.01 * rms(y_ref
+row)) (relative error 1e-3, guarded near zero crossings of the output)."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import runtime_mixed_precision_amd as A
+from runtime_mixed_precision_amd import synthetic as S
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+RTOL = 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_close(y, ref):
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert y.shape == ref.shape
+    rms = np.sqrt((ref ** 2).mean(axis=1, keepdims=True)) + 1e-300
+    den = np.maximum(np.abs(ref), 0.01 * rms)
+    err = np.abs(y - ref) / den
+    worst = np.unravel_index(np.argmax(err), err.shape)
+    assert err.max() <= RTOL, (err.max(), worst, y[worst], ref[worst])
+    return float(err.max())
+
+
+def operands(n, b, k, seed, outliers=0.01, wdev=DEV):
+    w = S.weights(n, k, seed=seed, tensor_id=1, device=wdev)
+    x = S.activations(b, k, seed=seed, tensor_id=2, outlier_frac=outliers, device=wdev)
+    return w, x
+
+
+def gpu_pack(w, x):
+    wp = A.quantize_weight(w, refine=True)
+    xp4 = A.quantize_activation(x)
+    xp6 = A.quantize_activation(x, refine=True, exclude_mask=wp.mask)
+    return wp, xp4, xp6
+
+
+def oracle_pack(w, x):
+    wn = w.cpu().numpy()
+    xn = x.float().cpu().numpy()
+    bits, _ = O.select_weight_mask(wn, 0.2)
+    wq = O.quantize_weight(wn, O.pack_nibbles(bits))
+    xq4 = O.quantize_activation(xn)
+    xq6 = O.quantize_activation(xn, refine=True, exclude_mask=wq["mask"])
+    return wq, xq4, xq6
+
+
+def run(fn, wp, xp4, xp6, level, **kw):
+    return fn(wp, xp6 if level == 6 else xp4, bits=level, **kw)
+
+
+@pytest.mark.parametrize("level", [2, 4, 6])
+@pytest.mark.parametrize("op", ["gemv", "gemm"])
+def test_config1_layer(level, op):
+    """16x256 bf16 activations (1% outliers x20) times a 256x256 weight."""
+    say(f"case: C1 {op} level {level}")
+    w = S.weights(256, 256, seed=0, tensor_id=2, heavy_frac=0.0, device=DEV)
+    x = S.activations(16, 256, seed=0, tensor_id=1, device=DEV)
+    wp, xp4, xp6 = gpu_pack(w, x)
+    wq, xq4, xq6 = oracle_pack(w, x)
+    y = run(getattr(A, op), wp, xp4, xp6, level)
+    ref = O.linear(wq, xq6 if level == 6 else xq4, level)
+    check_close(y.cpu().numpy(), ref)
+
+
+SHAPES = [  # (N, B, K)
+    (200, 1, 272), (200, 3, 4096 + 16), (64, 8, 512), (48, 16, 256), (130, 17, 384),
+    (96, 33, 1024), (40, 64, 128), (72, 100, 160), (16, 5, 16),
+]
+
+
+@pytest.mark.parametrize("n,b,k", SHAPES)
+@pytest.mark.parametrize("level", [2, 4, 6])
+def test_gemv_shapes(n, b, k, level):
+    say(f"case: gemv N={n} B={b} K={k} level {level}")
+    w, x = operands(n, b, k, seed=n * 7 + b)
+    wp, xp4, xp6 = gpu_pack(w, x)
+    wq, xq4, xq6 = oracle_pack(w, x)
+    y = run(A.gemv, wp, xp4, xp6, level)
+    check_close(y.cpu().numpy(), O.linear(wq, xq6 if level == 6 else xq4, level))
+
+
+GEMM_SHAPES = [(200, 130, 272), (384, 512, 1024), (128, 1, 64), (260, 129, 4096 + 16), (64, 300, 96)]
+
+
+@pytest.mark.parametrize("n,m,k", GEMM_SHAPES)
+@pytest.mark.parametrize("level", [2, 4, 6])
+def test_gemm_shapes(n, m, k, level):
+    say(f"case: gemm N={n} M={m} K={k} level {level}")
+    w, x = operands(n, m, k, seed=n + m + k, outliers=0.005)
+    wp, xp4, xp6 = gpu_pack(w, x)
+    wq, xq4, xq6 = oracle_pack(w, x)
+    y = run(A.gemm, wp, xp4, xp6, level)
+    check_close(y.cpu().numpy(), O.linear(wq, xq6 if level == 6 else xq4, level))
+
+
+@pytest.mark.parametrize("op", ["gemv", "gemm"])
+def test_bf16_output_and_device_level(op):
+    say(f"case: {op} bf16 output and device-side level")
+    w, x = operands(96, 12, 512, seed=4)
+    wp, xp4, xp6 = gpu_pack(w, x)
+    fn = getattr(A, op)
+    for level in (2, 4, 6):
+        y32 = fn(wp, xp6, bits=level)
+        y16 = fn(wp, xp6, bits=level, out_dtype=torch.bfloat16)
+        assert torch.equal(y16, y32.to(torch.bfloat16))
+        dev_bits = torch.tensor([level], dtype=torch.int32, device=DEV)
+        yd = fn(wp, xp6, bits=0, bits_dev=dev_bits)
+        if level != 6:
+            # the activation carries refinement, unused below level 6
+            assert torch.equal(yd, fn(wp, xp4 if level != 6 else xp6, bits=level))
+        else:
+            assert torch.equal(yd, y32)
+
+
+def test_gemv_equals_gemm():
+    say("case: gemv vs gemm agreement")
+    w, x = operands(300, 40, 1024, seed=9)
+    wp, xp4, xp6 = gpu_pack(w, x)
+    for level in (2, 4, 6):
+        xa = xp6 if level == 6 else xp4
+        a = A.gemv(wp, xa, bits=level).cpu().numpy()
+        b = A.gemm(wp, xa, bits=level).cpu().numpy()
+        assert np.abs(a - b).max() <= 1e-5 * np.abs(b).max()
+
+
+@pytest.mark.parametrize("name,b", [("wgate", 1), ("wgate", 8), ("wdown", 8), ("wqkv", 1)])
+def test_full_size_decode_sampled(name, b):
+    """Llama-3-8B-shaped layer at full size: every output of sampled weight
+    rows checked against the oracle at levels 2 and 4 (and 6 on Wqkv)."""
+    n, k = S.LLAMA8B[name]
+    say(f"case: full-size {name} {n}x{k} batch {b}")
+    w = S.weights(n, k, seed=1, tensor_id=list(S.LLAMA8B).index(name), device=DEV)
+    x = S.activations(b, k, seed=1, tensor_id=99, device=DEV)
+    levels = (2, 4, 6) if name == "wqkv" else (2, 4)
+    wp = A.quantize_weight(w, refine=(6 in levels))
+    xp4 = A.quantize_activation(x)
+    xn = x.float().cpu().numpy()
+    rows = np.random.default_rng(2).choice(n, 64, replace=False)
+    wn = w.cpu().numpy()
+    amax = np.abs(wn).max()
+    if 6 in levels:
+        bits, _ = O.select_weight_mask(wn, 0.2)
+        wq = O.quantize_weight(wn[rows], O.pack_nibbles(bits), tensor_amax=amax)
+        xp6 = A.quantize_activation(x, refine=True, exclude_mask=wp.mask)
+        xq6 = O.quantize_activation(xn, refine=True, exclude_mask=wq["mask"])
+    else:
+        wq = O.quantize_weight(wn[rows], tensor_amax=amax)
+        xp6 = xq6 = None
+    xq4 = O.quantize_activation(xn)
+    for level in levels:
+        y = A.gemv(wp, xp6 if level == 6 else xp4, bits=level).cpu().numpy()
+        ref = O.linear(wq, xq6 if level == 6 else xq4, level)
+        check_close(y[:, rows], ref)
+
+
+def test_prefill_sampled_full_size():
+    """2048 x 4096 prefill activations times the Wup shape (14336 x 4096) at
+    levels 4 and 6: sampled rows and columns against the oracle."""
+    say("case: full-size prefill GEMM 2048x4096x14336")
+    n, k = S.LLAMA8B["wup"]
+    w = S.weights(n, k, seed=2, tensor_id=5, device=DEV)
+    x = S.activations(2048, k, seed=2, tensor_id=6, outlier_frac=0.005, outlier_scale=30.0, device=DEV)
+    wp = A.quantize_weight(w, refine=True)
+    xp4 = A.quantize_activation(x)
+    xp6 = A.quantize_activation(x, refine=True, exclude_mask=wp.mask)
+    rng = np.random.default_rng(3)
+    rows = rng.choice(n, 32, replace=False)
+    toks = rng.choice(2048, 32, replace=False)
+    wn = w.cpu().numpy()
+    xn = x.float().cpu().numpy()
+    bits, _ = O.select_weight_mask(wn, 0.2)
+    wq = O.quantize_weight(wn[rows], O.pack_nibbles(bits), tensor_amax=np.abs(wn).max())
+    xa = np.abs(xn).max()
+    for level, xp in ((4, xp4), (6, xp6)):
+        xq = O.quantize_activation(xn[toks], refine=(level == 6), exclude_mask=wq["mask"], tensor_amax=xa)
+        y = A.gemm(wp, xp, bits=level).cpu().numpy()
+        check_close(y[np.ix_(toks, rows)], O.linear(wq, xq, level))

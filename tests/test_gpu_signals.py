@@ -1,0 +1,69 @@
+"""GPU parity of the runtime-policy signals G_E and L_A (tolerance 1e-3
+relative, 1e-6 absolute, against the fp64 oracle)."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import runtime_mixed_precision_amd as A
+from runtime_mixed_precision_amd import synthetic as S
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def close(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert (np.abs(a - b) <= 1e-3 * np.abs(b) + 1e-6).all(), (a, b)
+
+
+@pytest.mark.parametrize("batch,vocab", [(1, S.VOCAB), (4, S.VOCAB), (64, S.VOCAB), (3, 1000), (2, 37), (5, 130)])
+@pytest.mark.parametrize("top_k", [10, 1, 32, None])
+def test_entropy(batch, vocab, top_k):
+    k = vocab if top_k is None else top_k
+    say(f"case: entropy B={batch} V={vocab} k={k}")
+    z = S.logits(batch, vocab, seed=batch + vocab, device=DEV)
+    g, _ = A.policy_signals(logits=z, params=A.default_params(top_k=k))
+    close(g.cpu().numpy(), O.topk_entropy(z.cpu().numpy(), k))
+
+
+def test_entropy_ties_and_extremes():
+    say("case: entropy ties / extremes")
+    V = 5000
+    z = torch.full((3, V), -30.0, device=DEV)
+    z[0, 100:110] = 2.0                       # ten equal leaders -> 1
+    z[1, 7] = 80.0                            # one dominant logit -> 0
+    z[2, ::400] = 5.0                         # 13 tied maxima: top-10 are all 5.0
+    g, _ = A.policy_signals(logits=z)
+    close(g.cpu().numpy(), O.topk_entropy(z.cpu().numpy(), 10))
+    assert abs(float(g[0]) - 1.0) < 1e-6 and float(g[1]) < 1e-6
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("batch,hidden", [(1, 4096), (16, 4096), (64, 4096), (3, 100)])
+def test_update_norm(dtype, batch, hidden):
+    say(f"case: L_A B={batch} H={hidden} {dtype}")
+    hp = S.hidden(batch, hidden, seed=1, tensor_id=0, dtype=dtype, device=DEV)
+    d = S.hidden(batch, hidden, seed=1, tensor_id=1, dtype=torch.float32, device=DEV)
+    hc = (hp.float() + 0.1 * d).to(dtype)
+    _, la = A.policy_signals(h_prev=hp, h_cur=hc)
+    close(la.cpu().numpy(), O.update_norm(hp.float().cpu().numpy(), hc.float().cpu().numpy(), 1e-6))
+
+
+def test_both_signals_in_one_call():
+    say("case: both signals")
+    z = S.logits(8, S.VOCAB, seed=3, device=DEV)
+    hp = S.hidden(8, 4096, seed=3, tensor_id=0, device=DEV)
+    hc = S.hidden(8, 4096, seed=3, tensor_id=1, device=DEV)
+    g, la = A.policy_signals(logits=z, h_prev=hp, h_cur=hc)
+    close(g.cpu().numpy(), O.topk_entropy(z.cpu().numpy(), 10))
+    close(la.cpu().numpy(), O.update_norm(hp.cpu().numpy(), hc.cpu().numpy(), 1e-6))
