@@ -1,0 +1,369 @@
+#!/usr/bin/env python3
+"""AutoFP decode-step benchmark on one MI355X.
+
+Workload: the decode hot path over Llama-3-8B-shaped layers
+(Wqkv 6144x4096, Wo 4096x4096, Wgate|Wup fused 28672x4096, Wdown 4096x14336),
+batch 1 by default, synthetic seeded data. One step =
+  G_E of the next-token logits (128256 wide)                 (signal)
+  three layers, at levels 2, 4 and 6, each:
+    online AutoFP encode of each linear input (amax, NVFP4, 6-bit refinement)
+    AutoFP GEMV against the packed weight
+    L_A of the layer update and the device-side policy update
+Layers rotate through a pool larger than the 256 MB Infinity Cache, so the
+weights stream from HBM. Everything is captured once per pool position in a
+HIP graph and replayed.
+
+Printed (stdout, one JSON line): whole-step algorithmic HBM GB/s, the GEMV
+roofline (bytes / launch duration, HIP events around back-to-back GEMV-only
+graphs), the prefill GEMM TFLOP/s, and the CPU oracle on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP16_TFLOPS = 2500.0      # dense fp16/bf16 MFMA
+PEAK_FP4_TFLOPS = 10100.0      # dense fp4/fp6 MFMA
+LEVELS = (2, 4, 6)
+SHAPES = (("wqkv", 6144, 4096), ("wo", 4096, 4096), ("wgateup", 28672, 4096), ("wdown", 4096, 14336))
+METRIC = "AutoFP decode GEMV HBM GB/s (% peak); prefill GEMM TFLOP/s (% MFMA peak)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def w_bytes(wp, level):
+    b = wp.codes.numel() + wp.scales.numel() + 4
+    if level == 6:
+        b += wp.mask.numel() + wp.offsets.numel()
+    return b
+
+
+def x_bytes(rows, k, level):
+    b = rows * (k // 2) + rows * (k // 16) + 4
+    if level == 6:
+        b += rows * ((k + 31) // 32) + rows * (k // 4)
+    return b
+
+
+def gemv_bytes(wp, b, level):
+    """Algorithmic bytes of one GEMV: packed weight + packed activation + fp32 output."""
+    return w_bytes(wp, level) + x_bytes(b, wp.k, level) + 4 * b * wp.rows
+
+
+def encode_bytes(b, k, level):
+    """bf16 input read + packed activation written."""
+    return 2 * b * k + x_bytes(b, k, level)
+
+
+def build_pool(A, S, n_layers, device):
+    pool = []
+    for i in range(n_layers):
+        layer = {}
+        for j, (name, n, k) in enumerate(SHAPES):
+            w = S.weights(n, k, seed=100 + i, tensor_id=j, device=device)
+            layer[name] = A.quantize_weight(w, refine=True)
+            del w
+        pool.append(layer)
+        log(f"packed layer {i + 1}/{n_layers}")
+    import torch
+    torch.cuda.synchronize()
+    return pool
+
+
+class DecodeBench:
+    def __init__(self, A, S, pool, batch, device):
+        import torch
+        self.A, self.pool, self.b = A, pool, batch
+        self.p = A.default_params()
+        self.x_in = {name: S.activations(batch, k, seed=7, tensor_id=j, outlier_frac=0.0, device=device)
+                     for j, (name, n, k) in enumerate(SHAPES)}
+        self.xq = {name: A.alloc_activation(batch, k, refine=True, device=device) for name, n, k in SHAPES}
+        self.y = {name: torch.empty(batch, n, dtype=torch.float32, device=device) for name, n, k in SHAPES}
+        ks = sorted({k for _, _, k in SHAPES})
+        self.qws = {k: torch.empty(A.workspace_bytes(0, batch, k), dtype=torch.uint8, device=device) for k in ks}
+        self.gws = {k: torch.empty(A.workspace_bytes(2, batch, k), dtype=torch.uint8, device=device) for k in ks}
+        self.logits = S.logits(batch, S.VOCAB, seed=7, device=device)
+        self.h_prev = S.hidden(batch, S.HIDDEN, seed=7, tensor_id=0, device=device)
+        self.h_cur = (self.h_prev + 0.05 * S.hidden(batch, S.HIDDEN, seed=7, tensor_id=1, device=device)).contiguous()
+        self.g_e = torch.zeros(batch, dtype=torch.float32, device=device)
+        self.l_a = torch.zeros(batch, dtype=torch.float32, device=device)
+        self.state = A.policy_state(batch, device)
+        self.bits_rows = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.bits_layer = torch.zeros(1, dtype=torch.int32, device=device)
+        # activations encoded once per level for the GEMV-only timing
+        self.xq_l = {}
+        for name, n, k in SHAPES:
+            for level in LEVELS:
+                wp = pool[0][name]
+                self.xq_l[(name, level)] = A.quantize_activation(
+                    self.x_in[name], refine=(level == 6), exclude_mask=wp.mask if level == 6 else None)
+
+    def layers_of(self, s):
+        P = len(self.pool)
+        return [self.pool[(len(LEVELS) * s + j) % P] for j in range(len(LEVELS))]
+
+    def step(self, s):
+        A, p = self.A, self.p
+        A.policy_signals(logits=self.logits, out_entropy=self.g_e, params=p)
+        for j, (layer, level) in enumerate(zip(self.layers_of(s), LEVELS)):
+            for name, n, k in SHAPES:
+                wp = layer[name]
+                A.quantize_into(self.x_in[name], self.xq[name], refine=(level == 6),
+                                exclude_mask=wp.mask, workspace=self.qws[k], params=p)
+                A.gemv(wp, self.xq[name], bits=level, out=self.y[name], workspace=self.gws[k], params=p)
+            A.policy_signals(h_prev=self.h_prev, h_cur=self.h_cur, out_update=self.l_a, params=p)
+            A.policy_update(1, j, self.l_a, self.state, g_e=self.g_e, bits_rows=self.bits_rows,
+                            bits_layer=self.bits_layer, params=p)
+
+    def step_bytes(self):
+        b = self.b
+        tot = 4 * b * 128256 + 2 * 4 * b * 4096 * len(LEVELS)     # logits, h_prev/h_cur per layer
+        for layer, level in zip(self.layers_of(0), LEVELS):
+            for name, n, k in SHAPES:
+                tot += encode_bytes(b, k, level) + gemv_bytes(layer[name], b, level)
+        return tot
+
+    def gemv_only(self, s):
+        for layer, level in zip(self.layers_of(s), LEVELS):
+            for name, n, k in SHAPES:
+                self.A.gemv(layer[name], self.xq_l[(name, level)], bits=level, out=self.y[name],
+                            workspace=self.gws[k], params=self.p)
+
+    def gemv_only_bytes(self):
+        tot = 0
+        for layer, level in zip(self.layers_of(0), LEVELS):
+            for name, n, k in SHAPES:
+                tot += gemv_bytes(layer[name], self.b, level)
+        return tot
+
+
+def capture(fn_list):
+    import torch
+    graphs = []
+    for fn in fn_list:
+        fn()                                   # eager pass: code objects loaded, buffers touched
+    torch.cuda.synchronize()
+    for fn in fn_list:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_graphs(graphs, reps, warmup):
+    """Replay graphs round-robin; returns ms per replay (HIP events on the
+    replay stream, synchronized on both sides)."""
+    import torch
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(reps):
+        graphs[i % len(graphs)].replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def prefill_bench(A, S, device, reps):
+    import torch
+    out = {}
+    M = 2048
+    for name, n, k, tid in (("wup", 14336, 4096, 1), ("wdown", 4096, 14336, 3)):
+        w = S.weights(n, k, seed=200, tensor_id=tid, device=device)
+        wp = A.quantize_weight(w, refine=True)
+        del w
+        x = S.activations(M, k, seed=200, tensor_id=10 + tid, outlier_frac=0.005, outlier_scale=30.0,
+                          device=device)
+        ws = torch.empty(A.workspace_bytes(3, M, k), dtype=torch.uint8, device=device)
+        y = torch.empty(M, n, dtype=torch.bfloat16, device=device)
+        for level in (4, 6):
+            xp = A.quantize_activation(x, refine=(level == 6), exclude_mask=wp.mask if level == 6 else None)
+            fn = lambda: A.gemm(wp, xp, bits=level, out=y, workspace=ws)
+            g = capture([fn])
+            ms = time_graphs(g, reps, 2)
+            tflops = 2.0 * M * n * k / (ms * 1e-3) / 1e12
+            out[f"{name}_l{level}"] = {"ms": round(ms, 4), "tflops": round(tflops, 1)}
+        del wp, x, ws, y
+    vals = [v["tflops"] for v in out.values()]
+    best = max(vals)
+    return {"workload": "X[2048x4096] (Wup 14336x4096) and X'[2048x14336] (Wdown 4096x14336), "
+                        "bf16 out, levels 4 and 6",
+            "per_gemm": out, "tflops_mean": round(sum(vals) / len(vals), 1),
+            "frac_fp16_mfma_peak": round(best / PEAK_FP16_TFLOPS, 4),
+            "frac_fp4_mfma_peak": round(best / PEAK_FP4_TFLOPS, 4)}
+
+
+def cpu_baseline(batch, target_s=12.0):
+    """The CPU oracle (fp64 NumPy, one BLAS thread) on a bounded sample of the
+    same step: per level, encode each linear input and compute the layer
+    product on the first `rows` rows of each weight shape."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    from runtime_mixed_precision_amd import synthetic as S
+
+    rows = 512
+    with threadpool_limits(limits=1):
+        prepared = []
+        for j, (name, n, k) in enumerate(SHAPES):
+            w = S.weights(rows, k, seed=300, tensor_id=j).numpy()
+            x = S.activations(batch, k, seed=300, tensor_id=10 + j, outlier_frac=0.0).float().numpy()
+            bits, _ = O.select_weight_mask(w, 0.2)
+            wq = O.quantize_weight(w, O.pack_nibbles(bits))
+            prepared.append((w, x, wq, k))
+        done_bytes = 0
+        t0 = time.perf_counter()
+        passes = 0
+        while True:
+            for w, x, wq, k in prepared:
+                for level in LEVELS:
+                    xq = O.quantize_activation(x, refine=(level == 6),
+                                               exclude_mask=wq["mask"] if level == 6 else None)
+                    O.linear(wq, xq, level)
+                    wb = wq["codes"].size + wq["scales"].size + 4
+                    if level == 6:
+                        wb += wq["mask"].size + wq["offsets"].size
+                    done_bytes += wb + x_bytes(batch, k, level) + 4 * batch * rows + encode_bytes(batch, k, level)
+            passes += 1
+            if time.perf_counter() - t0 >= target_s:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} pass(es) x 12 GEMVs: first {rows} rows of each weight shape x levels "
+                      f"2/4/6, batch {batch}, online activation encode; {dt:.1f} s, fp64 NumPy, 1 thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--pool-layers", type=int, default=9)
+    ap.add_argument("--secondary-batch", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path, so --gpus must be 1",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.pool_layers % len(LEVELS):
+        raise SystemExit("--pool-layers must be a multiple of 3")
+
+    import torch
+
+    import runtime_mixed_precision_amd as A
+    from runtime_mixed_precision_amd import synthetic as S
+
+    device = "cuda:0"
+    A._native.lib()
+    log(f"device: {torch.cuda.get_device_name(0)}")
+    pool = build_pool(A, S, args.pool_layers, device)
+    pool_bytes = sum(w_bytes(wp, 6) for layer in pool for wp in layer.values())
+    G = args.pool_layers // len(LEVELS)
+
+    bench = DecodeBench(A, S, pool, args.batch, device)
+    graphs = capture([lambda s=s: bench.step(s) for s in range(G)])
+    ms_step = time_graphs(graphs, args.steps, args.warmup)
+    step_bytes = bench.step_bytes()
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"step: {ms_step:.4f} ms, {step_bytes / 1e6:.1f} MB, {value:.1f} GB/s")
+
+    # roofline of the GEMV kernel: GEMV-only graphs, same weights and levels
+    ggraphs = capture([lambda s=s: bench.gemv_only(s) for s in range(G)])
+    ms_g = time_graphs(ggraphs, max(args.steps, 10), args.warmup)
+    n_launch = len(LEVELS) * len(SHAPES)
+    g_bytes = bench.gemv_only_bytes()
+    achieved = g_bytes / (ms_g * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "gemv_small_kernel (batch <= 16)",
+                "avg_launch_us": round(ms_g * 1e3 / n_launch, 3),
+                "bytes_per_launch": int(g_bytes / n_launch)}
+    log(f"gemv-only: {ms_g:.4f} ms per {n_launch} launches, {achieved:.1f} GB/s")
+
+    extra = {}
+    if not args.no_breakdown:
+        br = {}
+        for name, n, k in SHAPES:
+            for level in LEVELS:
+                fns = [lambda i=i, name=name, level=level: A.gemv(
+                    pool[i][name], bench.xq_l[(name, level)], bits=level, out=bench.y[name],
+                    workspace=bench.gws[k]) for i in range(args.pool_layers)]
+                g = capture([lambda: [f() for f in fns]])
+                ms = time_graphs(g, 10, 2) / args.pool_layers
+                gb = gemv_bytes(pool[0][name], args.batch, level) / (ms * 1e-3) / 1e9
+                br[f"{name}_l{level}"] = {"us": round(ms * 1e3, 2), "gbs": round(gb, 1)}
+        extra["gemv_breakdown_b%d" % args.batch] = br
+    if args.secondary_batch and args.secondary_batch != args.batch:
+        b2 = DecodeBench(A, S, pool, args.secondary_batch, device)
+        g2 = capture([lambda s=s: b2.gemv_only(s) for s in range(G)])
+        ms2 = time_graphs(g2, max(args.steps, 10), args.warmup)
+        extra[f"gemv_b{args.secondary_batch}"] = {
+            "gbs": round(b2.gemv_only_bytes() / (ms2 * 1e-3) / 1e9, 1),
+            "avg_launch_us": round(ms2 * 1e3 / n_launch, 3)}
+        s2 = capture([lambda s=s: b2.step(s) for s in range(G)])
+        ms2s = time_graphs(s2, args.steps, args.warmup)
+        extra[f"step_b{args.secondary_batch}"] = {
+            "ms": round(ms2s, 4), "gbs": round(b2.step_bytes() / (ms2s * 1e-3) / 1e9, 1)}
+        del b2, g2, s2
+    if not args.no_prefill:
+        del graphs, ggraphs
+        extra["prefill_gemm"] = prefill_bench(A, S, device, 5)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.batch)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "AutoFP decode step over Llama-3-8B-shaped layers (Wqkv 6144x4096, Wo 4096x4096, "
+                        "Wgate|Wup 28672x4096, Wdown 4096x14336): G_E over 128256 logits, then 3 layers at "
+                        "levels 2/4/6, each with online activation encode, 4 GEMVs, L_A and the policy update",
+            "batch": args.batch,
+            "pool_layers": args.pool_layers,
+            "pool_bytes": int(pool_bytes),
+            "step_bytes": int(step_bytes),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "frac_hbm_peak": round(value / PEAK_HBM_GBS, 4),
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -57,7 +57,31 @@ typedef struct {
   float   c2;              /* 2.0   AutoFP2 scale multiple c ([AE] App. B.4, Eq. 4)          */
   int32_t top_k;           /* 10    G_E top-K; top_k >= vocab means the whole vocabulary     */
   float   eps;             /* 1e-6  L_A stability term ([AE] Eq. 1; value not in the paper)  */
+  double  tau;             /* 0.10  entropy threshold between decode regimes ([AE] §3.1)     */
+  double  lambda_d;        /* 0.7   decode metric weight M = l*L_A + (1-l)*G_E (Table 1)     */
+  int32_t alpha;           /* 4     trend lengths of Table 1 (alpha > beta)                  */
+  int32_t beta;            /* 2                                                              */
+  int32_t n_p;             /* 2     prefill trend length                                     */
+  int32_t reserved;        /* 0                                                              */
 } autofp_params;
+
+/*
+ * Device-resident state of the runtime policy for one sequence (one batch
+ * row). Zero-fill it before a sequence starts; autofp_policy_update() owns it
+ * afterwards. mean/m2/count are the running (Welford) statistics of the
+ * metric M in the current phase; up/down count consecutive layers above /
+ * below the running mean; bits is the level chosen for the next layer.
+ */
+typedef struct {
+  double  mean;
+  double  m2;
+  int32_t count;
+  int32_t up;
+  int32_t down;
+  int32_t bits;
+  int32_t spike;           /* prefill: the spike layer has been seen */
+  int32_t reserved[3];
+} autofp_policy_state;
 
 /*
  * One AutoFP tensor ([AE] §4: "E2M1 base values with E4M3 group scales, signed
@@ -205,6 +229,33 @@ autofp_status autofp_policy_signals(const float *logits, int64_t batch, int64_t 
                                     const void *h_prev, const void *h_cur, int32_t h_dtype,
                                     int64_t hidden, const autofp_params *p,
                                     float *entropy_out, float *update_out, void *stream);
+
+/*
+ * One step of the runtime precision policy after layer `layer` has run
+ * ([AE] §3.1 and Table 1), for every batch row b, on the device:
+ *   prefill (phase 0): M = L_A; layers up to and including the first spike
+ *     (M > mu + 3 sigma with at least two earlier values) run at 6 bits;
+ *     after it, n_p consecutive layers below (above) mu lower (raise) the next
+ *     layer one level of {2, 4, 6}, saturating.
+ *   decode (phase 1): M = lambda_d * L_A + (1 - lambda_d) * G_E, G_E of the
+ *     previous step (g_e[b]); layer 0 runs at 4 bits; with G_E >= tau, beta
+ *     consecutive layers above mu raise and alpha below lower the next layer;
+ *     with G_E < tau, alpha and beta swap.
+ * mu and sigma (population) are running statistics of the earlier M of the
+ * sequence in the current phase, excluding the value being judged. At
+ * layer 0 the trend counters restart and the level is reset (6 in prefill,
+ * 4 in decode); new_sequence != 0 also clears the statistics.
+ * l_a [batch] fp32 (device): L_A of this layer; g_e [batch] fp32 (device,
+ * decode only, may be NULL in prefill); state [batch] (device);
+ * bits_rows [batch] int32 (device, out): level of layer+1 per row;
+ * bits_layer [1] int32 (device, out, may be NULL): the highest level over the
+ * rows, the level at which a batched layer runs.
+ * Errors: NULL, SHAPE, ARG (phase not 0/1, layer < 0), HIP.
+ */
+autofp_status autofp_policy_update(int32_t phase, int32_t layer, int32_t new_sequence,
+                                   const float *l_a, const float *g_e, int64_t batch,
+                                   const autofp_params *p, autofp_policy_state *state,
+                                   int32_t *bits_rows, int32_t *bits_layer, void *stream);
 
 #ifdef __cplusplus
 }

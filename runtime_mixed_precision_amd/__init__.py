@@ -21,7 +21,9 @@ from ._native import AutofpError, NativeLibraryError, Params  # noqa: F401
 __all__ = [
     "AutoFPTensor", "default_params", "packed_bytes", "weight_refined_count", "workspace_bytes",
     "select_weight_mask", "quantize", "quantize_weight", "quantize_activation",
-    "gemv", "gemm", "policy_signals", "AutofpError", "NativeLibraryError",
+    "alloc_activation", "quantize_into",
+    "gemv", "gemm", "policy_signals", "policy_state", "policy_update", "AutofpError",
+    "NativeLibraryError",
 ]
 
 _DT = {torch.float32: N.F32, torch.bfloat16: N.BF16}
@@ -169,6 +171,27 @@ def quantize(x: torch.Tensor, kind: int, refine=False, exclude_mask=None, weight
     return out
 
 
+def alloc_activation(rows, k, refine=True, device="cuda:0") -> AutoFPTensor:
+    """Device buffers for a [rows x k] activation (with refinement storage)."""
+    return _alloc_packed(rows, k, N.ACTIVATION, refine, 0, device)
+
+
+def quantize_into(x: torch.Tensor, out: AutoFPTensor, refine=False, exclude_mask=None,
+                  workspace=None, params=None, stream=None) -> AutoFPTensor:
+    """autofp_quantize into preallocated buffers (no allocation; graph-safe
+    when ``workspace`` is given)."""
+    if x.dim() != 2 or x.dtype not in _DT or tuple(x.shape) != (out.rows, out.k):
+        raise ValueError("x must be 2-D float32/bfloat16 with the output's shape")
+    p = params or default_params()
+    if workspace is None:
+        workspace = _workspace(N.OP_QUANTIZE, out.rows, out.k, x.device)
+    st = out.struct()
+    N.check(N.lib().autofp_quantize(_ptr(x), _DT[x.dtype], int(bool(refine)), _ptr(exclude_mask),
+                                    C.byref(p), C.byref(st), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)), "autofp_quantize")
+    return out
+
+
 def quantize_weight(w: torch.Tensor, refine=True, params=None, stream=None) -> AutoFPTensor:
     """Offline weight packing: M_W selection (when ``refine``) and encode."""
     if refine:
@@ -212,7 +235,8 @@ def gemm(w: AutoFPTensor, x: AutoFPTensor, bits=4, bits_dev=None, out_dtype=torc
                    workspace, out, stream)
 
 
-def policy_signals(logits=None, h_prev=None, h_cur=None, params=None, stream=None):
+def policy_signals(logits=None, h_prev=None, h_cur=None, params=None, stream=None,
+                   out_entropy=None, out_update=None):
     """(G_E per row or None, L_A per row or None) via autofp_policy_signals."""
     _dev_check(logits, h_prev, h_cur)
     p = params or default_params()
@@ -223,7 +247,8 @@ def policy_signals(logits=None, h_prev=None, h_cur=None, params=None, stream=Non
         if logits.dtype != torch.float32 or logits.dim() != 2:
             raise ValueError("logits must be 2-D float32")
         batch, vocab = logits.shape
-        ent = torch.empty(batch, dtype=torch.float32, device=logits.device)
+        ent = out_entropy if out_entropy is not None else \
+            torch.empty(batch, dtype=torch.float32, device=logits.device)
     if h_prev is not None:
         if h_prev.shape != h_cur.shape or h_prev.dtype != h_cur.dtype or h_prev.dim() != 2:
             raise ValueError("h_prev and h_cur must be matching 2-D tensors")
@@ -231,8 +256,32 @@ def policy_signals(logits=None, h_prev=None, h_cur=None, params=None, stream=Non
             raise ValueError("logits and hidden states need the same batch")
         batch, hidden = h_prev.shape
         hdt = _DT[h_prev.dtype]
-        upd = torch.empty(batch, dtype=torch.float32, device=h_prev.device)
+        upd = out_update if out_update is not None else \
+            torch.empty(batch, dtype=torch.float32, device=h_prev.device)
     N.check(N.lib().autofp_policy_signals(_ptr(logits), batch, vocab, _ptr(h_prev), _ptr(h_cur), hdt,
                                           hidden, C.byref(p), _ptr(ent), _ptr(upd), _stream(stream)),
             "autofp_policy_signals")
     return ent, upd
+
+
+def policy_state(batch, device="cuda:0") -> torch.Tensor:
+    """Zero-filled device state for ``batch`` sequences (autofp_policy_state)."""
+    return torch.zeros(batch, N.POLICY_STATE_BYTES, dtype=torch.uint8, device=device)
+
+
+def policy_update(phase, layer, l_a, state, g_e=None, new_sequence=False, bits_rows=None,
+                  bits_layer=None, params=None, stream=None):
+    """One device-side policy step after ``layer`` (autofp_policy_update).
+    phase 0 = prefill, 1 = decode. Returns (bits_rows [batch] int32,
+    bits_layer [1] int32), the levels of the next layer."""
+    _dev_check(l_a, g_e, state)
+    batch = l_a.shape[0]
+    if bits_rows is None:
+        bits_rows = torch.empty(batch, dtype=torch.int32, device=l_a.device)
+    if bits_layer is None:
+        bits_layer = torch.empty(1, dtype=torch.int32, device=l_a.device)
+    p = params or default_params()
+    N.check(N.lib().autofp_policy_update(int(phase), int(layer), int(bool(new_sequence)), _ptr(l_a),
+                                         _ptr(g_e), batch, C.byref(p), _ptr(state), _ptr(bits_rows),
+                                         _ptr(bits_layer), _stream(stream)), "autofp_policy_update")
+    return bits_rows, bits_layer

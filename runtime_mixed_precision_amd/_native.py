@@ -27,6 +27,7 @@ EXPORTS = (
     "autofp_default_params", "autofp_status_string", "autofp_packed_bytes",
     "autofp_weight_refined_count", "autofp_workspace_bytes", "autofp_select_weight_mask",
     "autofp_quantize", "autofp_gemv", "autofp_gemm", "autofp_policy_signals",
+    "autofp_policy_update",
 )
 
 
@@ -42,7 +43,18 @@ class AutofpError(RuntimeError):
 
 class Params(C.Structure):
     _fields_ = [("rho", C.c_double), ("act_nmse_thresh", C.c_float), ("c2", C.c_float),
-                ("top_k", C.c_int32), ("eps", C.c_float)]
+                ("top_k", C.c_int32), ("eps", C.c_float), ("tau", C.c_double),
+                ("lambda_d", C.c_double), ("alpha", C.c_int32), ("beta", C.c_int32),
+                ("n_p", C.c_int32), ("reserved", C.c_int32)]
+
+
+class PolicyState(C.Structure):
+    _fields_ = [("mean", C.c_double), ("m2", C.c_double), ("count", C.c_int32), ("up", C.c_int32),
+                ("down", C.c_int32), ("bits", C.c_int32), ("spike", C.c_int32),
+                ("reserved", C.c_int32 * 3)]
+
+
+POLICY_STATE_BYTES = 48
 
 
 class Packed(C.Structure):
@@ -85,6 +97,8 @@ def lib():
                                   C.c_size_t, vp]),
         "autofp_policy_signals": (C.c_int, [vp, C.c_int64, C.c_int64, vp, vp, C.c_int32, C.c_int64,
                                             P(Params), vp, vp, vp]),
+        "autofp_policy_update": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, vp, vp, C.c_int64,
+                                           P(Params), vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)

@@ -80,6 +80,7 @@ struct LinearArgs {
 };
 int64_t xh_kpad(int64_t k);
 hipError_t launch_act_dequant(const LinearArgs &a, hipStream_t s);
+bool gemv_needs_panel(int64_t tokens);   // true when the GEMV reads the fp16 activation panel
 hipError_t launch_gemv(const LinearArgs &a, hipStream_t s);
 
 // ---- gemm.hip ----
@@ -88,6 +89,16 @@ hipError_t launch_gemm(const LinearArgs &a, hipStream_t s);
 // ---- signals.hip ----
 hipError_t launch_entropy(const float *logits, int64_t batch, int64_t vocab, int top_k,
                           float *out, hipStream_t s);
+struct PolicyArgs {
+  int phase, layer, new_sequence;
+  const float *l_a, *g_e;
+  int64_t batch;
+  double tau, lambda_d;
+  int alpha, beta, n_p;
+  autofp_policy_state *state;
+  int32_t *bits_rows, *bits_layer;
+};
+hipError_t launch_policy_update(const PolicyArgs &a, hipStream_t s);
 hipError_t launch_update_norm(const void *h_prev, const void *h_cur, int dtype, int64_t batch,
                               int64_t hidden, float eps, float *out, hipStream_t s);
 

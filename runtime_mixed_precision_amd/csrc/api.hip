@@ -8,6 +8,9 @@
 
 using namespace afp;
 
+static_assert(sizeof(autofp_policy_state) == 48, "policy state layout");
+static_assert(sizeof(autofp_params) == 56, "params layout");
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -122,6 +125,12 @@ autofp_status autofp_default_params(autofp_params *p) {
   p->c2 = 2.0f;
   p->top_k = 10;
   p->eps = 1e-6f;
+  p->tau = 0.10;
+  p->lambda_d = 0.7;
+  p->alpha = 4;
+  p->beta = 2;
+  p->n_p = 2;
+  p->reserved = 0;
   return AUTOFP_OK;
 }
 
@@ -277,8 +286,10 @@ autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_
       linear_common(w, x, bits, bits_dev, y, y_dtype, p, workspace, workspace_bytes, a);
   if (st != AUTOFP_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_act_dequant(a, s);
-  if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  if (gemv_needs_panel(a.b)) {
+    const hipError_t e = launch_act_dequant(a, s);
+    if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  }
   return from_hip(launch_gemv(a, s));
 }
 
@@ -329,6 +340,36 @@ autofp_status autofp_policy_signals(const float *logits, int64_t batch, int64_t 
     if (e != hipSuccess) return AUTOFP_ERR_HIP;
   }
   return AUTOFP_OK;
+}
+
+autofp_status autofp_policy_update(int32_t phase, int32_t layer, int32_t new_sequence,
+                                   const float *l_a, const float *g_e, int64_t batch,
+                                   const autofp_params *p, autofp_policy_state *state,
+                                   int32_t *bits_rows, int32_t *bits_layer, void *stream) {
+  const autofp_params pp = params_or_default(p);
+  if (!l_a || !state || !bits_rows) return AUTOFP_ERR_NULL;
+  if (phase != 0 && phase != 1) return AUTOFP_ERR_ARG;
+  if (phase == 1 && !g_e) return AUTOFP_ERR_NULL;
+  if (batch < 1) return AUTOFP_ERR_SHAPE;
+  if (layer < 0 || pp.alpha < 1 || pp.beta < 1 || pp.n_p < 1 ||
+      !(pp.lambda_d >= 0.0 && pp.lambda_d <= 1.0))
+    return AUTOFP_ERR_ARG;
+  PolicyArgs a{};
+  a.phase = phase;
+  a.layer = layer;
+  a.new_sequence = new_sequence;
+  a.l_a = l_a;
+  a.g_e = g_e;
+  a.batch = batch;
+  a.tau = pp.tau;
+  a.lambda_d = pp.lambda_d;
+  a.alpha = pp.alpha;
+  a.beta = pp.beta;
+  a.n_p = pp.n_p;
+  a.state = state;
+  a.bits_rows = bits_rows;
+  a.bits_layer = bits_layer;
+  return from_hip(launch_policy_update(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -189,7 +189,105 @@ __global__ __launch_bounds__(256) void update_norm_kernel(const void *__restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// Runtime precision policy ([AE] §3.1, Table 1), one thread per sequence.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void trend(autofp_policy_state &s, double m) {
+  if (m > s.mean) {
+    s.up += 1;
+    s.down = 0;
+  } else if (m < s.mean) {
+    s.down += 1;
+    s.up = 0;
+  } else {
+    s.up = 0;
+    s.down = 0;
+  }
+}
+
+__global__ __launch_bounds__(256) void policy_update_kernel(PolicyArgs a) {
+#pragma clang fp contract(off)
+  int mx = 0;
+  for (int64_t b = threadIdx.x; b < a.batch; b += 256) {
+    autofp_policy_state s = a.state[b];
+    if (a.layer == 0) {
+      if (a.new_sequence) {
+        s.mean = 0.0;
+        s.m2 = 0.0;
+        s.count = 0;
+      }
+      s.up = 0;
+      s.down = 0;
+      s.spike = 0;
+      s.bits = a.phase == 0 ? 6 : 4;
+    }
+    const double la = (double)a.l_a[b];
+    int p = s.bits;
+    double m;
+    if (a.phase == 0) {
+      m = la;
+      if (!s.spike) {
+        if (s.count >= 2 && m > s.mean + 3.0 * sqrt(s.m2 / (double)s.count)) s.spike = 1;
+      } else {
+        trend(s, m);
+        if (s.up >= a.n_p) {
+          p = p + 2 > 6 ? 6 : p + 2;
+          s.up = 0;
+        } else if (s.down >= a.n_p) {
+          p = p - 2 < 2 ? 2 : p - 2;
+          s.down = 0;
+        }
+      }
+    } else {
+      const double g = (double)a.g_e[b];
+      m = a.lambda_d * la + (1.0 - a.lambda_d) * g;
+      const bool high = g >= a.tau;
+      const int n_up = high ? a.beta : a.alpha;
+      const int n_down = high ? a.alpha : a.beta;
+      if (s.count) {
+        trend(s, m);
+        if (s.up >= n_up) {
+          p = p + 2 > 6 ? 6 : p + 2;
+          s.up = 0;
+        } else if (s.down >= n_down) {
+          p = p - 2 < 2 ? 2 : p - 2;
+          s.down = 0;
+        }
+      }
+    }
+    s.count += 1;
+    const double delta = m - s.mean;
+    s.mean += delta / (double)s.count;
+    s.m2 += delta * (m - s.mean);
+    s.bits = p;
+    a.state[b] = s;
+    a.bits_rows[b] = p;
+    mx = p > mx ? p : mx;
+  }
+  if (a.bits_layer) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const int v = __shfl_xor(mx, o, 64);
+      mx = v > mx ? v : mx;
+    }
+    __shared__ int red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int r = red[0];
+      for (int w = 1; w < 4; ++w) r = red[w] > r ? red[w] : r;
+      *a.bits_layer = r;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_policy_update(const PolicyArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(policy_update_kernel, dim3(1), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_entropy(const float *logits, int64_t batch, int64_t vocab, int top_k, float *out,
                           hipStream_t s) {

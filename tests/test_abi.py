@@ -56,6 +56,9 @@ def test_default_params_are_the_papers(N):
     p = params(N)
     assert p.rho == pytest.approx(0.2) and p.act_nmse_thresh == pytest.approx(0.003)
     assert p.c2 == 2.0 and p.top_k == 10
+    assert p.tau == pytest.approx(0.10) and p.lambda_d == pytest.approx(0.7)
+    assert (p.alpha, p.beta, p.n_p) == (4, 2, 2)
+    assert C.sizeof(N.Params) == 56 and C.sizeof(N.PolicyState) == N.POLICY_STATE_BYTES
     assert N.lib().autofp_default_params(None) == 1
 
 
@@ -144,3 +147,17 @@ def test_signals_reject_bad_arguments(N):
     p.top_k = 10
     assert sig(None, 1, 0, FAKE, FAKE, 3, 64, C.byref(p), None, FAKE) == 7
     assert sig(None, 0, 0, FAKE, FAKE, N.F32, 64, C.byref(p), None, FAKE) == 2
+
+
+def test_policy_update_rejects_bad_arguments(N):
+    L = N.lib()
+    p = params(N)
+    up = lambda phase, layer, la, ge, batch, st, br: L.autofp_policy_update(
+        phase, layer, 0, la, ge, batch, C.byref(p), st, br, None, None)
+    assert up(0, 0, None, None, 1, FAKE, FAKE) == 1
+    assert up(1, 0, FAKE, None, 1, FAKE, FAKE) == 1        # decode needs G_E
+    assert up(2, 0, FAKE, FAKE, 1, FAKE, FAKE) == 8
+    assert up(0, -1, FAKE, FAKE, 1, FAKE, FAKE) == 8
+    assert up(0, 0, FAKE, FAKE, 0, FAKE, FAKE) == 2
+    p.alpha = 0
+    assert up(1, 0, FAKE, FAKE, 1, FAKE, FAKE) == 8
