@@ -62,7 +62,8 @@ typedef struct {
   int32_t alpha;           /* 4     trend lengths of Table 1 (alpha > beta)                  */
   int32_t beta;            /* 2                                                              */
   int32_t n_p;             /* 2     prefill trend length                                     */
-  int32_t reserved;        /* 0                                                              */
+  int32_t gemv_waves;      /* 0     autofp_gemv wavefronts per 16-row tile: 0 = automatic,   */
+                           /*       or 1, 2, 4, 8, 16 to force it (tuning and tests)         */
 } autofp_params;
 
 /*

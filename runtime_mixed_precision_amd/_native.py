@@ -45,7 +45,7 @@ class Params(C.Structure):
     _fields_ = [("rho", C.c_double), ("act_nmse_thresh", C.c_float), ("c2", C.c_float),
                 ("top_k", C.c_int32), ("eps", C.c_float), ("tau", C.c_double),
                 ("lambda_d", C.c_double), ("alpha", C.c_int32), ("beta", C.c_int32),
-                ("n_p", C.c_int32), ("reserved", C.c_int32)]
+                ("n_p", C.c_int32), ("gemv_waves", C.c_int32)]
 
 
 class PolicyState(C.Structure):

@@ -70,6 +70,7 @@ struct LinearArgs {
   int32_t bits;
   const int32_t *bits_dev;
   float c2;
+  int32_t waves;                // GEMV wavefronts per tile (0 = automatic)
   // output
   void *y;
   int y_dtype;
@@ -80,7 +81,7 @@ struct LinearArgs {
 };
 int64_t xh_kpad(int64_t k);
 hipError_t launch_act_dequant(const LinearArgs &a, hipStream_t s);
-bool gemv_needs_panel(int64_t tokens);   // true when the GEMV reads the fp16 activation panel
+bool gemv_needs_panel(const LinearArgs &a);   // true when the GEMV reads the fp16 activation panel
 hipError_t launch_gemv(const LinearArgs &a, hipStream_t s);
 
 // ---- gemm.hip ----

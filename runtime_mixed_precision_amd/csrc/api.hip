@@ -86,6 +86,9 @@ autofp_status linear_common(const autofp_packed *w, const autofp_packed *x, int3
   if (y_dtype != AUTOFP_F32 && y_dtype != AUTOFP_BF16) return AUTOFP_ERR_DTYPE;
   if (!bits_dev && bits != 2 && bits != 4 && bits != 6) return AUTOFP_ERR_BITS;
   if ((bits_dev || bits == 6) && !has_refinement(w, x)) return AUTOFP_ERR_MISSING_REFINEMENT;
+  if (p && p->gemv_waves != 0 && p->gemv_waves != 1 && p->gemv_waves != 2 && p->gemv_waves != 4 &&
+      p->gemv_waves != 8 && p->gemv_waves != 16)
+    return AUTOFP_ERR_ARG;
   const size_t need = ws_linear(x->rows, x->k);
   if (!ws || ws_bytes < need) return AUTOFP_ERR_WORKSPACE;
   if (!aligned16(ws)) return AUTOFP_ERR_ARG;
@@ -106,6 +109,7 @@ autofp_status linear_common(const autofp_packed *w, const autofp_packed *x, int3
   a.bits = bits;
   a.bits_dev = bits_dev;
   a.c2 = pp.c2;
+  a.waves = pp.gemv_waves;
   a.y = y;
   a.y_dtype = y_dtype;
   a.kpad = xh_kpad(x->k);
@@ -130,7 +134,7 @@ autofp_status autofp_default_params(autofp_params *p) {
   p->alpha = 4;
   p->beta = 2;
   p->n_p = 2;
-  p->reserved = 0;
+  p->gemv_waves = 0;
   return AUTOFP_OK;
 }
 
@@ -286,7 +290,7 @@ autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_
       linear_common(w, x, bits, bits_dev, y, y_dtype, p, workspace, workspace_bytes, a);
   if (st != AUTOFP_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (gemv_needs_panel(a.b)) {
+  if (gemv_needs_panel(a)) {
     const hipError_t e = launch_act_dequant(a, s);
     if (e != hipSuccess) return AUTOFP_ERR_HIP;
   }

@@ -191,3 +191,50 @@ def test_prefill_sampled_full_size():
         xq = O.quantize_activation(xn[toks], refine=(level == 6), exclude_mask=wq["mask"], tensor_amax=xa)
         y = A.gemm(wp, xp, bits=level).cpu().numpy()
         check_close(y[np.ix_(toks, rows)], O.linear(wq, xq, level))
+
+
+def _all_scale_codes_weight(n, k, seed):
+    """Weights whose 16-element groups span the whole E4M3 scale range: each
+    group's absolute maximum is 2^u with u uniform in [-17, 0] (one element set
+    to +-that value, one row holding 1.0), so B = E4M3(448 * amax_j / amax)
+    takes codes from the subnormal range up to 448."""
+    rng = np.random.default_rng(seed)
+    g = k // 16
+    amax_g = np.exp2(rng.uniform(-17.0, 0.0, (n, g)))
+    amax_g[0, 0] = 1.0
+    w = rng.uniform(-1.0, 1.0, (n, g, 16)) * amax_g[:, :, None]
+    w[:, :, 0] = np.where(rng.random((n, g)) < 0.5, -1.0, 1.0) * amax_g
+    return w.reshape(n, k).astype(np.float32)
+
+
+@pytest.mark.parametrize("level", [2, 4, 6])
+@pytest.mark.parametrize("b", [1, 5])
+def test_gemv_all_scale_codes(level, b):
+    """Every E4M3 group-scale code range (subnormal to 448) through the GEMV's
+    scale conversion."""
+    say(f"case: gemv all scale codes level {level} B={b}")
+    n, k = 48, 19 * 16 * 8
+    wn = _all_scale_codes_weight(n, k, seed=11)
+    w = torch.from_numpy(wn).to(DEV)
+    x = S.activations(b, k, seed=12, tensor_id=0, device=DEV)
+    wp, xp4, xp6 = gpu_pack(w, x)
+    codes = set(np.unique(wp.scales.cpu().numpy()).tolist())
+    assert len(codes) >= 100, len(codes)
+    wq, xq4, xq6 = oracle_pack(w, x)
+    y = run(A.gemv, wp, xp4, xp6, level)
+    check_close(y.cpu().numpy(), O.linear(wq, xq6 if level == 6 else xq4, level))
+
+
+@pytest.mark.parametrize("waves", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("n,b,k", [(40, 1, 4096 + 256), (33, 3, 2304 + 64), (16, 16, 1040)])
+def test_gemv_forced_waves(waves, n, b, k):
+    """The GEMV at every wavefront count; with one wavefront per tile and
+    K = 4352 a wavefront walks 17 chunks (two rounds of its offset plan)."""
+    say(f"case: gemv waves={waves} N={n} B={b} K={k}")
+    w, x = operands(n, b, k, seed=waves * 31 + n)
+    wp, xp4, xp6 = gpu_pack(w, x)
+    wq, xq4, xq6 = oracle_pack(w, x)
+    p = A.default_params(gemv_waves=waves)
+    for level in (2, 4, 6):
+        y = run(A.gemv, wp, xp4, xp6, level, params=p)
+        check_close(y.cpu().numpy(), O.linear(wq, xq6 if level == 6 else xq4, level))
