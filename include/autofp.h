@@ -63,7 +63,8 @@ typedef struct {
   int32_t beta;            /* 2                                                              */
   int32_t n_p;             /* 2     prefill trend length                                     */
   int32_t gemv_waves;      /* 0     autofp_gemv wavefronts per 16-row tile: 0 = automatic,   */
-                           /*       or 1, 2, 4, 8, 16 to force it (tuning and tests)         */
+                           /*       or 1, 2, 4, 8, 16 to request it (tuning and tests); the  */
+                           /*       kernel raises it to ceil(k / 4096) when that is larger   */
 } autofp_params;
 
 /*
@@ -98,7 +99,10 @@ typedef struct {
  *               Group 2g is the low nibble; bit s of a nibble = subgroup s.
  *               NULL when the tensor carries no 6-bit refinement.
  *  offsets      WEIGHT:     [rows][n_refined]   one byte per refined subgroup, in
- *                                               ascending (group, subgroup) order;
+ *                                               ascending (group, subgroup) order,
+ *                                               followed by 16 bytes of padding that
+ *                                               autofp_gemv may read (any content,
+ *                                               never written);
  *               ACTIVATION: [rows][k/4]         one byte per subgroup (0 where the
  *                                               subgroup is not refined).
  *               Byte = four 2-bit two's-complement d, element e of the subgroup
@@ -133,7 +137,8 @@ autofp_status autofp_default_params(autofp_params *p);
 const char *autofp_status_string(autofp_status s);
 
 /* Bytes of each buffer of one packed tensor, written to out_bytes (host):
- * [0] codes, [1] scales, [2] tensor_scale, [3] mask, [4] offsets.
+ * [0] codes, [1] scales, [2] tensor_scale, [3] mask, [4] offsets (for a
+ * WEIGHT: rows * n_refined + 16, the padding included).
  * refine = 0 gives 0 for mask and offsets. For WEIGHT, n_refined is the value
  * autofp_weight_refined_count() returns. Errors: NULL, SHAPE, KIND, ARG. */
 autofp_status autofp_packed_bytes(int64_t rows, int64_t k, int32_t kind, int32_t refine,
@@ -198,7 +203,8 @@ autofp_status autofp_quantize(const void *x, int32_t x_dtype, int32_t refine,
  * If bits_dev != NULL the level is read on the device when the kernels run
  * (graph-capturable, no host read); `bits` is then ignored but a level-6 call
  * must be allowed by the operands (both carry refinement).
- * Best for x->rows <= 64; larger batches run in slices of 64 tokens.
+ * Best for x->rows <= 64; larger batches run in slices of 64 tokens. With at
+ * most 16 tokens, a level-6 call (or one with bits_dev) needs k <= 65536.
  * Errors: NULL, SHAPE, KIND, BITS, MISSING_REFINEMENT, DTYPE, WORKSPACE, HIP.
  */
 autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_t bits,

@@ -126,9 +126,11 @@ def _alloc_packed(rows, k, kind, refine, n_refined, device):
     ts = torch.empty(1, dtype=torch.float32, device=device)
     if kind == N.WEIGHT:
         mask = buf(nb[3], (mb,))
-        offs = buf(nb[4], (rows, n_refined))
-        if refine and n_refined == 0:
-            offs = torch.zeros(rows, 1, dtype=torch.uint8, device=device)
+        offs = None
+        if refine:
+            # rows x n_refined bytes plus the padding the GEMV may read past the end
+            flat = torch.zeros(max(nb[4], rows * n_refined + 16), dtype=torch.uint8, device=device)
+            offs = flat[: rows * n_refined].view(rows, n_refined)
     else:
         mask = buf(nb[3], (rows, mb))
         offs = buf(nb[4], (rows, k // 4))

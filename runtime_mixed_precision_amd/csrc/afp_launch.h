@@ -70,7 +70,8 @@ struct LinearArgs {
   int32_t bits;
   const int32_t *bits_dev;
   float c2;
-  int32_t waves;                // GEMV wavefronts per tile (0 = automatic)
+  int32_t waves;                // GEMV wavefronts per tile requested (0 = automatic)
+  int32_t wk;                   // GEMV wavefronts per tile chosen at launch
   // output
   void *y;
   int y_dtype;

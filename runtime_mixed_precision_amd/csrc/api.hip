@@ -14,6 +14,8 @@ static_assert(sizeof(autofp_params) == 56, "params layout");
 namespace {
 
 constexpr size_t kAlign = 256;
+// bytes past the last row of a weight's offsets that the GEMV may read (never writes)
+constexpr size_t kOffsetPad = 16;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -168,7 +170,7 @@ autofp_status autofp_packed_bytes(int64_t rows, int64_t k, int32_t kind, int32_t
   if (refine) {
     if (kind == AUTOFP_WEIGHT) {
       out_bytes[3] = (size_t)mask_bytes(k);
-      out_bytes[4] = (size_t)rows * (size_t)n_refined;
+      out_bytes[4] = (size_t)rows * (size_t)n_refined + kOffsetPad;
     } else {
       out_bytes[3] = (size_t)(rows * mask_bytes(k));
       out_bytes[4] = (size_t)(rows * (k / 4));
@@ -289,6 +291,7 @@ autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_
   const autofp_status st =
       linear_common(w, x, bits, bits_dev, y, y_dtype, p, workspace, workspace_bytes, a);
   if (st != AUTOFP_OK) return st;
+  if ((bits_dev || bits == 6) && x->rows <= 16 && x->k > 65536) return AUTOFP_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   if (gemv_needs_panel(a)) {
     const hipError_t e = launch_act_dequant(a, s);

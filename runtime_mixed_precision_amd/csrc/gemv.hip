@@ -41,11 +41,13 @@ namespace afp {
 
 namespace {
 
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
 constexpr int kCh = 256;         // K elements per chunk
 constexpr int kInflight = 4;     // chunks of weight loads in flight per wavefront
 constexpr int kMaxWaves = 16;    // wavefronts per block (1024 threads)
-constexpr int kPlanChunks = 16;  // chunks per wavefront covered by one offset plan
-static_assert(kPlanChunks % kInflight == 0, "plan rounds must start at a load group");
+constexpr int kPlanChunks = 16;  // chunks per wavefront covered by its offset plan
 
 __device__ __forceinline__ int run_level(const LinearArgs &a) {
   return a.bits_dev ? *a.bits_dev : a.bits;
@@ -72,24 +74,6 @@ __device__ __forceinline__ uint32_t as_u(half2v h) { return __builtin_bit_cast(u
 __device__ __forceinline__ uint32_t autofp2_remap(uint32_t w) {
   const uint32_t t = (((w & 0x77777777u) + 0x22222222u) >> 1) & 0x66666666u;
   return t | (w & 0x88888888u);
-}
-
-// 8 mask bytes of chunk c (64 subgroups); bytes past the mask are zero.
-__device__ __forceinline__ uint64_t chunk_mask(const uint8_t *mask, int64_t mbytes, int64_t c) {
-  const int64_t b0 = 8 * c;
-  if (b0 + 8 <= mbytes) return *(const uint64_t *)(mask + b0);
-  uint64_t m = 0;
-  for (int i = 0; i < 8; ++i)
-    if (b0 + i < mbytes) m |= (uint64_t)mask[b0 + i] << (8 * i);
-  return m;
-}
-
-__device__ __forceinline__ uint32_t load_dword_guarded(const uint8_t *base, int64_t at, int64_t total) {
-  if (at + 4 <= total) return *(const uint32_t *)(base + at);
-  uint32_t v = 0;
-  for (int i = 0; i < 4; ++i)
-    if (at + i < total) v |= (uint32_t)base[at + i] << (8 * i);
-  return v;
 }
 
 // Per-lane plan entry of one (chunk, lane group): byte selectors (one per
@@ -126,40 +110,6 @@ struct WChunk {
   uint32_t s;       // 4 E4M3 group scales
   uint32_t o[3];    // offset dwords covering the lane's offset window
 };
-
-// Weight codes and scales of one lane for chunk c (elements e0 .. e0+63).
-template <bool FAST>
-__device__ __forceinline__ void load_codes(const uint8_t *crow, const uint8_t *srow, int64_t K, int64_t e0,
-                                           bool live, WChunk &w) {
-  if (FAST) {
-    if (live && e0 < K) {   // K % 64 == 0: the lane's 64 elements are all in range
-      const uint4 a = *(const uint4 *)(crow + (e0 >> 1));
-      const uint4 b = *(const uint4 *)(crow + (e0 >> 1) + 16);
-      w.c[0] = a.x; w.c[1] = a.y; w.c[2] = a.z; w.c[3] = a.w;
-      w.c[4] = b.x; w.c[5] = b.y; w.c[6] = b.z; w.c[7] = b.w;
-      w.s = *(const uint32_t *)(srow + (e0 >> 4));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w.c[i] = 0;
-      w.s = 0;
-    }
-  } else {
-    w.s = 0;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int64_t e = e0 + 16 * g;
-      if (live && e < K) {
-        const uint2 v = *(const uint2 *)(crow + (e >> 1));
-        w.c[2 * g] = v.x;
-        w.c[2 * g + 1] = v.y;
-        w.s |= (uint32_t)srow[e >> 4] << (8 * g);
-      } else {
-        w.c[2 * g] = 0;
-        w.c[2 * g + 1] = 0;
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Activation decode: fp16 B_A * (q + delta_A) of 8 consecutive elements
@@ -201,63 +151,185 @@ __global__ __launch_bounds__(256) void act_dequant_kernel(LinearArgs a) {
 // Streaming GEMV, up to 16 tokens per launch
 // ---------------------------------------------------------------------------
 //
-// Dynamic LDS layout: [delta table 256 x 8 B][activations B x kp fp16 (XLDS)
-// or nothing], the reduction buffer W x 64 x 16 B aliasing the activations
-// after the main loop.
-template <bool XLDS, bool FAST>
-__global__ __launch_bounds__(1024) void gemv_stream_kernel(LinearArgs a) {
-  extern __shared__ __align__(16) unsigned char lds[];
-  uint2 *lut = (uint2 *)lds;
-  _Float16 *xs = (_Float16 *)(lds + 256 * sizeof(uint2));
-  float4v *red = (float4v *)(lds + 256 * sizeof(uint2));
+// Dynamic LDS layout: [delta table 256 x 8 B][XLDS: activations B x kp fp16,
+// then a 128-byte zero row read by the lanes of absent tokens]; the
+// reduction buffer W x 64 x 16 B reuses the space after the main loop.
+//
+// Every global read goes through a buffer resource covering the block's rows,
+// so rows past the end of the weight and chunks past a wavefront's range read
+// as zero (an out-of-range offset) instead of branching: each chunk issues the
+// same loads, which lets the compiler keep kInflight chunks in flight.
 
+constexpr uint32_t kOOB = 0x80000000u;   // buffer offset that is always out of range
+constexpr int64_t kLutBytes = 256 * 8;   // delta table
+
+// LDS bytes of the weight-mask copy (zero-padded so 8-byte chunk reads stay inside)
+__host__ __device__ __forceinline__ int64_t mask_lds_bytes(int64_t k) {
+  return ((((k + 31) >> 5) + 15) / 16) * 16 + 16;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                           (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF), 0x00020000);
+}
+
+__device__ __forceinline__ uint4 ld_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t ld_b32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
+// Scheduling fence that keeps vector-memory instructions in program order
+// while letting ALU, MFMA and LDS work move across it.
+__device__ __forceinline__ void vmem_fence() { __builtin_amdgcn_sched_barrier(0x78F); }
+
+// One block: RT row tiles of 16 rows x WK wavefronts per tile (RT * WK
+// wavefronts, blockDim = 64 * RT * WK). Wavefront w works on tile w / WK and
+// on the (w % WK)-th contiguous range of 256-element chunks of K.
+template <int L, bool XLDS, bool FAST>
+__device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *lds) {
+  constexpr bool REF = (L == 6);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
+  const int WK = a.wk;
+  const int tile = wave / WK;
+  const int kw = wave - tile * WK;
   const int r = lane & 15;
   const int ks = lane >> 4;
   const int64_t K = a.k;
   const int64_t nch = (K + kCh - 1) / kCh;
   const int64_t kp = nch * kCh;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int L = run_level(a);
-  const bool refine_w = (L == 6) && a.w_mask != nullptr && a.n_refined > 0 && a.w_offsets != nullptr;
-  const bool refine_x = (L == 6) && a.x_offsets != nullptr;
-
-  const int64_t row = n0 + r;
-  const bool row_ok = row < a.n;
-  const uint8_t *crow = a.w_codes + (row_ok ? row : 0) * (K >> 1);
-  const uint8_t *srow = a.w_scales + (row_ok ? row : 0) * (K >> 4);
-  const int64_t obase = (row_ok ? row : 0) * (int64_t)a.n_refined;
-  const int64_t ototal = a.n * (int64_t)a.n_refined;
+  const int64_t n0 = ((int64_t)blockIdx.x * (nw / WK) + tile) * 16;
+  int64_t rows = a.n - n0;
+  rows = rows < 0 ? 0 : rows > 16 ? 16 : rows;
+  const int64_t R = a.n_refined;
+  const bool refine_w = REF && a.w_mask != nullptr && R > 0 && a.w_offsets != nullptr;
+  const bool refine_x = REF && a.x_offsets != nullptr;
+  const bool tok_ok = r < a.b;
   const int64_t mbytes = (K + 31) >> 5;
 
-  const int64_t c0 = (nch * wave) / nw;
-  const int64_t c1 = (nch * (wave + 1)) / nw;
+  uint2 *lut = (uint2 *)lds;
+  uint8_t *mlds = lds + kLutBytes;
+  _Float16 *xs = (_Float16 *)(lds + kLutBytes + mask_lds_bytes(K));
+  float4v *red = (float4v *)(lds + kLutBytes);
 
-  // 1. first weight loads
+  const int64_t nb0 = rows > 0 ? n0 : 0;   // keep resource bases inside the tensors
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.w_codes + nb0 * (K >> 1), rows * (K >> 1));
+  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(a.w_scales + nb0 * (K >> 4), rows * (K >> 4));
+  // weight offsets: the tile's rows plus the 16 padding bytes every offsets buffer carries
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc(refine_w ? a.w_offsets + nb0 * R : a.w_codes, rows > 0 ? rows * R + 16 : 0);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xh, XLDS ? 0 : a.b * a.kpad * 2);
+  const uint32_t crow = (uint32_t)(r * (K >> 1) + 32 * ks);    // + 128 bytes per chunk
+  const uint32_t srow = (uint32_t)(r * (K >> 4) + 4 * ks);     // + 16 bytes per chunk
+  const uint32_t orow = (uint32_t)(r * R);
+
+  const int64_t c0 = (nch * kw) / WK;
+  const int64_t c1 = (nch * (kw + 1)) / WK;
+
+  // Weight codes and scales of chunk c. A buffer load whose range is not
+  // wholly inside the resource reads as zero; chunks past the wavefront's
+  // range use an out-of-range scalar offset. With K % 256 == 0 (FAST) every
+  // lane's 64 elements lie inside K; otherwise each 16-element group is
+  // loaded on its own.
+  auto load_codes = [&](int64_t c, WChunk &w) {
+    if (FAST) {
+      // the chunk offset goes in the scalar offset; a chunk past the range
+      // moves the lane offset out of range (the range check is made on the
+      // lane offset)
+      const bool live = c < c1;
+      const uint32_t so = live ? (uint32_t)(c * 128) : 0u;
+      const uint32_t vo = live ? crow : kOOB;
+      const u32x4v lo = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)vo, (int)so, 0);
+      const u32x4v hi = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(vo + 16), (int)so, 0);
+      w.c[0] = lo[0]; w.c[1] = lo[1]; w.c[2] = lo[2]; w.c[3] = lo[3];
+      w.c[4] = hi[0]; w.c[5] = hi[1]; w.c[6] = hi[2]; w.c[7] = hi[3];
+      w.s = 0;   // scales come per load group (load_scales)
+    } else {
+      const int64_t e0 = c * kCh + 64 * ks;
+      w.s = 0;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t e = e0 + 16 * g;
+        const bool live = c < c1 && e < K;
+        const uint32_t oc = live ? (uint32_t)(r * (K >> 1) + (e >> 1)) : kOOB;
+        const u32x2v v = __builtin_amdgcn_raw_buffer_load_b64(rc, (int)oc, 0, 0);
+        w.c[2 * g] = v[0];
+        w.c[2 * g + 1] = v[1];
+        const uint32_t os = live ? (uint32_t)(r * (K >> 4) + (e >> 4)) : kOOB;
+        w.s |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsc, (int)os, 0, 0) << (8 * g);
+      }
+    }
+    w.o[0] = w.o[1] = w.o[2] = 0;
+  };
+
+  // Group scales (FAST): lane (r, j) loads the 16 scale bytes of row r in
+  // chunk g + j - one 16-byte load per lane for a whole load group, so each
+  // row's scales arrive as 64 contiguous bytes - and a 4 x 4 transpose across
+  // the lane groups (v_permlane32_swap, v_permlane16_swap) leaves in register
+  // u of lane (r, ks) the 4 scale bytes of its groups in chunk g + u.
+  static_assert(kInflight == 4, "the scale transpose assumes 4 chunks per load group");
+  uint32_t sc_nxt[4] = {0, 0, 0, 0}, sc_cur[4] = {0, 0, 0, 0};
+  auto load_scales = [&](int64_t g) {
+    if (!FAST) return;
+    const int64_t c = g + ks;
+    const uint32_t vo = (c < c1) ? (uint32_t)(r * (K >> 4) + 16 * c) : kOOB;
+    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rsc, (int)vo, 0, 0);
+    sc_nxt[0] = v[0]; sc_nxt[1] = v[1]; sc_nxt[2] = v[2]; sc_nxt[3] = v[3];
+  };
+  auto transpose_scales = [&]() {
+    if (!FAST) return;
+    const auto a = __builtin_amdgcn_permlane32_swap(sc_nxt[0], sc_nxt[2], false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(sc_nxt[1], sc_nxt[3], false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    sc_cur[0] = c[0]; sc_cur[1] = c[1]; sc_cur[2] = d[0]; sc_cur[3] = d[1];
+  };
+
+  // 1. first weight loads, kept in issue order: the loop below relies on
+  //    every step finding the same loads in flight, oldest buffer first. At
+  //    level 6 the offsets of a chunk follow its codes, so those loads wait
+  //    for the offset plan (step 3).
   WChunk buf[kInflight];
+  if (!REF) {
+    load_scales(c0);
 #pragma unroll
-  for (int u = 0; u < kInflight; ++u) {
-    const int64_t c = c0 + u;
-    load_codes<FAST>(crow, srow, K, c * kCh + 64 * ks, row_ok && c < c1, buf[u]);
-    buf[u].o[0] = buf[u].o[1] = buf[u].o[2] = 0;
+    for (int u = 0; u < kInflight; ++u) {
+      load_codes(c0 + u, buf[u]);
+      vmem_fence();
+    }
   }
 
-  // 2. offset plan of this wavefront (lane = 4 * chunk + lane group)
-  PlanEntry pe{};
-  int64_t pbase = c0;   // first chunk of the current plan
-  int32_t pdone = 0;    // refined subgroups before chunk pbase
-  if (refine_w && c0 < c1) {
-    int32_t before = 0;
-    for (int64_t i = lane; i < 8 * c0 && i < mbytes; i += 64) before += __popc((uint32_t)a.w_mask[i]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) before += __shfl_xor(before, o, 64);
-    pdone = before;
+  // 2. block prologue in LDS: delta table, weight-mask copy, activations
+  if (refine_w) {
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) lut[i] = delta_words((uint32_t)i);
+    const int64_t mpad = mask_lds_bytes(K);
+    for (int64_t i = threadIdx.x; i < mpad; i += blockDim.x) mlds[i] = i < mbytes ? a.w_mask[i] : 0;
   }
-  auto build_plan = [&](int64_t cbase) {
-    const int64_t ce = cbase + (lane >> 2);
-    const uint64_t m64 = (ce < c1) ? chunk_mask(a.w_mask, mbytes, ce) : 0ull;
+  if (XLDS) {
+    const int64_t per_row = kp / 8;
+    for (int64_t i = threadIdx.x; i < a.b * per_row + 8; i += blockDim.x) {
+      if (i < a.b * per_row) {
+        const int64_t t = i / per_row;
+        const int64_t k0 = (i - t * per_row) * 8;
+        *(uint4 *)(xs + t * kp + k0) = act_decode8(a, t, k0, refine_x);
+      } else {
+        *(uint4 *)(xs + a.b * kp + 8 * (i - a.b * per_row)) = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();
+
+  // 3. offset plan of this wavefront (lane = 4 * chunk + lane group), from
+  //    the LDS mask copy, and the first offset loads
+  PlanEntry pe{};
+  const int64_t pbase = c0;
+  auto build_plan = [&](int32_t pdone) {
+    const int64_t ce = pbase + (lane >> 2);
+    const uint64_t m64 = (ce < c1) ? *(const uint64_t *)(mlds + 8 * ce) : 0ull;
     const uint32_t m16 = (uint32_t)(m64 >> (16 * (lane & 3))) & 0xFFFFu;
     const int32_t cnt = __popc(m16);
     int32_t incl = cnt;
@@ -267,92 +339,97 @@ __global__ __launch_bounds__(1024) void gemv_stream_kernel(LinearArgs a) {
       if (lane >= o) incl += t;
     }
     pe = make_entry(m16, pdone + incl - cnt);
-    pdone += __shfl(incl, 63, 64);
   };
   auto offsets_load = [&](int64_t c, WChunk &w) {
     const int src = 4 * (int)(c - pbase) + ks;
     const int32_t pos = __shfl(pe.pos, src, 64);
-    const uint32_t bits = __shfl(pe.bits, src, 64);
-    if (row_ok && bits != 0u) {
-      const int64_t at = obase + pos;
-      const int64_t al = at & ~(int64_t)3;
-      w.o[0] = load_dword_guarded(a.w_offsets, al, ototal);
-      w.o[1] = load_dword_guarded(a.w_offsets, al + 4, ototal);
-      w.o[2] = load_dword_guarded(a.w_offsets, al + 8, ototal);
-    }
+    const bool live = refine_w && c < c1;
+    const uint32_t al = live ? ((orow + (uint32_t)pos) & ~3u) : kOOB;
+    w.o[0] = ld_b32(ro, al);
+    w.o[1] = ld_b32(ro, al + 4);
+    w.o[2] = ld_b32(ro, al + 8);
   };
-  if (refine_w && c0 < c1) {
-    build_plan(pbase);
-#pragma unroll
-    for (int u = 0; u < kInflight; ++u)
-      if (c0 + u < c1) offsets_load(c0 + u, buf[u]);
-  }
-
-  // 3. block prologue: delta table, LDS activations
   if (refine_w) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) lut[i] = delta_words((uint32_t)i);
+    int32_t before = 0;
+    for (int64_t i = lane; i < 8 * c0; i += 64) before += __popc((uint32_t)mlds[i]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) before += __shfl_xor(before, o, 64);
+    build_plan(before);
   }
-  if (XLDS) {
-    const int64_t per_row = kp / 8;
-    for (int64_t i = threadIdx.x; i < a.b * per_row; i += blockDim.x) {
-      const int64_t t = i / per_row;
-      const int64_t k0 = (i - t * per_row) * 8;
-      *(uint4 *)(xs + t * kp + k0) = act_decode8(a, t, k0, refine_x);
+  if (REF) {
+    load_scales(c0);
+#pragma unroll
+    for (int u = 0; u < kInflight; ++u) {
+      load_codes(c0 + u, buf[u]);
+      offsets_load(c0 + u, buf[u]);
+      vmem_fence();
     }
   }
-  __syncthreads();
 
   // 4. main loop
-  float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
-  const bool tok_ok = r < a.b;
-  const _Float16 *xrow = XLDS ? xs + (tok_ok ? r : 0) * kp : a.xh + (tok_ok ? r : 0) * a.kpad;
+  float4v acc0 = float4v{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  const _Float16 *xrow = xs + (tok_ok ? r * kp : 0) + 64 * ks;
+  const _Float16 *xzero = xs + a.b * kp;
+  const uint32_t xoff_row = (uint32_t)(r * a.kpad * 2 + 128 * ks);
 
-  auto process = [&](int64_t c, const WChunk &w) {
-    const int64_t e0 = c * kCh + 64 * ks;
-    const half2v s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.s, 1.0f, false);
-    const half2v s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.s, 1.0f, true);
-    uint32_t E[4] = {0, 0, 0, 0};
-    uint32_t any = 0;
+  auto process = [&](int64_t c, const WChunk &w, uint32_t sc) {
+    uint32_t cw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cw[i] = (L == 2) ? autofp2_remap(w.c[i]) : w.c[i];
+    const half2v s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
+    const half2v s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, true);
+
+    uint32_t any = 0, wlo = 0, whi = 0;
+    int src = 0;
     if (refine_w) {
-      const int src = 4 * (int)(c - pbase) + ks;
+      src = 4 * (int)(c - pbase) + ks;
       const uint32_t b16 = __shfl(pe.bits, src, 64);
       any = b16 | __shfl_xor(b16, 16, 64);
       any |= __shfl_xor(any, 32, 64);
       any = __builtin_amdgcn_readfirstlane(any);
       if (any) {
         const int32_t pos = __shfl(pe.pos, src, 64);
-        const uint32_t sh = (uint32_t)((obase + pos) & 3);
-        const uint32_t lo = __builtin_amdgcn_alignbyte(w.o[1], w.o[0], sh);
-        const uint32_t hi = __builtin_amdgcn_alignbyte(w.o[2], w.o[1], sh);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) E[q] = __builtin_amdgcn_perm(hi, lo, __shfl(pe.sel[q], src, 64));
+        const uint32_t sh = (orow + (uint32_t)pos) & 3u;
+        wlo = __builtin_amdgcn_alignbyte(w.o[1], w.o[0], sh);
+        whi = __builtin_amdgcn_alignbyte(w.o[2], w.o[1], sh);
       }
     }
-    // two halves of 32 elements: 4 MFMAs each
+
+    const _Float16 *xp = tok_ok ? xrow + c * kCh : xzero;
+    const uint32_t xo = tok_ok ? xoff_row + (uint32_t)(c * kCh * 2) : kOOB;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       half8v xv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        xv[i] = tok_ok ? *(const half8v *)(xrow + e0 + 32 * hf + 8 * i) : half8v{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int i = 0; i < 4; ++i) {
+        if (XLDS) {
+          xv[i] = *(const half8v *)(xp + 32 * hf + 8 * i);
+        } else {
+          const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xo + 64 * hf + 16 * i), 0, 0);
+          xv[i] = __builtin_bit_cast(half8v, v);
+        }
+      }
       half2v h[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t cw = (L == 2) ? autofp2_remap(w.c[4 * hf + i]) : w.c[4 * hf + i];
-        h[4 * i + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0);
-        h[4 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1);
-        h[4 * i + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2);
-        h[4 * i + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3);
+        const uint32_t q = cw[4 * hf + i];
+        h[4 * i + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 0);
+        h[4 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 1);
+        h[4 * i + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 2);
+        h[4 * i + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 3);
       }
-      if (refine_w) {
+      if (refine_w && (any & (0xFFu << (8 * hf)))) {
+        // one offset byte per subgroup slot of this half (0 where not refined)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int s = 8 * hf + t;
-          if (any & (1u << s)) {
-            const uint32_t byte = (E[s >> 2] >> (8 * (s & 3))) & 0xFFu;
-            const uint2 d = lut[byte];
-            h[2 * t] += as_h2(d.x);
-            h[2 * t + 1] += as_h2(d.y);
+        for (int qq = 0; qq < 2; ++qq) {
+          const uint32_t E = __builtin_amdgcn_perm(whi, wlo, __shfl(pe.sel[2 * hf + qq], src, 64));
+          uint2 d[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) d[t] = lut[(E >> (8 * t)) & 0xFFu];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            h[8 * qq + 2 * t] += as_h2(d[t].x);
+            h[8 * qq + 2 * t + 1] += as_h2(d[t].y);
           }
         }
       }
@@ -364,44 +441,37 @@ __global__ __launch_bounds__(1024) void gemv_stream_kernel(LinearArgs a) {
         const half2v b2 = half2v{bb, bb};
         const half2v p0 = h[4 * i] * b2, p1 = h[4 * i + 1] * b2, p2 = h[4 * i + 2] * b2, p3 = h[4 * i + 3] * b2;
         const half8v wv = half8v{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, xv[i], acc, 0, 0, 0);
+        if (i & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, xv[i], acc1, 0, 0, 0);
+        else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, xv[i], acc0, 0, 0, 0);
       }
     }
   };
 
+  // One load group: process kInflight buffered chunks, each followed by the
+  // refill of its buffer kInflight chunks ahead, so kInflight - 1 chunks stay
+  // in flight while a chunk is computed.
   for (int64_t g = c0; g < c1; g += kInflight) {
-    if (refine_w && g - pbase >= kPlanChunks) {
-      // next plan round (kPlanChunks is a multiple of kInflight, so rounds
-      // start at a group): the buffered chunks g .. g+kInflight-1 still lack
-      // their offsets
-      pbase = g;
-      build_plan(pbase);
-#pragma unroll
-      for (int u = 0; u < kInflight; ++u)
-        if (g + u < c1) offsets_load(g + u, buf[u]);
-    }
+    transpose_scales();
 #pragma unroll
     for (int u = 0; u < kInflight; ++u) {
       const int64_t c = g + u;
-      if (c < c1) {
-        process(c, buf[u]);
-        const int64_t cn = c + kInflight;
-        if (cn < c1) {
-          load_codes<FAST>(crow, srow, K, cn * kCh + 64 * ks, row_ok, buf[u]);
-          buf[u].o[0] = buf[u].o[1] = buf[u].o[2] = 0;
-          if (refine_w && cn - pbase < kPlanChunks) offsets_load(cn, buf[u]);
-        }
-      }
+      if (c < c1) process(c, buf[u], FAST ? sc_cur[u] : buf[u].s);
+      vmem_fence();
+      if (u == 0) load_scales(g + kInflight);
+      load_codes(c + kInflight, buf[u]);
+      if (REF) offsets_load(c + kInflight, buf[u]);   // unconditional loads: uniform waits
+      vmem_fence();
     }
   }
 
-  // 5. sum the wavefront tiles and store
+  // 5. sum the K-split tiles of each row tile and store
+  const float4v acc = acc0 + acc1;
   __syncthreads();
   red[wave * 64 + lane] = acc;
   __syncthreads();
-  if (wave != 0) return;
-  float4v s = red[lane];
-  for (int w = 1; w < nw; ++w) s += red[w * 64 + lane];
+  if (kw != 0 || rows == 0) return;
+  float4v s = red[wave * 64 + lane];
+  for (int w = 1; w < WK; ++w) s += red[(wave + w) * 64 + lane];
   if (!tok_ok) return;
   float scale = (*a.w_T) * (*a.x_T);
   if (L == 2) scale *= a.c2;
@@ -422,6 +492,15 @@ __global__ __launch_bounds__(1024) void gemv_stream_kernel(LinearArgs a) {
         if (nb + v < a.n) y[nb + v] = s[v] * scale;
     }
   }
+}
+
+template <bool XLDS, bool FAST>
+__global__ __launch_bounds__(1024) void gemv_stream_kernel(LinearArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int L = run_level(a);
+  if (L == 6) stream_tile<6, XLDS, FAST>(a, lds);
+  else if (L == 2) stream_tile<2, XLDS, FAST>(a, lds);
+  else stream_tile<4, XLDS, FAST>(a, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -610,7 +689,9 @@ __global__ __launch_bounds__(256) void gemv_panel_kernel(LinearArgs a) {
 // ---------------------------------------------------------------------------
 
 struct StreamCfg {
-  int waves;
+  int waves;   // wavefronts per block = rt * wk
+  int wk;      // wavefronts per row tile (K split)
+  int rt;      // row tiles per block
   bool xlds;
   bool fast;
   size_t lds;
@@ -632,20 +713,27 @@ int max_lds_per_block() {
 StreamCfg stream_cfg(const LinearArgs &a) {
   StreamCfg c{};
   const int64_t nch = (a.k + kCh - 1) / kCh;
-  const int64_t blocks = (a.n + 15) / 16;
-  int64_t w = (4096 + blocks - 1) / blocks;   // aim at 4096 wavefronts in the grid
-  int p = 1;
-  while (p < w && p < kMaxWaves) p <<= 1;
-  while (p > 1 && p > nch) p >>= 1;
-  if (a.waves > 0) p = a.waves;
-  c.waves = p;
-  c.fast = (a.k % 64) == 0;
-  const size_t lut = 256 * sizeof(uint2);
-  const size_t red = (size_t)p * 64 * sizeof(float4v);
-  const size_t xs = (size_t)a.b * (size_t)(nch * kCh) * sizeof(_Float16);
-  const size_t budget = max_lds_per_block() < 65536 ? (size_t)max_lds_per_block() : 65536;
-  c.xlds = lut + (xs > red ? xs : red) <= budget;
-  c.lds = lut + (c.xlds ? (xs > red ? xs : red) : red);
+  const int64_t tiles = (a.n + 15) / 16;
+  // wavefronts per tile (K split): enough wavefronts in the grid, and every
+  // wavefront's range within one offset plan
+  int wk = 1;
+  const int64_t want = 2048;   // ~8 wavefronts per CU
+  while (wk < kMaxWaves && tiles * wk < want && nch / (2 * wk) >= 2) wk <<= 1;
+  if (a.waves > 0) wk = a.waves;
+  while (wk < kMaxWaves && (nch + wk - 1) / wk > kPlanChunks) wk <<= 1;
+  // row tiles per block: share the LDS activation copy among up to 16 wavefronts
+  int rt = 1;
+  while (rt * wk * 2 <= 4 && tiles >= (int64_t)rt * 2 * 256) rt <<= 1;
+  c.wk = wk;
+  c.rt = rt;
+  c.waves = wk * rt;
+  c.fast = (a.k % kCh) == 0;
+  const size_t lut = (size_t)kLutBytes;
+  const size_t red = (size_t)c.waves * 64 * sizeof(float4v);
+  const size_t msk = (size_t)mask_lds_bytes(a.k);
+  const size_t xs = (size_t)a.b * (size_t)(nch * kCh) * sizeof(_Float16) + 128;
+  c.xlds = lut + (msk + xs > red ? msk + xs : red) <= (size_t)max_lds_per_block();
+  c.lds = lut + (c.xlds ? (msk + xs > red ? msk + xs : red) : (msk > red ? msk : red));
   return c;
 }
 
@@ -667,13 +755,16 @@ hipError_t launch_act_dequant(const LinearArgs &a, hipStream_t s) {
 hipError_t launch_gemv(const LinearArgs &a0, hipStream_t s) {
   if (a0.b <= 16) {
     const StreamCfg c = stream_cfg(a0);
-    const dim3 grid((unsigned)((a0.n + 15) / 16)), block((unsigned)(64 * c.waves));
+    LinearArgs a1 = a0;
+    a1.wk = c.wk;
+    const int64_t tiles = (a0.n + 15) / 16;
+    const dim3 grid((unsigned)((tiles + c.rt - 1) / c.rt)), block((unsigned)(64 * c.waves));
     if (c.xlds) {
-      if (c.fast) hipLaunchKernelGGL((gemv_stream_kernel<true, true>), grid, block, c.lds, s, a0);
-      else hipLaunchKernelGGL((gemv_stream_kernel<true, false>), grid, block, c.lds, s, a0);
+      if (c.fast) hipLaunchKernelGGL((gemv_stream_kernel<true, true>), grid, block, c.lds, s, a1);
+      else hipLaunchKernelGGL((gemv_stream_kernel<true, false>), grid, block, c.lds, s, a1);
     } else {
-      if (c.fast) hipLaunchKernelGGL((gemv_stream_kernel<false, true>), grid, block, c.lds, s, a0);
-      else hipLaunchKernelGGL((gemv_stream_kernel<false, false>), grid, block, c.lds, s, a0);
+      if (c.fast) hipLaunchKernelGGL((gemv_stream_kernel<false, true>), grid, block, c.lds, s, a1);
+      else hipLaunchKernelGGL((gemv_stream_kernel<false, false>), grid, block, c.lds, s, a1);
     }
     return hipGetLastError();
   }

@@ -68,7 +68,7 @@ def test_sizes(N):
     assert L.autofp_packed_bytes(16, 256, N.ACTIVATION, 1, 0, out) == 0
     assert list(out) == [16 * 128, 16 * 16, 4, 16 * 8, 16 * 64]
     assert L.autofp_packed_bytes(256, 4096, N.WEIGHT, 1, 204, out) == 0
-    assert list(out) == [256 * 2048, 256 * 256, 4, 128, 256 * 204]
+    assert list(out) == [256 * 2048, 256 * 256, 4, 128, 256 * 204 + 16]
     assert L.autofp_packed_bytes(16, 250, N.WEIGHT, 0, 0, out) == 2
     n = C.c_int32()
     p = params(N)
