@@ -48,6 +48,8 @@ constexpr int kCh = 256;         // K elements per chunk
 constexpr int kInflight = 4;     // chunks of weight loads in flight per wavefront
 constexpr int kMaxWaves = 16;    // wavefronts per block (1024 threads)
 constexpr int kPlanChunks = 16;  // chunks per wavefront covered by its offset plan
+constexpr int kProItems = 4;     // activation items (8 elements) per thread loaded by the block prologue
+constexpr int kProMask = 2;      // weight-mask dwords per thread loaded by the block prologue
 
 __device__ __forceinline__ int run_level(const LinearArgs &a) {
   return a.bits_dev ? *a.bits_dev : a.bits;
@@ -135,6 +137,26 @@ __device__ __forceinline__ uint4 act_decode8(const LinearArgs &a, int64_t tok, i
   return make_uint4(as_u(h[0] * b2), as_u(h[1] * b2), as_u(h[2] * b2), as_u(h[3] * b2));
 }
 
+// The same decode from already loaded bytes: 8 codes, their group scale byte
+// and (refine) the two offset bytes of their subgroups.
+__device__ __forceinline__ uint4 act_decode8_vals(uint32_t cw, uint32_t sbyte, uint32_t ob, bool refine) {
+  half2v h[4];
+  h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0);
+  h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1);
+  h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2);
+  h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3);
+  if (refine) {
+    const uint2 d0 = delta_words(ob & 0xFFu), d1 = delta_words((ob >> 8) & 0xFFu);
+    h[0] += as_h2(d0.x);
+    h[1] += as_h2(d0.y);
+    h[2] += as_h2(d1.x);
+    h[3] += as_h2(d1.y);
+  }
+  const _Float16 B = (_Float16)e4m3_value(sbyte & 0xFFu);
+  const half2v b2 = half2v{B, B};
+  return make_uint4(as_u(h[0] * b2), as_u(h[1] * b2), as_u(h[2] * b2), as_u(h[3] * b2));
+}
+
 // fp16 panel of the activations for the workspace path: xh[b][kpad],
 // zero-padded past k. One thread per 8 elements.
 __global__ __launch_bounds__(256) void act_dequant_kernel(LinearArgs a) {
@@ -151,8 +173,10 @@ __global__ __launch_bounds__(256) void act_dequant_kernel(LinearArgs a) {
 // Streaming GEMV, up to 16 tokens per launch
 // ---------------------------------------------------------------------------
 //
-// Dynamic LDS layout: [delta table 256 x 8 B][XLDS: activations B x kp fp16,
-// then a 128-byte zero row read by the lanes of absent tokens]; the
+// Dynamic LDS layout: [delta table 256 x 8 B][XLDS: activations B x kp fp16
+// at a row pitch of kp + 8 (16 bytes of padding put the rows of different
+// tokens on different LDS banks), then a 128-byte zero row read by the lanes
+// of absent tokens]; the
 // reduction buffer W x 64 x 16 B reuses the space after the main loop.
 //
 // Every global read goes through a buffer resource covering the block's rows,
@@ -202,6 +226,7 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
   const int64_t K = a.k;
   const int64_t nch = (K + kCh - 1) / kCh;
   const int64_t kp = nch * kCh;
+  const int64_t xpitch = kp + 8;   // LDS row pitch of the activations (halves)
   const int64_t n0 = ((int64_t)blockIdx.x * (nw / WK) + tile) * 16;
   int64_t rows = a.n - n0;
   rows = rows < 0 ? 0 : rows > 16 ? 16 : rows;
@@ -289,6 +314,42 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
     sc_cur[0] = c[0]; sc_cur[1] = c[1]; sc_cur[2] = d[0]; sc_cur[3] = d[1];
   };
 
+  // 0. block prologue loads: the activation codes / scales / offsets and the
+  //    weight mask, issued before the weight loads so that waiting for them
+  //    leaves the weight loads in flight (a fixed number of loads per thread;
+  //    items past the end read as zero).
+  const int nthr = blockDim.x;
+  const int64_t per_row = kp / 8;
+  const int64_t items = XLDS ? a.b * per_row : 0;
+  const int64_t mdw = refine_w ? (mbytes + 3) / 4 : 0;
+  const bool pro_static = FAST && items <= (int64_t)kProItems * nthr && mask_lds_bytes(K) <= 4 * (int64_t)kProMask * nthr;
+  uint32_t pq[kProItems], ps[kProItems], po[kProItems], pm[kProMask];
+  if (pro_static) {
+    const __amdgpu_buffer_rsrc_t rxc = make_rsrc(a.x_codes, a.b * (K >> 1));
+    const __amdgpu_buffer_rsrc_t rxs = make_rsrc(a.x_scales, a.b * (K >> 4));
+    const __amdgpu_buffer_rsrc_t rxo = make_rsrc(refine_x ? a.x_offsets : a.x_codes, refine_x ? a.b * (K >> 2) : 0);
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(refine_w ? a.w_mask : a.w_codes, refine_w ? mbytes : 0);
+    // FAST: the LDS row pitch is K, so item i covers elements 8i .. 8i + 7
+    // of the token-major activations, i.e. code bytes 4i, scale byte i / 2
+    // and offset bytes 2i, 2i + 1.
+#pragma unroll
+    for (int j = 0; j < kProItems; ++j) {
+      const uint32_t i = threadIdx.x + (uint32_t)(j * nthr);
+      const bool live = i < (uint32_t)items;
+      pq[j] = ld_b32(rxc, live ? 4 * i : kOOB);
+      ps[j] = __builtin_amdgcn_raw_buffer_load_b8(rxs, (int)(live ? i >> 1 : kOOB), 0, 0);
+      po[j] = REF ? __builtin_amdgcn_raw_buffer_load_b16(rxo, (int)(live && refine_x ? 2 * i : kOOB), 0, 0) : 0u;
+    }
+    if (REF) {
+#pragma unroll
+      for (int j = 0; j < kProMask; ++j) {
+        const uint32_t i = threadIdx.x + (uint32_t)(j * nthr);
+        pm[j] = ld_b32(rm, i < (uint32_t)mdw ? 4 * i : kOOB);
+      }
+    }
+    vmem_fence();
+  }
+
   // 1. first weight loads, kept in issue order: the loop below relies on
   //    every step finding the same loads in flight, oldest buffer first. At
   //    level 6 the offsets of a chunk follow its codes, so those loads wait
@@ -304,23 +365,41 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
   }
 
   // 2. block prologue in LDS: delta table, weight-mask copy, activations
+  //    (+ a zero row for absent tokens)
+  const int64_t mpad = mask_lds_bytes(K);
   if (refine_w) {
     for (int i = threadIdx.x; i < 256; i += blockDim.x) lut[i] = delta_words((uint32_t)i);
-    const int64_t mpad = mask_lds_bytes(K);
-    for (int64_t i = threadIdx.x; i < mpad; i += blockDim.x) mlds[i] = i < mbytes ? a.w_mask[i] : 0;
   }
-  if (XLDS) {
-    const int64_t per_row = kp / 8;
-    for (int64_t i = threadIdx.x; i < a.b * per_row + 8; i += blockDim.x) {
-      if (i < a.b * per_row) {
+  if (pro_static) {
+    if (REF) {
+#pragma unroll
+      for (int j = 0; j < kProMask; ++j) {
+        const uint32_t i = threadIdx.x + (uint32_t)(j * nthr);
+        if (4 * i < (uint32_t)mpad) *(uint32_t *)(mlds + 4 * i) = pm[j];   // zero past the mask
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kProItems; ++j) {
+      const uint32_t i = threadIdx.x + (uint32_t)(j * nthr);
+      if (i < (uint32_t)items) {
+        const uint32_t t = i / (uint32_t)per_row;
+        const uint32_t k0 = (i - t * (uint32_t)per_row) * 8;
+        *(uint4 *)(xs + t * xpitch + k0) = act_decode8_vals(pq[j], ps[j], po[j], refine_x);
+      }
+    }
+  } else {
+    if (refine_w) {
+      for (int64_t i = threadIdx.x; i < mpad; i += blockDim.x) mlds[i] = i < mbytes ? a.w_mask[i] : 0;
+    }
+    if (XLDS) {
+      for (int64_t i = threadIdx.x; i < items; i += blockDim.x) {
         const int64_t t = i / per_row;
         const int64_t k0 = (i - t * per_row) * 8;
-        *(uint4 *)(xs + t * kp + k0) = act_decode8(a, t, k0, refine_x);
-      } else {
-        *(uint4 *)(xs + a.b * kp + 8 * (i - a.b * per_row)) = make_uint4(0, 0, 0, 0);
+        *(uint4 *)(xs + t * xpitch + k0) = act_decode8(a, t, k0, refine_x);
       }
     }
   }
+  if (XLDS && threadIdx.x < 8) *(uint4 *)(xs + a.b * xpitch + 8 * threadIdx.x) = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
   // 3. offset plan of this wavefront (lane = 4 * chunk + lane group), from
@@ -368,8 +447,8 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
 
   // 4. main loop
   float4v acc0 = float4v{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  const _Float16 *xrow = xs + (tok_ok ? r * kp : 0) + 64 * ks;
-  const _Float16 *xzero = xs + a.b * kp;
+  const _Float16 *xrow = xs + (tok_ok ? r * xpitch : 0) + 64 * ks;
+  const _Float16 *xzero = xs + a.b * xpitch;
   const uint32_t xoff_row = (uint32_t)(r * a.kpad * 2 + 128 * ks);
 
   auto process = [&](int64_t c, const WChunk &w, uint32_t sc) {
@@ -731,7 +810,7 @@ StreamCfg stream_cfg(const LinearArgs &a) {
   const size_t lut = (size_t)kLutBytes;
   const size_t red = (size_t)c.waves * 64 * sizeof(float4v);
   const size_t msk = (size_t)mask_lds_bytes(a.k);
-  const size_t xs = (size_t)a.b * (size_t)(nch * kCh) * sizeof(_Float16) + 128;
+  const size_t xs = (size_t)a.b * (size_t)(nch * kCh + 8) * sizeof(_Float16) + 128;
   c.xlds = lut + (msk + xs > red ? msk + xs : red) <= (size_t)max_lds_per_block();
   c.lds = lut + (c.xlds ? (msk + xs > red ? msk + xs : red) : (msk > red ? msk : red));
   return c;
