@@ -95,6 +95,7 @@ class DecodeBench:
         self.qws = {k: torch.empty(A.workspace_bytes(0, batch, k), dtype=torch.uint8, device=device) for k in ks}
         self.gws = {k: torch.empty(A.workspace_bytes(2, batch, k), dtype=torch.uint8, device=device) for k in ks}
         self.logits = S.logits(batch, S.VOCAB, seed=7, device=device)
+        self.sws = torch.empty(A.workspace_bytes(4, batch, S.VOCAB), dtype=torch.uint8, device=device)
         self.h_prev = S.hidden(batch, S.HIDDEN, seed=7, tensor_id=0, device=device)
         self.h_cur = (self.h_prev + 0.05 * S.hidden(batch, S.HIDDEN, seed=7, tensor_id=1, device=device)).contiguous()
         self.g_e = torch.zeros(batch, dtype=torch.float32, device=device)
@@ -116,7 +117,7 @@ class DecodeBench:
 
     def step(self, s):
         A, p = self.A, self.p
-        A.policy_signals(logits=self.logits, out_entropy=self.g_e, params=p)
+        A.policy_signals(logits=self.logits, out_entropy=self.g_e, params=p, workspace=self.sws)
         for j, (layer, level) in enumerate(zip(self.layers_of(s), LEVELS)):
             for name, n, k in SHAPES:
                 wp = layer[name]
@@ -298,7 +299,7 @@ def main():
     achieved = g_bytes / (ms_g * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": "gemv_small_kernel (batch <= 16)",
+                "kernel": "gemv_stream_kernel (batch <= 16)",
                 "avg_launch_us": round(ms_g * 1e3 / n_launch, 3),
                 "bytes_per_launch": int(g_bytes / n_launch)}
     log(f"gemv-only: {ms_g:.4f} ms per {n_launch} launches, {achieved:.1f} GB/s")

@@ -127,7 +127,8 @@ typedef enum {
   AUTOFP_OP_QUANTIZE = 0,     /* rows, k of the input                           */
   AUTOFP_OP_SELECT_MASK = 1,  /* rows, k of the weight                          */
   AUTOFP_OP_GEMV = 2,         /* rows = batch (tokens), k                       */
-  AUTOFP_OP_GEMM = 3          /* rows = tokens, k                               */
+  AUTOFP_OP_GEMM = 3,         /* rows = tokens, k                               */
+  AUTOFP_OP_SIGNALS = 4       /* rows = batch, k = vocab (any vocab >= 1)       */
 } autofp_op;
 
 /* Fills *p with the paper's hyperparameters. Errors: NULL. */
@@ -230,12 +231,16 @@ autofp_status autofp_gemm(const autofp_packed *w, const autofp_packed *x, int32_
  *  - update_out[b] = L_A = ||h_cur[b] - h_prev[b]||_2 / (||h_prev[b]||_2 + eps)
  *    ([AE] Eq. 1); h_prev, h_cur [batch x hidden] in h_dtype (F32 or BF16).
  * Either signal is skipped when its output pointer is NULL (its inputs may
- * then be NULL too). Errors: NULL, SHAPE, DTYPE, ARG, HIP.
+ * then be NULL too). G_E needs a workspace of autofp_workspace_bytes(
+ * AUTOFP_OP_SIGNALS, batch, vocab) bytes (per-slice candidates of the
+ * vocabulary); L_A needs none (workspace may be NULL when entropy_out is).
+ * Errors: NULL, SHAPE, DTYPE, ARG, WORKSPACE, HIP.
  */
 autofp_status autofp_policy_signals(const float *logits, int64_t batch, int64_t vocab,
                                     const void *h_prev, const void *h_cur, int32_t h_dtype,
                                     int64_t hidden, const autofp_params *p,
-                                    float *entropy_out, float *update_out, void *stream);
+                                    float *entropy_out, float *update_out, void *workspace,
+                                    size_t workspace_bytes, void *stream);
 
 /*
  * One step of the runtime precision policy after layer `layer` has run

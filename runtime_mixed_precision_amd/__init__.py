@@ -238,8 +238,12 @@ def gemm(w: AutoFPTensor, x: AutoFPTensor, bits=4, bits_dev=None, out_dtype=torc
 
 
 def policy_signals(logits=None, h_prev=None, h_cur=None, params=None, stream=None,
-                   out_entropy=None, out_update=None):
-    """(G_E per row or None, L_A per row or None) via autofp_policy_signals."""
+                   out_entropy=None, out_update=None, workspace=None):
+    """(G_E per row or None, L_A per row or None) via autofp_policy_signals.
+
+    ``workspace`` (uint8 device tensor of workspace_bytes(OP_SIGNALS, batch,
+    vocab) bytes) is allocated per call when not given; pass one to keep the
+    call free of allocations (e.g. under graph capture)."""
     _dev_check(logits, h_prev, h_cur)
     p = params or default_params()
     ent = upd = None
@@ -251,6 +255,8 @@ def policy_signals(logits=None, h_prev=None, h_cur=None, params=None, stream=Non
         batch, vocab = logits.shape
         ent = out_entropy if out_entropy is not None else \
             torch.empty(batch, dtype=torch.float32, device=logits.device)
+        if workspace is None:
+            workspace = _workspace(N.OP_SIGNALS, batch, vocab, logits.device)
     if h_prev is not None:
         if h_prev.shape != h_cur.shape or h_prev.dtype != h_cur.dtype or h_prev.dim() != 2:
             raise ValueError("h_prev and h_cur must be matching 2-D tensors")
@@ -260,8 +266,10 @@ def policy_signals(logits=None, h_prev=None, h_cur=None, params=None, stream=Non
         hdt = _DT[h_prev.dtype]
         upd = out_update if out_update is not None else \
             torch.empty(batch, dtype=torch.float32, device=h_prev.device)
+    wsb = workspace.numel() if workspace is not None else 0
     N.check(N.lib().autofp_policy_signals(_ptr(logits), batch, vocab, _ptr(h_prev), _ptr(h_cur), hdt,
-                                          hidden, C.byref(p), _ptr(ent), _ptr(upd), _stream(stream)),
+                                          hidden, C.byref(p), _ptr(ent), _ptr(upd), _ptr(workspace),
+                                          wsb, _stream(stream)),
             "autofp_policy_signals")
     return ent, upd
 

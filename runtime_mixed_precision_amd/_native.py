@@ -20,7 +20,7 @@ STATUS_NAMES = {
 }
 F32, BF16 = 0, 1
 WEIGHT, ACTIVATION = 0, 1
-OP_QUANTIZE, OP_SELECT_MASK, OP_GEMV, OP_GEMM = 0, 1, 2, 3
+OP_QUANTIZE, OP_SELECT_MASK, OP_GEMV, OP_GEMM, OP_SIGNALS = 0, 1, 2, 3, 4
 
 # Every symbol include/autofp.h declares.
 EXPORTS = (
@@ -96,7 +96,7 @@ def lib():
         "autofp_gemm": (C.c_int, [P(Packed), P(Packed), C.c_int32, vp, vp, C.c_int32, P(Params), vp,
                                   C.c_size_t, vp]),
         "autofp_policy_signals": (C.c_int, [vp, C.c_int64, C.c_int64, vp, vp, C.c_int32, C.c_int64,
-                                            P(Params), vp, vp, vp]),
+                                            P(Params), vp, vp, vp, C.c_size_t, vp]),
         "autofp_policy_update": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, vp, vp, C.c_int64,
                                            P(Params), vp, vp, vp, vp]),
     }

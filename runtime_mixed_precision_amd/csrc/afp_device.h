@@ -118,6 +118,38 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Largest value of the wavefront in every lane, through DPP row moves and the
+// gfx950 row swaps (no LDS traffic, ALU latency only).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  auto dmax = [](uint32_t x, int ctrl) -> uint32_t {
+    uint32_t y = 0;
+    switch (ctrl) {   // the DPP control must be a constant
+      case 0: y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false); break;   // quad xor 1
+      case 1: y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false); break;   // quad xor 2
+      case 2: y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false); break;  // row half mirror
+      default: y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false); break; // row mirror
+    }
+    return x > y ? x : y;
+  };
+  v = dmax(v, 0);
+  v = dmax(v, 1);
+  v = dmax(v, 2);
+  v = dmax(v, 3);   // every lane: max of its row of 16
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = a[0] > a[1] ? a[0] : a[1];   // max of rows (0, 1) and of rows (2, 3)
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return b[0] > b[1] ? b[0] : b[1];
+}
+
+// Order-preserving map of fp32 to uint32 (for -inf < ... < +inf; NaN unordered).
+__device__ __forceinline__ uint32_t f32_order(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float f32_unorder(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
 __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -47,7 +47,11 @@ struct EncodeArgs {
   int32_t n_refined;
   uint8_t *w_offsets;           // [rows][n_refined]
 };
-hipError_t launch_encode(const EncodeArgs &a, hipStream_t s);
+// small: every block takes the amax of the whole tensor itself (one launch,
+// for rows * k <= kSmallEncode; a.partial is not read); otherwise a.partial
+// holds the amax partials of launch_amax_partial.
+constexpr int64_t kSmallEncode = 1 << 14;
+hipError_t launch_encode(const EncodeArgs &a, bool small, hipStream_t s);
 
 // Weight-mask selection ([AE] App. E, Alg. 1 allocation with H = I).
 hipError_t launch_select_mask(const float *w, int64_t rows, int64_t k, int32_t budget,
@@ -89,8 +93,10 @@ hipError_t launch_gemv(const LinearArgs &a, hipStream_t s);
 hipError_t launch_gemm(const LinearArgs &a, hipStream_t s);
 
 // ---- signals.hip ----
+int64_t entropy_slices(int64_t vocab);                        // vocabulary slices per row
+size_t entropy_workspace_bytes(int64_t batch, int64_t vocab);  // per-slice candidates / partials
 hipError_t launch_entropy(const float *logits, int64_t batch, int64_t vocab, int top_k,
-                          float *out, hipStream_t s);
+                          float *out, void *workspace, hipStream_t s);
 struct PolicyArgs {
   int phase, layer, new_sequence;
   const float *l_a, *g_e;

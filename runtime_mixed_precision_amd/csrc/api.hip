@@ -189,6 +189,11 @@ autofp_status autofp_weight_refined_count(int64_t k, const autofp_params *p, int
 
 autofp_status autofp_workspace_bytes(int32_t op, int64_t rows, int64_t k, size_t *bytes) {
   if (!bytes) return AUTOFP_ERR_NULL;
+  if (op == AUTOFP_OP_SIGNALS) {
+    if (rows < 1 || k < 1 || rows > 65535) return AUTOFP_ERR_SHAPE;
+    *bytes = entropy_workspace_bytes(rows, k);
+    return AUTOFP_OK;
+  }
   if (rows < 1 || !valid_k(k)) return AUTOFP_ERR_SHAPE;
   switch (op) {
     case AUTOFP_OP_QUANTIZE: *bytes = ws_quantize(rows, k); return AUTOFP_OK;
@@ -254,9 +259,13 @@ autofp_status autofp_quantize(const void *x, int32_t x_dtype, int32_t refine,
   float *partial = (float *)workspace;
   int32_t *prefix = (int32_t *)((char *)workspace + align_up(sizeof(float) * kAmaxBlocks));
   const int64_t n = out->rows * out->k;
+  const bool small = n <= kSmallEncode;
   const int np = amax_partial_count(n);
-  hipError_t e = launch_amax_partial(x, x_dtype, n, partial, np, s);
-  if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  hipError_t e = hipSuccess;
+  if (!small) {
+    e = launch_amax_partial(x, x_dtype, n, partial, np, s);
+    if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  }
   if (w_refine) {
     e = launch_mask_prefix(out->mask, mask_bytes(out->k), prefix, s);
     if (e != hipSuccess) return AUTOFP_ERR_HIP;
@@ -280,7 +289,7 @@ autofp_status autofp_quantize(const void *x, int32_t x_dtype, int32_t refine,
   a.w_prefix = prefix;
   a.n_refined = out->n_refined;
   a.w_offsets = out->offsets;
-  return from_hip(launch_encode(a, s));
+  return from_hip(launch_encode(a, small, s));
 }
 
 autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_t bits,
@@ -321,7 +330,8 @@ autofp_status autofp_gemm(const autofp_packed *w, const autofp_packed *x, int32_
 autofp_status autofp_policy_signals(const float *logits, int64_t batch, int64_t vocab,
                                     const void *h_prev, const void *h_cur, int32_t h_dtype,
                                     int64_t hidden, const autofp_params *p, float *entropy_out,
-                                    float *update_out, void *stream) {
+                                    float *update_out, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
   const autofp_params pp = params_or_default(p);
   if (!entropy_out && !update_out) return AUTOFP_ERR_NULL;
   if (batch < 1) return AUTOFP_ERR_SHAPE;
@@ -330,6 +340,9 @@ autofp_status autofp_policy_signals(const float *logits, int64_t batch, int64_t 
     if (vocab < 1) return AUTOFP_ERR_SHAPE;
     if (pp.top_k < 1 || (pp.top_k > 32 && pp.top_k < vocab)) return AUTOFP_ERR_ARG;
     if (!aligned16(logits)) return AUTOFP_ERR_ARG;
+    if (batch > 65535) return AUTOFP_ERR_SHAPE;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < entropy_workspace_bytes(batch, vocab))
+      return AUTOFP_ERR_WORKSPACE;
   }
   if (update_out) {
     if (!h_prev || !h_cur) return AUTOFP_ERR_NULL;
@@ -339,7 +352,7 @@ autofp_status autofp_policy_signals(const float *logits, int64_t batch, int64_t 
   }
   hipStream_t s = (hipStream_t)stream;
   if (entropy_out) {
-    const hipError_t e = launch_entropy(logits, batch, vocab, pp.top_k, entropy_out, s);
+    const hipError_t e = launch_entropy(logits, batch, vocab, pp.top_k, entropy_out, workspace, s);
     if (e != hipSuccess) return AUTOFP_ERR_HIP;
   }
   if (update_out) {

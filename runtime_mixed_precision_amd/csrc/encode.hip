@@ -186,111 +186,147 @@ __device__ __forceinline__ void load_pair(const void *x, int dtype, int64_t base
 }
 
 // ---------------------------------------------------------------------------
-// Encoder: one thread per 32 elements (two groups) of one row.
+// Encoder: one thread per subgroup (4 elements); the 4 lanes of a quad hold
+// one 16-element group and share its amax through DPP quad moves.
+// Block (bx, by) covers subgroups [256 bx, 256 bx + 256) of rows by,
+// by + gridDim.y, ...
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
+constexpr int kEncThreads = 256;
+
+__device__ __forceinline__ float quad_max(float v) {
+  const float a = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v = fmaxf(v, a);
+  const float b = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  return fmaxf(v, b);
+}
+
+// amax over all n elements, computed by the whole block (small tensors)
+__device__ float block_amax_all(const void *x, int dtype, int64_t n) {
+  float m = 0.0f;
+  const int64_t n8 = n / 8;   // n is a multiple of 16
+  for (int64_t u0 = threadIdx.x; u0 < n8; u0 += 4 * kEncThreads) {
+    uint4 p[4];
+    float4 f[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t u = u0 + (int64_t)j * kEncThreads;
+      if (dtype == AUTOFP_BF16) {
+        p[j] = u < n8 ? ((const uint4 *)x)[u] : make_uint4(0, 0, 0, 0);
+      } else {
+        f[2 * j] = u < n8 ? ((const float4 *)x)[2 * u] : make_float4(0.f, 0.f, 0.f, 0.f);
+        f[2 * j + 1] = u < n8 ? ((const float4 *)x)[2 * u + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (dtype == AUTOFP_BF16) {
+        const uint32_t w[4] = {p[j].x, p[j].y, p[j].z, p[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          m = fmaxf(m, fabsf(__uint_as_float(w[i] << 16)));
+          m = fmaxf(m, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+        }
+      } else {
+        const float4 a = f[2 * j], b = f[2 * j + 1];
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+      }
+    }
+  }
+  m = wave_max(m);
+  __shared__ float red[kEncThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kEncThreads / 64; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
+
+template <bool SMALL>
+__global__ __launch_bounds__(kEncThreads) void encode_kernel(EncodeArgs a) {
 #pragma clang fp contract(off)
-  const float amax = fold_partials(a.partial, a.n_partial);
+  const float amax = SMALL ? block_amax_all(a.x, a.dtype, a.rows * a.k) : fold_partials(a.partial, a.n_partial);
   const float T = amax / 2688.0f;
   const float sixT = 6.0f * T;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.tensor_scale = T;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.tensor_scale = T;
 
-  const int64_t P2 = (a.k + 31) / 32;
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= a.rows * P2) return;
-  const int64_t row = idx / P2;
-  const int64_t pr = idx - row * P2;
-  const int64_t k0 = pr * 32;
-  const int nel = (int)((a.k - k0) < 32 ? (a.k - k0) : 32);
-  const int ng = nel / 16;
-  const bool vec_ok = (a.k % 32) == 0;
-
-  float xv[32];
-  load_pair(a.x, a.dtype, row * a.k + k0, nel, vec_ok, xv);
-  PairEnc e;
-  encode_pair(xv, ng, T, sixT, e);
-
-  // codes: element 2i in the low nibble of byte i
-  uint32_t cw[4];
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint32_t acc = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc |= e.q[8 * w + j] << (4 * j);
-    cw[w] = acc;
-  }
-  uint8_t *cdst = a.codes + row * (a.k / 2) + k0 / 2;
-  uint8_t *sdst = a.scales + row * (a.k / 16) + k0 / 16;
-  if (vec_ok) {
-    *(uint4 *)cdst = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-    *(uint16_t *)sdst = (uint16_t)(e.B[0] | (e.B[1] << 8));
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (i < nel / 2) cdst[i] = (uint8_t)(cw[i >> 2] >> (8 * (i & 3)));
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-      if (g < ng) sdst[g] = (uint8_t)e.B[g];
-  }
-
+  const int64_t ns = a.k / 4;                                  // subgroups per row
+  const int64_t mb = (a.k + 31) / 32;                          // mask bytes per row
+  const int64_t s = (int64_t)blockIdx.x * kEncThreads + threadIdx.x;
+  const bool live = s < ns;
+  const int lane = threadIdx.x & 63;
   const bool want_act = a.act_refine != 0;
   const bool want_w = a.w_mask != nullptr;
-  if (!want_act && !want_w) return;
-
-  // per-subgroup offset bytes (d = argmin |r - d/8|, r = v - q, exact in fp32)
-  uint32_t ob[8];
-#pragma unroll
-  for (int sg = 0; sg < 8; ++sg) {
-    uint32_t byte = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int el = 4 * sg + i;
-      const float r = e.v[el] - e2m1_value(e.q[el]);
-      byte |= offset_code(r) << (2 * i);
-    }
-    ob[sg] = byte;
+  const uint32_t ex = (want_act && a.exclude_mask && live) ? ((uint32_t)a.exclude_mask[s >> 3] >> (s & 7)) & 1u : 0u;
+  uint32_t wbyte = 0;
+  int32_t wpos = 0;
+  if (want_w && live) {
+    wbyte = a.w_mask[s >> 3];
+    wpos = a.w_prefix[s >> 3] + __popc(wbyte & ((1u << (s & 7)) - 1u));
   }
 
-  if (want_act) {
-    const uint32_t ex = a.exclude_mask ? (uint32_t)a.exclude_mask[pr] : 0u;
-    uint32_t mbits = 0;
+  for (int64_t row = blockIdx.y; row < a.rows; row += gridDim.y) {
+    float x[4] = {0.f, 0.f, 0.f, 0.f};
+    if (live) {
+      const int64_t e = row * a.k + 4 * s;
+      if (a.dtype == AUTOFP_BF16) {
+        const uint2 p = *(const uint2 *)((const uint16_t *)a.x + e);
+        x[0] = __uint_as_float(p.x << 16);
+        x[1] = __uint_as_float(p.x & 0xFFFF0000u);
+        x[2] = __uint_as_float(p.y << 16);
+        x[3] = __uint_as_float(p.y & 0xFFFF0000u);
+      } else {
+        const float4 p = *(const float4 *)((const float *)a.x + e);
+        x[0] = p.x;
+        x[1] = p.y;
+        x[2] = p.z;
+        x[3] = p.w;
+      }
+    }
+    // group scale (the quad's 16 elements)
+    const float gm = quad_max(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
+    const float b = sixT > 0.0f ? gm / sixT : 0.0f;
+    const uint32_t B = e4m3_encode(b);
+    const float sc = T * e4m3_value(B);
+    float v[4];
+    uint32_t q[4];
 #pragma unroll
-    for (int sg = 0; sg < 8; ++sg) {
+    for (int i = 0; i < 4; ++i) {
+      v[i] = (sc != 0.0f) ? x[i] / sc : 0.0f;
+      q[i] = e2m1_encode(v[i]);
+    }
+    if (live) {
+      *(uint16_t *)(a.codes + row * (a.k / 2) + 2 * s) = (uint16_t)(q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12));
+      if ((s & 3) == 0) a.scales[row * (a.k / 16) + (s >> 2)] = (uint8_t)B;
+    }
+    if (!want_act && !want_w) continue;
+
+    // offsets d = argmin |r - d/8|, r = v - q (exact in fp32)
+    uint32_t ob = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ob |= offset_code(v[i] - e2m1_value(q[i])) << (2 * i);
+
+    if (want_act) {
       float num = 0.0f, den = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int el = 4 * sg + i;
-        const float r = e.v[el] - e2m1_value(e.q[el]);
+        const float r = v[i] - e2m1_value(q[i]);
         const float rr = r * r;
-        const float vv = e.v[el] * e.v[el];
+        const float vv = v[i] * v[i];
         num = (i == 0) ? rr : num + rr;
         den = (i == 0) ? vv : den + vv;
       }
       const float thr = a.thresh * den;
-      const bool refine = (4 * sg < nel) && den > 0.0f && num > thr && !((ex >> sg) & 1u);
-      if (refine) mbits |= 1u << sg;
-      else ob[sg] = 0;
+      const bool refine = live && den > 0.0f && num > thr && !ex;
+      const uint64_t bits = __ballot(refine);
+      if (live) {
+        a.act_offsets[row * ns + s] = (uint8_t)(refine ? ob : 0u);
+        if ((s & 7) == 0) a.act_mask[row * mb + (s >> 3)] = (uint8_t)(bits >> lane);
+      }
     }
-    a.act_mask[row * P2 + pr] = (uint8_t)mbits;
-    uint8_t *odst = a.act_offsets + row * (a.k / 4) + k0 / 4;
-    if (vec_ok) {
-      *(uint2 *)odst = make_uint2(ob[0] | (ob[1] << 8) | (ob[2] << 16) | (ob[3] << 24),
-                                  ob[4] | (ob[5] << 8) | (ob[6] << 16) | (ob[7] << 24));
-    } else {
-#pragma unroll
-      for (int sg = 0; sg < 8; ++sg)
-        if (sg < nel / 4) odst[sg] = (uint8_t)ob[sg];
-    }
-  }
-  if (want_w) {
-    const uint32_t mb = a.w_mask[pr];
-    int32_t pos = a.w_prefix[pr];
-    uint8_t *odst = a.w_offsets + row * (int64_t)a.n_refined;
-#pragma unroll
-    for (int sg = 0; sg < 8; ++sg) {
-      if ((mb >> sg) & 1u) odst[pos++] = (uint8_t)ob[sg];
-    }
+    if (want_w && live && ((wbyte >> (s & 7)) & 1u)) a.w_offsets[row * (int64_t)a.n_refined + wpos] = (uint8_t)ob;
   }
 }
 
@@ -451,9 +487,17 @@ hipError_t launch_mask_prefix(const uint8_t *mask, int64_t nbytes, int32_t *pref
   return hipGetLastError();
 }
 
-hipError_t launch_encode(const EncodeArgs &a, hipStream_t s) {
-  const int64_t threads = a.rows * ((a.k + 31) / 32);
-  hipLaunchKernelGGL(encode_kernel, dim3(grid_for(threads, kThreads)), dim3(kThreads), 0, s, a);
+hipError_t launch_encode(const EncodeArgs &a, bool small, hipStream_t s) {
+  const int64_t ns = a.k / 4;
+  const int64_t gx = (ns + kEncThreads - 1) / kEncThreads;
+  // rows per block: enough blocks to fill the chip, few enough that the
+  // per-block amax fold stays small next to the encode work
+  int64_t gy = (16384 + gx - 1) / gx;
+  gy = gy < a.rows ? gy : a.rows;
+  gy = gy < 65535 ? gy : 65535;
+  const dim3 grid((unsigned)gx, (unsigned)gy);
+  if (small) hipLaunchKernelGGL(encode_kernel<true>, grid, dim3(kEncThreads), 0, s, a);
+  else hipLaunchKernelGGL(encode_kernel<false>, grid, dim3(kEncThreads), 0, s, a);
   return hipGetLastError();
 }
 

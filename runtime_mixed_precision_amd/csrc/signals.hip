@@ -1,7 +1,8 @@
 // Runtime-policy signals for gfx950 ("AutoEMatic", arXiv 2611.10165v1, §3.1):
 //   G_E  normalized Shannon entropy of the top-K next-token logits (K = 10)
 //   L_A  ||H_l - H_(l-1)||_2 / (||H_(l-1)||_2 + eps)             (Eq. 1)
-// Both are single-pass reductions, one block per row.
+// G_E reads the logits once (slices of the vocabulary in parallel, then a
+// merge of the per-slice candidates); L_A is one block per row.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -12,7 +13,10 @@ namespace afp {
 
 namespace {
 
-constexpr int kEntThreads = 512;
+constexpr int kEntThreads = 256;                 // 4 wavefronts
+constexpr int kEntPer = 16;                      // logits per thread in the slice pass
+constexpr int kEntSlice = kEntThreads * kEntPer; // logits per block in the slice pass
+constexpr int kEntWaves = kEntThreads / 64;
 
 // Insert v into a descending list of KM values (the smallest drops out).
 template <int KM>
@@ -26,165 +30,286 @@ __device__ __forceinline__ void topk_insert(float (&lst)[KM], float v) {
   }
 }
 
+// Top `top_k` values of the union of the 64 lanes' descending lists: round r
+// takes the largest list head (DPP max, lowest lane on ties) and pops it. Lane
+// r of the result holds the r-th largest value (-inf for r >= top_k).
 template <int KM>
-__global__ __launch_bounds__(kEntThreads) void entropy_topk_kernel(const float *__restrict__ logits,
-                                                                   int64_t vocab, int top_k,
-                                                                   float *__restrict__ out) {
-  const float *z = logits + (int64_t)blockIdx.x * vocab;
-  float lst[KM];
-#pragma unroll
-  for (int j = 0; j < KM; ++j) lst[j] = -INFINITY;
-  const bool vec = (vocab & 3) == 0;
-  if (vec) {
-    const float4 *z4 = (const float4 *)z;
-    for (int64_t i = threadIdx.x; i < vocab / 4; i += kEntThreads) {
-      const float4 v = z4[i];
-      if (v.x > lst[KM - 1]) topk_insert(lst, v.x);
-      if (v.y > lst[KM - 1]) topk_insert(lst, v.y);
-      if (v.z > lst[KM - 1]) topk_insert(lst, v.z);
-      if (v.w > lst[KM - 1]) topk_insert(lst, v.w);
-    }
-  } else {
-    for (int64_t i = threadIdx.x; i < vocab; i += kEntThreads) {
-      const float v = z[i];
-      if (v > lst[KM - 1]) topk_insert(lst, v);
-    }
-  }
-  // merge the per-thread sorted lists: top_k rounds of a block-wide max of the heads
-  __shared__ float wbest[kEntThreads / 64];
-  __shared__ int wowner[kEntThreads / 64];
-  __shared__ float picked[32];
+__device__ __forceinline__ float wave_topk(const float (&lst)[KM], int top_k) {
+  const int lane = threadIdx.x & 63;
   int head = 0;
+  float mine = -INFINITY;
   for (int r = 0; r < top_k; ++r) {
     float h = -INFINITY;
 #pragma unroll
     for (int j = 0; j < KM; ++j)
       if (j == head) h = lst[j];
-    float best = h;
-    int owner = threadIdx.x;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ob = __shfl_xor(best, o, 64);
-      const int oo = __shfl_xor(owner, o, 64);
-      if (ob > best || (ob == best && oo < owner)) {
-        best = ob;
-        owner = oo;
-      }
-    }
-    if ((threadIdx.x & 63) == 0) {
-      wbest[threadIdx.x >> 6] = best;
-      wowner[threadIdx.x >> 6] = owner;
-    }
-    __syncthreads();
-    float gb = wbest[0];
-    int go = wowner[0];
-    for (int w = 1; w < kEntThreads / 64; ++w) {
-      if (wbest[w] > gb || (wbest[w] == gb && wowner[w] < go)) {
-        gb = wbest[w];
-        go = wowner[w];
-      }
-    }
-    if ((int)threadIdx.x == go) ++head;
-    if (threadIdx.x == 0) picked[r] = gb;
-    __syncthreads();
+    const uint32_t hu = f32_order(h);
+    const uint32_t best = wave_max_u32(hu);
+    const uint64_t who = __ballot(hu == best);
+    const int owner = __ffsll((unsigned long long)who) - 1;
+    if (lane == owner) ++head;
+    if (lane == r) mine = f32_unorder(best);
   }
-  if (threadIdx.x == 0) {
-    const double m = (double)picked[0];
-    double s = 0.0, s1 = 0.0;
-    for (int r = 0; r < top_k; ++r) {
-      const double t = (double)picked[r] - m;
-      const double e = exp(t);
-      s += e;
-      s1 += t * e;
+  return mine;
+}
+
+// Top `top_k` values of a block's per-thread lists, in lanes 0 .. top_k - 1 of
+// wavefront 0 (other lanes and wavefronts: -inf).
+template <int KM>
+__device__ __forceinline__ float block_topk(const float (&lst)[KM], int top_k) {
+  __shared__ float wtop[kEntWaves * KM];
+  const int lane = threadIdx.x & 63;
+  const float t = wave_topk(lst, top_k);
+  if (lane < top_k) wtop[(threadIdx.x >> 6) * top_k + lane] = t;
+  __syncthreads();
+  float l2[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) l2[j] = -INFINITY;
+  if (threadIdx.x < 64)
+    for (int i = lane; i < kEntWaves * top_k; i += 64) topk_insert(l2, wtop[i]);
+  return threadIdx.x < 64 ? wave_topk(l2, top_k) : -INFINITY;
+}
+
+// Slice pass: block (s, row) reads logits [s * kEntSlice, (s + 1) * kEntSlice)
+// of its row once and writes its top_k values to cand[row][s][0 .. top_k).
+template <int KM>
+__global__ __launch_bounds__(kEntThreads) void entropy_slice_kernel(const float *__restrict__ logits,
+                                                                    int64_t vocab, int top_k,
+                                                                    float *__restrict__ cand) {
+  const int64_t row = blockIdx.y;
+  const float *z = logits + row * vocab;
+  const int64_t base = (int64_t)blockIdx.x * kEntSlice;
+  float v[kEntPer];
+  if ((vocab & 3) == 0) {
+    // 4 x 16-byte loads per thread, all issued before any is used
+#pragma unroll
+    for (int j = 0; j < kEntPer / 4; ++j) {
+      const int64_t i = base + 4 * (threadIdx.x + (int64_t)j * kEntThreads);
+      float4 q = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      if (i < vocab) q = *(const float4 *)(z + i);
+      v[4 * j] = q.x;
+      v[4 * j + 1] = q.y;
+      v[4 * j + 2] = q.z;
+      v[4 * j + 3] = q.w;
     }
-    const double h = log(s) - s1 / s;
-    out[blockIdx.x] = top_k > 1 ? (float)(h / log((double)top_k)) : 0.0f;
+  } else {
+#pragma unroll
+    for (int j = 0; j < kEntPer; ++j) {
+      const int64_t i = base + threadIdx.x + (int64_t)j * kEntThreads;
+      v[j] = i < vocab ? z[i] : -INFINITY;
+    }
+  }
+  float lst[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) lst[j] = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kEntPer; ++j) topk_insert(lst, v[j]);
+  const float t = block_topk(lst, top_k);
+  if (threadIdx.x < (unsigned)top_k) cand[(row * gridDim.x + blockIdx.x) * top_k + threadIdx.x] = t;
+}
+
+// Merge pass: one wavefront per row over its n_cand candidates, then
+// G_E = (ln S - S1 / S) / ln(top_k) with S = sum e^(z - m), S1 = sum (z - m) e^(z - m)
+// over the top_k values (m the largest), in fp64.
+template <int KM>
+__global__ __launch_bounds__(64) void entropy_merge_kernel(const float *__restrict__ cand,
+                                                           int64_t n_cand, int top_k,
+                                                           float *__restrict__ out) {
+  const float *c = cand + (int64_t)blockIdx.x * n_cand;
+  const int lane = threadIdx.x;
+  float lst[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) lst[j] = -INFINITY;
+  for (int64_t i0 = lane; i0 < n_cand; i0 += 8 * 64) {
+    float v[8];   // eight independent loads in flight
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (i0 + 64 * u < n_cand) ? c[i0 + 64 * u] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) topk_insert(lst, v[u]);
+  }
+  const float f = wave_topk(lst, top_k);
+  const double m = (double)__shfl(f, 0, 64);
+  double e = 0.0, te = 0.0;
+  if (lane < top_k) {
+    const double d = (double)f - m;
+    e = exp(d);
+    te = d * e;
+  }
+  const double S = wave_sum_d(e);
+  const double S1 = wave_sum_d(te);
+  if (lane == 0) out[blockIdx.x] = top_k > 1 ? (float)((log(S) - S1 / S) / log((double)top_k)) : 0.0f;
+}
+
+// Whole-vocabulary entropy, slice pass: per block (m, S, S1) with
+// S = sum e^(z - m), S1 = sum (z - m) e^(z - m) over its slice (fp64).
+struct LseAcc {
+  double m, s, s1;
+};
+
+__device__ __forceinline__ LseAcc lse_merge(LseAcc a, LseAcc b) {
+  if (a.m == -INFINITY) return b;
+  if (b.m == -INFINITY) return a;
+  const double mm = fmax(a.m, b.m);
+  const double ea = exp(a.m - mm), eb = exp(b.m - mm);
+  LseAcc r;
+  r.m = mm;
+  r.s = ea * a.s + eb * b.s;
+  r.s1 = ea * (a.s1 + (a.m - mm) * a.s) + eb * (b.s1 + (b.m - mm) * b.s);
+  return r;
+}
+
+__device__ __forceinline__ LseAcc wave_lse(LseAcc a) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    LseAcc b;
+    b.m = __shfl_xor(a.m, o, 64);
+    b.s = __shfl_xor(a.s, o, 64);
+    b.s1 = __shfl_xor(a.s1, o, 64);
+    a = lse_merge(a, b);
+  }
+  return a;
+}
+
+__device__ LseAcc block_lse(LseAcc a) {
+  __shared__ double sm[kEntWaves][3];
+  a = wave_lse(a);
+  if ((threadIdx.x & 63) == 0) {
+    sm[threadIdx.x >> 6][0] = a.m;
+    sm[threadIdx.x >> 6][1] = a.s;
+    sm[threadIdx.x >> 6][2] = a.s1;
+  }
+  __syncthreads();
+  LseAcc r{-INFINITY, 0.0, 0.0};
+  for (int w = 0; w < kEntWaves; ++w) r = lse_merge(r, LseAcc{sm[w][0], sm[w][1], sm[w][2]});
+  return r;
+}
+
+__global__ __launch_bounds__(kEntThreads) void entropy_full_slice_kernel(const float *__restrict__ logits,
+                                                                         int64_t vocab,
+                                                                         double *__restrict__ part) {
+  const int64_t row = blockIdx.y;
+  const float *z = logits + row * vocab;
+  const int64_t base = (int64_t)blockIdx.x * kEntSlice;
+  float v[kEntPer];
+#pragma unroll
+  for (int j = 0; j < kEntPer; ++j) {
+    const int64_t i = base + threadIdx.x + (int64_t)j * kEntThreads;
+    v[j] = i < vocab ? z[i] : -INFINITY;
+  }
+  double m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kEntPer; ++j) m = fmax(m, (double)v[j]);
+  LseAcc a{m, 0.0, 0.0};
+  if (m != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < kEntPer; ++j) {
+      if (v[j] != -INFINITY) {
+        const double t = (double)v[j] - m;
+        const double e = exp(t);
+        a.s += e;
+        a.s1 += t * e;
+      }
+    }
+  }
+  a = block_lse(a);
+  if (threadIdx.x == 0) {
+    double *p = part + 3 * (row * gridDim.x + blockIdx.x);
+    p[0] = a.m;
+    p[1] = a.s;
+    p[2] = a.s1;
   }
 }
 
-// Whole-vocabulary entropy with an online log-sum-exp: per thread
-// (m, S = sum e^(z-m), S1 = sum (z-m) e^(z-m)); H = ln S - S1 / S.
-__global__ __launch_bounds__(kEntThreads) void entropy_full_kernel(const float *__restrict__ logits,
-                                                                   int64_t vocab,
-                                                                   float *__restrict__ out) {
-  const float *z = logits + (int64_t)blockIdx.x * vocab;
-  double m = -INFINITY, s = 0.0, s1 = 0.0;
-  for (int64_t i = threadIdx.x; i < vocab; i += kEntThreads) {
-    const double v = (double)z[i];
-    if (v > m) {
-      const double sc = (m == -INFINITY) ? 0.0 : exp(m - v);
-      s1 = (m == -INFINITY) ? 0.0 : sc * (s1 + (m - v) * s);
-      s = sc * s + 1.0;
-      m = v;
-    } else {
-      const double t = v - m;
-      const double e = exp(t);
-      s += e;
-      s1 += t * e;
-    }
-  }
-  __shared__ double sm[kEntThreads], ss[kEntThreads], ss1[kEntThreads];
-  sm[threadIdx.x] = m;
-  ss[threadIdx.x] = s;
-  ss1[threadIdx.x] = s1;
-  __syncthreads();
-  for (int half = kEntThreads / 2; half > 0; half >>= 1) {
-    if ((int)threadIdx.x < half) {
-      const double ma = sm[threadIdx.x], mb = sm[threadIdx.x + half];
-      const double sa = ss[threadIdx.x], sb = ss[threadIdx.x + half];
-      const double s1a = ss1[threadIdx.x], s1b = ss1[threadIdx.x + half];
-      const double mm = fmax(ma, mb);
-      double rs = 0.0, rs1 = 0.0;
-      if (ma != -INFINITY) {
-        const double ea = exp(ma - mm);
-        rs += ea * sa;
-        rs1 += ea * (s1a + (ma - mm) * sa);
-      }
-      if (mb != -INFINITY) {
-        const double eb = exp(mb - mm);
-        rs += eb * sb;
-        rs1 += eb * (s1b + (mb - mm) * sb);
-      }
-      sm[threadIdx.x] = mm;
-      ss[threadIdx.x] = rs;
-      ss1[threadIdx.x] = rs1;
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    const double h = log(ss[0]) - ss1[0] / ss[0];
-    out[blockIdx.x] = vocab > 1 ? (float)(h / log((double)vocab)) : 0.0f;
-  }
+__global__ __launch_bounds__(kEntThreads) void entropy_full_merge_kernel(const double *__restrict__ part,
+                                                                         int64_t n_part, int64_t vocab,
+                                                                         float *__restrict__ out) {
+  const double *p = part + 3 * (int64_t)blockIdx.x * n_part;
+  LseAcc a{-INFINITY, 0.0, 0.0};
+  for (int64_t i = threadIdx.x; i < n_part; i += kEntThreads)
+    a = lse_merge(a, LseAcc{p[3 * i], p[3 * i + 1], p[3 * i + 2]});
+  a = block_lse(a);
+  if (threadIdx.x == 0) out[blockIdx.x] = vocab > 1 ? (float)((log(a.s) - a.s1 / a.s) / log((double)vocab)) : 0.0f;
 }
 
 __device__ __forceinline__ float load_h(const void *p, int dtype, int64_t i) {
   return dtype == AUTOFP_BF16 ? bf16_to_f32(((const uint16_t *)p)[i]) : ((const float *)p)[i];
 }
 
-__global__ __launch_bounds__(256) void update_norm_kernel(const void *__restrict__ hp,
-                                                          const void *__restrict__ hc, int dtype,
-                                                          int64_t hidden, float eps,
-                                                          float *__restrict__ out) {
+// 8 consecutive hidden-state values as fp32 (16- or 32-byte aligned vector loads)
+__device__ __forceinline__ void load8_h(const void *p, int dtype, int64_t i8, float (&v)[8]) {
+  if (dtype == AUTOFP_BF16) {
+    const uint4 q = ((const uint4 *)p)[i8];
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(w[j] << 16);
+      v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 a = ((const float4 *)p)[2 * i8];
+    const float4 b = ((const float4 *)p)[2 * i8 + 1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+constexpr int kNormThreads = 256;
+constexpr int kNormUnroll = 4;   // vectors of 8 per thread loaded before any is used
+
+__global__ __launch_bounds__(kNormThreads) void update_norm_kernel(const void *__restrict__ hp,
+                                                                   const void *__restrict__ hc, int dtype,
+                                                                   int64_t hidden, float eps,
+                                                                   float *__restrict__ out) {
   const int64_t base = (int64_t)blockIdx.x * hidden;
   double num = 0.0, den = 0.0;
-  for (int64_t i = threadIdx.x; i < hidden; i += 256) {
-    const float p = load_h(hp, dtype, base + i);
-    const float c = load_h(hc, dtype, base + i);
-    const double d = (double)c - (double)p;
-    num += d * d;
-    den += (double)p * (double)p;
+  if ((hidden & 7) == 0 && (((uintptr_t)hp | (uintptr_t)hc) & 15) == 0) {
+    const int64_t n8 = hidden / 8, b8 = base / 8;
+    for (int64_t i0 = threadIdx.x; i0 < n8; i0 += kNormUnroll * kNormThreads) {
+      float p[kNormUnroll][8], c[kNormUnroll][8];
+#pragma unroll
+      for (int u = 0; u < kNormUnroll; ++u) {
+        const int64_t i = i0 + (int64_t)u * kNormThreads;
+        if (i < n8) {
+          load8_h(hp, dtype, b8 + i, p[u]);
+          load8_h(hc, dtype, b8 + i, c[u]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) p[u][j] = c[u][j] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kNormUnroll; ++u) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const double d = (double)c[u][j] - (double)p[u][j];
+          num += d * d;
+          den += (double)p[u][j] * (double)p[u][j];
+        }
+      }
+    }
+  } else {
+    for (int64_t i = threadIdx.x; i < hidden; i += kNormThreads) {
+      const float p = load_h(hp, dtype, base + i);
+      const float c = load_h(hc, dtype, base + i);
+      const double d = (double)c - (double)p;
+      num += d * d;
+      den += (double)p * (double)p;
+    }
   }
   num = wave_sum_d(num);
   den = wave_sum_d(den);
-  __shared__ double rn[4], rd[4];
+  __shared__ double rn[kNormThreads / 64], rd[kNormThreads / 64];
   if ((threadIdx.x & 63) == 0) {
     rn[threadIdx.x >> 6] = num;
     rd[threadIdx.x >> 6] = den;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    const double n = rn[0] + rn[1] + rn[2] + rn[3];
-    const double d = rd[0] + rd[1] + rd[2] + rd[3];
+    double n = 0.0, d = 0.0;
+    for (int w = 0; w < kNormThreads / 64; ++w) {
+      n += rn[w];
+      d += rd[w];
+    }
     out[blockIdx.x] = (float)(sqrt(n) / (sqrt(d) + (double)eps));
   }
 }
@@ -289,24 +414,40 @@ hipError_t launch_policy_update(const PolicyArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+int64_t entropy_slices(int64_t vocab) { return (vocab + kEntSlice - 1) / kEntSlice; }
+
+size_t entropy_workspace_bytes(int64_t batch, int64_t vocab) {
+  const size_t topk = (size_t)batch * (size_t)entropy_slices(vocab) * 32 * sizeof(float);
+  const size_t full = (size_t)batch * (size_t)entropy_slices(vocab) * 3 * sizeof(double);
+  return topk > full ? topk : full;
+}
+
 hipError_t launch_entropy(const float *logits, int64_t batch, int64_t vocab, int top_k, float *out,
-                          hipStream_t s) {
+                          void *ws, hipStream_t s) {
+  const int64_t ns = entropy_slices(vocab);
+  const dim3 grid((unsigned)ns, (unsigned)batch);
   if (top_k >= vocab) {
-    hipLaunchKernelGGL(entropy_full_kernel, dim3((unsigned)batch), dim3(kEntThreads), 0, s, logits,
-                       vocab, out);
+    hipLaunchKernelGGL(entropy_full_slice_kernel, grid, dim3(kEntThreads), 0, s, logits, vocab,
+                       (double *)ws);
+    hipLaunchKernelGGL(entropy_full_merge_kernel, dim3((unsigned)batch), dim3(kEntThreads), 0, s,
+                       (const double *)ws, ns, vocab, out);
   } else if (top_k <= 10) {
-    hipLaunchKernelGGL(entropy_topk_kernel<10>, dim3((unsigned)batch), dim3(kEntThreads), 0, s,
-                       logits, vocab, top_k, out);
+    hipLaunchKernelGGL(entropy_slice_kernel<10>, grid, dim3(kEntThreads), 0, s, logits, vocab, top_k,
+                       (float *)ws);
+    hipLaunchKernelGGL(entropy_merge_kernel<10>, dim3((unsigned)batch), dim3(64), 0, s,
+                       (const float *)ws, ns * top_k, top_k, out);
   } else {
-    hipLaunchKernelGGL(entropy_topk_kernel<32>, dim3((unsigned)batch), dim3(kEntThreads), 0, s,
-                       logits, vocab, top_k, out);
+    hipLaunchKernelGGL(entropy_slice_kernel<32>, grid, dim3(kEntThreads), 0, s, logits, vocab, top_k,
+                       (float *)ws);
+    hipLaunchKernelGGL(entropy_merge_kernel<32>, dim3((unsigned)batch), dim3(64), 0, s,
+                       (const float *)ws, ns * top_k, top_k, out);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_update_norm(const void *h_prev, const void *h_cur, int dtype, int64_t batch,
                               int64_t hidden, float eps, float *out, hipStream_t s) {
-  hipLaunchKernelGGL(update_norm_kernel, dim3((unsigned)batch), dim3(256), 0, s, h_prev, h_cur, dtype,
+  hipLaunchKernelGGL(update_norm_kernel, dim3((unsigned)batch), dim3(kNormThreads), 0, s, h_prev, h_cur, dtype,
                      hidden, eps, out);
   return hipGetLastError();
 }

@@ -139,7 +139,7 @@ def test_linear_rejects_bad_arguments(N):
 def test_signals_reject_bad_arguments(N):
     L = N.lib()
     p = params(N)
-    sig = lambda *a: L.autofp_policy_signals(*a, None)
+    sig = lambda *a, ws=FAKE, wsb=1 << 30: L.autofp_policy_signals(*a, ws, wsb, None)
     assert sig(FAKE, 1, 100, None, None, N.F32, 0, C.byref(p), None, None) == 1
     assert sig(None, 1, 100, None, None, N.F32, 0, C.byref(p), FAKE, None) == 1
     p.top_k = 40
@@ -147,6 +147,24 @@ def test_signals_reject_bad_arguments(N):
     p.top_k = 10
     assert sig(None, 1, 0, FAKE, FAKE, 3, 64, C.byref(p), None, FAKE) == 7
     assert sig(None, 0, 0, FAKE, FAKE, N.F32, 64, C.byref(p), None, FAKE) == 2
+    # G_E needs the slice workspace; L_A alone does not
+    need = C.c_size_t()
+    assert L.autofp_workspace_bytes(N.OP_SIGNALS, 2, 128256, C.byref(need)) == 0
+    assert sig(FAKE, 2, 128256, None, None, N.F32, 0, C.byref(p), FAKE, None, ws=None) == 5
+    assert sig(FAKE, 2, 128256, None, None, N.F32, 0, C.byref(p), FAKE, None, wsb=need.value - 1) == 5
+    assert sig(FAKE, 70000, 100, None, None, N.F32, 0, C.byref(p), FAKE, None) == 2
+
+
+def test_signals_workspace_size(N):
+    L = N.lib()
+    b = C.c_size_t()
+    # one candidate list of up to 32 floats per 4096-logit slice
+    for batch, vocab in ((1, 128256), (64, 128256), (3, 50257), (1, 1)):
+        assert L.autofp_workspace_bytes(N.OP_SIGNALS, batch, vocab, C.byref(b)) == 0
+        slices = -(-vocab // 4096)
+        assert b.value >= batch * slices * 32 * 4
+    assert L.autofp_workspace_bytes(N.OP_SIGNALS, 0, 100, C.byref(b)) == 2
+    assert L.autofp_workspace_bytes(N.OP_SIGNALS, 1, 0, C.byref(b)) == 2
 
 
 def test_policy_update_rejects_bad_arguments(N):

@@ -65,6 +65,22 @@ def test_activation_encode_config1(dtype, refine):
     assert_same_packed(pk, ref)
 
 
+@pytest.mark.parametrize("shape", [(1, 4096), (8, 14336), (8192, 16), (8193, 16), (16, 14336), (3, 65536)])
+def test_activation_encode_one_and_two_launch_paths(shape):
+    """Decode-step activation shapes on both sides of the single-launch limit
+    (2^17 elements): bit-exact codes, scales, T, mask and offsets."""
+    rows, k = shape
+    say(f"case: activation encode {rows}x{k} (bf16, refine, exclusion mask)")
+    x = S.activations(rows, k, seed=rows + k, tensor_id=3, dtype=torch.bfloat16, device=DEV)
+    g = torch.Generator().manual_seed(k)
+    excl = torch.randint(0, 256, ((k + 31) // 32,), generator=g, dtype=torch.uint8).to(DEV)
+    pk = A.quantize_activation(x, refine=True, exclude_mask=excl)
+    ref = O.quantize_activation(x.float().cpu().numpy(), refine=True, exclude_mask=excl.cpu().numpy())
+    assert_same_packed(pk, ref)
+    pk4 = A.quantize_activation(x, refine=False)
+    assert_same_packed(pk4, O.quantize_activation(x.float().cpu().numpy(), refine=False))
+
+
 @pytest.mark.parametrize("shape,rho", [((256, 256), 0.2), ((48, 272), 0.2), ((300, 512), 0.35),
                                        ((7, 32), 0.5)])
 def test_weight_mask_and_encode(shape, rho):

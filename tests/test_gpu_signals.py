@@ -26,7 +26,8 @@ def close(a, b):
     assert (np.abs(a - b) <= 1e-3 * np.abs(b) + 1e-6).all(), (a, b)
 
 
-@pytest.mark.parametrize("batch,vocab", [(1, S.VOCAB), (4, S.VOCAB), (64, S.VOCAB), (3, 1000), (2, 37), (5, 130)])
+@pytest.mark.parametrize("batch,vocab", [(1, S.VOCAB), (4, S.VOCAB), (64, S.VOCAB), (3, 1000), (2, 37), (5, 130),
+                                         (2, 8192), (2, 8195), (1, 4097)])
 @pytest.mark.parametrize("top_k", [10, 1, 32, None])
 def test_entropy(batch, vocab, top_k):
     k = vocab if top_k is None else top_k
@@ -46,6 +47,40 @@ def test_entropy_ties_and_extremes():
     g, _ = A.policy_signals(logits=z)
     close(g.cpu().numpy(), O.topk_entropy(z.cpu().numpy(), 10))
     assert abs(float(g[0]) - 1.0) < 1e-6 and float(g[1]) < 1e-6
+
+
+@pytest.mark.parametrize("top_k", [10, 32])
+def test_entropy_leaders_in_one_place(top_k):
+    """All leaders in the 16 logits one thread reads, or in the last, partial slice."""
+    say(f"case: entropy concentrated leaders k={top_k}")
+    V = S.VOCAB
+    z = S.logits(3, V, seed=11, device=DEV)
+    one_thread = [4 * 5 + i + 1024 * j for j in range(4) for i in range(4)]   # thread 5 of slice 0
+    z[0, one_thread] = 40.0 + torch.arange(16, device=DEV, dtype=torch.float32) * 0.25
+    z[1, V - 40:] = 30.0 + torch.arange(40, device=DEV, dtype=torch.float32) * 0.1
+    z[2, 4096 * 7 + 64 * 3: 4096 * 7 + 64 * 3 + 40] = 25.0                    # one wavefront's range, tied
+    g, _ = A.policy_signals(logits=z, params=A.default_params(top_k=top_k))
+    close(g.cpu().numpy(), O.topk_entropy(z.cpu().numpy(), top_k))
+
+
+def test_entropy_workspace_reuse():
+    say("case: entropy workspace reused across shapes")
+    ws = torch.empty(A.workspace_bytes(4, 8, S.VOCAB), dtype=torch.uint8, device=DEV)
+    for b, v in ((8, S.VOCAB), (2, 5000), (8, S.VOCAB)):
+        z = S.logits(b, v, seed=b * v, device=DEV)
+        g, _ = A.policy_signals(logits=z, workspace=ws)
+        close(g.cpu().numpy(), O.topk_entropy(z.cpu().numpy(), 10))
+
+
+def test_update_norm_unaligned_rows():
+    say("case: L_A on views that are not 16-byte aligned")
+    base = S.hidden(4, 4097, seed=5, tensor_id=0, device=DEV)
+    hp = base[:, 1:]                                   # row stride 4097, offset 1 element
+    hc = (hp + 0.2).contiguous()[:, :]
+    hp2 = torch.empty(4 * 4096 + 1, device=DEV)[1:].view(4, 4096)
+    hp2.copy_(hp)
+    _, la = A.policy_signals(h_prev=hp2, h_cur=hc)
+    close(la.cpu().numpy(), O.update_norm(hp2.cpu().numpy(), hc.cpu().numpy(), 1e-6))
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
