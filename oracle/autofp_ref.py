@@ -413,8 +413,8 @@ def quantize_activation(x, refine=False, exclude_mask=None, thresh=0.003, tensor
 def quantize_weight(w, mask=None, tensor_amax=None):
     """Encode a weight W [N, K] (fp32): NVFP4 base; with a packed weight mask
     [K/32] also the compacted offsets [N, R]: for every row, one byte per
-    refined subgroup in ascending (group, subgroup) order ([AE] §4: "signed
-    offsets d stored as one byte per refined subgroup"; Fig. 23)."""
+    refined subgroup in ascending (group, subgroup) order ([AE] §4 stores the
+    signed offsets of each refined subgroup in a byte of their own; Fig. 23)."""
     base = nvfp4_quantize(w, tensor_amax)
     N, K = base.codes.shape
     out = dict(codes=pack_nibbles(base.codes), scales=base.scales.copy(), T=base.T,

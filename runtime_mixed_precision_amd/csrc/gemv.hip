@@ -19,7 +19,7 @@
 // [64*(l/16), 64*(l/16)+64): 32 bytes of codes (two 16-byte loads, so the 4
 // lanes of a row read one full 128-byte line), 4 scale bytes (one dword) and,
 // at level 6, a window of up to 8 compacted offset bytes. Each wavefront keeps
-// kInflight chunks of loads in flight. The activation operand comes from an
+// 4 or 8 chunks of loads in flight. The activation operand comes from an
 // fp16 copy of the decoded activations: in LDS when it fits (the block decodes
 // it once, overlapped with the first weight loads), otherwise from an fp16
 // panel in the workspace that a small pre-pass writes. Partial 16x16 tiles of
@@ -45,7 +45,7 @@ typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 
 constexpr int kCh = 256;         // K elements per chunk
-constexpr int kInflight = 4;     // chunks of weight loads in flight per wavefront
+constexpr int kGroup = 4;        // chunks per scale load group
 constexpr int kMaxWaves = 16;    // wavefronts per block (1024 threads)
 constexpr int kPlanChunks = 16;  // chunks per wavefront covered by its offset plan
 constexpr int kProItems = 4;     // activation items (8 elements) per thread loaded by the block prologue
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void act_dequant_kernel(LinearArgs a) {
 // Every global read goes through a buffer resource covering the block's rows,
 // so rows past the end of the weight and chunks past a wavefront's range read
 // as zero (an out-of-range offset) instead of branching: each chunk issues the
-// same loads, which lets the compiler keep kInflight chunks in flight.
+// same loads, which lets the compiler keep a fixed number of chunks in flight.
 
 constexpr uint32_t kOOB = 0x80000000u;   // buffer offset that is always out of range
 constexpr int64_t kLutBytes = 256 * 8;   // delta table
@@ -212,8 +212,11 @@ __device__ __forceinline__ void vmem_fence() { __builtin_amdgcn_sched_barrier(0x
 // One block: RT row tiles of 16 rows x WK wavefronts per tile (RT * WK
 // wavefronts, blockDim = 64 * RT * WK). Wavefront w works on tile w / WK and
 // on the (w % WK)-th contiguous range of 256-element chunks of K.
-template <int L, bool XLDS, bool FAST>
+// PD chunks of weight loads are kept in flight per wavefront (4 or 8).
+template <int L, bool XLDS, bool FAST, int PD>
 __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *lds) {
+  static_assert(PD % kGroup == 0, "whole scale load groups");
+  constexpr int NG = PD / kGroup;   // scale load groups in flight
   constexpr bool REF = (L == 6);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -296,19 +299,20 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
   // row's scales arrive as 64 contiguous bytes - and a 4 x 4 transpose across
   // the lane groups (v_permlane32_swap, v_permlane16_swap) leaves in register
   // u of lane (r, ks) the 4 scale bytes of its groups in chunk g + u.
-  static_assert(kInflight == 4, "the scale transpose assumes 4 chunks per load group");
-  uint32_t sc_nxt[4] = {0, 0, 0, 0}, sc_cur[4] = {0, 0, 0, 0};
-  auto load_scales = [&](int64_t g) {
+  static_assert(kGroup == 4, "the scale transpose assumes 4 chunks per load group");
+  uint32_t sc_ring[NG][4] = {}, sc_cur[4] = {0, 0, 0, 0};
+  auto load_scales = [&](int64_t g, int slot) {
     if (!FAST) return;
     const int64_t c = g + ks;
     const uint32_t vo = (c < c1) ? (uint32_t)(r * (K >> 4) + 16 * c) : kOOB;
     const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rsc, (int)vo, 0, 0);
-    sc_nxt[0] = v[0]; sc_nxt[1] = v[1]; sc_nxt[2] = v[2]; sc_nxt[3] = v[3];
+    sc_ring[slot][0] = v[0]; sc_ring[slot][1] = v[1]; sc_ring[slot][2] = v[2]; sc_ring[slot][3] = v[3];
   };
-  auto transpose_scales = [&]() {
+  auto transpose_scales = [&](int slot) {
     if (!FAST) return;
-    const auto a = __builtin_amdgcn_permlane32_swap(sc_nxt[0], sc_nxt[2], false, false);
-    const auto b = __builtin_amdgcn_permlane32_swap(sc_nxt[1], sc_nxt[3], false, false);
+    const uint32_t *sn = sc_ring[slot];
+    const auto a = __builtin_amdgcn_permlane32_swap(sn[0], sn[2], false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(sn[1], sn[3], false, false);
     const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
     const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
     sc_cur[0] = c[0]; sc_cur[1] = c[1]; sc_cur[2] = d[0]; sc_cur[3] = d[1];
@@ -354,11 +358,11 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
   //    every step finding the same loads in flight, oldest buffer first. At
   //    level 6 the offsets of a chunk follow its codes, so those loads wait
   //    for the offset plan (step 3).
-  WChunk buf[kInflight];
+  WChunk buf[PD];
   if (!REF) {
-    load_scales(c0);
 #pragma unroll
-    for (int u = 0; u < kInflight; ++u) {
+    for (int u = 0; u < PD; ++u) {
+      if (u % kGroup == 0) load_scales(c0 + u, u / kGroup);
       load_codes(c0 + u, buf[u]);
       vmem_fence();
     }
@@ -436,9 +440,9 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
     build_plan(before);
   }
   if (REF) {
-    load_scales(c0);
 #pragma unroll
-    for (int u = 0; u < kInflight; ++u) {
+    for (int u = 0; u < PD; ++u) {
+      if (u % kGroup == 0) load_scales(c0 + u, u / kGroup);
       load_codes(c0 + u, buf[u]);
       offsets_load(c0 + u, buf[u]);
       vmem_fence();
@@ -526,20 +530,24 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
     }
   };
 
-  // One load group: process kInflight buffered chunks, each followed by the
-  // refill of its buffer kInflight chunks ahead, so kInflight - 1 chunks stay
-  // in flight while a chunk is computed.
-  for (int64_t g = c0; g < c1; g += kInflight) {
-    transpose_scales();
+  // PD buffered chunks per step, each processed and then refilled with the
+  // chunk PD ahead, so PD - 1 chunks stay in flight while one is computed;
+  // each scale load group is loaded with the first chunk of its group.
+  for (int64_t g = c0; g < c1; g += PD) {
 #pragma unroll
-    for (int u = 0; u < kInflight; ++u) {
-      const int64_t c = g + u;
-      if (c < c1) process(c, buf[u], FAST ? sc_cur[u] : buf[u].s);
-      vmem_fence();
-      if (u == 0) load_scales(g + kInflight);
-      load_codes(c + kInflight, buf[u]);
-      if (REF) offsets_load(c + kInflight, buf[u]);   // unconditional loads: uniform waits
-      vmem_fence();
+    for (int j = 0; j < NG; ++j) {
+      transpose_scales(j);
+#pragma unroll
+      for (int u = 0; u < kGroup; ++u) {
+        const int b = kGroup * j + u;
+        const int64_t c = g + b;
+        if (c < c1) process(c, buf[b], FAST ? sc_cur[u] : buf[b].s);
+        vmem_fence();
+        if (u == 0) load_scales(c + PD, j);
+        load_codes(c + PD, buf[b]);
+        if (REF) offsets_load(c + PD, buf[b]);   // unconditional loads: uniform waits
+        vmem_fence();
+      }
     }
   }
 
@@ -573,13 +581,15 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
   }
 }
 
-template <bool XLDS, bool FAST>
-__global__ __launch_bounds__(1024) void gemv_stream_kernel(LinearArgs a) {
+// PD = 4: blocks of up to 1024 threads, 128 VGPRs; PD = 8: up to 512 threads,
+// 256 VGPRs (two wavefronts per SIMD).
+template <bool XLDS, bool FAST, int PD>
+__global__ __launch_bounds__(PD == 8 ? 512 : 1024) void gemv_stream_kernel(LinearArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int L = run_level(a);
-  if (L == 6) stream_tile<6, XLDS, FAST>(a, lds);
-  else if (L == 2) stream_tile<2, XLDS, FAST>(a, lds);
-  else stream_tile<4, XLDS, FAST>(a, lds);
+  if (L == 6) stream_tile<6, XLDS, FAST, PD>(a, lds);
+  else if (L == 2) stream_tile<2, XLDS, FAST, PD>(a, lds);
+  else stream_tile<4, XLDS, FAST, PD>(a, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -771,6 +781,7 @@ struct StreamCfg {
   int waves;   // wavefronts per block = rt * wk
   int wk;      // wavefronts per row tile (K split)
   int rt;      // row tiles per block
+  int pd;      // chunks in flight per wavefront (4 or 8)
   bool xlds;
   bool fast;
   size_t lds;
@@ -793,11 +804,11 @@ StreamCfg stream_cfg(const LinearArgs &a) {
   StreamCfg c{};
   const int64_t nch = (a.k + kCh - 1) / kCh;
   const int64_t tiles = (a.n + 15) / 16;
-  // wavefronts per tile (K split): enough wavefronts in the grid, and every
-  // wavefront's range within one offset plan
+  // wavefronts per tile (K split): about six wavefronts per CU, at least four
+  // chunks per wavefront, and every wavefront's range within one offset plan
   int wk = 1;
-  const int64_t want = 2048;   // ~8 wavefronts per CU
-  while (wk < kMaxWaves && tiles * wk < want && nch / (2 * wk) >= 2) wk <<= 1;
+  const int64_t want = 1536;
+  while (wk < kMaxWaves && tiles * wk < want && nch / (2 * wk) >= 4) wk <<= 1;
   if (a.waves > 0) wk = a.waves;
   while (wk < kMaxWaves && (nch + wk - 1) / wk > kPlanChunks) wk <<= 1;
   // row tiles per block: share the LDS activation copy among up to 16 wavefronts
@@ -806,6 +817,9 @@ StreamCfg stream_cfg(const LinearArgs &a) {
   c.wk = wk;
   c.rt = rt;
   c.waves = wk * rt;
+  // 4 chunks in flight per wavefront: 8 (at two wavefronts per SIMD, 256
+  // VGPRs) measured slower on every decode shape
+  c.pd = 4;
   c.fast = (a.k % kCh) == 0;
   const size_t lut = (size_t)kLutBytes;
   const size_t red = (size_t)c.waves * 64 * sizeof(float4v);
@@ -838,13 +852,10 @@ hipError_t launch_gemv(const LinearArgs &a0, hipStream_t s) {
     a1.wk = c.wk;
     const int64_t tiles = (a0.n + 15) / 16;
     const dim3 grid((unsigned)((tiles + c.rt - 1) / c.rt)), block((unsigned)(64 * c.waves));
-    if (c.xlds) {
-      if (c.fast) hipLaunchKernelGGL((gemv_stream_kernel<true, true>), grid, block, c.lds, s, a1);
-      else hipLaunchKernelGGL((gemv_stream_kernel<true, false>), grid, block, c.lds, s, a1);
-    } else {
-      if (c.fast) hipLaunchKernelGGL((gemv_stream_kernel<false, true>), grid, block, c.lds, s, a1);
-      else hipLaunchKernelGGL((gemv_stream_kernel<false, false>), grid, block, c.lds, s, a1);
-    }
+#define AFP_STREAM(X, F, P) hipLaunchKernelGGL((gemv_stream_kernel<X, F, P>), grid, block, c.lds, s, a1)
+    if (c.xlds) { if (c.fast) AFP_STREAM(true, true, 4); else AFP_STREAM(true, false, 4); }
+    else { if (c.fast) AFP_STREAM(false, true, 4); else AFP_STREAM(false, false, 4); }
+#undef AFP_STREAM
     return hipGetLastError();
   }
   // slices of at most 64 tokens

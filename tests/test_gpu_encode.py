@@ -155,3 +155,20 @@ def test_full_size_weight_sampled_rows():
     assert (h["codes"][rows] == ref["codes"]).all()
     assert (h["scales"][rows] == ref["scales"]).all()
     assert (h["offsets"][rows] == ref["offsets"]).all()
+
+
+def test_many_rows_weight_encode_row_loop():
+    """More rows than encoder blocks along the row axis (each block encodes
+    several rows): codes, scales and compacted offsets of sampled rows."""
+    say("case: weight encode 20000x256, rows looped per block")
+    w = S.weights(20000, 256, seed=4, tensor_id=5, device=DEV)
+    pk = A.quantize_weight(w, refine=True)
+    wn = w.cpu().numpy()
+    bits, _ = O.select_weight_mask(wn, 0.2)
+    rows = np.sort(np.random.default_rng(2).choice(20000, 64, replace=False))
+    rows[-1] = 19999
+    ref = O.quantize_weight(wn[rows], O.pack_nibbles(bits), tensor_amax=np.abs(wn).max())
+    h = pk.to_host()
+    assert np.float32(h["T"]) == np.float32(ref["T"])
+    for f in ("codes", "scales", "offsets"):
+        assert (h[f][rows] == ref[f]).all(), f

@@ -225,6 +225,20 @@ def test_gemv_all_scale_codes(level, b):
     check_close(y.cpu().numpy(), O.linear(wq, xq6 if level == 6 else xq4, level))
 
 
+@pytest.mark.parametrize("n,b,k,waves", [(33024, 1, 512, 0), (33024, 3, 768, 1), (8192, 2, 1024, 4)])
+def test_gemv_many_tiles(n, b, k, waves):
+    """Enough row tiles that the kernel keeps 4 rather than 8 chunks in flight
+    per wavefront (more than 2048 wavefronts), against the oracle."""
+    say(f"case: gemv many tiles N={n} B={b} K={k} waves={waves}")
+    w, x = operands(n, b, k, seed=n + k)
+    wp, xp4, xp6 = gpu_pack(w, x)
+    wq, xq4, xq6 = oracle_pack(w, x)
+    p = A.default_params(gemv_waves=waves)
+    for level in (2, 4, 6):
+        y = run(A.gemv, wp, xp4, xp6, level, params=p)
+        check_close(y.cpu().numpy(), O.linear(wq, xq6 if level == 6 else xq4, level))
+
+
 @pytest.mark.parametrize("waves", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("n,b,k", [(40, 1, 4096 + 256), (33, 3, 2304 + 64), (16, 16, 1040)])
 def test_gemv_forced_waves(waves, n, b, k):
