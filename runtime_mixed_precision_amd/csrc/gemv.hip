@@ -43,6 +43,7 @@ namespace {
 
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3v __attribute__((ext_vector_type(3)));
 
 constexpr int kCh = 256;         // K elements per chunk
 constexpr int kGroup = 4;        // chunks per scale load group
@@ -84,8 +85,8 @@ __device__ __forceinline__ uint32_t autofp2_remap(uint32_t w) {
 struct PlanEntry {
   uint32_t sel[4];
   int32_t pos;
-  uint32_t bits;    // the 16 subgroup bits of the lane group
 };
+constexpr int kPlanBytesPerWave = 64 * 20;   // 64 entries: selectors (16 B) and position (4 B)
 
 __device__ __forceinline__ PlanEntry make_entry(uint32_t m16, int32_t pos) {
   PlanEntry e;
@@ -103,7 +104,6 @@ __device__ __forceinline__ PlanEntry make_entry(uint32_t m16, int32_t pos) {
     e.sel[q] = w;
   }
   e.pos = pos;
-  e.bits = m16;
   return e;
 }
 
@@ -173,10 +173,11 @@ __global__ __launch_bounds__(256) void act_dequant_kernel(LinearArgs a) {
 // Streaming GEMV, up to 16 tokens per launch
 // ---------------------------------------------------------------------------
 //
-// Dynamic LDS layout: [delta table 256 x 8 B][XLDS: activations B x kp fp16
-// at a row pitch of kp + 8 (16 bytes of padding put the rows of different
-// tokens on different LDS banks), then a 128-byte zero row read by the lanes
-// of absent tokens]; the
+// Dynamic LDS layout: [delta table 256 x 8 B][weight-mask copy][XLDS:
+// activations B x kp fp16 at a row pitch of kp + 8 (16 bytes of padding put
+// the rows of different tokens on different LDS banks), then a 128-byte zero
+// row read by the lanes of absent tokens][level 6: each wavefront's offset
+// plan, 64 x 16 B selectors then 64 x 4 B positions]; the
 // reduction buffer W x 64 x 16 B reuses the space after the main loop.
 //
 // Every global read goes through a buffer resource covering the block's rows,
@@ -243,6 +244,11 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
   uint8_t *mlds = lds + kLutBytes;
   _Float16 *xs = (_Float16 *)(lds + kLutBytes + mask_lds_bytes(K));
   float4v *red = (float4v *)(lds + kLutBytes);
+  const int64_t xs_bytes = XLDS ? (a.b * xpitch + 64) * 2 : 0;
+  unsigned char *plan = lds + kLutBytes + mask_lds_bytes(K) + ((xs_bytes + 15) & ~(int64_t)15) +
+                        (int64_t)wave * kPlanBytesPerWave;
+  uint4 *plan_sel = (uint4 *)plan;
+  int32_t *plan_pos = (int32_t *)(plan + 64 * 16);
 
   const int64_t nb0 = rows > 0 ? n0 : 0;   // keep resource bases inside the tensors
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.w_codes + nb0 * (K >> 1), rows * (K >> 1));
@@ -408,7 +414,6 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
 
   // 3. offset plan of this wavefront (lane = 4 * chunk + lane group), from
   //    the LDS mask copy, and the first offset loads
-  PlanEntry pe{};
   const int64_t pbase = c0;
   auto build_plan = [&](int32_t pdone) {
     const int64_t ce = pbase + (lane >> 2);
@@ -421,16 +426,19 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
       const int32_t t = __shfl_up(incl, o, 64);
       if (lane >= o) incl += t;
     }
-    pe = make_entry(m16, pdone + incl - cnt);
+    const PlanEntry pe = make_entry(m16, pdone + incl - cnt);
+    plan_sel[lane] = make_uint4(pe.sel[0], pe.sel[1], pe.sel[2], pe.sel[3]);
+    plan_pos[lane] = pe.pos;
   };
+  // the 12 aligned bytes holding the lane's (at most 8) offset bytes of chunk c
   auto offsets_load = [&](int64_t c, WChunk &w) {
-    const int src = 4 * (int)(c - pbase) + ks;
-    const int32_t pos = __shfl(pe.pos, src, 64);
     const bool live = refine_w && c < c1;
+    const int32_t pos = live ? plan_pos[4 * (int)(c - pbase) + ks] : 0;
     const uint32_t al = live ? ((orow + (uint32_t)pos) & ~3u) : kOOB;
-    w.o[0] = ld_b32(ro, al);
-    w.o[1] = ld_b32(ro, al + 4);
-    w.o[2] = ld_b32(ro, al + 8);
+    const u32x3v v = __builtin_amdgcn_raw_buffer_load_b96(ro, (int)al, 0, 0);
+    w.o[0] = v[0];
+    w.o[1] = v[1];
+    w.o[2] = v[2];
   };
   if (refine_w) {
     int32_t before = 0;
@@ -462,20 +470,14 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
     const half2v s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
     const half2v s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, true);
 
-    uint32_t any = 0, wlo = 0, whi = 0;
-    int src = 0;
+    uint32_t wlo = 0, whi = 0;
+    uint4 sel = make_uint4(0, 0, 0, 0);
     if (refine_w) {
-      src = 4 * (int)(c - pbase) + ks;
-      const uint32_t b16 = __shfl(pe.bits, src, 64);
-      any = b16 | __shfl_xor(b16, 16, 64);
-      any |= __shfl_xor(any, 32, 64);
-      any = __builtin_amdgcn_readfirstlane(any);
-      if (any) {
-        const int32_t pos = __shfl(pe.pos, src, 64);
-        const uint32_t sh = (orow + (uint32_t)pos) & 3u;
-        wlo = __builtin_amdgcn_alignbyte(w.o[1], w.o[0], sh);
-        whi = __builtin_amdgcn_alignbyte(w.o[2], w.o[1], sh);
-      }
+      const int ent = 4 * (int)(c - pbase) + ks;
+      sel = plan_sel[ent];
+      const uint32_t sh = (orow + (uint32_t)plan_pos[ent]) & 3u;
+      wlo = __builtin_amdgcn_alignbyte(w.o[1], w.o[0], sh);
+      whi = __builtin_amdgcn_alignbyte(w.o[2], w.o[1], sh);
     }
 
     const _Float16 *xp = tok_ok ? xrow + c * kCh : xzero;
@@ -501,11 +503,12 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
         h[4 * i + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 2);
         h[4 * i + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 3);
       }
-      if (refine_w && (any & (0xFFu << (8 * hf)))) {
+      if (refine_w) {
         // one offset byte per subgroup slot of this half (0 where not refined)
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
-          const uint32_t E = __builtin_amdgcn_perm(whi, wlo, __shfl(pe.sel[2 * hf + qq], src, 64));
+          const uint32_t sq = (2 * hf + qq == 0) ? sel.x : (2 * hf + qq == 1) ? sel.y : (2 * hf + qq == 2) ? sel.z : sel.w;
+          const uint32_t E = __builtin_amdgcn_perm(whi, wlo, sq);
           uint2 d[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) d[t] = lut[(E >> (8 * t)) & 0xFFu];
@@ -824,9 +827,11 @@ StreamCfg stream_cfg(const LinearArgs &a) {
   const size_t lut = (size_t)kLutBytes;
   const size_t red = (size_t)c.waves * 64 * sizeof(float4v);
   const size_t msk = (size_t)mask_lds_bytes(a.k);
-  const size_t xs = (size_t)a.b * (size_t)(nch * kCh + 8) * sizeof(_Float16) + 128;
-  c.xlds = lut + (msk + xs > red ? msk + xs : red) <= (size_t)max_lds_per_block();
-  c.lds = lut + (c.xlds ? (msk + xs > red ? msk + xs : red) : (msk > red ? msk : red));
+  const size_t xs = ((size_t)a.b * (size_t)(nch * kCh + 8) * sizeof(_Float16) + 128 + 15) & ~(size_t)15;
+  const size_t plan = a.w_mask ? (size_t)c.waves * kPlanBytesPerWave : 0;
+  const size_t with_x = msk + xs + plan, without_x = msk + plan;
+  c.xlds = lut + (with_x > red ? with_x : red) <= (size_t)max_lds_per_block();
+  c.lds = lut + (c.xlds ? (with_x > red ? with_x : red) : (without_x > red ? without_x : red));
   return c;
 }
 
