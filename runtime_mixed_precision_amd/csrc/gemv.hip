@@ -49,7 +49,6 @@ constexpr int kCh = 256;         // K elements per chunk
 constexpr int kGroup = 4;        // chunks per scale load group
 constexpr int kMaxWaves = 16;    // wavefronts per block (1024 threads)
 constexpr int kPlanChunks = 16;  // chunks per wavefront covered by its offset plan
-constexpr int kProItems = 4;     // activation items (8 elements) per thread loaded by the block prologue
 constexpr int kProMask = 2;      // weight-mask dwords per thread loaded by the block prologue
 
 __device__ __forceinline__ int run_level(const LinearArgs &a) {
@@ -213,8 +212,10 @@ __device__ __forceinline__ void vmem_fence() { __builtin_amdgcn_sched_barrier(0x
 // One block: RT row tiles of 16 rows x WK wavefronts per tile (RT * WK
 // wavefronts, blockDim = 64 * RT * WK). Wavefront w works on tile w / WK and
 // on the (w % WK)-th contiguous range of 256-element chunks of K.
-// PD chunks of weight loads are kept in flight per wavefront (4 or 8).
-template <int L, bool XLDS, bool FAST, int PD>
+// PD chunks of weight loads are kept in flight per wavefront; the block
+// prologue loads up to PRO activation items (8 elements each) per thread
+// ahead of the weight loads (more fall back to a plain loop).
+template <int L, bool XLDS, bool FAST, int PD, int PRO>
 __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *lds) {
   static_assert(PD % kGroup == 0, "whole scale load groups");
   constexpr int NG = PD / kGroup;   // scale load groups in flight
@@ -332,30 +333,32 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
   const int64_t per_row = kp / 8;
   const int64_t items = XLDS ? a.b * per_row : 0;
   const int64_t mdw = refine_w ? (mbytes + 3) / 4 : 0;
-  const bool pro_static = FAST && items <= (int64_t)kProItems * nthr && mask_lds_bytes(K) <= 4 * (int64_t)kProMask * nthr;
-  uint32_t pq[kProItems], ps[kProItems], po[kProItems], pm[kProMask];
+  const bool pro_static = FAST && items <= (int64_t)PRO * nthr && mask_lds_bytes(K) <= 4 * (int64_t)kProMask * nthr;
+  uint32_t pq[PRO], ps[PRO], po[PRO], pm[kProMask];
   if (pro_static) {
     const __amdgpu_buffer_rsrc_t rxc = make_rsrc(a.x_codes, a.b * (K >> 1));
     const __amdgpu_buffer_rsrc_t rxs = make_rsrc(a.x_scales, a.b * (K >> 4));
     const __amdgpu_buffer_rsrc_t rxo = make_rsrc(refine_x ? a.x_offsets : a.x_codes, refine_x ? a.b * (K >> 2) : 0);
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(refine_w ? a.w_mask : a.w_codes, refine_w ? mbytes : 0);
-    // FAST: the LDS row pitch is K, so item i covers elements 8i .. 8i + 7
-    // of the token-major activations, i.e. code bytes 4i, scale byte i / 2
-    // and offset bytes 2i, 2i + 1.
-#pragma unroll
-    for (int j = 0; j < kProItems; ++j) {
-      const uint32_t i = threadIdx.x + (uint32_t)(j * nthr);
-      const bool live = i < (uint32_t)items;
-      pq[j] = ld_b32(rxc, live ? 4 * i : kOOB);
-      ps[j] = __builtin_amdgcn_raw_buffer_load_b8(rxs, (int)(live ? i >> 1 : kOOB), 0, 0);
-      po[j] = REF ? __builtin_amdgcn_raw_buffer_load_b16(rxo, (int)(live && refine_x ? 2 * i : kOOB), 0, 0) : 0u;
-    }
+    // the weight-mask loads first: the mask is written to LDS before the
+    // activations, so its wait leaves the activation loads in flight
     if (REF) {
 #pragma unroll
       for (int j = 0; j < kProMask; ++j) {
         const uint32_t i = threadIdx.x + (uint32_t)(j * nthr);
         pm[j] = ld_b32(rm, i < (uint32_t)mdw ? 4 * i : kOOB);
       }
+    }
+    // Item i covers elements 8i .. 8i + 7 of the token-major activations
+    // (K % 256 == 0, so no item straddles a row): code bytes 4i .. 4i + 3,
+    // scale byte i / 2 and offset bytes 2i, 2i + 1.
+#pragma unroll
+    for (int j = 0; j < PRO; ++j) {
+      const uint32_t i = threadIdx.x + (uint32_t)(j * nthr);
+      const bool live = i < (uint32_t)items;
+      pq[j] = ld_b32(rxc, live ? 4 * i : kOOB);
+      ps[j] = __builtin_amdgcn_raw_buffer_load_b8(rxs, (int)(live ? i >> 1 : kOOB), 0, 0);
+      po[j] = REF ? __builtin_amdgcn_raw_buffer_load_b16(rxo, (int)(live && refine_x ? 2 * i : kOOB), 0, 0) : 0u;
     }
     vmem_fence();
   }
@@ -389,7 +392,7 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
       }
     }
 #pragma unroll
-    for (int j = 0; j < kProItems; ++j) {
+    for (int j = 0; j < PRO; ++j) {
       const uint32_t i = threadIdx.x + (uint32_t)(j * nthr);
       if (i < (uint32_t)items) {
         const uint32_t t = i / (uint32_t)per_row;
@@ -586,13 +589,13 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
 
 // PD = 4: blocks of up to 1024 threads, 128 VGPRs; PD = 8: up to 512 threads,
 // 256 VGPRs (two wavefronts per SIMD).
-template <bool XLDS, bool FAST, int PD>
+template <bool XLDS, bool FAST, int PD, int PRO>
 __global__ __launch_bounds__(PD == 8 ? 512 : 1024) void gemv_stream_kernel(LinearArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int L = run_level(a);
-  if (L == 6) stream_tile<6, XLDS, FAST, PD>(a, lds);
-  else if (L == 2) stream_tile<2, XLDS, FAST, PD>(a, lds);
-  else stream_tile<4, XLDS, FAST, PD>(a, lds);
+  if (L == 6) stream_tile<6, XLDS, FAST, PD, PRO>(a, lds);
+  else if (L == 2) stream_tile<2, XLDS, FAST, PD, PRO>(a, lds);
+  else stream_tile<4, XLDS, FAST, PD, PRO>(a, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -857,9 +860,18 @@ hipError_t launch_gemv(const LinearArgs &a0, hipStream_t s) {
     a1.wk = c.wk;
     const int64_t tiles = (a0.n + 15) / 16;
     const dim3 grid((unsigned)((tiles + c.rt - 1) / c.rt)), block((unsigned)(64 * c.waves));
-#define AFP_STREAM(X, F, P) hipLaunchKernelGGL((gemv_stream_kernel<X, F, P>), grid, block, c.lds, s, a1)
-    if (c.xlds) { if (c.fast) AFP_STREAM(true, true, 4); else AFP_STREAM(true, false, 4); }
-    else { if (c.fast) AFP_STREAM(false, true, 4); else AFP_STREAM(false, false, 4); }
+#define AFP_STREAM(X, F, P, R) hipLaunchKernelGGL((gemv_stream_kernel<X, F, P, R>), grid, block, c.lds, s, a1)
+    // prologue items per thread: 4 covers one token; 16 the rest (4 would
+    // leave larger batches on the loop, whose loads wait one by one)
+    const int64_t items = a0.b * ((a0.k + kCh - 1) / kCh) * (kCh / 8);
+    if (c.xlds && c.fast) {
+      if (items <= 4 * 64 * (int64_t)c.waves) AFP_STREAM(true, true, 4, 4);
+      else AFP_STREAM(true, true, 4, 16);
+    } else if (c.xlds) {
+      AFP_STREAM(true, false, 4, 4);
+    } else {
+      if (c.fast) AFP_STREAM(false, true, 4, 4); else AFP_STREAM(false, false, 4, 4);
+    }
 #undef AFP_STREAM
     return hipGetLastError();
   }

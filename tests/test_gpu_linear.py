@@ -139,7 +139,7 @@ def test_gemv_equals_gemm():
         assert np.abs(a - b).max() <= 1e-5 * np.abs(b).max()
 
 
-@pytest.mark.parametrize("name,b", [("wgate", 1), ("wgate", 8), ("wdown", 8), ("wqkv", 1)])
+@pytest.mark.parametrize("name,b", [("wgate", 1), ("wgate", 8), ("wdown", 8), ("wqkv", 1), ("wqkv", 8)])
 def test_full_size_decode_sampled(name, b):
     """Llama-3-8B-shaped layer at full size: every output of sampled weight
     rows checked against the oracle at levels 2 and 4 (and 6 on Wqkv)."""
