@@ -90,6 +90,19 @@ __device__ __forceinline__ half8v fp4x8_to_half8(uint32_t w) {
   return half8v{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// Four fp16 offsets d/8 of one offset byte (2-bit codes 00 -> 0, 01 -> +1/8,
+// 10 -> -1/4, 11 -> -1/8), as two packed half2 words. Branch-free: the four
+// fp16 values have a zero low byte, so a byte permute of the table of their
+// high bytes (code 0: 0x00, 1: 0x30, 2: 0xB4, 3: 0xB0) builds two of them per
+// word (selector 0x0C gives a zero byte).
+__device__ __forceinline__ uint2 delta_words(uint32_t byte) {
+  constexpr uint32_t kHi = 0xB0B43000u;
+  const uint32_t c0 = byte & 3u, c1 = (byte >> 2) & 3u, c2 = (byte >> 4) & 3u, c3 = (byte >> 6) & 3u;
+  const uint32_t s01 = 0x000C000Cu | (c0 << 8) | (c1 << 24);
+  const uint32_t s23 = 0x000C000Cu | (c2 << 8) | (c3 << 24);
+  return make_uint2(__builtin_amdgcn_perm(kHi, kHi, s01), __builtin_amdgcn_perm(kHi, kHi, s23));
+}
+
 // AutoFP2 digit codes from eight E2M1 codes: keep the sign, magnitude bits
 // {e1 AND e0, e1 XOR e0} placed as the E2M1 codes of 2 (0b100) and 1 (0b010).
 __device__ __forceinline__ uint32_t autofp2_codes(uint32_t w) {

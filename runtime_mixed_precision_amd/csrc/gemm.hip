@@ -25,6 +25,8 @@ namespace afp {
 
 namespace {
 
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
 constexpr int BM = 128;   // tokens per tile
 constexpr int BN = 128;   // weight rows per tile
 constexpr int BK = 64;    // K per step
@@ -197,9 +199,242 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile GEMM (K % 64 == 0): a block of 4 wavefronts computes 256 tokens x
+// BN weight rows (BN = 256 or 128) in K steps of 64, with two LDS stages.
+// Activation tiles (fp16 panel) go from memory straight to LDS with
+// buffer_load ... lds (no registers, no ALU); weight tiles are loaded into
+// registers, decoded to fp16 and written to LDS. The loads of step k + 1 are
+// issued before the MFMAs of step k. LDS rows are 128 bytes (64 halves) with
+// the 16-byte chunk index XOR-swizzled by row % 8, so the fragment reads of a
+// 32x32x16 MFMA (32 rows, one chunk) spread over all banks. Each wavefront
+// owns 128 tokens x BN/2 rows: 4 x (BN/64) tiles of v_mfma_f32_32x32x16_f16.
+// ---------------------------------------------------------------------------
+
+typedef uint32_t u32x3v __attribute__((ext_vector_type(3)));
+#define AFP_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+constexpr int kBM2 = 256;
+constexpr int kBK2 = 64;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                           (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF), 0x00020000);
+}
+
+// LDS byte offset of 16-byte chunk c (0..7) of tile row r
+__device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * 128u + ((c ^ (r & 7u)) << 4); }
+
+template <int BN>
+__global__ __launch_bounds__(256) void gemm_lds_kernel(LinearArgs a) {
+  constexpr int WN = BN / 2;          // weight rows per wavefront
+  constexpr int TJ = WN / 32;         // 32-row MFMA tiles per wavefront along N
+  constexpr int TI = 4;               // 32-token MFMA tiles per wavefront along M
+  constexpr int A_BYTES = kBM2 * kBK2 * 2;
+  constexpr int W_BYTES = BN * kBK2 * 2;
+  constexpr int STAGE = A_BYTES + W_BYTES;
+  constexpr int HPT = BN / 128;       // 32-element weight halves per thread and step
+  extern __shared__ __align__(16) unsigned char lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t K = a.k;
+  const int64_t mtiles = (a.b + kBM2 - 1) / kBM2;
+  const int64_t mt = blockIdx.x % mtiles;
+  const int64_t nt = blockIdx.x / mtiles;
+  const int64_t m0 = mt * kBM2, n0 = nt * BN;
+  const int L = run_level(a);
+  const bool refine_w = (L == 6) && a.w_mask != nullptr && a.w_offsets != nullptr && a.n_refined > 0;
+  const int64_t R = a.n_refined;
+
+  // activation panel [b][kpad] fp16: rows past b read as zero
+  const __amdgpu_buffer_rsrc_t rx = rsrc(a.xh, a.b * a.kpad * 2);
+  // weight rows of this block: rows past n read as zero
+  const int64_t nrows = (a.n - n0) < BN ? (a.n - n0) : BN;
+  const __amdgpu_buffer_rsrc_t rc = rsrc(a.w_codes + n0 * (K >> 1), nrows * (K >> 1));
+  const __amdgpu_buffer_rsrc_t rs = rsrc(a.w_scales + n0 * (K >> 4), nrows * (K >> 4));
+  const __amdgpu_buffer_rsrc_t ro = rsrc(refine_w ? a.w_offsets + n0 * R : a.w_codes, refine_w ? nrows * R + 16 : 0);
+
+  // DMA mapping: instruction d of a wavefront covers A rows 32 * wave + 8 d ..
+  // + 7; lane i -> row + i / 8, LDS chunk i % 8 (global chunk (i % 8) ^ (row % 8))
+  const uint32_t arow_l = (uint32_t)(lane >> 3);
+  auto issue_a = [&](int64_t k0, int stage) {
+    unsigned char *base = lds + stage * STAGE;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t r = (uint32_t)(64 * wave + 8 * d) + arow_l;   // tile row 0..255
+      const uint32_t cg = (uint32_t)(lane & 7) ^ (r & 7u);
+      const int64_t tok = m0 + r;
+      const uint32_t off = tok < a.b ? (uint32_t)((tok * a.kpad + k0 + 8 * cg) * 2) : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, AFP_LDS(base + (64 * wave + 8 * d) * 128), 16, (int)off, 0, 0, 0);
+    }
+  };
+
+  // weight rows of this thread: row = tid % BN, halves h0 .. h0 + HPT - 1
+  const int wr = (BN == 256) ? tid : (tid >> 1);
+  const int h0 = (BN == 256) ? 0 : (tid & 1);
+  struct WRegs {
+    u32x4v c[HPT];
+    uint32_t s;
+    u32x3v o[HPT];
+    int32_t pos[HPT];
+    uint32_t mb[HPT];
+  };
+  auto load_w = [&](int64_t k0, WRegs &w) {
+#pragma unroll
+    for (int i = 0; i < HPT; ++i) {
+      const int64_t ke = k0 + 32 * (h0 + i);
+      w.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(wr * (K >> 1) + (ke >> 1)), 0, 0);
+    }
+    if (HPT == 2) {
+      w.s = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(wr * (K >> 4) + (k0 >> 4)), 0, 0);
+    } else {
+      w.s = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(wr * (K >> 4) + ((k0 + 32 * h0) >> 4)), 0, 0);
+    }
+    if (refine_w) {
+#pragma unroll
+      for (int i = 0; i < HPT; ++i) {
+        const int64_t mi = (k0 >> 5) + h0 + i;   // mask byte (32 elements)
+        w.mb[i] = a.w_mask[mi];
+        w.pos[i] = a.prefix[mi];
+        const uint32_t al = (uint32_t)((wr * R + w.pos[i]) & ~(int64_t)3);
+        w.o[i] = __builtin_amdgcn_raw_buffer_load_b96(ro, (int)al, 0, 0);
+      }
+    }
+  };
+  auto store_w = [&](const WRegs &w, int stage) {
+    unsigned char *base = lds + stage * STAGE + A_BYTES;
+#pragma unroll
+    for (int i = 0; i < HPT; ++i) {
+      uint32_t w4[4] = {w.c[i][0], w.c[i][1], w.c[i][2], w.c[i][3]};
+      if (L == 2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w4[j] = autofp2_codes(w4[j]);
+      }
+      half8v h[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) h[j] = fp4x8_to_half8(w4[j]);
+      if (refine_w) {
+        // the (at most 8) offset bytes of these 32 elements, in subgroup order;
+        // one byte per subgroup (0 where not refined) via a byte permute
+        const uint32_t m = w.mb[i];
+        const uint32_t sh = (uint32_t)((wr * R + w.pos[i]) & 3);
+        const uint32_t lo = __builtin_amdgcn_alignbyte(w.o[i][1], w.o[i][0], sh);
+        const uint32_t hi = __builtin_amdgcn_alignbyte(w.o[i][2], w.o[i][1], sh);
+        uint32_t sel[2] = {0, 0}, j = 0;
+#pragma unroll
+        for (int sg = 0; sg < 8; ++sg) {
+          const uint32_t on = (m >> sg) & 1u;
+          sel[sg >> 2] |= (on ? j : 0x0Cu) << (8 * (sg & 3));
+          j += on;
+        }
+        const uint32_t E[2] = {__builtin_amdgcn_perm(hi, lo, sel[0]), __builtin_amdgcn_perm(hi, lo, sel[1])};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint2 de = delta_words((E[p >> 1] >> (16 * (p & 1))) & 0xFFu);
+          const uint2 dd = delta_words((E[p >> 1] >> (16 * (p & 1) + 8)) & 0xFFu);
+          h[p] += __builtin_bit_cast(half8v, make_uint4(de.x, de.y, dd.x, dd.y));
+        }
+      }
+      const uint32_t sbytes = (HPT == 2) ? (w.s >> (16 * i)) : w.s;
+      const _Float16 b0 = (_Float16)e4m3_value(sbytes & 0xFFu);
+      const _Float16 b1 = (_Float16)e4m3_value((sbytes >> 8) & 0xFFu);
+      h[0] *= b0;
+      h[1] *= b0;
+      h[2] *= b1;
+      h[3] *= b1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *(half8v *)(base + swz((uint32_t)wr, (uint32_t)(4 * (h0 + i) + j))) = h[j];
+    }
+  };
+
+  float16v acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int64_t nkt = K / kBK2;
+  WRegs wreg;
+  issue_a(0, 0);
+  load_w(0, wreg);
+  store_w(wreg, 0);
+  __builtin_amdgcn_s_waitcnt(0);   // every load of step 0 (the activation copy included) has landed
+  __syncthreads();
+  for (int64_t kt = 0; kt < nkt; ++kt) {
+    const int st = (int)(kt & 1);
+    const bool more = kt + 1 < nkt;
+    if (more) {
+      issue_a((kt + 1) * kBK2, st ^ 1);
+      load_w((kt + 1) * kBK2, wreg);
+    }
+    const unsigned char *As = lds + st * STAGE;
+    const unsigned char *Wsb = As + A_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < kBK2 / 16; ++kk) {
+      const uint32_t ch = (uint32_t)(2 * kk + (lane >> 5));
+      half8v af[TI], bf[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i) af[i] = *(const half8v *)(As + swz((uint32_t)(wm * 128 + 32 * i + (lane & 31)), ch));
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) bf[j] = *(const half8v *)(Wsb + swz((uint32_t)(wn * WN + 32 * j + (lane & 31)), ch));
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) store_w(wreg, st ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);   // the next step's activation copy has landed
+    __syncthreads();
+  }
+
+  float scale = (*a.w_T) * (*a.x_T);
+  if (L == 2) scale *= a.c2;
+  // D tile (i, j): lane holds weight row 32 j + lane % 32 and tokens
+  // 8 (v / 4) + 4 (lane / 32) + v % 4 of the 32-token tile i
+  const bool out_bf16 = a.y_dtype == AUTOFP_BF16;
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int64_t n = n0 + wn * WN + 32 * j + (lane & 31);
+    if (n >= a.n) continue;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int64_t mb0 = m0 + wm * 128 + 32 * i + 4 * (lane >> 5);
+      const bool full = m0 + wm * 128 + 32 * i + 32 <= a.b;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = mb0 + 8 * (v >> 2) + (v & 3);
+        if (!full && m >= a.b) continue;
+        const float val = acc[i][j][v] * scale;
+        if (out_bf16) ((uint16_t *)a.y)[m * a.n + n] = f32_to_bf16_rne(val);
+        else ((float *)a.y)[m * a.n + n] = val;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const LinearArgs &a, hipStream_t s) {
+  if (a.k % kBK2 == 0 && a.b >= 128) {
+    // 256 x 256 tiles when they still give every CU a block, else 256 x 128
+    const int64_t mtiles = (a.b + kBM2 - 1) / kBM2;
+    const int64_t big = mtiles * ((a.n + 255) / 256);
+    if (big >= 256) {
+      const size_t lds = 2 * (size_t)(kBM2 * kBK2 * 2 + 256 * kBK2 * 2);
+      hipLaunchKernelGGL(gemm_lds_kernel<256>, dim3((unsigned)big), dim3(256), lds, s, a);
+    } else {
+      const size_t lds = 2 * (size_t)(kBM2 * kBK2 * 2 + 128 * kBK2 * 2);
+      hipLaunchKernelGGL(gemm_lds_kernel<128>, dim3((unsigned)(mtiles * ((a.n + 127) / 128))), dim3(256),
+                         lds, s, a);
+    }
+    return hipGetLastError();
+  }
   const int64_t mtiles = (a.b + BM - 1) / BM;
   const int64_t ntiles = (a.n + BN - 1) / BN;
   hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)(mtiles * ntiles)), dim3(256), 0, s, a);

@@ -55,18 +55,6 @@ __device__ __forceinline__ int run_level(const LinearArgs &a) {
   return a.bits_dev ? *a.bits_dev : a.bits;
 }
 
-// Four fp16 offsets d/8 of one offset byte (2-bit codes 00 -> 0, 01 -> +1/8,
-// 10 -> -1/4, 11 -> -1/8), as two packed half2 words. Branch-free: the four
-// fp16 values have a zero low byte, so a byte permute of the table of their
-// high bytes (code 0: 0x00, 1: 0x30, 2: 0xB4, 3: 0xB0) builds two of them per
-// word (selector 0x0C gives a zero byte).
-__device__ __forceinline__ uint2 delta_words(uint32_t byte) {
-  constexpr uint32_t kHi = 0xB0B43000u;
-  const uint32_t c0 = byte & 3u, c1 = (byte >> 2) & 3u, c2 = (byte >> 4) & 3u, c3 = (byte >> 6) & 3u;
-  const uint32_t s01 = 0x000C000Cu | (c0 << 8) | (c1 << 24);
-  const uint32_t s23 = 0x000C000Cu | (c2 << 8) | (c3 << 24);
-  return make_uint2(__builtin_amdgcn_perm(kHi, kHi, s01), __builtin_amdgcn_perm(kHi, kHi, s23));
-}
 
 __device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 __device__ __forceinline__ uint32_t as_u(half2v h) { return __builtin_bit_cast(uint32_t, h); }

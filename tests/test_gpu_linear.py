@@ -95,18 +95,24 @@ def test_gemv_shapes(n, b, k, level):
     check_close(y.cpu().numpy(), O.linear(wq, xq6 if level == 6 else xq4, level))
 
 
-GEMM_SHAPES = [(200, 130, 272), (384, 512, 1024), (128, 1, 64), (260, 129, 4096 + 16), (64, 300, 96)]
+GEMM_SHAPES = [(200, 130, 272), (384, 512, 1024), (128, 1, 64), (260, 129, 4096 + 16), (64, 300, 96),
+               (1000, 300, 512), (72, 257, 192), (8200, 2000, 128)]   # the last three: large-tile kernel
 
 
 @pytest.mark.parametrize("n,m,k", GEMM_SHAPES)
 @pytest.mark.parametrize("level", [2, 4, 6])
 def test_gemm_shapes(n, m, k, level):
+    """Ragged tiles in M and N for both GEMM kernels; 8200 x 2000 x 128 takes
+    the 256 x 256 tiles (264 blocks), 1000 x 300 and 72 x 257 the 256 x 128."""
     say(f"case: gemm N={n} M={m} K={k} level {level}")
     w, x = operands(n, m, k, seed=n + m + k, outliers=0.005)
     wp, xp4, xp6 = gpu_pack(w, x)
     wq, xq4, xq6 = oracle_pack(w, x)
     y = run(A.gemm, wp, xp4, xp6, level)
     check_close(y.cpu().numpy(), O.linear(wq, xq6 if level == 6 else xq4, level))
+    if level == 4:
+        yb = run(A.gemm, wp, xp4, xp6, level, out_dtype=torch.bfloat16)
+        assert torch.equal(yb, y.to(torch.bfloat16)), "bf16 output is not the RNE of the fp32 result"
 
 
 @pytest.mark.parametrize("op", ["gemv", "gemm"])
