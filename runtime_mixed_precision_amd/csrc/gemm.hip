@@ -206,8 +206,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a) {
 // buffer_load ... lds (no registers, no ALU); weight tiles are loaded into
 // registers, decoded to fp16 and written to LDS. The loads of step k + 1 are
 // issued before the MFMAs of step k. LDS rows are 128 bytes (64 halves) with
-// the 16-byte chunk index XOR-swizzled by row % 8, so the fragment reads of a
-// 32x32x16 MFMA (32 rows, one chunk) spread over all banks. Each wavefront
+// the 16-byte chunk index XOR-swizzled by (row / 2) % 8, so the fragment reads
+// of a 32x32x16 MFMA (32 rows, one chunk) spread over all banks. Each wavefront
 // owns 128 tokens x BN/2 rows: 4 x (BN/64) tiles of v_mfma_f32_32x32x16_f16.
 // ---------------------------------------------------------------------------
 
@@ -215,6 +215,7 @@ typedef uint32_t u32x3v __attribute__((ext_vector_type(3)));
 #define AFP_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 constexpr int kBM2 = 256;
+constexpr int kGemmWaves = 8;   // wavefronts per 256 x 256 block (two per SIMD)
 constexpr int kBK2 = 64;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
@@ -222,24 +223,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t
                                            (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF), 0x00020000);
 }
 
-// LDS byte offset of 16-byte chunk c (0..7) of tile row r
-__device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * 128u + ((c ^ (r & 7u)) << 4); }
+// LDS byte offset of 16-byte chunk c (0..7) of tile row r: the chunk index is
+// XORed with (r / 2) % 8, so the 16 rows at one chunk that a b128 LDS access
+// serves per cycle fall on 16 distinct 16-byte bank groups (64 banks)
+__device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * 128u + ((c ^ ((r >> 1) & 7u)) << 4); }
 
-template <int BN>
-__global__ __launch_bounds__(256) void gemm_lds_kernel(LinearArgs a) {
-  constexpr int WN = BN / 2;          // weight rows per wavefront
+// NW wavefronts (4: one per SIMD; 8: two per SIMD, so one wavefront's
+// decode and waits overlap the other's MFMAs) in a 2 x NW/2 grid over the
+// 256 x BN tile.
+template <int BN, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
+  constexpr int WN = BN / (NW / 2);   // weight rows per wavefront
   constexpr int TJ = WN / 32;         // 32-row MFMA tiles per wavefront along N
   constexpr int TI = 4;               // 32-token MFMA tiles per wavefront along M
   constexpr int A_BYTES = kBM2 * kBK2 * 2;
   constexpr int W_BYTES = BN * kBK2 * 2;
   constexpr int STAGE = A_BYTES + W_BYTES;
-  constexpr int HPT = BN / 128;       // 32-element weight halves per thread and step
+  constexpr int WITEMS = 2 * BN;              // (row, 32-element half) weight items per step
+  constexpr int HPT = WITEMS >= 128 * NW ? 2 : 1;   // items per thread (threads past WITEMS idle)
+  constexpr int APW = 32 / NW;                // activation copy instructions per wavefront and step
+  static_assert(WITEMS == 64 * NW * HPT || (HPT == 1 && WITEMS < 64 * NW), "weight items per thread");
   extern __shared__ __align__(16) unsigned char lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
   const int64_t K = a.k;
   const int64_t mtiles = (a.b + kBM2 - 1) / kBM2;
   const int64_t mt = blockIdx.x % mtiles;
@@ -257,24 +266,25 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(LinearArgs a) {
   const __amdgpu_buffer_rsrc_t rs = rsrc(a.w_scales + n0 * (K >> 4), nrows * (K >> 4));
   const __amdgpu_buffer_rsrc_t ro = rsrc(refine_w ? a.w_offsets + n0 * R : a.w_codes, refine_w ? nrows * R + 16 : 0);
 
-  // DMA mapping: instruction d of a wavefront covers A rows 32 * wave + 8 d ..
-  // + 7; lane i -> row + i / 8, LDS chunk i % 8 (global chunk (i % 8) ^ (row % 8))
+  // DMA mapping: instruction d of a wavefront covers A rows 8 (APW wave + d) ..
+  // + 7; lane i -> row + i / 8, LDS chunk i % 8 (global chunk (i % 8) ^ ((row / 2) % 8))
   const uint32_t arow_l = (uint32_t)(lane >> 3);
   auto issue_a = [&](int64_t k0, int stage) {
     unsigned char *base = lds + stage * STAGE;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const uint32_t r = (uint32_t)(64 * wave + 8 * d) + arow_l;   // tile row 0..255
-      const uint32_t cg = (uint32_t)(lane & 7) ^ (r & 7u);
+    for (int d = 0; d < APW; ++d) {
+      const uint32_t r = (uint32_t)(8 * (APW * wave + d)) + arow_l;   // tile row 0..255
+      const uint32_t cg = (uint32_t)(lane & 7) ^ ((r >> 1) & 7u);
       const int64_t tok = m0 + r;
       const uint32_t off = tok < a.b ? (uint32_t)((tok * a.kpad + k0 + 8 * cg) * 2) : 0x80000000u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, AFP_LDS(base + (64 * wave + 8 * d) * 128), 16, (int)off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, AFP_LDS(base + 8 * (APW * wave + d) * 128), 16, (int)off, 0, 0, 0);
     }
   };
 
-  // weight rows of this thread: row = tid % BN, halves h0 .. h0 + HPT - 1
-  const int wr = (BN == 256) ? tid : (tid >> 1);
-  const int h0 = (BN == 256) ? 0 : (tid & 1);
+  // weight rows of this thread: halves h0 .. h0 + HPT - 1 of row wr
+  const int wr = (HPT == 2) ? tid : (tid >> 1);
+  const int h0 = (HPT == 2) ? 0 : (tid & 1);
+  const bool w_thread = tid < WITEMS / HPT;   // whole wavefronts: WITEMS is a multiple of 64
   struct WRegs {
     u32x4v c[HPT];
     uint32_t s;
@@ -361,8 +371,10 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(LinearArgs a) {
   const int64_t nkt = K / kBK2;
   WRegs wreg;
   issue_a(0, 0);
-  load_w(0, wreg);
-  store_w(wreg, 0);
+  if (w_thread) {
+    load_w(0, wreg);
+    store_w(wreg, 0);
+  }
   __builtin_amdgcn_s_waitcnt(0);   // every load of step 0 (the activation copy included) has landed
   __syncthreads();
   for (int64_t kt = 0; kt < nkt; ++kt) {
@@ -370,7 +382,7 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(LinearArgs a) {
     const bool more = kt + 1 < nkt;
     if (more) {
       issue_a((kt + 1) * kBK2, st ^ 1);
-      load_w((kt + 1) * kBK2, wreg);
+      if (w_thread) load_w((kt + 1) * kBK2, wreg);
     }
     const unsigned char *As = lds + st * STAGE;
     const unsigned char *Wsb = As + A_BYTES;
@@ -388,7 +400,7 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(LinearArgs a) {
         for (int j = 0; j < TJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    if (more) store_w(wreg, st ^ 1);
+    if (more && w_thread) store_w(wreg, st ^ 1);
     __builtin_amdgcn_s_waitcnt(0);   // the next step's activation copy has landed
     __syncthreads();
   }
@@ -427,11 +439,11 @@ hipError_t launch_gemm(const LinearArgs &a, hipStream_t s) {
     const int64_t big = mtiles * ((a.n + 255) / 256);
     if (big >= 256) {
       const size_t lds = 2 * (size_t)(kBM2 * kBK2 * 2 + 256 * kBK2 * 2);
-      hipLaunchKernelGGL(gemm_lds_kernel<256>, dim3((unsigned)big), dim3(256), lds, s, a);
+      hipLaunchKernelGGL((gemm_lds_kernel<256, kGemmWaves>), dim3((unsigned)big), dim3(64 * kGemmWaves), lds, s, a);
     } else {
       const size_t lds = 2 * (size_t)(kBM2 * kBK2 * 2 + 128 * kBK2 * 2);
-      hipLaunchKernelGGL(gemm_lds_kernel<128>, dim3((unsigned)(mtiles * ((a.n + 127) / 128))), dim3(256),
-                         lds, s, a);
+      hipLaunchKernelGGL((gemm_lds_kernel<128, kGemmWaves>), dim3((unsigned)(mtiles * ((a.n + 127) / 128))),
+                         dim3(64 * kGemmWaves), lds, s, a);
     }
     return hipGetLastError();
   }
