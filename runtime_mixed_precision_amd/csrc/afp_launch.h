@@ -91,6 +91,8 @@ hipError_t launch_gemv(const LinearArgs &a, hipStream_t s);
 
 // ---- gemm.hip ----
 hipError_t launch_gemm(const LinearArgs &a, hipStream_t s);
+bool gemm_small_m_ok(const LinearArgs &a);   // the 64-token GEMM tile applies (K % 64 == 0)
+hipError_t launch_gemm_small_m(const LinearArgs &a, hipStream_t s);   // reads a.xh and, at level 6, a.prefix
 
 // ---- signals.hip ----
 int64_t entropy_slices(int64_t vocab);                        // vocabulary slices per row

@@ -231,17 +231,18 @@ __device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * 128
 // NW wavefronts (4: one per SIMD; 8: two per SIMD, so one wavefront's
 // decode and waits overlap the other's MFMAs) in a 2 x NW/2 grid over the
 // 256 x BN tile.
-template <int BN, int NW>
+template <int BM, int BN, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
   constexpr int WN = BN / (NW / 2);   // weight rows per wavefront
   constexpr int TJ = WN / 32;         // 32-row MFMA tiles per wavefront along N
-  constexpr int TI = 4;               // 32-token MFMA tiles per wavefront along M
-  constexpr int A_BYTES = kBM2 * kBK2 * 2;
+  constexpr int TI = BM / 64;         // 32-token MFMA tiles per wavefront along M
+  constexpr int A_BYTES = BM * kBK2 * 2;
   constexpr int W_BYTES = BN * kBK2 * 2;
   constexpr int STAGE = A_BYTES + W_BYTES;
   constexpr int WITEMS = 2 * BN;              // (row, 32-element half) weight items per step
   constexpr int HPT = WITEMS >= 128 * NW ? 2 : 1;   // items per thread (threads past WITEMS idle)
-  constexpr int APW = 32 / NW;                // activation copy instructions per wavefront and step
+  constexpr int APW = BM / 8 / NW;            // activation copy instructions per wavefront and step
+  static_assert(APW >= 1, "at least one activation copy per wavefront");
   static_assert(WITEMS == 64 * NW * HPT || (HPT == 1 && WITEMS < 64 * NW), "weight items per thread");
   extern __shared__ __align__(16) unsigned char lds[];
 
@@ -250,10 +251,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
   const int wave = tid >> 6;
   const int wm = wave / (NW / 2), wn = wave % (NW / 2);
   const int64_t K = a.k;
-  const int64_t mtiles = (a.b + kBM2 - 1) / kBM2;
+  const int64_t mtiles = (a.b + BM - 1) / BM;
   const int64_t mt = blockIdx.x % mtiles;
   const int64_t nt = blockIdx.x / mtiles;
-  const int64_t m0 = mt * kBM2, n0 = nt * BN;
+  const int64_t m0 = mt * BM, n0 = nt * BN;
   const int L = run_level(a);
   const bool refine_w = (L == 6) && a.w_mask != nullptr && a.w_offsets != nullptr && a.n_refined > 0;
   const int64_t R = a.n_refined;
@@ -391,7 +392,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
       const uint32_t ch = (uint32_t)(2 * kk + (lane >> 5));
       half8v af[TI], bf[TJ];
 #pragma unroll
-      for (int i = 0; i < TI; ++i) af[i] = *(const half8v *)(As + swz((uint32_t)(wm * 128 + 32 * i + (lane & 31)), ch));
+      for (int i = 0; i < TI; ++i)
+        af[i] = *(const half8v *)(As + swz((uint32_t)(wm * (BM / 2) + 32 * i + (lane & 31)), ch));
 #pragma unroll
       for (int j = 0; j < TJ; ++j) bf[j] = *(const half8v *)(Wsb + swz((uint32_t)(wn * WN + 32 * j + (lane & 31)), ch));
 #pragma unroll
@@ -416,8 +418,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
     if (n >= a.n) continue;
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
-      const int64_t mb0 = m0 + wm * 128 + 32 * i + 4 * (lane >> 5);
-      const bool full = m0 + wm * 128 + 32 * i + 32 <= a.b;
+      const int64_t mb0 = m0 + wm * (BM / 2) + 32 * i + 4 * (lane >> 5);
+      const bool full = m0 + wm * (BM / 2) + 32 * i + 32 <= a.b;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t m = mb0 + 8 * (v >> 2) + (v & 3);
@@ -432,6 +434,19 @@ __global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
 
 }  // namespace
 
+bool gemm_small_m_ok(const LinearArgs &a) { return a.k % kBK2 == 0; }
+
+// 64 tokens x 256 rows per block: the batched-decode path (17..64 tokens per
+// launch), where the weight stream bounds the time and every decoded weight
+// tile serves all tokens from LDS.
+hipError_t launch_gemm_small_m(const LinearArgs &a, hipStream_t s) {
+  const int64_t mtiles = (a.b + 63) / 64;
+  const size_t lds = 2 * (size_t)(64 * kBK2 * 2 + 256 * kBK2 * 2);
+  hipLaunchKernelGGL((gemm_lds_kernel<64, 256, kGemmWaves>), dim3((unsigned)(mtiles * ((a.n + 255) / 256))),
+                     dim3(64 * kGemmWaves), lds, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const LinearArgs &a, hipStream_t s) {
   if (a.k % kBK2 == 0 && a.b >= 128) {
     // 256 x 256 tiles when they still give every CU a block, else 256 x 128
@@ -439,14 +454,16 @@ hipError_t launch_gemm(const LinearArgs &a, hipStream_t s) {
     const int64_t big = mtiles * ((a.n + 255) / 256);
     if (big >= 256) {
       const size_t lds = 2 * (size_t)(kBM2 * kBK2 * 2 + 256 * kBK2 * 2);
-      hipLaunchKernelGGL((gemm_lds_kernel<256, kGemmWaves>), dim3((unsigned)big), dim3(64 * kGemmWaves), lds, s, a);
+      hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 256, kGemmWaves>), dim3((unsigned)big), dim3(64 * kGemmWaves), lds, s,
+                         a);
     } else {
       const size_t lds = 2 * (size_t)(kBM2 * kBK2 * 2 + 128 * kBK2 * 2);
-      hipLaunchKernelGGL((gemm_lds_kernel<128, kGemmWaves>), dim3((unsigned)(mtiles * ((a.n + 127) / 128))),
+      hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 128, kGemmWaves>), dim3((unsigned)(mtiles * ((a.n + 127) / 128))),
                          dim3(64 * kGemmWaves), lds, s, a);
     }
     return hipGetLastError();
   }
+  if (a.k % kBK2 == 0) return launch_gemm_small_m(a, s);
   const int64_t mtiles = (a.b + BM - 1) / BM;
   const int64_t ntiles = (a.n + BN - 1) / BN;
   hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)(mtiles * ntiles)), dim3(256), 0, s, a);

@@ -322,12 +322,15 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
   const int64_t per_row = kp / 8;
   const int64_t items = XLDS ? a.b * per_row : 0;
   const int64_t mdw = refine_w ? (mbytes + 3) / 4 : 0;
-  const bool pro_static = FAST && items <= (int64_t)PRO * nthr && mask_lds_bytes(K) <= 4 * (int64_t)kProMask * nthr;
+  // (FAST) the first PRO items per thread go ahead of the weight loads; any
+  // further items follow in rounds of 8 per thread, each round's loads issued
+  // together
+  const bool pro_static = FAST && mask_lds_bytes(K) <= 4 * (int64_t)kProMask * nthr;
   uint32_t pq[PRO], ps[PRO], po[PRO], pm[kProMask];
+  const __amdgpu_buffer_rsrc_t rxc = make_rsrc(a.x_codes, a.b * (K >> 1));
+  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(a.x_scales, a.b * (K >> 4));
+  const __amdgpu_buffer_rsrc_t rxo = make_rsrc(refine_x ? a.x_offsets : a.x_codes, refine_x ? a.b * (K >> 2) : 0);
   if (pro_static) {
-    const __amdgpu_buffer_rsrc_t rxc = make_rsrc(a.x_codes, a.b * (K >> 1));
-    const __amdgpu_buffer_rsrc_t rxs = make_rsrc(a.x_scales, a.b * (K >> 4));
-    const __amdgpu_buffer_rsrc_t rxo = make_rsrc(refine_x ? a.x_offsets : a.x_codes, refine_x ? a.b * (K >> 2) : 0);
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(refine_w ? a.w_mask : a.w_codes, refine_w ? mbytes : 0);
     // the weight-mask loads first: the mask is written to LDS before the
     // activations, so its wait leaves the activation loads in flight
@@ -387,6 +390,26 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
         const uint32_t t = i / (uint32_t)per_row;
         const uint32_t k0 = (i - t * (uint32_t)per_row) * 8;
         *(uint4 *)(xs + t * xpitch + k0) = act_decode8_vals(pq[j], ps[j], po[j], refine_x);
+      }
+    }
+    for (int64_t base = (int64_t)PRO * nthr; base < items; base += 8 * (int64_t)nthr) {
+      uint32_t q8[8], s8[8], o8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t i = (uint32_t)base + threadIdx.x + (uint32_t)(j * nthr);
+        const bool live = i < (uint32_t)items;
+        q8[j] = ld_b32(rxc, live ? 4 * i : kOOB);
+        s8[j] = __builtin_amdgcn_raw_buffer_load_b8(rxs, (int)(live ? i >> 1 : kOOB), 0, 0);
+        o8[j] = REF ? __builtin_amdgcn_raw_buffer_load_b16(rxo, (int)(live && refine_x ? 2 * i : kOOB), 0, 0) : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t i = (uint32_t)base + threadIdx.x + (uint32_t)(j * nthr);
+        if (i < (uint32_t)items) {
+          const uint32_t t = i / (uint32_t)per_row;
+          const uint32_t k0 = (i - t * (uint32_t)per_row) * 8;
+          *(uint4 *)(xs + t * xpitch + k0) = act_decode8_vals(q8[j], s8[j], o8[j], refine_x);
+        }
       }
     }
   } else {
@@ -864,7 +887,10 @@ hipError_t launch_gemv(const LinearArgs &a0, hipStream_t s) {
 #undef AFP_STREAM
     return hipGetLastError();
   }
-  // slices of at most 64 tokens
+  // more than 16 tokens: for wide weights (enough 256-row tiles to fill the
+  // chip) the 64-token GEMM tile, where every decoded weight tile serves all
+  // tokens from LDS; otherwise slices of at most 64 tokens
+  if (gemm_small_m_ok(a0) && a0.n >= 8192) return launch_gemm_small_m(a0, s);
   for (int64_t t0 = 0; t0 < a0.b; t0 += 64) {
     LinearArgs a = a0;
     a.b = (a0.b - t0) < 64 ? (a0.b - t0) : 64;

@@ -145,7 +145,8 @@ def test_gemv_equals_gemm():
         assert np.abs(a - b).max() <= 1e-5 * np.abs(b).max()
 
 
-@pytest.mark.parametrize("name,b", [("wgate", 1), ("wgate", 8), ("wdown", 8), ("wqkv", 1), ("wqkv", 8)])
+@pytest.mark.parametrize("name,b", [("wgate", 1), ("wgate", 8), ("wdown", 8), ("wqkv", 1), ("wqkv", 8), ("wqkv", 16),
+                                    ("wdown", 64)])
 def test_full_size_decode_sampled(name, b):
     """Llama-3-8B-shaped layer at full size: every output of sampled weight
     rows checked against the oracle at levels 2 and 4 (and 6 on Wqkv)."""
@@ -173,6 +174,26 @@ def test_full_size_decode_sampled(name, b):
         y = A.gemv(wp, xp6 if level == 6 else xp4, bits=level).cpu().numpy()
         ref = O.linear(wq, xq6 if level == 6 else xq4, level)
         check_close(y[:, rows], ref)
+
+
+@pytest.mark.parametrize("b", [16, 64])
+def test_full_size_70b_gemv_sampled(b):
+    """The 70B-shaped projection (28672 x 8192) at 16 and 64 tokens, levels 2
+    and 4: every output of 64 sampled weight rows against the oracle."""
+    n, k = 28672, 8192
+    say(f"case: full-size 70B GEMV {n}x{k} batch {b}")
+    w = S.weights(n, k, seed=3, tensor_id=70, device=DEV)
+    x = S.activations(b, k, seed=3, tensor_id=71, device=DEV)
+    wp = A.quantize_weight(w)
+    xp4 = A.quantize_activation(x)
+    rows = np.random.default_rng(5).choice(n, 64, replace=False)
+    wn = w.cpu().numpy()
+    wq = O.quantize_weight(wn[rows], tensor_amax=np.abs(wn).max())
+    xq4 = O.quantize_activation(x.float().cpu().numpy())
+    del w, wn
+    for level in (2, 4):
+        y = A.gemv(wp, xp4, bits=level).cpu().numpy()
+        check_close(y[:, rows], O.linear(wq, xq4, level))
 
 
 def test_prefill_sampled_full_size():
