@@ -260,6 +260,29 @@ def prefill_bench(A, S, device, reps):
             "frac_fp4_mfma_peak": round(best / PEAK_FP4_TFLOPS, 4)}
 
 
+def gemv_70b(A, S, device, batch=64, pool_n=5):
+    """The 70B-shaped projection (28672 x 8192) at 64 tokens, level 4: weights
+    rotated over a pool larger than the Infinity Cache, one graph per weight."""
+    import torch
+    n, k = 28672, 8192
+    pool = []
+    for i in range(pool_n):
+        w = S.weights(n, k, seed=700 + i, tensor_id=0, device=device)
+        pool.append(A.quantize_weight(w))
+        del w
+    x = S.activations(batch, k, seed=700, tensor_id=1, outlier_frac=0.0, device=device)
+    xp = A.quantize_activation(x)
+    y = torch.empty(batch, n, dtype=torch.float32, device=device)
+    ws = torch.empty(A.workspace_bytes(2, batch, k), dtype=torch.uint8, device=device)
+    graphs = capture([lambda wp=wp: A.gemv(wp, xp, bits=4, out=y, workspace=ws) for wp in pool])
+    ms = time_graphs(graphs, 20, 3)
+    by = gemv_bytes(pool[0], batch, 4)
+    out = {"workload": "W 28672x8192 at 64 tokens, level 4", "us": round(ms * 1e3, 2),
+           "gbs": round(by / (ms * 1e-3) / 1e9, 1), "tflops": round(2.0 * batch * n * k / (ms * 1e-3) / 1e12, 1)}
+    del pool, graphs
+    return out
+
+
 def cpu_baseline(batch, target_s=12.0):
     """The CPU oracle (fp64 NumPy, one BLAS thread) on a bounded sample of the
     same step: per level, encode each linear input and compute the layer
@@ -313,6 +336,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--no-batches", action="store_true", help="skip the batch-16/64 and 70B-shape GEMV lines")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run only the workload of the HBM-counter runs (no JSON line)")
     args = ap.parse_args()
@@ -383,6 +407,16 @@ def main():
         extra[f"step_b{args.secondary_batch}"] = {
             "ms": round(ms2s, 4), "gbs": round(b2.step_bytes() / (ms2s * 1e-3) / 1e9, 1)}
         del b2, g2, s2
+    if not args.no_batches:
+        # the 32-layer step's larger batches: GEMV-only rate over the same 12 launches
+        for bb in (16, 64):
+            b3 = DecodeBench(A, S, pool, bb, device)
+            g3 = capture([lambda s=s: b3.gemv_only(s) for s in range(G)])
+            ms3 = time_graphs(g3, 10, args.warmup)
+            extra[f"gemv_b{bb}"] = {"gbs": round(b3.gemv_only_bytes() / (ms3 * 1e-3) / 1e9, 1),
+                                    "avg_launch_us": round(ms3 * 1e3 / n_launch, 3)}
+            del b3, g3
+        extra["gemv_70b_b64"] = gemv_70b(A, S, device)
     if not args.no_prefill:
         del graphs, ggraphs
         extra["prefill_gemm"] = prefill_bench(A, S, device, 5)
