@@ -215,7 +215,8 @@ typedef uint32_t u32x3v __attribute__((ext_vector_type(3)));
 #define AFP_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 constexpr int kBM2 = 256;
-constexpr int kGemmWaves = 8;   // wavefronts per 256 x 256 block (two per SIMD)
+constexpr int kGemmWaves = 16;  // wavefronts per prefill block (four per SIMD, 128 VGPRs each)
+constexpr int kDecodeWaves = 8; // wavefronts per 64-token block
 constexpr int kBK2 = 64;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
@@ -228,14 +229,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t
 // serves per cycle fall on 16 distinct 16-byte bank groups (64 banks)
 __device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * 128u + ((c ^ ((r >> 1) & 7u)) << 4); }
 
-// NW wavefronts (4: one per SIMD; 8: two per SIMD, so one wavefront's
-// decode and waits overlap the other's MFMAs) in a 2 x NW/2 grid over the
-// 256 x BN tile.
+// NW wavefronts (8 or 16: two or four per SIMD, so one wavefront's decode
+// and waits overlap the others' MFMAs) in a WGM x NW/WGM grid over the
+// BM x BN tile (WGM = 4 for 16 wavefronts on 256 tokens, else 2).
 template <int BM, int BN, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
-  constexpr int WN = BN / (NW / 2);   // weight rows per wavefront
+  constexpr int WGM = (NW >= 16 && BM >= 256) ? 4 : 2;   // wavefronts along M
+  constexpr int WGN = NW / WGM;                         // wavefronts along N
+  constexpr int WM = BM / WGM;        // tokens per wavefront
+  constexpr int WN = BN / WGN;        // weight rows per wavefront
   constexpr int TJ = WN / 32;         // 32-row MFMA tiles per wavefront along N
-  constexpr int TI = BM / 64;         // 32-token MFMA tiles per wavefront along M
+  constexpr int TI = WM / 32;         // 32-token MFMA tiles per wavefront along M
   constexpr int A_BYTES = BM * kBK2 * 2;
   constexpr int W_BYTES = BN * kBK2 * 2;
   constexpr int STAGE = A_BYTES + W_BYTES;
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
+  const int wm = wave / WGN, wn = wave % WGN;
   const int64_t K = a.k;
   const int64_t mtiles = (a.b + BM - 1) / BM;
   const int64_t mt = blockIdx.x % mtiles;
@@ -393,7 +397,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
       half8v af[TI], bf[TJ];
 #pragma unroll
       for (int i = 0; i < TI; ++i)
-        af[i] = *(const half8v *)(As + swz((uint32_t)(wm * (BM / 2) + 32 * i + (lane & 31)), ch));
+        af[i] = *(const half8v *)(As + swz((uint32_t)(wm * WM + 32 * i + (lane & 31)), ch));
 #pragma unroll
       for (int j = 0; j < TJ; ++j) bf[j] = *(const half8v *)(Wsb + swz((uint32_t)(wn * WN + 32 * j + (lane & 31)), ch));
 #pragma unroll
@@ -418,8 +422,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
     if (n >= a.n) continue;
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
-      const int64_t mb0 = m0 + wm * (BM / 2) + 32 * i + 4 * (lane >> 5);
-      const bool full = m0 + wm * (BM / 2) + 32 * i + 32 <= a.b;
+      const int64_t mb0 = m0 + wm * WM + 32 * i + 4 * (lane >> 5);
+      const bool full = m0 + wm * WM + 32 * i + 32 <= a.b;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t m = mb0 + 8 * (v >> 2) + (v & 3);
@@ -442,8 +446,8 @@ bool gemm_small_m_ok(const LinearArgs &a) { return a.k % kBK2 == 0; }
 hipError_t launch_gemm_small_m(const LinearArgs &a, hipStream_t s) {
   const int64_t mtiles = (a.b + 63) / 64;
   const size_t lds = 2 * (size_t)(64 * kBK2 * 2 + 256 * kBK2 * 2);
-  hipLaunchKernelGGL((gemm_lds_kernel<64, 256, kGemmWaves>), dim3((unsigned)(mtiles * ((a.n + 255) / 256))),
-                     dim3(64 * kGemmWaves), lds, s, a);
+  hipLaunchKernelGGL((gemm_lds_kernel<64, 256, kDecodeWaves>), dim3((unsigned)(mtiles * ((a.n + 255) / 256))),
+                     dim3(64 * kDecodeWaves), lds, s, a);
   return hipGetLastError();
 }
 
