@@ -44,6 +44,7 @@ namespace {
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3v __attribute__((ext_vector_type(3)));
+typedef int32_t i32x8v __attribute__((ext_vector_type(8)));
 
 constexpr int kCh = 256;         // K elements per chunk
 constexpr int kGroup = 4;        // chunks per scale load group
@@ -611,6 +612,202 @@ __global__ __launch_bounds__(PD == 8 ? 512 : 1024) void gemv_stream_kernel(Linea
 }
 
 // ---------------------------------------------------------------------------
+// One-token GEMV on the fp4 matrix cores (levels 2 and 4)
+// ---------------------------------------------------------------------------
+//
+// v_mfma_scale_f32_16x16x128_f8f6f4 with both operands in E2M1 (scales 2^0)
+// multiplies a 16 x 128 block by a 128 x 16 block exactly: every product is
+// a multiple of 1/4 of magnitude at most 36. The weight codes enter unchanged
+// as the B operand (column j = weight row j; lane l holds column l % 16 and
+// the 32 elements 32 * (l / 16) .. + 31 of the MFMA's K range, low nibble
+// first). The A operand is the activation laid out block-diagonally: row s
+// holds the 16 codes of one 16-element group and zeros elsewhere, so
+// D[s][j] is the exact dot product of that group of the activation with
+// weight row j. The E4M3 group scales of both operands are applied to D in
+// fp32, so no element is converted: per 256-element chunk a lane does two
+// MFMAs and 16 scale multiply-adds instead of 32 fp4 -> fp16 conversions.
+//
+// A lane (row r = l % 16, lane group q = l / 16) loads, per chunk, the same
+// 32 code bytes as the streaming kernel: elements 64q .. 64q + 63, the first
+// half for MFMA h = 0 and the second for h = 1. MFMA h thus sees, in lane
+// group q, the groups 4q + 2h and 4q + 2h + 1 of the chunk; A row s < 8 is
+// the group 4 * (s / 2) + 2h + s % 2. Output lane (r, q) holds rows 4q .. 4q+3
+// of D, i.e. for q < 2 the groups 8q + {0, 1, 4, 5} + 2h of weight row r.
+constexpr int kFp4Chunks = 16;                          // chunks per wavefront at most
+constexpr int kFp4Pitch = kFp4Chunks * 16 + 16;            // LDS row pitch of the weight scales
+constexpr int kFp4WaveLds = 16 * kFp4Pitch + kFp4Chunks * (128 + 16);
+constexpr int kFp4Depth = 8;                               // chunks of code loads in flight
+
+template <int L, int PD>
+__device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int WK = a.wk;
+  const int tile = wave / WK;
+  const int kw = wave - tile * WK;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int64_t K = a.k;
+  const int64_t nch = K / kCh;
+  const int64_t n0 = ((int64_t)blockIdx.x * (nw / WK) + tile) * 16;
+  int64_t rows = a.n - n0;
+  rows = rows < 0 ? 0 : rows > 16 ? 16 : rows;
+  const int64_t nb0 = rows > 0 ? n0 : 0;
+  const int64_t c0 = (nch * kw) / WK;
+  const int64_t c1 = (nch * (kw + 1)) / WK;
+  const int len = (int)(c1 - c0);   // at most kFp4Chunks
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.w_codes + nb0 * (K >> 1), rows * (K >> 1));
+  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(a.w_scales + nb0 * (K >> 4), rows * (K >> 4));
+  const __amdgpu_buffer_rsrc_t rxc = make_rsrc(a.x_codes, K >> 1);
+  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(a.x_scales, K >> 4);
+  const uint32_t crow = (uint32_t)(r * (K >> 1) + 32 * q);
+
+  // wavefront-private LDS: weight scales [16 rows][kFp4Chunks chunks][16 B]
+  // at a row pitch of kFp4Chunks * 16 + 16 bytes (the 16 rows' 8-byte reads
+  // then cover all 64 banks once), then the activation codes and scales of
+  // the range
+  unsigned char *wl = lds + (size_t)wave * kFp4WaveLds;
+  unsigned char *wsc = wl;
+  unsigned char *xsl = wl + 16 * kFp4Pitch;
+  unsigned char *sxl = xsl + kFp4Chunks * 128;
+
+  // 1. the range's scales and activation bytes, each lane one 16-byte piece
+  //    per load: weight-scale piece j * 64 + l is row l % 16, chunk 4j + l / 16
+  uint32_t pw[kFp4Chunks / 4][4], px[2][4], ps[4];
+#pragma unroll
+  for (int j = 0; j < kFp4Chunks / 4; ++j) {
+    const int p = 4 * j + q;
+    const uint32_t o = p < len ? (uint32_t)(r * (K >> 4) + 16 * (c0 + p)) : kOOB;
+    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rsc, (int)o, 0, 0);
+    pw[j][0] = v[0]; pw[j][1] = v[1]; pw[j][2] = v[2]; pw[j][3] = v[3];
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int p = 64 * j + lane;   // 16-byte piece of the range's activation codes
+    const uint32_t o = p < 8 * len ? (uint32_t)(128 * c0 + 16 * p) : kOOB;
+    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rxc, (int)o, 0, 0);
+    px[j][0] = v[0]; px[j][1] = v[1]; px[j][2] = v[2]; px[j][3] = v[3];
+  }
+  {
+    const uint32_t o = lane < len ? (uint32_t)(16 * (c0 + lane)) : kOOB;
+    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rxs, (int)o, 0, 0);
+    ps[0] = v[0]; ps[1] = v[1]; ps[2] = v[2]; ps[3] = v[3];
+  }
+  vmem_fence();
+
+  // 2. the first PD chunks of weight codes
+  struct Buf {
+    uint32_t c[8];   // 64 weight codes
+  };
+  auto load = [&](int i, Buf &b) {
+    const bool live = i < len;
+    const uint32_t so = live ? (uint32_t)((c0 + i) * 128) : 0u;
+    const uint32_t vo = live ? crow : kOOB;
+    const u32x4v lo = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)vo, (int)so, 0);
+    const u32x4v hi = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(vo + 16), (int)so, 0);
+    b.c[0] = lo[0]; b.c[1] = lo[1]; b.c[2] = lo[2]; b.c[3] = lo[3];
+    b.c[4] = hi[0]; b.c[5] = hi[1]; b.c[6] = hi[2]; b.c[7] = hi[3];
+  };
+  Buf buf[PD];
+#pragma unroll
+  for (int u = 0; u < PD; ++u) {
+    load(u, buf[u]);
+    vmem_fence();
+  }
+
+  // 3. prologue bytes to LDS (waits for them only: the code loads stay in flight)
+#pragma unroll
+  for (int j = 0; j < kFp4Chunks / 4; ++j)
+    *(uint4 *)(wsc + r * kFp4Pitch + 16 * (4 * j + q)) = make_uint4(pw[j][0], pw[j][1], pw[j][2], pw[j][3]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    *(uint4 *)(xsl + 16 * (64 * j + lane)) = make_uint4(px[j][0], px[j][1], px[j][2], px[j][3]);
+  if (lane < kFp4Chunks) *(uint4 *)(sxl + 16 * lane) = make_uint4(ps[0], ps[1], ps[2], ps[3]);
+
+  // A operand: lane (s = r, q) carries group 4q + 2h + (r & 1) when r / 2 == q
+  const bool a_live = r < 8 && (r >> 1) == q;
+  const bool a_hi = (r & 1) != 0;
+  const uint32_t xoff = (uint32_t)(32 * q + 8 * (r & 1));
+  float acc0 = 0.f, acc1 = 0.f;
+  auto process = [&](int i, const Buf &b) {
+    const uint2 sw2 = *(const uint2 *)(wsc + r * kFp4Pitch + 16 * i + 8 * (q & 1));
+    const uint2 sx2 = *(const uint2 *)(sxl + 16 * i + 8 * (q & 1));
+    const uint2 x0 = *(const uint2 *)(xsl + 128 * i + xoff);
+    const uint2 x1 = *(const uint2 *)(xsl + 128 * i + xoff + 16);
+    float sw[8], sx[8];
+    const uint32_t swd[2] = {sw2.x, sw2.y}, sxd[2] = {sx2.x, sx2.y};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const auto w0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(swd[j], 1.0f, false);
+      const auto w1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(swd[j], 1.0f, true);
+      const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sxd[j], 1.0f, false);
+      const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sxd[j], 1.0f, true);
+      sw[4 * j + 0] = w0[0]; sw[4 * j + 1] = w0[1]; sw[4 * j + 2] = w1[0]; sw[4 * j + 3] = w1[1];
+      sx[4 * j + 0] = v0[0]; sx[4 * j + 1] = v0[1]; sx[4 * j + 2] = v1[0]; sx[4 * j + 3] = v1[1];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      i32x8v bw, ax;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w = b.c[4 * h + k];
+        bw[k] = (int)(L == 2 ? autofp2_remap(w) : w);
+        bw[4 + k] = 0;
+      }
+      const uint32_t xl = a_live ? (h ? x1.x : x0.x) : 0u, xh = a_live ? (h ? x1.y : x0.y) : 0u;
+      ax[0] = (int)(a_hi ? 0u : xl);
+      ax[1] = (int)(a_hi ? 0u : xh);
+      ax[2] = (int)(a_hi ? xl : 0u);
+      ax[3] = (int)(a_hi ? xh : 0u);
+      ax[4] = ax[5] = ax[6] = ax[7] = 0;
+      const float4v d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          ax, bw, float4v{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, 127, 0, 127);
+      // D rows 4q + k <-> groups 8q + {0, 1, 4, 5}[k] + 2h (q < 2)
+      acc0 = fmaf(d[0], sw[0 + 2 * h] * sx[0 + 2 * h], acc0);
+      acc1 = fmaf(d[1], sw[1 + 2 * h] * sx[1 + 2 * h], acc1);
+      acc0 = fmaf(d[2], sw[4 + 2 * h] * sx[4 + 2 * h], acc0);
+      acc1 = fmaf(d[3], sw[5 + 2 * h] * sx[5 + 2 * h], acc1);
+    }
+  };
+
+  // 4. PD buffered chunks, each processed and then refilled PD chunks ahead
+  for (int g = 0; g < len; g += PD) {
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+      if (g + u < len) process(g + u, buf[u]);
+      vmem_fence();
+      load(g + u + PD, buf[u]);
+      vmem_fence();
+    }
+  }
+
+  // 5. rows 8..15 of D are zero: lane groups 0 and 1 hold the sums; then the
+  //    K-split wavefronts of each row tile are added in LDS
+  float acc = acc0 + acc1;
+  acc += __shfl_xor(acc, 16, 64);
+  float *red = (float *)lds;
+  __syncthreads();
+  if (lane < 16) red[wave * 16 + lane] = acc;
+  __syncthreads();
+  if (kw != 0 || rows == 0 || lane >= 16 || r >= rows) return;
+  float s = red[wave * 16 + lane];
+  for (int w = 1; w < WK; ++w) s += red[(wave + w) * 16 + lane];
+  float scale = (*a.w_T) * (*a.x_T);
+  if (L == 2) scale *= a.c2;
+  const float v = s * scale;
+  if (a.y_dtype == AUTOFP_BF16) ((uint16_t *)a.y)[n0 + r] = f32_to_bf16_rne(v);
+  else ((float *)a.y)[n0 + r] = v;
+}
+
+template <int PD>
+__global__ __launch_bounds__(1024) void gemv_fp4_kernel(LinearArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  if (a.bits == 2) fp4_tile<2, PD>(a, lds);
+  else fp4_tile<4, PD>(a, lds);
+}
+
+// ---------------------------------------------------------------------------
 // GEMV for 17..64 tokens: activations from the fp16 panel
 // ---------------------------------------------------------------------------
 
@@ -866,6 +1063,20 @@ hipError_t launch_act_dequant(const LinearArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_gemv(const LinearArgs &a0, hipStream_t s) {
+  // one token at a host-given level 2 or 4: the fp4 matrix-core kernel
+  if (a0.b == 1 && a0.bits_dev == nullptr && (a0.bits == 2 || a0.bits == 4) && a0.k % kCh == 0) {
+    const StreamCfg c = stream_cfg(a0);
+    const int64_t nch = a0.k / kCh;
+    const size_t lds = (size_t)c.waves * kFp4WaveLds;
+    if ((nch + c.wk - 1) / c.wk <= kFp4Chunks && lds <= (size_t)max_lds_per_block()) {
+      LinearArgs a1 = a0;
+      a1.wk = c.wk;
+      const int64_t tiles = (a0.n + 15) / 16;
+      const dim3 grid((unsigned)((tiles + c.rt - 1) / c.rt)), block((unsigned)(64 * c.waves));
+      hipLaunchKernelGGL((gemv_fp4_kernel<kFp4Depth>), grid, block, lds, s, a1);
+      return hipGetLastError();
+    }
+  }
   if (a0.b <= 16) {
     const StreamCfg c = stream_cfg(a0);
     LinearArgs a1 = a0;

@@ -279,3 +279,36 @@ def test_gemv_forced_waves(waves, n, b, k):
     for level in (2, 4, 6):
         y = run(A.gemv, wp, xp4, xp6, level, params=p)
         check_close(y.cpu().numpy(), O.linear(wq, xq6 if level == 6 else xq4, level))
+
+
+@pytest.mark.parametrize("n,k,waves", [(200, 256, 0), (1000, 4096, 0), (17, 2560, 1), (33, 768, 2),
+                                       (300, 14336, 0), (40, 4096 + 256, 16)])
+@pytest.mark.parametrize("level", [2, 4])
+def test_gemv_one_token_matrix_core_path(n, k, waves, level):
+    """One token at a host-given level 2 or 4 with K % 256 == 0 (the fp4
+    matrix-core GEMV): ragged row tiles, uneven and forced K splits."""
+    say(f"case: one-token gemv N={n} K={k} waves={waves} level {level}")
+    w, x = operands(n, 1, k, seed=n + k + waves)
+    wp, xp4, xp6 = gpu_pack(w, x)
+    wq, xq4, xq6 = oracle_pack(w, x)
+    p = A.default_params(gemv_waves=waves)
+    y = run(A.gemv, wp, xp4, xp6, level, params=p)
+    check_close(y.cpu().numpy(), O.linear(wq, xq4, level))
+    yb = run(A.gemv, wp, xp4, xp6, level, params=p, out_dtype=torch.bfloat16)
+    assert torch.equal(yb, y.to(torch.bfloat16)), "bf16 output is not the RNE of the fp32 result"
+
+
+@pytest.mark.parametrize("level", [2, 4])
+def test_gemv_one_token_all_scale_codes(level):
+    """Every E4M3 scale range through the one-token matrix-core GEMV (scales
+    applied in fp32 to exact per-group dot products)."""
+    say(f"case: one-token gemv all scale codes level {level}")
+    n, k = 48, 2560
+    wn = _all_scale_codes_weight(n, k, seed=13)
+    w = torch.from_numpy(wn).to(DEV)
+    x = S.activations(1, k, seed=14, tensor_id=0, device=DEV)
+    wp, xp4, xp6 = gpu_pack(w, x)
+    assert len(set(np.unique(wp.scales.cpu().numpy()).tolist())) >= 100
+    wq, xq4, xq6 = oracle_pack(w, x)
+    y = run(A.gemv, wp, xp4, xp6, level)
+    check_close(y.cpu().numpy(), O.linear(wq, xq4, level))
