@@ -636,10 +636,28 @@ __global__ __launch_bounds__(PD == 8 ? 512 : 1024) void gemv_stream_kernel(Linea
 constexpr int kFp4Chunks = 16;                          // chunks per wavefront at most
 constexpr int kFp4Pitch = kFp4Chunks * 16 + 16;            // LDS row pitch of the weight scales
 constexpr int kFp4WaveLds = 16 * kFp4Pitch + kFp4Chunks * (128 + 16);
+// level 6 adds: activation offsets as E2M1 d/2 (128 B per chunk), the offset
+// plan (64 entries of 16 selector bytes + a position) and a 256-entry table
+constexpr int kFp4WaveLds6 = kFp4WaveLds + kFp4Chunks * 128 + kPlanBytesPerWave + 512;
 constexpr int kFp4Depth = 8;                               // chunks of code loads in flight
+constexpr int kFp4Depth6 = 4;                              // level 6 (offset windows too)
+
+// Four 2-bit offsets d (two's complement, element e in bits 2e+1:2e) as four
+// E2M1 codes of d/2 in the nibbles of a 16-bit value: +1 -> 0.5 (0001),
+// 0 -> 0, -1 -> -0.5 (1001), -2 -> -1 (1010). Two bytes at once: byte j of
+// v (j = 0, 1) -> bits 16j .. 16j + 15.
+__device__ __forceinline__ uint32_t offsets_to_e2m1(uint32_t v) {
+  uint32_t t = v & 0xFFFFu;
+  t = (t | (t << 8)) & 0x00FF00FFu;
+  t = (t | (t << 4)) & 0x0F0F0F0Fu;
+  t = (t | (t << 2)) & 0x33333333u;
+  const uint32_t b0 = t & 0x11111111u, b1 = (t >> 1) & 0x11111111u;
+  return b0 | (b1 << 3) | ((b1 & ~b0) << 1);
+}
 
 template <int L, int PD>
 __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds) {
+  constexpr bool REF = (L == 6);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
@@ -657,24 +675,43 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
   const int64_t c0 = (nch * kw) / WK;
   const int64_t c1 = (nch * (kw + 1)) / WK;
   const int len = (int)(c1 - c0);   // at most kFp4Chunks
+  const int64_t R = a.n_refined;
+  const bool refine_w = REF && a.w_mask != nullptr && R > 0 && a.w_offsets != nullptr;
+  const bool refine_x = REF && a.x_offsets != nullptr;
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.w_codes + nb0 * (K >> 1), rows * (K >> 1));
   const __amdgpu_buffer_rsrc_t rsc = make_rsrc(a.w_scales + nb0 * (K >> 4), rows * (K >> 4));
+  // weight offsets: the tile's rows plus the 16 padding bytes every offsets buffer carries
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc(refine_w ? a.w_offsets + nb0 * R : a.w_codes, refine_w && rows > 0 ? rows * R + 16 : 0);
   const __amdgpu_buffer_rsrc_t rxc = make_rsrc(a.x_codes, K >> 1);
   const __amdgpu_buffer_rsrc_t rxs = make_rsrc(a.x_scales, K >> 4);
+  const __amdgpu_buffer_rsrc_t rxo = make_rsrc(refine_x ? a.x_offsets : a.x_codes, refine_x ? K >> 2 : 0);
+  const __amdgpu_buffer_rsrc_t rm = make_rsrc(refine_w ? a.w_mask : a.w_codes, refine_w ? K >> 5 : 0);
   const uint32_t crow = (uint32_t)(r * (K >> 1) + 32 * q);
+  const uint32_t orow = (uint32_t)(r * R);
 
   // wavefront-private LDS: weight scales [16 rows][kFp4Chunks chunks][16 B]
   // at a row pitch of kFp4Chunks * 16 + 16 bytes (the 16 rows' 8-byte reads
-  // then cover all 64 banks once), then the activation codes and scales of
-  // the range
-  unsigned char *wl = lds + (size_t)wave * kFp4WaveLds;
+  // then cover all 64 banks once), the activation codes and scales of the
+  // range; level 6: the activation offsets as E2M1 d/2 codes (laid out like
+  // the activation codes), the offset plan and the offset-byte table
+  unsigned char *wl = lds + (size_t)wave * (REF ? kFp4WaveLds6 : kFp4WaveLds);
   unsigned char *wsc = wl;
   unsigned char *xsl = wl + 16 * kFp4Pitch;
   unsigned char *sxl = xsl + kFp4Chunks * 128;
+  unsigned char *dxl = sxl + kFp4Chunks * 16;
+  uint4 *plan_sel = (uint4 *)(dxl + kFp4Chunks * 128);
+  int32_t *plan_pos = (int32_t *)(plan_sel + 64);
+  uint16_t *lut = (uint16_t *)(plan_pos + 64);
 
   // 1. the range's scales and activation bytes, each lane one 16-byte piece
   //    per load: weight-scale piece j * 64 + l is row l % 16, chunk 4j + l / 16
-  uint32_t pw[kFp4Chunks / 4][4], px[2][4], ps[4];
+  uint32_t pw[kFp4Chunks / 4][4], px[2][4], ps[4], pd[4] = {0, 0, 0, 0}, pm = 0;
+  if (refine_w) {
+    // mask bits of lane e = 4 * chunk + q: the 16 subgroups of its 64 elements
+    const uint32_t o = (lane >> 2) < len ? (uint32_t)(8 * (c0 + (lane >> 2)) + 2 * (lane & 3)) : kOOB;
+    pm = __builtin_amdgcn_raw_buffer_load_b16(rm, (int)o, 0, 0);
+  }
 #pragma unroll
   for (int j = 0; j < kFp4Chunks / 4; ++j) {
     const int p = 4 * j + q;
@@ -694,11 +731,44 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
     const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rxs, (int)o, 0, 0);
     ps[0] = v[0]; ps[1] = v[1]; ps[2] = v[2]; ps[3] = v[3];
   }
+  if (refine_x) {
+    const uint32_t o = lane < 4 * len ? (uint32_t)(64 * c0 + 16 * lane) : kOOB;
+    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rxo, (int)o, 0, 0);
+    pd[0] = v[0]; pd[1] = v[1]; pd[2] = v[2]; pd[3] = v[3];
+  }
   vmem_fence();
 
-  // 2. the first PD chunks of weight codes
+  // 2. level 6: refined subgroups before the range, and the offset plan
+  //    (the mask is shared by every row, so one plan serves the 16 rows)
+  if (refine_w) {
+    int32_t before = 0;
+    const int64_t mdw = 2 * c0;   // mask dwords before the range
+    for (int64_t i = lane; i < mdw; i += 64) before += __popc(ld_b32(rm, (uint32_t)(4 * i)));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) before += __shfl_xor(before, o, 64);
+    const uint32_t m16 = pm & 0xFFFFu;
+    const int32_t cnt = __popc(m16);
+    int32_t incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    const PlanEntry pe = make_entry(m16, before + incl - cnt);
+    plan_sel[lane] = make_uint4(pe.sel[0], pe.sel[1], pe.sel[2], pe.sel[3]);
+    plan_pos[lane] = pe.pos;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t b = 4 * lane + 2 * j;
+      *(uint32_t *)(lut + b) = offsets_to_e2m1(b | ((b + 1) << 8));
+    }
+  }
+
+  // 3. the first PD chunks of weight codes (and level-6 offset windows)
   struct Buf {
     uint32_t c[8];   // 64 weight codes
+    uint32_t o[3];   // offset dwords covering the lane's offset window
+    uint32_t sh;     // byte position of the window in o
   };
   auto load = [&](int i, Buf &b) {
     const bool live = i < len;
@@ -708,6 +778,13 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
     const u32x4v hi = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(vo + 16), (int)so, 0);
     b.c[0] = lo[0]; b.c[1] = lo[1]; b.c[2] = lo[2]; b.c[3] = lo[3];
     b.c[4] = hi[0]; b.c[5] = hi[1]; b.c[6] = hi[2]; b.c[7] = hi[3];
+    if (refine_w) {
+      const int32_t pos = live ? plan_pos[4 * i + q] : 0;
+      const uint32_t at = orow + (uint32_t)pos;
+      const u32x3v v = __builtin_amdgcn_raw_buffer_load_b96(ro, (int)(live ? at & ~3u : kOOB), 0, 0);
+      b.o[0] = v[0]; b.o[1] = v[1]; b.o[2] = v[2];
+      b.sh = at & 3u;
+    }
   };
   Buf buf[PD];
 #pragma unroll
@@ -716,7 +793,7 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
     vmem_fence();
   }
 
-  // 3. prologue bytes to LDS (waits for them only: the code loads stay in flight)
+  // 4. prologue bytes to LDS (waits for them only: the code loads stay in flight)
 #pragma unroll
   for (int j = 0; j < kFp4Chunks / 4; ++j)
     *(uint4 *)(wsc + r * kFp4Pitch + 16 * (4 * j + q)) = make_uint4(pw[j][0], pw[j][1], pw[j][2], pw[j][3]);
@@ -724,17 +801,37 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
   for (int j = 0; j < 2; ++j)
     *(uint4 *)(xsl + 16 * (64 * j + lane)) = make_uint4(px[j][0], px[j][1], px[j][2], px[j][3]);
   if (lane < kFp4Chunks) *(uint4 *)(sxl + 16 * lane) = make_uint4(ps[0], ps[1], ps[2], ps[3]);
+  if (REF) {
+    // 64 offsets (16 bytes) -> 64 E2M1 codes (32 bytes)
+    uint32_t e[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      e[2 * j] = offsets_to_e2m1(pd[j]);
+      e[2 * j + 1] = offsets_to_e2m1(pd[j] >> 16);
+    }
+    *(uint4 *)(dxl + 32 * lane) = make_uint4(e[0], e[1], e[2], e[3]);
+    *(uint4 *)(dxl + 32 * lane + 16) = make_uint4(e[4], e[5], e[6], e[7]);
+  }
 
-  // A operand: lane (s = r, q) carries group 4q + 2h + (r & 1) when r / 2 == q
-  const bool a_live = r < 8 && (r >> 1) == q;
+  // A operand: lane (s = r, q) carries, in A row s, group 4q + 2h + (s & 1)
+  // of the activation codes (s < 8) or of its offsets d/2 (s >= 8, level 6)
+  // when (s & 7) / 2 == q
+  const bool a_live = ((r & 7) >> 1) == q && (r < 8 || REF);
   const bool a_hi = (r & 1) != 0;
-  const uint32_t xoff = (uint32_t)(32 * q + 8 * (r & 1));
+  const unsigned char *abase = (r < 8 ? xsl : dxl) + 32 * q + 8 * (r & 1);
   float acc0 = 0.f, acc1 = 0.f;
   auto process = [&](int i, const Buf &b) {
     const uint2 sw2 = *(const uint2 *)(wsc + r * kFp4Pitch + 16 * i + 8 * (q & 1));
     const uint2 sx2 = *(const uint2 *)(sxl + 16 * i + 8 * (q & 1));
-    const uint2 x0 = *(const uint2 *)(xsl + 128 * i + xoff);
-    const uint2 x1 = *(const uint2 *)(xsl + 128 * i + xoff + 16);
+    const uint2 x0 = *(const uint2 *)(abase + 128 * i);
+    const uint2 x1 = *(const uint2 *)(abase + 128 * i + 16);
+    uint4 sel = make_uint4(0, 0, 0, 0);
+    uint32_t wlo = 0, whi = 0;
+    if (refine_w) {
+      sel = plan_sel[4 * i + q];
+      wlo = __builtin_amdgcn_alignbyte(b.o[1], b.o[0], b.sh);
+      whi = __builtin_amdgcn_alignbyte(b.o[2], b.o[1], b.sh);
+    }
     float sw[8], sx[8];
     const uint32_t swd[2] = {sw2.x, sw2.y}, sxd[2] = {sx2.x, sx2.y};
 #pragma unroll
@@ -761,9 +858,22 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
       ax[2] = (int)(a_hi ? xl : 0u);
       ax[3] = (int)(a_hi ? xh : 0u);
       ax[4] = ax[5] = ax[6] = ax[7] = 0;
-      const float4v d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+      float4v d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
           ax, bw, float4v{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, 127, 0, 127);
-      // D rows 4q + k <-> groups 8q + {0, 1, 4, 5}[k] + 2h (q < 2)
+      if (refine_w) {
+        // weight offsets d_W / 2 of the lane's 8 subgroup slots, as E2M1,
+        // added at scale 2^-2: D += A * (d_W / 2) / 4 = A * d_W / 8
+        const uint32_t e0 = __builtin_amdgcn_perm(whi, wlo, h ? sel.z : sel.x);
+        const uint32_t e1 = __builtin_amdgcn_perm(whi, wlo, h ? sel.w : sel.y);
+        i32x8v bo;
+        bo[0] = (int)(lut[e0 & 0xFFu] | ((uint32_t)lut[(e0 >> 8) & 0xFFu] << 16));
+        bo[1] = (int)(lut[(e0 >> 16) & 0xFFu] | ((uint32_t)lut[e0 >> 24] << 16));
+        bo[2] = (int)(lut[e1 & 0xFFu] | ((uint32_t)lut[(e1 >> 8) & 0xFFu] << 16));
+        bo[3] = (int)(lut[(e1 >> 16) & 0xFFu] | ((uint32_t)lut[e1 >> 24] << 16));
+        bo[4] = bo[5] = bo[6] = bo[7] = 0;
+        d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ax, bo, d, 4, 4, 0, 127, 0, 125);
+      }
+      // D rows 4q + k <-> groups 8 (q & 1) + {0, 1, 4, 5}[k] + 2h
       acc0 = fmaf(d[0], sw[0 + 2 * h] * sx[0 + 2 * h], acc0);
       acc1 = fmaf(d[1], sw[1 + 2 * h] * sx[1 + 2 * h], acc1);
       acc0 = fmaf(d[2], sw[4 + 2 * h] * sx[4 + 2 * h], acc0);
@@ -771,7 +881,7 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
     }
   };
 
-  // 4. PD buffered chunks, each processed and then refilled PD chunks ahead
+  // 5. PD buffered chunks, each processed and then refilled PD chunks ahead
   for (int g = 0; g < len; g += PD) {
 #pragma unroll
     for (int u = 0; u < PD; ++u) {
@@ -782,9 +892,11 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
     }
   }
 
-  // 5. rows 8..15 of D are zero: lane groups 0 and 1 hold the sums; then the
-  //    K-split wavefronts of each row tile are added in LDS
-  float acc = acc0 + acc1;
+  // 6. D rows 8..15 (lane groups 2, 3) hold the products with d_A / 2, worth
+  //    a quarter (zero below level 6); the K-split wavefronts of each row
+  //    tile are then added in LDS
+  float acc = (acc0 + acc1) * (q < 2 ? 1.0f : 0.25f);
+  acc += __shfl_xor(acc, 32, 64);
   acc += __shfl_xor(acc, 16, 64);
   float *red = (float *)lds;
   __syncthreads();
@@ -800,11 +912,12 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
   else ((float *)a.y)[n0 + r] = v;
 }
 
-template <int PD>
 __global__ __launch_bounds__(1024) void gemv_fp4_kernel(LinearArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
-  if (a.bits == 2) fp4_tile<2, PD>(a, lds);
-  else fp4_tile<4, PD>(a, lds);
+  const int L = run_level(a);
+  if (L == 6) fp4_tile<6, kFp4Depth6>(a, lds);
+  else if (L == 2) fp4_tile<2, kFp4Depth>(a, lds);
+  else fp4_tile<4, kFp4Depth>(a, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1064,16 +1177,17 @@ hipError_t launch_act_dequant(const LinearArgs &a, hipStream_t s) {
 
 hipError_t launch_gemv(const LinearArgs &a0, hipStream_t s) {
   // one token at a host-given level 2 or 4: the fp4 matrix-core kernel
-  if (a0.b == 1 && a0.bits_dev == nullptr && (a0.bits == 2 || a0.bits == 4) && a0.k % kCh == 0) {
+  if (a0.b == 1 && a0.k % kCh == 0) {
     const StreamCfg c = stream_cfg(a0);
     const int64_t nch = a0.k / kCh;
-    const size_t lds = (size_t)c.waves * kFp4WaveLds;
+    const bool six = a0.bits_dev != nullptr || a0.bits == 6;
+    const size_t lds = (size_t)c.waves * (six ? kFp4WaveLds6 : kFp4WaveLds);
     if ((nch + c.wk - 1) / c.wk <= kFp4Chunks && lds <= (size_t)max_lds_per_block()) {
       LinearArgs a1 = a0;
       a1.wk = c.wk;
       const int64_t tiles = (a0.n + 15) / 16;
       const dim3 grid((unsigned)((tiles + c.rt - 1) / c.rt)), block((unsigned)(64 * c.waves));
-      hipLaunchKernelGGL((gemv_fp4_kernel<kFp4Depth>), grid, block, lds, s, a1);
+      hipLaunchKernelGGL(gemv_fp4_kernel, grid, block, lds, s, a1);
       return hipGetLastError();
     }
   }

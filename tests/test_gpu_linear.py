@@ -283,22 +283,41 @@ def test_gemv_forced_waves(waves, n, b, k):
 
 @pytest.mark.parametrize("n,k,waves", [(200, 256, 0), (1000, 4096, 0), (17, 2560, 1), (33, 768, 2),
                                        (300, 14336, 0), (40, 4096 + 256, 16)])
-@pytest.mark.parametrize("level", [2, 4])
+@pytest.mark.parametrize("level", [2, 4, 6])
 def test_gemv_one_token_matrix_core_path(n, k, waves, level):
-    """One token at a host-given level 2 or 4 with K % 256 == 0 (the fp4
-    matrix-core GEMV): ragged row tiles, uneven and forced K splits."""
+    """One token with K % 256 == 0 (the fp4 matrix-core GEMV): ragged row
+    tiles, uneven and forced K splits, host- and device-side level."""
     say(f"case: one-token gemv N={n} K={k} waves={waves} level {level}")
     w, x = operands(n, 1, k, seed=n + k + waves)
     wp, xp4, xp6 = gpu_pack(w, x)
     wq, xq4, xq6 = oracle_pack(w, x)
     p = A.default_params(gemv_waves=waves)
     y = run(A.gemv, wp, xp4, xp6, level, params=p)
-    check_close(y.cpu().numpy(), O.linear(wq, xq4, level))
+    check_close(y.cpu().numpy(), O.linear(wq, xq6 if level == 6 else xq4, level))
     yb = run(A.gemv, wp, xp4, xp6, level, params=p, out_dtype=torch.bfloat16)
     assert torch.equal(yb, y.to(torch.bfloat16)), "bf16 output is not the RNE of the fp32 result"
+    dev_bits = torch.tensor([level], dtype=torch.int32, device=DEV)
+    yd = A.gemv(wp, xp6, bits=0, bits_dev=dev_bits, params=p)   # refinement unused below level 6
+    assert torch.equal(yd, y), "device-side level differs from the host-given level"
 
 
-@pytest.mark.parametrize("level", [2, 4])
+@pytest.mark.parametrize("n,k", [(64, 4096), (48, 1024)])
+def test_gemv_one_token_overlapping_refinement(n, k):
+    """Activation refined in subgroups the weight also refines (no exclusion
+    mask): the product needs the d_W * d_A / 64 term too."""
+    say(f"case: one-token gemv overlapping refinement N={n} K={k}")
+    w, x = operands(n, 1, k, seed=n * 3 + k)
+    wp = A.quantize_weight(w, refine=True)
+    xp = A.quantize_activation(x, refine=True)
+    wq, _, _ = oracle_pack(w, x)
+    xq = O.quantize_activation(x.float().cpu().numpy(), refine=True)
+    both = (wq["mask"][None, :] & xq["mask"]).any()
+    assert both, "the case needs subgroups refined on both sides"
+    y = A.gemv(wp, xp, bits=6)
+    check_close(y.cpu().numpy(), O.linear(wq, xq, 6))
+
+
+@pytest.mark.parametrize("level", [2, 4, 6])
 def test_gemv_one_token_all_scale_codes(level):
     """Every E4M3 scale range through the one-token matrix-core GEMV (scales
     applied in fp32 to exact per-group dot products)."""
@@ -311,4 +330,4 @@ def test_gemv_one_token_all_scale_codes(level):
     assert len(set(np.unique(wp.scales.cpu().numpy()).tolist())) >= 100
     wq, xq4, xq6 = oracle_pack(w, x)
     y = run(A.gemv, wp, xp4, xp6, level)
-    check_close(y.cpu().numpy(), O.linear(wq, xq4, level))
+    check_close(y.cpu().numpy(), O.linear(wq, xq6 if level == 6 else xq4, level))
