@@ -377,7 +377,7 @@ def main():
     achieved = g_bytes / (ms_g * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
-                "kernel": "gemv_stream_kernel (batch <= 16)",
+                "kernel": "gemv_fp4_kernel (one token)",
                 "avg_launch_us": round(ms_g * 1e3 / n_launch, 3),
                 "bytes_per_launch": int(g_bytes / n_launch)}
     log(f"gemv-only: {ms_g:.4f} ms per {n_launch} launches, {achieved:.1f} GB/s")

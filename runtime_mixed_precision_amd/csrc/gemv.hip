@@ -1160,6 +1160,42 @@ StreamCfg stream_cfg(const LinearArgs &a) {
   return c;
 }
 
+// Launch shape of the one-token matrix-core GEMV. When the row tiles split
+// evenly over the compute units, 256 blocks of tiles / 256 tiles each, so
+// every CU streams the same bytes (with 1 or 2 blocks per CU, a CU holding
+// two finishes last: the per-CU load rate, not HBM, bounds a CU); the
+// blocks' LDS keeps them one per CU. Otherwise the streaming kernel's shape.
+struct Fp4Cfg {
+  int wk, rt;
+  size_t lds;
+  bool ok;
+};
+
+Fp4Cfg fp4_cfg(const LinearArgs &a, bool six) {
+  Fp4Cfg c{};
+  const int64_t nch = a.k / kCh;
+  const int64_t tiles = (a.n + 15) / 16;
+  const int64_t kCUs = 256;
+  const int64_t per_cu = tiles / kCUs;
+  if (tiles % kCUs == 0 && per_cu >= 2 && per_cu <= kMaxWaves) {
+    c.rt = (int)per_cu;
+    int wk = a.waves > 0 ? a.waves : 1;
+    while ((nch + wk - 1) / wk > kFp4Chunks) ++wk;
+    if (a.waves == 0) {
+      while (c.rt * wk * 2 <= kMaxWaves && nch / (2 * wk) >= 8) wk *= 2;
+    }
+    c.wk = wk;
+  } else {
+    const StreamCfg sc = stream_cfg(a);
+    c.wk = sc.wk;
+    c.rt = sc.rt;
+  }
+  c.lds = (size_t)c.wk * c.rt * (six ? kFp4WaveLds6 : kFp4WaveLds);
+  c.ok = c.wk * c.rt <= kMaxWaves && (nch + c.wk - 1) / c.wk <= kFp4Chunks &&
+         c.lds <= (size_t)max_lds_per_block();
+  return c;
+}
+
 }  // namespace
 
 int64_t xh_kpad(int64_t k) { return round_up(k, kCh); }
@@ -1178,16 +1214,14 @@ hipError_t launch_act_dequant(const LinearArgs &a, hipStream_t s) {
 hipError_t launch_gemv(const LinearArgs &a0, hipStream_t s) {
   // one token at a host-given level 2 or 4: the fp4 matrix-core kernel
   if (a0.b == 1 && a0.k % kCh == 0) {
-    const StreamCfg c = stream_cfg(a0);
-    const int64_t nch = a0.k / kCh;
     const bool six = a0.bits_dev != nullptr || a0.bits == 6;
-    const size_t lds = (size_t)c.waves * (six ? kFp4WaveLds6 : kFp4WaveLds);
-    if ((nch + c.wk - 1) / c.wk <= kFp4Chunks && lds <= (size_t)max_lds_per_block()) {
+    const Fp4Cfg c = fp4_cfg(a0, six);
+    if (c.ok) {
       LinearArgs a1 = a0;
       a1.wk = c.wk;
       const int64_t tiles = (a0.n + 15) / 16;
-      const dim3 grid((unsigned)((tiles + c.rt - 1) / c.rt)), block((unsigned)(64 * c.waves));
-      hipLaunchKernelGGL(gemv_fp4_kernel, grid, block, lds, s, a1);
+      const dim3 grid((unsigned)((tiles + c.rt - 1) / c.rt)), block((unsigned)(64 * c.wk * c.rt));
+      hipLaunchKernelGGL(gemv_fp4_kernel, grid, block, c.lds, s, a1);
       return hipGetLastError();
     }
   }
