@@ -199,6 +199,139 @@ class DecodeBench:
         return tot
 
 
+class Step32:
+    """The full decode step of a 32-layer Llama-3-8B-shaped model under the
+    device-side policy: G_E of the step's logits, then per layer the encode
+    of each linear input, a = Wqkv h (first 4096 outputs as the attention
+    stand-in), o = Wo a, h1 = h + o, [g|u] = Wgate|Wup h1, f = silu(g) * u,
+    h2 = h1 + Wdown f, L_A(h, h2) and the policy update, whose level the next
+    layer's GEMVs read on the device. Several consecutive steps (logits drawn
+    per step) form one HIP graph; the levels chosen are logged on the device
+    and read back after timing."""
+
+    def __init__(self, A, S, layers, batch, device, steps=4):
+        import torch
+        self.A, self.S, self.layers, self.b, self.T = A, S, layers, batch, steps
+        H, F, V = S.HIDDEN, S.FFN, S.VOCAB
+        self.H, self.F, self.V = H, F, V
+        L = len(layers)
+        self.h0 = S.hidden(batch, H, seed=41, tensor_id=0, dtype=torch.float32, device=device)
+        self.logits = [S.logits(batch, V, seed=42 + s, device=device) for s in range(steps)]
+        self.xh = A.alloc_activation(batch, H, refine=True, device=device)
+        self.xf = A.alloc_activation(batch, F, refine=True, device=device)
+        self.qws = {k: torch.empty(A.workspace_bytes(0, batch, k), dtype=torch.uint8, device=device) for k in (H, F)}
+        self.gws = {k: torch.empty(A.workspace_bytes(2, batch, k), dtype=torch.uint8, device=device) for k in (H, F)}
+        self.sws = torch.empty(A.workspace_bytes(4, batch, V), dtype=torch.uint8, device=device)
+        self.y = {"wqkv": torch.empty(batch, 3 * 2048, device=device), "wo": torch.empty(batch, H, device=device),
+                  "wgateup": torch.empty(batch, 2 * F, device=device), "wdown": torch.empty(batch, H, device=device)}
+        self.h = torch.empty(batch, H, device=device)
+        self.h1 = torch.empty(batch, H, device=device)
+        self.h2 = torch.empty(batch, H, device=device)
+        self.a = torch.empty(batch, H, device=device)
+        self.f = torch.empty(batch, F, device=device)
+        self.g_e = torch.empty(batch, device=device)
+        self.l_a = torch.empty(batch, device=device)
+        self.rows = torch.empty(batch, dtype=torch.int32, device=device)
+        self.lay = torch.empty(steps, L + 1, dtype=torch.int32, device=device)
+        self.state = A.policy_state(batch, device)
+
+    def run(self):
+        A = self.A
+        for s in range(self.T):
+            lay = self.lay[s]
+            A.policy_signals(logits=self.logits[s], out_entropy=self.g_e, workspace=self.sws)
+            self.h.copy_(self.h0)
+            lay[0].fill_(4)                                   # a decode step starts at 4 bits
+            for i, w in enumerate(self.layers):
+                bits = lay[i:i + 1]
+                A.quantize_into(self.h, self.xh, refine=True, exclude_mask=w["wqkv"].mask, workspace=self.qws[self.H])
+                A.gemv(w["wqkv"], self.xh, bits_dev=bits, out=self.y["wqkv"], workspace=self.gws[self.H])
+                self.a.copy_(self.y["wqkv"][:, :self.H])
+                A.quantize_into(self.a, self.xh, refine=True, exclude_mask=w["wo"].mask, workspace=self.qws[self.H])
+                A.gemv(w["wo"], self.xh, bits_dev=bits, out=self.y["wo"], workspace=self.gws[self.H])
+                torch_add(self.h, self.y["wo"], self.h1)
+                A.quantize_into(self.h1, self.xh, refine=True, exclude_mask=w["wgateup"].mask,
+                                workspace=self.qws[self.H])
+                A.gemv(w["wgateup"], self.xh, bits_dev=bits, out=self.y["wgateup"], workspace=self.gws[self.H])
+                silu_mul(self.y["wgateup"], self.F, self.f)
+                A.quantize_into(self.f, self.xf, refine=True, exclude_mask=w["wdown"].mask, workspace=self.qws[self.F])
+                A.gemv(w["wdown"], self.xf, bits_dev=bits, out=self.y["wdown"], workspace=self.gws[self.F])
+                torch_add(self.h1, self.y["wdown"], self.h2)
+                A.policy_signals(h_prev=self.h, h_cur=self.h2, out_update=self.l_a)
+                A.policy_update(1, i, self.l_a, self.state, g_e=self.g_e, new_sequence=(s == 0 and i == 0),
+                                bits_rows=self.rows, bits_layer=lay[i + 1:i + 2])
+                self.h.copy_(self.h2)
+
+    def bytes_of(self, lay):
+        """Algorithmic bytes of the logged steps: packed weights at the level
+        each layer ran, the encoded activations (fp32 in, packed out), GEMV
+        outputs, the logits and the L_A reads."""
+        b, tot = self.b, 0
+        for s in range(self.T):
+            tot += 4 * b * self.V
+            for i, w in enumerate(self.layers):
+                L = int(lay[s][i])
+                for name, wp in w.items():
+                    tot += 4 * b * wp.k + gemv_bytes(wp, b, L)
+                tot += 2 * 4 * b * self.H
+        return tot
+
+
+def torch_add(x, y, out):
+    import torch
+    torch.add(x, y, out=out)
+
+
+def silu_mul(gu, F, out):
+    import torch
+    torch.mul(torch.nn.functional.silu(gu[:, :F]), gu[:, F:], out=out)
+
+
+def step32_bench(A, S, device, batches=(1, 16, 64), reps=3):
+    """C4: the 32-layer step at each batch size, four steps per graph."""
+    import torch
+    layers = []
+    for i in range(32):
+        layer = {}
+        for j, (name, n, k) in enumerate(SHAPES):
+            w = S.weights(n, k, seed=300 + i, tensor_id=j, device=device)
+            layer[name] = A.quantize_weight(w, refine=True)
+            del w
+        layers.append(layer)
+    torch.cuda.synchronize()
+    log("packed 32 layers for the 32-layer step")
+    out = {"workload": "32 Llama-3-8B-shaped layers (Wqkv, Wo, Wgate|Wup, Wdown; 128256-wide logits), "
+                       "levels chosen per layer on the device (G_E + L_A policy), 4 steps per graph"}
+    for b in batches:
+        m = Step32(A, S, layers, b, device)
+        m.state.zero_()
+        m.run()                                   # eager pass: code objects, buffers
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        m.state.zero_()
+        with torch.cuda.graph(g):
+            m.run()
+        g.replay()
+        torch.cuda.synchronize()
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record()
+        for _ in range(reps):
+            g.replay()
+        en.record()
+        torch.cuda.synchronize()
+        ms = st.elapsed_time(en) / (reps * m.T)
+        lay = m.lay.cpu().tolist()
+        by = m.bytes_of(lay) / m.T
+        mix = {str(L): sum(row[:32].count(L) for row in lay) for L in (2, 4, 6)}
+        out[f"b{b}"] = {"ms_per_step": round(ms, 4), "gbs": round(by / (ms * 1e-3) / 1e9, 1),
+                        "mb_per_step": round(by / 1e6, 1), "level_mix_layers": mix}
+        log(f"32-layer step, batch {b}: {ms:.3f} ms, {by / (ms * 1e-3) / 1e9:.1f} GB/s, levels {mix}")
+        del m, g
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
 def capture(fn_list):
     import torch
     graphs = []
@@ -337,6 +470,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-batches", action="store_true", help="skip the batch-16/64 and 70B-shape GEMV lines")
+    ap.add_argument("--no-step32", action="store_true", help="skip the 32-layer policy-driven step")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run only the workload of the HBM-counter runs (no JSON line)")
     args = ap.parse_args()
@@ -420,6 +554,10 @@ def main():
     if not args.no_prefill:
         del graphs, ggraphs
         extra["prefill_gemm"] = prefill_bench(A, S, device, 5)
+    if not args.no_step32:
+        del pool, bench
+        torch.cuda.empty_cache()
+        extra["step32"] = step32_bench(A, S, device)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.batch)
