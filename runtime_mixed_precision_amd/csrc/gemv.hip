@@ -635,10 +635,12 @@ __global__ __launch_bounds__(PD == 8 ? 512 : 1024) void gemv_stream_kernel(Linea
 // of D, i.e. for q < 2 the groups 8q + {0, 1, 4, 5} + 2h of weight row r.
 constexpr int kFp4Chunks = 16;                          // chunks per wavefront at most
 constexpr int kFp4Pitch = kFp4Chunks * 16 + 16;            // LDS row pitch of the weight scales
-constexpr int kFp4WaveLds = 16 * kFp4Pitch + kFp4Chunks * (128 + 16);
+constexpr int kFp4WaveLds = 16 * kFp4Pitch + kFp4Chunks * (128 + 64);
 // level 6 adds: activation offsets as E2M1 d/2 (128 B per chunk), the offset
 // plan (64 entries of 16 selector bytes + a position) and a 256-entry table
 constexpr int kFp4WaveLds6 = kFp4WaveLds + kFp4Chunks * 128 + kPlanBytesPerWave + 512;
+// levels 2 and 4: a 2 KB slot where each chunk's codes change lane layout
+constexpr int kFp4WaveLds4 = kFp4WaveLds + 2048;
 constexpr int kFp4Depth = 8;                               // chunks of code loads in flight
 constexpr int kFp4Depth6 = 4;                              // level 6 (offset windows too)
 
@@ -655,9 +657,10 @@ __device__ __forceinline__ uint32_t offsets_to_e2m1(uint32_t v) {
   return b0 | (b1 << 3) | ((b1 & ~b0) << 1);
 }
 
-template <int L, int PD>
+template <int L, int PD, bool ROWS>
 __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds) {
   constexpr bool REF = (L == 6);
+  constexpr bool P3 = ROWS && !REF;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
@@ -692,17 +695,18 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
 
   // wavefront-private LDS: weight scales [16 rows][kFp4Chunks chunks][16 B]
   // at a row pitch of kFp4Chunks * 16 + 16 bytes (the 16 rows' 8-byte reads
-  // then cover all 64 banks once), the activation codes and scales of the
-  // range; level 6: the activation offsets as E2M1 d/2 codes (laid out like
-  // the activation codes), the offset plan and the offset-byte table
-  unsigned char *wl = lds + (size_t)wave * (REF ? kFp4WaveLds6 : kFp4WaveLds);
+  // then cover all 64 banks once), the activation codes and scales (fp32) of
+  // the range; level 6: the activation offsets as E2M1 d/2 codes (laid out
+  // like the activation codes), the offset plan and the offset-byte table
+  unsigned char *wl = lds + (size_t)wave * (REF ? kFp4WaveLds6 : kFp4WaveLds4);
   unsigned char *wsc = wl;
   unsigned char *xsl = wl + 16 * kFp4Pitch;
-  unsigned char *sxl = xsl + kFp4Chunks * 128;
-  unsigned char *dxl = sxl + kFp4Chunks * 16;
+  float *sxf = (float *)(xsl + kFp4Chunks * 128);
+  unsigned char *dxl = (unsigned char *)(sxf + kFp4Chunks * 16);
   uint4 *plan_sel = (uint4 *)(dxl + kFp4Chunks * 128);
   int32_t *plan_pos = (int32_t *)(plan_sel + 64);
   uint16_t *lut = (uint16_t *)(plan_pos + 64);
+  unsigned char *tsl = dxl;   // levels 2 and 4: the code transpose slot
 
   // 1. the range's scales and activation bytes, each lane one 16-byte piece
   //    per load: weight-scale piece j * 64 + l is row l % 16, chunk 4j + l / 16
@@ -770,12 +774,24 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
     uint32_t o[3];   // offset dwords covering the lane's offset window
     uint32_t sh;     // byte position of the window in o
   };
+  // With ROWS, levels 2 and 4 load whole rows: load A brings rows 0..7 of the chunk
+  // (lane l: row l / 8), load B rows 8..15, each 8 lanes one 128-byte row;
+  // lane slot s of row rho holds 16-byte piece s ^ (rho / 2) (the XOR keeps
+  // the transposed reads in process free of bank conflicts). Non-temporal:
+  // the codes are read once. Otherwise, and always at level 6 (its offset
+  // windows follow it), the MFMA lane layout: lane (r, q) loads bytes
+  // 32q .. 32q + 31 of row r. Whole rows read faster (8 full 128-byte lines
+  // per load instead of 16 half lines) but put an LDS round trip in each
+  // chunk: worth it when the launch has enough wavefronts to hide it.
+  const uint32_t rowA = (uint32_t)(lane >> 3), rowB = rowA + 8;
+  const uint32_t pA = (uint32_t)(((lane & 7) ^ (rowA >> 1)) * 16), pB = (uint32_t)(((lane & 7) ^ (rowB >> 1)) * 16);
+  const uint32_t voA = P3 ? rowA * (uint32_t)(K >> 1) + pA : crow;
+  const uint32_t voB = P3 ? rowB * (uint32_t)(K >> 1) + pB : crow + 16;
   auto load = [&](int i, Buf &b) {
     const bool live = i < len;
     const uint32_t so = live ? (uint32_t)((c0 + i) * 128) : 0u;
-    const uint32_t vo = live ? crow : kOOB;
-    const u32x4v lo = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)vo, (int)so, 0);
-    const u32x4v hi = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(vo + 16), (int)so, 0);
+    const u32x4v lo = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(live ? voA : kOOB), (int)so, P3 ? 2 : 0);
+    const u32x4v hi = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(live ? voB : kOOB), (int)so, P3 ? 2 : 0);
     b.c[0] = lo[0]; b.c[1] = lo[1]; b.c[2] = lo[2]; b.c[3] = lo[3];
     b.c[4] = hi[0]; b.c[5] = hi[1]; b.c[6] = hi[2]; b.c[7] = hi[3];
     if (refine_w) {
@@ -800,7 +816,15 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     *(uint4 *)(xsl + 16 * (64 * j + lane)) = make_uint4(px[j][0], px[j][1], px[j][2], px[j][3]);
-  if (lane < kFp4Chunks) *(uint4 *)(sxl + 16 * lane) = make_uint4(ps[0], ps[1], ps[2], ps[3]);
+  if (lane < kFp4Chunks) {
+    // the chunk's 16 activation group scales as fp32
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ps[j], 1.0f, false);
+      const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ps[j], 1.0f, true);
+      *(float4v *)(sxf + 16 * lane + 4 * j) = float4v{v0[0], v0[1], v1[0], v1[1]};
+    }
+  }
   if (REF) {
     // 64 offsets (16 bytes) -> 64 E2M1 codes (32 bytes)
     uint32_t e[8];
@@ -816,13 +840,54 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
   // A operand: lane (s = r, q) carries, in A row s, group 4q + 2h + (s & 1)
   // of the activation codes (s < 8) or of its offsets d/2 (s >= 8, level 6)
   // when (s & 7) / 2 == q
+  //    (levels 2 and 4: MFMA h sees bytes 64h + 16q .. + 15 of row r in lane
+  //    group q, so A row s < 8 is group 8h + s)
   const bool a_live = ((r & 7) >> 1) == q && (r < 8 || REF);
   const bool a_hi = (r & 1) != 0;
-  const unsigned char *abase = (r < 8 ? xsl : dxl) + 32 * q + 8 * (r & 1);
+  const unsigned char *abase = P3 ? xsl + 8 * r : (r < 8 ? xsl : dxl) + 32 * q + 8 * (r & 1);
   float acc0 = 0.f, acc1 = 0.f;
+  auto process3 = [&](int i, const Buf &b) {
+    // whole rows -> MFMA lane layout: lane (r, q) takes pieces 4h + q of row r
+    *(uint4 *)(tsl + 16 * lane) = make_uint4(b.c[0], b.c[1], b.c[2], b.c[3]);
+    *(uint4 *)(tsl + 1024 + 16 * lane) = make_uint4(b.c[4], b.c[5], b.c[6], b.c[7]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 wv = *(const uint4 *)(tsl + 128 * r + 16 * ((4 * h + q) ^ (r >> 1)));
+      const uint2 xv = *(const uint2 *)(abase + 128 * i + 64 * h);
+      const uint32_t swd = *(const uint32_t *)(wsc + r * kFp4Pitch + 16 * i + 8 * h + 4 * (q & 1));
+      const float4v sx = *(const float4v *)(sxf + 16 * i + 8 * h + 4 * (q & 1));
+      const auto w0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(swd, 1.0f, false);
+      const auto w1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(swd, 1.0f, true);
+      i32x8v bw, ax;
+      const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        bw[k] = (int)(L == 2 ? autofp2_remap(wd[k]) : wd[k]);
+        bw[4 + k] = 0;
+      }
+      const uint32_t xl = a_live ? xv.x : 0u, xh = a_live ? xv.y : 0u;
+      ax[0] = (int)(a_hi ? 0u : xl);
+      ax[1] = (int)(a_hi ? 0u : xh);
+      ax[2] = (int)(a_hi ? xl : 0u);
+      ax[3] = (int)(a_hi ? xh : 0u);
+      ax[4] = ax[5] = ax[6] = ax[7] = 0;
+      const float4v d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          ax, bw, float4v{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, 127, 0, 127);
+      // D rows 4q + k <-> group 8h + 4 (q & 1) + k
+      acc0 = fmaf(d[0], w0[0] * sx[0], acc0);
+      acc1 = fmaf(d[1], w0[1] * sx[1], acc1);
+      acc0 = fmaf(d[2], w1[0] * sx[2], acc0);
+      acc1 = fmaf(d[3], w1[1] * sx[3], acc1);
+    }
+  };
   auto process = [&](int i, const Buf &b) {
+    if (P3) {
+      process3(i, b);
+      return;
+    }
     const uint2 sw2 = *(const uint2 *)(wsc + r * kFp4Pitch + 16 * i + 8 * (q & 1));
-    const uint2 sx2 = *(const uint2 *)(sxl + 16 * i + 8 * (q & 1));
+    const float4v sxa = *(const float4v *)(sxf + 16 * i + 8 * (q & 1));
+    const float4v sxb = *(const float4v *)(sxf + 16 * i + 8 * (q & 1) + 4);
     const uint2 x0 = *(const uint2 *)(abase + 128 * i);
     const uint2 x1 = *(const uint2 *)(abase + 128 * i + 16);
     uint4 sel = make_uint4(0, 0, 0, 0);
@@ -832,16 +897,14 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
       wlo = __builtin_amdgcn_alignbyte(b.o[1], b.o[0], b.sh);
       whi = __builtin_amdgcn_alignbyte(b.o[2], b.o[1], b.sh);
     }
-    float sw[8], sx[8];
-    const uint32_t swd[2] = {sw2.x, sw2.y}, sxd[2] = {sx2.x, sx2.y};
+    float sw[8];
+    const float sx[8] = {sxa[0], sxa[1], sxa[2], sxa[3], sxb[0], sxb[1], sxb[2], sxb[3]};
+    const uint32_t swd[2] = {sw2.x, sw2.y};
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const auto w0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(swd[j], 1.0f, false);
       const auto w1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(swd[j], 1.0f, true);
-      const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sxd[j], 1.0f, false);
-      const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sxd[j], 1.0f, true);
       sw[4 * j + 0] = w0[0]; sw[4 * j + 1] = w0[1]; sw[4 * j + 2] = w1[0]; sw[4 * j + 3] = w1[1];
-      sx[4 * j + 0] = v0[0]; sx[4 * j + 1] = v0[1]; sx[4 * j + 2] = v1[0]; sx[4 * j + 3] = v1[1];
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -912,12 +975,13 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
   else ((float *)a.y)[n0 + r] = v;
 }
 
+template <bool ROWS>
 __global__ __launch_bounds__(1024) void gemv_fp4_kernel(LinearArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int L = run_level(a);
-  if (L == 6) fp4_tile<6, kFp4Depth6>(a, lds);
-  else if (L == 2) fp4_tile<2, kFp4Depth>(a, lds);
-  else fp4_tile<4, kFp4Depth>(a, lds);
+  if (L == 6) fp4_tile<6, kFp4Depth6, false>(a, lds);
+  else if (L == 2) fp4_tile<2, kFp4Depth, ROWS>(a, lds);
+  else fp4_tile<4, kFp4Depth, ROWS>(a, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1181,16 +1245,26 @@ Fp4Cfg fp4_cfg(const LinearArgs &a, bool six) {
     c.rt = (int)per_cu;
     int wk = a.waves > 0 ? a.waves : 1;
     while ((nch + wk - 1) / wk > kFp4Chunks) ++wk;
-    if (a.waves == 0) {
+    if (a.waves == 0 && six) {
       while (c.rt * wk * 2 <= kMaxWaves && nch / (2 * wk) >= 8) wk *= 2;
     }
     c.wk = wk;
+  } else if (!six && a.waves == 0) {
+    // levels 2 and 4 (8 chunks in flight): long ranges, about 400 or more
+    // wavefronts; every wavefront's prologue costs the same few loads, so
+    // short ranges make the launch instruction-bound (measured: Wqkv 6.4 us
+    // at one wavefront per tile, 7.7 at four; Wo 4.9 at two, 5.3 at four)
+    int wk = 1;
+    while ((nch + wk - 1) / wk > kFp4Chunks) wk <<= 1;
+    while (tiles * wk < 384 && nch / (2 * wk) >= 4) wk <<= 1;
+    c.wk = wk;
+    c.rt = 1;
   } else {
     const StreamCfg sc = stream_cfg(a);
     c.wk = sc.wk;
     c.rt = sc.rt;
   }
-  c.lds = (size_t)c.wk * c.rt * (six ? kFp4WaveLds6 : kFp4WaveLds);
+  c.lds = (size_t)c.wk * c.rt * (six ? kFp4WaveLds6 : kFp4WaveLds4);
   c.ok = c.wk * c.rt <= kMaxWaves && (nch + c.wk - 1) / c.wk <= kFp4Chunks &&
          c.lds <= (size_t)max_lds_per_block();
   return c;
@@ -1221,7 +1295,10 @@ hipError_t launch_gemv(const LinearArgs &a0, hipStream_t s) {
       a1.wk = c.wk;
       const int64_t tiles = (a0.n + 15) / 16;
       const dim3 grid((unsigned)((tiles + c.rt - 1) / c.rt)), block((unsigned)(64 * c.wk * c.rt));
-      hipLaunchKernelGGL(gemv_fp4_kernel, grid, block, c.lds, s, a1);
+      // whole-row loads from 1024 wavefronts up (measured: Wgate|Wup, Wdown and
+      // the 70B shape 3-7 % faster; Wqkv and Wo, 384-512 wavefronts, slower)
+      if ((int64_t)grid.x * c.wk * c.rt >= 1024) hipLaunchKernelGGL(gemv_fp4_kernel<true>, grid, block, c.lds, s, a1);
+      else hipLaunchKernelGGL(gemv_fp4_kernel<false>, grid, block, c.lds, s, a1);
       return hipGetLastError();
     }
   }

@@ -282,11 +282,12 @@ def test_gemv_forced_waves(waves, n, b, k):
 
 
 @pytest.mark.parametrize("n,k,waves", [(200, 256, 0), (1000, 4096, 0), (17, 2560, 1), (33, 768, 2),
-                                       (300, 14336, 0), (40, 4096 + 256, 16)])
+                                       (300, 14336, 0), (40, 4096 + 256, 16), (16400, 256, 0)])
 @pytest.mark.parametrize("level", [2, 4, 6])
 def test_gemv_one_token_matrix_core_path(n, k, waves, level):
     """One token with K % 256 == 0 (the fp4 matrix-core GEMV): ragged row
-    tiles, uneven and forced K splits, host- and device-side level."""
+    tiles, uneven and forced K splits, host- and device-side level; 16400
+    rows (1025 row tiles) takes the whole-row loads at levels 2 and 4."""
     say(f"case: one-token gemv N={n} K={k} waves={waves} level {level}")
     w, x = operands(n, 1, k, seed=n + k + waves)
     wp, xp4, xp6 = gpu_pack(w, x)
