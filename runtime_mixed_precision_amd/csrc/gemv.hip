@@ -635,14 +635,28 @@ __global__ __launch_bounds__(PD == 8 ? 512 : 1024) void gemv_stream_kernel(Linea
 // of D, i.e. for q < 2 the groups 8q + {0, 1, 4, 5} + 2h of weight row r.
 constexpr int kFp4Chunks = 16;                          // chunks per wavefront at most
 constexpr int kFp4Pitch = kFp4Chunks * 16 + 16;            // LDS row pitch of the weight scales
-constexpr int kFp4WaveLds = 16 * kFp4Pitch + kFp4Chunks * (128 + 64);
-// level 6 adds: activation offsets as E2M1 d/2 (128 B per chunk), the offset
-// plan (64 entries of 16 selector bytes + a position) and a 256-entry table
-constexpr int kFp4WaveLds6 = kFp4WaveLds + kFp4Chunks * 128 + kPlanBytesPerWave + 512;
-// levels 2 and 4: a 2 KB slot where each chunk's codes change lane layout
-constexpr int kFp4WaveLds4 = kFp4WaveLds + 2048;
 constexpr int kFp4Depth = 8;                               // chunks of code loads in flight
 constexpr int kFp4Depth6 = 4;                              // level 6 (offset windows too)
+
+// Wavefront-private LDS of the matrix-core GEMV for up to BT tokens: weight
+// scales [16 rows][16 chunks][16 B] at a row pitch of 272 B (the 16 rows'
+// reads then cover all 64 banks once); the activation codes [BT][cap][128 B]
+// and scales as fp32 [BT][cap][16]; then at level 6 the activation offsets as
+// E2M1 d/2 codes [BT][cap][128 B], the offset plan and the offset-byte table,
+// or at levels 2 and 4 a 2 KB slot where each chunk's codes change lane
+// layout. cap (chunks per wavefront) keeps BT * cap <= 32 above one token.
+template <int BT>
+struct Fp4Lay {
+  static constexpr int cap = BT == 1 ? kFp4Chunks : 32 / BT;
+  static constexpr int tc = BT * cap;
+  static constexpr int xs = 16 * kFp4Pitch;
+  static constexpr int sx = xs + tc * 128;
+  static constexpr int dx = sx + tc * 64;
+  static constexpr int plan = dx + tc * 128;
+  static constexpr int lut = plan + kPlanBytesPerWave;
+  static constexpr int bytes4 = dx + 2048;
+  static constexpr int bytes6 = lut + 512;
+};
 
 // Four 2-bit offsets d (two's complement, element e in bits 2e+1:2e) as four
 // E2M1 codes of d/2 in the nibbles of a 16-bit value: +1 -> 0.5 (0001),
@@ -657,10 +671,16 @@ __device__ __forceinline__ uint32_t offsets_to_e2m1(uint32_t v) {
   return b0 | (b1 << 3) | ((b1 & ~b0) << 1);
 }
 
-template <int L, int PD, bool ROWS>
+// Up to BT tokens: each MFMA's 16 A rows hold 8 group slots of two tokens
+// (levels 2 and 4: tokens 2m and 2m + 1) or of one token's codes and its
+// offsets d/2 (level 6: token m), so M = ceil(BT / 2) or BT MFMAs per
+// half-chunk reuse one weight operand.
+template <int L, int PD, bool ROWS, int BT>
 __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds) {
   constexpr bool REF = (L == 6);
   constexpr bool P3 = ROWS && !REF;
+  constexpr int M = REF ? BT : (BT + 1) / 2;
+  typedef Fp4Lay<BT> Lay;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
@@ -669,6 +689,7 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
   const int kw = wave - tile * WK;
   const int r = lane & 15;
   const int q = lane >> 4;
+  const int B = (int)a.b;
   const int64_t K = a.k;
   const int64_t nch = K / kCh;
   const int64_t n0 = ((int64_t)blockIdx.x * (nw / WK) + tile) * 16;
@@ -677,7 +698,7 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
   const int64_t nb0 = rows > 0 ? n0 : 0;
   const int64_t c0 = (nch * kw) / WK;
   const int64_t c1 = (nch * (kw + 1)) / WK;
-  const int len = (int)(c1 - c0);   // at most kFp4Chunks
+  const int len = (int)(c1 - c0);   // at most Lay::cap
   const int64_t R = a.n_refined;
   const bool refine_w = REF && a.w_mask != nullptr && R > 0 && a.w_offsets != nullptr;
   const bool refine_x = REF && a.x_offsets != nullptr;
@@ -686,31 +707,29 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
   // weight offsets: the tile's rows plus the 16 padding bytes every offsets buffer carries
   const __amdgpu_buffer_rsrc_t ro =
       make_rsrc(refine_w ? a.w_offsets + nb0 * R : a.w_codes, refine_w && rows > 0 ? rows * R + 16 : 0);
-  const __amdgpu_buffer_rsrc_t rxc = make_rsrc(a.x_codes, K >> 1);
-  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(a.x_scales, K >> 4);
-  const __amdgpu_buffer_rsrc_t rxo = make_rsrc(refine_x ? a.x_offsets : a.x_codes, refine_x ? K >> 2 : 0);
+  const __amdgpu_buffer_rsrc_t rxc = make_rsrc(a.x_codes, B * (K >> 1));
+  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(a.x_scales, B * (K >> 4));
+  const __amdgpu_buffer_rsrc_t rxo = make_rsrc(refine_x ? a.x_offsets : a.x_codes, refine_x ? B * (K >> 2) : 0);
   const __amdgpu_buffer_rsrc_t rm = make_rsrc(refine_w ? a.w_mask : a.w_codes, refine_w ? K >> 5 : 0);
   const uint32_t crow = (uint32_t)(r * (K >> 1) + 32 * q);
   const uint32_t orow = (uint32_t)(r * R);
 
-  // wavefront-private LDS: weight scales [16 rows][kFp4Chunks chunks][16 B]
-  // at a row pitch of kFp4Chunks * 16 + 16 bytes (the 16 rows' 8-byte reads
-  // then cover all 64 banks once), the activation codes and scales (fp32) of
-  // the range; level 6: the activation offsets as E2M1 d/2 codes (laid out
-  // like the activation codes), the offset plan and the offset-byte table
-  unsigned char *wl = lds + (size_t)wave * (REF ? kFp4WaveLds6 : kFp4WaveLds4);
+  unsigned char *wl = lds + (size_t)wave * (REF ? Lay::bytes6 : Lay::bytes4);
   unsigned char *wsc = wl;
-  unsigned char *xsl = wl + 16 * kFp4Pitch;
-  float *sxf = (float *)(xsl + kFp4Chunks * 128);
-  unsigned char *dxl = (unsigned char *)(sxf + kFp4Chunks * 16);
-  uint4 *plan_sel = (uint4 *)(dxl + kFp4Chunks * 128);
+  unsigned char *xsl = wl + Lay::xs;
+  float *sxf = (float *)(wl + Lay::sx);
+  unsigned char *dxl = wl + Lay::dx;
+  uint4 *plan_sel = (uint4 *)(wl + Lay::plan);
   int32_t *plan_pos = (int32_t *)(plan_sel + 64);
-  uint16_t *lut = (uint16_t *)(plan_pos + 64);
+  uint16_t *lut = (uint16_t *)(wl + Lay::lut);
   unsigned char *tsl = dxl;   // levels 2 and 4: the code transpose slot
 
-  // 1. the range's scales and activation bytes, each lane one 16-byte piece
-  //    per load: weight-scale piece j * 64 + l is row l % 16, chunk 4j + l / 16
-  uint32_t pw[kFp4Chunks / 4][4], px[2][4], ps[4], pd[4] = {0, 0, 0, 0}, pm = 0;
+  // 1. the range's scales and activation bytes, one 16-byte piece per lane
+  //    per load: weight-scale piece j * 64 + l is row l % 16, chunk 4j + l / 16;
+  //    activation pieces run token by token over the range
+  constexpr int NX = Lay::tc * 8 / 64;   // activation-code loads per lane
+  constexpr int NO = Lay::tc * 4 / 64;   // activation-offset loads per lane (level 6)
+  uint32_t pw[kFp4Chunks / 4][4], px[NX][4], ps[4], pd[NO > 0 ? NO : 1][4], pm = 0;
   if (refine_w) {
     // mask bits of lane e = 4 * chunk + q: the 16 subgroups of its 64 elements
     const uint32_t o = (lane >> 2) < len ? (uint32_t)(8 * (c0 + (lane >> 2)) + 2 * (lane & 3)) : kOOB;
@@ -724,21 +743,28 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
     pw[j][0] = v[0]; pw[j][1] = v[1]; pw[j][2] = v[2]; pw[j][3] = v[3];
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int p = 64 * j + lane;   // 16-byte piece of the range's activation codes
-    const uint32_t o = p < 8 * len ? (uint32_t)(128 * c0 + 16 * p) : kOOB;
+  for (int j = 0; j < NX; ++j) {
+    const int p = 64 * j + lane;
+    const int t = p / (8 * Lay::cap), w = p - t * 8 * Lay::cap;
+    const uint32_t o = (t < B && w < 8 * len) ? (uint32_t)(t * (K >> 1) + 128 * c0 + 16 * w) : kOOB;
     const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rxc, (int)o, 0, 0);
     px[j][0] = v[0]; px[j][1] = v[1]; px[j][2] = v[2]; px[j][3] = v[3];
   }
   {
-    const uint32_t o = lane < len ? (uint32_t)(16 * (c0 + lane)) : kOOB;
+    const int t = lane / Lay::cap, c = lane - t * Lay::cap;
+    const uint32_t o = (lane < Lay::tc && t < B && c < len) ? (uint32_t)(t * (K >> 4) + 16 * (c0 + c)) : kOOB;
     const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rxs, (int)o, 0, 0);
     ps[0] = v[0]; ps[1] = v[1]; ps[2] = v[2]; ps[3] = v[3];
   }
-  if (refine_x) {
-    const uint32_t o = lane < 4 * len ? (uint32_t)(64 * c0 + 16 * lane) : kOOB;
-    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rxo, (int)o, 0, 0);
-    pd[0] = v[0]; pd[1] = v[1]; pd[2] = v[2]; pd[3] = v[3];
+  if (REF) {
+#pragma unroll
+    for (int j = 0; j < NO; ++j) {
+      const int p = 64 * j + lane;
+      const int t = p / (4 * Lay::cap), w = p - t * 4 * Lay::cap;
+      const uint32_t o = (refine_x && t < B && w < 4 * len) ? (uint32_t)(t * (K >> 2) + 64 * c0 + 16 * w) : kOOB;
+      const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rxo, (int)o, 0, 0);
+      pd[j][0] = v[0]; pd[j][1] = v[1]; pd[j][2] = v[2]; pd[j][3] = v[3];
+    }
   }
   vmem_fence();
 
@@ -768,21 +794,22 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
     }
   }
 
-  // 3. the first PD chunks of weight codes (and level-6 offset windows)
+  // 3. the first PD chunks of weight codes (and level-6 offset windows).
+  //    With ROWS, levels 2 and 4 load whole rows: load A brings rows 0..7 of
+  //    the chunk (lane l: row l / 8), load B rows 8..15, each 8 lanes one
+  //    128-byte row; lane slot s of row rho holds 16-byte piece s ^ (rho / 2)
+  //    (the XOR keeps the transposed reads in process free of bank conflicts).
+  //    Non-temporal: the codes are read once. Otherwise, and always at level 6
+  //    (its offset windows follow it), the MFMA lane layout: lane (r, q)
+  //    loads bytes 32q .. 32q + 31 of row r. Whole rows read faster (8 full
+  //    128-byte lines per load instead of 16 half lines) but put an LDS round
+  //    trip in each chunk: worth it when the launch has enough wavefronts to
+  //    hide it.
   struct Buf {
     uint32_t c[8];   // 64 weight codes
     uint32_t o[3];   // offset dwords covering the lane's offset window
     uint32_t sh;     // byte position of the window in o
   };
-  // With ROWS, levels 2 and 4 load whole rows: load A brings rows 0..7 of the chunk
-  // (lane l: row l / 8), load B rows 8..15, each 8 lanes one 128-byte row;
-  // lane slot s of row rho holds 16-byte piece s ^ (rho / 2) (the XOR keeps
-  // the transposed reads in process free of bank conflicts). Non-temporal:
-  // the codes are read once. Otherwise, and always at level 6 (its offset
-  // windows follow it), the MFMA lane layout: lane (r, q) loads bytes
-  // 32q .. 32q + 31 of row r. Whole rows read faster (8 full 128-byte lines
-  // per load instead of 16 half lines) but put an LDS round trip in each
-  // chunk: worth it when the launch has enough wavefronts to hide it.
   const uint32_t rowA = (uint32_t)(lane >> 3), rowB = rowA + 8;
   const uint32_t pA = (uint32_t)(((lane & 7) ^ (rowA >> 1)) * 16), pB = (uint32_t)(((lane & 7) ^ (rowB >> 1)) * 16);
   const uint32_t voA = P3 ? rowA * (uint32_t)(K >> 1) + pA : crow;
@@ -814,10 +841,10 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
   for (int j = 0; j < kFp4Chunks / 4; ++j)
     *(uint4 *)(wsc + r * kFp4Pitch + 16 * (4 * j + q)) = make_uint4(pw[j][0], pw[j][1], pw[j][2], pw[j][3]);
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < NX; ++j)
     *(uint4 *)(xsl + 16 * (64 * j + lane)) = make_uint4(px[j][0], px[j][1], px[j][2], px[j][3]);
-  if (lane < kFp4Chunks) {
-    // the chunk's 16 activation group scales as fp32
+  if (lane < Lay::tc) {
+    // a (token, chunk)'s 16 activation group scales as fp32
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ps[j], 1.0f, false);
@@ -827,69 +854,32 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
   }
   if (REF) {
     // 64 offsets (16 bytes) -> 64 E2M1 codes (32 bytes)
-    uint32_t e[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      e[2 * j] = offsets_to_e2m1(pd[j]);
-      e[2 * j + 1] = offsets_to_e2m1(pd[j] >> 16);
-    }
-    *(uint4 *)(dxl + 32 * lane) = make_uint4(e[0], e[1], e[2], e[3]);
-    *(uint4 *)(dxl + 32 * lane + 16) = make_uint4(e[4], e[5], e[6], e[7]);
-  }
-
-  // A operand: lane (s = r, q) carries, in A row s, group 4q + 2h + (s & 1)
-  // of the activation codes (s < 8) or of its offsets d/2 (s >= 8, level 6)
-  // when (s & 7) / 2 == q
-  //    (levels 2 and 4: MFMA h sees bytes 64h + 16q .. + 15 of row r in lane
-  //    group q, so A row s < 8 is group 8h + s)
-  const bool a_live = ((r & 7) >> 1) == q && (r < 8 || REF);
-  const bool a_hi = (r & 1) != 0;
-  const unsigned char *abase = P3 ? xsl + 8 * r : (r < 8 ? xsl : dxl) + 32 * q + 8 * (r & 1);
-  float acc0 = 0.f, acc1 = 0.f;
-  auto process3 = [&](int i, const Buf &b) {
-    // whole rows -> MFMA lane layout: lane (r, q) takes pieces 4h + q of row r
-    *(uint4 *)(tsl + 16 * lane) = make_uint4(b.c[0], b.c[1], b.c[2], b.c[3]);
-    *(uint4 *)(tsl + 1024 + 16 * lane) = make_uint4(b.c[4], b.c[5], b.c[6], b.c[7]);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint4 wv = *(const uint4 *)(tsl + 128 * r + 16 * ((4 * h + q) ^ (r >> 1)));
-      const uint2 xv = *(const uint2 *)(abase + 128 * i + 64 * h);
-      const uint32_t swd = *(const uint32_t *)(wsc + r * kFp4Pitch + 16 * i + 8 * h + 4 * (q & 1));
-      const float4v sx = *(const float4v *)(sxf + 16 * i + 8 * h + 4 * (q & 1));
-      const auto w0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(swd, 1.0f, false);
-      const auto w1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(swd, 1.0f, true);
-      i32x8v bw, ax;
-      const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+    for (int j = 0; j < NO; ++j) {
+      uint32_t e[8];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        bw[k] = (int)(L == 2 ? autofp2_remap(wd[k]) : wd[k]);
-        bw[4 + k] = 0;
+        e[2 * k] = offsets_to_e2m1(pd[j][k]);
+        e[2 * k + 1] = offsets_to_e2m1(pd[j][k] >> 16);
       }
-      const uint32_t xl = a_live ? xv.x : 0u, xh = a_live ? xv.y : 0u;
-      ax[0] = (int)(a_hi ? 0u : xl);
-      ax[1] = (int)(a_hi ? 0u : xh);
-      ax[2] = (int)(a_hi ? xl : 0u);
-      ax[3] = (int)(a_hi ? xh : 0u);
-      ax[4] = ax[5] = ax[6] = ax[7] = 0;
-      const float4v d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          ax, bw, float4v{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, 127, 0, 127);
-      // D rows 4q + k <-> group 8h + 4 (q & 1) + k
-      acc0 = fmaf(d[0], w0[0] * sx[0], acc0);
-      acc1 = fmaf(d[1], w0[1] * sx[1], acc1);
-      acc0 = fmaf(d[2], w1[0] * sx[2], acc0);
-      acc1 = fmaf(d[3], w1[1] * sx[3], acc1);
+      *(uint4 *)(dxl + 32 * (64 * j + lane)) = make_uint4(e[0], e[1], e[2], e[3]);
+      *(uint4 *)(dxl + 32 * (64 * j + lane) + 16) = make_uint4(e[4], e[5], e[6], e[7]);
     }
-  };
+  }
+
+  // A operand of MFMA m: lane (s = r, q) carries, in A row s, one group of
+  // token ta(m, s) (levels 2/4: codes of token 2m + s / 8; level 6: codes of
+  // token m for s < 8, its offsets d/2 for s >= 8) when (s & 7) / 2 == q:
+  // group 4q + 2h + (s & 1) in the MFMA lane layout, 8h + (s & 7) with whole
+  // rows. D row 4q + k of MFMA m belongs to token td(m, q) (2m + q / 2, or m).
+  const bool a_slot = ((r & 7) >> 1) == q;
+  const bool a_hi = (r & 1) != 0;
+  const uint32_t a_off = P3 ? (uint32_t)(8 * (r & 7)) : (uint32_t)(32 * q + 8 * (r & 1));
+  const uint32_t sxo = P3 ? (uint32_t)(4 * (q & 1)) : (uint32_t)(8 * (q & 1));
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.f;
   auto process = [&](int i, const Buf &b) {
-    if (P3) {
-      process3(i, b);
-      return;
-    }
-    const uint2 sw2 = *(const uint2 *)(wsc + r * kFp4Pitch + 16 * i + 8 * (q & 1));
-    const float4v sxa = *(const float4v *)(sxf + 16 * i + 8 * (q & 1));
-    const float4v sxb = *(const float4v *)(sxf + 16 * i + 8 * (q & 1) + 4);
-    const uint2 x0 = *(const uint2 *)(abase + 128 * i);
-    const uint2 x1 = *(const uint2 *)(abase + 128 * i + 16);
     uint4 sel = make_uint4(0, 0, 0, 0);
     uint32_t wlo = 0, whi = 0;
     if (refine_w) {
@@ -897,50 +887,89 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
       wlo = __builtin_amdgcn_alignbyte(b.o[1], b.o[0], b.sh);
       whi = __builtin_amdgcn_alignbyte(b.o[2], b.o[1], b.sh);
     }
+    if (P3) {
+      *(uint4 *)(tsl + 16 * lane) = make_uint4(b.c[0], b.c[1], b.c[2], b.c[3]);
+      *(uint4 *)(tsl + 1024 + 16 * lane) = make_uint4(b.c[4], b.c[5], b.c[6], b.c[7]);
+    }
+    // weight group scales of the lane's D rows: 4 per half (whole rows) or
+    // 8 per chunk (MFMA lane layout)
     float sw[8];
-    const float sx[8] = {sxa[0], sxa[1], sxa[2], sxa[3], sxb[0], sxb[1], sxb[2], sxb[3]};
-    const uint32_t swd[2] = {sw2.x, sw2.y};
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const auto w0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(swd[j], 1.0f, false);
-      const auto w1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(swd[j], 1.0f, true);
-      sw[4 * j + 0] = w0[0]; sw[4 * j + 1] = w0[1]; sw[4 * j + 2] = w1[0]; sw[4 * j + 3] = w1[1];
+    {
+      const uint2 sw2 = *(const uint2 *)(wsc + r * kFp4Pitch + 16 * i + (P3 ? 4 * (q & 1) : 8 * (q & 1)));
+      const uint32_t sa = sw2.x, sb = P3 ? *(const uint32_t *)(wsc + r * kFp4Pitch + 16 * i + 8 + 4 * (q & 1)) : sw2.y;
+      const auto w0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sa, 1.0f, false);
+      const auto w1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sa, 1.0f, true);
+      const auto w2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb, 1.0f, false);
+      const auto w3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb, 1.0f, true);
+      sw[0] = w0[0]; sw[1] = w0[1]; sw[2] = w1[0]; sw[3] = w1[1];
+      sw[4] = w2[0]; sw[5] = w2[1]; sw[6] = w3[0]; sw[7] = w3[1];
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      i32x8v bw, ax;
+      i32x8v bw, bo;
+      uint32_t wd[4];
+      if (P3) {
+        const uint4 wv = *(const uint4 *)(tsl + 128 * r + 16 * ((4 * h + q) ^ (r >> 1)));
+        wd[0] = wv.x; wd[1] = wv.y; wd[2] = wv.z; wd[3] = wv.w;
+      } else {
+        wd[0] = b.c[4 * h]; wd[1] = b.c[4 * h + 1]; wd[2] = b.c[4 * h + 2]; wd[3] = b.c[4 * h + 3];
+      }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint32_t w = b.c[4 * h + k];
-        bw[k] = (int)(L == 2 ? autofp2_remap(w) : w);
+        bw[k] = (int)(L == 2 ? autofp2_remap(wd[k]) : wd[k]);
         bw[4 + k] = 0;
       }
-      const uint32_t xl = a_live ? (h ? x1.x : x0.x) : 0u, xh = a_live ? (h ? x1.y : x0.y) : 0u;
-      ax[0] = (int)(a_hi ? 0u : xl);
-      ax[1] = (int)(a_hi ? 0u : xh);
-      ax[2] = (int)(a_hi ? xl : 0u);
-      ax[3] = (int)(a_hi ? xh : 0u);
-      ax[4] = ax[5] = ax[6] = ax[7] = 0;
-      float4v d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          ax, bw, float4v{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, 127, 0, 127);
       if (refine_w) {
-        // weight offsets d_W / 2 of the lane's 8 subgroup slots, as E2M1,
-        // added at scale 2^-2: D += A * (d_W / 2) / 4 = A * d_W / 8
+        // weight offsets d_W / 2 of the lane's 8 subgroup slots, as E2M1
         const uint32_t e0 = __builtin_amdgcn_perm(whi, wlo, h ? sel.z : sel.x);
         const uint32_t e1 = __builtin_amdgcn_perm(whi, wlo, h ? sel.w : sel.y);
-        i32x8v bo;
         bo[0] = (int)(lut[e0 & 0xFFu] | ((uint32_t)lut[(e0 >> 8) & 0xFFu] << 16));
         bo[1] = (int)(lut[(e0 >> 16) & 0xFFu] | ((uint32_t)lut[e0 >> 24] << 16));
         bo[2] = (int)(lut[e1 & 0xFFu] | ((uint32_t)lut[(e1 >> 8) & 0xFFu] << 16));
         bo[3] = (int)(lut[(e1 >> 16) & 0xFFu] | ((uint32_t)lut[e1 >> 24] << 16));
         bo[4] = bo[5] = bo[6] = bo[7] = 0;
-        d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ax, bo, d, 4, 4, 0, 127, 0, 125);
       }
-      // D rows 4q + k <-> groups 8 (q & 1) + {0, 1, 4, 5}[k] + 2h
-      acc0 = fmaf(d[0], sw[0 + 2 * h] * sx[0 + 2 * h], acc0);
-      acc1 = fmaf(d[1], sw[1 + 2 * h] * sx[1 + 2 * h], acc1);
-      acc0 = fmaf(d[2], sw[4 + 2 * h] * sx[4 + 2 * h], acc0);
-      acc1 = fmaf(d[3], sw[5 + 2 * h] * sx[5 + 2 * h], acc1);
+      // the lane's 4 D rows <-> groups: whole rows 8h + 4 (q & 1) + k;
+      // MFMA lane layout 8 (q & 1) + {0, 1, 4, 5}[k] + 2h
+      const float s0 = P3 ? sw[4 * h + 0] : sw[0 + 2 * h], s1 = P3 ? sw[4 * h + 1] : sw[1 + 2 * h];
+      const float s2 = P3 ? sw[4 * h + 2] : sw[4 + 2 * h], s3 = P3 ? sw[4 * h + 3] : sw[5 + 2 * h];
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const int ta = REF ? m : 2 * m + (r >> 3);
+        const int td = REF ? m : 2 * m + (q >> 1);
+        const unsigned char *ab = (REF && r >= 8 ? dxl : xsl) + ta * (Lay::cap * 128) + 128 * i + a_off +
+                                  (P3 ? 64 * h : 16 * h);
+        const uint2 xv = *(const uint2 *)ab;
+        const bool live = a_slot && ta < B && (r < 8 || REF || BT > 1);
+        const uint32_t xl = live ? xv.x : 0u, xh = live ? xv.y : 0u;
+        i32x8v ax;
+        ax[0] = (int)(a_hi ? 0u : xl);
+        ax[1] = (int)(a_hi ? 0u : xh);
+        ax[2] = (int)(a_hi ? xl : 0u);
+        ax[3] = (int)(a_hi ? xh : 0u);
+        ax[4] = ax[5] = ax[6] = ax[7] = 0;
+        float4v d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            ax, bw, float4v{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, 127, 0, 127);
+        if (refine_w) {
+          // + A * (d_W / 2) at scale 2^-2 = A * d_W / 8
+          d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ax, bo, d, 4, 4, 0, 127, 0, 125);
+        }
+        const float *sp = sxf + (td * Lay::cap + i) * 16;
+        float x0, x1, x2, x3;
+        if (P3) {
+          const float4v v = *(const float4v *)(sp + 8 * h + sxo);
+          x0 = v[0]; x1 = v[1]; x2 = v[2]; x3 = v[3];
+        } else {
+          const float4v va = *(const float4v *)(sp + sxo), vb = *(const float4v *)(sp + sxo + 4);
+          x0 = h ? va[2] : va[0]; x1 = h ? va[3] : va[1]; x2 = h ? vb[2] : vb[0]; x3 = h ? vb[3] : vb[1];
+        }
+        float t = acc[m];
+        t = fmaf(d[0], s0 * x0, t);
+        t = fmaf(d[1], s1 * x1, t);
+        t = fmaf(d[2], s2 * x2, t);
+        t = fmaf(d[3], s3 * x3, t);
+        acc[m] = t;
+      }
     }
   };
 
@@ -955,33 +984,54 @@ __device__ __forceinline__ void fp4_tile(const LinearArgs &a, unsigned char *lds
     }
   }
 
-  // 6. D rows 8..15 (lane groups 2, 3) hold the products with d_A / 2, worth
-  //    a quarter (zero below level 6); the K-split wavefronts of each row
-  //    tile are then added in LDS
-  float acc = (acc0 + acc1) * (q < 2 ? 1.0f : 0.25f);
-  acc += __shfl_xor(acc, 32, 64);
-  acc += __shfl_xor(acc, 16, 64);
+  // 6. per MFMA: level 6 adds the offset rows (lane groups 2, 3) at a
+  //    quarter into lane group 0; levels 2/4 add lane groups 0 + 1 (token
+  //    2m) and 2 + 3 (token 2m + 1). Then the K-split wavefronts of each row
+  //    tile are summed in LDS, [wave][token][row].
   float *red = (float *)lds;
   __syncthreads();
-  if (lane < 16) red[wave * 16 + lane] = acc;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float v = acc[m];
+    if (REF) {
+      v *= (q < 2 ? 1.0f : 0.25f);
+      v += __shfl_xor(v, 32, 64);
+    }
+    v += __shfl_xor(v, 16, 64);
+    const int td = REF ? m : 2 * m + (q >> 1);
+    if ((REF ? q == 0 : (q & 1) == 0) && td < BT) red[(wave * BT + td) * 16 + r] = v;
+  }
   __syncthreads();
-  if (kw != 0 || rows == 0 || lane >= 16 || r >= rows) return;
-  float s = red[wave * 16 + lane];
-  for (int w = 1; w < WK; ++w) s += red[(wave + w) * 16 + lane];
+  if (kw != 0 || rows == 0) return;
   float scale = (*a.w_T) * (*a.x_T);
   if (L == 2) scale *= a.c2;
-  const float v = s * scale;
-  if (a.y_dtype == AUTOFP_BF16) ((uint16_t *)a.y)[n0 + r] = f32_to_bf16_rne(v);
-  else ((float *)a.y)[n0 + r] = v;
+  for (int e = lane; e < B * 16; e += 64) {
+    const int t = e >> 4, rr = e & 15;
+    if (rr >= rows) continue;
+    float s = 0.f;
+    for (int w = 0; w < WK; ++w) s += red[((wave + w) * BT + t) * 16 + rr];
+    const float v = s * scale;
+    if (a.y_dtype == AUTOFP_BF16) ((uint16_t *)a.y)[t * a.n + n0 + rr] = f32_to_bf16_rne(v);
+    else ((float *)a.y)[t * a.n + n0 + rr] = v;
+  }
 }
 
-template <bool ROWS>
+// Chunks of code loads in flight: fewer as the token slots take registers.
+// Level 6 runs up to 4 token slots (8 would spill: 16 MFMAs per half-chunk);
+// the launcher sends 5-8 tokens at level 6 to the streaming kernel.
+template <bool ROWS, int BT>
 __global__ __launch_bounds__(1024) void gemv_fp4_kernel(LinearArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
+  constexpr int D4 = BT <= 2 ? kFp4Depth : kFp4Depth / 2;
+  constexpr int D6 = BT <= 2 ? kFp4Depth6 : kFp4Depth6 / 2;
   const int L = run_level(a);
-  if (L == 6) fp4_tile<6, kFp4Depth6, false>(a, lds);
-  else if (L == 2) fp4_tile<2, kFp4Depth, ROWS>(a, lds);
-  else fp4_tile<4, kFp4Depth, ROWS>(a, lds);
+  if (L == 6) {
+    if constexpr (BT <= 4) fp4_tile<6, D6, false, BT>(a, lds);
+  } else if (L == 2) {
+    fp4_tile<2, D4, ROWS, BT>(a, lds);
+  } else {
+    fp4_tile<4, D4, ROWS, BT>(a, lds);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1224,49 +1274,63 @@ StreamCfg stream_cfg(const LinearArgs &a) {
   return c;
 }
 
-// Launch shape of the one-token matrix-core GEMV. When the row tiles split
-// evenly over the compute units, 256 blocks of tiles / 256 tiles each, so
-// every CU streams the same bytes (with 1 or 2 blocks per CU, a CU holding
-// two finishes last: the per-CU load rate, not HBM, bounds a CU); the
-// blocks' LDS keeps them one per CU. Otherwise the streaming kernel's shape.
+// Launch shape of the matrix-core GEMV for bt (1, 2, 4 or 8) token slots.
+// Levels 2 and 4 (8 chunks in flight) take long K ranges and about 400 or
+// more wavefronts: every wavefront's prologue costs the same few loads, so
+// short ranges make the launch instruction-bound (measured at one token:
+// Wqkv 6.4 us at one wavefront per tile, 7.7 at four; Wo 4.9 at two, 5.3 at
+// four). Level 6 (or a device-side level) takes the streaming kernel's
+// shape, about 1536 wavefronts. When the row tiles split evenly over the
+// compute units, 256 blocks of tiles / 256 tiles each. Ranges are capped at
+// the LDS staging capacity (16 chunks at one token, 32 / bt above).
 struct Fp4Cfg {
   int wk, rt;
   size_t lds;
   bool ok;
 };
 
-Fp4Cfg fp4_cfg(const LinearArgs &a, bool six) {
+int fp4_cap(int bt) { return bt == 1 ? kFp4Chunks : 32 / bt; }
+
+size_t fp4_wave_lds(int bt, bool six) {
+  switch (bt) {
+    case 1: return six ? Fp4Lay<1>::bytes6 : Fp4Lay<1>::bytes4;
+    case 2: return six ? Fp4Lay<2>::bytes6 : Fp4Lay<2>::bytes4;
+    case 4: return six ? Fp4Lay<4>::bytes6 : Fp4Lay<4>::bytes4;
+    default: return six ? Fp4Lay<8>::bytes6 : Fp4Lay<8>::bytes4;
+  }
+}
+
+Fp4Cfg fp4_cfg(const LinearArgs &a, bool six, int bt) {
   Fp4Cfg c{};
   const int64_t nch = a.k / kCh;
   const int64_t tiles = (a.n + 15) / 16;
   const int64_t kCUs = 256;
   const int64_t per_cu = tiles / kCUs;
-  if (tiles % kCUs == 0 && per_cu >= 2 && per_cu <= kMaxWaves) {
+  const int cap = fp4_cap(bt);
+  const size_t wave_lds = fp4_wave_lds(bt, six);
+  int wk = a.waves > 0 ? a.waves : 1;
+  while ((nch + wk - 1) / wk > cap) ++wk;
+  if (tiles % kCUs == 0 && per_cu >= 2 && per_cu * wk <= kMaxWaves &&
+      (size_t)(per_cu * wk) * wave_lds <= (size_t)max_lds_per_block()) {
     c.rt = (int)per_cu;
-    int wk = a.waves > 0 ? a.waves : 1;
-    while ((nch + wk - 1) / wk > kFp4Chunks) ++wk;
     if (a.waves == 0 && six) {
-      while (c.rt * wk * 2 <= kMaxWaves && nch / (2 * wk) >= 8) wk *= 2;
+      while (c.rt * wk * 2 <= kMaxWaves && nch / (2 * wk) >= 8 &&
+             (size_t)(c.rt * wk * 2) * wave_lds <= (size_t)max_lds_per_block())
+        wk *= 2;
     }
     c.wk = wk;
   } else if (!six && a.waves == 0) {
-    // levels 2 and 4 (8 chunks in flight): long ranges, about 400 or more
-    // wavefronts; every wavefront's prologue costs the same few loads, so
-    // short ranges make the launch instruction-bound (measured: Wqkv 6.4 us
-    // at one wavefront per tile, 7.7 at four; Wo 4.9 at two, 5.3 at four)
-    int wk = 1;
-    while ((nch + wk - 1) / wk > kFp4Chunks) wk <<= 1;
     while (tiles * wk < 384 && nch / (2 * wk) >= 4) wk <<= 1;
     c.wk = wk;
     c.rt = 1;
   } else {
     const StreamCfg sc = stream_cfg(a);
-    c.wk = sc.wk;
-    c.rt = sc.rt;
+    c.wk = sc.wk > wk ? sc.wk : wk;
+    while ((nch + c.wk - 1) / c.wk > cap) ++c.wk;
+    c.rt = c.wk == sc.wk ? sc.rt : 1;
   }
-  c.lds = (size_t)c.wk * c.rt * (six ? kFp4WaveLds6 : kFp4WaveLds4);
-  c.ok = c.wk * c.rt <= kMaxWaves && (nch + c.wk - 1) / c.wk <= kFp4Chunks &&
-         c.lds <= (size_t)max_lds_per_block();
+  c.lds = (size_t)c.wk * c.rt * wave_lds;
+  c.ok = c.wk * c.rt <= kMaxWaves && (nch + c.wk - 1) / c.wk <= cap && c.lds <= (size_t)max_lds_per_block();
   return c;
 }
 
@@ -1286,19 +1350,32 @@ hipError_t launch_act_dequant(const LinearArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_gemv(const LinearArgs &a0, hipStream_t s) {
-  // one token at a host-given level 2 or 4: the fp4 matrix-core kernel
-  if (a0.b == 1 && a0.k % kCh == 0) {
-    const bool six = a0.bits_dev != nullptr || a0.bits == 6;
-    const Fp4Cfg c = fp4_cfg(a0, six);
-    if (c.ok) {
+  // up to 8 tokens (4 at level 6) with K % 256 == 0: the fp4 matrix-core kernel
+  const bool six0 = a0.bits_dev != nullptr || a0.bits == 6;
+  if (a0.b <= (six0 ? 4 : 8) && a0.k % kCh == 0) {
+    const bool six = six0;
+    const int bt = a0.b == 1 ? 1 : a0.b == 2 ? 2 : a0.b <= 4 ? 4 : 8;
+    const Fp4Cfg c = fp4_cfg(a0, six, bt);
+    // on wide weights (1024+ row tiles) the short ranges of 8 token slots,
+    // and level 6 at 4 (two chunks in flight), lose to the streaming kernel
+    // (measured on Wgate|Wup: 22.6 vs 18.8 us at 8 tokens, level 4; 37.4 vs
+    // 28.3 us at 4 tokens, level 6)
+    const bool wide = (a0.n + 15) / 16 >= 1024;
+    if (c.ok && !(wide && (bt == 8 || (bt == 4 && six)))) {
       LinearArgs a1 = a0;
       a1.wk = c.wk;
       const int64_t tiles = (a0.n + 15) / 16;
       const dim3 grid((unsigned)((tiles + c.rt - 1) / c.rt)), block((unsigned)(64 * c.wk * c.rt));
-      // whole-row loads from 1024 wavefronts up (measured: Wgate|Wup, Wdown and
-      // the 70B shape 3-7 % faster; Wqkv and Wo, 384-512 wavefronts, slower)
-      if ((int64_t)grid.x * c.wk * c.rt >= 1024) hipLaunchKernelGGL(gemv_fp4_kernel<true>, grid, block, c.lds, s, a1);
-      else hipLaunchKernelGGL(gemv_fp4_kernel<false>, grid, block, c.lds, s, a1);
+      // whole-row loads from 1024 wavefronts up (measured at one token:
+      // Wgate|Wup, Wdown and the 70B shape 3-7 % faster; Wqkv and Wo,
+      // 384-512 wavefronts, slower)
+      const bool rows = (int64_t)grid.x * c.wk * c.rt >= 1024;
+#define AFP_FP4(R, T) hipLaunchKernelGGL((gemv_fp4_kernel<R, T>), grid, block, c.lds, s, a1)
+      if (bt == 1) { if (rows) AFP_FP4(true, 1); else AFP_FP4(false, 1); }
+      else if (bt == 2) { if (rows) AFP_FP4(true, 2); else AFP_FP4(false, 2); }
+      else if (bt == 4) { if (rows) AFP_FP4(true, 4); else AFP_FP4(false, 4); }
+      else { if (rows) AFP_FP4(true, 8); else AFP_FP4(false, 8); }
+#undef AFP_FP4
       return hipGetLastError();
     }
   }

@@ -302,6 +302,28 @@ def test_gemv_one_token_matrix_core_path(n, k, waves, level):
     assert torch.equal(yd, y), "device-side level differs from the host-given level"
 
 
+@pytest.mark.parametrize("n,b,k,waves", [(200, 2, 256, 0), (1000, 3, 4096, 0), (64, 4, 2560, 1),
+                                         (300, 5, 14336, 0), (40, 8, 4352, 0), (33, 7, 768, 2),
+                                         (16400, 8, 256, 0), (9000, 2, 1024, 0)])
+@pytest.mark.parametrize("level", [2, 4, 6])
+def test_gemv_few_tokens_matrix_core_path(n, b, k, waves, level):
+    """2-8 tokens with K % 256 == 0: two tokens per MFMA (one token's codes
+    and offsets at level 6, which takes up to 4 tokens); odd token counts
+    leave A rows empty; host- and device-side level; bf16 output."""
+    say(f"case: few-token gemv N={n} B={b} K={k} waves={waves} level {level}")
+    w, x = operands(n, b, k, seed=n + 7 * b + k + waves)
+    wp, xp4, xp6 = gpu_pack(w, x)
+    wq, xq4, xq6 = oracle_pack(w, x)
+    p = A.default_params(gemv_waves=waves)
+    y = run(A.gemv, wp, xp4, xp6, level, params=p)
+    check_close(y.cpu().numpy(), O.linear(wq, xq6 if level == 6 else xq4, level))
+    yb = run(A.gemv, wp, xp4, xp6, level, params=p, out_dtype=torch.bfloat16)
+    assert torch.equal(yb, y.to(torch.bfloat16)), "bf16 output is not the RNE of the fp32 result"
+    dev_bits = torch.tensor([level], dtype=torch.int32, device=DEV)
+    yd = A.gemv(wp, xp6, bits=0, bits_dev=dev_bits, params=p)
+    check_close(yd.cpu().numpy(), O.linear(wq, xq6 if level == 6 else xq4, level))
+
+
 @pytest.mark.parametrize("n,k", [(64, 4096), (48, 1024)])
 def test_gemv_one_token_overlapping_refinement(n, k):
     """Activation refined in subgroups the weight also refines (no exclusion
