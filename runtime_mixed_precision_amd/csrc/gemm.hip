@@ -445,9 +445,21 @@ bool gemm_small_m_ok(const LinearArgs &a) { return a.k % kBK2 == 0; }
 // tile serves all tokens from LDS.
 hipError_t launch_gemm_small_m(const LinearArgs &a, hipStream_t s) {
   const int64_t mtiles = (a.b + 63) / 64;
-  const size_t lds = 2 * (size_t)(64 * kBK2 * 2 + 256 * kBK2 * 2);
-  hipLaunchKernelGGL((gemm_lds_kernel<64, 256, kDecodeWaves>), dim3((unsigned)(mtiles * ((a.n + 255) / 256))),
-                     dim3(64 * kDecodeWaves), lds, s, a);
+  if (mtiles * ((a.n + 255) / 256) >= 256) {
+    const size_t lds = 2 * (size_t)(64 * kBK2 * 2 + 256 * kBK2 * 2);
+    hipLaunchKernelGGL((gemm_lds_kernel<64, 256, kDecodeWaves>), dim3((unsigned)(mtiles * ((a.n + 255) / 256))),
+                       dim3(64 * kDecodeWaves), lds, s, a);
+  } else if (mtiles * ((a.n + 127) / 128) >= 256) {
+    // narrower tiles when 256-row tiles leave CUs idle (28672 x 8192 at 64
+    // tokens: 161 us at 256 rows, 122 at 128, 114 at 64)
+    const size_t lds = 2 * (size_t)(64 * kBK2 * 2 + 128 * kBK2 * 2);
+    hipLaunchKernelGGL((gemm_lds_kernel<64, 128, kDecodeWaves>), dim3((unsigned)(mtiles * ((a.n + 127) / 128))),
+                       dim3(64 * kDecodeWaves), lds, s, a);
+  } else {
+    const size_t lds = 2 * (size_t)(64 * kBK2 * 2 + 64 * kBK2 * 2);
+    hipLaunchKernelGGL((gemm_lds_kernel<64, 64, 4>), dim3((unsigned)(mtiles * ((a.n + 63) / 64))), dim3(64 * 4),
+                       lds, s, a);
+  }
   return hipGetLastError();
 }
 
