@@ -11,3 +11,4 @@ Each function cites the section, equation, table or figure it follows.
 """
 
 from .autofp_ref import *  # noqa: F401,F403
+from .kv_ref import *  # noqa: F401,F403
