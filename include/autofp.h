@@ -128,7 +128,9 @@ typedef enum {
   AUTOFP_OP_SELECT_MASK = 1,  /* rows, k of the weight                          */
   AUTOFP_OP_GEMV = 2,         /* rows = batch (tokens), k                       */
   AUTOFP_OP_GEMM = 3,         /* rows = tokens, k                               */
-  AUTOFP_OP_SIGNALS = 4       /* rows = batch, k = vocab (any vocab >= 1)       */
+  AUTOFP_OP_SIGNALS = 4,      /* rows = batch, k = vocab (any vocab >= 1)       */
+  AUTOFP_OP_KV_WRITE = 5,     /* rows = tokens * KV heads, k = head_dim         */
+  AUTOFP_OP_KV_ATTENTION = 6  /* rows = batch * query heads, k = max_pages      */
 } autofp_op;
 
 /* Fills *p with the paper's hyperparameters. Errors: NULL. */
@@ -268,6 +270,101 @@ autofp_status autofp_policy_update(int32_t phase, int32_t layer, int32_t new_seq
                                    const float *l_a, const float *g_e, int64_t batch,
                                    const autofp_params *p, autofp_policy_state *state,
                                    int32_t *bits_rows, int32_t *bits_layer, void *stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * AutoFP KV cache and decode attention ([AE] §4.1, last paragraph; §5.1)
+ * ---------------------------------------------------------------------------
+ * K and V are kept in AutoFP in two page types of equal byte size ([AE] §4.1):
+ * a base page holds 64 tokens (the KV page size T of [AE] §5.1) with their
+ * NVFP4 base values; a refinement page holds 32 refined tokens with base
+ * values and signed offsets, the offsets stored as 4*delta = d/2 in E2M1
+ * ({-1, -0.5, 0, +0.5}). Every (token, KV head) vector of head_dim = 128
+ * elements is one NVFP4 row: E4M3 scale per 16 elements along the head
+ * dimension, one FP32 tensor scale for the whole K cache and one for V. A
+ * refined token has an offset d for every subgroup (the argmin of autofp_quantize).
+ *
+ * Pools: k_pages and v_pages are [n_pages][h_kv][AUTOFP_KV_PAGE_BYTES]; one
+ * page id addresses the same tokens in both pools and in every KV head; its
+ * type is page_kind[id] (0 base, 1 refinement). Layout of one KV-head section
+ * (C = 64 tokens for a base page, 32 for a refinement page; token t of the page;
+ * E2M1 nibbles with element 2i in the low nibble):
+ *   K: codes   [C][64]  at 0          token-major, dims in order
+ *      scales  [C][8]   at 64*C       E4M3, group j of token t at 8*t + j
+ *      offsets [C][64]  at 72*C       (refinement pages) E2M1 codes of d/2, like codes
+ *   V: codes   [C/8][16][8][4] at 0   block (t/8, dim/8), then t%8: one dword per
+ *                                     token holds dims 8*(dim/8) .. +7
+ *      scales  [8][C]   at 64*C       group-major: group j of token t at C*j + t
+ *      offsets (refinement pages) at 72*C, laid out like the V codes
+ * A refinement section uses 4352 of its 4608 bytes; the tail is never read.
+ *
+ * A sequence b owns the pages page_table[b][0 .. seq_pages[b]-1] (any order:
+ * the attention of one query does not depend on the order of the context);
+ * page id p holds page_tokens[p] tokens in positions 0 .. page_tokens[p]-1
+ * (clamped to its capacity), so a sequence may keep one partly filled page of
+ * each type. Page ids outside [0, n_pages) are skipped as empty.
+ */
+#define AUTOFP_KV_PAGE_TOKENS 64     /* base-page capacity ([AE] §5.1, T = 64)  */
+#define AUTOFP_KV_HEAD_DIM 128       /* the head dimension the kernels support  */
+#define AUTOFP_KV_PAGE_BYTES 4608    /* one KV head of one page: 64 x (64 + 8)  */
+
+typedef struct {
+  int32_t  h_kv;                   /* KV heads                                      */
+  int32_t  head_dim;               /* must be AUTOFP_KV_HEAD_DIM                    */
+  int32_t  n_pages;                /* pages in each pool                            */
+  int32_t  max_pages;              /* columns of page_table                         */
+  uint8_t *k_pages;                /* [n_pages][h_kv][AUTOFP_KV_PAGE_BYTES]         */
+  uint8_t *v_pages;                /* [n_pages][h_kv][AUTOFP_KV_PAGE_BYTES]         */
+  const uint8_t *page_kind;        /* [n_pages] 0 base, 1 refinement                */
+  float   *k_scale;                /* [1] FP32 tensor scale T of the K cache        */
+  float   *v_scale;                /* [1] FP32 tensor scale T of the V cache        */
+  const int32_t *page_table;       /* [batch][max_pages] page ids of each sequence  */
+  const int32_t *seq_pages;        /* [batch] pages in use (clamped to max_pages)   */
+  const int32_t *page_tokens;      /* [n_pages] tokens held by each page            */
+} autofp_kv_cache;
+
+/*
+ * Encode new K/V tokens into their pages. k and v are [n_tokens][h_kv][128]
+ * in `dtype` (F32 or BF16, bf16 widened exactly); slots [n_tokens] (device)
+ * give each token's destination as page_id * 64 + position, with position
+ * below the page's capacity (64 base, 32 refinement); other slots are skipped.
+ * set_scale != 0: first sets *k_scale = amax(k) / 2688 and *v_scale =
+ * amax(v) / 2688 over this call's tokens ([AE] App. B.1, Eq. 2), as for a
+ * prompt; otherwise the stored tensor scales are used and values beyond
+ * 6 * 448 * T saturate. Group scales and codes follow autofp_quantize (Eqs.
+ * 2-3, fp32, ties to even); tokens of refinement pages also get their offsets.
+ * The page table fields of `cache` are not read. Workspace:
+ * autofp_workspace_bytes(AUTOFP_OP_KV_WRITE, n_tokens * h_kv, 128) bytes
+ * (may be NULL when set_scale == 0).
+ * Errors: NULL, SHAPE, DTYPE, WORKSPACE, ARG, HIP.
+ */
+autofp_status autofp_kv_write(const void *k, const void *v, int32_t dtype, int64_t n_tokens,
+                              const int32_t *slots, int32_t set_scale,
+                              const autofp_kv_cache *cache, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
+ * Decode attention over an AutoFP KV cache ([AE] §4.1): for batch row b and
+ * query head h (KV head g = h / (h_q / h_kv)),
+ *   s_j = sm_scale * q[b][h] . K_hat[g][j],  p = softmax(s) over the
+ *   sequence's tokens,  out[b][h] = sum_j p_j V_hat[g][j]
+ * with K_hat, V_hat = T * B * q (NVFP4) and, at level 6, T * B * (q + d/8) for
+ * tokens of refinement pages. Levels 2 and 4 read the KV cache at 4 bits (the
+ * 2-bit level is for weights only, [AE] §3.1 W2A4KV4). bits_dev != NULL: the
+ * level is read on the device at run time (`bits` ignored).
+ * q [batch][h_q][128] F32 or BF16. On the matrix cores K_hat and V_hat are
+ * exact in fp16, and the query and the probabilities enter as sums of two
+ * fp16 parts (relative error about 2^-22); products accumulate in fp32.
+ * out [batch][h_q][128] fp32. h_q must be a multiple of h_kv with at
+ * most 16 query heads per KV head. A sequence with no tokens gives zeros.
+ * Workspace: autofp_workspace_bytes(AUTOFP_OP_KV_ATTENTION, batch * h_q,
+ * cache->max_pages) bytes (partial results of the context splits).
+ * Errors: NULL, SHAPE, BITS, DTYPE, WORKSPACE, ARG, HIP.
+ */
+autofp_status autofp_kv_attention(const void *q, int32_t q_dtype, int64_t batch, int32_t h_q,
+                                  const autofp_kv_cache *cache, int32_t bits,
+                                  const int32_t *bits_dev, float sm_scale, float *out,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

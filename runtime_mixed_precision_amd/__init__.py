@@ -23,7 +23,7 @@ __all__ = [
     "select_weight_mask", "quantize", "quantize_weight", "quantize_activation",
     "alloc_activation", "quantize_into",
     "gemv", "gemm", "policy_signals", "policy_state", "policy_update", "AutofpError",
-    "NativeLibraryError",
+    "NativeLibraryError", "KVCache", "kv_write", "kv_attention",
 ]
 
 _DT = {torch.float32: N.F32, torch.bfloat16: N.BF16}
@@ -295,3 +295,72 @@ def policy_update(phase, layer, l_a, state, g_e=None, new_sequence=False, bits_r
                                          _ptr(g_e), batch, C.byref(p), _ptr(state), _ptr(bits_rows),
                                          _ptr(bits_layer), _stream(stream)), "autofp_policy_update")
     return bits_rows, bits_layer
+
+
+class KVCache:
+    """Device buffers of an AutoFP KV cache (autofp_kv_cache): K and V page
+    pools [n_pages][h_kv][4608] bytes, the page types (0 base: 64 tokens,
+    1 refinement: 32 refined tokens), the tokens each page holds, the two
+    tensor scales and a page table of ``batch`` sequences."""
+
+    def __init__(self, n_pages, h_kv, batch, max_pages, device="cuda:0"):
+        dev = torch.device(device)
+        self.h_kv, self.n_pages, self.batch, self.max_pages = h_kv, n_pages, batch, max_pages
+        self.k_pages = torch.zeros(n_pages, h_kv, N.KV_PAGE_BYTES, dtype=torch.uint8, device=dev)
+        self.v_pages = torch.zeros_like(self.k_pages)
+        self.page_kind = torch.zeros(n_pages, dtype=torch.uint8, device=dev)
+        self.scales = torch.zeros(2, dtype=torch.float32, device=dev)       # T_K, T_V
+        self.page_table = torch.full((batch, max_pages), -1, dtype=torch.int32, device=dev)
+        self.seq_pages = torch.zeros(batch, dtype=torch.int32, device=dev)
+        self.page_tokens = torch.zeros(n_pages, dtype=torch.int32, device=dev)
+
+    def struct(self) -> N.KvCache:
+        c = N.KvCache()
+        c.h_kv, c.head_dim, c.n_pages, c.max_pages = self.h_kv, N.KV_HEAD_DIM, self.n_pages, self.max_pages
+        c.k_pages, c.v_pages = self.k_pages.data_ptr(), self.v_pages.data_ptr()
+        c.page_kind = self.page_kind.data_ptr()
+        c.k_scale = self.scales.data_ptr()
+        c.v_scale = self.scales.data_ptr() + 4
+        c.page_table = self.page_table.data_ptr()
+        c.seq_pages = self.seq_pages.data_ptr()
+        c.page_tokens = self.page_tokens.data_ptr()
+        return c
+
+
+def kv_write(cache: KVCache, k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor, set_scale=False,
+             workspace=None, stream=None):
+    """Encode tokens k, v [n, h_kv, 128] (fp32 or bf16) into the pages named by
+    ``slots`` [n] int32 (page * 64 + position), autofp_kv_write."""
+    _dev_check(k, v, slots)
+    if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 3:
+        raise ValueError("k and v must be matching [n, h_kv, head_dim] tensors")
+    if slots.dtype != torch.int32 or slots.numel() != k.shape[0]:
+        raise ValueError("slots must be int32 with one entry per token")
+    n = k.shape[0]
+    if workspace is None and set_scale:
+        workspace = _workspace(N.OP_KV_WRITE, n * cache.h_kv, N.KV_HEAD_DIM, k.device)
+    c = cache.struct()
+    N.check(N.lib().autofp_kv_write(_ptr(k), _ptr(v), _DT[k.dtype], n, _ptr(slots), int(bool(set_scale)),
+                                    C.byref(c), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                    _stream(stream)), "autofp_kv_write")
+
+
+def kv_attention(q: torch.Tensor, cache: KVCache, bits=4, bits_dev=None, sm_scale=None, out=None,
+                 workspace=None, stream=None) -> torch.Tensor:
+    """Decode attention of q [batch, h_q, 128] (fp32 or bf16) over the cache,
+    autofp_kv_attention; returns [batch, h_q, 128] fp32."""
+    _dev_check(q, bits_dev)
+    if q.dim() != 3:
+        raise ValueError("q must be [batch, h_q, head_dim]")
+    batch, h_q, _ = q.shape
+    if sm_scale is None:
+        sm_scale = N.KV_HEAD_DIM ** -0.5
+    if out is None:
+        out = torch.empty(batch, h_q, N.KV_HEAD_DIM, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = _workspace(N.OP_KV_ATTENTION, batch * h_q, cache.max_pages, q.device)
+    c = cache.struct()
+    N.check(N.lib().autofp_kv_attention(_ptr(q), _DT[q.dtype], batch, h_q, C.byref(c), int(bits),
+                                        _ptr(bits_dev), float(sm_scale), _ptr(out), _ptr(workspace),
+                                        workspace.numel(), _stream(stream)), "autofp_kv_attention")
+    return out

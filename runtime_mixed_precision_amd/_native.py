@@ -21,13 +21,15 @@ STATUS_NAMES = {
 F32, BF16 = 0, 1
 WEIGHT, ACTIVATION = 0, 1
 OP_QUANTIZE, OP_SELECT_MASK, OP_GEMV, OP_GEMM, OP_SIGNALS = 0, 1, 2, 3, 4
+OP_KV_WRITE, OP_KV_ATTENTION = 5, 6
+KV_PAGE_TOKENS, KV_HEAD_DIM, KV_PAGE_BYTES = 64, 128, 4608
 
 # Every symbol include/autofp.h declares.
 EXPORTS = (
     "autofp_default_params", "autofp_status_string", "autofp_packed_bytes",
     "autofp_weight_refined_count", "autofp_workspace_bytes", "autofp_select_weight_mask",
     "autofp_quantize", "autofp_gemv", "autofp_gemm", "autofp_policy_signals",
-    "autofp_policy_update",
+    "autofp_policy_update", "autofp_kv_write", "autofp_kv_attention",
 )
 
 
@@ -61,6 +63,14 @@ class Packed(C.Structure):
     _fields_ = [("rows", C.c_int64), ("k", C.c_int64), ("kind", C.c_int32), ("n_refined", C.c_int32),
                 ("codes", C.c_void_p), ("scales", C.c_void_p), ("tensor_scale", C.c_void_p),
                 ("mask", C.c_void_p), ("offsets", C.c_void_p)]
+
+
+class KvCache(C.Structure):
+    _fields_ = [("h_kv", C.c_int32), ("head_dim", C.c_int32), ("n_pages", C.c_int32),
+                ("max_pages", C.c_int32), ("k_pages", C.c_void_p), ("v_pages", C.c_void_p),
+                ("page_kind", C.c_void_p), ("k_scale", C.c_void_p), ("v_scale", C.c_void_p),
+                ("page_table", C.c_void_p), ("seq_pages", C.c_void_p),
+                ("page_tokens", C.c_void_p)]
 
 
 _lib = None
@@ -99,6 +109,10 @@ def lib():
                                             P(Params), vp, vp, vp, C.c_size_t, vp]),
         "autofp_policy_update": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, vp, vp, C.c_int64,
                                            P(Params), vp, vp, vp, vp]),
+        "autofp_kv_write": (C.c_int, [vp, vp, C.c_int32, C.c_int64, vp, C.c_int32, P(KvCache), vp,
+                                      C.c_size_t, vp]),
+        "autofp_kv_attention": (C.c_int, [vp, C.c_int32, C.c_int64, C.c_int32, P(KvCache), C.c_int32,
+                                          vp, C.c_float, vp, vp, C.c_size_t, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)

@@ -112,4 +112,42 @@ hipError_t launch_policy_update(const PolicyArgs &a, hipStream_t s);
 hipError_t launch_update_norm(const void *h_prev, const void *h_cur, int dtype, int64_t batch,
                               int64_t hidden, float eps, float *out, hipStream_t s);
 
+// ---- kv.hip ----
+struct KvWriteArgs {
+  const void *k, *v;
+  int dtype;
+  int64_t n_tokens;
+  int h_kv;
+  const int32_t *slots;
+  int n_pages;
+  uint8_t *k_pages, *v_pages;
+  const uint8_t *page_kind;
+  float *k_scale, *v_scale;
+  int set_scale;                 // fold the partial maxima into new tensor scales
+  const float *k_part, *v_part;  // amax partials of k and v (set_scale)
+  int n_part;
+};
+hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s);
+
+struct KvAttnArgs {
+  const void *q;
+  int q_dtype;
+  int64_t batch;
+  int h_q, h_kv, grp;            // grp = h_q / h_kv query heads per KV head
+  const uint8_t *k_pages, *v_pages, *page_kind;
+  const float *k_scale, *v_scale;
+  const int32_t *page_table, *seq_pages, *page_tokens;
+  int n_pages, max_pages;
+  int bits;
+  const int32_t *bits_dev;
+  float sm_scale;
+  float *part;                   // [batch * h_q][n_split][kHd + 4] split records
+  int n_split;
+  float *out;
+};
+int kv_attn_splits(int64_t rows, int64_t max_pages);
+int64_t kv_attn_max_pages();
+size_t kv_attn_workspace_bytes(int64_t rows, int64_t max_pages);
+hipError_t launch_kv_attention(const KvAttnArgs &a, hipStream_t s);
+
 }  // namespace afp

@@ -56,6 +56,17 @@ size_t ws_linear(int64_t tokens, int64_t k) {
          align_up(sizeof(int32_t) * (mask_bytes(k) + 1));
 }
 
+size_t ws_kv_write() { return 2 * align_up(sizeof(float) * kAmaxBlocks); }
+
+autofp_status check_kv_cache(const autofp_kv_cache *c) {
+  if (!c) return AUTOFP_ERR_NULL;
+  if (!c->k_pages || !c->v_pages || !c->page_kind || !c->k_scale || !c->v_scale) return AUTOFP_ERR_NULL;
+  if (c->head_dim != AUTOFP_KV_HEAD_DIM || c->h_kv < 1 || c->h_kv > 65535 || c->n_pages < 1)
+    return AUTOFP_ERR_SHAPE;
+  if (!aligned16(c->k_pages) || !aligned16(c->v_pages)) return AUTOFP_ERR_ARG;
+  return AUTOFP_OK;
+}
+
 autofp_status check_packed(const autofp_packed *t, int32_t kind) {
   if (!t) return AUTOFP_ERR_NULL;
   if (t->kind != kind) return AUTOFP_ERR_KIND;
@@ -189,6 +200,16 @@ autofp_status autofp_weight_refined_count(int64_t k, const autofp_params *p, int
 
 autofp_status autofp_workspace_bytes(int32_t op, int64_t rows, int64_t k, size_t *bytes) {
   if (!bytes) return AUTOFP_ERR_NULL;
+  if (op == AUTOFP_OP_KV_WRITE) {
+    if (rows < 1 || k != AUTOFP_KV_HEAD_DIM) return AUTOFP_ERR_SHAPE;
+    *bytes = ws_kv_write();
+    return AUTOFP_OK;
+  }
+  if (op == AUTOFP_OP_KV_ATTENTION) {
+    if (rows < 1 || k < 1 || k > kv_attn_max_pages()) return AUTOFP_ERR_SHAPE;
+    *bytes = kv_attn_workspace_bytes(rows, k);
+    return AUTOFP_OK;
+  }
   if (op == AUTOFP_OP_SIGNALS) {
     if (rows < 1 || k < 1 || rows > 65535) return AUTOFP_ERR_SHAPE;
     *bytes = entropy_workspace_bytes(rows, k);
@@ -394,6 +415,92 @@ autofp_status autofp_policy_update(int32_t phase, int32_t layer, int32_t new_seq
   a.bits_rows = bits_rows;
   a.bits_layer = bits_layer;
   return from_hip(launch_policy_update(a, (hipStream_t)stream));
+}
+
+autofp_status autofp_kv_write(const void *k, const void *v, int32_t dtype, int64_t n_tokens,
+                              const int32_t *slots, int32_t set_scale,
+                              const autofp_kv_cache *cache, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  if (!k || !v || !slots) return AUTOFP_ERR_NULL;
+  const autofp_status cs = check_kv_cache(cache);
+  if (cs != AUTOFP_OK) return cs;
+  if (n_tokens < 1 || n_tokens * cache->h_kv > ((int64_t)1 << 40) / AUTOFP_KV_HEAD_DIM)
+    return AUTOFP_ERR_SHAPE;
+  if (dtype != AUTOFP_F32 && dtype != AUTOFP_BF16) return AUTOFP_ERR_DTYPE;
+  if (!aligned16(k) || !aligned16(v)) return AUTOFP_ERR_ARG;
+  KvWriteArgs a{};
+  a.k = k;
+  a.v = v;
+  a.dtype = dtype;
+  a.n_tokens = n_tokens;
+  a.h_kv = cache->h_kv;
+  a.slots = slots;
+  a.n_pages = cache->n_pages;
+  a.k_pages = cache->k_pages;
+  a.v_pages = cache->v_pages;
+  a.page_kind = cache->page_kind;
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.set_scale = set_scale != 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (a.set_scale) {
+    if (!workspace || !aligned16(workspace) || workspace_bytes < ws_kv_write()) return AUTOFP_ERR_WORKSPACE;
+    float *kp = (float *)workspace;
+    float *vp = (float *)((char *)workspace + align_up(sizeof(float) * kAmaxBlocks));
+    const int64_t n = n_tokens * cache->h_kv * AUTOFP_KV_HEAD_DIM;
+    const int np = amax_partial_count(n);
+    hipError_t e = launch_amax_partial(k, dtype, n, kp, np, s);
+    if (e == hipSuccess) e = launch_amax_partial(v, dtype, n, vp, np, s);
+    if (e != hipSuccess) return AUTOFP_ERR_HIP;
+    a.k_part = kp;
+    a.v_part = vp;
+    a.n_part = np;
+  }
+  return from_hip(launch_kv_write(a, s));
+}
+
+autofp_status autofp_kv_attention(const void *q, int32_t q_dtype, int64_t batch, int32_t h_q,
+                                  const autofp_kv_cache *cache, int32_t bits,
+                                  const int32_t *bits_dev, float sm_scale, float *out,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+  if (!q || !out) return AUTOFP_ERR_NULL;
+  const autofp_status cs = check_kv_cache(cache);
+  if (cs != AUTOFP_OK) return cs;
+  if (!cache->page_table || !cache->seq_pages || !cache->page_tokens) return AUTOFP_ERR_NULL;
+  if (batch < 1 || batch > 65535 || h_q < 1 || h_q % cache->h_kv != 0 || h_q / cache->h_kv > 16)
+    return AUTOFP_ERR_SHAPE;
+  if (cache->max_pages < 1 || cache->max_pages > kv_attn_max_pages()) return AUTOFP_ERR_SHAPE;
+  if (!bits_dev && bits != 2 && bits != 4 && bits != 6) return AUTOFP_ERR_BITS;
+  if (q_dtype != AUTOFP_F32 && q_dtype != AUTOFP_BF16) return AUTOFP_ERR_DTYPE;
+  if (!isfinite(sm_scale)) return AUTOFP_ERR_ARG;
+  if (!aligned16(q) || !aligned16(out)) return AUTOFP_ERR_ARG;
+  const int64_t rows = batch * h_q;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < kv_attn_workspace_bytes(rows, cache->max_pages))
+    return AUTOFP_ERR_WORKSPACE;
+  KvAttnArgs a{};
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.batch = batch;
+  a.h_q = h_q;
+  a.h_kv = cache->h_kv;
+  a.grp = h_q / cache->h_kv;
+  a.k_pages = cache->k_pages;
+  a.v_pages = cache->v_pages;
+  a.page_kind = cache->page_kind;
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.page_table = cache->page_table;
+  a.seq_pages = cache->seq_pages;
+  a.page_tokens = cache->page_tokens;
+  a.n_pages = cache->n_pages;
+  a.max_pages = cache->max_pages;
+  a.bits = bits;
+  a.bits_dev = bits_dev;
+  a.sm_scale = sm_scale;
+  a.part = (float *)workspace;
+  a.n_split = kv_attn_splits(rows, cache->max_pages);
+  a.out = out;
+  return from_hip(launch_kv_attention(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

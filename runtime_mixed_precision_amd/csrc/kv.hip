@@ -1,0 +1,527 @@
+// AutoFP KV cache for gfx950: encoding tokens into base / refinement pages and
+// decode attention over them.
+//
+// "AutoEMatic: Runtime-Adaptive Mixed-Precision LLM Inference via Automatic
+// Exponent-Mantissa Refinement" (arXiv 2611.10165v1):
+//   §4.1 (last paragraph)  attention reads K/V in the AutoFP construction; two
+//                          page types of equal size: T base tokens, or T/2
+//                          refined tokens with offsets stored as 4*delta in E2M1
+//   §5.1                   KV page size T = 64
+//   App. B.1, Eqs. 2-3     NVFP4 encode (T, E4M3 group scales, E2M1 codes)
+//   §3.1                   the 2-bit level is for weights only (W2A4KV4)
+//
+// Attention (one wavefront per (context split, KV head, sequence)):
+//   QK   S^T[token][head] = K_hat (16 tokens x 32 dims) . Q^T on
+//        v_mfma_f32_16x16x32_f16, K_hat = B*q (+ B*d/8) exact in fp16, the
+//        query heads of the KV head in the 16 columns, the query as a sum of
+//        two fp16 parts;
+//   PV   O^T[dim][head] += V_hat^T (16 dims x 32 tokens) . P^T, same MFMA,
+//        V_hat exact in fp16 and P as a sum of two fp16 parts;
+//   an online softmax per head between the two (base-2 exponentials), and the
+//   tensor scales T_K (in the score scale) and T_V (at the merge) in fp32.
+// The token order inside a QK tile is chosen so that the score each lane
+// holds is the probability its lane supplies to the PV tile: no data moves
+// between the two products. A split's (m, l, O) go to the workspace; a merge
+// kernel combines the splits of each (sequence, query head).
+#include <hip/hip_runtime.h>
+
+#include "afp_device.h"
+#include "afp_launch.h"
+
+namespace afp {
+
+namespace {
+
+constexpr int kPageTok = AUTOFP_KV_PAGE_TOKENS;   // base-page capacity
+constexpr int kHd = AUTOFP_KV_HEAD_DIM;
+constexpr int kSec = AUTOFP_KV_PAGE_BYTES;        // bytes of one KV head of one page
+constexpr int kRec = kHd + 4;                     // floats per split record: O, m, l, pad
+constexpr int kMaxPagesPerSplit = 64;
+constexpr int kMaxSplits = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// Page write: one thread per (token, KV head, 16-element group), K and V.
+// ---------------------------------------------------------------------------
+
+struct Enc16 {
+  uint32_t B;          // E4M3 code
+  uint32_t q[16];      // E2M1 codes
+  uint32_t o[16];      // E2M1 codes of d/2 (refined tokens)
+};
+
+// [AE] App. B.1 Eqs. 2-3 for one group, plus the offsets of [AE] §3.2 stored as
+// E2M1 of d/2 ([AE] §4.1): d = +1 -> 0001, 0 -> 0000, -1 -> 1001, -2 -> 1010.
+__device__ __forceinline__ void encode_group16(const float *x, float T, float sixT, bool refine,
+                                               Enc16 &e) {
+#pragma clang fp contract(off)
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(x[i]));
+  const float b = sixT > 0.0f ? a / sixT : 0.0f;
+  e.B = e4m3_encode(b);
+  const float s = T * e4m3_value(e.B);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float v = (s != 0.0f) ? x[i] / s : 0.0f;
+    e.q[i] = e2m1_encode(v);
+    const uint32_t dc = refine ? offset_code(v - e2m1_value(e.q[i])) : 0u;
+    e.o[i] = (0x9A10u >> (4 * dc)) & 0xFu;   // code 0, 1, 2, 3 (d = 0, 1, -2, -1)
+  }
+}
+
+__device__ __forceinline__ void load16(const void *x, int dtype, int64_t e, float *v) {
+  if (dtype == AUTOFP_BF16) {
+    const uint4 *p = (const uint4 *)((const uint16_t *)x + e);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint4 w = p[c];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * c + 2 * j] = __uint_as_float(ww[j] << 16);
+        v[8 * c + 2 * j + 1] = __uint_as_float(ww[j] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const float4 *p = (const float4 *)((const float *)x + e);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float4 w = p[c];
+      v[4 * c] = w.x;
+      v[4 * c + 1] = w.y;
+      v[4 * c + 2] = w.z;
+      v[4 * c + 3] = w.w;
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t pack8(const uint32_t *c) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= c[i] << (4 * i);
+  return w;
+}
+
+// Largest value of the partial maxima, by the whole block (identical in every block).
+__device__ float block_fold_max(const float *partial, int n) {
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) m = fmaxf(m, partial[i]);
+  m = wave_max(m);
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+constexpr int kWriteThreads = 256;
+
+__global__ __launch_bounds__(kWriteThreads) void kv_write_kernel(KvWriteArgs a) {
+#pragma clang fp contract(off)
+  float Tk, Tv;
+  if (a.set_scale) {
+    Tk = block_fold_max(a.k_part, a.n_part) / 2688.0f;
+    Tv = block_fold_max(a.v_part, a.n_part) / 2688.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      *a.k_scale = Tk;
+      *a.v_scale = Tv;
+    }
+  } else {
+    Tk = *a.k_scale;
+    Tv = *a.v_scale;
+  }
+  const int64_t idx = (int64_t)blockIdx.x * kWriteThreads + threadIdx.x;
+  if (idx >= a.n_tokens * a.h_kv * (kHd / 16)) return;
+  const int j = (int)(idx & 7);
+  const int64_t th = idx >> 3;
+  const int h = (int)(th % a.h_kv);
+  const int64_t t = th / a.h_kv;
+  const int32_t slot = a.slots[t];
+  if (slot < 0) return;
+  const int32_t page = slot / kPageTok, pos = slot % kPageTok;
+  if (page >= a.n_pages) return;
+  const bool refine = a.page_kind[page] != 0;
+  const int cap = refine ? kPageTok / 2 : kPageTok;
+  if (pos >= cap) return;
+  const int64_t sec = ((int64_t)page * a.h_kv + h) * kSec;
+  const int64_t e0 = (t * a.h_kv + h) * kHd + 16 * j;
+
+  float x[16];
+  Enc16 e;
+  // K: token-major codes, [token][group] scales
+  load16(a.k, a.dtype, e0, x);
+  encode_group16(x, Tk, 6.0f * Tk, refine, e);
+  uint8_t *kp = a.k_pages + sec;
+  *(uint2 *)(kp + pos * 64 + 8 * j) = make_uint2(pack8(e.q), pack8(e.q + 8));
+  kp[64 * cap + 8 * pos + j] = (uint8_t)e.B;
+  if (refine) *(uint2 *)(kp + 72 * cap + pos * 64 + 8 * j) = make_uint2(pack8(e.o), pack8(e.o + 8));
+
+  // V: [token/8][dim/8][token%8] dwords, [group][token] scales
+  load16(a.v, a.dtype, e0, x);
+  encode_group16(x, Tv, 6.0f * Tv, refine, e);
+  uint8_t *vp = a.v_pages + sec;
+  const int dw = ((pos >> 3) * 16 + 2 * j) * 32 + (pos & 7) * 4;
+  *(uint32_t *)(vp + dw) = pack8(e.q);
+  *(uint32_t *)(vp + dw + 32) = pack8(e.q + 8);
+  vp[64 * cap + cap * j + pos] = (uint8_t)e.B;
+  if (refine) {
+    *(uint32_t *)(vp + 72 * cap + dw) = pack8(e.o);
+    *(uint32_t *)(vp + 72 * cap + dw + 32) = pack8(e.o + 8);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Attention over one context split
+// ---------------------------------------------------------------------------
+
+// One page's loads for the lane (r = lane % 16, g = lane / 16). Slot 0 holds
+// tokens 0..31; slot 1 tokens 32..63 of a base page or the offsets of a
+// refinement page (level 6 only).
+struct PageRegs {
+  uint4 kc[2][2];     // [slot][b]: K codes of token tok(b, r), dims 32g .. 32g+31
+  uint32_t ks[2];     // [slot]: K scales of groups 2g, 2g+1 for b = 0 (low half), 1 (high half)
+  uint4 vc[2][2];     // [slot][half]: V codes of tokens 8g .. 8g+7, dims 8r .. 8r+7
+  uint2 vs[2];        // [slot]: V scales of group r/2, tokens 8g .. 8g+7
+};
+
+// Token of row r of QK tile b (of a 32-token slot): 8 (r / 4) + 4 b + r % 4, so
+// that the output rows 4g .. 4g+3 of tiles 0 and 1 are tokens 8g .. 8g+7.
+__device__ __forceinline__ int qk_token(int b, int r) { return 8 * (r >> 2) + 4 * b + (r & 3); }
+
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ldnt16(const uint8_t *p) {
+  const u32x4v v = __builtin_nontemporal_load((const u32x4v *)p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Two E2M1 codes of byte m of w as fp16 (the byte selector must be a constant).
+__device__ __forceinline__ half2v fp4_byte(uint32_t w, int m) {
+  switch (m) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  }
+}
+
+__device__ __forceinline__ void load_page(PageRegs &pr, const uint8_t *ks, const uint8_t *vs,
+                                          bool refinement, bool six, int r, int g) {
+  const int C = refinement ? kPageTok / 2 : kPageTok;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int t = qk_token(b, r);
+    pr.kc[0][b] = ldnt16(ks + t * 64 + 16 * g);
+  }
+  pr.ks[0] = (uint32_t)*(const uint16_t *)(ks + 64 * C + 8 * qk_token(0, r) + 2 * g) |
+             ((uint32_t)*(const uint16_t *)(ks + 64 * C + 8 * qk_token(1, r) + 2 * g) << 16);
+  pr.vc[0][0] = ldnt16(vs + (g * 16 + r) * 32);
+  pr.vc[0][1] = ldnt16(vs + (g * 16 + r) * 32 + 16);
+  pr.vs[0] = *(const uint2 *)(vs + 64 * C + (r >> 1) * C + 8 * g);
+  if (!refinement) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) pr.kc[1][b] = ldnt16(ks + (32 + qk_token(b, r)) * 64 + 16 * g);
+    pr.ks[1] = (uint32_t)*(const uint16_t *)(ks + 64 * C + 8 * (32 + qk_token(0, r)) + 2 * g) |
+               ((uint32_t)*(const uint16_t *)(ks + 64 * C + 8 * (32 + qk_token(1, r)) + 2 * g) << 16);
+    pr.vc[1][0] = ldnt16(vs + ((4 + g) * 16 + r) * 32);
+    pr.vc[1][1] = ldnt16(vs + ((4 + g) * 16 + r) * 32 + 16);
+    pr.vs[1] = *(const uint2 *)(vs + 64 * C + (r >> 1) * C + 32 + 8 * g);
+  } else if (six) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) pr.kc[1][b] = ldnt16(ks + 72 * C + qk_token(b, r) * 64 + 16 * g);
+    pr.vc[1][0] = ldnt16(vs + 72 * C + (g * 16 + r) * 32);
+    pr.vc[1][1] = ldnt16(vs + 72 * C + (g * 16 + r) * 32 + 16);
+  }
+}
+
+__device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
+__device__ __forceinline__ uint32_t as_u(half2v h) { return __builtin_bit_cast(uint32_t, h); }
+
+__device__ __forceinline__ uint32_t u4(const uint4 &v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+struct SoftState {
+  float m, l;
+  float4v O[8];       // O[n][i]: head r, dim 32g + 8i + n
+};
+
+// One 32-token slot: QK, online softmax, PV. `valid` = tokens of the slot that
+// hold data (1..32); ref = the slot's offsets are in slot 1 (level 6).
+__device__ __forceinline__ void attend_slot(const PageRegs &pr, int slot, bool ref, int valid,
+                                            const half8v *qb, const half8v *ql, bool qlo, float cs,
+                                            int g, SoftState &st) {
+  // --- scores of tokens 8g .. 8g+7 for head r
+  float x[8];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const uint32_t sb = (pr.ks[slot] >> (16 * b)) & 0xFFFFu;
+    const half2v sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
+    float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      half8v k8 = fp4x8_to_half8(u4(pr.kc[slot][b], s));
+      if (ref) k8 += fp4x8_to_half8(u4(pr.kc[1][b], s)) * (_Float16)0.25f;
+      const _Float16 bs = (s < 2) ? sc[0] : sc[1];
+      k8 *= bs;
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k8, qb[s], acc, 0, 0, 0);
+      if (qlo) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k8, ql[s], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * b + i;
+      x[j] = (8 * g + j < valid) ? acc[i] * cs : -INFINITY;
+    }
+  }
+  float mb = x[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) mb = fmaxf(mb, x[j]);
+  mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+  mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+  const float mn = fmaxf(st.m, mb);
+  const float alpha = exp2f(st.m - mn);
+  float p[8], ps = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = exp2f(x[j] - mn);
+    ps += p[j];
+  }
+  st.l = st.l * alpha + ps;
+  st.m = mn;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) st.O[n] *= alpha;
+  // p = P + Pl with both parts in fp16 (error ~2^-22 p), so the fp16 operand
+  // rounding of the probabilities does not reach the output
+  half8v P, Pl;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    P[j] = (_Float16)p[j];
+    Pl[j] = (_Float16)(p[j] - (float)P[j]);
+  }
+
+  // --- V_hat^T operands: dim 8r + n, tokens 8g .. 8g+7
+  uint2 vsc = pr.vs[slot];
+  const int nv = valid - 8 * g;   // tokens of this lane group that hold data
+  if (nv < 8) {
+    const uint64_t keep = nv <= 0 ? 0ull : (~0ull >> (64 - 8 * nv));
+    vsc.x &= (uint32_t)keep;
+    vsc.y &= (uint32_t)(keep >> 32);
+  }
+  half2v bp[4];
+  bp[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vsc.x, 1.0f, false);
+  bp[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vsc.x, 1.0f, true);
+  bp[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vsc.y, 1.0f, false);
+  bp[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vsc.y, 1.0f, true);
+  uint32_t X[8], Y[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    X[j] = u4(pr.vc[slot][j >> 2], j & 3);
+    Y[j] = ref ? u4(pr.vc[1][j >> 2], j & 3) : 0u;
+  }
+  uint32_t A[8][4];   // [n][token pair]
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int jp = 0; jp < 4; ++jp) {
+      half2v c0 = fp4_byte(X[2 * jp], m);
+      half2v c1 = fp4_byte(X[2 * jp + 1], m);
+      if (ref) {
+        const half2v q4 = half2v{(_Float16)0.25f, (_Float16)0.25f};
+        c0 += fp4_byte(Y[2 * jp], m) * q4;
+        c1 += fp4_byte(Y[2 * jp + 1], m) * q4;
+      }
+      const half2v lo = as_h2(__builtin_amdgcn_perm(as_u(c1), as_u(c0), 0x05040100u)) * bp[jp];
+      const half2v hi = as_h2(__builtin_amdgcn_perm(as_u(c1), as_u(c0), 0x07060302u)) * bp[jp];
+      A[2 * m][jp] = as_u(lo);
+      A[2 * m + 1][jp] = as_u(hi);
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const half8v a8 = __builtin_bit_cast(half8v, make_uint4(A[n][0], A[n][1], A[n][2], A[n][3]));
+    st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, P, st.O[n], 0, 0, 0);
+    st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, Pl, st.O[n], 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(64) void kv_attn_split_kernel(KvAttnArgs a) {
+  const int split = blockIdx.x, hk = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
+  const int level = a.bits_dev ? *a.bits_dev : a.bits;
+  const bool six = level == 6;
+
+  int np = a.seq_pages[b];
+  np = np < 0 ? 0 : (np > a.max_pages ? a.max_pages : np);
+  const int pps = (np + a.n_split - 1) / a.n_split;
+  const int p0 = split * pps;
+  const int p1 = (p0 + pps) < np ? (p0 + pps) : np;
+  const int npp = p1 > p0 ? p1 - p0 : 0;
+
+  // page id, type and fill of the split's pages, one page per lane; pages
+  // without tokens are dropped here (id -1)
+  int my_pg = -1, my_kind = 0, my_fill = 0;
+  if (lane < npp) {
+    const int pg = a.page_table[b * a.max_pages + p0 + lane];
+    if (pg >= 0 && pg < a.n_pages) {
+      my_kind = a.page_kind[pg] != 0 ? 1 : 0;
+      const int cap = my_kind ? kPageTok / 2 : kPageTok;
+      const int f = a.page_tokens[pg];
+      my_fill = f < 0 ? 0 : (f > cap ? cap : f);
+      my_pg = my_fill > 0 ? pg : -1;
+    }
+  }
+
+  // query fragment: head hk*grp + r (zeros for the unused columns), dims
+  // 32g + 8s + 0..7, as fp16 q = qb + ql (ql is zero for bf16 queries in the
+  // fp16 range; its MFMA is skipped when the whole wavefront's ql is zero)
+  half8v qb[4], ql[4];
+  bool any_lo = false;
+  {
+    const int head = hk * a.grp + r;
+    const bool live = r < a.grp;
+    const int64_t q0 = (b * a.h_q + (live ? head : 0)) * kHd + 32 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float f[8];
+      if (a.q_dtype == AUTOFP_BF16) {
+        const uint4 w = *(const uint4 *)((const uint16_t *)a.q + q0 + 8 * s);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f[2 * j] = __uint_as_float(ww[j] << 16);
+          f[2 * j + 1] = __uint_as_float(ww[j] & 0xFFFF0000u);
+        }
+      } else {
+        const float4 u = *(const float4 *)((const float *)a.q + q0 + 8 * s);
+        const float4 v = *(const float4 *)((const float *)a.q + q0 + 8 * s + 4);
+        f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
+        f[4] = v.x; f[5] = v.y; f[6] = v.z; f[7] = v.w;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float fj = live ? f[j] : 0.0f;
+        qb[s][j] = (_Float16)fj;
+        ql[s][j] = (_Float16)(fj - (float)qb[s][j]);
+        any_lo |= ql[s][j] != (_Float16)0.0f;
+      }
+    }
+  }
+  const bool qlo = __any(any_lo);
+  const float cs = a.sm_scale * *a.k_scale * kLog2e;
+
+  SoftState st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) st.O[n] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t head_off = (int64_t)hk * kSec;
+  const int64_t page_stride = (int64_t)a.h_kv * kSec;
+  PageRegs cur, nxt;
+  auto issue = [&](PageRegs &pr, int i) {
+    const int pg = __builtin_amdgcn_readlane(my_pg, i);
+    const int kind = __builtin_amdgcn_readlane(my_kind, i);
+    if (pg < 0) return;
+    const uint8_t *kp = a.k_pages + pg * page_stride + head_off;
+    const uint8_t *vp = a.v_pages + pg * page_stride + head_off;
+    load_page(pr, kp, vp, kind != 0, six, r, g);
+  };
+  if (npp > 0) issue(cur, 0);
+  for (int i = 0; i < npp; ++i) {
+    if (i + 1 < npp) issue(nxt, i + 1);
+    const int pg = __builtin_amdgcn_readlane(my_pg, i);
+    const int kind = __builtin_amdgcn_readlane(my_kind, i);
+    if (pg >= 0) {
+      const int valid = __builtin_amdgcn_readlane(my_fill, i);
+      if (kind) {
+        attend_slot(cur, 0, six, valid, qb, ql, qlo, cs, g, st);
+      } else {
+        attend_slot(cur, 0, false, valid, qb, ql, qlo, cs, g, st);
+        if (valid > 32) attend_slot(cur, 1, false, valid - 32, qb, ql, qlo, cs, g, st);
+      }
+    }
+    cur = nxt;
+  }
+
+  // split record: O (dims 32g .. 32g+31 of head r), m, l
+  float l = st.l + __shfl_xor(st.l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (r < a.grp) {
+    float *rec = a.part + ((b * a.h_q + hk * a.grp + r) * a.n_split + split) * kRec;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *(float4 *)(rec + 32 * g + 8 * i) = make_float4(st.O[0][i], st.O[1][i], st.O[2][i], st.O[3][i]);
+      *(float4 *)(rec + 32 * g + 8 * i + 4) = make_float4(st.O[4][i], st.O[5][i], st.O[6][i], st.O[7][i]);
+    }
+    if (g == 0) {
+      rec[kHd] = st.m;
+      rec[kHd + 1] = l;
+    }
+  }
+}
+
+// Combine the splits of one (sequence, query head): one wavefront, two dims per lane.
+__global__ __launch_bounds__(64) void kv_attn_merge_kernel(const float *__restrict__ part, int n_split,
+                                                           const float *__restrict__ v_scale,
+                                                           float *__restrict__ out) {
+  const int64_t row = blockIdx.x;
+  const float *rec0 = part + row * n_split * kRec;
+  const int lane = threadIdx.x;
+  float mloc = -INFINITY;
+  for (int s = lane; s < n_split; s += 64) mloc = fmaxf(mloc, rec0[s * kRec + kHd]);
+  const float M = wave_max(mloc);
+  float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < n_split; ++s) {
+      const float *rec = rec0 + s * kRec;
+      const float ms = rec[kHd];
+      if (ms == -INFINITY) continue;
+      const float w = exp2f(ms - M);
+      L += rec[kHd + 1] * w;
+      const float2 o = *(const float2 *)(rec + 2 * lane);
+      o0 += o.x * w;
+      o1 += o.y * w;
+    }
+  }
+  const float f = L > 0.0f ? *v_scale / L : 0.0f;
+  *(float2 *)(out + row * kHd + 2 * lane) = make_float2(o0 * f, o1 * f);
+}
+
+}  // namespace
+
+int kv_attn_splits(int64_t rows, int64_t max_pages) {
+  int64_t s = (16384 + rows - 1) / rows;
+  const int64_t need = (max_pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit;
+  if (s < need) s = need;
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s > max_pages) s = max_pages;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+int64_t kv_attn_max_pages() { return (int64_t)kMaxSplits * kMaxPagesPerSplit; }
+
+size_t kv_attn_workspace_bytes(int64_t rows, int64_t max_pages) {
+  return (size_t)rows * (size_t)kv_attn_splits(rows, max_pages) * kRec * sizeof(float);
+}
+
+hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s) {
+  const int64_t n = a.n_tokens * a.h_kv * (kHd / 16);
+  hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)((n + kWriteThreads - 1) / kWriteThreads)),
+                     dim3(kWriteThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_attention(const KvAttnArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(kv_attn_split_kernel, dim3((unsigned)a.n_split, (unsigned)a.h_kv, (unsigned)a.batch),
+                     dim3(64), 0, s, a);
+  hipLaunchKernelGGL(kv_attn_merge_kernel, dim3((unsigned)(a.batch * a.h_q)), dim3(64), 0, s, a.part,
+                     a.n_split, a.v_scale, a.out);
+  return hipGetLastError();
+}
+
+}  // namespace afp

@@ -70,3 +70,77 @@ def hidden(batch, dim=HIDDEN, seed=0, tensor_id=0, dtype=torch.float32, device="
     """Hidden states ~ N(0, 1) [batch x dim]."""
     g = _gen(seed, tensor_id, device)
     return torch.randn(batch, dim, generator=g, device=device, dtype=torch.float32).to(dtype)
+
+
+def kv_tokens(n, h_kv, head_dim=128, seed=0, tensor_id=0, dtype=torch.bfloat16, device="cpu"):
+    """K or V vectors ~ N(0, 1) [n x h_kv x head_dim], rounded to ``dtype``."""
+    g = _gen(seed, tensor_id, device)
+    return torch.randn(n, h_kv, head_dim, generator=g, device=device, dtype=torch.float32).to(dtype)
+
+
+def kv_page_plan(lengths, refine_frac=0.0, seed=0, max_run=96, page_tokens=64):
+    """A page layout for sequences of the given token counts (host bookkeeping).
+
+    Each sequence's tokens come in runs of 1 .. max_run tokens; a run is
+    refined with probability ``refine_frac`` (all runs refined for 1.0, none
+    for 0.0). A sequence keeps one open page per type (base: page_tokens
+    tokens, refinement: page_tokens / 2) and opens a new one when it fills.
+    Page ids are a random permutation, so a sequence's pages are scattered.
+
+    Returns a dict of numpy arrays: page_kind [n_pages] uint8, page_tokens
+    [n_pages] int32, page_table [batch, max_pages] int32 (-1 padded),
+    seq_pages [batch] int32, and per sequence: slots (page * page_tokens +
+    position per token, in token order) and refine (bool per token).
+    """
+    import numpy as np
+
+    rng = np.random.default_rng([int(seed), 7])
+    kinds, fills, owners = [], [], []
+    seq_slots, seq_refine, seq_pages_l = [], [], []
+    for b, L in enumerate(lengths):
+        ref = np.zeros(L, dtype=bool)
+        if refine_frac >= 1.0:
+            ref[:] = True
+        elif refine_frac > 0.0:
+            t = 0
+            while t < L:
+                run = int(rng.integers(1, max_run + 1))
+                ref[t:t + run] = rng.random() < refine_frac
+                t += run
+        open_page = {0: -1, 1: -1}
+        slots = np.empty(L, dtype=np.int64)
+        pages = []
+        for t in range(L):
+            kd = int(ref[t])
+            cap = page_tokens // 2 if kd else page_tokens
+            p = open_page[kd]
+            if p < 0 or fills[p] == cap:
+                p = len(kinds)
+                kinds.append(kd)
+                fills.append(0)
+                owners.append(b)
+                open_page[kd] = p
+                pages.append(p)
+            slots[t] = p * page_tokens + fills[p]
+            fills[p] += 1
+        seq_slots.append(slots)
+        seq_refine.append(ref)
+        seq_pages_l.append(pages)
+    n_pages = max(len(kinds), 1)
+    perm = rng.permutation(n_pages)           # logical page -> physical id
+    page_kind = np.zeros(n_pages, np.uint8)
+    page_fill = np.zeros(n_pages, np.int32)
+    for p in range(len(kinds)):
+        page_kind[perm[p]] = kinds[p]
+        page_fill[perm[p]] = fills[p]
+    max_pages = max(1, max(len(p) for p in seq_pages_l))
+    table = np.full((len(lengths), max_pages), -1, np.int32)
+    for b, pages in enumerate(seq_pages_l):
+        table[b, :len(pages)] = perm[np.asarray(pages, dtype=np.int64)] if pages else []
+    out_slots = []
+    for slots in seq_slots:
+        p, pos = slots // page_tokens, slots % page_tokens
+        out_slots.append((perm[p] * page_tokens + pos).astype(np.int32) if len(slots) else slots.astype(np.int32))
+    return dict(page_kind=page_kind, page_tokens=page_fill, page_table=table,
+                seq_pages=np.array([len(p) for p in seq_pages_l], np.int32),
+                slots=out_slots, refine=seq_refine, n_pages=n_pages, max_pages=max_pages)

@@ -179,3 +179,59 @@ def test_policy_update_rejects_bad_arguments(N):
     assert up(0, 0, FAKE, FAKE, 0, FAKE, FAKE) == 2
     p.alpha = 0
     assert up(1, 0, FAKE, FAKE, 1, FAKE, FAKE) == 8
+
+
+def kv_cache(N, h_kv=8, n_pages=4, max_pages=4, head_dim=128):
+    return N.KvCache(h_kv, head_dim, n_pages, max_pages, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def test_kv_workspace_sizes(N):
+    L = N.lib()
+    b = C.c_size_t()
+    assert C.sizeof(N.KvCache) == 80
+    assert L.autofp_workspace_bytes(N.OP_KV_WRITE, 16, 128, C.byref(b)) == 0 and b.value >= 2 * 4 * 1024
+    assert L.autofp_workspace_bytes(N.OP_KV_WRITE, 16, 64, C.byref(b)) == 2
+    # one record of 128 + 4 floats per (row, context split)
+    assert L.autofp_workspace_bytes(N.OP_KV_ATTENTION, 512, 512, C.byref(b)) == 0
+    assert b.value % (512 * 132 * 4) == 0 and 1 <= b.value // (512 * 132 * 4) <= 64
+    assert L.autofp_workspace_bytes(N.OP_KV_ATTENTION, 1, 1, C.byref(b)) == 0 and b.value == 132 * 4
+    assert L.autofp_workspace_bytes(N.OP_KV_ATTENTION, 4, 64 * 64 + 1, C.byref(b)) == 2
+
+
+def test_kv_write_rejects_bad_arguments(N):
+    L = N.lib()
+    c = kv_cache(N)
+    w = lambda k, v, dt, n, slots, c_, ws=FAKE, wsb=1 << 20, ss=0: L.autofp_kv_write(
+        k, v, dt, n, slots, ss, c_, ws, wsb, None)
+    assert w(None, FAKE, N.F32, 4, FAKE, C.byref(c)) == 1
+    assert w(FAKE, FAKE, N.F32, 4, None, C.byref(c)) == 1
+    assert w(FAKE, FAKE, N.F32, 4, FAKE, None) == 1
+    assert w(FAKE, FAKE, 3, 4, FAKE, C.byref(c)) == 7
+    assert w(FAKE, FAKE, N.F32, 0, FAKE, C.byref(c)) == 2
+    bad = kv_cache(N, head_dim=64)
+    assert w(FAKE, FAKE, N.F32, 4, FAKE, C.byref(bad)) == 2
+    assert w(FAKE + 4, FAKE, N.F32, 4, FAKE, C.byref(c)) == 8
+    assert w(FAKE, FAKE, N.F32, 4, FAKE, C.byref(c), ws=None, ss=1) == 5   # the scale pass needs scratch
+    assert w(FAKE, FAKE, N.F32, 4, FAKE, C.byref(c), wsb=16, ss=1) == 5
+
+
+def test_kv_attention_rejects_bad_arguments(N):
+    L = N.lib()
+    c = kv_cache(N)
+    a = lambda q, batch, hq, c_, bits=4, out=FAKE, ws=FAKE, wsb=1 << 30, dt=0, sm=0.088: \
+        L.autofp_kv_attention(q, dt, batch, hq, c_, bits, None, sm, out, ws, wsb, None)
+    assert a(None, 2, 32, C.byref(c)) == 1
+    assert a(FAKE, 2, 32, C.byref(c), out=None) == 1
+    assert a(FAKE, 2, 30, C.byref(c)) == 2                 # 30 query heads over 8 KV heads
+    assert a(FAKE, 2, 8 * 17, C.byref(c)) == 2             # more than 16 query heads per KV head
+    assert a(FAKE, 0, 32, C.byref(c)) == 2
+    assert a(FAKE, 2, 32, C.byref(c), bits=5) == 3
+    assert a(FAKE, 2, 32, C.byref(c), dt=4) == 7
+    assert a(FAKE, 2, 32, C.byref(c), sm=float("inf")) == 8
+    assert a(FAKE, 2, 32, C.byref(c), wsb=16) == 5
+    assert a(FAKE, 2, 32, C.byref(c), ws=None) == 5
+    nt = kv_cache(N)
+    nt.page_table = None
+    assert a(FAKE, 2, 32, C.byref(nt)) == 1
+    big = kv_cache(N, max_pages=64 * 64 + 1)
+    assert a(FAKE, 2, 32, C.byref(big)) == 2

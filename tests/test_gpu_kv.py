@@ -1,0 +1,299 @@
+"""GPU parity of the AutoFP KV cache against the oracle.
+
+  - autofp_kv_write: every written token's E2M1 codes, E4M3 scales, offsets
+    (E2M1 codes of d/2) and the two tensor scales equal the oracle's,
+    bit for bit, read back through the page layout that include/autofp.h
+    documents (decoded here independently of the library);
+  - autofp_kv_attention: outputs within 1e-3 (relative, with a floor of 0.01
+    x the row's rms) of the oracle's fp64 attention over its own decoded K/V,
+    at levels 2/4/6, fp32 and bf16 queries, ragged and empty sequences, mixed
+    page types, 1/4/16 query heads per KV head, and the device-side level;
+  - the full decode shape (16 sequences x 32768 tokens, 32 query / 8 KV
+    heads) on sampled (sequence, head) pairs.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import runtime_mixed_precision_amd as A
+from runtime_mixed_precision_amd import synthetic as S
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+HD = 128
+PT = 64
+TOL = 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def nibbles(b):
+    b = np.asarray(b, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.uint8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return out
+
+
+OFFSET_OF_CODE = {0x0: 0, 0x1: 1, 0x9: -1, 0xA: -2}
+
+
+def read_section(sec, refined, which):
+    """(codes [C, 128], scales [C, 8], d [C, 128] or None) of one KV-head page
+    section, following the layout of include/autofp.h."""
+    C = PT // 2 if refined else PT
+    sec = np.asarray(sec, dtype=np.uint8)
+
+    def codes_at(off):
+        raw = sec[off:off + 64 * C]
+        if which == "k":
+            return nibbles(raw.reshape(C, 64))
+        blk = raw.reshape(C // 8, 16, 8, 4).transpose(0, 2, 1, 3).reshape(C, 64)
+        return nibbles(blk)
+
+    codes = codes_at(0)
+    sc = sec[64 * C:72 * C]
+    scales = sc.reshape(C, 8) if which == "k" else sc.reshape(8, C).T
+    d = None
+    if refined:
+        oc = codes_at(72 * C)
+        bad = ~np.isin(oc, list(OFFSET_OF_CODE))
+        assert not bad.any(), "offset code outside {0000, 0001, 1001, 1010}"
+        d = np.vectorize(OFFSET_OF_CODE.get)(oc).astype(np.int8)
+    return codes, scales, d
+
+
+class Case:
+    """A KV cache of ragged sequences written through autofp_kv_write."""
+
+    def __init__(self, lengths, h_kv, refine_frac, seed, dtype=torch.bfloat16, max_pages=None):
+        self.lengths, self.h_kv = list(lengths), h_kv
+        self.plan = S.kv_page_plan(self.lengths, refine_frac, seed=seed)
+        n = sum(self.lengths)
+        self.k = S.kv_tokens(max(n, 1), h_kv, seed=seed, tensor_id=1, dtype=dtype, device=DEV)
+        self.v = S.kv_tokens(max(n, 1), h_kv, seed=seed, tensor_id=2, dtype=dtype, device=DEV)
+        mp = max_pages or self.plan["max_pages"]
+        self.cache = A.KVCache(self.plan["n_pages"], h_kv, len(self.lengths), mp, device=DEV)
+        self.cache.page_kind.copy_(torch.from_numpy(self.plan["page_kind"]))
+        self.cache.page_tokens.copy_(torch.from_numpy(self.plan["page_tokens"]))
+        tbl = np.full((len(self.lengths), mp), -1, np.int32)
+        tbl[:, :self.plan["max_pages"]] = self.plan["page_table"]
+        self.cache.page_table.copy_(torch.from_numpy(tbl))
+        self.cache.seq_pages.copy_(torch.from_numpy(self.plan["seq_pages"]))
+        slots = np.concatenate(self.plan["slots"]) if n else np.zeros(0, np.int32)
+        self.slots = torch.from_numpy(slots.astype(np.int32)).to(DEV)
+        self.n = n
+        if n:
+            A.kv_write(self.cache, self.k[:n], self.v[:n], self.slots, set_scale=True)
+        torch.cuda.synchronize()
+        self.kf = self.k[:n].float().cpu().numpy()
+        self.vf = self.v[:n].float().cpu().numpy()
+        self.refine = np.concatenate(self.plan["refine"]) if n else np.zeros(0, bool)
+        self.starts = np.concatenate([[0], np.cumsum(self.lengths)])
+
+    def oracle_kv(self, which, amax=None):
+        x = self.kf if which == "k" else self.vf
+        rows = x.reshape(-1, HD)
+        ref = np.repeat(self.refine, self.h_kv)
+        return O.kv_quantize(rows, ref, tensor_amax=amax)
+
+    def oracle_attention(self, q, level, sm_scale, kvq=None, seqs=None, heads=None):
+        kq, vq = kvq or (self.oracle_kv("k"), self.oracle_kv("v"))
+        kh = O.kv_decode(kq, level).reshape(self.n, self.h_kv, HD)
+        vh = O.kv_decode(vq, level).reshape(self.n, self.h_kv, HD)
+        B, hq = q.shape[0], q.shape[1]
+        out = np.zeros((B, hq, HD))
+        for b in (seqs if seqs is not None else range(B)):
+            s0, s1 = self.starts[b], self.starts[b + 1]
+            if s1 == s0:
+                continue
+            kb = kh[s0:s1].transpose(1, 0, 2)
+            vb = vh[s0:s1].transpose(1, 0, 2)
+            out[b] = O.kv_attention(q[b], kb, vb, sm_scale)
+        return out
+
+
+def check_close(y, ref, where):
+    y = np.asarray(y, np.float64).reshape(-1, HD)
+    ref = np.asarray(ref, np.float64).reshape(-1, HD)
+    rms = np.sqrt((ref ** 2).mean(axis=1, keepdims=True))
+    den = np.maximum(np.abs(ref), 0.01 * rms)
+    den = np.where(den > 0, den, 1.0)
+    err = np.abs(y - ref) / den
+    assert np.all(np.isfinite(y)), where
+    assert err.max() <= TOL, (where, float(err.max()), np.unravel_index(err.argmax(), err.shape))
+    return float(err.max())
+
+
+def check_pages(case, kq, vq, tokens=None):
+    """Bit-exact comparison of the written pages with the oracle's codes."""
+    kp = case.cache.k_pages.cpu().numpy()
+    vp = case.cache.v_pages.cpu().numpy()
+    slots = case.slots.cpu().numpy()
+    kinds = case.plan["page_kind"]
+    toks = range(case.n) if tokens is None else tokens
+    for t in toks:
+        page, pos = int(slots[t]) // PT, int(slots[t]) % PT
+        refined = bool(kinds[page])
+        assert refined == bool(case.refine[t])
+        for h in range(case.h_kv):
+            row = t * case.h_kv + h
+            for which, pool, ref in (("k", kp, kq), ("v", vp, vq)):
+                codes, scales, d = read_section(pool[page, h], refined, which)
+                assert np.array_equal(codes[pos], ref["q"][row]), (which, t, h)
+                assert np.array_equal(scales[pos], ref["scales"][row]), (which, t, h)
+                if refined:
+                    assert np.array_equal(d[pos], ref["d"][row]), (which, t, h)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_kv_write_bit_exact(dtype):
+    say(f"case: kv_write mixed pages, {dtype}")
+    case = Case([1, 100, 700, 0, 64, 33], h_kv=8, refine_frac=0.5, seed=11, dtype=dtype)
+    kq, vq = case.oracle_kv("k"), case.oracle_kv("v")
+    T = case.cache.scales.cpu().numpy()
+    assert np.float32(T[0]) == np.float32(kq["T"]) and np.float32(T[1]) == np.float32(vq["T"])
+    check_pages(case, kq, vq)
+
+
+def test_kv_write_append_uses_stored_scale():
+    say("case: kv_write append with the stored tensor scales")
+    case = Case([300, 50], h_kv=2, refine_frac=0.5, seed=12)
+    amax_k = float(np.max(np.abs(case.kf)))
+    amax_v = float(np.max(np.abs(case.vf)))
+    # new tokens (scaled up so some saturate) into the free positions of fresh pages
+    extra = 40
+    kx = (S.kv_tokens(extra, 2, seed=13, tensor_id=1, device=DEV).float() * 3.0).to(torch.bfloat16)
+    vx = (S.kv_tokens(extra, 2, seed=13, tensor_id=2, device=DEV).float() * 3.0).to(torch.bfloat16)
+    kinds = case.plan["page_kind"]
+    # a new cache of two pages (one of each type) receives the appended tokens
+    c2 = A.KVCache(2, 2, 1, 2, device=DEV)
+    c2.page_kind.copy_(torch.tensor([0, 1], dtype=torch.uint8))
+    c2.scales.copy_(case.cache.scales)
+    ref = np.zeros(extra, bool)
+    ref[::3] = True                                   # every third token refined
+    slots, fill = [], [0, 0]
+    for t in range(extra):
+        p = int(ref[t])
+        slots.append(p * PT + fill[p])
+        fill[p] += 1
+    st = torch.tensor(slots, dtype=torch.int32, device=DEV)
+    A.kv_write(c2, kx, vx, st, set_scale=False)
+    torch.cuda.synchronize()
+    assert torch.equal(c2.scales, case.cache.scales)
+    kxr = kx.float().cpu().numpy().reshape(-1, HD)
+    vxr = vx.float().cpu().numpy().reshape(-1, HD)
+    kq = O.kv_quantize(kxr, np.repeat(ref, 2), tensor_amax=np.float32(amax_k))
+    vq = O.kv_quantize(vxr, np.repeat(ref, 2), tensor_amax=np.float32(amax_v))
+    assert np.float32(kq["T"]) == np.float32(case.cache.scales[0].item())
+    kp, vp = c2.k_pages.cpu().numpy(), c2.v_pages.cpu().numpy()
+    for t in range(extra):
+        page, pos = slots[t] // PT, slots[t] % PT
+        for h in range(2):
+            for which, pool, r in (("k", kp, kq), ("v", vp, vq)):
+                codes, scales, d = read_section(pool[page, h], bool(page), which)
+                row = 2 * t + h
+                assert np.array_equal(codes[pos], r["q"][row])
+                assert np.array_equal(scales[pos], r["scales"][row])
+                if page:
+                    assert np.array_equal(d[pos], r["d"][row])
+    assert kinds is not None
+
+
+@pytest.mark.parametrize("level", [2, 4, 6])
+@pytest.mark.parametrize("qdt", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("heads", [(32, 8), (8, 8), (16, 1)])
+def test_kv_attention_parity(level, qdt, heads):
+    hq, hkv = heads
+    say(f"case: kv_attention level {level}, q {qdt}, heads {hq}/{hkv}")
+    case = Case([1, 100, 700, 0, 64, 33, 1500], h_kv=hkv, refine_frac=0.5, seed=21 + hkv)
+    B = len(case.lengths)
+    q = S.kv_tokens(B, hq, seed=22, tensor_id=3, dtype=qdt, device=DEV)
+    sm = HD ** -0.5
+    y = A.kv_attention(q, case.cache, bits=level, sm_scale=sm).cpu().numpy()
+    qn = q.float().cpu().numpy()
+    ref = case.oracle_attention(qn, level, sm)
+    e = check_close(y, ref, (level, str(qdt), heads))
+    # the empty sequence gives zeros
+    assert not y[3].any()
+    say(f"max rel err {e:.2e}")
+
+
+def test_kv_attention_device_level_and_scale():
+    say("case: kv_attention device level, sm_scale, all refined and all base")
+    for frac in (0.0, 1.0):
+        case = Case([257, 31, 900], h_kv=4, refine_frac=frac, seed=31)
+        q = S.kv_tokens(3, 16, seed=32, tensor_id=3, dtype=torch.float32, device=DEV)
+        for level in (2, 4, 6):
+            lv = torch.tensor([level], dtype=torch.int32, device=DEV)
+            y_host = A.kv_attention(q, case.cache, bits=level, sm_scale=0.3)
+            y_dev = A.kv_attention(q, case.cache, bits=4, bits_dev=lv, sm_scale=0.3)
+            assert torch.equal(y_host, y_dev), level
+            ref = case.oracle_attention(q.cpu().numpy(), level, 0.3)
+            check_close(y_host.cpu().numpy(), ref, (frac, level))
+        # level 2 reads the cache at 4 bits
+        y2 = A.kv_attention(q, case.cache, bits=2, sm_scale=0.3)
+        y4 = A.kv_attention(q, case.cache, bits=4, sm_scale=0.3)
+        assert torch.equal(y2, y4)
+
+
+def test_kv_attention_full_decode_shape_sampled():
+    """16 sequences x 32768 tokens, 32 query / 8 KV heads, bf16 K/V and q, all
+    base pages (the 4-bit decode configuration), then the same context with
+    every token refined at level 6; sampled (sequence, head) pairs."""
+    B, L, hq, hkv = 16, 32768, 32, 8
+    for frac, level in ((0.0, 4), (1.0, 6)):
+        say(f"case: full decode shape, refine_frac {frac}, level {level}")
+        plan = S.kv_page_plan([L] * B, frac, seed=41)
+        n = B * L
+        k = S.kv_tokens(n, hkv, seed=42, tensor_id=1, device=DEV)
+        v = S.kv_tokens(n, hkv, seed=42, tensor_id=2, device=DEV)
+        cache = A.KVCache(plan["n_pages"], hkv, B, plan["max_pages"], device=DEV)
+        cache.page_kind.copy_(torch.from_numpy(plan["page_kind"]))
+        cache.page_tokens.copy_(torch.from_numpy(plan["page_tokens"]))
+        cache.page_table.copy_(torch.from_numpy(plan["page_table"]))
+        cache.seq_pages.copy_(torch.from_numpy(plan["seq_pages"]))
+        slots = torch.from_numpy(np.concatenate(plan["slots"])).to(DEV)
+        A.kv_write(cache, k, v, slots, set_scale=True)
+        q = S.kv_tokens(B, hq, seed=43, tensor_id=3, device=DEV)
+        y = A.kv_attention(q, cache, bits=level).cpu().numpy()
+        amax_k = float(k.abs().max().float())
+        amax_v = float(v.abs().max().float())
+        torch.cuda.synchronize()
+        assert np.isfinite(y).all()
+        qn = q.float().cpu().numpy()
+        kinds = plan["page_kind"]
+        kp_all, vp_all = cache.k_pages.cpu().numpy(), cache.v_pages.cpu().numpy()
+        grp = hq // hkv
+        for b in (0, 7, 15):
+            for g in (0, hkv - 1):
+                kb = k[b * L:(b + 1) * L, g].float().cpu().numpy()
+                vb = v[b * L:(b + 1) * L, g].float().cpu().numpy()
+                ref_rows = plan["refine"][b]
+                kq = O.kv_quantize(kb, ref_rows, tensor_amax=np.float32(amax_k))
+                vq = O.kv_quantize(vb, ref_rows, tensor_amax=np.float32(amax_v))
+                assert np.float32(kq["T"]) == np.float32(cache.scales[0].item())
+                # codes of a few tokens of this sequence and head, bit for bit
+                for t in (0, 1, L // 2 + 3, L - 1):
+                    s = int(plan["slots"][b][t])
+                    page, pos = s // PT, s % PT
+                    for which, pool, r in (("k", kp_all, kq), ("v", vp_all, vq)):
+                        codes, scales, d = read_section(pool[page, g], bool(kinds[page]), which)
+                        assert np.array_equal(codes[pos], r["q"][t])
+                        assert np.array_equal(scales[pos], r["scales"][t])
+                        if kinds[page]:
+                            assert np.array_equal(d[pos], r["d"][t])
+                kh = O.kv_decode(kq, level)[None]
+                vh = O.kv_decode(vq, level)[None]
+                ref = O.kv_attention(qn[b, g * grp:(g + 1) * grp], kh, vh, HD ** -0.5)
+                e = check_close(y[b, g * grp:(g + 1) * grp], ref, ("full", frac, b, g))
+                say(f"sequence {b}, KV head {g}: max rel err {e:.2e}")
+        del cache, k, v
+        torch.cuda.empty_cache()
