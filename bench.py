@@ -416,6 +416,48 @@ def gemv_70b(A, S, device, batch=64, pool_n=5):
     return out
 
 
+def kv_bench(A, S, device, batch=16, ctx=32768, h_q=32, h_kv=8, reps=20):
+    """Decode attention over an AutoFP KV cache: ``batch`` sequences of ``ctx``
+    tokens, h_q query / h_kv KV heads, head_dim 128, bf16 K/V/q. Two caches:
+    every page a base page (the 4-bit configuration, level 4) and every token
+    refined (level 6). Algorithmic bytes per launch: each cached token's codes
+    and E4M3 scales (72 B per KV head, K and V; + 64 B of offsets per refined
+    token at level 6), the page table, q (bf16) and the fp32 output."""
+    import numpy as np
+    import torch
+    out = {"workload": f"{batch} sequences x {ctx} tokens, {h_q} query / {h_kv} KV heads, head_dim 128, "
+                       "bf16 K/V/q; level 4 over base pages, level 6 over refined pages"}
+    hd = 128
+    for frac, level in ((0.0, 4), (1.0, 6)):
+        plan = S.kv_page_plan([ctx] * batch, frac, seed=41)
+        n = batch * ctx
+        cache = A.KVCache(plan["n_pages"], h_kv, batch, plan["max_pages"], device=device)
+        cache.page_kind.copy_(torch.from_numpy(plan["page_kind"]))
+        cache.page_tokens.copy_(torch.from_numpy(plan["page_tokens"]))
+        cache.page_table.copy_(torch.from_numpy(plan["page_table"]))
+        cache.seq_pages.copy_(torch.from_numpy(plan["seq_pages"]))
+        slots = torch.from_numpy(np.concatenate(plan["slots"])).to(device)
+        k = S.kv_tokens(n, h_kv, seed=42, tensor_id=1, device=device)
+        v = S.kv_tokens(n, h_kv, seed=42, tensor_id=2, device=device)
+        A.kv_write(cache, k, v, slots, set_scale=True)
+        del k, v, slots
+        q = S.kv_tokens(batch, h_q, seed=43, tensor_id=3, device=device)
+        y = torch.empty(batch, h_q, hd, dtype=torch.float32, device=device)
+        ws = torch.empty(A.workspace_bytes(6, batch * h_q, plan["max_pages"]), dtype=torch.uint8, device=device)
+        g = capture([lambda: A.kv_attention(q, cache, bits=level, out=y, workspace=ws)])
+        ms = time_graphs(g, reps, 3)
+        n_ref = int(sum(r.sum() for r in plan["refine"]))
+        tok_bytes = 2 * h_kv * (72 * n + (64 * n_ref if level == 6 else 0))
+        by = tok_bytes + 4 * batch * plan["max_pages"] + 2 * batch * h_q * hd + 4 * batch * h_q * hd
+        gbs = by / (ms * 1e-3) / 1e9
+        out[f"l{level}"] = {"us": round(ms * 1e3, 2), "bytes": int(by), "gbs": round(gbs, 1),
+                            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "refined_tokens": n_ref}
+        log(f"kv attention level {level}: {ms * 1e3:.1f} us, {by / 1e6:.1f} MB, {gbs:.1f} GB/s")
+        del cache, q, y, ws, g
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(batch, target_s=12.0):
     """The CPU oracle (fp64 NumPy, one BLAS thread) on a bounded sample of the
     same step: per level, encode each linear input and compute the layer
@@ -471,6 +513,8 @@ def main():
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-batches", action="store_true", help="skip the batch-16/64 and 70B-shape GEMV lines")
     ap.add_argument("--no-step32", action="store_true", help="skip the 32-layer policy-driven step")
+    ap.add_argument("--no-kv", action="store_true", help="skip the KV-cache decode attention line")
+    ap.add_argument("--kv-only", action="store_true", help="run only the KV-cache attention (no JSON line)")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run only the workload of the HBM-counter runs (no JSON line)")
     args = ap.parse_args()
@@ -491,6 +535,9 @@ def main():
     log(f"device: {torch.cuda.get_device_name(0)}")
     if args.pmc_pass:
         pmc_pass(A, S, device)
+        return
+    if args.kv_only:
+        log(json.dumps(kv_bench(A, S, device, reps=max(args.steps, 5))))
         return
     pool = build_pool(A, S, args.pool_layers, device)
     pool_bytes = sum(w_bytes(wp, 6) for layer in pool for wp in layer.values())
@@ -558,6 +605,9 @@ def main():
         del pool, bench
         torch.cuda.empty_cache()
         extra["step32"] = step32_bench(A, S, device)
+    if not args.no_kv:
+        torch.cuda.empty_cache()
+        extra["kv_attention"] = kv_bench(A, S, device)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.batch)

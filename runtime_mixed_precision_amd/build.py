@@ -25,6 +25,10 @@ ARCH = os.environ.get("AUTOFP_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 vector instructions are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source flags. kv.hip: MFMA accumulators in ordinary VGPRs, so the split
+# kernel's output tile is not held twice (accumulation registers + VGPRs) and
+# two wavefronts fit per SIMD.
+SOURCE_FLAGS = {"kv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument"]
 
@@ -38,7 +42,7 @@ def hipcc():
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")

@@ -179,10 +179,13 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_kernel(KvWriteArgs a) 
 
 // One page's loads for the lane (r = lane % 16, g = lane / 16). Slot 0 holds
 // tokens 0..31; slot 1 tokens 32..63 of a base page or the offsets of a
-// refinement page (level 6 only).
+// refinement page (level 6 only). Every page issues the same 14 loads: where
+// a refinement page has no slot 1 (level 4), or its slot 1 needs no scales of
+// its own, those loads repeat addresses of slot 0 (cache hits), so the number
+// of loads in flight is the same on every path and the waits stay exact.
 struct PageRegs {
   uint4 kc[2][2];     // [slot][b]: K codes of token tok(b, r), dims 32g .. 32g+31
-  uint32_t ks[2];     // [slot]: K scales of groups 2g, 2g+1 for b = 0 (low half), 1 (high half)
+  uint32_t ks[2][2];  // [slot][b]: the dword of token tok(b, r)'s K scales holding groups 2g, 2g+1
   uint4 vc[2][2];     // [slot][half]: V codes of tokens 8g .. 8g+7, dims 8r .. 8r+7
   uint2 vs[2];        // [slot]: V scales of group r/2, tokens 8g .. 8g+7
 };
@@ -192,11 +195,7 @@ struct PageRegs {
 __device__ __forceinline__ int qk_token(int b, int r) { return 8 * (r >> 2) + 4 * b + (r & 3); }
 
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint4 ldnt16(const uint8_t *p) {
-  const u32x4v v = __builtin_nontemporal_load((const u32x4v *)p);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 
 // Two E2M1 codes of byte m of w as fp16 (the byte selector must be a constant).
 __device__ __forceinline__ half2v fp4_byte(uint32_t w, int m) {
@@ -208,33 +207,65 @@ __device__ __forceinline__ half2v fp4_byte(uint32_t w, int m) {
   }
 }
 
-__device__ __forceinline__ void load_page(PageRegs &pr, const uint8_t *ks, const uint8_t *vs,
-                                          bool refinement, bool six, int r, int g) {
-  const int C = refinement ? kPageTok / 2 : kPageTok;
+// Per-lane byte offsets inside a page section, the same for every page.
+struct LaneOffsets {
+  uint32_t kc[2];     // K codes of token tok(b, r), dims 32g ..
+  uint32_t ks[2];     // K scale dword of token tok(b, r) holding groups 2g, 2g+1 (after 64 C)
+  uint32_t vc;        // V codes, block (t/8 = g, dim/8 = r)
+  uint32_t vs64, vs32;  // V scales of group r/2, tokens 8g.. (after 64 C), for C = 64 and 32
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(int r, int g) {
+  LaneOffsets o;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int t = qk_token(b, r);
-    pr.kc[0][b] = ldnt16(ks + t * 64 + 16 * g);
+    o.kc[b] = (uint32_t)(t * 64 + 16 * g);
+    o.ks[b] = (uint32_t)(8 * t + 4 * (g >> 1));
   }
-  pr.ks[0] = (uint32_t)*(const uint16_t *)(ks + 64 * C + 8 * qk_token(0, r) + 2 * g) |
-             ((uint32_t)*(const uint16_t *)(ks + 64 * C + 8 * qk_token(1, r) + 2 * g) << 16);
-  pr.vc[0][0] = ldnt16(vs + (g * 16 + r) * 32);
-  pr.vc[0][1] = ldnt16(vs + (g * 16 + r) * 32 + 16);
-  pr.vs[0] = *(const uint2 *)(vs + 64 * C + (r >> 1) * C + 8 * g);
-  if (!refinement) {
+  o.vc = (uint32_t)((g * 16 + r) * 32);
+  o.vs64 = (uint32_t)((r >> 1) * 64 + 8 * g);
+  o.vs32 = (uint32_t)((r >> 1) * 32 + 8 * g);
+  return o;
+}
+
+constexpr int kStream = 2;   // cache policy of the page loads: streamed, non-temporal
+
+// Loads of one page through buffer resources over its K and V sections: the
+// page base is wavefront-uniform (scalar registers), the lane part a fixed
+// 32-bit offset, and the page type only changes scalar offsets.
+__device__ __forceinline__ void load_page(PageRegs &pr, const uint8_t *ks, const uint8_t *vs,
+                                          bool refinement, bool six, const LaneOffsets &o) {
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(ks), (short)0, kSec,
+                                                                      0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(vs), (short)0, kSec,
+                                                                      0x00020000);
+  const int C = refinement ? kPageTok / 2 : kPageTok;
+  // slot 1: tokens 32..63 (base), offsets (refinement, level 6), or slot 0 again
+  const int code1 = refinement ? (six ? 72 * C : 0) : 32 * 64;
+  const int ksc1 = refinement ? 0 : 8 * 32;
+  const int vsc1 = refinement ? 0 : 32;
+  const uint32_t ovs = refinement ? o.vs32 : o.vs64;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) pr.kc[1][b] = ldnt16(ks + (32 + qk_token(b, r)) * 64 + 16 * g);
-    pr.ks[1] = (uint32_t)*(const uint16_t *)(ks + 64 * C + 8 * (32 + qk_token(0, r)) + 2 * g) |
-               ((uint32_t)*(const uint16_t *)(ks + 64 * C + 8 * (32 + qk_token(1, r)) + 2 * g) << 16);
-    pr.vc[1][0] = ldnt16(vs + ((4 + g) * 16 + r) * 32);
-    pr.vc[1][1] = ldnt16(vs + ((4 + g) * 16 + r) * 32 + 16);
-    pr.vs[1] = *(const uint2 *)(vs + 64 * C + (r >> 1) * C + 32 + 8 * g);
-  } else if (six) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b) pr.kc[1][b] = ldnt16(ks + 72 * C + qk_token(b, r) * 64 + 16 * g);
-    pr.vc[1][0] = ldnt16(vs + 72 * C + (g * 16 + r) * 32);
-    pr.vc[1][1] = ldnt16(vs + 72 * C + (g * 16 + r) * 32 + 16);
+  for (int b = 0; b < 2; ++b) {
+    u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)o.kc[b], 0, kStream);
+    pr.kc[0][b] = make_uint4(v[0], v[1], v[2], v[3]);
+    v = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)o.kc[b], code1, kStream);
+    pr.kc[1][b] = make_uint4(v[0], v[1], v[2], v[3]);
+    pr.ks[0][b] = __builtin_amdgcn_raw_buffer_load_b32(rk, (int)o.ks[b], 64 * C, kStream);
+    pr.ks[1][b] = __builtin_amdgcn_raw_buffer_load_b32(rk, (int)o.ks[b], 64 * C + ksc1, kStream);
   }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(o.vc + 16 * h), 0, kStream);
+    pr.vc[0][h] = make_uint4(v[0], v[1], v[2], v[3]);
+    v = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(o.vc + 16 * h), code1, kStream);
+    pr.vc[1][h] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  u32x2v w = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)ovs, 64 * C, kStream);
+  pr.vs[0] = make_uint2(w[0], w[1]);
+  w = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)ovs, 64 * C + vsc1, kStream);
+  pr.vs[1] = make_uint2(w[0], w[1]);
 }
 
 __device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
@@ -245,9 +276,13 @@ __device__ __forceinline__ uint32_t u4(const uint4 &v, int i) {
 }
 
 struct SoftState {
-  float m, l;
+  float m, l;         // reference maximum (base-2 score units) and sum of p of head r
   float4v O[8];       // O[n][i]: head r, dim 32g + 8i + n
 };
+
+// Largest step of a stale reference maximum: p = 2^(s - m) stays below 2^8,
+// so the fp16 parts of p and the fp32 sums keep their precision.
+constexpr float kRescaleSlack = 8.0f;
 
 // One 32-token slot: QK, online softmax, PV. `valid` = tokens of the slot that
 // hold data (1..32); ref = the slot's offsets are in slot 1 (level 6).
@@ -258,7 +293,7 @@ __device__ __forceinline__ void attend_slot(const PageRegs &pr, int slot, bool r
   float x[8];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    const uint32_t sb = (pr.ks[slot] >> (16 * b)) & 0xFFFFu;
+    const uint32_t sb = (pr.ks[slot][b] >> (16 * (g & 1))) & 0xFFFFu;
     const half2v sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
     float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -281,18 +316,24 @@ __device__ __forceinline__ void attend_slot(const PageRegs &pr, int slot, bool r
   for (int j = 1; j < 8; ++j) mb = fmaxf(mb, x[j]);
   mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
   mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-  const float mn = fmaxf(st.m, mb);
-  const float alpha = exp2f(st.m - mn);
+  // The reference maximum moves only when a score passes it by more than the
+  // slack (always on the first slot, where it is -inf); the result does not
+  // depend on it, and most slots then skip rescaling O.
+  if (__any(mb > st.m + kRescaleSlack)) {
+    const float mn = fmaxf(st.m, mb);
+    const float alpha = exp2f(st.m - mn);
+    st.l *= alpha;
+    st.m = mn;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st.O[n] *= alpha;
+  }
   float p[8], ps = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    p[j] = exp2f(x[j] - mn);
+    p[j] = exp2f(x[j] - st.m);
     ps += p[j];
   }
-  st.l = st.l * alpha + ps;
-  st.m = mn;
-#pragma unroll
-  for (int n = 0; n < 8; ++n) st.O[n] *= alpha;
+  st.l += ps;
   // p = P + Pl with both parts in fp16 (error ~2^-22 p), so the fp16 operand
   // rounding of the probabilities does not reach the output
   half8v P, Pl;
@@ -302,7 +343,9 @@ __device__ __forceinline__ void attend_slot(const PageRegs &pr, int slot, bool r
     Pl[j] = (_Float16)(p[j] - (float)P[j]);
   }
 
-  // --- V_hat^T operands: dim 8r + n, tokens 8g .. 8g+7
+  // --- V_hat^T operands: dim 8r + n, tokens 8g .. 8g+7; byte m of a token's
+  // code dword gives dims 8r + 2m, 8r + 2m + 1, and their two MFMAs (P and Pl
+  // parts) follow right away
   uint2 vsc = pr.vs[slot];
   const int nv = valid - 8 * g;   // tokens of this lane group that hold data
   if (nv < 8) {
@@ -315,35 +358,29 @@ __device__ __forceinline__ void attend_slot(const PageRegs &pr, int slot, bool r
   bp[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vsc.x, 1.0f, true);
   bp[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vsc.y, 1.0f, false);
   bp[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vsc.y, 1.0f, true);
-  uint32_t X[8], Y[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    X[j] = u4(pr.vc[slot][j >> 2], j & 3);
-    Y[j] = ref ? u4(pr.vc[1][j >> 2], j & 3) : 0u;
-  }
-  uint32_t A[8][4];   // [n][token pair]
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
+    uint32_t lo4[4], hi4[4];
 #pragma unroll
     for (int jp = 0; jp < 4; ++jp) {
-      half2v c0 = fp4_byte(X[2 * jp], m);
-      half2v c1 = fp4_byte(X[2 * jp + 1], m);
+      const uint32_t x0 = u4(pr.vc[slot][jp >> 1], 2 * (jp & 1));
+      const uint32_t x1 = u4(pr.vc[slot][jp >> 1], 2 * (jp & 1) + 1);
+      half2v c0 = fp4_byte(x0, m);
+      half2v c1 = fp4_byte(x1, m);
       if (ref) {
         const half2v q4 = half2v{(_Float16)0.25f, (_Float16)0.25f};
-        c0 += fp4_byte(Y[2 * jp], m) * q4;
-        c1 += fp4_byte(Y[2 * jp + 1], m) * q4;
+        c0 += fp4_byte(u4(pr.vc[1][jp >> 1], 2 * (jp & 1)), m) * q4;
+        c1 += fp4_byte(u4(pr.vc[1][jp >> 1], 2 * (jp & 1) + 1), m) * q4;
       }
-      const half2v lo = as_h2(__builtin_amdgcn_perm(as_u(c1), as_u(c0), 0x05040100u)) * bp[jp];
-      const half2v hi = as_h2(__builtin_amdgcn_perm(as_u(c1), as_u(c0), 0x07060302u)) * bp[jp];
-      A[2 * m][jp] = as_u(lo);
-      A[2 * m + 1][jp] = as_u(hi);
+      lo4[jp] = as_u(as_h2(__builtin_amdgcn_perm(as_u(c1), as_u(c0), 0x05040100u)) * bp[jp]);
+      hi4[jp] = as_u(as_h2(__builtin_amdgcn_perm(as_u(c1), as_u(c0), 0x07060302u)) * bp[jp]);
     }
-  }
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const half8v a8 = __builtin_bit_cast(half8v, make_uint4(A[n][0], A[n][1], A[n][2], A[n][3]));
-    st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, P, st.O[n], 0, 0, 0);
-    st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, Pl, st.O[n], 0, 0, 0);
+    const half8v alo = __builtin_bit_cast(half8v, make_uint4(lo4[0], lo4[1], lo4[2], lo4[3]));
+    const half8v ahi = __builtin_bit_cast(half8v, make_uint4(hi4[0], hi4[1], hi4[2], hi4[3]));
+    st.O[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, P, st.O[2 * m], 0, 0, 0);
+    st.O[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, Pl, st.O[2 * m], 0, 0, 0);
+    st.O[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, P, st.O[2 * m + 1], 0, 0, 0);
+    st.O[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, Pl, st.O[2 * m + 1], 0, 0, 0);
   }
 }
 
@@ -421,28 +458,32 @@ __global__ __launch_bounds__(64) void kv_attn_split_kernel(KvAttnArgs a) {
 
   const int64_t head_off = (int64_t)hk * kSec;
   const int64_t page_stride = (int64_t)a.h_kv * kSec;
+  // The loads of page i + 1 are issued before page i is processed; the copy
+  // into `cur` at the end of an iteration waits for them, by then in flight
+  // for a whole page. Past the last page the loads repeat it, and a dropped
+  // page (id -1) loads page 0: both are skipped when processed.
+  const LaneOffsets lo = lane_offsets(r, g);
   PageRegs cur, nxt;
   auto issue = [&](PageRegs &pr, int i) {
-    const int pg = __builtin_amdgcn_readlane(my_pg, i);
+    i = i < npp ? i : npp - 1;
+    int pg = __builtin_amdgcn_readlane(my_pg, i);
     const int kind = __builtin_amdgcn_readlane(my_kind, i);
-    if (pg < 0) return;
+    pg = pg < 0 ? 0 : pg;
     const uint8_t *kp = a.k_pages + pg * page_stride + head_off;
     const uint8_t *vp = a.v_pages + pg * page_stride + head_off;
-    load_page(pr, kp, vp, kind != 0, six, r, g);
+    load_page(pr, kp, vp, kind != 0, six, lo);
   };
   if (npp > 0) issue(cur, 0);
   for (int i = 0; i < npp; ++i) {
-    if (i + 1 < npp) issue(nxt, i + 1);
+    issue(nxt, i + 1);
     const int pg = __builtin_amdgcn_readlane(my_pg, i);
-    const int kind = __builtin_amdgcn_readlane(my_kind, i);
     if (pg >= 0) {
+      const int kind = __builtin_amdgcn_readlane(my_kind, i);
       const int valid = __builtin_amdgcn_readlane(my_fill, i);
-      if (kind) {
-        attend_slot(cur, 0, six, valid, qb, ql, qlo, cs, g, st);
-      } else {
-        attend_slot(cur, 0, false, valid, qb, ql, qlo, cs, g, st);
-        if (valid > 32) attend_slot(cur, 1, false, valid - 32, qb, ql, qlo, cs, g, st);
-      }
+      // slot 0: a refinement page's tokens (with their offsets at level 6) or
+      // a base page's first 32; slot 1: a base page's tokens 32 .. 63
+      attend_slot(cur, 0, kind != 0 && six, valid < 32 ? valid : 32, qb, ql, qlo, cs, g, st);
+      if (!kind && valid > 32) attend_slot(cur, 1, false, valid - 32, qb, ql, qlo, cs, g, st);
     }
     cur = nxt;
   }
@@ -464,27 +505,35 @@ __global__ __launch_bounds__(64) void kv_attn_split_kernel(KvAttnArgs a) {
   }
 }
 
-// Combine the splits of one (sequence, query head): one wavefront, two dims per lane.
+// Combine the splits of one (sequence, query head): one wavefront, two dims per
+// lane. Lane s holds split s's (m, l) and its weight 2^(m_s - M); the output
+// loop then issues the splits' O loads eight at a time (n_split <= 64).
 __global__ __launch_bounds__(64) void kv_attn_merge_kernel(const float *__restrict__ part, int n_split,
                                                            const float *__restrict__ v_scale,
                                                            float *__restrict__ out) {
   const int64_t row = blockIdx.x;
   const float *rec0 = part + row * n_split * kRec;
   const int lane = threadIdx.x;
-  float mloc = -INFINITY;
-  for (int s = lane; s < n_split; s += 64) mloc = fmaxf(mloc, rec0[s * kRec + kHd]);
-  const float M = wave_max(mloc);
-  float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < n_split; ++s) {
-      const float *rec = rec0 + s * kRec;
-      const float ms = rec[kHd];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - M);
-      L += rec[kHd + 1] * w;
-      const float2 o = *(const float2 *)(rec + 2 * lane);
-      o0 += o.x * w;
-      o1 += o.y * w;
+  const float ms = lane < n_split ? rec0[lane * kRec + kHd] : -INFINITY;
+  const float ls = lane < n_split ? rec0[lane * kRec + kHd + 1] : 0.0f;
+  const float M = wave_max(ms);
+  const float w = (M != -INFINITY && ms != -INFINITY) ? exp2f(ms - M) : 0.0f;
+  float L = ls * w;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) L += __shfl_xor(L, d, 64);
+  float o0 = 0.0f, o1 = 0.0f;
+  for (int s0 = 0; s0 < n_split; s0 += 8) {
+    float2 o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sj = s0 + j < n_split ? s0 + j : n_split - 1;
+      o[j] = *(const float2 *)(rec0 + sj * kRec + 2 * lane);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float wj = __shfl(w, s0 + j, 64);   // 0 past n_split (lanes >= n_split hold w = 0)
+      o0 += o[j].x * wj;
+      o1 += o[j].y * wj;
     }
   }
   const float f = L > 0.0f ? *v_scale / L : 0.0f;
