@@ -327,7 +327,7 @@ autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_
     const hipError_t e = launch_act_dequant(a, s);
     if (e != hipSuccess) return AUTOFP_ERR_HIP;
   }
-  if (x->rows > 16 && gemm_small_m_ok(a) && w->rows >= 8192 && w->mask && (bits_dev || bits == 6)) {
+  if (gemv_small_m_route(a) && w->mask && (bits_dev || bits == 6)) {
     const hipError_t e = launch_mask_prefix(w->mask, mask_bytes(w->k), a.prefix, s);
     if (e != hipSuccess) return AUTOFP_ERR_HIP;
   }

@@ -232,8 +232,15 @@ __device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * 128
 // NW wavefronts (8 or 16: two or four per SIMD, so one wavefront's decode
 // and waits overlap the others' MFMAs) in a WGM x NW/WGM grid over the
 // BM x BN tile (WGM = 4 for 16 wavefronts on 256 tokens, else 2).
-template <int BM, int BN, int NW>
-__global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
+//
+// KG > 1 (batched decode): KG groups of NW wavefronts share the block's tile,
+// each group running the K loop over its own quarter (half, ...) of K with its
+// own two LDS stages, so KG times as many loads are in flight per tile while
+// every weight and activation byte is still read once; a step past a group's
+// range (or past K) loads zeros. At the end the groups' accumulators are
+// summed through LDS in group order (deterministic) by group 0.
+template <int BM, int BN, int NW, int KG = 1>
+__global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
   constexpr int WGM = (NW >= 16 && BM >= 256) ? 4 : 2;   // wavefronts along M
   constexpr int WGN = NW / WGM;                         // wavefronts along N
   constexpr int WM = BM / WGM;        // tokens per wavefront
@@ -250,11 +257,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
   static_assert(WITEMS == 64 * NW * HPT || (HPT == 1 && WITEMS < 64 * NW), "weight items per thread");
   extern __shared__ __align__(16) unsigned char lds[];
 
-  const int tid = threadIdx.x;
+  const int kg = KG > 1 ? (int)(threadIdx.x / (64 * NW)) : 0;   // K group
+  const int tid = KG > 1 ? (int)(threadIdx.x % (64 * NW)) : (int)threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int64_t K = a.k;
+  unsigned char *glds = lds + kg * 2 * STAGE;   // this group's two stages
   const int64_t mtiles = (a.b + BM - 1) / BM;
   const int64_t mt = blockIdx.x % mtiles;
   const int64_t nt = blockIdx.x / mtiles;
@@ -275,13 +284,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
   // + 7; lane i -> row + i / 8, LDS chunk i % 8 (global chunk (i % 8) ^ ((row / 2) % 8))
   const uint32_t arow_l = (uint32_t)(lane >> 3);
   auto issue_a = [&](int64_t k0, int stage) {
-    unsigned char *base = lds + stage * STAGE;
+    unsigned char *base = glds + stage * STAGE;
 #pragma unroll
     for (int d = 0; d < APW; ++d) {
       const uint32_t r = (uint32_t)(8 * (APW * wave + d)) + arow_l;   // tile row 0..255
       const uint32_t cg = (uint32_t)(lane & 7) ^ ((r >> 1) & 7u);
       const int64_t tok = m0 + r;
-      const uint32_t off = tok < a.b ? (uint32_t)((tok * a.kpad + k0 + 8 * cg) * 2) : 0x80000000u;
+      const uint32_t off = (tok < a.b && k0 < K) ? (uint32_t)((tok * a.kpad + k0 + 8 * cg) * 2) : 0x80000000u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, AFP_LDS(base + 8 * (APW * wave + d) * 128), 16, (int)off, 0, 0, 0);
     }
   };
@@ -297,22 +306,27 @@ __global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
     int32_t pos[HPT];
     uint32_t mb[HPT];
   };
+  // a step past K (a K group's tail) loads zeros: out-of-range buffer offsets,
+  // and no refined subgroups
   auto load_w = [&](int64_t k0, WRegs &w) {
+    const bool kin = k0 < K;
 #pragma unroll
     for (int i = 0; i < HPT; ++i) {
       const int64_t ke = k0 + 32 * (h0 + i);
-      w.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(wr * (K >> 1) + (ke >> 1)), 0, 0);
+      w.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, kin ? (int)(wr * (K >> 1) + (ke >> 1)) : (int)0x80000000u,
+                                                     0, 0);
     }
     if (HPT == 2) {
-      w.s = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(wr * (K >> 4) + (k0 >> 4)), 0, 0);
+      w.s = __builtin_amdgcn_raw_buffer_load_b32(rs, kin ? (int)(wr * (K >> 4) + (k0 >> 4)) : (int)0x80000000u, 0, 0);
     } else {
-      w.s = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(wr * (K >> 4) + ((k0 + 32 * h0) >> 4)), 0, 0);
+      w.s = __builtin_amdgcn_raw_buffer_load_b16(
+          rs, kin ? (int)(wr * (K >> 4) + ((k0 + 32 * h0) >> 4)) : (int)0x80000000u, 0, 0);
     }
     if (refine_w) {
 #pragma unroll
       for (int i = 0; i < HPT; ++i) {
-        const int64_t mi = (k0 >> 5) + h0 + i;   // mask byte (32 elements)
-        w.mb[i] = a.w_mask[mi];
+        const int64_t mi = kin ? (k0 >> 5) + h0 + i : 0;   // mask byte (32 elements)
+        w.mb[i] = kin ? a.w_mask[mi] : 0u;
         w.pos[i] = a.prefix[mi];
         const uint32_t al = (uint32_t)((wr * R + w.pos[i]) & ~(int64_t)3);
         w.o[i] = __builtin_amdgcn_raw_buffer_load_b96(ro, (int)al, 0, 0);
@@ -320,7 +334,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
     }
   };
   auto store_w = [&](const WRegs &w, int stage) {
-    unsigned char *base = lds + stage * STAGE + A_BYTES;
+    unsigned char *base = glds + stage * STAGE + A_BYTES;
 #pragma unroll
     for (int i = 0; i < HPT; ++i) {
       uint32_t w4[4] = {w.c[i][0], w.c[i][1], w.c[i][2], w.c[i][3]};
@@ -373,11 +387,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int64_t nkt = K / kBK2;
+  // K steps of this group: [kb, kb + nkt) (the same count in every group)
+  const int64_t nkt = (K / kBK2 + KG - 1) / KG;
+  const int64_t kb = nkt * kg;
   WRegs wreg;
-  issue_a(0, 0);
+  issue_a(kb * kBK2, 0);
   if (w_thread) {
-    load_w(0, wreg);
+    load_w(kb * kBK2, wreg);
     store_w(wreg, 0);
   }
   __builtin_amdgcn_s_waitcnt(0);   // every load of step 0 (the activation copy included) has landed
@@ -386,10 +402,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
     const int st = (int)(kt & 1);
     const bool more = kt + 1 < nkt;
     if (more) {
-      issue_a((kt + 1) * kBK2, st ^ 1);
-      if (w_thread) load_w((kt + 1) * kBK2, wreg);
+      issue_a((kb + kt + 1) * kBK2, st ^ 1);
+      if (w_thread) load_w((kb + kt + 1) * kBK2, wreg);
     }
-    const unsigned char *As = lds + st * STAGE;
+    const unsigned char *As = glds + st * STAGE;
     const unsigned char *Wsb = As + A_BYTES;
 #pragma unroll
     for (int kk = 0; kk < kBK2 / 16; ++kk) {
@@ -409,6 +425,33 @@ __global__ __launch_bounds__(64 * NW) void gemm_lds_kernel(LinearArgs a) {
     if (more && w_thread) store_w(wreg, st ^ 1);
     __builtin_amdgcn_s_waitcnt(0);   // the next step's activation copy has landed
     __syncthreads();
+  }
+
+  if (KG > 1) {
+    // groups 1 .. KG-1 leave their accumulators in LDS (lane-minor), group 0
+    // adds them in group order
+    float *red = (float *)lds;
+    constexpr int PER = TI * TJ * 16;   // accumulator floats per lane
+    if (kg > 0) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            red[(((kg - 1) * NW + wave) * PER + (i * TJ + j) * 16 + v) * 64 + lane] = acc[i][j][v];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int g = 1; g < KG; ++g)
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            acc[i][j][v] += red[(((g - 1) * NW + wave) * PER + (i * TJ + j) * 16 + v) * 64 + lane];
   }
 
   float scale = (*a.w_T) * (*a.x_T);
@@ -455,10 +498,16 @@ hipError_t launch_gemm_small_m(const LinearArgs &a, hipStream_t s) {
     const size_t lds = 2 * (size_t)(64 * kBK2 * 2 + 128 * kBK2 * 2);
     hipLaunchKernelGGL((gemm_lds_kernel<64, 128, kDecodeWaves>), dim3((unsigned)(mtiles * ((a.n + 127) / 128))),
                        dim3(64 * kDecodeWaves), lds, s, a);
+  } else if (mtiles * ((a.n + 63) / 64) >= 256) {
+    // two wavefront groups over K (28672 x 8192 at 64 tokens: 126 -> 102 us;
+    // four groups: 118 us)
+    const size_t lds = 2 * 2 * (size_t)(64 * kBK2 * 2 + 64 * kBK2 * 2);
+    hipLaunchKernelGGL((gemm_lds_kernel<64, 64, 4, 2>), dim3((unsigned)(mtiles * ((a.n + 63) / 64))),
+                       dim3(64 * 4 * 2), lds, s, a);
   } else {
-    const size_t lds = 2 * (size_t)(64 * kBK2 * 2 + 64 * kBK2 * 2);
-    hipLaunchKernelGGL((gemm_lds_kernel<64, 64, 4>), dim3((unsigned)(mtiles * ((a.n + 63) / 64))), dim3(64 * 4),
-                       lds, s, a);
+    const size_t lds = 4 * 2 * (size_t)(64 * kBK2 * 2 + 64 * kBK2 * 2);
+    hipLaunchKernelGGL((gemm_lds_kernel<64, 64, 4, 4>), dim3((unsigned)(mtiles * ((a.n + 63) / 64))),
+                       dim3(64 * 4 * 4), lds, s, a);
   }
   return hipGetLastError();
 }

@@ -1338,6 +1338,15 @@ Fp4Cfg fp4_cfg(const LinearArgs &a, bool six, int bt) {
 
 int64_t xh_kpad(int64_t k) { return round_up(k, kCh); }
 
+// 17-64 tokens with K % 64 == 0 on weights of 8192+ rows run the 64-token
+// GEMM tile (enough row tiles to fill the chip); narrower weights the panel
+// kernel. On the tile with four wavefront groups over K, 64 tokens took
+// Wqkv 6144 x 4096 29.9 us (panel 44.2) but Wo 29.6 (26.1), Wdown
+// 4096 x 14336 83.7 (72.1), and level 6 up to 1.6x the panel's time.
+bool gemv_small_m_route(const LinearArgs &a) {
+  return a.b > 16 && gemm_small_m_ok(a) && a.n >= 8192;
+}
+
 bool gemv_needs_panel(const LinearArgs &a) {
   if (a.b > 16) return true;
   return !stream_cfg(a).xlds;
@@ -1403,7 +1412,7 @@ hipError_t launch_gemv(const LinearArgs &a0, hipStream_t s) {
   // more than 16 tokens: for wide weights (enough 256-row tiles to fill the
   // chip) the 64-token GEMM tile, where every decoded weight tile serves all
   // tokens from LDS; otherwise slices of at most 64 tokens
-  if (gemm_small_m_ok(a0) && a0.n >= 8192) return launch_gemm_small_m(a0, s);
+  if (gemv_small_m_route(a0)) return launch_gemm_small_m(a0, s);
   for (int64_t t0 = 0; t0 < a0.b; t0 += 64) {
     LinearArgs a = a0;
     a.b = (a0.b - t0) < 64 ? (a0.b - t0) : 64;

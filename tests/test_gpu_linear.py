@@ -266,6 +266,22 @@ def test_gemv_many_tiles(n, b, k, waves):
         check_close(y.cpu().numpy(), O.linear(wq, xq6 if level == 6 else xq4, level))
 
 
+@pytest.mark.parametrize("n,b,k", [(8200, 64, 448), (8256, 17, 64 * 9), (12300, 40, 64 * 5), (8192, 33, 64),
+                                   (16448, 20, 64 * 3)])
+def test_gemv_batched_k_groups(n, b, k):
+    """17-64 tokens on weights of 8192+ rows: the 64-token tile whose wavefront
+    groups each take a share of the K steps (four groups below 256 row tiles,
+    two from 256: 16448 rows), with step counts that do not divide evenly, a
+    single step and ragged row tiles, against the oracle at every level."""
+    say(f"case: batched gemv K groups N={n} B={b} K={k}")
+    w, x = operands(n, b, k, seed=n + b + k)
+    wp, xp4, xp6 = gpu_pack(w, x)
+    wq, xq4, xq6 = oracle_pack(w, x)
+    for level in (2, 4, 6):
+        y = run(A.gemv, wp, xp4, xp6, level)
+        check_close(y.cpu().numpy(), O.linear(wq, xq6 if level == 6 else xq4, level))
+
+
 @pytest.mark.parametrize("waves", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("n,b,k", [(40, 1, 4096 + 256), (33, 3, 2304 + 64), (16, 16, 1040)])
 def test_gemv_forced_waves(waves, n, b, k):
