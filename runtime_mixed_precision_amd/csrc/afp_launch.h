@@ -88,6 +88,7 @@ int64_t xh_kpad(int64_t k);
 hipError_t launch_act_dequant(const LinearArgs &a, hipStream_t s);
 bool gemv_needs_panel(const LinearArgs &a);   // true when the GEMV reads the fp16 activation panel
 bool gemv_small_m_route(const LinearArgs &a);   // 17-64 tokens on the 64-token GEMM tile
+bool gemv_panel_packed(const LinearArgs &a);    // 17+ tokens: panel kernel on packed activations
 hipError_t launch_gemv(const LinearArgs &a, hipStream_t s);
 
 // ---- gemm.hip ----

@@ -1121,7 +1121,11 @@ __device__ __forceinline__ int32_t w_prefix(const LinearArgs &a, int64_t c0) {
   return pre;
 }
 
-template <int TT, int U>
+// XP: the activations are read packed (E2M1 codes, E4M3 scales and, at level
+// 6, offset bytes: 0.5625 to 0.8125 B per element instead of the 2 B of the
+// fp16 panel) and decoded in registers; K % 32 == 0. Every block reads all
+// tokens' activations, so their bytes, not the weights', bound the launch.
+template <int TT, int U, bool XP>
 __global__ __launch_bounds__(256) void gemv_panel_kernel(LinearArgs a) {
   __shared__ float4v red[4][TT][64];
   const int lane = threadIdx.x & 63;
@@ -1147,6 +1151,7 @@ __global__ __launch_bounds__(256) void gemv_panel_kernel(LinearArgs a) {
   const int64_t c0 = wave * per;
   const int64_t c1 = (c0 + per < nch) ? c0 + per : nch;
   int32_t pre = (refine_w && c0 < c1) ? w_prefix(a, c0) : 0;
+  const bool refine_x = XP && L == 6 && a.x_offsets != nullptr;
 
   float4v acc[TT];
 #pragma unroll
@@ -1155,7 +1160,10 @@ __global__ __launch_bounds__(256) void gemv_panel_kernel(LinearArgs a) {
   for (int64_t cb = c0; cb < c1; cb += U) {
     uint4 cw[U];
     uint32_t sw[U];
-    half8v xv[U][TT][4];
+    half8v xv[XP ? 1 : U][TT][4];
+    uint4 xc[XP ? U : 1][TT];      // XP: 32 codes, their 2 scales and 8 offset bytes
+    uint32_t xs[XP ? U : 1][TT];
+    uint2 xo[XP ? U : 1][TT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t c = cb + u;
@@ -1164,10 +1172,18 @@ __global__ __launch_bounds__(256) void gemv_panel_kernel(LinearArgs a) {
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
         const int64_t tok = 16 * t + r;
-        const bool tok_ok = (c < c1) && tok < a.b;
-        const half8v *src = (const half8v *)(a.xh + (tok_ok ? tok : 0) * a.kpad + (c < c1 ? ke : 0));
+        if (XP) {
+          const bool ok = (c < c1) && tok < a.b && ke < K;
+          const int64_t tk = ok ? tok : 0, kk = ok ? ke : 0;
+          xc[u][t] = ok ? *(const uint4 *)(a.x_codes + tk * (K >> 1) + (kk >> 1)) : make_uint4(0, 0, 0, 0);
+          xs[u][t] = ok ? (uint32_t)*(const uint16_t *)(a.x_scales + tk * (K >> 4) + (kk >> 4)) : 0u;
+          xo[u][t] = (ok && refine_x) ? *(const uint2 *)(a.x_offsets + tk * (K >> 2) + (kk >> 2)) : make_uint2(0, 0);
+        } else {
+          const bool tok_ok = (c < c1) && tok < a.b;
+          const half8v *src = (const half8v *)(a.xh + (tok_ok ? tok : 0) * a.kpad + (c < c1 ? ke : 0));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xv[u][t][i] = tok_ok ? src[i] : half8v{0, 0, 0, 0, 0, 0, 0, 0};
+          for (int i = 0; i < 4; ++i) xv[u][t][i] = tok_ok ? src[i] : half8v{0, 0, 0, 0, 0, 0, 0, 0};
+        }
       }
     }
 #pragma unroll
@@ -1179,8 +1195,17 @@ __global__ __launch_bounds__(256) void gemv_panel_kernel(LinearArgs a) {
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(h[i], xv[u][t][i], acc[t], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          half8v xi;
+          if (XP) {
+            const uint32_t cwi = i == 0 ? xc[u][t].x : i == 1 ? xc[u][t].y : i == 2 ? xc[u][t].z : xc[u][t].w;
+            const uint32_t obi = (i < 2 ? xo[u][t].x : xo[u][t].y) >> (16 * (i & 1));
+            xi = __builtin_bit_cast(half8v, act_decode8_vals(cwi, xs[u][t] >> (8 * (i >> 1)), obi, refine_x));
+          } else {
+            xi = xv[u][t][i];
+          }
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(h[i], xi, acc[t], 0, 0, 0);
+        }
       }
     }
   }
@@ -1347,8 +1372,17 @@ bool gemv_small_m_route(const LinearArgs &a) {
   return a.b > 16 && gemm_small_m_ok(a) && a.n >= 8192;
 }
 
+// 17+ tokens off the GEMM tile with K % 32 == 0 at a host-side level 2 or 4:
+// the panel kernel reads the packed activations (no fp16 panel). 64 tokens:
+// Wqkv 43.9 -> 29.5 us, Wo 26.0 -> 22.2, Wdown 71.1 -> 66.1 at level 4; at
+// level 6 the offset decode made it slower (Wdown 101 -> 121 us), so level 6
+// and a device-side level keep the fp16 panel.
+bool gemv_panel_packed(const LinearArgs &a) {
+  return a.b > 16 && !gemv_small_m_route(a) && (a.k & 31) == 0 && a.bits_dev == nullptr && a.bits != 6;
+}
+
 bool gemv_needs_panel(const LinearArgs &a) {
-  if (a.b > 16) return true;
+  if (a.b > 16) return !gemv_panel_packed(a);
   return !stream_cfg(a).xlds;
 }
 
@@ -1422,13 +1456,18 @@ hipError_t launch_gemv(const LinearArgs &a0, hipStream_t s) {
     a.x_offsets = a0.x_offsets ? a0.x_offsets + t0 * (a0.k / 4) : nullptr;
     a.y = (char *)a0.y + t0 * a0.n * (a0.y_dtype == AUTOFP_BF16 ? 2 : 4);
     const dim3 grid((unsigned)((a.n + 15) / 16));
+    const bool xp = gemv_panel_packed(a0);
+#define AFP_PANEL(TT, U)                                                                      \
+    if (xp) hipLaunchKernelGGL((gemv_panel_kernel<TT, U, true>), grid, dim3(256), 0, s, a); \
+    else hipLaunchKernelGGL((gemv_panel_kernel<TT, U, false>), grid, dim3(256), 0, s, a)
     if (a.b <= 16) {
-      hipLaunchKernelGGL((gemv_panel_kernel<1, 4>), grid, dim3(256), 0, s, a);
+      AFP_PANEL(1, 4);
     } else if (a.b <= 32) {
-      hipLaunchKernelGGL((gemv_panel_kernel<2, 4>), grid, dim3(256), 0, s, a);
+      AFP_PANEL(2, 4);
     } else {
-      hipLaunchKernelGGL((gemv_panel_kernel<4, 2>), grid, dim3(256), 0, s, a);
+      AFP_PANEL(4, 2);
     }
+#undef AFP_PANEL
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -80,7 +80,7 @@ def test_config1_layer(level, op):
 
 SHAPES = [  # (N, B, K)
     (200, 1, 272), (200, 3, 4096 + 16), (64, 8, 512), (48, 16, 256), (130, 17, 384),
-    (96, 33, 1024), (40, 64, 128), (72, 100, 160), (16, 5, 16),
+    (96, 33, 1024), (40, 64, 128), (72, 100, 160), (16, 5, 16), (50, 20, 272),
 ]
 
 
