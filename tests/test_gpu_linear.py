@@ -146,7 +146,7 @@ def test_gemv_equals_gemm():
 
 
 @pytest.mark.parametrize("name,b", [("wgate", 1), ("wgate", 8), ("wdown", 8), ("wqkv", 1), ("wqkv", 8), ("wqkv", 16),
-                                    ("wdown", 64)])
+                                    ("wdown", 64), ("wqkv", 64), ("wgate", 64)])
 def test_full_size_decode_sampled(name, b):
     """Llama-3-8B-shaped layer at full size: every output of sampled weight
     rows checked against the oracle at levels 2 and 4 (and 6 on Wqkv)."""
