@@ -15,7 +15,9 @@ HIP graph and replayed.
 
 Printed (stdout, one JSON line): whole-step algorithmic HBM GB/s, the GEMV
 roofline (bytes / launch duration, HIP events around back-to-back GEMV-only
-graphs), the prefill GEMM TFLOP/s, and the CPU oracle on a bounded sample.
+graphs), the prefill GEMM TFLOP/s, batched-decode and 32-layer-step lines,
+decode attention over an AutoFP KV cache (16 x 32768 tokens, GQA 32/8), and
+the CPU oracle on a bounded sample.
 """
 
 from __future__ import annotations
