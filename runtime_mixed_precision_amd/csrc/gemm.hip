@@ -218,6 +218,7 @@ constexpr int kBM2 = 256;
 constexpr int kGemmWaves = 16;  // wavefronts per prefill block (four per SIMD, 128 VGPRs each)
 constexpr int kDecodeWaves = 8; // wavefronts per 64-token block
 constexpr int kBK2 = 64;
+constexpr size_t kTabBytes = 2 * 256 * 8;   // level-6 decode tables of gemm_lds_kernel
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
@@ -271,6 +272,27 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
   const int L = run_level(a);
   const bool refine_w = (L == 6) && a.w_mask != nullptr && a.w_offsets != nullptr && a.n_refined > 0;
   const int64_t R = a.n_refined;
+
+  // level 6: per-block tables after the stages. dtab[byte] = the four fp16
+  // offsets d/8 of an offset byte; stab[mask byte] = the byte selectors that
+  // spread a row's compacted offset bytes over the 8 subgroups of 32
+  // elements (0x0C: no offset). A lookup replaces a few dozen bit operations
+  // per 32 decoded weights.
+  uint2 *dtab = (uint2 *)(lds + KG * 2 * STAGE);
+  uint2 *stab = dtab + 256;
+  if (refine_w) {
+    for (int i = (int)threadIdx.x; i < 256; i += (int)blockDim.x) {
+      dtab[i] = delta_words((uint32_t)i);
+      uint32_t sel[2] = {0, 0}, j = 0;
+      for (int sg = 0; sg < 8; ++sg) {
+        const uint32_t on = ((uint32_t)i >> sg) & 1u;
+        sel[sg >> 2] |= (on ? j : 0x0Cu) << (8 * (sg & 3));
+        j += on;
+      }
+      stab[i] = make_uint2(sel[0], sel[1]);
+    }
+    __syncthreads();
+  }
 
   // activation panel [b][kpad] fp16: rows past b read as zero
   const __amdgpu_buffer_rsrc_t rx = rsrc(a.xh, a.b * a.kpad * 2);
@@ -352,18 +374,12 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
         const uint32_t sh = (uint32_t)((wr * R + w.pos[i]) & 3);
         const uint32_t lo = __builtin_amdgcn_alignbyte(w.o[i][1], w.o[i][0], sh);
         const uint32_t hi = __builtin_amdgcn_alignbyte(w.o[i][2], w.o[i][1], sh);
-        uint32_t sel[2] = {0, 0}, j = 0;
-#pragma unroll
-        for (int sg = 0; sg < 8; ++sg) {
-          const uint32_t on = (m >> sg) & 1u;
-          sel[sg >> 2] |= (on ? j : 0x0Cu) << (8 * (sg & 3));
-          j += on;
-        }
-        const uint32_t E[2] = {__builtin_amdgcn_perm(hi, lo, sel[0]), __builtin_amdgcn_perm(hi, lo, sel[1])};
+        const uint2 sel = stab[m & 0xFFu];
+        const uint32_t E[2] = {__builtin_amdgcn_perm(hi, lo, sel.x), __builtin_amdgcn_perm(hi, lo, sel.y)};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const uint2 de = delta_words((E[p >> 1] >> (16 * (p & 1))) & 0xFFu);
-          const uint2 dd = delta_words((E[p >> 1] >> (16 * (p & 1) + 8)) & 0xFFu);
+          const uint2 de = dtab[(E[p >> 1] >> (16 * (p & 1))) & 0xFFu];
+          const uint2 dd = dtab[(E[p >> 1] >> (16 * (p & 1) + 8)) & 0xFFu];
           h[p] += __builtin_bit_cast(half8v, make_uint4(de.x, de.y, dd.x, dd.y));
         }
       }
@@ -489,23 +505,23 @@ bool gemm_small_m_ok(const LinearArgs &a) { return a.k % kBK2 == 0; }
 hipError_t launch_gemm_small_m(const LinearArgs &a, hipStream_t s) {
   const int64_t mtiles = (a.b + 63) / 64;
   if (mtiles * ((a.n + 255) / 256) >= 256) {
-    const size_t lds = 2 * (size_t)(64 * kBK2 * 2 + 256 * kBK2 * 2);
+    const size_t lds = 2 * (size_t)(64 * kBK2 * 2 + 256 * kBK2 * 2) + kTabBytes;
     hipLaunchKernelGGL((gemm_lds_kernel<64, 256, kDecodeWaves>), dim3((unsigned)(mtiles * ((a.n + 255) / 256))),
                        dim3(64 * kDecodeWaves), lds, s, a);
   } else if (mtiles * ((a.n + 127) / 128) >= 256) {
     // narrower tiles when 256-row tiles leave CUs idle (28672 x 8192 at 64
     // tokens: 161 us at 256 rows, 122 at 128, 114 at 64)
-    const size_t lds = 2 * (size_t)(64 * kBK2 * 2 + 128 * kBK2 * 2);
+    const size_t lds = 2 * (size_t)(64 * kBK2 * 2 + 128 * kBK2 * 2) + kTabBytes;
     hipLaunchKernelGGL((gemm_lds_kernel<64, 128, kDecodeWaves>), dim3((unsigned)(mtiles * ((a.n + 127) / 128))),
                        dim3(64 * kDecodeWaves), lds, s, a);
   } else if (mtiles * ((a.n + 63) / 64) >= 256) {
     // two wavefront groups over K (28672 x 8192 at 64 tokens: 126 -> 102 us;
     // four groups: 118 us)
-    const size_t lds = 2 * 2 * (size_t)(64 * kBK2 * 2 + 64 * kBK2 * 2);
+    const size_t lds = 2 * 2 * (size_t)(64 * kBK2 * 2 + 64 * kBK2 * 2) + kTabBytes;
     hipLaunchKernelGGL((gemm_lds_kernel<64, 64, 4, 2>), dim3((unsigned)(mtiles * ((a.n + 63) / 64))),
                        dim3(64 * 4 * 2), lds, s, a);
   } else {
-    const size_t lds = 4 * 2 * (size_t)(64 * kBK2 * 2 + 64 * kBK2 * 2);
+    const size_t lds = 4 * 2 * (size_t)(64 * kBK2 * 2 + 64 * kBK2 * 2) + kTabBytes;
     hipLaunchKernelGGL((gemm_lds_kernel<64, 64, 4, 4>), dim3((unsigned)(mtiles * ((a.n + 63) / 64))),
                        dim3(64 * 4 * 4), lds, s, a);
   }
@@ -518,11 +534,11 @@ hipError_t launch_gemm(const LinearArgs &a, hipStream_t s) {
     const int64_t mtiles = (a.b + kBM2 - 1) / kBM2;
     const int64_t big = mtiles * ((a.n + 255) / 256);
     if (big >= 256) {
-      const size_t lds = 2 * (size_t)(kBM2 * kBK2 * 2 + 256 * kBK2 * 2);
+      const size_t lds = 2 * (size_t)(kBM2 * kBK2 * 2 + 256 * kBK2 * 2) + kTabBytes;
       hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 256, kGemmWaves>), dim3((unsigned)big), dim3(64 * kGemmWaves), lds, s,
                          a);
     } else {
-      const size_t lds = 2 * (size_t)(kBM2 * kBK2 * 2 + 128 * kBK2 * 2);
+      const size_t lds = 2 * (size_t)(kBM2 * kBK2 * 2 + 128 * kBK2 * 2) + kTabBytes;
       hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 128, kGemmWaves>), dim3((unsigned)(mtiles * ((a.n + 127) / 128))),
                          dim3(64 * kGemmWaves), lds, s, a);
     }
