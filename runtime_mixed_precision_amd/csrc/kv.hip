@@ -337,7 +337,9 @@ __device__ __forceinline__ void qk_slot(const PageRegs &pr, int slot, int valid,
   }
 }
 
-// Online softmax over N scores of head r (N / 8 slots): moves the reference
+// Online softmax over N scores of head r (N / 8 slots), with the hardware
+// base-2 exponential (results below 2^-126, which add nothing next to the
+// reference maximum's 1, flush to zero): moves the reference
 // maximum only when a score passes it by more than the slack (always on the
 // first page, where it is -inf; the result does not depend on it), then
 // p = 2^(x - m) as P + Pl, both fp16 (error ~2^-22 p), so the fp16 operand
@@ -351,7 +353,7 @@ __device__ __forceinline__ void softmax_update(const float *x, SoftState &st, ha
   mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
   if (__any(mb > st.m + kRescaleSlack)) {
     const float mn = fmaxf(st.m, mb);
-    const float alpha = exp2f(st.m - mn);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
     st.l *= alpha;
     st.m = mn;
 #pragma unroll
@@ -360,7 +362,7 @@ __device__ __forceinline__ void softmax_update(const float *x, SoftState &st, ha
   float ps = 0.0f;
 #pragma unroll
   for (int j = 0; j < N; ++j) {
-    const float p = exp2f(x[j] - st.m);
+    const float p = __builtin_amdgcn_exp2f(x[j] - st.m);
     ps += p;
     const _Float16 h = (_Float16)p;
     P[j / 8][j % 8] = h;
