@@ -292,8 +292,8 @@ autofp_status autofp_policy_update(int32_t phase, int32_t layer, int32_t new_seq
  *   K: codes   [C][64]  at 0          token-major, dims in order
  *      scales  [C][8]   at 64*C       E4M3, group j of token t at 8*t + j
  *      offsets [C][64]  at 72*C       (refinement pages) E2M1 codes of d/2, like codes
- *   V: codes   [C/8][16][8][4] at 0   block (t/8, dim/8), then t%8: one dword per
- *                                     token holds dims 8*(dim/8) .. +7
+ *   V: codes   [C/8][16][8][4] at 0   block (t/8, dim/8), then dim%8: one dword per
+ *                                     dim holds tokens 8*(t/8) .. +7, token t in nibble t%8
  *      scales  [8][C]   at 64*C       group-major: group j of token t at C*j + t
  *      offsets (refinement pages) at 72*C, laid out like the V codes
  * A refinement section uses 4352 of its 4608 bytes; the tail is never read.

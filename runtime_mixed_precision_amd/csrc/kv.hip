@@ -41,7 +41,8 @@ constexpr int kMaxSplits = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
-// Page write: one thread per (token, KV head, 16-element group), K and V.
+// Page write: one thread per (8 consecutive tokens of the call, KV head,
+// 16-element group), K and V.
 // ---------------------------------------------------------------------------
 
 struct Enc16 {
@@ -133,43 +134,96 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_kernel(KvWriteArgs a) 
     Tk = *a.k_scale;
     Tv = *a.v_scale;
   }
+  // thread: 8 consecutive tokens of the call, one KV head, one 16-dim group
   const int64_t idx = (int64_t)blockIdx.x * kWriteThreads + threadIdx.x;
-  if (idx >= a.n_tokens * a.h_kv * (kHd / 16)) return;
+  const int64_t nblk = (a.n_tokens + 7) / 8;
+  if (idx >= nblk * a.h_kv * (kHd / 16)) return;
   const int j = (int)(idx & 7);
   const int64_t th = idx >> 3;
   const int h = (int)(th % a.h_kv);
-  const int64_t t = th / a.h_kv;
-  const int32_t slot = a.slots[t];
-  if (slot < 0) return;
-  const int32_t page = slot / kPageTok, pos = slot % kPageTok;
-  if (page >= a.n_pages) return;
-  const bool refine = a.page_kind[page] != 0;
-  const int cap = refine ? kPageTok / 2 : kPageTok;
-  if (pos >= cap) return;
-  const int64_t sec = ((int64_t)page * a.h_kv + h) * kSec;
-  const int64_t e0 = (t * a.h_kv + h) * kHd + 16 * j;
+  const int64_t t0 = 8 * (th / a.h_kv);
+  const int nt = (a.n_tokens - t0) < 8 ? (int)(a.n_tokens - t0) : 8;
+
+  // V fast path: the 8 tokens fill positions 8i .. 8i+7 of one page in order
+  // (a prompt), so this thread owns whole V dwords and stores them; otherwise
+  // each token merges its nibbles into dwords shared with other tokens
+  const int32_t s0 = a.slots[t0];
+  bool whole = nt == 8 && s0 >= 0 && (s0 & 7) == 0 && s0 / kPageTok < a.n_pages;
+  for (int i = 1; i < 8 && whole; ++i) whole = a.slots[t0 + i] == s0 + i;
+  if (whole) whole = (s0 % kPageTok) + 8 <= (a.page_kind[s0 / kPageTok] != 0 ? kPageTok / 2 : kPageTok);
+  uint32_t vq[16], vo[16];
+#pragma unroll
+  for (int d = 0; d < 16; ++d) vq[d] = vo[d] = 0u;
 
   float x[16];
   Enc16 e;
-  // K: token-major codes, [token][group] scales
-  load16(a.k, a.dtype, e0, x);
-  encode_group16(x, Tk, 6.0f * Tk, refine, e);
-  uint8_t *kp = a.k_pages + sec;
-  *(uint2 *)(kp + pos * 64 + 8 * j) = make_uint2(pack8(e.q), pack8(e.q + 8));
-  kp[64 * cap + 8 * pos + j] = (uint8_t)e.B;
-  if (refine) *(uint2 *)(kp + 72 * cap + pos * 64 + 8 * j) = make_uint2(pack8(e.o), pack8(e.o + 8));
+  for (int i = 0; i < nt; ++i) {
+    const int64_t t = t0 + i;
+    const int32_t slot = a.slots[t];
+    if (slot < 0) continue;
+    const int32_t page = slot / kPageTok, pos = slot % kPageTok;
+    if (page >= a.n_pages) continue;
+    const bool refine = a.page_kind[page] != 0;
+    const int cap = refine ? kPageTok / 2 : kPageTok;
+    if (pos >= cap) continue;
+    const int64_t sec = ((int64_t)page * a.h_kv + h) * kSec;
+    const int64_t e0 = (t * a.h_kv + h) * kHd + 16 * j;
 
-  // V: [token/8][dim/8][token%8] dwords, [group][token] scales
-  load16(a.v, a.dtype, e0, x);
-  encode_group16(x, Tv, 6.0f * Tv, refine, e);
-  uint8_t *vp = a.v_pages + sec;
-  const int dw = ((pos >> 3) * 16 + 2 * j) * 32 + (pos & 7) * 4;
-  *(uint32_t *)(vp + dw) = pack8(e.q);
-  *(uint32_t *)(vp + dw + 32) = pack8(e.q + 8);
-  vp[64 * cap + cap * j + pos] = (uint8_t)e.B;
-  if (refine) {
-    *(uint32_t *)(vp + 72 * cap + dw) = pack8(e.o);
-    *(uint32_t *)(vp + 72 * cap + dw + 32) = pack8(e.o + 8);
+    // K: token-major codes, [token][group] scales
+    load16(a.k, a.dtype, e0, x);
+    encode_group16(x, Tk, 6.0f * Tk, refine, e);
+    uint8_t *kp = a.k_pages + sec;
+    *(uint2 *)(kp + pos * 64 + 8 * j) = make_uint2(pack8(e.q), pack8(e.q + 8));
+    kp[64 * cap + 8 * pos + j] = (uint8_t)e.B;
+    if (refine) *(uint2 *)(kp + 72 * cap + pos * 64 + 8 * j) = make_uint2(pack8(e.o), pack8(e.o + 8));
+
+    // V: [token/8][dim/8][dim%8] dwords, each the 8 tokens 8 (token/8) .. + 7
+    // of one dim (token t in nibble t % 8), so that a dword is a row of the
+    // V_hat^T operand; [group][token] scales
+    load16(a.v, a.dtype, e0, x);
+    encode_group16(x, Tv, 6.0f * Tv, refine, e);
+    uint8_t *vp = a.v_pages + sec;
+    const uint32_t sh = 4u * (uint32_t)(pos & 7);
+    vp[64 * cap + cap * j + pos] = (uint8_t)e.B;
+    if (whole) {
+#pragma unroll
+      for (int d = 0; d < 16; ++d) {
+        vq[d] |= e.q[d] << sh;
+        vo[d] |= e.o[d] << sh;
+      }
+      continue;
+    }
+    // dims 16j + d, d = 0..15: blocks 2j and 2j + 1, dword d % 8 of each, i.e.
+    // dword d from here; clear the token's nibble, then set it (atomic: other
+    // writers of the launch hold the other nibbles)
+    uint32_t *vd = (uint32_t *)(vp + ((pos >> 3) * 16 + 2 * j) * 32);
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+      atomicAnd(vd + d, ~(0xFu << sh));
+      atomicOr(vd + d, e.q[d] << sh);
+    }
+    if (refine) {
+      uint32_t *vr = (uint32_t *)(vp + 72 * cap + ((pos >> 3) * 16 + 2 * j) * 32);
+#pragma unroll
+      for (int d = 0; d < 16; ++d) {
+        atomicAnd(vr + d, ~(0xFu << sh));
+        atomicOr(vr + d, e.o[d] << sh);
+      }
+    }
+  }
+  if (whole) {
+    const int32_t page = s0 / kPageTok, pos = s0 % kPageTok;
+    const bool refine = a.page_kind[page] != 0;
+    const int cap = refine ? kPageTok / 2 : kPageTok;
+    uint8_t *vp = a.v_pages + ((int64_t)page * a.h_kv + h) * kSec;
+    uint4 *vd = (uint4 *)(vp + ((pos >> 3) * 16 + 2 * j) * 32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) vd[q] = make_uint4(vq[4 * q], vq[4 * q + 1], vq[4 * q + 2], vq[4 * q + 3]);
+    if (refine) {
+      uint4 *vr = (uint4 *)(vp + 72 * cap + ((pos >> 3) * 16 + 2 * j) * 32);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vr[q] = make_uint4(vo[4 * q], vo[4 * q + 1], vo[4 * q + 2], vo[4 * q + 3]);
+    }
   }
 }
 
@@ -371,9 +425,9 @@ __device__ __forceinline__ void softmax_update(const float *x, SoftState &st, ha
   st.l += ps;
 }
 
-// O^T[dim][head] += V_hat^T (16 dims x 32 tokens) . P^T for one slot: dim
-// 8r + n, tokens 8g .. 8g+7; byte m of a token's code dword gives dims
-// 8r + 2m, 8r + 2m + 1, and their two MFMAs (P and Pl parts) follow right away.
+// O^T[dim][head] += V_hat^T (16 dims x 32 tokens) . P^T for one slot: output
+// tile n holds dims 8r + n; lane (r, g) supplies tokens 8g .. 8g+7 of dim
+// 8r + n, one code dword of the page, times the tokens' scales.
 template <bool REF>
 __device__ __forceinline__ void pv_slot(const PageRegs &pr, int slot, int valid, const half8v &P,
                                         const half8v &Pl, int g, SoftState &st) {
@@ -384,34 +438,29 @@ __device__ __forceinline__ void pv_slot(const PageRegs &pr, int slot, int valid,
     vsc.x &= (uint32_t)keep;
     vsc.y &= (uint32_t)(keep >> 32);
   }
-  half2v bp[4];
+  half2v bp[4];   // scales of tokens 2m, 2m + 1 of the lane group
   bp[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vsc.x, 1.0f, false);
   bp[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vsc.x, 1.0f, true);
   bp[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vsc.y, 1.0f, false);
   bp[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(vsc.y, 1.0f, true);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    uint32_t lo4[4], hi4[4];
+  for (int n = 0; n < 8; ++n) {
+    // dword n of the lane's block: dim 8r + n, tokens 8g .. 8g+7 (byte m =
+    // tokens 2m, 2m + 1), already the operand's order
+    const uint32_t dv = u4(pr.vc[slot][n >> 2], n & 3);
+    half2v c[4];
 #pragma unroll
-    for (int jp = 0; jp < 4; ++jp) {
-      const uint32_t x0 = u4(pr.vc[slot][jp >> 1], 2 * (jp & 1));
-      const uint32_t x1 = u4(pr.vc[slot][jp >> 1], 2 * (jp & 1) + 1);
-      half2v c0 = fp4_byte(x0, m);
-      half2v c1 = fp4_byte(x1, m);
+    for (int m = 0; m < 4; ++m) {
+      half2v v = fp4_byte(dv, m);
       if (REF) {
         const half2v q4 = half2v{(_Float16)0.25f, (_Float16)0.25f};
-        c0 += fp4_byte(u4(pr.vc[1][jp >> 1], 2 * (jp & 1)), m) * q4;
-        c1 += fp4_byte(u4(pr.vc[1][jp >> 1], 2 * (jp & 1) + 1), m) * q4;
+        v += fp4_byte(u4(pr.vc[1][n >> 2], n & 3), m) * q4;
       }
-      lo4[jp] = as_u(as_h2(__builtin_amdgcn_perm(as_u(c1), as_u(c0), 0x05040100u)) * bp[jp]);
-      hi4[jp] = as_u(as_h2(__builtin_amdgcn_perm(as_u(c1), as_u(c0), 0x07060302u)) * bp[jp]);
+      c[m] = v * bp[m];
     }
-    const half8v alo = __builtin_bit_cast(half8v, make_uint4(lo4[0], lo4[1], lo4[2], lo4[3]));
-    const half8v ahi = __builtin_bit_cast(half8v, make_uint4(hi4[0], hi4[1], hi4[2], hi4[3]));
-    st.O[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, P, st.O[2 * m], 0, 0, 0);
-    st.O[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, Pl, st.O[2 * m], 0, 0, 0);
-    st.O[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, P, st.O[2 * m + 1], 0, 0, 0);
-    st.O[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, Pl, st.O[2 * m + 1], 0, 0, 0);
+    const half8v a8 = half8v{c[0][0], c[0][1], c[1][0], c[1][1], c[2][0], c[2][1], c[3][0], c[3][1]};
+    st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, P, st.O[n], 0, 0, 0);
+    st.O[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, Pl, st.O[n], 0, 0, 0);
   }
 }
 
@@ -640,7 +689,7 @@ size_t kv_attn_workspace_bytes(int64_t rows, int64_t max_pages) {
 }
 
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s) {
-  const int64_t n = a.n_tokens * a.h_kv * (kHd / 16);
+  const int64_t n = (a.n_tokens + 7) / 8 * a.h_kv * (kHd / 16);
   hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)((n + kWriteThreads - 1) / kWriteThreads)),
                      dim3(kWriteThreads), 0, s, a);
   return hipGetLastError();

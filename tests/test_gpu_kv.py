@@ -55,8 +55,9 @@ def read_section(sec, refined, which):
         raw = sec[off:off + 64 * C]
         if which == "k":
             return nibbles(raw.reshape(C, 64))
-        blk = raw.reshape(C // 8, 16, 8, 4).transpose(0, 2, 1, 3).reshape(C, 64)
-        return nibbles(blk)
+        # V: [token block][dim block][dim % 8] dwords, token t % 8 in nibble t % 8
+        nib = nibbles(raw.reshape(C // 8, 16, 8, 4))            # [tb][db][d][j]
+        return nib.transpose(0, 3, 1, 2).reshape(C, 128)        # [tb, j][db, d]
 
     codes = codes_at(0)
     sc = sec[64 * C:72 * C]
