@@ -8,7 +8,7 @@ batch 1 by default, synthetic seeded data. One step =
   three layers, at levels 2, 4 and 6, each:
     online AutoFP encode of each linear input (amax, NVFP4, 6-bit refinement)
     AutoFP GEMV against the packed weight
-    L_A of the layer update and the device-side policy update
+    L_A of the layer update and the device-side policy update (one call)
 Layers rotate through a pool larger than the 256 MB Infinity Cache, so the
 weights stream from HBM. Everything is captured once per pool position in a
 HIP graph and replayed.
@@ -175,9 +175,8 @@ class DecodeBench:
                 A.quantize_into(self.x_in[name], self.xq[name], refine=(level == 6),
                                 exclude_mask=wp.mask, workspace=self.qws[k], params=p)
                 A.gemv(wp, self.xq[name], bits=level, out=self.y[name], workspace=self.gws[k], params=p)
-            A.policy_signals(h_prev=self.h_prev, h_cur=self.h_cur, out_update=self.l_a, params=p)
-            A.policy_update(1, j, self.l_a, self.state, g_e=self.g_e, bits_rows=self.bits_rows,
-                            bits_layer=self.bits_layer, params=p)
+            A.policy_layer(1, j, self.h_prev, self.h_cur, self.state, g_e=self.g_e, l_a=self.l_a,
+                           bits_rows=self.bits_rows, bits_layer=self.bits_layer, params=p)
 
     def step_bytes(self):
         b = self.b
@@ -259,9 +258,8 @@ class Step32:
                 A.quantize_into(self.f, self.xf, refine=True, exclude_mask=w["wdown"].mask, workspace=self.qws[self.F])
                 A.gemv(w["wdown"], self.xf, bits_dev=bits, out=self.y["wdown"], workspace=self.gws[self.F])
                 torch_add(self.h1, self.y["wdown"], self.h2)
-                A.policy_signals(h_prev=self.h, h_cur=self.h2, out_update=self.l_a)
-                A.policy_update(1, i, self.l_a, self.state, g_e=self.g_e, new_sequence=(s == 0 and i == 0),
-                                bits_rows=self.rows, bits_layer=lay[i + 1:i + 2])
+                A.policy_layer(1, i, self.h, self.h2, self.state, g_e=self.g_e, new_sequence=(s == 0 and i == 0),
+                               l_a=self.l_a, bits_rows=self.rows, bits_layer=lay[i + 1:i + 2])
                 self.h.copy_(self.h2)
 
     def bytes_of(self, lay):

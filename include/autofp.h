@@ -272,6 +272,24 @@ autofp_status autofp_policy_update(int32_t phase, int32_t layer, int32_t new_seq
                                    int32_t *bits_rows, int32_t *bits_layer, void *stream);
 
 /*
+ * The per-layer step of the policy in one call ([AE] §3.1: Eq. 1, then
+ * Table 1): L_A of every row from the layer's input and output hidden states,
+ * written to l_a_out [batch] fp32 (device), then autofp_policy_update with it.
+ * The results equal autofp_policy_signals (update part) followed by
+ * autofp_policy_update, value for value (the same fp64 summation order). Up to
+ * 4 rows it is one launch; above, the two launches. h_prev, h_cur
+ * [batch][hidden] in h_dtype (F32 or BF16); other arguments as in
+ * autofp_policy_update.
+ * Errors: NULL, SHAPE, DTYPE, ARG, HIP.
+ */
+autofp_status autofp_policy_layer(int32_t phase, int32_t layer, int32_t new_sequence,
+                                  const void *h_prev, const void *h_cur, int32_t h_dtype,
+                                  int64_t hidden, const float *g_e, int64_t batch,
+                                  const autofp_params *p, autofp_policy_state *state,
+                                  float *l_a_out, int32_t *bits_rows, int32_t *bits_layer,
+                                  void *stream);
+
+/*
  * ---------------------------------------------------------------------------
  * AutoFP KV cache and decode attention ([AE] §4.1, last paragraph; §5.1)
  * ---------------------------------------------------------------------------

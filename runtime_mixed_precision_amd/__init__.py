@@ -297,6 +297,30 @@ def policy_update(phase, layer, l_a, state, g_e=None, new_sequence=False, bits_r
     return bits_rows, bits_layer
 
 
+def policy_layer(phase, layer, h_prev, h_cur, state, g_e=None, new_sequence=False, l_a=None, bits_rows=None,
+                 bits_layer=None, params=None, stream=None):
+    """L_A of the layer and the policy step in one call (autofp_policy_layer).
+    h_prev, h_cur [batch, hidden] fp32 or bf16. Returns (l_a [batch] fp32,
+    bits_rows [batch] int32, bits_layer [1] int32)."""
+    _dev_check(h_prev, h_cur, g_e, state)
+    if h_prev.shape != h_cur.shape or h_prev.dtype != h_cur.dtype or h_prev.dim() != 2:
+        raise ValueError("h_prev and h_cur must be matching [batch, hidden] tensors")
+    batch, hidden = h_prev.shape
+    dev = h_prev.device
+    if l_a is None:
+        l_a = torch.empty(batch, dtype=torch.float32, device=dev)
+    if bits_rows is None:
+        bits_rows = torch.empty(batch, dtype=torch.int32, device=dev)
+    if bits_layer is None:
+        bits_layer = torch.empty(1, dtype=torch.int32, device=dev)
+    p = params or default_params()
+    N.check(N.lib().autofp_policy_layer(int(phase), int(layer), int(bool(new_sequence)), _ptr(h_prev),
+                                        _ptr(h_cur), _DT[h_prev.dtype], hidden, _ptr(g_e), batch, C.byref(p),
+                                        _ptr(state), _ptr(l_a), _ptr(bits_rows), _ptr(bits_layer),
+                                        _stream(stream)), "autofp_policy_layer")
+    return l_a, bits_rows, bits_layer
+
+
 class KVCache:
     """Device buffers of an AutoFP KV cache (autofp_kv_cache): K and V page
     pools [n_pages][h_kv][4608] bytes, the page types (0 base: 64 tokens,

@@ -29,7 +29,7 @@ EXPORTS = (
     "autofp_default_params", "autofp_status_string", "autofp_packed_bytes",
     "autofp_weight_refined_count", "autofp_workspace_bytes", "autofp_select_weight_mask",
     "autofp_quantize", "autofp_gemv", "autofp_gemm", "autofp_policy_signals",
-    "autofp_policy_update", "autofp_kv_write", "autofp_kv_attention",
+    "autofp_policy_update", "autofp_policy_layer", "autofp_kv_write", "autofp_kv_attention",
 )
 
 
@@ -109,6 +109,8 @@ def lib():
                                             P(Params), vp, vp, vp, C.c_size_t, vp]),
         "autofp_policy_update": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, vp, vp, C.c_int64,
                                            P(Params), vp, vp, vp, vp]),
+        "autofp_policy_layer": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, vp, vp, C.c_int32, C.c_int64, vp,
+                                          C.c_int64, P(Params), vp, vp, vp, vp, vp]),
         "autofp_kv_write": (C.c_int, [vp, vp, C.c_int32, C.c_int64, vp, C.c_int32, P(KvCache), vp,
                                       C.c_size_t, vp]),
         "autofp_kv_attention": (C.c_int, [vp, C.c_int32, C.c_int64, C.c_int32, P(KvCache), C.c_int32,

@@ -109,8 +109,15 @@ struct PolicyArgs {
   int alpha, beta, n_p;
   autofp_policy_state *state;
   int32_t *bits_rows, *bits_layer;
+  // launch_policy_layer: L_A computed from the hidden states into l_a_out
+  const void *h_prev, *h_cur;
+  int h_dtype;
+  int64_t hidden;
+  float eps;
+  float *l_a_out;
 };
 hipError_t launch_policy_update(const PolicyArgs &a, hipStream_t s);
+hipError_t launch_policy_layer(const PolicyArgs &a, hipStream_t s);
 hipError_t launch_update_norm(const void *h_prev, const void *h_cur, int dtype, int64_t batch,
                               int64_t hidden, float eps, float *out, hipStream_t s);
 

@@ -417,6 +417,44 @@ autofp_status autofp_policy_update(int32_t phase, int32_t layer, int32_t new_seq
   return from_hip(launch_policy_update(a, (hipStream_t)stream));
 }
 
+autofp_status autofp_policy_layer(int32_t phase, int32_t layer, int32_t new_sequence,
+                                  const void *h_prev, const void *h_cur, int32_t h_dtype,
+                                  int64_t hidden, const float *g_e, int64_t batch,
+                                  const autofp_params *p, autofp_policy_state *state,
+                                  float *l_a_out, int32_t *bits_rows, int32_t *bits_layer,
+                                  void *stream) {
+  const autofp_params pp = params_or_default(p);
+  if (!h_prev || !h_cur || !l_a_out || !state || !bits_rows) return AUTOFP_ERR_NULL;
+  if (phase != 0 && phase != 1) return AUTOFP_ERR_ARG;
+  if (phase == 1 && !g_e) return AUTOFP_ERR_NULL;
+  if (batch < 1 || hidden < 1) return AUTOFP_ERR_SHAPE;
+  if (h_dtype != AUTOFP_F32 && h_dtype != AUTOFP_BF16) return AUTOFP_ERR_DTYPE;
+  if (layer < 0 || pp.alpha < 1 || pp.beta < 1 || pp.n_p < 1 ||
+      !(pp.lambda_d >= 0.0 && pp.lambda_d <= 1.0) || !(pp.eps >= 0.0f))
+    return AUTOFP_ERR_ARG;
+  PolicyArgs a{};
+  a.phase = phase;
+  a.layer = layer;
+  a.new_sequence = new_sequence;
+  a.g_e = g_e;
+  a.batch = batch;
+  a.tau = pp.tau;
+  a.lambda_d = pp.lambda_d;
+  a.alpha = pp.alpha;
+  a.beta = pp.beta;
+  a.n_p = pp.n_p;
+  a.state = state;
+  a.bits_rows = bits_rows;
+  a.bits_layer = bits_layer;
+  a.h_prev = h_prev;
+  a.h_cur = h_cur;
+  a.h_dtype = h_dtype;
+  a.hidden = hidden;
+  a.eps = pp.eps;
+  a.l_a_out = l_a_out;
+  return from_hip(launch_policy_layer(a, (hipStream_t)stream));
+}
+
 autofp_status autofp_kv_write(const void *k, const void *v, int32_t dtype, int64_t n_tokens,
                               const int32_t *slots, int32_t set_scale,
                               const autofp_kv_cache *cache, void *workspace,

@@ -181,6 +181,22 @@ def test_policy_update_rejects_bad_arguments(N):
     assert up(1, 0, FAKE, FAKE, 1, FAKE, FAKE) == 8
 
 
+def test_policy_layer_rejects_bad_arguments(N):
+    L = N.lib()
+    p = params(N)
+    pl = lambda phase, layer, hp, hc, dt, hidden, ge, batch, st, la, br: L.autofp_policy_layer(
+        phase, layer, 0, hp, hc, dt, hidden, ge, batch, C.byref(p), st, la, br, None, None)
+    assert pl(0, 0, None, FAKE, N.F32, 16, None, 1, FAKE, FAKE, FAKE) == 1
+    assert pl(0, 0, FAKE, FAKE, N.F32, 16, None, 1, FAKE, None, FAKE) == 1   # l_a output
+    assert pl(1, 0, FAKE, FAKE, N.F32, 16, None, 1, FAKE, FAKE, FAKE) == 1   # decode needs G_E
+    assert pl(2, 0, FAKE, FAKE, N.F32, 16, FAKE, 1, FAKE, FAKE, FAKE) == 8
+    assert pl(0, 0, FAKE, FAKE, N.F32, 0, None, 1, FAKE, FAKE, FAKE) == 2
+    assert pl(0, 0, FAKE, FAKE, N.F32, 16, None, 0, FAKE, FAKE, FAKE) == 2
+    assert pl(0, 0, FAKE, FAKE, 9, 16, None, 1, FAKE, FAKE, FAKE) == 7   # dtype
+    p.alpha = 0
+    assert pl(0, 1, FAKE, FAKE, N.F32, 16, None, 1, FAKE, FAKE, FAKE) == 8
+
+
 def kv_cache(N, h_kv=8, n_pages=4, max_pages=4, head_dim=128):
     return N.KvCache(h_kv, head_dim, n_pages, max_pages, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
 

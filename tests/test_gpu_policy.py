@@ -70,3 +70,31 @@ def test_decode_policy_matches_oracle_over_steps():
             assert got[s][b] == want, (s, b, got[s][b], want)
     levels = {v for s in got for row in s for v in row}
     assert levels == {2, 4, 6}                # the case exercises every level
+
+
+@pytest.mark.parametrize("batch", [1, 3, 4, 5, 17])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_policy_layer_equals_signals_then_update(batch, dtype):
+    """autofp_policy_layer (L_A and the policy step in one call: one launch up
+    to 4 rows, two above) gives the same L_A, levels and state, value for
+    value, as autofp_policy_signals followed by autofp_policy_update, over a
+    prefill pass and decode steps."""
+    say(f"case: policy_layer batch {batch} {dtype}")
+    g = torch.Generator(device="cpu").manual_seed(batch)
+    hidden = 4096
+    st_a = A.policy_state(batch, DEV)
+    st_b = A.policy_state(batch, DEV)
+    for step, phase in enumerate((0, 1, 1)):
+        g_e = None if phase == 0 else torch.rand(batch, generator=g).to(DEV) * 0.3
+        h = torch.randn(batch, hidden, generator=g).to(DEV, dtype)
+        for layer in range(12):
+            scale = 0.05 + 0.2 * float(torch.rand(1, generator=g))
+            h2 = (h.float() + scale * torch.randn(batch, hidden, generator=g).to(DEV)).to(dtype)
+            la_b = A.policy_signals(h_prev=h, h_cur=h2)[1]
+            rows_b, lay_b = A.policy_update(phase, layer, la_b, st_b, g_e=g_e, new_sequence=(step == 0))
+            la_a, rows_a, lay_a = A.policy_layer(phase, layer, h, h2, st_a, g_e=g_e, new_sequence=(step == 0))
+            assert torch.equal(la_a, la_b), (step, layer)
+            assert torch.equal(rows_a, rows_b) and torch.equal(lay_a, lay_b), (step, layer)
+            h = h2
+        torch.cuda.synchronize()
+        assert torch.equal(st_a.view(torch.uint8), st_b.view(torch.uint8)), step
