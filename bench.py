@@ -519,7 +519,7 @@ def main():
                     help="run only the workload of the HBM-counter runs (no JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path, so --gpus must be 1",
+        print("bench.py measures one GPU: the library has no multi-GPU path, so --gpus must be 1",
               file=sys.stderr)
         sys.exit(2)
     if args.pool_layers % len(LEVELS):
