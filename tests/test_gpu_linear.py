@@ -115,10 +115,14 @@ def test_gemm_shapes(n, m, k, level):
         assert torch.equal(yb, y.to(torch.bfloat16)), "bf16 output is not the RNE of the fp32 result"
 
 
-@pytest.mark.parametrize("op", ["gemv", "gemm"])
-def test_bf16_output_and_device_level(op):
-    say(f"case: {op} bf16 output and device-side level")
-    w, x = operands(96, 12, 512, seed=4)
+@pytest.mark.parametrize("op,n,b", [("gemv", 96, 12), ("gemm", 96, 12), ("gemv", 200, 40), ("gemv", 8200, 40)])
+def test_bf16_output_and_device_level(op, n, b):
+    """bf16 outputs are the fp32 results rounded; a level read on the device
+    gives the host-level result, bit for bit (40 tokens: the panel kernel,
+    which reads packed activations at host levels 2 and 4 and the fp16 panel
+    for a device-side level; 8200 rows: the 64-token GEMM tile)."""
+    say(f"case: {op} bf16 output and device-side level N={n} B={b}")
+    w, x = operands(n, b, 512, seed=4)
     wp, xp4, xp6 = gpu_pack(w, x)
     fn = getattr(A, op)
     for level in (2, 4, 6):
