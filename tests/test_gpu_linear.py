@@ -180,6 +180,30 @@ def test_full_size_decode_sampled(name, b):
         check_close(y[:, rows], ref)
 
 
+@pytest.mark.parametrize("name,n,k", [("wo", 4096, 4096), ("wdown", 4096, 14336), ("wgateup", 28672, 4096)])
+def test_full_size_one_token_all_levels(name, n, k):
+    """The one-token launches the decode benchmark times, at full size and at
+    all three levels (the fused Wgate|Wup is one 28672 x 4096 weight): every
+    output of 64 sampled weight rows, the first and last among them, against
+    the oracle. The oracle selects M_W over the whole weight."""
+    say(f"case: full-size one token {name} {n}x{k}")
+    w = S.weights(n, k, seed=3, tensor_id=7, device=DEV)
+    x = S.activations(1, k, seed=3, tensor_id=98, device=DEV)
+    wp = A.quantize_weight(w, refine=True)
+    xp4 = A.quantize_activation(x)
+    xp6 = A.quantize_activation(x, refine=True, exclude_mask=wp.mask)
+    wn = w.cpu().numpy()
+    xn = x.float().cpu().numpy()
+    rows = np.concatenate([[0, n - 1], np.random.default_rng(4).choice(np.arange(1, n - 1), 62, replace=False)])
+    bits, _ = O.select_weight_mask(wn, 0.2)
+    wq = O.quantize_weight(wn[rows], O.pack_nibbles(bits), tensor_amax=np.abs(wn).max())
+    xq4 = O.quantize_activation(xn)
+    xq6 = O.quantize_activation(xn, refine=True, exclude_mask=wq["mask"])
+    for level in (2, 4, 6):
+        y = A.gemv(wp, xp6 if level == 6 else xp4, bits=level).cpu().numpy()
+        check_close(y[:, rows], O.linear(wq, xq6 if level == 6 else xq4, level))
+
+
 @pytest.mark.parametrize("b", [16, 64])
 def test_full_size_70b_gemv_sampled(b):
     """The 70B-shaped projection (28672 x 8192) at 16 and 64 tokens, levels 2
