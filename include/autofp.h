@@ -206,8 +206,10 @@ autofp_status autofp_quantize(const void *x, int32_t x_dtype, int32_t refine,
  * If bits_dev != NULL the level is read on the device when the kernels run
  * (graph-capturable, no host read); `bits` is then ignored but a level-6 call
  * must be allowed by the operands (both carry refinement).
- * Best for x->rows <= 64; larger batches run in slices of 64 tokens. With at
- * most 16 tokens, a level-6 call (or one with bits_dev) needs k <= 65536.
+ * Best for x->rows <= 64; larger batches run in slices of 64 tokens. k must
+ * be at most 2^22 (4194304); with at most 16 tokens, a level-6 call (or one
+ * with bits_dev) needs k <= 65536. Any number of tokens: the kernels address
+ * the activations one tile of rows at a time.
  * Errors: NULL, SHAPE, KIND, BITS, MISSING_REFINEMENT, DTYPE, WORKSPACE, HIP.
  */
 autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_t bits,
@@ -216,8 +218,14 @@ autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_
                           void *stream);
 
 /*
- * Prefill-phase linear layer: the same result as autofp_gemv for any number of
- * tokens, tiled for the matrix cores. Same arguments and errors.
+ * Prefill-phase linear layer ([AE] §4.1, "Extended-K GEMM": the same product
+ * as the decode GEMV, run for every prompt token at once; §5.3 prefill of 1K
+ * to 128K input tokens): y = Xhat . What^T for any number of tokens, tiled
+ * for the matrix cores (256-token x 256-row tiles when K % 64 == 0). The
+ * fp16 activations are staged in the workspace (autofp_workspace_bytes(
+ * AUTOFP_OP_GEMM, tokens, k): 2 * tokens * round_up(k, 256) bytes plus the
+ * weight-mask prefix). k <= 2^22. Same arguments, results and errors as
+ * autofp_gemv.
  */
 autofp_status autofp_gemm(const autofp_packed *w, const autofp_packed *x, int32_t bits,
                           const int32_t *bits_dev, void *y, int32_t y_dtype,
@@ -229,7 +237,8 @@ autofp_status autofp_gemm(const autofp_packed *w, const autofp_packed *x, int32_
  *  - entropy_out[b] = G_E of logits row b: softmax over the top_k largest
  *    logits, H = -sum p ln p, divided by ln(top_k) (ln(vocab) when
  *    top_k >= vocab). logits [batch x vocab] fp32. top_k must be 1..32 or
- *    >= vocab.
+ *    >= vocab. Masked entries may hold -inf (probability 0, no term of H) as
+ *    long as each row has at least one finite logit.
  *  - update_out[b] = L_A = ||h_cur[b] - h_prev[b]||_2 / (||h_prev[b]||_2 + eps)
  *    ([AE] Eq. 1); h_prev, h_cur [batch x hidden] in h_dtype (F32 or BF16).
  * Either signal is skipped when its output pointer is NULL (its inputs may
@@ -349,7 +358,11 @@ typedef struct {
  * set_scale != 0: first sets *k_scale = amax(k) / 2688 and *v_scale =
  * amax(v) / 2688 over this call's tokens ([AE] App. B.1, Eq. 2), as for a
  * prompt; otherwise the stored tensor scales are used and values beyond
- * 6 * 448 * T saturate. Group scales and codes follow autofp_quantize (Eqs.
+ * 6 * 448 * T saturate. The tensor scales are shared by every page of the
+ * cache and read by autofp_kv_attention for all of them: set them only when
+ * the cache is first filled (its first prompt). A later call with
+ * set_scale != 0 rescales the pages already written by other calls, which then
+ * decode wrongly; later prompts and decode tokens use set_scale = 0. Group scales and codes follow autofp_quantize (Eqs.
  * 2-3, fp32, ties to even); tokens of refinement pages also get their offsets.
  * The page table fields of `cache` are not read. Workspace:
  * autofp_workspace_bytes(AUTOFP_OP_KV_WRITE, n_tokens * h_kv, 128) bytes

@@ -30,7 +30,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # two wavefronts fit per SIMD.
 SOURCE_FLAGS = {"kv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
-          "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument"]
+          "-Wall", "-Werror", "-Wno-unused-function", "-Wno-unused-command-line-argument"]
 
 
 def hipcc():

@@ -11,11 +11,14 @@ using namespace afp;
 static_assert(sizeof(autofp_policy_state) == 48, "policy state layout");
 static_assert(sizeof(autofp_params) == 56, "params layout");
 
+
 namespace {
 
 constexpr size_t kAlign = 256;
 // bytes past the last row of a weight's offsets that the GEMV may read (never writes)
 constexpr size_t kOffsetPad = 16;
+// largest reduction dimension of autofp_gemv / autofp_gemm
+constexpr int64_t kMaxLinearK = (int64_t)1 << 22;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -94,6 +97,9 @@ autofp_status linear_common(const autofp_packed *w, const autofp_packed *x, int3
   st = check_packed(x, AUTOFP_ACTIVATION);
   if (st != AUTOFP_OK) return st;
   if (w->k != x->k) return AUTOFP_ERR_SHAPE;
+  // the GEMM addresses one tile's fp16 activation rows ([256][round_up(k, 256)])
+  // with 32-bit buffer offsets
+  if (x->k > kMaxLinearK) return AUTOFP_ERR_SHAPE;
   if (!y) return AUTOFP_ERR_NULL;
   if (!aligned16(y)) return AUTOFP_ERR_ARG;
   if (y_dtype != AUTOFP_F32 && y_dtype != AUTOFP_BF16) return AUTOFP_ERR_DTYPE;
@@ -130,6 +136,73 @@ autofp_status linear_common(const autofp_packed *w, const autofp_packed *x, int3
   a.prefix = (int32_t *)((char *)ws + align_up(sizeof(_Float16) * (size_t)x->rows * (size_t)a.kpad));
   return AUTOFP_OK;
 }
+
+
+autofp_status check_quantize(const void *x, int32_t x_dtype, int32_t refine, const uint8_t *exclude_mask,
+                             const autofp_packed *out) {
+  if (!x || !out) return AUTOFP_ERR_NULL;
+  if (x_dtype != AUTOFP_F32 && x_dtype != AUTOFP_BF16) return AUTOFP_ERR_DTYPE;
+  if (out->kind != AUTOFP_WEIGHT && out->kind != AUTOFP_ACTIVATION) return AUTOFP_ERR_KIND;
+  if (out->rows < 1 || !valid_k(out->k)) return AUTOFP_ERR_SHAPE;
+  if (!out->codes || !out->scales || !out->tensor_scale) return AUTOFP_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out->codes) || !aligned16(out->scales) ||
+      !aligned16(out->tensor_scale) || (out->mask && !aligned16(out->mask)) ||
+      (out->offsets && !aligned16(out->offsets)) || (exclude_mask && !aligned16(exclude_mask)))
+    return AUTOFP_ERR_ARG;
+  const bool act_refine = out->kind == AUTOFP_ACTIVATION && refine;
+  const bool w_refine = out->kind == AUTOFP_WEIGHT && out->mask != nullptr;
+  if (act_refine && (!out->mask || !out->offsets)) return AUTOFP_ERR_MISSING_REFINEMENT;
+  if (out->kind == AUTOFP_WEIGHT && refine && !out->mask) return AUTOFP_ERR_MISSING_REFINEMENT;
+  if (w_refine) {
+    if (out->n_refined < 0 || out->n_refined > 2 * (out->k / 16)) return AUTOFP_ERR_ARG;
+    if (out->n_refined > 0 && !out->offsets) return AUTOFP_ERR_MISSING_REFINEMENT;
+  }
+  return AUTOFP_OK;
+}
+
+// The encode's launches on scratch `ws` (ws_quantize bytes: amax partials,
+// then the weight-mask prefix table); arguments already checked.
+autofp_status launch_quantize(const void *x, int32_t x_dtype, int32_t refine, const uint8_t *exclude_mask,
+                              const autofp_params *p, const autofp_packed *out, void *ws, hipStream_t s) {
+  const autofp_params pp = params_or_default(p);
+  const bool act_refine = out->kind == AUTOFP_ACTIVATION && refine;
+  const bool w_refine = out->kind == AUTOFP_WEIGHT && out->mask != nullptr;
+  float *partial = (float *)ws;
+  int32_t *prefix = (int32_t *)((char *)ws + align_up(sizeof(float) * kAmaxBlocks));
+  const int64_t n = out->rows * out->k;
+  const bool small = n <= kSmallEncode;
+  const int np = amax_partial_count(n);
+  hipError_t e = hipSuccess;
+  if (!small) {
+    e = launch_amax_partial(x, x_dtype, n, partial, np, s);
+    if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  }
+  if (w_refine) {
+    e = launch_mask_prefix(out->mask, mask_bytes(out->k), prefix, s);
+    if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  }
+  EncodeArgs a{};
+  a.x = x;
+  a.dtype = x_dtype;
+  a.rows = out->rows;
+  a.k = out->k;
+  a.partial = partial;
+  a.n_partial = np;
+  a.codes = out->codes;
+  a.scales = out->scales;
+  a.tensor_scale = out->tensor_scale;
+  a.act_refine = act_refine ? 1 : 0;
+  a.exclude_mask = act_refine ? exclude_mask : nullptr;
+  a.thresh = pp.act_nmse_thresh;
+  a.act_mask = act_refine ? out->mask : nullptr;
+  a.act_offsets = act_refine ? out->offsets : nullptr;
+  a.w_mask = w_refine ? out->mask : nullptr;
+  a.w_prefix = prefix;
+  a.n_refined = out->n_refined;
+  a.w_offsets = out->offsets;
+  return from_hip(launch_encode(a, small, s));
+}
+
 
 }  // namespace
 
@@ -256,61 +329,11 @@ autofp_status autofp_quantize(const void *x, int32_t x_dtype, int32_t refine,
                               const uint8_t *exclude_mask, const autofp_params *p,
                               autofp_packed *out, void *workspace, size_t workspace_bytes,
                               void *stream) {
-  if (!x || !out) return AUTOFP_ERR_NULL;
-  if (x_dtype != AUTOFP_F32 && x_dtype != AUTOFP_BF16) return AUTOFP_ERR_DTYPE;
-  if (out->kind != AUTOFP_WEIGHT && out->kind != AUTOFP_ACTIVATION) return AUTOFP_ERR_KIND;
-  if (out->rows < 1 || !valid_k(out->k)) return AUTOFP_ERR_SHAPE;
-  if (!out->codes || !out->scales || !out->tensor_scale) return AUTOFP_ERR_NULL;
-  if (!aligned16(x) || !aligned16(out->codes) || !aligned16(out->scales) ||
-      !aligned16(out->tensor_scale) || (out->mask && !aligned16(out->mask)) ||
-      (out->offsets && !aligned16(out->offsets)) || (exclude_mask && !aligned16(exclude_mask)))
-    return AUTOFP_ERR_ARG;
-  const autofp_params pp = params_or_default(p);
-  const bool act_refine = out->kind == AUTOFP_ACTIVATION && refine;
-  const bool w_refine = out->kind == AUTOFP_WEIGHT && out->mask != nullptr;
-  if (act_refine && (!out->mask || !out->offsets)) return AUTOFP_ERR_MISSING_REFINEMENT;
-  if (out->kind == AUTOFP_WEIGHT && refine && !out->mask) return AUTOFP_ERR_MISSING_REFINEMENT;
-  if (w_refine) {
-    if (out->n_refined < 0 || out->n_refined > 2 * (out->k / 16)) return AUTOFP_ERR_ARG;
-    if (out->n_refined > 0 && !out->offsets) return AUTOFP_ERR_MISSING_REFINEMENT;
-  }
+  const autofp_status st = check_quantize(x, x_dtype, refine, exclude_mask, out);
+  if (st != AUTOFP_OK) return st;
   if (!workspace || workspace_bytes < ws_quantize(out->rows, out->k)) return AUTOFP_ERR_WORKSPACE;
   if (!aligned16(workspace)) return AUTOFP_ERR_ARG;
-  hipStream_t s = (hipStream_t)stream;
-  float *partial = (float *)workspace;
-  int32_t *prefix = (int32_t *)((char *)workspace + align_up(sizeof(float) * kAmaxBlocks));
-  const int64_t n = out->rows * out->k;
-  const bool small = n <= kSmallEncode;
-  const int np = amax_partial_count(n);
-  hipError_t e = hipSuccess;
-  if (!small) {
-    e = launch_amax_partial(x, x_dtype, n, partial, np, s);
-    if (e != hipSuccess) return AUTOFP_ERR_HIP;
-  }
-  if (w_refine) {
-    e = launch_mask_prefix(out->mask, mask_bytes(out->k), prefix, s);
-    if (e != hipSuccess) return AUTOFP_ERR_HIP;
-  }
-  EncodeArgs a{};
-  a.x = x;
-  a.dtype = x_dtype;
-  a.rows = out->rows;
-  a.k = out->k;
-  a.partial = partial;
-  a.n_partial = np;
-  a.codes = out->codes;
-  a.scales = out->scales;
-  a.tensor_scale = out->tensor_scale;
-  a.act_refine = act_refine ? 1 : 0;
-  a.exclude_mask = act_refine ? exclude_mask : nullptr;
-  a.thresh = pp.act_nmse_thresh;
-  a.act_mask = act_refine ? out->mask : nullptr;
-  a.act_offsets = act_refine ? out->offsets : nullptr;
-  a.w_mask = w_refine ? out->mask : nullptr;
-  a.w_prefix = prefix;
-  a.n_refined = out->n_refined;
-  a.w_offsets = out->offsets;
-  return from_hip(launch_encode(a, small, s));
+  return launch_quantize(x, x_dtype, refine, exclude_mask, p, out, workspace, (hipStream_t)stream);
 }
 
 autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_t bits,

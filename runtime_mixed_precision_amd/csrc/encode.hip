@@ -326,7 +326,10 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(EncodeArgs a) {
         if ((s & 7) == 0) a.act_mask[row * mb + (s >> 3)] = (uint8_t)(bits >> lane);
       }
     }
-    if (want_w && live && ((wbyte >> (s & 7)) & 1u)) a.w_offsets[row * (int64_t)a.n_refined + wpos] = (uint8_t)ob;
+    // the mask's popcount should equal n_refined; a mask with more refined
+    // subgroups writes only the first n_refined of each row
+    if (want_w && live && ((wbyte >> (s & 7)) & 1u) && wpos < a.n_refined)
+      a.w_offsets[row * (int64_t)a.n_refined + wpos] = (uint8_t)ob;
   }
 }
 

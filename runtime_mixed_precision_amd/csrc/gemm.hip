@@ -10,12 +10,15 @@
 // B*(q + d/8) (up to 10 significant bits) exactly. The operands are therefore
 // decoded into fp16 - exact - and multiplied at the fp16 MFMA rate.
 //
-// Tiling: a block of 4 wavefronts computes a 128-token x 128-row tile with
-// K steps of 64. Each step loads the packed weight tile (16 B of codes and two
-// scale bytes per thread, plus refinement offsets at level 6), decodes it into
-// LDS, copies the fp16 activation tile into LDS, and each wavefront runs a 2x2
-// grid of 32x32x16 MFMAs over its 64x64 quadrant. The next step's global loads
-// are issued before the current step's MFMAs.
+// Two kernels:
+//  - gemm_lds_kernel (K % 64 == 0, the prefill and batched-decode path): a
+//    block of 8 or 16 wavefronts computes BM tokens x BN weight rows (256 x 256
+//    or 256 x 128 for prefill, 64 x 64..256 for 17-64 decode tokens) in K steps
+//    of 64 with two LDS stages; the fp16 activation panel goes memory -> LDS
+//    with buffer_load ... lds, the packed weight tile is decoded in registers
+//    and written to LDS (description above the kernel).
+//  - gemm_kernel (any K % 16 == 0): 4 wavefronts on a 128 x 128 tile, both
+//    operands through registers; the fallback for K % 64 != 0.
 #include <hip/hip_runtime.h>
 
 #include "afp_device.h"
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a) {
 #pragma unroll
           for (int s = 0; s < 8; ++s) {
             t.offs[s] = 0;
-            if ((m >> s) & 1u) t.offs[s] = woff[pos++];
+            if (((m >> s) & 1u) && pos < a.n_refined) t.offs[s] = woff[pos++];
           }
         }
       }
@@ -200,15 +203,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Large-tile GEMM (K % 64 == 0): a block of 4 wavefronts computes 256 tokens x
-// BN weight rows (BN = 256 or 128) in K steps of 64, with two LDS stages.
+// Large-tile GEMM (K % 64 == 0): a block of NW wavefronts (8 or 16) computes
+// BM tokens x BN weight rows in K steps of 64, with two LDS stages.
 // Activation tiles (fp16 panel) go from memory straight to LDS with
 // buffer_load ... lds (no registers, no ALU); weight tiles are loaded into
 // registers, decoded to fp16 and written to LDS. The loads of step k + 1 are
 // issued before the MFMAs of step k. LDS rows are 128 bytes (64 halves) with
 // the 16-byte chunk index XOR-swizzled by (row / 2) % 8, so the fragment reads
-// of a 32x32x16 MFMA (32 rows, one chunk) spread over all banks. Each wavefront
-// owns 128 tokens x BN/2 rows: 4 x (BN/64) tiles of v_mfma_f32_32x32x16_f16.
+// of a 32x32x16 MFMA (32 rows, one chunk) spread over all banks. The
+// wavefronts form a WGM x (NW / WGM) grid over the tile, each running a grid
+// of v_mfma_f32_32x32x16_f16 tiles over its part.
 // ---------------------------------------------------------------------------
 
 typedef uint32_t u32x3v __attribute__((ext_vector_type(3)));
@@ -294,8 +298,11 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
     __syncthreads();
   }
 
-  // activation panel [b][kpad] fp16: rows past b read as zero
-  const __amdgpu_buffer_rsrc_t rx = rsrc(a.xh, a.b * a.kpad * 2);
+  // activation panel [b][kpad] fp16, this block's BM rows only (so a panel
+  // of any size is addressed with 32-bit offsets: BM * kpad * 2 < 2^31 for
+  // k <= 2^22, which the entry points check); rows past b read as zero
+  const int64_t mrows = (a.b - m0) < BM ? (a.b - m0) : BM;
+  const __amdgpu_buffer_rsrc_t rx = rsrc(a.xh + m0 * a.kpad, mrows * a.kpad * 2);
   // weight rows of this block: rows past n read as zero
   const int64_t nrows = (a.n - n0) < BN ? (a.n - n0) : BN;
   const __amdgpu_buffer_rsrc_t rc = rsrc(a.w_codes + n0 * (K >> 1), nrows * (K >> 1));
@@ -311,8 +318,7 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
     for (int d = 0; d < APW; ++d) {
       const uint32_t r = (uint32_t)(8 * (APW * wave + d)) + arow_l;   // tile row 0..255
       const uint32_t cg = (uint32_t)(lane & 7) ^ ((r >> 1) & 7u);
-      const int64_t tok = m0 + r;
-      const uint32_t off = (tok < a.b && k0 < K) ? (uint32_t)((tok * a.kpad + k0 + 8 * cg) * 2) : 0x80000000u;
+      const uint32_t off = ((int64_t)r < mrows && k0 < K) ? (uint32_t)(((int64_t)r * a.kpad + k0 + 8 * cg) * 2) : 0x80000000u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, AFP_LDS(base + 8 * (APW * wave + d) * 128), 16, (int)off, 0, 0, 0);
     }
   };

@@ -34,6 +34,8 @@
 // adds the fp16 offsets d/8 of each refined slot from a 256-entry LDS table.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "afp_device.h"
 #include "afp_launch.h"
 
@@ -249,7 +251,6 @@ __device__ __forceinline__ void stream_tile(const LinearArgs &a, unsigned char *
       make_rsrc(refine_w ? a.w_offsets + nb0 * R : a.w_codes, rows > 0 ? rows * R + 16 : 0);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xh, XLDS ? 0 : a.b * a.kpad * 2);
   const uint32_t crow = (uint32_t)(r * (K >> 1) + 32 * ks);    // + 128 bytes per chunk
-  const uint32_t srow = (uint32_t)(r * (K >> 4) + 4 * ks);     // + 16 bytes per chunk
   const uint32_t orow = (uint32_t)(r * R);
 
   const int64_t c0 = (nch * kw) / WK;
@@ -1254,17 +1255,20 @@ struct StreamCfg {
   size_t lds;
 };
 
+// The library's only host-side mutable state: a per-device cache of one
+// device property (LDS bytes per block). Relaxed atomics make concurrent
+// first calls benign: every writer stores the same value.
 int max_lds_per_block() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
-  if (cached[dev] == 0) {
-    int v = 0;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
       v = 65536;
-    cached[dev] = v;
+    cached[dev].store(v, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return v;
 }
 
 StreamCfg stream_cfg(const LinearArgs &a) {

@@ -296,7 +296,7 @@ constexpr int kCopyLoads = 10;   // buffer->LDS loads per page
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt(10), other counters free; and
 // lgkmcnt(0), other counters free.
-constexpr int kWaitVm10 = 10 | (0x7 << 4) | (0xF << 8);
+constexpr int kWaitVm10 = kCopyLoads | (0x7 << 4) | (0xF << 8);
 constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
 
 // Copy one page's K and V sections of this KV head into ring slot `dst`

@@ -130,7 +130,9 @@ __global__ __launch_bounds__(64) void entropy_merge_kernel(const float *__restri
   const float f = wave_topk(lst, top_k);
   const double m = (double)__shfl(f, 0, 64);
   double e = 0.0, te = 0.0;
-  if (lane < top_k) {
+  // a candidate of -inf (fewer than top_k finite logits) has probability 0
+  // and adds nothing to S or S1
+  if (lane < top_k && f != -INFINITY) {
     const double d = (double)f - m;
     e = exp(d);
     te = d * e;

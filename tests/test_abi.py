@@ -134,6 +134,13 @@ def test_linear_rejects_bad_arguments(N):
         assert call(w, x2, 4) == 2                        # K mismatch
         wbad = packed(N, N.WEIGHT, rows=8, k=64, refine=True, n_refined=99)
         assert call(wbad, x, 4) == 8                      # n_refined beyond 2 per group
+        # the largest reduction dimension: 2^22 (one 256-token tile of fp16
+        # activation rows stays below 2^31 bytes); one group more is rejected
+        kmax = 1 << 22
+        wk, xk = packed(N, N.WEIGHT, rows=8, k=kmax + 16), packed(N, N.ACTIVATION, rows=2, k=kmax + 16)
+        assert call(wk, xk, 4) == 2
+        wk, xk = packed(N, N.WEIGHT, rows=8, k=kmax), packed(N, N.ACTIVATION, rows=2, k=kmax)
+        assert call(wk, xk, 4, ws=16) == 5                # passes the shape check, fails on workspace
 
 
 def test_signals_reject_bad_arguments(N):

@@ -208,6 +208,66 @@ def test_kv_write_append_uses_stored_scale():
     assert kinds is not None
 
 
+def test_kv_second_prompt_into_shared_cache():
+    """Two prompts written into one cache by two calls: the first sets the
+    tensor scales (set_scale=1), the second appends its sequence with
+    set_scale=0. The second call leaves the scales and the first sequence's
+    pages as they were; both sequences' pages and attention match the oracle,
+    which encodes both with the first prompt's tensor scales."""
+    say("case: second prompt appended to a shared cache with set_scale=0")
+    h_kv, hq, lengths = 4, 16, [700, 450]
+    plan = S.kv_page_plan(lengths, 0.5, seed=51)
+    cache = A.KVCache(plan["n_pages"], h_kv, 2, plan["max_pages"], device=DEV)
+    cache.page_kind.copy_(torch.from_numpy(plan["page_kind"]))
+    cache.page_tokens.copy_(torch.from_numpy(plan["page_tokens"]))
+    cache.page_table.copy_(torch.from_numpy(plan["page_table"]))
+    cache.seq_pages.copy_(torch.from_numpy(plan["seq_pages"]))
+    ks = [S.kv_tokens(L, h_kv, seed=52 + b, tensor_id=1, device=DEV) for b, L in enumerate(lengths)]
+    vs = [S.kv_tokens(L, h_kv, seed=52 + b, tensor_id=2, device=DEV) for b, L in enumerate(lengths)]
+    # the second prompt is larger in magnitude: some of its values saturate
+    ks[1] = (ks[1].float() * 1.7).to(torch.bfloat16)
+    vs[1] = (vs[1].float() * 1.7).to(torch.bfloat16)
+    slots = [torch.from_numpy(plan["slots"][b]).to(DEV) for b in range(2)]
+    A.kv_write(cache, ks[0], vs[0], slots[0], set_scale=True)
+    torch.cuda.synchronize()
+    scales0 = cache.scales.clone()
+    kp0, vp0 = cache.k_pages.clone(), cache.v_pages.clone()
+    A.kv_write(cache, ks[1], vs[1], slots[1], set_scale=False)
+    torch.cuda.synchronize()
+    assert torch.equal(cache.scales, scales0)
+    # the first sequence's pages are untouched by the second call
+    own0 = torch.from_numpy(plan["page_table"][0, :plan["seq_pages"][0]].astype(np.int64)).to(DEV)
+    assert torch.equal(cache.k_pages[own0], kp0[own0]) and torch.equal(cache.v_pages[own0], vp0[own0])
+    amax_k = np.float32(ks[0].abs().max().float().item())
+    amax_v = np.float32(vs[0].abs().max().float().item())
+    q = S.kv_tokens(2, hq, seed=55, tensor_id=3, dtype=torch.float32, device=DEV)
+    qn = q.cpu().numpy()
+    kinds = plan["page_kind"]
+    kp, vp = cache.k_pages.cpu().numpy(), cache.v_pages.cpu().numpy()
+    grp = hq // h_kv
+    for level in (4, 6):
+        y = A.kv_attention(q, cache, bits=level, sm_scale=0.1).cpu().numpy()
+        for b in range(2):
+            kf = ks[b].float().cpu().numpy()
+            vf = vs[b].float().cpu().numpy()
+            ref_rows = plan["refine"][b]
+            for g in range(h_kv):
+                kq = O.kv_quantize(kf[:, g], ref_rows, tensor_amax=amax_k)
+                vq = O.kv_quantize(vf[:, g], ref_rows, tensor_amax=amax_v)
+                if level == 4:
+                    for t in range(lengths[b]):
+                        page, pos = int(plan["slots"][b][t]) // PT, int(plan["slots"][b][t]) % PT
+                        for which, pool, r in (("k", kp, kq), ("v", vp, vq)):
+                            codes, scales, d = read_section(pool[page, g], bool(kinds[page]), which)
+                            assert np.array_equal(codes[pos], r["q"][t]), (b, g, t, which)
+                            assert np.array_equal(scales[pos], r["scales"][t]), (b, g, t, which)
+                            if kinds[page]:
+                                assert np.array_equal(d[pos], r["d"][t]), (b, g, t, which)
+                ref = O.kv_attention(qn[b, g * grp:(g + 1) * grp], O.kv_decode(kq, level)[None],
+                                     O.kv_decode(vq, level)[None], 0.1)
+                check_close(y[b, g * grp:(g + 1) * grp], ref, ("shared cache", level, b, g))
+
+
 @pytest.mark.parametrize("level", [2, 4, 6])
 @pytest.mark.parametrize("qdt", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("heads", [(32, 8), (8, 8), (16, 1)])

@@ -13,6 +13,7 @@ import torch
 
 import oracle as O
 import runtime_mixed_precision_amd as A
+from runtime_mixed_precision_amd import _native as N
 from runtime_mixed_precision_amd import synthetic as S
 
 pytestmark = pytest.mark.gpu
@@ -224,19 +225,25 @@ def test_full_size_70b_gemv_sampled(b):
         check_close(y[:, rows], O.linear(wq, xq4, level))
 
 
-def test_prefill_sampled_full_size():
-    """2048 x 4096 prefill activations times the Wup shape (14336 x 4096) at
-    levels 4 and 6: sampled rows and columns against the oracle."""
-    say("case: full-size prefill GEMM 2048x4096x14336")
-    n, k = S.LLAMA8B["wup"]
-    w = S.weights(n, k, seed=2, tensor_id=5, device=DEV)
-    x = S.activations(2048, k, seed=2, tensor_id=6, outlier_frac=0.005, outlier_scale=30.0, device=DEV)
+@pytest.mark.parametrize("name", ["wup", "wdown"])
+def test_prefill_sampled_full_size(name):
+    """The prefill GEMMs the benchmark times, at full size, levels 4 and 6:
+    2048 x 4096 activations times Wup (14336 x 4096), and the FFN output
+    X' (2048 x 14336) times Wdown (4096 x 14336, 224 K steps of the 256 x 128
+    tile). Sampled tokens and weight rows (the first and last of each among
+    them) against the oracle."""
+    n, k = S.LLAMA8B[name]
+    m = 2048
+    say(f"case: full-size prefill GEMM {name} {m}x{k}x{n}")
+    w = S.weights(n, k, seed=2, tensor_id=5 if name == "wup" else 8, device=DEV)
+    x = S.activations(m, k, seed=2, tensor_id=6 if name == "wup" else 9, outlier_frac=0.005,
+                      outlier_scale=30.0, device=DEV)
     wp = A.quantize_weight(w, refine=True)
     xp4 = A.quantize_activation(x)
     xp6 = A.quantize_activation(x, refine=True, exclude_mask=wp.mask)
     rng = np.random.default_rng(3)
-    rows = rng.choice(n, 32, replace=False)
-    toks = rng.choice(2048, 32, replace=False)
+    rows = np.concatenate([[0, n - 1], rng.choice(np.arange(1, n - 1), 30, replace=False)])
+    toks = np.concatenate([[0, m - 1], rng.choice(np.arange(1, m - 1), 30, replace=False)])
     wn = w.cpu().numpy()
     xn = x.float().cpu().numpy()
     bits, _ = O.select_weight_mask(wn, 0.2)
@@ -245,7 +252,89 @@ def test_prefill_sampled_full_size():
     for level, xp in ((4, xp4), (6, xp6)):
         xq = O.quantize_activation(xn[toks], refine=(level == 6), exclude_mask=wq["mask"], tensor_amax=xa)
         y = A.gemm(wp, xp, bits=level).cpu().numpy()
-        check_close(y[np.ix_(toks, rows)], O.linear(wq, xq, level))
+        e = check_close(y[np.ix_(toks, rows)], O.linear(wq, xq, level))
+        say(f"level {level}: max rel err {e:.2e}")
+
+
+def test_prefill_activation_panel_beyond_2gib():
+    """75000 prefill tokens at K = 14336: the fp16 activation panel in the
+    workspace holds 75000 x 14336 x 2 = 2.15e9 bytes, past 2^31, so tokens
+    74899 .. 74999 lie beyond the reach of one 32-bit buffer offset from the
+    panel's start. Sampled tokens on both sides of that point (the first and
+    the last token among them) at levels 4 and 6 against the oracle; the
+    oracle takes the tensor scale of the whole activation (its absolute
+    maximum, found on the host)."""
+    n, k, m = 256, 14336, 75000
+    say(f"case: prefill GEMM {m}x{k}x{n}, activation panel past 2^31 bytes")
+    assert m * k * 2 > 2 ** 31
+    w = S.weights(n, k, seed=4, tensor_id=11, device=DEV)
+    x = S.activations(m, k, seed=4, tensor_id=12, outlier_frac=0.005, outlier_scale=30.0, device=DEV)
+    wp = A.quantize_weight(w, refine=True)
+    xp4 = A.quantize_activation(x)
+    xp6 = A.quantize_activation(x, refine=True, exclude_mask=wp.mask)
+    first_far = -(-2 ** 31 // (k * 2))                # first token whose panel row starts past 2^31
+    rng = np.random.default_rng(13)
+    toks = np.unique(np.concatenate([[0, 1, first_far - 1, first_far, m - 1],
+                                     rng.choice(m, 20, replace=False),
+                                     rng.choice(np.arange(first_far, m), 10, replace=False)]))
+    x_host = x.cpu()
+    xa = np.float32(x_host.abs().max().float().item())
+    xn = x_host[torch.from_numpy(toks)].float().numpy()
+    del x_host, x
+    wn = w.cpu().numpy()
+    bits, _ = O.select_weight_mask(wn, 0.2)
+    wq = O.quantize_weight(wn, O.pack_nibbles(bits), tensor_amax=np.abs(wn).max())
+    for level, xp in ((4, xp4), (6, xp6)):
+        say(f"level {level}")
+        y = A.gemm(wp, xp, bits=level)
+        ys = y[torch.from_numpy(toks).to(DEV)].cpu().numpy()
+        del y
+        xq = O.quantize_activation(xn, refine=(level == 6), exclude_mask=wq["mask"], tensor_amax=xa)
+        e = check_close(ys, O.linear(wq, xq, level))
+        say(f"level {level}: max rel err {e:.2e}")
+    del xp4, xp6
+    torch.cuda.empty_cache()
+
+
+def _budget_mask(k, R, seed):
+    """A valid weight mask chosen by the test: R refined subgroups spread at
+    random over the 16-element groups, at most two per group (returned as one
+    4-bit value per group). GEMV parity does not depend on how M_W was
+    selected; the selection has tests of its own."""
+    rng = np.random.default_rng(seed)
+    G = k // 16
+    nib = np.zeros(G, np.uint8)
+    for slot in rng.permutation(2 * G)[:R]:
+        g = slot // 2
+        free = [b for b in range(4) if not (int(nib[g]) >> b) & 1]
+        nib[g] |= np.uint8(1 << int(rng.choice(free)))
+    return nib
+
+
+@pytest.mark.parametrize("b", [16, 64])
+def test_full_size_70b_gemv_level6(b):
+    """The 70B-shaped projection (28672 x 8192) at 16 and 64 tokens, level 6
+    (the 64-token tile refines both operands): every output of 64 sampled
+    weight rows, the first and last among them, against the oracle."""
+    n, k = 28672, 8192
+    say(f"case: full-size 70B GEMV {n}x{k} batch {b}, level 6")
+    w = S.weights(n, k, seed=3, tensor_id=70, device=DEV)
+    x = S.activations(b, k, seed=3, tensor_id=71, device=DEV)
+    R = A.weight_refined_count(k)
+    nib = _budget_mask(k, R, seed=6)
+    assert sum(bin(int(v)).count("1") for v in nib) == R
+    mask_np = O.pack_nibbles(nib)
+    mask = torch.from_numpy(mask_np).to(DEV)
+    wp = A.quantize(w, N.WEIGHT, weight_mask=mask, n_refined=R)
+    xp6 = A.quantize_activation(x, refine=True, exclude_mask=mask)
+    rows = np.concatenate([[0, n - 1], np.random.default_rng(5).choice(np.arange(1, n - 1), 62, replace=False)])
+    wn = w.cpu().numpy()
+    wq = O.quantize_weight(wn[rows], mask_np, tensor_amax=np.abs(wn).max())
+    xq6 = O.quantize_activation(x.float().cpu().numpy(), refine=True, exclude_mask=mask_np)
+    del w, wn
+    y = A.gemv(wp, xp6, bits=6).cpu().numpy()
+    e = check_close(y[:, rows], O.linear(wq, xq6, 6))
+    say(f"max rel err {e:.2e}")
 
 
 def _all_scale_codes_weight(n, k, seed):

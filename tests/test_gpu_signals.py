@@ -49,6 +49,28 @@ def test_entropy_ties_and_extremes():
     assert abs(float(g[0]) - 1.0) < 1e-6 and float(g[1]) < 1e-6
 
 
+@pytest.mark.parametrize("top_k", [10, 32, None])
+def test_entropy_masked_logits(top_k):
+    """Vocabulary entries masked with -inf (probability 0): a row with fewer
+    finite logits than top_k, one with a single finite logit, and one with the
+    finite logits spread over many slices. G_E stays finite and equals the
+    oracle's, which drops zero-probability terms."""
+    V = S.VOCAB
+    k = V if top_k is None else top_k
+    say(f"case: entropy with -inf masked logits k={k}")
+    z = torch.full((4, V), float("-inf"), device=DEV)
+    z[0, [5, 900, 70000, V - 1]] = torch.tensor([1.0, 2.0, 0.5, 1.5], device=DEV)   # 4 finite
+    z[1, 12345] = 3.0                                                                # 1 finite
+    z[2, ::37] = S.logits(1, V, seed=5, device=DEV)[0, ::37]                        # 3467 finite
+    z[3] = S.logits(1, V, seed=6, device=DEV)[0]
+    z[3, 1000:50000] = float("-inf")
+    g, _ = A.policy_signals(logits=z, params=A.default_params(top_k=k))
+    gn = g.cpu().numpy()
+    assert np.isfinite(gn).all(), gn
+    close(gn, O.topk_entropy(z.cpu().numpy(), k))
+    assert abs(float(gn[1])) < 1e-6
+
+
 @pytest.mark.parametrize("top_k", [10, 32])
 def test_entropy_leaders_in_one_place(top_k):
     """All leaders in the 16 logits one thread reads, or in the last, partial slice."""
