@@ -136,7 +136,7 @@ def build_pool(A, S, n_layers, device):
 class DecodeBench:
     def __init__(self, A, S, pool, batch, device):
         import torch
-        self.A, self.pool, self.b = A, pool, batch
+        self.A, self.pool, self.b, self.device = A, pool, batch, device
         self.p = A.default_params()
         self.x_in = {name: S.activations(batch, k, seed=7, tensor_id=j, outlier_frac=0.0, device=device)
                      for j, (name, n, k) in enumerate(SHAPES)}
@@ -154,6 +154,7 @@ class DecodeBench:
         self.state = A.policy_state(batch, device)
         self.bits_rows = torch.zeros(batch, dtype=torch.int32, device=device)
         self.bits_layer = torch.zeros(1, dtype=torch.int32, device=device)
+        self._chain_buffers(S)
         # activations encoded once per level for the GEMV-only timing
         self.xq_l = {}
         for name, n, k in SHAPES:
@@ -166,24 +167,109 @@ class DecodeBench:
         P = len(self.pool)
         return [self.pool[(len(LEVELS) * s + j) % P] for j in range(len(LEVELS))]
 
+    def _chain_buffers(self, S):
+        """Buffers of the chained step: the hidden state (ping-pong), the
+        linear outputs z, the encoded input of each linear."""
+        import torch
+        if hasattr(self, "z"):
+            return
+        A, b, dev = self.A, self.b, self.device
+        H = S.HIDDEN
+        self.h0 = S.hidden(b, H, seed=7, tensor_id=0, device=dev)
+        self.hbuf = [torch.empty(b, H, device=dev) for _ in range(2)]
+        self.h1 = torch.empty(b, H, device=dev)
+        self.z = {name: torch.empty(b, n, dtype=torch.float32, device=dev) for name, n, k in SHAPES}
+        self.f = torch.empty(b, S.FFN, device=dev)
+        self.a = torch.empty(b, H, device=dev)
+
     def step(self, s):
+        """One decode step with the layers chained and each linear's output
+        post-processed into the next linear's input in one call
+        (autofp_epilogue_quantize: copy / residual add / SwiGLU, then the
+        encode): G_E, then per layer GEMV Wqkv -> copy of the first 4096
+        outputs -> GEMV Wo -> h1 = h + o -> GEMV Wgate|Wup -> silu(g) * u ->
+        GEMV Wdown -> h2 = h1 + d, encoded for the next layer -> L_A and the
+        policy update."""
         A, p = self.A, self.p
         A.policy_signals(logits=self.logits, out_entropy=self.g_e, params=p, workspace=self.sws)
-        for j, (layer, level) in enumerate(zip(self.layers_of(s), LEVELS)):
-            for name, n, k in SHAPES:
-                wp = layer[name]
-                A.quantize_into(self.x_in[name], self.xq[name], refine=(level == 6),
-                                exclude_mask=wp.mask, workspace=self.qws[k], params=p)
-                A.gemv(wp, self.xq[name], bits=level, out=self.y[name], workspace=self.gws[k], params=p)
-            A.policy_layer(1, j, self.h_prev, self.h_cur, self.state, g_e=self.g_e, l_a=self.l_a,
+        layers = self.layers_of(s)
+        h_in = self.h0
+        A.quantize_into(h_in, self.xq["wqkv"], refine=True, exclude_mask=layers[0]["wqkv"].mask,
+                        workspace=self.qws[4096], params=p)
+        for j, (layer, level) in enumerate(zip(layers, LEVELS)):
+            h_out = self.hbuf[j % 2]
+            nxt = layers[j + 1] if j + 1 < len(layers) else layers[0]
+            g = lambda name, k: A.gemv(layer[name], self.xq[name], bits=level, out=self.z[name],
+                                       workspace=self.gws[k], params=p)
+            g("wqkv", 4096)
+            A.epilogue_quantize("copy", self.z["wqkv"], self.xq["wo"], refine=True, exclude_mask=layer["wo"].mask,
+                                workspace=self.qws[4096], params=p)
+            g("wo", 4096)
+            A.epilogue_quantize("residual", self.z["wo"], self.xq["wgateup"], residual=h_in, v_out=self.h1,
+                                refine=True, exclude_mask=layer["wgateup"].mask, workspace=self.qws[4096], params=p)
+            g("wgateup", 4096)
+            A.epilogue_quantize("swiglu", self.z["wgateup"], self.xq["wdown"], refine=True,
+                                exclude_mask=layer["wdown"].mask, workspace=self.qws[14336], params=p)
+            g("wdown", 14336)
+            A.epilogue_quantize("residual", self.z["wdown"], self.xq["wqkv"], residual=self.h1, v_out=h_out,
+                                refine=True, exclude_mask=nxt["wqkv"].mask, workspace=self.qws[4096], params=p)
+            A.policy_layer(1, j, h_in, h_out, self.state, g_e=self.g_e, l_a=self.l_a,
                            bits_rows=self.bits_rows, bits_layer=self.bits_layer, params=p)
+            h_in = h_out
+
+    def step_unfused(self, s):
+        """The same chained step with the elementwise steps as separate torch
+        kernels and a separate encode launch per linear input (no producer
+        epilogue): the comparison for the fused form."""
+        import torch
+        A, p = self.A, self.p
+        A.policy_signals(logits=self.logits, out_entropy=self.g_e, params=p, workspace=self.sws)
+        layers = self.layers_of(s)
+        h_in = self.h0
+        A.quantize_into(h_in, self.xq["wqkv"], refine=True, exclude_mask=layers[0]["wqkv"].mask,
+                        workspace=self.qws[4096], params=p)
+        for j, (layer, level) in enumerate(zip(layers, LEVELS)):
+            h_out = self.hbuf[j % 2]
+            nxt = layers[j + 1] if j + 1 < len(layers) else layers[0]
+            g = lambda name, k: A.gemv(layer[name], self.xq[name], bits=level, out=self.z[name],
+                                       workspace=self.gws[k], params=p)
+            g("wqkv", 4096)
+            self.a.copy_(self.z["wqkv"][:, :4096])
+            A.quantize_into(self.a, self.xq["wo"], refine=True, exclude_mask=layer["wo"].mask,
+                            workspace=self.qws[4096], params=p)
+            g("wo", 4096)
+            torch.add(h_in, self.z["wo"], out=self.h1)
+            A.quantize_into(self.h1, self.xq["wgateup"], refine=True, exclude_mask=layer["wgateup"].mask,
+                            workspace=self.qws[4096], params=p)
+            g("wgateup", 4096)
+            silu_mul(self.z["wgateup"], 14336, self.f)
+            A.quantize_into(self.f, self.xq["wdown"], refine=True, exclude_mask=layer["wdown"].mask,
+                            workspace=self.qws[14336], params=p)
+            g("wdown", 14336)
+            torch.add(self.h1, self.z["wdown"], out=h_out)
+            A.quantize_into(h_out, self.xq["wqkv"], refine=True, exclude_mask=nxt["wqkv"].mask,
+                            workspace=self.qws[4096], params=p)
+            A.policy_layer(1, j, h_in, h_out, self.state, g_e=self.g_e, l_a=self.l_a,
+                           bits_rows=self.bits_rows, bits_layer=self.bits_layer, params=p)
+            h_in = h_out
 
     def step_bytes(self):
-        b = self.b
-        tot = 4 * b * 128256 + 2 * 4 * b * 4096 * len(LEVELS)     # logits, h_prev/h_cur per layer
+        """Algorithmic bytes of the chained step: logits; the first encode (fp32
+        hidden in, packed out); per layer the four GEMVs (packed weight at the
+        layer's level, packed activation, fp32 output) and the four epilogues
+        (fp32 inputs read: the copied 4096 outputs, residual + output, both
+        SwiGLU halves; fp32 hidden states written by the residual steps;
+        the refined packed activation written); L_A reads h and h2."""
+        b, H, F = self.b, 4096, 14336
+        tot = 4 * b * 128256 + 4 * b * H + x_bytes(b, H, 6)
         for layer, level in zip(self.layers_of(0), LEVELS):
             for name, n, k in SHAPES:
-                tot += encode_bytes(b, k, level) + gemv_bytes(layer[name], b, level)
+                tot += gemv_bytes(layer[name], b, level)
+            tot += 4 * b * H + x_bytes(b, H, 6)                     # copy
+            tot += 3 * 4 * b * H + x_bytes(b, H, 6)                 # residual (z, h read; h1 written)
+            tot += 2 * 4 * b * F + x_bytes(b, F, 6)                 # SwiGLU
+            tot += 3 * 4 * b * H + x_bytes(b, H, 6)                 # residual (z, h1 read; h2 written)
+            tot += 2 * 4 * b * H                                    # L_A
         return tot
 
     def gemv_only(self, s):
@@ -202,13 +288,14 @@ class DecodeBench:
 
 class Step32:
     """The full decode step of a 32-layer Llama-3-8B-shaped model under the
-    device-side policy: G_E of the step's logits, then per layer the encode
-    of each linear input, a = Wqkv h (first 4096 outputs as the attention
-    stand-in), o = Wo a, h1 = h + o, [g|u] = Wgate|Wup h1, f = silu(g) * u,
-    h2 = h1 + Wdown f, L_A(h, h2) and the policy update, whose level the next
-    layer's GEMVs read on the device. Several consecutive steps (logits drawn
-    per step) form one HIP graph; the levels chosen are logged on the device
-    and read back after timing."""
+    device-side policy: G_E of the step's logits, then per layer
+    a = Wqkv h (first 4096 outputs as the attention stand-in), o = Wo a,
+    h1 = h + o, [g|u] = Wgate|Wup h1, f = silu(g) * u, h2 = h1 + Wdown f, each
+    linear's output turned into the next linear's encoded input by one
+    producer-epilogue call, then L_A(h, h2) and the policy update, whose level
+    the next layer's GEMVs read on the device. Several consecutive steps
+    (logits drawn per step) form one HIP graph; the levels chosen are logged
+    on the device and read back after timing."""
 
     def __init__(self, A, S, layers, batch, device, steps=4):
         import torch
@@ -218,18 +305,18 @@ class Step32:
         L = len(layers)
         self.h0 = S.hidden(batch, H, seed=41, tensor_id=0, dtype=torch.float32, device=device)
         self.logits = [S.logits(batch, V, seed=42 + s, device=device) for s in range(steps)]
-        self.xh = A.alloc_activation(batch, H, refine=True, device=device)
-        self.xf = A.alloc_activation(batch, F, refine=True, device=device)
+        # odd steps have one dominant next token (G_E near 0, below tau): the
+        # low-entropy regime of the policy, where lower levels are reached
+        for s in range(1, steps, 2):
+            self.logits[s][:, 17] += 25.0
+        self.xq = {name: A.alloc_activation(batch, k, refine=True, device=device) for name, n, k in SHAPES}
         self.qws = {k: torch.empty(A.workspace_bytes(0, batch, k), dtype=torch.uint8, device=device) for k in (H, F)}
         self.gws = {k: torch.empty(A.workspace_bytes(2, batch, k), dtype=torch.uint8, device=device) for k in (H, F)}
         self.sws = torch.empty(A.workspace_bytes(4, batch, V), dtype=torch.uint8, device=device)
         self.y = {"wqkv": torch.empty(batch, 3 * 2048, device=device), "wo": torch.empty(batch, H, device=device),
                   "wgateup": torch.empty(batch, 2 * F, device=device), "wdown": torch.empty(batch, H, device=device)}
-        self.h = torch.empty(batch, H, device=device)
+        self.hb = [torch.empty(batch, H, device=device) for _ in range(2)]
         self.h1 = torch.empty(batch, H, device=device)
-        self.h2 = torch.empty(batch, H, device=device)
-        self.a = torch.empty(batch, H, device=device)
-        self.f = torch.empty(batch, F, device=device)
         self.g_e = torch.empty(batch, device=device)
         self.l_a = torch.empty(batch, device=device)
         self.rows = torch.empty(batch, dtype=torch.int32, device=device)
@@ -241,39 +328,46 @@ class Step32:
         for s in range(self.T):
             lay = self.lay[s]
             A.policy_signals(logits=self.logits[s], out_entropy=self.g_e, workspace=self.sws)
-            self.h.copy_(self.h0)
             lay[0].fill_(4)                                   # a decode step starts at 4 bits
+            h_in = self.h0
+            A.quantize_into(h_in, self.xq["wqkv"], refine=True, exclude_mask=self.layers[0]["wqkv"].mask,
+                            workspace=self.qws[self.H])
             for i, w in enumerate(self.layers):
                 bits = lay[i:i + 1]
-                A.quantize_into(self.h, self.xh, refine=True, exclude_mask=w["wqkv"].mask, workspace=self.qws[self.H])
-                A.gemv(w["wqkv"], self.xh, bits_dev=bits, out=self.y["wqkv"], workspace=self.gws[self.H])
-                self.a.copy_(self.y["wqkv"][:, :self.H])
-                A.quantize_into(self.a, self.xh, refine=True, exclude_mask=w["wo"].mask, workspace=self.qws[self.H])
-                A.gemv(w["wo"], self.xh, bits_dev=bits, out=self.y["wo"], workspace=self.gws[self.H])
-                torch_add(self.h, self.y["wo"], self.h1)
-                A.quantize_into(self.h1, self.xh, refine=True, exclude_mask=w["wgateup"].mask,
-                                workspace=self.qws[self.H])
-                A.gemv(w["wgateup"], self.xh, bits_dev=bits, out=self.y["wgateup"], workspace=self.gws[self.H])
-                silu_mul(self.y["wgateup"], self.F, self.f)
-                A.quantize_into(self.f, self.xf, refine=True, exclude_mask=w["wdown"].mask, workspace=self.qws[self.F])
-                A.gemv(w["wdown"], self.xf, bits_dev=bits, out=self.y["wdown"], workspace=self.gws[self.F])
-                torch_add(self.h1, self.y["wdown"], self.h2)
-                A.policy_layer(1, i, self.h, self.h2, self.state, g_e=self.g_e, new_sequence=(s == 0 and i == 0),
+                h_out = self.hb[i % 2]
+                nxt = self.layers[(i + 1) % len(self.layers)]
+                A.gemv(w["wqkv"], self.xq["wqkv"], bits_dev=bits, out=self.y["wqkv"], workspace=self.gws[self.H])
+                A.epilogue_quantize("copy", self.y["wqkv"], self.xq["wo"], refine=True, exclude_mask=w["wo"].mask,
+                                    workspace=self.qws[self.H])
+                A.gemv(w["wo"], self.xq["wo"], bits_dev=bits, out=self.y["wo"], workspace=self.gws[self.H])
+                A.epilogue_quantize("residual", self.y["wo"], self.xq["wgateup"], residual=h_in, v_out=self.h1,
+                                    refine=True, exclude_mask=w["wgateup"].mask, workspace=self.qws[self.H])
+                A.gemv(w["wgateup"], self.xq["wgateup"], bits_dev=bits, out=self.y["wgateup"],
+                       workspace=self.gws[self.H])
+                A.epilogue_quantize("swiglu", self.y["wgateup"], self.xq["wdown"], refine=True,
+                                    exclude_mask=w["wdown"].mask, workspace=self.qws[self.F])
+                A.gemv(w["wdown"], self.xq["wdown"], bits_dev=bits, out=self.y["wdown"], workspace=self.gws[self.F])
+                A.epilogue_quantize("residual", self.y["wdown"], self.xq["wqkv"], residual=self.h1, v_out=h_out,
+                                    refine=True, exclude_mask=nxt["wqkv"].mask, workspace=self.qws[self.H])
+                A.policy_layer(1, i, h_in, h_out, self.state, g_e=self.g_e, new_sequence=(s == 0 and i == 0),
                                l_a=self.l_a, bits_rows=self.rows, bits_layer=lay[i + 1:i + 2])
-                self.h.copy_(self.h2)
+                h_in = h_out
 
     def bytes_of(self, lay):
-        """Algorithmic bytes of the logged steps: packed weights at the level
-        each layer ran, the encoded activations (fp32 in, packed out), GEMV
-        outputs, the logits and the L_A reads."""
-        b, tot = self.b, 0
+        """Algorithmic bytes of the logged steps: logits; per step the first
+        encode; per layer the packed weights at the level the layer ran, its
+        packed activations and fp32 outputs, the four producer epilogues (fp32
+        reads and writes, the refined packed activation written) and the L_A
+        reads."""
+        b, H, F, tot = self.b, self.H, self.F, 0
         for s in range(self.T):
-            tot += 4 * b * self.V
+            tot += 4 * b * self.V + 4 * b * H + x_bytes(b, H, 6)
             for i, w in enumerate(self.layers):
                 L = int(lay[s][i])
                 for name, wp in w.items():
-                    tot += 4 * b * wp.k + gemv_bytes(wp, b, L)
-                tot += 2 * 4 * b * self.H
+                    tot += gemv_bytes(wp, b, L)
+                tot += 4 * b * H + 2 * (3 * 4 * b * H) + 2 * 4 * b * F
+                tot += 3 * x_bytes(b, H, 6) + x_bytes(b, F, 6) + 2 * 4 * b * H
         return tot
 
 
@@ -549,6 +643,10 @@ def main():
     step_bytes = bench.step_bytes()
     value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"step: {ms_step:.4f} ms, {step_bytes / 1e6:.1f} MB, {value:.1f} GB/s")
+    ugraphs = capture([lambda s=s: bench.step_unfused(s) for s in range(G)])
+    ms_unf = time_graphs(ugraphs, args.steps, args.warmup)
+    del ugraphs
+    log(f"same step without the producer epilogue: {ms_unf:.4f} ms")
 
     # roofline of the GEMV kernel: GEMV-only graphs, same weights and levels
     ggraphs = capture([lambda s=s: bench.gemv_only(s) for s in range(G)])
@@ -563,7 +661,9 @@ def main():
                 "bytes_per_launch": int(g_bytes / n_launch)}
     log(f"gemv-only: {ms_g:.4f} ms per {n_launch} launches, {achieved:.1f} GB/s")
 
-    extra = {}
+    extra = {"step_unfused": {"ms": round(ms_unf, 5), "gbs": round(step_bytes / (ms_unf * 1e-3) / 1e9, 1),
+                              "note": "the same chained step with torch elementwise kernels and a separate "
+                                      "encode per linear input instead of autofp_epilogue_quantize"}}
     if not args.no_breakdown:
         br = {}
         for name, n, k in SHAPES:
@@ -627,8 +727,10 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "AutoFP decode step over Llama-3-8B-shaped layers (Wqkv 6144x4096, Wo 4096x4096, "
-                        "Wgate|Wup 28672x4096, Wdown 4096x14336): G_E over 128256 logits, then 3 layers at "
-                        "levels 2/4/6, each with online activation encode, 4 GEMVs, L_A and the policy update",
+                        "Wgate|Wup 28672x4096, Wdown 4096x14336): G_E over 128256 logits, then 3 chained layers "
+                        "at levels 2/4/6, each: 4 GEMVs, each output post-processed into the next input by one "
+                        "producer-epilogue call (copy / residual / SwiGLU + AutoFP encode), L_A and the policy "
+                        "update",
             "batch": args.batch,
             "pool_layers": args.pool_layers,
             "pool_bytes": int(pool_bytes),

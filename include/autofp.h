@@ -194,6 +194,34 @@ autofp_status autofp_quantize(const void *x, int32_t x_dtype, int32_t refine,
                               autofp_packed *out, void *workspace, size_t workspace_bytes,
                               void *stream);
 
+/* Elementwise step between a linear layer's output and the next layer's input
+ * (autofp_epilogue_quantize). */
+typedef enum {
+  AUTOFP_EPI_COPY = 1,      /* v = z[:, :k]                                   */
+  AUTOFP_EPI_RESIDUAL = 2,  /* v = residual + z[:, :k]                        */
+  AUTOFP_EPI_SWIGLU = 3     /* v = silu(z[:, :k]) * z[:, k:2k], silu(g) = g / (1 + e^-g) */
+} autofp_epilogue_op;
+
+/*
+ * Producer epilogue: the post-processing of a completed linear output into
+ * the next layer's input activation ([AE] §6.4, "Shared Post-Processing
+ * Unit": completed outputs are quantized into the next layer's activations,
+ * with the NMSE refinement outside M_W and the non-linear operations). From
+ * z [out->rows][ldz] fp32 (a linear layer's output, e.g. from autofp_gemv)
+ * it forms v [out->rows][out->k] in fp32 with `op`, writes v to v_out (may be
+ * NULL) and encodes v into `out` exactly as autofp_quantize would encode v
+ * (same arguments refine / exclude_mask / p, same results bit for bit). One
+ * launch for out->rows * out->k <= 16384 elements, two above. COPY and
+ * RESIDUAL need ldz >= k, SWIGLU ldz >= 2k; residual [rows][k] fp32 (RESIDUAL
+ * only). z, residual, v_out 16-byte aligned, ldz % 4 == 0. Workspace as
+ * autofp_quantize (AUTOFP_OP_QUANTIZE, rows, k); out->kind ACTIVATION.
+ * Errors: NULL, SHAPE, KIND, ARG, WORKSPACE, MISSING_REFINEMENT, HIP.
+ */
+autofp_status autofp_epilogue_quantize(int32_t op, const float *z, int64_t ldz, const float *residual,
+                                       float *v_out, int32_t refine, const uint8_t *exclude_mask,
+                                       const autofp_params *p, autofp_packed *out, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
 /*
  * Decode-phase linear layer ([AE] §3.1-3.2, §4): for b < x->rows, n < w->rows
  *   y[b][n] = sum_k What[n][k] * Xhat[b][k]
@@ -216,6 +244,28 @@ autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_
                           const int32_t *bits_dev, void *y, int32_t y_dtype,
                           const autofp_params *p, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/*
+ * Decode-phase linear layer for a batch whose rows (tokens) run at different
+ * precision levels ([AE] §4.2 "Serving Mixed-Precision Batches": requests of
+ * one batch that chose different levels share one GEMM over the union of
+ * their refinements, Fig. 6; the levels come from the policy per request,
+ * §3.1 and autofp_policy_update's bits_rows):
+ *   y[b][n] = sum_k What_l[n][k] * Xhat_l[b][k],  l = bits_rows[b] in {2, 4, 6}
+ * with the operands of level l as in autofp_gemv (row b at level 6 uses its
+ * own activation refinement M_A and the weight refinement M_W; at 4 plain
+ * NVFP4; at 2 the AutoFP2 weight digits times the NVFP4 activation). Each row
+ * equals the row autofp_gemv gives at that row's level. bits_rows [x->rows]
+ * int32 (device, read when the kernels run); a value outside {2, 4, 6} gives
+ * a zero row. Any row may be at level 6, so both operands must carry their
+ * refinement (weight mask and offsets; activation mask and offsets).
+ * k % 128 == 0 and k <= 2^22; any number of rows (slices of 64). Workspace as
+ * autofp_gemv. Errors: NULL, SHAPE, KIND, MISSING_REFINEMENT, DTYPE,
+ * WORKSPACE, ARG, HIP.
+ */
+autofp_status autofp_gemv_rows(const autofp_packed *w, const autofp_packed *x, const int32_t *bits_rows,
+                               void *y, int32_t y_dtype, const autofp_params *p, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
 /*
  * Prefill-phase linear layer ([AE] §4.1, "Extended-K GEMM": the same product

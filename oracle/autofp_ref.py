@@ -41,6 +41,7 @@ __all__ = [
     "quantize_activation", "quantize_weight", "select_weight_mask",
     "decode_activation", "decode_weight", "linear",
     "topk_entropy", "update_norm", "PolicyState", "policy_prefill", "policy_decode_step",
+    "silu", "epilogue",
 ]
 
 # [AE] App. B.1: 16 contiguous elements along the reduction dimension share one
@@ -489,6 +490,36 @@ def linear(wpk, xpk, level, c2=2.0):
     X = decode_activation(xpk, a_level)
     W = decode_weight(wpk, level, c2)
     return X @ W.T
+
+
+# ----------------------------------------------------------------------------
+# Producer epilogue (the layer's elementwise step before the next encode)
+# ----------------------------------------------------------------------------
+
+def silu(g):
+    """silu(g) = g / (1 + e^-g) = g * sigmoid(g), fp64."""
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(-g))
+
+
+def epilogue(op, z, k, residual=None):
+    """The elementwise step the post-processing unit applies to a completed
+    linear output before quantizing it into the next layer's activation
+    ([AE] §6.4: the PPU quantizes completed outputs into the next layer's
+    input activations and performs the non-linear operations). fp64:
+      "copy"     v = z[:, :k]
+      "residual" v = residual + z[:, :k]
+      "swiglu"   v = silu(z[:, :k]) * z[:, k:2k]
+    Reading: the pages name no model; these are the residual stream and the
+    gated MLP of the Llama-shaped layers the workloads use."""
+    z = np.asarray(z, dtype=np.float64)
+    if op == "copy":
+        return z[:, :k].copy()
+    if op == "residual":
+        return np.asarray(residual, dtype=np.float64) + z[:, :k]
+    if op == "swiglu":
+        return silu(z[:, :k]) * z[:, k:2 * k]
+    raise ValueError(op)
 
 
 # ----------------------------------------------------------------------------

@@ -21,8 +21,8 @@ from ._native import AutofpError, NativeLibraryError, Params  # noqa: F401
 __all__ = [
     "AutoFPTensor", "default_params", "packed_bytes", "weight_refined_count", "workspace_bytes",
     "select_weight_mask", "quantize", "quantize_weight", "quantize_activation",
-    "alloc_activation", "quantize_into",
-    "gemv", "gemm", "policy_signals", "policy_state", "policy_update", "AutofpError",
+    "alloc_activation", "quantize_into", "epilogue_quantize",
+    "gemv", "gemv_rows", "gemm", "policy_signals", "policy_state", "policy_update", "AutofpError",
     "NativeLibraryError", "KVCache", "kv_write", "kv_attention",
 ]
 
@@ -194,6 +194,27 @@ def quantize_into(x: torch.Tensor, out: AutoFPTensor, refine=False, exclude_mask
     return out
 
 
+def epilogue_quantize(op, z: torch.Tensor, out: AutoFPTensor, residual=None, v_out=None, refine=False,
+                      exclude_mask=None, workspace=None, params=None, stream=None) -> AutoFPTensor:
+    """autofp_epilogue_quantize: v = op(z) (``"copy"``: the first out.k columns
+    of z; ``"residual"``: residual + z; ``"swiglu"``: silu(z[:, :k]) *
+    z[:, k:2k]) in fp32, written to ``v_out`` when given, and encoded into
+    ``out`` as autofp_quantize encodes v."""
+    ops = {"copy": N.EPI_COPY, "residual": N.EPI_RESIDUAL, "swiglu": N.EPI_SWIGLU}
+    _dev_check(residual, v_out, exclude_mask)
+    if z.dtype != torch.float32 or z.dim() != 2 or z.stride(1) != 1 or z.shape[0] != out.rows:
+        raise ValueError("z must be a 2-D float32 tensor with unit column stride and out.rows rows")
+    p = params or default_params()
+    if workspace is None:
+        workspace = _workspace(N.OP_QUANTIZE, out.rows, out.k, z.device)
+    st = out.struct()
+    N.check(N.lib().autofp_epilogue_quantize(ops[op], _ptr(z), z.stride(0), _ptr(residual), _ptr(v_out),
+                                             int(bool(refine)), _ptr(exclude_mask), C.byref(p), C.byref(st),
+                                             _ptr(workspace), workspace.numel(), _stream(stream)),
+            "autofp_epilogue_quantize")
+    return out
+
+
 def quantize_weight(w: torch.Tensor, refine=True, params=None, stream=None) -> AutoFPTensor:
     """Offline weight packing: M_W selection (when ``refine``) and encode."""
     if refine:
@@ -228,6 +249,25 @@ def gemv(w: AutoFPTensor, x: AutoFPTensor, bits=4, bits_dev=None, out_dtype=torc
     """y = Xhat . What^T at level ``bits`` (decode path, autofp_gemv)."""
     return _linear(N.lib().autofp_gemv, "autofp_gemv", w, x, bits, bits_dev, out_dtype, params,
                    workspace, out, stream)
+
+
+def gemv_rows(w: AutoFPTensor, x: AutoFPTensor, bits_rows: torch.Tensor, out_dtype=torch.float32,
+              params=None, workspace=None, out=None, stream=None) -> torch.Tensor:
+    """y = Xhat . What^T with row b at level ``bits_rows[b]`` (int32 device
+    tensor of 2/4/6 per token; autofp_gemv_rows)."""
+    _dev_check(bits_rows)
+    if bits_rows.dtype != torch.int32 or bits_rows.numel() != x.rows:
+        raise ValueError("bits_rows must be int32 with one level per activation row")
+    p = params or default_params()
+    if out is None:
+        out = torch.empty(x.rows, w.rows, dtype=out_dtype, device=w.codes.device)
+    if workspace is None:
+        workspace = _workspace(N.OP_GEMV, x.rows, x.k, w.codes.device)
+    ws_, xs_ = w.struct(), x.struct()
+    N.check(N.lib().autofp_gemv_rows(C.byref(ws_), C.byref(xs_), _ptr(bits_rows), _ptr(out), _DT[out.dtype],
+                                     C.byref(p), _ptr(workspace), workspace.numel(), _stream(stream)),
+            "autofp_gemv_rows")
+    return out
 
 
 def gemm(w: AutoFPTensor, x: AutoFPTensor, bits=4, bits_dev=None, out_dtype=torch.float32,

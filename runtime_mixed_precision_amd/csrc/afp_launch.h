@@ -46,12 +46,22 @@ struct EncodeArgs {
   const int32_t *w_prefix;      // mask prefix table
   int32_t n_refined;
   uint8_t *w_offsets;           // [rows][n_refined]
+  // producer epilogue (op != 0): the encoded tensor is v = op(z, resid),
+  // [rows][k], computed on the fly from z [rows][ldz] fp32 (x is unused) and
+  // written to v_out when non-null. Ops: autofp_epilogue_op.
+  int op;
+  const float *z;
+  int64_t ldz;
+  const float *resid;           // [rows][k] (residual op)
+  float *v_out;                 // [rows][k] or null
 };
 // small: every block takes the amax of the whole tensor itself (one launch,
 // for rows * k <= kSmallEncode; a.partial is not read); otherwise a.partial
 // holds the amax partials of launch_amax_partial.
 constexpr int64_t kSmallEncode = 1 << 14;
 hipError_t launch_encode(const EncodeArgs &a, bool small, hipStream_t s);
+// The partial maxima of the epilogue tensor v = op(z, resid) of a.
+hipError_t launch_amax_partial_op(const EncodeArgs &a, float *partial, int n_partial, hipStream_t s);
 
 // Weight-mask selection ([AE] App. E, Alg. 1 allocation with H = I).
 hipError_t launch_select_mask(const float *w, int64_t rows, int64_t k, int32_t budget,
@@ -83,6 +93,11 @@ struct LinearArgs {
   _Float16 *xh;                 // dequantized activations [b][kpad]
   int64_t kpad;
   int32_t *prefix;              // weight-mask prefix table (GEMM)
+  // per-token levels ([b] int32 device, 2/4/6) or null: one level for the call
+  const int32_t *bits_rows;
+  // batched GEMV: fp32 partial tiles of the K splits ([splits][b][n]) and their count
+  float *part;
+  int32_t splits;
 };
 int64_t xh_kpad(int64_t k);
 hipError_t launch_act_dequant(const LinearArgs &a, hipStream_t s);
@@ -90,6 +105,14 @@ bool gemv_needs_panel(const LinearArgs &a);   // true when the GEMV reads the fp
 bool gemv_small_m_route(const LinearArgs &a);   // 17-64 tokens on the 64-token GEMM tile
 bool gemv_panel_packed(const LinearArgs &a);    // 17+ tokens: panel kernel on packed activations
 hipError_t launch_gemv(const LinearArgs &a, hipStream_t s);
+
+// ---- gemv_batch.hip ----
+// Batched decode GEMV, 17-64 tokens per slice (and every call with per-token
+// levels): K % 128 == 0. Reads a.prefix at level 6 (or a device/per-token
+// level) and a.part when the K range is split.
+bool gemv_batch_ok(const LinearArgs &a);
+int64_t gemv_batch_part_floats(int64_t tokens);   // floats of a.part the launcher may use
+hipError_t launch_gemv_batch(const LinearArgs &a, hipStream_t s);
 
 // ---- gemm.hip ----
 hipError_t launch_gemm(const LinearArgs &a, hipStream_t s);

@@ -11,7 +11,6 @@ using namespace afp;
 static_assert(sizeof(autofp_policy_state) == 48, "policy state layout");
 static_assert(sizeof(autofp_params) == 56, "params layout");
 
-
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -54,9 +53,12 @@ size_t ws_select(int64_t rows, int64_t k) {
          align_up(sizeof(double) * (ncol + 2 * ng) + sizeof(int32_t) * 4 * ng);
 }
 
+// fp16 activation panel, weight-mask prefix table, split-K partial tiles of
+// the batched GEMV
 size_t ws_linear(int64_t tokens, int64_t k) {
   return align_up(sizeof(_Float16) * (size_t)tokens * (size_t)xh_kpad(k)) +
-         align_up(sizeof(int32_t) * (mask_bytes(k) + 1));
+         align_up(sizeof(int32_t) * (mask_bytes(k) + 1)) +
+         align_up(sizeof(float) * (size_t)gemv_batch_part_floats(tokens));
 }
 
 size_t ws_kv_write() { return 2 * align_up(sizeof(float) * kAmaxBlocks); }
@@ -134,6 +136,9 @@ autofp_status linear_common(const autofp_packed *w, const autofp_packed *x, int3
   a.kpad = xh_kpad(x->k);
   a.xh = (_Float16 *)ws;
   a.prefix = (int32_t *)((char *)ws + align_up(sizeof(_Float16) * (size_t)x->rows * (size_t)a.kpad));
+  a.part = (float *)((char *)a.prefix + align_up(sizeof(int32_t) * (mask_bytes(x->k) + 1)));
+  a.splits = 1;
+  a.bits_rows = nullptr;
   return AUTOFP_OK;
 }
 
@@ -161,9 +166,11 @@ autofp_status check_quantize(const void *x, int32_t x_dtype, int32_t refine, con
 }
 
 // The encode's launches on scratch `ws` (ws_quantize bytes: amax partials,
-// then the weight-mask prefix table); arguments already checked.
+// then the weight-mask prefix table); arguments already checked. `epi`
+// (op != 0) encodes the producer epilogue's v instead of x.
 autofp_status launch_quantize(const void *x, int32_t x_dtype, int32_t refine, const uint8_t *exclude_mask,
-                              const autofp_params *p, const autofp_packed *out, void *ws, hipStream_t s) {
+                              const autofp_params *p, const autofp_packed *out, void *ws, hipStream_t s,
+                              const EncodeArgs *epi = nullptr) {
   const autofp_params pp = params_or_default(p);
   const bool act_refine = out->kind == AUTOFP_ACTIVATION && refine;
   const bool w_refine = out->kind == AUTOFP_WEIGHT && out->mask != nullptr;
@@ -172,20 +179,27 @@ autofp_status launch_quantize(const void *x, int32_t x_dtype, int32_t refine, co
   const int64_t n = out->rows * out->k;
   const bool small = n <= kSmallEncode;
   const int np = amax_partial_count(n);
+  EncodeArgs a{};
+  if (epi) {
+    a.op = epi->op;
+    a.z = epi->z;
+    a.ldz = epi->ldz;
+    a.resid = epi->resid;
+    a.v_out = epi->v_out;
+  }
+  a.rows = out->rows;
+  a.k = out->k;
   hipError_t e = hipSuccess;
   if (!small) {
-    e = launch_amax_partial(x, x_dtype, n, partial, np, s);
+    e = a.op ? launch_amax_partial_op(a, partial, np, s) : launch_amax_partial(x, x_dtype, n, partial, np, s);
     if (e != hipSuccess) return AUTOFP_ERR_HIP;
   }
   if (w_refine) {
     e = launch_mask_prefix(out->mask, mask_bytes(out->k), prefix, s);
     if (e != hipSuccess) return AUTOFP_ERR_HIP;
   }
-  EncodeArgs a{};
   a.x = x;
   a.dtype = x_dtype;
-  a.rows = out->rows;
-  a.k = out->k;
   a.partial = partial;
   a.n_partial = np;
   a.codes = out->codes;
@@ -202,7 +216,6 @@ autofp_status launch_quantize(const void *x, int32_t x_dtype, int32_t refine, co
   a.w_offsets = out->offsets;
   return from_hip(launch_encode(a, small, s));
 }
-
 
 }  // namespace
 
@@ -336,6 +349,30 @@ autofp_status autofp_quantize(const void *x, int32_t x_dtype, int32_t refine,
   return launch_quantize(x, x_dtype, refine, exclude_mask, p, out, workspace, (hipStream_t)stream);
 }
 
+autofp_status autofp_epilogue_quantize(int32_t op, const float *z, int64_t ldz, const float *residual,
+                                       float *v_out, int32_t refine, const uint8_t *exclude_mask,
+                                       const autofp_params *p, autofp_packed *out, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
+  if (!z) return AUTOFP_ERR_NULL;
+  if (op != AUTOFP_EPI_COPY && op != AUTOFP_EPI_RESIDUAL && op != AUTOFP_EPI_SWIGLU) return AUTOFP_ERR_ARG;
+  if (op == AUTOFP_EPI_RESIDUAL && !residual) return AUTOFP_ERR_NULL;
+  // the encode's own checks, with z standing in for the input pointer
+  const autofp_status st = check_quantize(z, AUTOFP_F32, refine, exclude_mask, out);
+  if (st != AUTOFP_OK) return st;
+  if (out->kind != AUTOFP_ACTIVATION) return AUTOFP_ERR_KIND;
+  if (ldz < (op == AUTOFP_EPI_SWIGLU ? 2 : 1) * out->k || (ldz & 3) != 0) return AUTOFP_ERR_SHAPE;
+  if ((residual && !aligned16(residual)) || (v_out && !aligned16(v_out))) return AUTOFP_ERR_ARG;
+  if (!workspace || workspace_bytes < ws_quantize(out->rows, out->k)) return AUTOFP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return AUTOFP_ERR_ARG;
+  EncodeArgs epi{};
+  epi.op = op;
+  epi.z = z;
+  epi.ldz = ldz;
+  epi.resid = op == AUTOFP_EPI_RESIDUAL ? residual : nullptr;
+  epi.v_out = v_out;
+  return launch_quantize(z, AUTOFP_F32, refine, exclude_mask, p, out, workspace, (hipStream_t)stream, &epi);
+}
+
 autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_t bits,
                           const int32_t *bits_dev, void *y, int32_t y_dtype,
                           const autofp_params *p, void *workspace, size_t workspace_bytes,
@@ -350,11 +387,33 @@ autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_
     const hipError_t e = launch_act_dequant(a, s);
     if (e != hipSuccess) return AUTOFP_ERR_HIP;
   }
-  if (gemv_small_m_route(a) && w->mask && (bits_dev || bits == 6)) {
+  if ((gemv_small_m_route(a) || (a.b > 16 && gemv_batch_ok(a))) && w->mask && (bits_dev || bits == 6)) {
     const hipError_t e = launch_mask_prefix(w->mask, mask_bytes(w->k), a.prefix, s);
     if (e != hipSuccess) return AUTOFP_ERR_HIP;
   }
   return from_hip(launch_gemv(a, s));
+}
+
+autofp_status autofp_gemv_rows(const autofp_packed *w, const autofp_packed *x, const int32_t *bits_rows,
+                               void *y, int32_t y_dtype, const autofp_params *p, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  if (!bits_rows) return AUTOFP_ERR_NULL;
+  if (!aligned16(bits_rows)) return AUTOFP_ERR_ARG;
+  LinearArgs a{};
+  // every row may run at level 6: both operands must carry their refinement
+  const autofp_status st =
+      linear_common(w, x, 4, bits_rows, y, y_dtype, p, workspace, workspace_bytes, a);
+  if (st != AUTOFP_OK) return st;
+  if (x->k % 128 != 0) return AUTOFP_ERR_SHAPE;
+  a.bits_dev = nullptr;
+  a.bits_rows = bits_rows;
+  if (!gemv_batch_ok(a)) return AUTOFP_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  if (w->mask) {
+    const hipError_t e = launch_mask_prefix(w->mask, mask_bytes(w->k), a.prefix, s);
+    if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  }
+  return from_hip(launch_gemv_batch(a, s));
 }
 
 autofp_status autofp_gemm(const autofp_packed *w, const autofp_packed *x, int32_t bits,

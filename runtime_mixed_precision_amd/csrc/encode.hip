@@ -29,6 +29,59 @@ __device__ __forceinline__ float load_elem(const void *x, int dtype, int64_t i) 
 }
 
 // ---------------------------------------------------------------------------
+// Producer epilogue ([AE] §6.4: the post-processing unit turns completed
+// outputs into the next layer's input activations, non-linear operations
+// included): four consecutive elements j .. j + 3 of row r of
+//   COPY      v = z[r][j]                         (the first k columns of z)
+//   RESIDUAL  v = resid[r][j] + z[r][j]
+//   SWIGLU    v = silu(z[r][j]) * z[r][k + j],    silu(g) = g / (1 + e^-g)
+// in fp32 (expf, one IEEE division, one product).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float silu_f32(float g) {
+#pragma clang fp contract(off)
+  return g / (1.0f + expf(-g));
+}
+
+__device__ __forceinline__ float4 epilogue4(const EncodeArgs &a, int64_t r, int64_t j) {
+#pragma clang fp contract(off)
+  const float4 zz = *(const float4 *)(a.z + r * a.ldz + j);
+  if (a.op == AUTOFP_EPI_RESIDUAL) {
+    const float4 rr = *(const float4 *)(a.resid + r * a.k + j);
+    return make_float4(rr.x + zz.x, rr.y + zz.y, rr.z + zz.z, rr.w + zz.w);
+  }
+  if (a.op == AUTOFP_EPI_SWIGLU) {
+    const float4 u = *(const float4 *)(a.z + r * a.ldz + a.k + j);
+    return make_float4(silu_f32(zz.x) * u.x, silu_f32(zz.y) * u.y, silu_f32(zz.z) * u.z, silu_f32(zz.w) * u.w);
+  }
+  return zz;
+}
+
+__device__ __forceinline__ float max4(float4 v) {
+  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// |v| maxima of the epilogue tensor, one value per block (grid-stride over
+// the rows x k/4 quads)
+__global__ __launch_bounds__(kThreads) void amax_partial_op_kernel(EncodeArgs a, float *__restrict__ partial) {
+  float m = 0.0f;
+  const int64_t nq = a.k / 4, tot = a.rows * nq;
+  for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < tot; u += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = u / nq;
+    m = fmaxf(m, max4(epilogue4(a, r, 4 * (u - r * nq))));
+  }
+  m = wave_max(m);
+  __shared__ float red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[w]);
+    partial[blockIdx.x] = r;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Tensor scale: partial maxima, then every encode block folds them (no atomics,
 // no zero-initialised scratch, identical T in every block).
 // ---------------------------------------------------------------------------
@@ -244,10 +297,29 @@ __device__ float block_amax_all(const void *x, int dtype, int64_t n) {
   return r;
 }
 
+// amax of the whole epilogue tensor, computed by the block (small tensors)
+__device__ float block_amax_op(const EncodeArgs &a) {
+  float m = 0.0f;
+  const int64_t nq = a.k / 4, tot = a.rows * nq;
+  for (int64_t u = threadIdx.x; u < tot; u += kEncThreads) {
+    const int64_t r = u / nq;
+    m = fmaxf(m, max4(epilogue4(a, r, 4 * (u - r * nq))));
+  }
+  m = wave_max(m);
+  __shared__ float red[kEncThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kEncThreads / 64; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
+
 template <bool SMALL>
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(EncodeArgs a) {
 #pragma clang fp contract(off)
-  const float amax = SMALL ? block_amax_all(a.x, a.dtype, a.rows * a.k) : fold_partials(a.partial, a.n_partial);
+  const float amax = SMALL ? (a.op ? block_amax_op(a) : block_amax_all(a.x, a.dtype, a.rows * a.k))
+                           : fold_partials(a.partial, a.n_partial);
   const float T = amax / 2688.0f;
   const float sixT = 6.0f * T;
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.tensor_scale = T;
@@ -269,7 +341,14 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(EncodeArgs a) {
 
   for (int64_t row = blockIdx.y; row < a.rows; row += gridDim.y) {
     float x[4] = {0.f, 0.f, 0.f, 0.f};
-    if (live) {
+    if (live && a.op) {
+      const float4 v4 = epilogue4(a, row, 4 * s);
+      x[0] = v4.x;
+      x[1] = v4.y;
+      x[2] = v4.z;
+      x[3] = v4.w;
+      if (a.v_out) *(float4 *)(a.v_out + row * a.k + 4 * s) = v4;
+    } else if (live) {
       const int64_t e = row * a.k + 4 * s;
       if (a.dtype == AUTOFP_BF16) {
         const uint2 p = *(const uint2 *)((const uint16_t *)a.x + e);
@@ -482,6 +561,11 @@ int amax_partial_count(int64_t n) {
 hipError_t launch_amax_partial(const void *x, int dtype, int64_t n, float *partial, int n_partial,
                                hipStream_t s) {
   hipLaunchKernelGGL(amax_partial_kernel, dim3(n_partial), dim3(kThreads), 0, s, x, dtype, n, partial);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_partial_op(const EncodeArgs &a, float *partial, int n_partial, hipStream_t s) {
+  hipLaunchKernelGGL(amax_partial_op_kernel, dim3(n_partial), dim3(kThreads), 0, s, a, partial);
   return hipGetLastError();
 }
 

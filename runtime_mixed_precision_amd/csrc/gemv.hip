@@ -1373,7 +1373,7 @@ int64_t xh_kpad(int64_t k) { return round_up(k, kCh); }
 // Wqkv 6144 x 4096 29.9 us (panel 44.2) but Wo 29.6 (26.1), Wdown
 // 4096 x 14336 83.7 (72.1), and level 6 up to 1.6x the panel's time.
 bool gemv_small_m_route(const LinearArgs &a) {
-  return a.b > 16 && gemm_small_m_ok(a) && a.n >= 8192;
+  return a.b > 16 && !gemv_batch_ok(a) && gemm_small_m_ok(a) && a.n >= 8192;
 }
 
 // 17+ tokens off the GEMM tile with K % 32 == 0 at a host-side level 2 or 4:
@@ -1382,10 +1382,12 @@ bool gemv_small_m_route(const LinearArgs &a) {
 // level 6 the offset decode made it slower (Wdown 101 -> 121 us), so level 6
 // and a device-side level keep the fp16 panel.
 bool gemv_panel_packed(const LinearArgs &a) {
-  return a.b > 16 && !gemv_small_m_route(a) && (a.k & 31) == 0 && a.bits_dev == nullptr && a.bits != 6;
+  return a.b > 16 && !gemv_batch_ok(a) && !gemv_small_m_route(a) && (a.k & 31) == 0 && a.bits_dev == nullptr &&
+         a.bits != 6;
 }
 
 bool gemv_needs_panel(const LinearArgs &a) {
+  if (a.b > 16 && gemv_batch_ok(a)) return false;
   if (a.b > 16) return !gemv_panel_packed(a);
   return !stream_cfg(a).xlds;
 }
@@ -1447,9 +1449,10 @@ hipError_t launch_gemv(const LinearArgs &a0, hipStream_t s) {
 #undef AFP_STREAM
     return hipGetLastError();
   }
-  // more than 16 tokens: for wide weights (enough 256-row tiles to fill the
-  // chip) the 64-token GEMM tile, where every decoded weight tile serves all
-  // tokens from LDS; otherwise slices of at most 64 tokens
+  // more than 16 tokens with K % 64 == 0: the batched kernel (slices of 64
+  // tokens); otherwise, for wide weights, the 64-token GEMM tile, and slices
+  // of at most 64 tokens on the panel kernel
+  if (gemv_batch_ok(a0)) return launch_gemv_batch(a0, s);
   if (gemv_small_m_route(a0)) return launch_gemm_small_m(a0, s);
   for (int64_t t0 = 0; t0 < a0.b; t0 += 64) {
     LinearArgs a = a0;

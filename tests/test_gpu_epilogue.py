@@ -1,0 +1,90 @@
+"""GPU parity of the producer epilogue (autofp_epilogue_quantize): the layer's
+elementwise step on a completed linear output (copy of the first k columns,
+residual add, SwiGLU) fused with the AutoFP encode of the result into the
+next layer's activation ([AE] §6.4).
+
+  - v (written to v_out) against the oracle's fp64 epilogue: bit for bit for
+    copy and residual (one fp32 rounding of an exact sum), within 2e-6
+    relative for SwiGLU (fp32 exp and division);
+  - the packed output bit for bit against the oracle's encode of that same v
+    (the encode of a given fp32 tensor is exact), at 1 token (one launch), 4
+    and 64 tokens, with and without refinement and an exclusion mask;
+  - and against autofp_quantize of v, byte for byte.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import runtime_mixed_precision_amd as A
+from runtime_mixed_precision_amd import synthetic as S
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def same_packed(gpu, ref, refine):
+    h = gpu.to_host()
+    keys = ("codes", "scales", "mask", "offsets") if refine else ("codes", "scales")
+    for key in keys:
+        assert np.array_equal(h[key], ref[key]), key
+    assert np.float32(h["T"]) == np.float32(ref["T"])
+
+
+@pytest.mark.parametrize("op", ["copy", "residual", "swiglu"])
+@pytest.mark.parametrize("rows,k", [(1, 4096), (4, 4096), (1, 14336), (64, 1024), (3, 272)])
+@pytest.mark.parametrize("refine", [False, True])
+def test_epilogue_quantize(op, rows, k, refine):
+    say(f"case: epilogue {op} rows={rows} k={k} refine={refine}")
+    ldz = (2 * k if op == "swiglu" else k + 256)
+    z = S.hidden(rows, ldz, seed=rows + k, tensor_id=1, device=DEV) * 3.0
+    resid = S.hidden(rows, k, seed=rows + k, tensor_id=2, device=DEV)
+    wm, _ = A.select_weight_mask(S.weights(64, k, seed=3, tensor_id=3, device=DEV))
+    ex = wm if refine else None
+    out = A.alloc_activation(rows, k, refine=refine, device=DEV)
+    v = torch.empty(rows, k, dtype=torch.float32, device=DEV)
+    A.epilogue_quantize(op, z, out, residual=resid if op == "residual" else None, v_out=v,
+                        refine=refine, exclude_mask=ex)
+    torch.cuda.synchronize()
+    vg = v.cpu().numpy()
+    vr = O.epilogue(op, z.cpu().numpy(), k, resid.cpu().numpy())
+    if op == "swiglu":
+        rel = np.abs(vg - vr) / np.maximum(np.abs(vr), 1e-30)
+        assert rel.max() <= 2e-6, rel.max()
+    else:
+        assert np.array_equal(vg, vr.astype(np.float32))
+    exn = None if ex is None else ex.cpu().numpy()
+    ref = O.quantize_activation(vg, refine=refine, exclude_mask=exn)
+    same_packed(out, ref, refine)
+    # the separate encode of the same v gives the same bytes
+    q = A.quantize_activation(v, refine=refine, exclude_mask=ex)
+    torch.cuda.synchronize()
+    for key in ("codes", "scales", "tensor_scale") + (("mask", "offsets") if refine else ()):
+        assert torch.equal(getattr(q, key), getattr(out, key)), key
+
+
+def test_epilogue_without_v_out_and_arguments():
+    rows, k = 2, 512
+    z = S.hidden(rows, 2 * k, seed=9, tensor_id=1, device=DEV)
+    out = A.alloc_activation(rows, k, refine=False, device=DEV)
+    A.epilogue_quantize("swiglu", z, out)
+    ref = O.quantize_activation(np.asarray(O.epilogue("swiglu", z.cpu().numpy(), k), np.float32))
+    # v is recomputed in fp32 on the device: compare through the device's own v
+    v = torch.empty(rows, k, dtype=torch.float32, device=DEV)
+    out2 = A.alloc_activation(rows, k, refine=False, device=DEV)
+    A.epilogue_quantize("swiglu", z, out2, v_out=v)
+    torch.cuda.synchronize()
+    assert torch.equal(out.codes, out2.codes) and torch.equal(out.scales, out2.scales)
+    assert ref["codes"].shape == out.to_host()["codes"].shape
+    with pytest.raises(A.AutofpError):
+        A.epilogue_quantize("swiglu", z[:, :k + 16].contiguous(), out)      # ldz < 2k
+    with pytest.raises(A.AutofpError):
+        A.epilogue_quantize("residual", z, out)                             # residual missing
