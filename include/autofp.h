@@ -223,6 +223,24 @@ autofp_status autofp_epilogue_quantize(int32_t op, const float *z, int64_t ldz, 
                                        size_t workspace_bytes, void *stream);
 
 /*
+ * autofp_quantize for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, checks and results, but no workspace argument. Its scratch
+ * (the amax partials and the weight-mask prefix table) lives in a static
+ * 64 KiB device array of the library, one per GPU, held until the process
+ * ends; nothing is allocated. Sizes whose scratch would exceed 64 KiB are
+ * rejected with AUTOFP_ERR_WORKSPACE: that is any k above 491488 (rows are
+ * not limited). Every call on one GPU shares that GPU's array, so calls that
+ * overlap in time on one GPU (different streams, different host threads)
+ * race and must be serialized by the caller.
+ * Errors: those of autofp_quantize (WORKSPACE for k > 491488); HIP also when
+ * the array's device address cannot be obtained.
+ */
+autofp_status autofp_quantize_noalloc(const void *x, int32_t x_dtype, int32_t refine,
+                                      const uint8_t *exclude_mask, const autofp_params *p,
+                                      autofp_packed *out, void *stream);
+
+/*
  * Decode-phase linear layer ([AE] §3.1-3.2, §4): for b < x->rows, n < w->rows
  *   y[b][n] = sum_k What[n][k] * Xhat[b][k]
  * with the operands at precision level `bits`:

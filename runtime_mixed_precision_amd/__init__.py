@@ -21,7 +21,7 @@ from ._native import AutofpError, NativeLibraryError, Params  # noqa: F401
 __all__ = [
     "AutoFPTensor", "default_params", "packed_bytes", "weight_refined_count", "workspace_bytes",
     "select_weight_mask", "quantize", "quantize_weight", "quantize_activation",
-    "alloc_activation", "quantize_into", "epilogue_quantize",
+    "alloc_activation", "quantize_into", "quantize_noalloc", "epilogue_quantize",
     "gemv", "gemv_rows", "gemm", "policy_signals", "policy_state", "policy_update", "AutofpError",
     "NativeLibraryError", "KVCache", "kv_write", "kv_attention",
 ]
@@ -212,6 +212,22 @@ def epilogue_quantize(op, z: torch.Tensor, out: AutoFPTensor, residual=None, v_o
                                              int(bool(refine)), _ptr(exclude_mask), C.byref(p), C.byref(st),
                                              _ptr(workspace), workspace.numel(), _stream(stream)),
             "autofp_epilogue_quantize")
+    return out
+
+
+def quantize_noalloc(x: torch.Tensor, out: AutoFPTensor, refine=False, exclude_mask=None, params=None,
+                     stream=None) -> AutoFPTensor:
+    """autofp_quantize_noalloc into preallocated buffers: no workspace, the
+    library's static per-GPU scratch instead (k <= 491488; calls that overlap
+    on one GPU race)."""
+    _dev_check(x, exclude_mask)
+    if x.dim() != 2 or x.dtype not in _DT or tuple(x.shape) != (out.rows, out.k):
+        raise ValueError("x must be 2-D float32/bfloat16 with the output's shape")
+    p = params or default_params()
+    st = out.struct()
+    N.check(N.lib().autofp_quantize_noalloc(_ptr(x), _DT[x.dtype], int(bool(refine)), _ptr(exclude_mask),
+                                            C.byref(p), C.byref(st), _stream(stream)),
+            "autofp_quantize_noalloc")
     return out
 
 

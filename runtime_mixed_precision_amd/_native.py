@@ -29,7 +29,7 @@ EPI_COPY, EPI_RESIDUAL, EPI_SWIGLU = 1, 2, 3
 EXPORTS = (
     "autofp_default_params", "autofp_status_string", "autofp_packed_bytes",
     "autofp_weight_refined_count", "autofp_workspace_bytes", "autofp_select_weight_mask",
-    "autofp_quantize", "autofp_epilogue_quantize", "autofp_gemv", "autofp_gemv_rows", "autofp_gemm", "autofp_policy_signals",
+    "autofp_quantize", "autofp_quantize_noalloc", "autofp_epilogue_quantize", "autofp_gemv", "autofp_gemv_rows", "autofp_gemm", "autofp_policy_signals",
     "autofp_policy_update", "autofp_policy_layer", "autofp_kv_write", "autofp_kv_attention",
 )
 
@@ -102,6 +102,7 @@ def lib():
                                                 C.c_size_t, vp]),
         "autofp_quantize": (C.c_int, [vp, C.c_int32, C.c_int32, vp, P(Params), P(Packed), vp,
                                       C.c_size_t, vp]),
+        "autofp_quantize_noalloc": (C.c_int, [vp, C.c_int32, C.c_int32, vp, P(Params), P(Packed), vp]),
         "autofp_epilogue_quantize": (C.c_int, [C.c_int32, vp, C.c_int64, vp, vp, C.c_int32, vp, P(Params),
                                                P(Packed), vp, C.c_size_t, vp]),
         "autofp_gemv": (C.c_int, [P(Packed), P(Packed), C.c_int32, vp, vp, C.c_int32, P(Params), vp,

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <atomic>
+
 #include "afp_launch.h"
 #include "autofp.h"
 
@@ -10,6 +12,10 @@ using namespace afp;
 
 static_assert(sizeof(autofp_policy_state) == 48, "policy state layout");
 static_assert(sizeof(autofp_params) == 56, "params layout");
+
+// Bytes of the static scratch array of autofp_quantize_noalloc (below).
+constexpr size_t kScratchBytes = 64 * 1024;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -217,6 +223,33 @@ autofp_status launch_quantize(const void *x, int32_t x_dtype, int32_t refine, co
   return from_hip(launch_encode(a, small, s));
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of autofp_quantize_noalloc: one file-scope device array. Every GPU
+// the library runs on holds its own copy (at its own address) until the
+// process ends. In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and only that address is
+// passed to kernels. Calls on one GPU share the array, so calls that overlap
+// in time on one GPU race; nothing in it needs to start at zero (each call
+// writes every entry it reads before reading it).
+// ---------------------------------------------------------------------------
+constexpr int kScratchDevices = 64;
+std::atomic<void *> g_scratch_dev[kScratchDevices];
+
+autofp_status scratch_ptr(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return AUTOFP_ERR_HIP;
+  if (dev < 0 || dev >= kScratchDevices) return AUTOFP_ERR_ARG;
+  void *p = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // the same address on every concurrent first call: storing it twice is benign
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return AUTOFP_ERR_HIP;
+    g_scratch_dev[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return AUTOFP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -371,6 +404,18 @@ autofp_status autofp_epilogue_quantize(int32_t op, const float *z, int64_t ldz, 
   epi.resid = op == AUTOFP_EPI_RESIDUAL ? residual : nullptr;
   epi.v_out = v_out;
   return launch_quantize(z, AUTOFP_F32, refine, exclude_mask, p, out, workspace, (hipStream_t)stream, &epi);
+}
+
+autofp_status autofp_quantize_noalloc(const void *x, int32_t x_dtype, int32_t refine,
+                                      const uint8_t *exclude_mask, const autofp_params *p,
+                                      autofp_packed *out, void *stream) {
+  const autofp_status st = check_quantize(x, x_dtype, refine, exclude_mask, out);
+  if (st != AUTOFP_OK) return st;
+  if (ws_quantize(out->rows, out->k) > kScratchBytes) return AUTOFP_ERR_WORKSPACE;
+  void *ws = nullptr;
+  const autofp_status ss = scratch_ptr(&ws);
+  if (ss != AUTOFP_OK) return ss;
+  return launch_quantize(x, x_dtype, refine, exclude_mask, p, out, ws, (hipStream_t)stream);
 }
 
 autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_t bits,

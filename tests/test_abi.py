@@ -116,6 +116,22 @@ def test_quantize_rejects_bad_arguments(N):
     assert q(FAKE, N.F32, 0, C.byref(good), 8) == 5       # workspace too small
 
 
+def test_quantize_noalloc_checks_and_size_limit(N):
+    """The static-scratch encode checks its arguments like autofp_quantize and
+    rejects any k whose scratch would pass 64 KiB (k > 491488) before touching
+    the device."""
+    L = N.lib()
+    p = params(N)
+    q = lambda x, dt, ref, out: L.autofp_quantize_noalloc(x, dt, ref, None, C.byref(p), out, None)
+    good = packed(N, N.ACTIVATION)
+    assert q(None, N.F32, 0, C.byref(good)) == 1
+    assert q(FAKE, 7, 0, C.byref(good)) == 7
+    assert q(FAKE, N.F32, 1, C.byref(good)) == 6
+    assert q(FAKE, N.F32, 0, C.byref(packed(N, N.ACTIVATION, k=40))) == 2
+    assert q(FAKE, N.F32, 0, C.byref(packed(N, N.ACTIVATION, rows=1, k=491504))) == 5
+    assert q(FAKE, N.F32, 0, C.byref(packed(N, N.WEIGHT, rows=1, k=491504))) == 5
+
+
 def test_linear_rejects_bad_arguments(N):
     L = N.lib()
     p = params(N)
