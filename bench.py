@@ -487,6 +487,43 @@ def prefill_bench(A, S, device, reps):
             "frac_fp4_mfma_peak": round(best / PEAK_FP4_TFLOPS, 4)}
 
 
+def formats_bench(A, S, device, reps=5, pool_n=6):
+    """The format variants ([AE] §6.5 / Fig. 14(a) exponent-scaled offsets,
+    App. I AutoFP8, App. B.2 FP6g) at their top level on the Wup shape
+    (14336 x 4096): prefill GEMM TFLOP/s at 2048 tokens, one-token decode
+    GB/s (all packed weight and activation bytes, weights rotated over a pool
+    larger than the Infinity Cache), and stored bits per weight."""
+    import torch
+    n, k, M = 14336, 4096, 2048
+    out = {}
+    x = S.activations(M, k, seed=300, tensor_id=1, outlier_frac=0.005, outlier_scale=30.0, device=device)
+    x1 = x[:1].contiguous()
+    ws = torch.empty(A.workspace_bytes(3, M, k), dtype=torch.uint8, device=device)
+    y = torch.empty(M, n, dtype=torch.bfloat16, device=device)
+    y1 = torch.empty(1, n, dtype=torch.float32, device=device)
+    for fmt, level in (("autofp6", 6), ("autofp6e", 6), ("autofp8", 6), ("autofp8", 8), ("fp6g", 6)):
+        pool = []
+        for i in range(pool_n):
+            w = S.weights(n, k, seed=300 + i, tensor_id=0, device=device)
+            pool.append(A.quantize_weight(w, format=fmt))
+            del w
+        wp = pool[0]
+        refine = fmt != "fp6g"
+        xp = A.quantize_activation(x, refine=refine, exclude_mask=wp.mask, format=fmt)
+        xp1 = A.quantize_activation(x1, refine=refine, exclude_mask=wp.mask, format=fmt)
+        ms = time_graphs(capture([lambda: A.gemm(wp, xp, bits=level, out=y, workspace=ws)]), reps, 2)
+        g1 = capture([lambda w_=w_: A.gemv(w_, xp1, bits=level, out=y1, workspace=ws) for w_ in pool])
+        us = time_graphs(g1, 20, 3) * 1e3
+        by = wp.nbytes + xp1.nbytes + 4 * n
+        out[f"{fmt}_l{level}"] = {"prefill_ms": round(ms, 4), "prefill_tflops": round(2.0 * M * n * k / (ms * 1e-3) / 1e12, 1),
+                                  "decode_us": round(us, 2), "decode_gbs": round(by / (us * 1e-6) / 1e9, 1),
+                                  "bits_per_weight": round(8.0 * wp.nbytes / (n * k), 3)}
+        del pool, wp, xp, xp1, g1
+    del x, x1, ws, y, y1
+    return {"workload": "Wup 14336x4096: X[2048x4096] prefill (bf16 out) and one-token decode, each format at its top level",
+            "per_format": out}
+
+
 def gemv_70b(A, S, device, batch=64, pool_n=5):
     """The 70B-shaped projection (28672 x 8192) at 64 tokens, level 4: weights
     rotated over a pool larger than the Infinity Cache, one graph per weight."""
@@ -608,6 +645,7 @@ def main():
     ap.add_argument("--no-batches", action="store_true", help="skip the batch-16/64 and 70B-shape GEMV lines")
     ap.add_argument("--no-step32", action="store_true", help="skip the 32-layer policy-driven step")
     ap.add_argument("--no-kv", action="store_true", help="skip the KV-cache decode attention line")
+    ap.add_argument("--no-formats", action="store_true", help="skip the format-variant comparison lines")
     ap.add_argument("--kv-only", action="store_true", help="run only the KV-cache attention (no JSON line)")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run only the workload of the HBM-counter runs (no JSON line)")
@@ -701,6 +739,9 @@ def main():
     if not args.no_prefill:
         del graphs, ggraphs
         extra["prefill_gemm"] = prefill_bench(A, S, device, 5)
+    if not args.no_formats:
+        torch.cuda.empty_cache()
+        extra["formats"] = formats_bench(A, S, device)
     if not args.no_step32:
         del pool, bench
         torch.cuda.empty_cache()

@@ -37,7 +37,7 @@ typedef enum {
   AUTOFP_OK = 0,
   AUTOFP_ERR_NULL = 1,               /* a required pointer is NULL                  */
   AUTOFP_ERR_SHAPE = 2,              /* k % 16 != 0, rows < 1, mismatched shapes    */
-  AUTOFP_ERR_BITS = 3,               /* precision level not in {2, 4, 6}            */
+  AUTOFP_ERR_BITS = 3,               /* level not in {2, 4, 6} (8: AutoFP8 only)    */
   AUTOFP_ERR_KIND = 4,               /* weight/activation operand in the wrong slot */
   AUTOFP_ERR_WORKSPACE = 5,          /* workspace NULL or smaller than required     */
   AUTOFP_ERR_MISSING_REFINEMENT = 6, /* level 6 without mask/offsets                */
@@ -48,6 +48,38 @@ typedef enum {
 
 typedef enum { AUTOFP_F32 = 0, AUTOFP_BF16 = 1 } autofp_dtype;
 typedef enum { AUTOFP_WEIGHT = 0, AUTOFP_ACTIVATION = 1 } autofp_kind;
+
+/*
+ * Element and offset format of a packed tensor (autofp_packed.format). The
+ * first three share the NVFP4 base (E2M1 codes, E4M3 group scales, FP32
+ * tensor scale) and the subgroup masks; they differ in the signed offsets d
+ * of the refined subgroups and their value delta:
+ *  AUTOFP6   d in {-2,-1,0,+1}, delta = d/8, 2 bits per element, one byte per
+ *            subgroup ([AE] §3.2). The default (zero).
+ *  AUTOFP6E  d in {-2,-1,0,+1}, delta = d * 2^(e-3) with e the unbiased
+ *            exponent of the element's E2M1 value q (0 for |q| < 1, 1 for
+ *            2 and 3, 2 for 4 and 6): the exponent-scaled offset step that
+ *            [AE] §6.5 / Fig. 14(a) compares with the fixed one. Same storage
+ *            as AUTOFP6.
+ *  AUTOFP8   d in {-8..7}, delta = d/8, 4 bits per element, two bytes per
+ *            subgroup, element e of the subgroup in bits [4e+3:4e] of the
+ *            little-endian 16-bit word ([AE] App. I, Table 10: offsets widened
+ *            from 2 to 4 bits; 5.3 bits per weight at rho = 0.2). Runs at
+ *            level 8 with d, and at level 6 with d clamped to [-2, +1] (the
+ *            AutoFP6 offset of the same element).
+ *  FP6G      the group-scaled 6-bit comparator of [AE] App. B.2: E2M3
+ *            elements (bias 1, maximum 7.5) under the NVFP4 scaling hierarchy,
+ *            T = amax/(7.5*448), B_j = E4M3(amax_j/(7.5 T)). Codes [rows][3k/4]:
+ *            four 6-bit codes s|e1|e0|m2|m1|m0 per three bytes, code i of a
+ *            subgroup at bits [6i+5:6i] of the little-endian 24-bit word. No
+ *            masks, no offsets; runs at level 6 only.
+ */
+typedef enum {
+  AUTOFP_FMT_AUTOFP6 = 0,
+  AUTOFP_FMT_AUTOFP6E = 1,
+  AUTOFP_FMT_AUTOFP8 = 2,
+  AUTOFP_FMT_FP6G = 3
+} autofp_format;
 
 /* Hyperparameters; autofp_default_params() fills the values of [AE] §5.1
  * ("Hyperparameters"). */
@@ -109,6 +141,10 @@ typedef struct {
  *               in bits [2e+1:2e]; value delta = d/8 ([AE] §3.2, fixed step).
  *  n_refined    WEIGHT only: number of refined subgroups per row (= popcount of
  *               mask); 0 otherwise.
+ *  format       autofp_format (0 = AUTOFP6, the layout above). AUTOFP8 offsets
+ *               take two bytes per subgroup (WEIGHT [rows][2 n_refined] + 16
+ *               bytes of padding, ACTIVATION [rows][k/2]); FP6G codes are
+ *               [rows][3k/4] and mask and offsets are NULL.
  */
 typedef struct {
   int64_t  rows;
@@ -120,6 +156,8 @@ typedef struct {
   float   *tensor_scale;
   uint8_t *mask;
   uint8_t *offsets;
+  int32_t  format;      /* autofp_format */
+  int32_t  reserved;    /* 0 */
 } autofp_packed;
 
 /* Operations whose scratch space autofp_workspace_bytes() sizes. */
@@ -139,13 +177,14 @@ autofp_status autofp_default_params(autofp_params *p);
 /* Human-readable name of a status code (static string, never NULL). */
 const char *autofp_status_string(autofp_status s);
 
-/* Bytes of each buffer of one packed tensor, written to out_bytes (host):
- * [0] codes, [1] scales, [2] tensor_scale, [3] mask, [4] offsets (for a
- * WEIGHT: rows * n_refined + 16, the padding included).
- * refine = 0 gives 0 for mask and offsets. For WEIGHT, n_refined is the value
- * autofp_weight_refined_count() returns. Errors: NULL, SHAPE, KIND, ARG. */
-autofp_status autofp_packed_bytes(int64_t rows, int64_t k, int32_t kind, int32_t refine,
-                                  int32_t n_refined, size_t out_bytes[5]);
+/* Bytes of each buffer of one packed tensor of format `format`, written to
+ * out_bytes (host): [0] codes, [1] scales, [2] tensor_scale, [3] mask,
+ * [4] offsets (for a WEIGHT: rows * n_refined * (2 for AUTOFP8, else 1) + 16,
+ * the padding included). refine = 0 gives 0 for mask and offsets. For WEIGHT,
+ * n_refined is the value autofp_weight_refined_count() returns.
+ * Errors: NULL, SHAPE, KIND, ARG (format unknown, or FP6G with refine). */
+autofp_status autofp_packed_bytes(int64_t rows, int64_t k, int32_t kind, int32_t format,
+                                  int32_t refine, int32_t n_refined, size_t out_bytes[5]);
 
 /* Number of refined subgroups per weight row: floor(rho * k / 4), at most two
  * per group ([AE] App. E, Alg. 1: budget rho*K/4, l_j in {0, 1, 2}).
@@ -162,14 +201,17 @@ autofp_status autofp_workspace_bytes(int32_t op, int64_t rows, int64_t k, size_t
  *  1. NVFP4-encode w (as autofp_quantize does) and, per row n, group j and
  *     subgroup s, the fp64 reduction in squared error from refining it:
  *       g = sum over the 4 elements of (eb*eb - er*er),
- *       eb = w - T*B*q, er = w - T*B*(q + d/8);
+ *       eb = w - T*B*q, er = w - T*B*(q + delta),
+ *     with d and delta those of `format` (AUTOFP6, AUTOFP6E or AUTOFP8; at
+ *     level 8 for AUTOFP8);
  *  2. sum g over rows n = 0..rows-1 in that order (fp64);
  *  3. refine the top n_refined (group, subgroup) candidates, at most two per
  *     group, ordered by gain (descending), then group, then subgroup.
  * Writes mask_out [ceil(k/32)] (device). n_refined comes from
- * autofp_weight_refined_count(). Errors: NULL, SHAPE, ARG, WORKSPACE, HIP.
+ * autofp_weight_refined_count(). Errors: NULL, SHAPE, ARG (also FP6G or an
+ * unknown format), WORKSPACE, HIP.
  */
-autofp_status autofp_select_weight_mask(const float *w, int64_t rows, int64_t k,
+autofp_status autofp_select_weight_mask(const float *w, int64_t rows, int64_t k, int32_t format,
                                         const autofp_params *p, uint8_t *mask_out,
                                         void *workspace, size_t workspace_bytes, void *stream);
 
@@ -187,7 +229,14 @@ autofp_status autofp_select_weight_mask(const float *w, int64_t rows, int64_t k,
  *    ((e0^2+e1^2)+e2^2)+e3^2 > thresh * ((v0^2+v1^2)+v2^2)+v3^2 (fp32, v = x/(TB),
  *    e = v - q; [AE] §6.4) that are not in exclude_mask (the layer's M_W,
  *    [ceil(k/32)], may be NULL) - and the dense offsets.
- * Errors: NULL, SHAPE, KIND, DTYPE, WORKSPACE, MISSING_REFINEMENT, HIP.
+ *  - out->format selects the offsets (autofp_format): AUTOFP6E takes
+ *    d = argmin |r - d 2^(e-3)|, AUTOFP8 d = argmin over {-8..7} of |r - d/8|
+ *    (r = x/(TB) - q, ties to the smaller |d|); the masks follow the same
+ *    rules. FP6G encodes T = amax/3360, B_j = E4M3(amax_j/(7.5 T)),
+ *    q_i = E2M3(x_i/(T B_j)) (nearest, ties to the even code, saturating at
+ *    7.5); it takes refine = 0 and no mask.
+ * Errors: NULL, SHAPE, KIND, DTYPE, WORKSPACE, MISSING_REFINEMENT, ARG
+ * (format unknown; FP6G with refine or a mask), HIP.
  */
 autofp_status autofp_quantize(const void *x, int32_t x_dtype, int32_t refine,
                               const uint8_t *exclude_mask, const autofp_params *p,
@@ -256,7 +305,15 @@ autofp_status autofp_quantize_noalloc(const void *x, int32_t x_dtype, int32_t re
  * be at most 2^22 (4194304); with at most 16 tokens, a level-6 call (or one
  * with bits_dev) needs k <= 65536. Any number of tokens: the kernels address
  * the activations one tile of rows at a time.
- * Errors: NULL, SHAPE, KIND, BITS, MISSING_REFINEMENT, DTYPE, WORKSPACE, HIP.
+ * Formats (autofp_format): w and x must have the same format. AUTOFP6E and
+ * AUTOFP8 run levels 2 and 4 as AUTOFP6 (their NVFP4 base), level 6 with
+ * their own delta, and AUTOFP8 also level 8: T*B*(q + d/8) with the full
+ * 4-bit d on both operands (W8A8). FP6G runs level 6 only, without bits_dev:
+ * T*B*q with its E2M3 codes (W6A6 of the comparator). Levels above 4 of the
+ * variant formats (and any bits_dev call on them) need k % 64 == 0 and run
+ * on the prefill GEMM's tiles.
+ * Errors: NULL, SHAPE, KIND, BITS, MISSING_REFINEMENT, DTYPE, WORKSPACE, ARG
+ * (formats differ or unknown), HIP.
  */
 autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_t bits,
                           const int32_t *bits_dev, void *y, int32_t y_dtype,
@@ -278,8 +335,8 @@ autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_
  * a zero row. Any row may be at level 6, so both operands must carry their
  * refinement (weight mask and offsets; activation mask and offsets).
  * k % 128 == 0 and k <= 2^22; any number of rows (slices of 64). Workspace as
- * autofp_gemv. Errors: NULL, SHAPE, KIND, MISSING_REFINEMENT, DTYPE,
- * WORKSPACE, ARG, HIP.
+ * autofp_gemv. Both operands AUTOFP6 (format 0). Errors: NULL, SHAPE, KIND,
+ * MISSING_REFINEMENT, DTYPE, WORKSPACE, ARG (also another format), HIP.
  */
 autofp_status autofp_gemv_rows(const autofp_packed *w, const autofp_packed *x, const int32_t *bits_rows,
                                void *y, int32_t y_dtype, const autofp_params *p, void *workspace,
@@ -292,8 +349,8 @@ autofp_status autofp_gemv_rows(const autofp_packed *w, const autofp_packed *x, c
  * for the matrix cores (256-token x 256-row tiles when K % 64 == 0). The
  * fp16 activations are staged in the workspace (autofp_workspace_bytes(
  * AUTOFP_OP_GEMM, tokens, k): 2 * tokens * round_up(k, 256) bytes plus the
- * weight-mask prefix). k <= 2^22. Same arguments, results and errors as
- * autofp_gemv.
+ * weight-mask prefix). k <= 2^22. Same arguments, results, formats and
+ * errors as autofp_gemv.
  */
 autofp_status autofp_gemm(const autofp_packed *w, const autofp_packed *x, int32_t bits,
                           const int32_t *bits_dev, void *y, int32_t y_dtype,

@@ -52,9 +52,19 @@ def default_params(**overrides) -> Params:
     return p
 
 
-def packed_bytes(rows, k, kind, refine=False, n_refined=0):
+def _fmt(format) -> int:
+    """autofp_format code of a format name ("autofp6", "autofp6e", "autofp8",
+    "fp6g") or code."""
+    if isinstance(format, str):
+        if format not in N.FORMATS:
+            raise ValueError(f"unknown format {format!r}; one of {sorted(N.FORMATS)}")
+        return N.FORMATS[format]
+    return int(format)
+
+
+def packed_bytes(rows, k, kind, refine=False, n_refined=0, format="autofp6"):
     out = (C.c_size_t * 5)()
-    N.check(N.lib().autofp_packed_bytes(rows, k, kind, int(bool(refine)), n_refined, out),
+    N.check(N.lib().autofp_packed_bytes(rows, k, kind, _fmt(format), int(bool(refine)), n_refined, out),
             "autofp_packed_bytes")
     return list(out)
 
@@ -89,11 +99,12 @@ class AutoFPTensor:
     mask: Optional[torch.Tensor] = None
     offsets: Optional[torch.Tensor] = None
     n_refined: int = 0
+    format: int = 0     # autofp_format
 
     def struct(self) -> N.Packed:
         return N.Packed(self.rows, self.k, self.kind, self.n_refined, _ptr(self.codes),
                         _ptr(self.scales), _ptr(self.tensor_scale), _ptr(self.mask),
-                        _ptr(self.offsets))
+                        _ptr(self.offsets), self.format, 0)
 
     @property
     def nbytes(self) -> int:
@@ -111,34 +122,38 @@ class AutoFPTensor:
             d["offsets"] = self.offsets.cpu().numpy()
         if self.kind == N.WEIGHT:
             d["n_refined"] = self.n_refined
+        d["format"] = self.format
         return d
 
 
-def _alloc_packed(rows, k, kind, refine, n_refined, device):
-    nb = packed_bytes(rows, k, kind, refine, n_refined)
+def _alloc_packed(rows, k, kind, refine, n_refined, device, format=0):
+    fmt = _fmt(format)
+    nb = packed_bytes(rows, k, kind, refine, n_refined, fmt)
 
     def buf(n, shape):
         return torch.zeros(shape, dtype=torch.uint8, device=device) if n else None
 
     mb = (k + 31) // 32
-    codes = torch.empty(rows, k // 2, dtype=torch.uint8, device=device)
+    ow = 2 if fmt == N.FMT_AUTOFP8 else 1       # offset bytes per subgroup
+    codes = torch.empty(rows, nb[0] // rows, dtype=torch.uint8, device=device)
     scales = torch.empty(rows, k // 16, dtype=torch.uint8, device=device)
     ts = torch.empty(1, dtype=torch.float32, device=device)
     if kind == N.WEIGHT:
         mask = buf(nb[3], (mb,))
         offs = None
         if refine:
-            # rows x n_refined bytes plus the padding the GEMV may read past the end
-            flat = torch.zeros(max(nb[4], rows * n_refined + 16), dtype=torch.uint8, device=device)
-            offs = flat[: rows * n_refined].view(rows, n_refined)
+            # rows x n_refined offset words plus the padding the GEMV may read past the end
+            flat = torch.zeros(max(nb[4], rows * n_refined * ow + 16), dtype=torch.uint8, device=device)
+            offs = flat[: rows * n_refined * ow].view(rows, n_refined * ow)
     else:
         mask = buf(nb[3], (rows, mb))
-        offs = buf(nb[4], (rows, k // 4))
-    return AutoFPTensor(rows, k, kind, codes, scales, ts, mask, offs, n_refined if kind == N.WEIGHT else 0)
+        offs = buf(nb[4], (rows, (k // 4) * ow))
+    return AutoFPTensor(rows, k, kind, codes, scales, ts, mask, offs, n_refined if kind == N.WEIGHT else 0, fmt)
 
 
-def select_weight_mask(w: torch.Tensor, params=None, stream=None):
-    """Weight mask M_W (device uint8 [ceil(k/32)]) and its refined-subgroup count."""
+def select_weight_mask(w: torch.Tensor, params=None, stream=None, format="autofp6"):
+    """Weight mask M_W (device uint8 [ceil(k/32)]) and its refined-subgroup
+    count, with the gains of ``format``'s offsets."""
     _dev_check(w)
     if w.dtype != torch.float32 or w.dim() != 2:
         raise ValueError("weight must be a 2-D float32 tensor")
@@ -146,25 +161,26 @@ def select_weight_mask(w: torch.Tensor, params=None, stream=None):
     rows, k = w.shape
     mask = torch.zeros((k + 31) // 32, dtype=torch.uint8, device=w.device)
     ws = _workspace(N.OP_SELECT_MASK, rows, k, w.device)
-    N.check(N.lib().autofp_select_weight_mask(_ptr(w), rows, k, C.byref(p), _ptr(mask), _ptr(ws),
+    N.check(N.lib().autofp_select_weight_mask(_ptr(w), rows, k, _fmt(format), C.byref(p), _ptr(mask), _ptr(ws),
                                               ws.numel(), _stream(stream)), "autofp_select_weight_mask")
     return mask, weight_refined_count(k, p)
 
 
 def quantize(x: torch.Tensor, kind: int, refine=False, exclude_mask=None, weight_mask=None,
-             n_refined=0, params=None, stream=None) -> AutoFPTensor:
-    """Encode a [rows x k] fp32/bf16 tensor to AutoFP (autofp_quantize)."""
+             n_refined=0, params=None, stream=None, format="autofp6") -> AutoFPTensor:
+    """Encode a [rows x k] fp32/bf16 tensor to AutoFP (autofp_quantize) in
+    ``format`` ("autofp6", "autofp6e", "autofp8" or "fp6g")."""
     _dev_check(x, exclude_mask, weight_mask)
     if x.dim() != 2 or x.dtype not in _DT:
         raise ValueError("x must be a 2-D float32 or bfloat16 tensor")
     rows, k = x.shape
     p = params or default_params()
     if kind == N.WEIGHT:
-        out = _alloc_packed(rows, k, kind, weight_mask is not None, n_refined, x.device)
+        out = _alloc_packed(rows, k, kind, weight_mask is not None, n_refined, x.device, format)
         if weight_mask is not None:
             out.mask = weight_mask
     else:
-        out = _alloc_packed(rows, k, kind, refine, 0, x.device)
+        out = _alloc_packed(rows, k, kind, refine, 0, x.device, format)
     ws = _workspace(N.OP_QUANTIZE, rows, k, x.device)
     st = out.struct()
     N.check(N.lib().autofp_quantize(_ptr(x), _DT[x.dtype], int(bool(refine)), _ptr(exclude_mask),
@@ -173,9 +189,9 @@ def quantize(x: torch.Tensor, kind: int, refine=False, exclude_mask=None, weight
     return out
 
 
-def alloc_activation(rows, k, refine=True, device="cuda:0") -> AutoFPTensor:
+def alloc_activation(rows, k, refine=True, device="cuda:0", format="autofp6") -> AutoFPTensor:
     """Device buffers for a [rows x k] activation (with refinement storage)."""
-    return _alloc_packed(rows, k, N.ACTIVATION, refine, 0, device)
+    return _alloc_packed(rows, k, N.ACTIVATION, refine, 0, device, format)
 
 
 def quantize_into(x: torch.Tensor, out: AutoFPTensor, refine=False, exclude_mask=None,
@@ -231,19 +247,19 @@ def quantize_noalloc(x: torch.Tensor, out: AutoFPTensor, refine=False, exclude_m
     return out
 
 
-def quantize_weight(w: torch.Tensor, refine=True, params=None, stream=None) -> AutoFPTensor:
+def quantize_weight(w: torch.Tensor, refine=True, params=None, stream=None, format="autofp6") -> AutoFPTensor:
     """Offline weight packing: M_W selection (when ``refine``) and encode."""
-    if refine:
-        mask, nref = select_weight_mask(w, params, stream)
+    if refine and _fmt(format) != N.FMT_FP6G:
+        mask, nref = select_weight_mask(w, params, stream, format)
         return quantize(w, N.WEIGHT, refine=True, weight_mask=mask, n_refined=nref, params=params,
-                        stream=stream)
-    return quantize(w, N.WEIGHT, params=params, stream=stream)
+                        stream=stream, format=format)
+    return quantize(w, N.WEIGHT, params=params, stream=stream, format=format)
 
 
 def quantize_activation(x: torch.Tensor, refine=False, exclude_mask=None, params=None,
-                        stream=None) -> AutoFPTensor:
+                        stream=None, format="autofp6") -> AutoFPTensor:
     return quantize(x, N.ACTIVATION, refine=refine, exclude_mask=exclude_mask, params=params,
-                    stream=stream)
+                    stream=stream, format=format)
 
 
 def _linear(fn, name, w, x, bits, bits_dev, out_dtype, params, workspace, out, stream):

@@ -24,6 +24,8 @@ OP_QUANTIZE, OP_SELECT_MASK, OP_GEMV, OP_GEMM, OP_SIGNALS = 0, 1, 2, 3, 4
 OP_KV_WRITE, OP_KV_ATTENTION = 5, 6
 KV_PAGE_TOKENS, KV_HEAD_DIM, KV_PAGE_BYTES = 64, 128, 4608
 EPI_COPY, EPI_RESIDUAL, EPI_SWIGLU = 1, 2, 3
+FMT_AUTOFP6, FMT_AUTOFP6E, FMT_AUTOFP8, FMT_FP6G = 0, 1, 2, 3
+FORMATS = {"autofp6": FMT_AUTOFP6, "autofp6e": FMT_AUTOFP6E, "autofp8": FMT_AUTOFP8, "fp6g": FMT_FP6G}
 
 # Every symbol include/autofp.h declares.
 EXPORTS = (
@@ -63,7 +65,7 @@ POLICY_STATE_BYTES = 48
 class Packed(C.Structure):
     _fields_ = [("rows", C.c_int64), ("k", C.c_int64), ("kind", C.c_int32), ("n_refined", C.c_int32),
                 ("codes", C.c_void_p), ("scales", C.c_void_p), ("tensor_scale", C.c_void_p),
-                ("mask", C.c_void_p), ("offsets", C.c_void_p)]
+                ("mask", C.c_void_p), ("offsets", C.c_void_p), ("format", C.c_int32), ("reserved", C.c_int32)]
 
 
 class KvCache(C.Structure):
@@ -94,11 +96,11 @@ def lib():
     sig = {
         "autofp_default_params": (C.c_int, [P(Params)]),
         "autofp_status_string": (C.c_char_p, [C.c_int]),
-        "autofp_packed_bytes": (C.c_int, [C.c_int64, C.c_int64, C.c_int32, C.c_int32, C.c_int32,
+        "autofp_packed_bytes": (C.c_int, [C.c_int64, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                           P(C.c_size_t)]),
         "autofp_weight_refined_count": (C.c_int, [C.c_int64, P(Params), P(C.c_int32)]),
         "autofp_workspace_bytes": (C.c_int, [C.c_int32, C.c_int64, C.c_int64, P(C.c_size_t)]),
-        "autofp_select_weight_mask": (C.c_int, [vp, C.c_int64, C.c_int64, P(Params), vp, vp,
+        "autofp_select_weight_mask": (C.c_int, [vp, C.c_int64, C.c_int64, C.c_int32, P(Params), vp, vp,
                                                 C.c_size_t, vp]),
         "autofp_quantize": (C.c_int, [vp, C.c_int32, C.c_int32, vp, P(Params), P(Packed), vp,
                                       C.c_size_t, vp]),

@@ -65,6 +65,39 @@ __device__ __forceinline__ uint32_t offset_code(float r) {
   return (uint32_t)d & 3u;
 }
 
+// Offset variants ("AutoEMatic" App. I: 4-bit offsets, AutoFP8; §6.5 /
+// Fig. 14(a): the step 2^(e-3) of the element's own exponent).
+//
+// 2^-e for the unbiased exponent e = max(field - 1, 0) of an E2M1 code's value
+// (fields 00 and 01 give e = 0, 10 gives 1, 11 gives 2): argmin over d of
+// |r - d 2^(e-3)| = argmin |r 2^-e - d/8|, the scaling being exact.
+__device__ __forceinline__ float e2m1_inv_pow2e(uint32_t code) {
+  const uint32_t f = (code >> 1) & 3u;
+  return f == 3u ? 0.25f : (f == 2u ? 0.5f : 1.0f);
+}
+
+// 4-bit signed offset: argmin over d in -8..7 of |r - d/8|, ties to the
+// smaller |d| (u = 8r is exact; |u| - 0.5 is exact for these magnitudes).
+__device__ __forceinline__ int offset8(float r) {
+  const float u = 8.0f * r;
+  const int m = (int)ceilf(fabsf(u) - 0.5f);
+  const int d = u < 0.0f ? -m : m;
+  return d < -8 ? -8 : (d > 7 ? 7 : d);
+}
+
+// E2M3 (FP6g element, bias 1, max 7.5) code of v with round half to even on
+// the code (the grid steps 1/8 below 2, 1/4 on [2, 4), 1/2 on [4, 7.5]);
+// saturates at 7.5; canonical +0. Every subtraction and scaling is exact.
+__device__ __forceinline__ uint32_t e2m3_encode(float v) {
+  const float a = fabsf(v);
+  uint32_t c;
+  if (!(a < 7.5f)) c = 31u;
+  else if (a < 2.0f) c = (uint32_t)rintf(a * 8.0f);                     // 0..16 (16 = 2.0)
+  else if (a < 4.0f) c = 16u + (uint32_t)rintf((a - 2.0f) * 4.0f);       // 16..24
+  else c = 24u + (uint32_t)rintf((a - 4.0f) * 2.0f);                     // 24..31
+  return c ? (c | ((__float_as_uint(v) >> 26) & 32u)) : 0u;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
@@ -119,6 +152,34 @@ __device__ __forceinline__ void offsets_to_half4(uint32_t byte, half2v &lo, half
   };
   lo = half2v{dv(byte), dv(byte >> 2)};
   hi = half2v{dv(byte >> 4), dv(byte >> 6)};
+}
+
+// Variant formats (compute side). 2^e of the E2M1 values in h (e = the
+// unbiased exponent, 0 below 1): the exponent bits of each fp16 value with a
+// zero mantissa, at least 1.0; the exponent-scaled offset is d/8 times it.
+__device__ __forceinline__ half2v pow2e_h2(half2v q) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, q);
+  uint32_t lo = u & 0x7C00u, hi = (u >> 16) & 0x7C00u;
+  lo = lo > 0x3C00u ? lo : 0x3C00u;
+  hi = hi > 0x3C00u ? hi : 0x3C00u;
+  return __builtin_bit_cast(half2v, lo | (hi << 16));
+}
+
+// d/8 of a 4-bit two's-complement offset (AutoFP8), d clamped to [-2, +1]
+// when `clamp6` (the same tensor at level 6); exact in fp16.
+__device__ __forceinline__ _Float16 delta8_h(uint32_t nib, bool clamp6) {
+  int d = (int)(nib & 15u) - (int)((nib & 8u) << 1);
+  if (clamp6) d = d < -2 ? -2 : (d > 1 ? 1 : d);
+  return (_Float16)((float)d * 0.125f);
+}
+
+// fp16 values of two 6-bit E2M3 codes (FP6g): the code's five magnitude bits
+// at fp16 bits [11:7] read 2^(e-15) (1 + m/8) for e > 0 and m 2^-17 for e = 0;
+// times 2^14 they are 2^(e-1) (1 + m/8) and m/8, the E2M3 values (exact).
+__device__ __forceinline__ half2v e2m3x2_to_half2(uint32_t c0, uint32_t c1) {
+  auto bits = [](uint32_t c) -> uint32_t { return ((c & 0x20u) << 10) | ((c & 0x1Fu) << 7); };
+  const half2v raw = __builtin_bit_cast(half2v, bits(c0) | (bits(c1) << 16));
+  return raw * half2v{(_Float16)16384.0f, (_Float16)16384.0f};
 }
 
 // ---------------------------------------------------------------------------

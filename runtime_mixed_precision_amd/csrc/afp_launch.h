@@ -46,6 +46,8 @@ struct EncodeArgs {
   const int32_t *w_prefix;      // mask prefix table
   int32_t n_refined;
   uint8_t *w_offsets;           // [rows][n_refined]
+  // element / offset format of the encoded tensor (autofp_format)
+  int fmt;
   // producer epilogue (op != 0): the encoded tensor is v = op(z, resid),
   // [rows][k], computed on the fly from z [rows][ldz] fp32 (x is unused) and
   // written to v_out when non-null. Ops: autofp_epilogue_op.
@@ -55,18 +57,18 @@ struct EncodeArgs {
   const float *resid;           // [rows][k] (residual op)
   float *v_out;                 // [rows][k] or null
 };
-// small: every block takes the amax of the whole tensor itself (one launch,
-// for rows * k <= kSmallEncode; a.partial is not read); otherwise a.partial
-// holds the amax partials of launch_amax_partial.
-constexpr int64_t kSmallEncode = 1 << 14;
-hipError_t launch_encode(const EncodeArgs &a, bool small, hipStream_t s);
+// Small tensors (encode_is_small: rows * roundup(k/4, 64) <= 4096) are
+// encoded in one launch that takes the amax itself (a.partial is not read);
+// otherwise a.partial holds the amax partials of launch_amax_partial(_op).
+bool encode_is_small(int64_t rows, int64_t k);
+hipError_t launch_encode(const EncodeArgs &a, hipStream_t s);
 // The partial maxima of the epilogue tensor v = op(z, resid) of a.
 hipError_t launch_amax_partial_op(const EncodeArgs &a, float *partial, int n_partial, hipStream_t s);
 
 // Weight-mask selection ([AE] App. E, Alg. 1 allocation with H = I).
 hipError_t launch_select_mask(const float *w, int64_t rows, int64_t k, int32_t budget,
                               const float *partial, int n_partial, double *row_gain,
-                              double *col_gain, uint8_t *mask_out, hipStream_t s);
+                              double *col_gain, uint8_t *mask_out, int fmt, hipStream_t s);
 
 // ---- gemv.hip ----
 struct LinearArgs {
@@ -98,6 +100,8 @@ struct LinearArgs {
   // batched GEMV: fp32 partial tiles of the K splits ([splits][b][n]) and their count
   float *part;
   int32_t splits;
+  // element / offset format of both operands (autofp_format)
+  int32_t fmt;
 };
 int64_t xh_kpad(int64_t k);
 hipError_t launch_act_dequant(const LinearArgs &a, hipStream_t s);
@@ -118,6 +122,10 @@ hipError_t launch_gemv_batch(const LinearArgs &a, hipStream_t s);
 hipError_t launch_gemm(const LinearArgs &a, hipStream_t s);
 bool gemm_small_m_ok(const LinearArgs &a);   // the 64-token GEMM tile applies (K % 64 == 0)
 hipError_t launch_gemm_small_m(const LinearArgs &a, hipStream_t s);   // reads a.xh and, at level 6, a.prefix
+// The variant formats (a.fmt != AUTOFP6) at any level, K % 64 == 0: reads the
+// fp16 panel a.xh that launch_act_dequant wrote for a.fmt and (offset
+// formats) a.prefix.
+hipError_t launch_gemm_fmt(const LinearArgs &a, hipStream_t s);
 
 // ---- signals.hip ----
 int64_t entropy_slices(int64_t vocab);                        // vocabulary slices per row

@@ -31,6 +31,11 @@ bool aligned16(const void *p) { return (((uintptr_t)p) & 15u) == 0; }
 
 bool valid_k(int64_t k) { return k >= 16 && (k % 16) == 0; }
 
+bool valid_format(int32_t f) { return f >= AUTOFP_FMT_AUTOFP6 && f <= AUTOFP_FMT_FP6G; }
+
+// bytes per refined subgroup's offsets
+int64_t offset_width(int32_t f) { return f == AUTOFP_FMT_AUTOFP8 ? 2 : 1; }
+
 autofp_status from_hip(hipError_t e) { return e == hipSuccess ? AUTOFP_OK : AUTOFP_ERR_HIP; }
 
 autofp_params params_or_default(const autofp_params *p) {
@@ -88,6 +93,7 @@ autofp_status check_packed(const autofp_packed *t, int32_t kind) {
     return AUTOFP_ERR_ARG;
   if (kind == AUTOFP_WEIGHT && (t->n_refined < 0 || t->n_refined > 2 * (t->k / 16)))
     return AUTOFP_ERR_ARG;
+  if (!valid_format(t->format)) return AUTOFP_ERR_ARG;
   return AUTOFP_OK;
 }
 
@@ -105,14 +111,22 @@ autofp_status linear_common(const autofp_packed *w, const autofp_packed *x, int3
   st = check_packed(x, AUTOFP_ACTIVATION);
   if (st != AUTOFP_OK) return st;
   if (w->k != x->k) return AUTOFP_ERR_SHAPE;
+  if (w->format != x->format) return AUTOFP_ERR_ARG;
   // the GEMM addresses one tile's fp16 activation rows ([256][round_up(k, 256)])
   // with 32-bit buffer offsets
   if (x->k > kMaxLinearK) return AUTOFP_ERR_SHAPE;
   if (!y) return AUTOFP_ERR_NULL;
   if (!aligned16(y)) return AUTOFP_ERR_ARG;
   if (y_dtype != AUTOFP_F32 && y_dtype != AUTOFP_BF16) return AUTOFP_ERR_DTYPE;
-  if (!bits_dev && bits != 2 && bits != 4 && bits != 6) return AUTOFP_ERR_BITS;
-  if ((bits_dev || bits == 6) && !has_refinement(w, x)) return AUTOFP_ERR_MISSING_REFINEMENT;
+  const int32_t fmt = w->format;
+  if (fmt == AUTOFP_FMT_FP6G) {
+    // the comparator format has one level and no refinement
+    if (bits_dev || bits != 6) return AUTOFP_ERR_BITS;
+  } else {
+    if (!bits_dev && bits != 2 && bits != 4 && bits != 6 && !(bits == 8 && fmt == AUTOFP_FMT_AUTOFP8))
+      return AUTOFP_ERR_BITS;
+    if ((bits_dev || bits >= 6) && !has_refinement(w, x)) return AUTOFP_ERR_MISSING_REFINEMENT;
+  }
   if (p && p->gemv_waves != 0 && p->gemv_waves != 1 && p->gemv_waves != 2 && p->gemv_waves != 4 &&
       p->gemv_waves != 8 && p->gemv_waves != 16)
     return AUTOFP_ERR_ARG;
@@ -145,7 +159,23 @@ autofp_status linear_common(const autofp_packed *w, const autofp_packed *x, int3
   a.part = (float *)((char *)a.prefix + align_up(sizeof(int32_t) * (mask_bytes(x->k) + 1)));
   a.splits = 1;
   a.bits_rows = nullptr;
+  a.fmt = fmt;
   return AUTOFP_OK;
+}
+
+// A call that needs a variant format's own decode (levels above 4, or a
+// level read on the device): it runs on the format-generic GEMM tiles.
+bool variant_route(const LinearArgs &a) { return a.fmt != AUTOFP_FMT_AUTOFP6 && (a.bits_dev || a.bits >= 6); }
+
+autofp_status launch_variant(const LinearArgs &a, hipStream_t s) {
+  if (a.k % 64 != 0) return AUTOFP_ERR_SHAPE;
+  hipError_t e = launch_act_dequant(a, s);
+  if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  if (a.fmt != AUTOFP_FMT_FP6G && a.w_mask) {
+    e = launch_mask_prefix(a.w_mask, mask_bytes(a.k), a.prefix, s);
+    if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  }
+  return from_hip(launch_gemm_fmt(a, s));
 }
 
 
@@ -160,6 +190,8 @@ autofp_status check_quantize(const void *x, int32_t x_dtype, int32_t refine, con
       !aligned16(out->tensor_scale) || (out->mask && !aligned16(out->mask)) ||
       (out->offsets && !aligned16(out->offsets)) || (exclude_mask && !aligned16(exclude_mask)))
     return AUTOFP_ERR_ARG;
+  if (!valid_format(out->format)) return AUTOFP_ERR_ARG;
+  if (out->format == AUTOFP_FMT_FP6G && (refine || out->mask)) return AUTOFP_ERR_ARG;
   const bool act_refine = out->kind == AUTOFP_ACTIVATION && refine;
   const bool w_refine = out->kind == AUTOFP_WEIGHT && out->mask != nullptr;
   if (act_refine && (!out->mask || !out->offsets)) return AUTOFP_ERR_MISSING_REFINEMENT;
@@ -183,7 +215,7 @@ autofp_status launch_quantize(const void *x, int32_t x_dtype, int32_t refine, co
   float *partial = (float *)ws;
   int32_t *prefix = (int32_t *)((char *)ws + align_up(sizeof(float) * kAmaxBlocks));
   const int64_t n = out->rows * out->k;
-  const bool small = n <= kSmallEncode;
+  const bool small = encode_is_small(out->rows, out->k);
   const int np = amax_partial_count(n);
   EncodeArgs a{};
   if (epi) {
@@ -220,7 +252,8 @@ autofp_status launch_quantize(const void *x, int32_t x_dtype, int32_t refine, co
   a.w_prefix = prefix;
   a.n_refined = out->n_refined;
   a.w_offsets = out->offsets;
-  return from_hip(launch_encode(a, small, s));
+  a.fmt = out->format;
+  return from_hip(launch_encode(a, s));
 }
 
 // ---------------------------------------------------------------------------
@@ -286,13 +319,15 @@ const char *autofp_status_string(autofp_status s) {
   return "unknown status";
 }
 
-autofp_status autofp_packed_bytes(int64_t rows, int64_t k, int32_t kind, int32_t refine,
-                                  int32_t n_refined, size_t out_bytes[5]) {
+autofp_status autofp_packed_bytes(int64_t rows, int64_t k, int32_t kind, int32_t format,
+                                  int32_t refine, int32_t n_refined, size_t out_bytes[5]) {
   if (!out_bytes) return AUTOFP_ERR_NULL;
   if (rows < 1 || !valid_k(k)) return AUTOFP_ERR_SHAPE;
   if (kind != AUTOFP_WEIGHT && kind != AUTOFP_ACTIVATION) return AUTOFP_ERR_KIND;
   if (n_refined < 0 || n_refined > 2 * (k / 16)) return AUTOFP_ERR_ARG;
-  out_bytes[0] = (size_t)(rows * (k / 2));
+  if (!valid_format(format) || (format == AUTOFP_FMT_FP6G && refine)) return AUTOFP_ERR_ARG;
+  const int64_t ow = offset_width(format);
+  out_bytes[0] = (size_t)(rows * (format == AUTOFP_FMT_FP6G ? 3 * k / 4 : k / 2));
   out_bytes[1] = (size_t)(rows * (k / 16));
   out_bytes[2] = sizeof(float);
   out_bytes[3] = 0;
@@ -300,10 +335,10 @@ autofp_status autofp_packed_bytes(int64_t rows, int64_t k, int32_t kind, int32_t
   if (refine) {
     if (kind == AUTOFP_WEIGHT) {
       out_bytes[3] = (size_t)mask_bytes(k);
-      out_bytes[4] = (size_t)rows * (size_t)n_refined + kOffsetPad;
+      out_bytes[4] = (size_t)rows * (size_t)n_refined * (size_t)ow + kOffsetPad;
     } else {
       out_bytes[3] = (size_t)(rows * mask_bytes(k));
-      out_bytes[4] = (size_t)(rows * (k / 4));
+      out_bytes[4] = (size_t)(rows * (k / 4) * ow);
     }
   }
   return AUTOFP_OK;
@@ -347,12 +382,13 @@ autofp_status autofp_workspace_bytes(int32_t op, int64_t rows, int64_t k, size_t
   }
 }
 
-autofp_status autofp_select_weight_mask(const float *w, int64_t rows, int64_t k,
+autofp_status autofp_select_weight_mask(const float *w, int64_t rows, int64_t k, int32_t format,
                                         const autofp_params *p, uint8_t *mask_out, void *workspace,
                                         size_t workspace_bytes, void *stream) {
   if (!w || !p || !mask_out) return AUTOFP_ERR_NULL;
   if (rows < 1 || !valid_k(k) || k > 65536) return AUTOFP_ERR_SHAPE;
   if (!(p->rho >= 0.0 && p->rho <= 1.0)) return AUTOFP_ERR_ARG;
+  if (!valid_format(format) || format == AUTOFP_FMT_FP6G) return AUTOFP_ERR_ARG;
   if (!aligned16(w) || !aligned16(mask_out)) return AUTOFP_ERR_ARG;
   if (!workspace || workspace_bytes < ws_select(rows, k)) return AUTOFP_ERR_WORKSPACE;
   if (!aligned16(workspace)) return AUTOFP_ERR_ARG;
@@ -367,7 +403,7 @@ autofp_status autofp_select_weight_mask(const float *w, int64_t rows, int64_t k,
   hipError_t e = launch_amax_partial(w, AUTOFP_F32, rows * k, partial, np, s);
   if (e != hipSuccess) return AUTOFP_ERR_HIP;
   e = launch_select_mask(w, rows, k, refined_budget(k, p->rho), partial, np, row_gain, col_gain,
-                         mask_out, s);
+                         mask_out, format, s);
   return from_hip(e);
 }
 
@@ -426,8 +462,9 @@ autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_
   const autofp_status st =
       linear_common(w, x, bits, bits_dev, y, y_dtype, p, workspace, workspace_bytes, a);
   if (st != AUTOFP_OK) return st;
-  if ((bits_dev || bits == 6) && x->rows <= 16 && x->k > 65536) return AUTOFP_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
+  if (variant_route(a)) return launch_variant(a, s);
+  if ((bits_dev || bits == 6) && x->rows <= 16 && x->k > 65536) return AUTOFP_ERR_SHAPE;
   if (gemv_needs_panel(a)) {
     const hipError_t e = launch_act_dequant(a, s);
     if (e != hipSuccess) return AUTOFP_ERR_HIP;
@@ -449,6 +486,7 @@ autofp_status autofp_gemv_rows(const autofp_packed *w, const autofp_packed *x, c
   const autofp_status st =
       linear_common(w, x, 4, bits_rows, y, y_dtype, p, workspace, workspace_bytes, a);
   if (st != AUTOFP_OK) return st;
+  if (a.fmt != AUTOFP_FMT_AUTOFP6) return AUTOFP_ERR_ARG;
   if (x->k % 128 != 0) return AUTOFP_ERR_SHAPE;
   a.bits_dev = nullptr;
   a.bits_rows = bits_rows;
@@ -470,6 +508,7 @@ autofp_status autofp_gemm(const autofp_packed *w, const autofp_packed *x, int32_
       linear_common(w, x, bits, bits_dev, y, y_dtype, p, workspace, workspace_bytes, a);
   if (st != AUTOFP_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  if (variant_route(a)) return launch_variant(a, s);
   hipError_t e = launch_act_dequant(a, s);
   if (e != hipSuccess) return AUTOFP_ERR_HIP;
   if (w->mask && (bits_dev || bits == 6)) {

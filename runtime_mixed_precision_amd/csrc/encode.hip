@@ -239,10 +239,8 @@ __device__ __forceinline__ void load_pair(const void *x, int dtype, int64_t base
 }
 
 // ---------------------------------------------------------------------------
-// Encoder: one thread per subgroup (4 elements); the 4 lanes of a quad hold
+// Encoders: one thread per subgroup (4 elements); the 4 lanes of a quad hold
 // one 16-element group and share its amax through DPP quad moves.
-// Block (bx, by) covers subgroups [256 bx, 256 bx + 256) of rows by,
-// by + gridDim.y, ...
 // ---------------------------------------------------------------------------
 
 constexpr int kEncThreads = 256;
@@ -254,163 +252,239 @@ __device__ __forceinline__ float quad_max(float v) {
   return fmaxf(v, b);
 }
 
-// amax over all n elements, computed by the whole block (small tensors)
-__device__ float block_amax_all(const void *x, int dtype, int64_t n) {
-  float m = 0.0f;
-  const int64_t n8 = n / 8;   // n is a multiple of 16
-  for (int64_t u0 = threadIdx.x; u0 < n8; u0 += 4 * kEncThreads) {
-    uint4 p[4];
-    float4 f[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t u = u0 + (int64_t)j * kEncThreads;
-      if (dtype == AUTOFP_BF16) {
-        p[j] = u < n8 ? ((const uint4 *)x)[u] : make_uint4(0, 0, 0, 0);
-      } else {
-        f[2 * j] = u < n8 ? ((const float4 *)x)[2 * u] : make_float4(0.f, 0.f, 0.f, 0.f);
-        f[2 * j + 1] = u < n8 ? ((const float4 *)x)[2 * u + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (dtype == AUTOFP_BF16) {
-        const uint32_t w[4] = {p[j].x, p[j].y, p[j].z, p[j].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          m = fmaxf(m, fabsf(__uint_as_float(w[i] << 16)));
-          m = fmaxf(m, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
-        }
-      } else {
-        const float4 a = f[2 * j], b = f[2 * j + 1];
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
-      }
-    }
-  }
-  m = wave_max(m);
-  __shared__ float red[kEncThreads / 64];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < kEncThreads / 64; ++w) r = fmaxf(r, red[w]);
-  return r;
-}
-
-// amax of the whole epilogue tensor, computed by the block (small tensors)
-__device__ float block_amax_op(const EncodeArgs &a) {
-  float m = 0.0f;
-  const int64_t nq = a.k / 4, tot = a.rows * nq;
-  for (int64_t u = threadIdx.x; u < tot; u += kEncThreads) {
-    const int64_t r = u / nq;
-    m = fmaxf(m, max4(epilogue4(a, r, 4 * (u - r * nq))));
-  }
-  m = wave_max(m);
-  __shared__ float red[kEncThreads / 64];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < kEncThreads / 64; ++w) r = fmaxf(r, red[w]);
-  return r;
-}
-
-template <bool SMALL>
-__global__ __launch_bounds__(kEncThreads) void encode_kernel(EncodeArgs a) {
+// Encode of subgroup s (4 elements x) of row `row` once T is known: E2M1
+// codes, the group's E4M3 scale, and the format's offsets and masks. Every
+// lane of the wavefront calls it (quad max, ballot); the subgroups of a
+// wavefront are 64 consecutive subgroups of one row, lane l holding one with
+// s = l (mod 64). ex: the subgroup is in the exclusion mask; wbyte / wpos: the
+// weight-mask byte of s and the compacted position of s in its row.
+__device__ __forceinline__ void encode_subgroup(const EncodeArgs &a, float T, int64_t row, int64_t s,
+                                                bool live, float4 x4, uint32_t ex, uint32_t wbyte,
+                                                int32_t wpos) {
 #pragma clang fp contract(off)
-  const float amax = SMALL ? (a.op ? block_amax_op(a) : block_amax_all(a.x, a.dtype, a.rows * a.k))
-                           : fold_partials(a.partial, a.n_partial);
-  const float T = amax / 2688.0f;
+  const float x[4] = {x4.x, x4.y, x4.z, x4.w};
   const float sixT = 6.0f * T;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.tensor_scale = T;
-
   const int64_t ns = a.k / 4;                                  // subgroups per row
   const int64_t mb = (a.k + 31) / 32;                          // mask bytes per row
-  const int64_t s = (int64_t)blockIdx.x * kEncThreads + threadIdx.x;
-  const bool live = s < ns;
   const int lane = threadIdx.x & 63;
   const bool want_act = a.act_refine != 0;
   const bool want_w = a.w_mask != nullptr;
-  const uint32_t ex = (want_act && a.exclude_mask && live) ? ((uint32_t)a.exclude_mask[s >> 3] >> (s & 7)) & 1u : 0u;
+  // group scale (the quad's 16 elements)
+  const float gm = quad_max(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
+  const float b = sixT > 0.0f ? gm / sixT : 0.0f;
+  const uint32_t B = e4m3_encode(b);
+  const float sc = T * e4m3_value(B);
+  float v[4];
+  uint32_t q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = (sc != 0.0f) ? x[i] / sc : 0.0f;
+    q[i] = e2m1_encode(v[i]);
+  }
+  if (live) {
+    *(uint16_t *)(a.codes + row * (a.k / 2) + 2 * s) = (uint16_t)(q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12));
+    if ((s & 3) == 0) a.scales[row * (a.k / 16) + (s >> 2)] = (uint8_t)B;
+  }
+  if (!want_act && !want_w) return;
+
+  // offsets d = argmin |r - d step|, r = v - q (exact in fp32): 2-bit codes
+  // (step 1/8, or 2^(e-3) for the exponent-scaled format), one byte per
+  // subgroup; AutoFP8: 4-bit codes (step 1/8), two bytes per subgroup
+  uint32_t ob = 0;
+  if (a.fmt == AUTOFP_FMT_AUTOFP8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ob |= ((uint32_t)offset8(v[i] - e2m1_value(q[i])) & 15u) << (4 * i);
+  } else if (a.fmt == AUTOFP_FMT_AUTOFP6E) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ob |= offset_code((v[i] - e2m1_value(q[i])) * e2m1_inv_pow2e(q[i])) << (2 * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ob |= offset_code(v[i] - e2m1_value(q[i])) << (2 * i);
+  }
+  const bool wide = a.fmt == AUTOFP_FMT_AUTOFP8;
+
+  if (want_act) {
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float r = v[i] - e2m1_value(q[i]);
+      const float rr = r * r;
+      const float vv = v[i] * v[i];
+      num = (i == 0) ? rr : num + rr;
+      den = (i == 0) ? vv : den + vv;
+    }
+    const float thr = a.thresh * den;
+    const bool refine = live && den > 0.0f && num > thr && !ex;
+    const uint64_t bits = __ballot(refine);
+    if (live) {
+      if (wide) *(uint16_t *)(a.act_offsets + row * 2 * ns + 2 * s) = (uint16_t)(refine ? ob : 0u);
+      else a.act_offsets[row * ns + s] = (uint8_t)(refine ? ob : 0u);
+      if ((s & 7) == 0) a.act_mask[row * mb + (s >> 3)] = (uint8_t)(bits >> lane);
+    }
+  }
+  // the mask's popcount should equal n_refined; a mask with more refined
+  // subgroups writes only the first n_refined of each row
+  if (want_w && live && ((wbyte >> (s & 7)) & 1u) && wpos < a.n_refined) {
+    if (wide) *(uint16_t *)(a.w_offsets + (row * (int64_t)a.n_refined + wpos) * 2) = (uint16_t)ob;
+    else a.w_offsets[row * (int64_t)a.n_refined + wpos] = (uint8_t)ob;
+  }
+}
+
+// FP6g ([AE] App. B.2): Eqs. 2-3 with the E2M3 maximum 7.5 in place of 6,
+// T = amax / (7.5 * 448), B_j = E4M3(amax_j / (7.5 T)), q_i = E2M3(x_i / (T B_j));
+// four 6-bit codes in three bytes (code i of a subgroup at bits 6i..6i+5 of a
+// little-endian 24-bit word). Called like encode_subgroup.
+__device__ __forceinline__ void encode_subgroup_fp6g(const EncodeArgs &a, float T, int64_t row, int64_t s,
+                                                     bool live, float4 x4) {
+#pragma clang fp contract(off)
+  const float x[4] = {x4.x, x4.y, x4.z, x4.w};
+  const float sevT = 7.5f * T;
+  const float gm = quad_max(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
+  const float b = sevT > 0.0f ? gm / sevT : 0.0f;
+  const uint32_t B = e4m3_encode(b);
+  const float sc = T * e4m3_value(B);
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) word |= e2m3_encode((sc != 0.0f) ? x[i] / sc : 0.0f) << (6 * i);
+  if (live) {
+    uint8_t *c = a.codes + row * (3 * a.k / 4) + 3 * s;
+    c[0] = (uint8_t)word;
+    c[1] = (uint8_t)(word >> 8);
+    c[2] = (uint8_t)(word >> 16);
+    if ((s & 3) == 0) a.scales[row * (a.k / 16) + (s >> 2)] = (uint8_t)B;
+  }
+}
+
+// tensor scale T = amax / (max element * 448)
+__device__ __forceinline__ float tensor_scale_of(const EncodeArgs &a, float amax) {
+  return a.fmt == AUTOFP_FMT_FP6G ? amax / 3360.0f : amax / 2688.0f;
+}
+
+// The four elements of subgroup s of row `row` of the tensor to encode (x,
+// or the epilogue's v).
+__device__ __forceinline__ float4 load_quad(const EncodeArgs &a, int64_t row, int64_t s) {
+  if (a.op) return epilogue4(a, row, 4 * s);
+  const int64_t e = row * a.k + 4 * s;
+  if (a.dtype == AUTOFP_BF16) {
+    const uint2 p = *(const uint2 *)((const uint16_t *)a.x + e);
+    return make_float4(__uint_as_float(p.x << 16), __uint_as_float(p.x & 0xFFFF0000u),
+                       __uint_as_float(p.y << 16), __uint_as_float(p.y & 0xFFFF0000u));
+  }
+  return *(const float4 *)((const float *)a.x + e);
+}
+
+// The same with the source fixed at compile time: 0 x fp32, 1 x bf16, or
+// 1 + the epilogue op (2 copy, 3 residual, 4 SwiGLU).
+template <int SRC>
+__device__ __forceinline__ float4 load_quad_t(const EncodeArgs &a, int64_t row, int64_t s) {
+  if constexpr (SRC >= 2) {
+    return epilogue4(a, row, 4 * s);
+  } else if constexpr (SRC == 1) {
+    const uint2 p = *(const uint2 *)((const uint16_t *)a.x + row * a.k + 4 * s);
+    return make_float4(__uint_as_float(p.x << 16), __uint_as_float(p.x & 0xFFFF0000u),
+                       __uint_as_float(p.y << 16), __uint_as_float(p.y & 0xFFFF0000u));
+  } else {
+    return *(const float4 *)((const float *)a.x + row * a.k + 4 * s);
+  }
+}
+
+// Encoder of larger tensors: T from the amax partials of the previous launch;
+// block (bx, by) covers subgroups [256 bx, 256 bx + 256) of rows by,
+// by + gridDim.y, ...
+__global__ __launch_bounds__(kEncThreads) void encode_kernel(EncodeArgs a) {
+  const float T = tensor_scale_of(a, fold_partials(a.partial, a.n_partial));
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.tensor_scale = T;
+  const int64_t ns = a.k / 4;
+  const int64_t s = (int64_t)blockIdx.x * kEncThreads + threadIdx.x;
+  const bool live = s < ns;
+  const bool fp6g = a.fmt == AUTOFP_FMT_FP6G;
+  const uint32_t ex = (a.act_refine && a.exclude_mask && live) ? ((uint32_t)a.exclude_mask[s >> 3] >> (s & 7)) & 1u : 0u;
   uint32_t wbyte = 0;
   int32_t wpos = 0;
-  if (want_w && live) {
+  if (a.w_mask && live) {
     wbyte = a.w_mask[s >> 3];
     wpos = a.w_prefix[s >> 3] + __popc(wbyte & ((1u << (s & 7)) - 1u));
   }
-
   for (int64_t row = blockIdx.y; row < a.rows; row += gridDim.y) {
-    float x[4] = {0.f, 0.f, 0.f, 0.f};
-    if (live && a.op) {
-      const float4 v4 = epilogue4(a, row, 4 * s);
-      x[0] = v4.x;
-      x[1] = v4.y;
-      x[2] = v4.z;
-      x[3] = v4.w;
-      if (a.v_out) *(float4 *)(a.v_out + row * a.k + 4 * s) = v4;
-    } else if (live) {
-      const int64_t e = row * a.k + 4 * s;
-      if (a.dtype == AUTOFP_BF16) {
-        const uint2 p = *(const uint2 *)((const uint16_t *)a.x + e);
-        x[0] = __uint_as_float(p.x << 16);
-        x[1] = __uint_as_float(p.x & 0xFFFF0000u);
-        x[2] = __uint_as_float(p.y << 16);
-        x[3] = __uint_as_float(p.y & 0xFFFF0000u);
-      } else {
-        const float4 p = *(const float4 *)((const float *)a.x + e);
-        x[0] = p.x;
-        x[1] = p.y;
-        x[2] = p.z;
-        x[3] = p.w;
-      }
-    }
-    // group scale (the quad's 16 elements)
-    const float gm = quad_max(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
-    const float b = sixT > 0.0f ? gm / sixT : 0.0f;
-    const uint32_t B = e4m3_encode(b);
-    const float sc = T * e4m3_value(B);
-    float v[4];
-    uint32_t q[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[i] = (sc != 0.0f) ? x[i] / sc : 0.0f;
-      q[i] = e2m1_encode(v[i]);
-    }
+    float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
     if (live) {
-      *(uint16_t *)(a.codes + row * (a.k / 2) + 2 * s) = (uint16_t)(q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12));
-      if ((s & 3) == 0) a.scales[row * (a.k / 16) + (s >> 2)] = (uint8_t)B;
+      v4 = load_quad(a, row, s);
+      if (a.op && a.v_out) *(float4 *)(a.v_out + row * a.k + 4 * s) = v4;
     }
-    if (!want_act && !want_w) continue;
-
-    // offsets d = argmin |r - d/8|, r = v - q (exact in fp32)
-    uint32_t ob = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ob |= offset_code(v[i] - e2m1_value(q[i])) << (2 * i);
-
-    if (want_act) {
-      float num = 0.0f, den = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float r = v[i] - e2m1_value(q[i]);
-        const float rr = r * r;
-        const float vv = v[i] * v[i];
-        num = (i == 0) ? rr : num + rr;
-        den = (i == 0) ? vv : den + vv;
-      }
-      const float thr = a.thresh * den;
-      const bool refine = live && den > 0.0f && num > thr && !ex;
-      const uint64_t bits = __ballot(refine);
-      if (live) {
-        a.act_offsets[row * ns + s] = (uint8_t)(refine ? ob : 0u);
-        if ((s & 7) == 0) a.act_mask[row * mb + (s >> 3)] = (uint8_t)(bits >> lane);
-      }
-    }
-    // the mask's popcount should equal n_refined; a mask with more refined
-    // subgroups writes only the first n_refined of each row
-    if (want_w && live && ((wbyte >> (s & 7)) & 1u) && wpos < a.n_refined)
-      a.w_offsets[row * (int64_t)a.n_refined + wpos] = (uint8_t)ob;
+    if (fp6g) encode_subgroup_fp6g(a, T, row, s, live, v4);
+    else encode_subgroup(a, T, row, s, live, v4, ex, wbyte, wpos);
   }
 }
+
+// ---------------------------------------------------------------------------
+// One-launch encoder of small tensors (rows * roundup(k/4, 64) <= 4096
+// subgroup slots): slot u holds subgroup s = u mod nqp of row u / nqp, nqp =
+// k/4 rounded up to 64 (so a wavefront never spans two rows). Block bx of TPB
+// threads encodes slots [TPB bx, TPB bx + TPB); every block loads all slots
+// (thread t: slots j TPB + t, j < 4096 / TPB) with every load in flight at
+// once, takes the amax of the whole tensor from them and encodes its own slot
+// from the registers: one round trip to memory, no second launch. The mask
+// bytes the encode needs are loaded before the reduction.
+// ---------------------------------------------------------------------------
+constexpr int kSmallSlots = 4096;
+constexpr int kSmallTPB = 512;
+
+template <int TPB, int SRC>
+__global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t nqp) {
+  constexpr int SPT = kSmallSlots / TPB;
+  static_assert((SPT & (SPT - 1)) == 0, "slot groups per thread: a power of two");
+  const int32_t nq = (int32_t)(a.k / 4);
+  const int32_t tot = (int32_t)a.rows * nqp;
+  const int bx = (int)blockIdx.x;
+  const int32_t u = bx * TPB + (int32_t)threadIdx.x;
+  const int32_t row = u / nqp, s = u - row * nqp;
+  const bool live = u < tot && s < nq;
+  const bool fp6g = a.fmt == AUTOFP_FMT_FP6G;
+  uint32_t ex = 0, wbyte = 0;
+  int32_t wpos = 0;
+  if (!fp6g && a.act_refine && a.exclude_mask && live) ex = ((uint32_t)a.exclude_mask[s >> 3] >> (s & 7)) & 1u;
+  if (!fp6g && a.w_mask && live) {
+    wbyte = a.w_mask[s >> 3];
+    wpos = a.w_prefix[s >> 3] + __popc(wbyte & ((1u << (s & 7)) - 1u));
+  }
+  // slot groups in the order bx, bx + 1, ... (mod SPT): the first is the
+  // block's own
+  float m = 0.0f;
+  float4 own = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int32_t uj = ((bx + j) & (SPT - 1)) * TPB + (int32_t)threadIdx.x;
+    const int32_t r = uj / nqp, sq = uj - r * nqp;
+    const bool ok = uj < tot && sq < nq;
+    float4 v = load_quad_t<SRC>(a, ok ? r : 0, ok ? sq : 0);   // slot 0 stands in for absent slots
+    v = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+    m = fmaxf(m, max4(v));
+    if (j == 0) own = v;
+  }
+  m = wave_max(m);
+  __shared__ float red[TPB / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float amax = red[0];
+#pragma unroll
+  for (int w = 1; w < TPB / 64; ++w) amax = fmaxf(amax, red[w]);
+  const float T = tensor_scale_of(a, amax);
+  if (bx == 0 && threadIdx.x == 0) *a.tensor_scale = T;
+
+  if (SRC >= 2 && live && a.v_out) *(float4 *)(a.v_out + (int64_t)row * a.k + 4 * s) = own;
+  if (fp6g) encode_subgroup_fp6g(a, T, row, s, live, own);
+  else encode_subgroup(a, T, row, s, live, own, ex, wbyte, wpos);
+}
+
+}  // namespace
+
+int64_t encode_slots_per_row(int64_t k) { return (k / 4 + 63) / 64 * 64; }
+
+bool encode_is_small(int64_t rows, int64_t k) {
+  return rows >= 1 && rows * encode_slots_per_row(k) <= kSmallSlots;
+}
+
+namespace {
 
 // ---------------------------------------------------------------------------
 // Weight-mask selection ([AE] App. E, Alg. 1 allocation, identity Hessian)
@@ -421,7 +495,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(EncodeArgs a) {
 __global__ __launch_bounds__(kThreads) void weight_gain_kernel(const float *__restrict__ w,
                                                                int64_t rows, int64_t k,
                                                                const float *partial, int n_partial,
-                                                               double *__restrict__ row_gain) {
+                                                               double *__restrict__ row_gain, int fmt) {
 #pragma clang fp contract(off)
   const float amax = fold_partials(partial, n_partial);
   const float T = amax / 2688.0f;
@@ -447,11 +521,18 @@ __global__ __launch_bounds__(kThreads) void weight_gain_kernel(const float *__re
     for (int i = 0; i < 4; ++i) {
       const int el = 4 * sg + i;
       const double q = (double)e2m1_value(e.q[el]);
-      const uint32_t dc = offset_code(e.v[el] - e2m1_value(e.q[el]));
-      const double d = (double)((int)dc - (int)((dc & 2u) << 1));
+      const float r = e.v[el] - e2m1_value(e.q[el]);
+      double delta;
+      if (fmt == AUTOFP_FMT_AUTOFP8) {
+        delta = (double)offset8(r) / 8.0;
+      } else {
+        const float inv = fmt == AUTOFP_FMT_AUTOFP6E ? e2m1_inv_pow2e(e.q[el]) : 1.0f;
+        const uint32_t dc = offset_code(r * inv);
+        delta = (double)((int)dc - (int)((dc & 2u) << 1)) / 8.0 / (double)inv;
+      }
       const double x = (double)xv[el];
       const double eb = x - tb * q;
-      const double er = x - tb * (q + d / 8.0);
+      const double er = x - tb * (q + delta);
       const double ge = eb * eb - er * er;
       g = (i == 0) ? ge : g + ge;
     }
@@ -574,7 +655,24 @@ hipError_t launch_mask_prefix(const uint8_t *mask, int64_t nbytes, int32_t *pref
   return hipGetLastError();
 }
 
-hipError_t launch_encode(const EncodeArgs &a, bool small, hipStream_t s) {
+hipError_t launch_encode(const EncodeArgs &a, hipStream_t s) {
+  if (encode_is_small(a.rows, a.k)) {
+    const int64_t nqp = encode_slots_per_row(a.k);
+    const unsigned gx = (unsigned)((a.rows * nqp + kSmallTPB - 1) / kSmallTPB);
+    const int src = a.op ? 1 + a.op : (a.dtype == AUTOFP_BF16 ? 1 : 0);
+    switch (src) {
+#define AFP_SMALL(S) \
+  case S: hipLaunchKernelGGL((encode_small_kernel<kSmallTPB, S>), dim3(gx), dim3(kSmallTPB), 0, s, a, (int32_t)nqp); break
+      AFP_SMALL(0);
+      AFP_SMALL(1);
+      AFP_SMALL(2);
+      AFP_SMALL(3);
+      AFP_SMALL(4);
+#undef AFP_SMALL
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const int64_t ns = a.k / 4;
   const int64_t gx = (ns + kEncThreads - 1) / kEncThreads;
   // rows per block: enough blocks to fill the chip, few enough that the
@@ -582,15 +680,13 @@ hipError_t launch_encode(const EncodeArgs &a, bool small, hipStream_t s) {
   int64_t gy = (16384 + gx - 1) / gx;
   gy = gy < a.rows ? gy : a.rows;
   gy = gy < 65535 ? gy : 65535;
-  const dim3 grid((unsigned)gx, (unsigned)gy);
-  if (small) hipLaunchKernelGGL(encode_kernel<true>, grid, dim3(kEncThreads), 0, s, a);
-  else hipLaunchKernelGGL(encode_kernel<false>, grid, dim3(kEncThreads), 0, s, a);
+  hipLaunchKernelGGL(encode_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kEncThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_select_mask(const float *w, int64_t rows, int64_t k, int32_t budget,
                               const float *partial, int n_partial, double *row_gain,
-                              double *col_gain, uint8_t *mask_out, hipStream_t s) {
+                              double *col_gain, uint8_t *mask_out, int fmt, hipStream_t s) {
   const int64_t P2 = (k + 31) / 32;
   const int64_t ncol = k / 4;
   const int64_t ngroups = k / 16;
@@ -598,7 +694,7 @@ hipError_t launch_select_mask(const float *w, int64_t rows, int64_t k, int32_t b
   int32_t *csg = (int32_t *)(cgain + 2 * ngroups);
   int32_t *sel = csg + 2 * ngroups;
   hipLaunchKernelGGL(weight_gain_kernel, dim3(grid_for(rows * P2, kThreads)), dim3(kThreads), 0, s,
-                     w, rows, k, partial, n_partial, row_gain);
+                     w, rows, k, partial, n_partial, row_gain, fmt);
   hipLaunchKernelGGL(gain_colsum_kernel, dim3(grid_for(ncol, kThreads)), dim3(kThreads), 0, s,
                      row_gain, rows, ncol, col_gain);
   hipLaunchKernelGGL(gain_candidates_kernel, dim3(grid_for(ngroups, kThreads)), dim3(kThreads), 0, s,

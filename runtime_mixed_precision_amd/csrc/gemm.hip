@@ -215,6 +215,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a) {
 // of v_mfma_f32_32x32x16_f16 tiles over its part.
 // ---------------------------------------------------------------------------
 
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3v __attribute__((ext_vector_type(3)));
 #define AFP_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
@@ -244,7 +245,13 @@ __device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * 128
 // every weight and activation byte is still read once; a step past a group's
 // range (or past K) loads zeros. At the end the groups' accumulators are
 // summed through LDS in group order (deterministic) by group 0.
-template <int BM, int BN, int NW, int KG = 1>
+//
+// FMT (autofp_format) selects the weight decode: AUTOFP6 (the default) and
+// AUTOFP6E (its offsets scaled by 2^e of each element's E2M1 value) read one
+// offset byte per refined subgroup; AUTOFP8 two (4-bit d, clamped to
+// [-2, +1] at level 6); FP6G reads 24 bytes of E2M3 codes per 32 elements and
+// no offsets.
+template <int BM, int BN, int NW, int KG = 1, int FMT = AUTOFP_FMT_AUTOFP6>
 __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
   constexpr int WGM = (NW >= 16 && BM >= 256) ? 4 : 2;   // wavefronts along M
   constexpr int WGN = NW / WGM;                         // wavefronts along N
@@ -273,18 +280,29 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
   const int64_t mt = blockIdx.x % mtiles;
   const int64_t nt = blockIdx.x / mtiles;
   const int64_t m0 = mt * BM, n0 = nt * BN;
+  constexpr bool F8 = FMT == AUTOFP_FMT_AUTOFP8;
+  constexpr bool G6 = FMT == AUTOFP_FMT_FP6G;
+  constexpr int64_t OW = F8 ? 2 : 1;                    // offset bytes per refined subgroup
   const int L = run_level(a);
-  const bool refine_w = (L == 6) && a.w_mask != nullptr && a.w_offsets != nullptr && a.n_refined > 0;
+  const bool refine_w = !G6 && (L == 6 || (F8 && L == 8)) && a.w_mask != nullptr && a.w_offsets != nullptr &&
+                        a.n_refined > 0;
   const int64_t R = a.n_refined;
+  const int64_t CB = G6 ? 3 * K / 4 : K / 2;            // code bytes per weight row
 
   // level 6: per-block tables after the stages. dtab[byte] = the four fp16
   // offsets d/8 of an offset byte; stab[mask byte] = the byte selectors that
   // spread a row's compacted offset bytes over the 8 subgroups of 32
   // elements (0x0C: no offset). A lookup replaces a few dozen bit operations
-  // per 32 decoded weights.
+  // per 32 decoded weights. AUTOFP8: t8[byte] = the two fp16 offsets d/8 of
+  // a byte of two 4-bit offsets.
   uint2 *dtab = (uint2 *)(lds + KG * 2 * STAGE);
   uint2 *stab = dtab + 256;
-  if (refine_w) {
+  uint32_t *t8 = (uint32_t *)dtab;
+  if (refine_w && F8) {
+    for (int i = (int)threadIdx.x; i < 256; i += (int)blockDim.x)
+      t8[i] = __builtin_bit_cast(uint32_t, half2v{delta8_h((uint32_t)i, L == 6), delta8_h((uint32_t)i >> 4, L == 6)});
+    __syncthreads();
+  } else if (refine_w) {
     for (int i = (int)threadIdx.x; i < 256; i += (int)blockDim.x) {
       dtab[i] = delta_words((uint32_t)i);
       uint32_t sel[2] = {0, 0}, j = 0;
@@ -305,9 +323,10 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
   const __amdgpu_buffer_rsrc_t rx = rsrc(a.xh + m0 * a.kpad, mrows * a.kpad * 2);
   // weight rows of this block: rows past n read as zero
   const int64_t nrows = (a.n - n0) < BN ? (a.n - n0) : BN;
-  const __amdgpu_buffer_rsrc_t rc = rsrc(a.w_codes + n0 * (K >> 1), nrows * (K >> 1));
+  const __amdgpu_buffer_rsrc_t rc = rsrc(a.w_codes + n0 * CB, nrows * CB);
   const __amdgpu_buffer_rsrc_t rs = rsrc(a.w_scales + n0 * (K >> 4), nrows * (K >> 4));
-  const __amdgpu_buffer_rsrc_t ro = rsrc(refine_w ? a.w_offsets + n0 * R : a.w_codes, refine_w ? nrows * R + 16 : 0);
+  const __amdgpu_buffer_rsrc_t ro =
+      rsrc(refine_w ? a.w_offsets + n0 * R * OW : a.w_codes, refine_w ? nrows * R * OW + 16 : 0);
 
   // DMA mapping: instruction d of a wavefront covers A rows 8 (APW wave + d) ..
   // + 7; lane i -> row + i / 8, LDS chunk i % 8 (global chunk (i % 8) ^ ((row / 2) % 8))
@@ -329,8 +348,11 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
   const bool w_thread = tid < WITEMS / HPT;   // whole wavefronts: WITEMS is a multiple of 64
   struct WRegs {
     u32x4v c[HPT];
+    u32x2v cx[HPT];   // FP6G: the last 8 of the 24 code bytes
     uint32_t s;
     u32x3v o[HPT];
+    u32x4v o4[HPT];   // AUTOFP8: 20 bytes of compacted offsets
+    uint32_t o5[HPT];
     int32_t pos[HPT];
     uint32_t mb[HPT];
   };
@@ -341,8 +363,14 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
 #pragma unroll
     for (int i = 0; i < HPT; ++i) {
       const int64_t ke = k0 + 32 * (h0 + i);
-      w.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, kin ? (int)(wr * (K >> 1) + (ke >> 1)) : (int)0x80000000u,
-                                                     0, 0);
+      if constexpr (G6) {
+        const int off = (int)(wr * CB + 3 * ke / 4);
+        w.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, kin ? off : (int)0x80000000u, 0, 0);
+        w.cx[i] = __builtin_amdgcn_raw_buffer_load_b64(rc, kin ? off + 16 : (int)0x80000000u, 0, 0);
+      } else {
+        w.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, kin ? (int)(wr * (K >> 1) + (ke >> 1)) : (int)0x80000000u,
+                                                       0, 0);
+      }
     }
     if (HPT == 2) {
       w.s = __builtin_amdgcn_raw_buffer_load_b32(rs, kin ? (int)(wr * (K >> 4) + (k0 >> 4)) : (int)0x80000000u, 0, 0);
@@ -356,8 +384,14 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
         const int64_t mi = kin ? (k0 >> 5) + h0 + i : 0;   // mask byte (32 elements)
         w.mb[i] = kin ? a.w_mask[mi] : 0u;
         w.pos[i] = a.prefix[mi];
-        const uint32_t al = (uint32_t)((wr * R + w.pos[i]) & ~(int64_t)3);
-        w.o[i] = __builtin_amdgcn_raw_buffer_load_b96(ro, (int)al, 0, 0);
+        if constexpr (F8) {
+          const uint32_t al = (uint32_t)(((wr * R + w.pos[i]) * 2) & ~(int64_t)3);
+          w.o4[i] = __builtin_amdgcn_raw_buffer_load_b128(ro, (int)al, 0, 0);
+          w.o5[i] = __builtin_amdgcn_raw_buffer_load_b32(ro, (int)(al + 16), 0, 0);
+        } else {
+          const uint32_t al = (uint32_t)((wr * R + w.pos[i]) & ~(int64_t)3);
+          w.o[i] = __builtin_amdgcn_raw_buffer_load_b96(ro, (int)al, 0, 0);
+        }
       }
     }
   };
@@ -365,15 +399,56 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
     unsigned char *base = glds + stage * STAGE + A_BYTES;
 #pragma unroll
     for (int i = 0; i < HPT; ++i) {
-      uint32_t w4[4] = {w.c[i][0], w.c[i][1], w.c[i][2], w.c[i][3]};
-      if (L == 2) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w4[j] = autofp2_codes(w4[j]);
-      }
       half8v h[4];
+      if constexpr (G6) {
+        // 32 six-bit codes in 24 bytes: 8 codes (48 bits) per fragment, at
+        // bits 0, 48, 96 and 144 of the six dwords
+        const uint64_t win4[4] = {
+            ((uint64_t)w.c[i][1] << 32) | w.c[i][0], (((uint64_t)w.c[i][2] << 32) | w.c[i][1]) >> 16,
+            ((uint64_t)w.cx[i][0] << 32) | w.c[i][3], (((uint64_t)w.cx[i][1] << 32) | w.cx[i][0]) >> 16};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) h[j] = fp4x8_to_half8(w4[j]);
-      if (refine_w) {
+        for (int j = 0; j < 4; ++j) {
+          const uint64_t win = win4[j];
+          half2v p[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            p[e] = e2m3x2_to_half2((uint32_t)(win >> (12 * e)) & 63u, (uint32_t)(win >> (12 * e + 6)) & 63u);
+          h[j] = half8v{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+        }
+      } else {
+        uint32_t w4[4] = {w.c[i][0], w.c[i][1], w.c[i][2], w.c[i][3]};
+        if (L == 2) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w4[j] = autofp2_codes(w4[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = fp4x8_to_half8(w4[j]);
+      }
+      if (F8 && refine_w) {
+        // the (at most 8) two-byte offset words of these 32 elements, in
+        // subgroup order, from the 20 loaded bytes shifted by the misalignment
+        const uint32_t m = w.mb[i];
+        const uint32_t sh = (uint32_t)(((wr * R + w.pos[i]) * 2) & 3);
+        const uint32_t W0 = __builtin_amdgcn_alignbyte(w.o4[i][1], w.o4[i][0], sh);
+        const uint32_t W1 = __builtin_amdgcn_alignbyte(w.o4[i][2], w.o4[i][1], sh);
+        const uint32_t W2 = __builtin_amdgcn_alignbyte(w.o4[i][3], w.o4[i][2], sh);
+        const uint32_t W3 = __builtin_amdgcn_alignbyte(w.o5[i], w.o4[i][3], sh);
+        const uint64_t lo = (uint64_t)W0 | ((uint64_t)W1 << 32), hi = (uint64_t)W2 | ((uint64_t)W3 << 32);
+        uint32_t wd[8];
+        uint32_t j = 0;
+#pragma unroll
+        for (int sg = 0; sg < 8; ++sg) {
+          const uint32_t on = (m >> sg) & 1u;
+          const uint64_t src = j < 4 ? lo : hi;
+          wd[sg] = on ? (uint32_t)(src >> (16 * (j & 3))) & 0xFFFFu : 0u;
+          j += on;
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t a0 = wd[2 * p], a1 = wd[2 * p + 1];
+          h[p] += __builtin_bit_cast(half8v, make_uint4(t8[a0 & 0xFFu], t8[a0 >> 8], t8[a1 & 0xFFu], t8[a1 >> 8]));
+        }
+      } else if (refine_w) {
         // the (at most 8) offset bytes of these 32 elements, in subgroup order;
         // one byte per subgroup (0 where not refined) via a byte permute
         const uint32_t m = w.mb[i];
@@ -386,7 +461,19 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
         for (int p = 0; p < 4; ++p) {
           const uint2 de = dtab[(E[p >> 1] >> (16 * (p & 1))) & 0xFFu];
           const uint2 dd = dtab[(E[p >> 1] >> (16 * (p & 1) + 8)) & 0xFFu];
-          h[p] += __builtin_bit_cast(half8v, make_uint4(de.x, de.y, dd.x, dd.y));
+          const half8v dl = __builtin_bit_cast(half8v, make_uint4(de.x, de.y, dd.x, dd.y));
+          if constexpr (FMT == AUTOFP_FMT_AUTOFP6E) {
+            // delta = d/8 * 2^e of each element's E2M1 value
+            const uint4 hv = __builtin_bit_cast(uint4, h[p]);
+            const uint4 fv = make_uint4(
+                __builtin_bit_cast(uint32_t, pow2e_h2(__builtin_bit_cast(half2v, hv.x))),
+                __builtin_bit_cast(uint32_t, pow2e_h2(__builtin_bit_cast(half2v, hv.y))),
+                __builtin_bit_cast(uint32_t, pow2e_h2(__builtin_bit_cast(half2v, hv.z))),
+                __builtin_bit_cast(uint32_t, pow2e_h2(__builtin_bit_cast(half2v, hv.w))));
+            h[p] += dl * __builtin_bit_cast(half8v, fv);
+          } else {
+            h[p] += dl;
+          }
         }
       }
       const uint32_t sbytes = (HPT == 2) ? (w.s >> (16 * i)) : w.s;
@@ -532,6 +619,47 @@ hipError_t launch_gemm_small_m(const LinearArgs &a, hipStream_t s) {
                        dim3(64 * 4 * 4), lds, s, a);
   }
   return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_gemm_fmt_t(const LinearArgs &a, hipStream_t s) {
+  const int64_t nt256 = (a.n + 255) / 256;
+  if (a.b >= 128) {
+    const int64_t mtiles = (a.b + kBM2 - 1) / kBM2;
+    // AUTOFP8 decodes on 128-row tiles (256 rows would exceed 128 VGPRs)
+    if constexpr (FMT != AUTOFP_FMT_AUTOFP8) {
+      if (mtiles * nt256 >= 256) {
+        const size_t lds = 2 * (size_t)(kBM2 * kBK2 * 2 + 256 * kBK2 * 2) + kTabBytes;
+        hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 256, kGemmWaves, 1, FMT>), dim3((unsigned)(mtiles * nt256)),
+                           dim3(64 * kGemmWaves), lds, s, a);
+        return hipGetLastError();
+      }
+    }
+    const size_t lds = 2 * (size_t)(kBM2 * kBK2 * 2 + 128 * kBK2 * 2) + kTabBytes;
+    hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 128, kGemmWaves, 1, FMT>),
+                       dim3((unsigned)(mtiles * ((a.n + 127) / 128))), dim3(64 * kGemmWaves), lds, s, a);
+    return hipGetLastError();
+  }
+  const int64_t mtiles = (a.b + 63) / 64;
+  if (mtiles * nt256 >= 256) {
+    const size_t lds = 2 * (size_t)(64 * kBK2 * 2 + 256 * kBK2 * 2) + kTabBytes;
+    hipLaunchKernelGGL((gemm_lds_kernel<64, 256, kDecodeWaves, 1, FMT>), dim3((unsigned)(mtiles * nt256)),
+                       dim3(64 * kDecodeWaves), lds, s, a);
+  } else {
+    const size_t lds = 4 * 2 * (size_t)(64 * kBK2 * 2 + 64 * kBK2 * 2) + kTabBytes;
+    hipLaunchKernelGGL((gemm_lds_kernel<64, 64, 4, 4, FMT>), dim3((unsigned)(mtiles * ((a.n + 63) / 64))),
+                       dim3(64 * 4 * 4), lds, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fmt(const LinearArgs &a, hipStream_t s) {
+  switch (a.fmt) {
+    case AUTOFP_FMT_AUTOFP6E: return launch_gemm_fmt_t<AUTOFP_FMT_AUTOFP6E>(a, s);
+    case AUTOFP_FMT_AUTOFP8: return launch_gemm_fmt_t<AUTOFP_FMT_AUTOFP8>(a, s);
+    case AUTOFP_FMT_FP6G: return launch_gemm_fmt_t<AUTOFP_FMT_FP6G>(a, s);
+    default: return launch_gemm(a, s);
+  }
 }
 
 hipError_t launch_gemm(const LinearArgs &a, hipStream_t s) {

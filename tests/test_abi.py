@@ -65,11 +65,24 @@ def test_default_params_are_the_papers(N):
 def test_sizes(N):
     L = N.lib()
     out = (C.c_size_t * 5)()
-    assert L.autofp_packed_bytes(16, 256, N.ACTIVATION, 1, 0, out) == 0
+    A6 = N.FMT_AUTOFP6
+    assert L.autofp_packed_bytes(16, 256, N.ACTIVATION, A6, 1, 0, out) == 0
     assert list(out) == [16 * 128, 16 * 16, 4, 16 * 8, 16 * 64]
-    assert L.autofp_packed_bytes(256, 4096, N.WEIGHT, 1, 204, out) == 0
+    assert L.autofp_packed_bytes(256, 4096, N.WEIGHT, A6, 1, 204, out) == 0
     assert list(out) == [256 * 2048, 256 * 256, 4, 128, 256 * 204 + 16]
-    assert L.autofp_packed_bytes(16, 250, N.WEIGHT, 0, 0, out) == 2
+    assert L.autofp_packed_bytes(16, 250, N.WEIGHT, A6, 0, 0, out) == 2
+    # the variant formats: AutoFP6E stores as AutoFP6; AutoFP8 two offset
+    # bytes per subgroup; FP6G 3k/4 code bytes and no refinement
+    assert L.autofp_packed_bytes(256, 4096, N.WEIGHT, N.FMT_AUTOFP6E, 1, 204, out) == 0
+    assert list(out) == [256 * 2048, 256 * 256, 4, 128, 256 * 204 + 16]
+    assert L.autofp_packed_bytes(256, 4096, N.WEIGHT, N.FMT_AUTOFP8, 1, 204, out) == 0
+    assert list(out) == [256 * 2048, 256 * 256, 4, 128, 2 * 256 * 204 + 16]
+    assert L.autofp_packed_bytes(16, 256, N.ACTIVATION, N.FMT_AUTOFP8, 1, 0, out) == 0
+    assert list(out) == [16 * 128, 16 * 16, 4, 16 * 8, 16 * 128]
+    assert L.autofp_packed_bytes(16, 256, N.ACTIVATION, N.FMT_FP6G, 0, 0, out) == 0
+    assert list(out) == [16 * 192, 16 * 16, 4, 0, 0]
+    assert L.autofp_packed_bytes(16, 256, N.ACTIVATION, N.FMT_FP6G, 1, 0, out) == 8
+    assert L.autofp_packed_bytes(16, 256, N.ACTIVATION, 4, 0, 0, out) == 8
     n = C.c_int32()
     p = params(N)
     for k, want in ((4096, 204), (14336, 716), (256, 12), (16, 0)):
@@ -114,6 +127,12 @@ def test_quantize_rejects_bad_arguments(N):
     assert q(FAKE, N.F32, 1, C.byref(good)) == 6          # refine without mask/offsets
     assert q(FAKE + 4, N.F32, 0, C.byref(good)) == 8      # misaligned input
     assert q(FAKE, N.F32, 0, C.byref(good), 8) == 5       # workspace too small
+    fmt = packed(N, N.ACTIVATION)
+    fmt.format = 4
+    assert q(FAKE, N.F32, 0, C.byref(fmt)) == 8           # unknown format
+    fmt = packed(N, N.ACTIVATION, refine=True)
+    fmt.format = N.FMT_FP6G
+    assert q(FAKE, N.F32, 1, C.byref(fmt)) == 8           # FP6G has no refinement
 
 
 def test_quantize_noalloc_checks_and_size_limit(N):
@@ -157,6 +176,18 @@ def test_linear_rejects_bad_arguments(N):
         assert call(wk, xk, 4) == 2
         wk, xk = packed(N, N.WEIGHT, rows=8, k=kmax), packed(N, N.ACTIVATION, rows=2, k=kmax)
         assert call(wk, xk, 4, ws=16) == 5                # passes the shape check, fails on workspace
+        # formats: both operands alike; level 8 for AutoFP8 only; FP6G at 6 only
+        assert call(w, x, 8) == 3
+        w8, x8 = packed(N, N.WEIGHT, rows=8, k=64), packed(N, N.ACTIVATION, rows=2, k=64)
+        w8.format = N.FMT_AUTOFP8
+        assert call(w8, x, 4) == 8                        # formats differ
+        x8.format = N.FMT_AUTOFP8
+        assert call(w8, x8, 8) == 6                       # level 8 needs refinement
+        assert call(w8, x8, 4, ws=16) == 5                # level 4 accepted
+        wg, xg = packed(N, N.WEIGHT, rows=8, k=64), packed(N, N.ACTIVATION, rows=2, k=64)
+        wg.format = xg.format = N.FMT_FP6G
+        assert call(wg, xg, 4) == 3 and call(wg, xg, 6, bd=FAKE) == 3
+        assert call(wg, xg, 6, ws=16) == 5
 
 
 def test_signals_reject_bad_arguments(N):
