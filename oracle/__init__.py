@@ -13,3 +13,4 @@ Each function cites the section, equation, table or figure it follows.
 from .autofp_ref import *  # noqa: F401,F403
 from .kv_ref import *  # noqa: F401,F403
 from . import formats_ref  # noqa: F401  (AutoFP8, exponent-scaled offsets, FP6g)
+from . import gptq_ref  # noqa: F401  (refinement-aware GPTQ calibration, App. E)

@@ -72,6 +72,21 @@ def hidden(batch, dim=HIDDEN, seed=0, tensor_id=0, dtype=torch.float32, device="
     return torch.randn(batch, dim, generator=g, device=device, dtype=torch.float32).to(dtype)
 
 
+def calibration(tokens, k, seed=0, tensor_id=0, corr=0.8, device="cpu"):
+    """Calibration activations [tokens x k] fp32 whose neighbouring channels
+    are correlated: x[:, 0] = z[:, 0], x[:, i] = corr * x[:, i-1] +
+    sqrt(1 - corr^2) * z[:, i] with z ~ N(0, 1) (unit variance per channel),
+    a stand-in for the activations a calibration set would give."""
+    g = _gen(seed, tensor_id, device)
+    z = torch.randn(tokens, k, generator=g, device=device, dtype=torch.float32)
+    x = torch.empty_like(z)
+    x[:, 0] = z[:, 0]
+    c = (1.0 - corr * corr) ** 0.5
+    for i in range(1, k):
+        x[:, i] = corr * x[:, i - 1] + c * z[:, i]
+    return x
+
+
 def kv_tokens(n, h_kv, head_dim=128, seed=0, tensor_id=0, dtype=torch.bfloat16, device="cpu"):
     """K or V vectors ~ N(0, 1) [n x h_kv x head_dim], rounded to ``dtype``."""
     g = _gen(seed, tensor_id, device)
