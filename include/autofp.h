@@ -168,7 +168,8 @@ typedef enum {
   AUTOFP_OP_GEMM = 3,         /* rows = tokens, k                               */
   AUTOFP_OP_SIGNALS = 4,      /* rows = batch, k = vocab (any vocab >= 1)       */
   AUTOFP_OP_KV_WRITE = 5,     /* rows = tokens * KV heads, k = head_dim         */
-  AUTOFP_OP_KV_ATTENTION = 6  /* rows = batch * query heads, k = max_pages      */
+  AUTOFP_OP_KV_ATTENTION = 6, /* rows = batch * query heads, k = max_pages      */
+  AUTOFP_OP_GPTQ = 7          /* rows, k of the weight                          */
 } autofp_op;
 
 /* Fills *p with the paper's hyperparameters. Errors: NULL. */
@@ -242,6 +243,41 @@ autofp_status autofp_quantize(const void *x, int32_t x_dtype, int32_t refine,
                               const uint8_t *exclude_mask, const autofp_params *p,
                               autofp_packed *out, void *workspace, size_t workspace_bytes,
                               void *stream);
+
+/*
+ * Refinement-aware GPTQ calibration of a weight w [rows x k] (fp32, device):
+ * [AE] App. E, Algorithm 1, with the group error of Eq. 7
+ *   E_j(m) = sum_{i in J} H_ii ||W[:, i] - What[:, i](m)||^2
+ * (J the 16 columns of group j, What(m) the group dequantized with the
+ * refined values T B (q + d/8) on the subgroups of mask m):
+ *  - T = amax(w) / 2688, fixed (line 4);
+ *  - the budget floor(rho k / 4) is spread over the groups by the greedy of
+ *    lines 5-12 on the original weights (at most two per group), which is
+ *    the selection of autofp_select_weight_mask with each column's gain
+ *    weighted by h_diag;
+ *  - for each group j in order (lines 13-24): B, q and d from the
+ *    error-compensated weights (rounded to fp32, encoded as autofp_quantize
+ *    does); the group's mask m*_j = the l_j subgroups with the largest Eq. 7
+ *    reductions over all rows (a tie goes to the lower subgroup); the group's
+ *    codes, scale and offsets; its error r = W_J - What_J(m*_j) propagated
+ *    to every later column: e U_JJ = r (forward substitution), then
+ *    W[:, later] -= e U[J, later], in fp64 with each product and sum rounded
+ *    in index order.
+ * u [k x k] fp64 row-major: the upper Cholesky factor of the inverse of the
+ * (dampened) Hessian, H^-1 = U^T U (entries below the diagonal are not read;
+ * its diagonal must be positive); h_diag [k] fp64: the Hessian's diagonal
+ * (H_ii >= 0). Writes out->codes, scales, tensor_scale, mask (M_W, popcount
+ * n_refined) and offsets; out: WEIGHT, AUTOFP6, rows and k of w, mask and
+ * offsets allocated, n_refined = autofp_weight_refined_count(k, p).
+ * k <= 65536, rows <= 1048560. Workspace: autofp_workspace_bytes(
+ * AUTOFP_OP_GPTQ, rows, k) (the fp64 working weights: 10 rows k bytes and
+ * more). 4 launches per 16-column group.
+ * Errors: NULL, SHAPE, KIND, ARG (format, n_refined, alignment), WORKSPACE,
+ * MISSING_REFINEMENT, HIP.
+ */
+autofp_status autofp_gptq_quantize(const float *w, int64_t rows, int64_t k, const double *u,
+                                   const double *h_diag, const autofp_params *p, autofp_packed *out,
+                                   void *workspace, size_t workspace_bytes, void *stream);
 
 /* Elementwise step between a linear layer's output and the next layer's input
  * (autofp_epilogue_quantize). */

@@ -21,7 +21,7 @@ from ._native import AutofpError, NativeLibraryError, Params  # noqa: F401
 __all__ = [
     "AutoFPTensor", "default_params", "packed_bytes", "weight_refined_count", "workspace_bytes",
     "select_weight_mask", "quantize", "quantize_weight", "quantize_activation",
-    "alloc_activation", "quantize_into", "quantize_noalloc", "epilogue_quantize",
+    "alloc_activation", "quantize_into", "quantize_noalloc", "epilogue_quantize", "gptq_quantize",
     "gemv", "gemv_rows", "gemm", "policy_signals", "policy_state", "policy_update", "AutofpError",
     "NativeLibraryError", "KVCache", "kv_write", "kv_attention",
 ]
@@ -254,6 +254,29 @@ def quantize_weight(w: torch.Tensor, refine=True, params=None, stream=None, form
         return quantize(w, N.WEIGHT, refine=True, weight_mask=mask, n_refined=nref, params=params,
                         stream=stream, format=format)
     return quantize(w, N.WEIGHT, params=params, stream=stream, format=format)
+
+
+def gptq_quantize(w: torch.Tensor, u: torch.Tensor, h_diag: torch.Tensor, params=None, workspace=None,
+                  stream=None) -> AutoFPTensor:
+    """Refinement-aware GPTQ (autofp_gptq_quantize): w [rows x k] fp32, u
+    [k x k] fp64 upper Cholesky factor of the inverse Hessian, h_diag [k]
+    fp64 Hessian diagonal; returns the packed AutoFP6 weight with its mask."""
+    _dev_check(w, u, h_diag)
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise ValueError("w must be a 2-D float32 tensor")
+    rows, k = w.shape
+    if u.dtype != torch.float64 or tuple(u.shape) != (k, k) or h_diag.dtype != torch.float64 or h_diag.numel() != k:
+        raise ValueError("u must be float64 [k, k] and h_diag float64 [k]")
+    p = params or default_params()
+    nref = weight_refined_count(k, p)
+    out = _alloc_packed(rows, k, N.WEIGHT, True, nref, w.device)
+    if workspace is None:
+        workspace = _workspace(N.OP_GPTQ, rows, k, w.device)
+    st = out.struct()
+    N.check(N.lib().autofp_gptq_quantize(_ptr(w), rows, k, _ptr(u), _ptr(h_diag), C.byref(p), C.byref(st),
+                                         _ptr(workspace), workspace.numel(), _stream(stream)),
+            "autofp_gptq_quantize")
+    return out
 
 
 def quantize_activation(x: torch.Tensor, refine=False, exclude_mask=None, params=None,

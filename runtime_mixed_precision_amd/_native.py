@@ -21,7 +21,7 @@ STATUS_NAMES = {
 F32, BF16 = 0, 1
 WEIGHT, ACTIVATION = 0, 1
 OP_QUANTIZE, OP_SELECT_MASK, OP_GEMV, OP_GEMM, OP_SIGNALS = 0, 1, 2, 3, 4
-OP_KV_WRITE, OP_KV_ATTENTION = 5, 6
+OP_KV_WRITE, OP_KV_ATTENTION, OP_GPTQ = 5, 6, 7
 KV_PAGE_TOKENS, KV_HEAD_DIM, KV_PAGE_BYTES = 64, 128, 4608
 EPI_COPY, EPI_RESIDUAL, EPI_SWIGLU = 1, 2, 3
 FMT_AUTOFP6, FMT_AUTOFP6E, FMT_AUTOFP8, FMT_FP6G = 0, 1, 2, 3
@@ -31,7 +31,7 @@ FORMATS = {"autofp6": FMT_AUTOFP6, "autofp6e": FMT_AUTOFP6E, "autofp8": FMT_AUTO
 EXPORTS = (
     "autofp_default_params", "autofp_status_string", "autofp_packed_bytes",
     "autofp_weight_refined_count", "autofp_workspace_bytes", "autofp_select_weight_mask",
-    "autofp_quantize", "autofp_quantize_noalloc", "autofp_epilogue_quantize", "autofp_gemv", "autofp_gemv_rows", "autofp_gemm", "autofp_policy_signals",
+    "autofp_quantize", "autofp_quantize_noalloc", "autofp_gptq_quantize", "autofp_epilogue_quantize", "autofp_gemv", "autofp_gemv_rows", "autofp_gemm", "autofp_policy_signals",
     "autofp_policy_update", "autofp_policy_layer", "autofp_kv_write", "autofp_kv_attention",
 )
 
@@ -105,6 +105,7 @@ def lib():
         "autofp_quantize": (C.c_int, [vp, C.c_int32, C.c_int32, vp, P(Params), P(Packed), vp,
                                       C.c_size_t, vp]),
         "autofp_quantize_noalloc": (C.c_int, [vp, C.c_int32, C.c_int32, vp, P(Params), P(Packed), vp]),
+        "autofp_gptq_quantize": (C.c_int, [vp, C.c_int64, C.c_int64, vp, vp, P(Params), P(Packed), vp, C.c_size_t, vp]),
         "autofp_epilogue_quantize": (C.c_int, [C.c_int32, vp, C.c_int64, vp, vp, C.c_int32, vp, P(Params),
                                                P(Packed), vp, C.c_size_t, vp]),
         "autofp_gemv": (C.c_int, [P(Packed), P(Packed), C.c_int32, vp, vp, C.c_int32, P(Params), vp,

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libautofp.so")
-SOURCES = ["api.hip", "encode.hip", "gemv.hip", "gemv_batch.hip", "gemm.hip", "kv.hip", "signals.hip"]
+SOURCES = ["api.hip", "encode.hip", "gemv.hip", "gemv_batch.hip", "gemm.hip", "gptq.hip", "kv.hip", "signals.hip"]
 ARCH = os.environ.get("AUTOFP_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 vector instructions are disabled for all device code.

@@ -68,7 +68,8 @@ hipError_t launch_amax_partial_op(const EncodeArgs &a, float *partial, int n_par
 // Weight-mask selection ([AE] App. E, Alg. 1 allocation with H = I).
 hipError_t launch_select_mask(const float *w, int64_t rows, int64_t k, int32_t budget,
                               const float *partial, int n_partial, double *row_gain,
-                              double *col_gain, uint8_t *mask_out, int fmt, hipStream_t s);
+                              double *col_gain, uint8_t *mask_out, int fmt, const double *hdiag,
+                              hipStream_t s);
 
 // ---- gemv.hip ----
 struct LinearArgs {
@@ -126,6 +127,15 @@ hipError_t launch_gemm_small_m(const LinearArgs &a, hipStream_t s);   // reads a
 // fp16 panel a.xh that launch_act_dequant wrote for a.fmt and (offset
 // formats) a.prefix.
 hipError_t launch_gemm_fmt(const LinearArgs &a, hipStream_t s);
+
+// ---- gptq.hip ----
+// Refinement-aware GPTQ ([AE] App. E, Algorithm 1) of w [rows][k] fp32 with the
+// inverse-Hessian factor u [k][k] and the Hessian diagonal hdiag [k]; writes
+// out's codes, scales, tensor scale, mask and offsets. Arguments checked by
+// the caller; ws of gptq_workspace_bytes(rows, k).
+size_t gptq_workspace_bytes(int64_t rows, int64_t k);
+hipError_t launch_gptq(const float *w, int64_t rows, int64_t k, const double *u, const double *hdiag,
+                       int32_t budget, const autofp_packed *out, void *ws, hipStream_t s);
 
 // ---- signals.hip ----
 int64_t entropy_slices(int64_t vocab);                        // vocabulary slices per row

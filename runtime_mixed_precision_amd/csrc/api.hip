@@ -22,6 +22,8 @@ namespace {
 constexpr size_t kAlign = 256;
 // bytes past the last row of a weight's offsets that the GEMV may read (never writes)
 constexpr size_t kOffsetPad = 16;
+// rows of autofp_gptq_quantize (16-row propagation blocks on grid.y)
+constexpr int64_t kMaxGptqRows = 65535 * 16;
 // largest reduction dimension of autofp_gemv / autofp_gemm
 constexpr int64_t kMaxLinearK = (int64_t)1 << 22;
 
@@ -378,6 +380,10 @@ autofp_status autofp_workspace_bytes(int32_t op, int64_t rows, int64_t k, size_t
       return AUTOFP_OK;
     case AUTOFP_OP_GEMV:
     case AUTOFP_OP_GEMM: *bytes = ws_linear(rows, k); return AUTOFP_OK;
+    case AUTOFP_OP_GPTQ:
+      if (k > 65536 || rows > kMaxGptqRows) return AUTOFP_ERR_SHAPE;
+      *bytes = gptq_workspace_bytes(rows, k);
+      return AUTOFP_OK;
     default: return AUTOFP_ERR_ARG;
   }
 }
@@ -403,8 +409,28 @@ autofp_status autofp_select_weight_mask(const float *w, int64_t rows, int64_t k,
   hipError_t e = launch_amax_partial(w, AUTOFP_F32, rows * k, partial, np, s);
   if (e != hipSuccess) return AUTOFP_ERR_HIP;
   e = launch_select_mask(w, rows, k, refined_budget(k, p->rho), partial, np, row_gain, col_gain,
-                         mask_out, format, s);
+                         mask_out, format, nullptr, s);
   return from_hip(e);
+}
+
+autofp_status autofp_gptq_quantize(const float *w, int64_t rows, int64_t k, const double *u,
+                                   const double *h_diag, const autofp_params *p, autofp_packed *out,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+  if (!w || !u || !h_diag || !out) return AUTOFP_ERR_NULL;
+  if (rows < 1 || !valid_k(k) || k > 65536 || rows > kMaxGptqRows) return AUTOFP_ERR_SHAPE;
+  if (out->kind != AUTOFP_WEIGHT) return AUTOFP_ERR_KIND;
+  if (out->rows != rows || out->k != k) return AUTOFP_ERR_SHAPE;
+  if (!out->codes || !out->scales || !out->tensor_scale) return AUTOFP_ERR_NULL;
+  if (!out->mask || !out->offsets) return AUTOFP_ERR_MISSING_REFINEMENT;
+  const autofp_params pp = params_or_default(p);
+  if (!(pp.rho >= 0.0 && pp.rho <= 1.0)) return AUTOFP_ERR_ARG;
+  if (out->format != AUTOFP_FMT_AUTOFP6 || out->n_refined != refined_budget(k, pp.rho)) return AUTOFP_ERR_ARG;
+  if (!aligned16(w) || !aligned16(u) || !aligned16(h_diag) || !aligned16(out->codes) || !aligned16(out->scales) ||
+      !aligned16(out->tensor_scale) || !aligned16(out->mask) || !aligned16(out->offsets))
+    return AUTOFP_ERR_ARG;
+  if (!workspace || workspace_bytes < gptq_workspace_bytes(rows, k)) return AUTOFP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return AUTOFP_ERR_ARG;
+  return from_hip(launch_gptq(w, rows, k, u, h_diag, out->n_refined, out, workspace, (hipStream_t)stream));
 }
 
 autofp_status autofp_quantize(const void *x, int32_t x_dtype, int32_t refine,

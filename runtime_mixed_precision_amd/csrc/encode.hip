@@ -495,7 +495,8 @@ namespace {
 __global__ __launch_bounds__(kThreads) void weight_gain_kernel(const float *__restrict__ w,
                                                                int64_t rows, int64_t k,
                                                                const float *partial, int n_partial,
-                                                               double *__restrict__ row_gain, int fmt) {
+                                                               double *__restrict__ row_gain, int fmt,
+                                                               const double *__restrict__ hdiag) {
 #pragma clang fp contract(off)
   const float amax = fold_partials(partial, n_partial);
   const float T = amax / 2688.0f;
@@ -533,7 +534,9 @@ __global__ __launch_bounds__(kThreads) void weight_gain_kernel(const float *__re
       const double x = (double)xv[el];
       const double eb = x - tb * q;
       const double er = x - tb * (q + delta);
-      const double ge = eb * eb - er * er;
+      const double ge0 = eb * eb - er * er;
+      // Hessian-diagonal weight of the column ([AE] Eq. 7), when given
+      const double ge = hdiag ? hdiag[k0 + el] * ge0 : ge0;
       g = (i == 0) ? ge : g + ge;
     }
     dst[sg] = g;
@@ -686,7 +689,8 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t s) {
 
 hipError_t launch_select_mask(const float *w, int64_t rows, int64_t k, int32_t budget,
                               const float *partial, int n_partial, double *row_gain,
-                              double *col_gain, uint8_t *mask_out, int fmt, hipStream_t s) {
+                              double *col_gain, uint8_t *mask_out, int fmt, const double *hdiag,
+                              hipStream_t s) {
   const int64_t P2 = (k + 31) / 32;
   const int64_t ncol = k / 4;
   const int64_t ngroups = k / 16;
@@ -694,7 +698,7 @@ hipError_t launch_select_mask(const float *w, int64_t rows, int64_t k, int32_t b
   int32_t *csg = (int32_t *)(cgain + 2 * ngroups);
   int32_t *sel = csg + 2 * ngroups;
   hipLaunchKernelGGL(weight_gain_kernel, dim3(grid_for(rows * P2, kThreads)), dim3(kThreads), 0, s,
-                     w, rows, k, partial, n_partial, row_gain, fmt);
+                     w, rows, k, partial, n_partial, row_gain, fmt, hdiag);
   hipLaunchKernelGGL(gain_colsum_kernel, dim3(grid_for(ncol, kThreads)), dim3(kThreads), 0, s,
                      row_gain, rows, ncol, col_gain);
   hipLaunchKernelGGL(gain_candidates_kernel, dim3(grid_for(ngroups, kThreads)), dim3(kThreads), 0, s,

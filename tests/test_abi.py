@@ -190,6 +190,29 @@ def test_linear_rejects_bad_arguments(N):
         assert call(wg, xg, 6, ws=16) == 5
 
 
+def test_gptq_rejects_bad_arguments(N):
+    L = N.lib()
+    p = params(N)
+    g = lambda w, rows, k, out, ws=1 << 30: L.autofp_gptq_quantize(w, rows, k, FAKE, FAKE, C.byref(p), out, FAKE,
+                                                                   ws, None)
+    good = packed(N, N.WEIGHT, rows=4, k=64, refine=True, n_refined=3)
+    assert g(None, 4, 64, C.byref(good)) == 1
+    assert g(FAKE, 4, 40, C.byref(good)) == 2                 # k % 16
+    assert g(FAKE, 5, 64, C.byref(good)) == 2                 # rows differ from the output's
+    assert g(FAKE, 4, 64, C.byref(packed(N, N.ACTIVATION, rows=4, k=64))) == 4
+    assert g(FAKE, 4, 64, C.byref(packed(N, N.WEIGHT, rows=4, k=64))) == 6   # no mask / offsets
+    bad = packed(N, N.WEIGHT, rows=4, k=64, refine=True, n_refined=2)
+    assert g(FAKE, 4, 64, C.byref(bad)) == 8                  # n_refined is not the budget
+    bad = packed(N, N.WEIGHT, rows=4, k=64, refine=True, n_refined=3)
+    bad.format = N.FMT_AUTOFP8
+    assert g(FAKE, 4, 64, C.byref(bad)) == 8
+    assert g(FAKE, 4, 64, C.byref(good), ws=16) == 5
+    assert g(FAKE + 8, 4, 64, C.byref(good)) == 8             # misaligned weight
+    b = C.c_size_t()
+    assert L.autofp_workspace_bytes(N.OP_GPTQ, 4096, 4096, C.byref(b)) == 0 and b.value > 10 * 4096 * 4096
+    assert L.autofp_workspace_bytes(N.OP_GPTQ, 8, 65552, C.byref(b)) == 2
+
+
 def test_signals_reject_bad_arguments(N):
     L = N.lib()
     p = params(N)
