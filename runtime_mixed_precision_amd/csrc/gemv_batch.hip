@@ -10,26 +10,25 @@
 // Result: y[t][n] = sum_k What_l(t)[n][k] * Xhat_l(t)[t][k], where l(t) is the
 // level of token t (one level for the whole call, or one per token). Decoded
 // operands without their tensor scales are exact in fp16 (at most 10
-// significant bits), so v_mfma_f32_32x32x16_f16 forms exact products and
+// significant bits), so v_mfma_f32_16x16x32_f16 forms exact products and
 // only the fp32 accumulation rounds; T_W * T_X (times c for a level-2 token)
 // is applied once per output.
 //
-// Work split. A block owns 64 weight rows and 32 or 64 tokens; its 4
-// wavefronts split the block's K range into four contiguous parts, and the
-// blocks of one row tile split K into S parts (S > 1 only when the row tiles
-// alone leave compute units idle). Per 64-element K step a lane (l % 32,
-// half h = l / 32) loads, straight into registers:
-//   - the weight codes of rows 32a + l % 32 (a = 0, 1), elements 32h .. 32h+31
-//     of the step (one 16-byte load each) and their two E4M3 scales;
-//   - the activation codes of tokens 32tt + l % 32, the same elements, their
-//     two scales and (level 6) their eight offset bytes;
-//   - at level 6, the 12-byte window of the row's compacted weight offsets
-//     that holds the refined subgroups of those 32 elements.
-// No operand goes through LDS, and no byte is loaded twice by one block.
-// MFMA kk (0..3) of a step takes, in K slot h, the lane's elements
-// 32h + 8kk .. +7 of both operands: the same K permutation on both sides, so
-// every element of the step is summed exactly once. Loads run two steps ahead
-// of the arithmetic.
+// Work split. A block of 4 wavefronts owns 16 NF weight rows (NF = 4, or 2
+// above 32 tokens with level-6 operands) and 16 TT tokens (TT = 1, 2 or 4
+// tiles of 16); the wavefronts split the block's K range into four contiguous
+// parts, and the blocks of one row tile split K into S parts (S > 1 only
+// when the row tiles alone leave compute units idle). Per 128-element K step
+// a lane (r16 = l % 16,
+// q = l / 16) loads, straight into registers, elements 32q .. 32q + 31 of
+// weight rows 16f + r16 and of tokens 16tt + r16 (one 16-byte load each) and,
+// at level 6, the 12-byte window of the row's compacted weight offsets and the
+// token's eight activation offset bytes. The E4M3 scales of the wavefront's
+// rows and tokens over its whole K range go to LDS once, with 8-byte loads, so
+// the loop issues only the code (and offset) loads. MFMA kk (0..3) of a step
+// takes, in K slot q, the lane's elements 32q + 8kk .. +7 of both operands:
+// the same K permutation on both sides. Loads run two steps ahead of the
+// arithmetic (one with level-6 operands).
 //
 // The 4 wavefronts' accumulators are added through LDS in wavefront order;
 // with S > 1 the block writes its fp32 partial tile to the workspace and a
