@@ -64,6 +64,48 @@ def build(verbose=False):
     return LIB
 
 
+# Host-side sanitizers for the C ABI's argument checks (api.hip's host code);
+# each flag goes to the host compile only, device code is built as in build().
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZED_LIB = os.path.join(BUILD, "libautofp_hostsan.so")
+
+
+def asan_runtime():
+    """Path of clang's shared AddressSanitizer runtime (to preload into a
+    process that loads the sanitized library), or None."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    for base in (os.path.join(root, "lib", "llvm"), os.path.join(root, "llvm"), "/opt/rocm/lib/llvm"):
+        hits = sorted(glob.glob(os.path.join(base, "lib", "clang", "*", "lib", "linux", "libclang_rt.asan-x86_64.so")))
+        if hits:
+            return hits[-1]
+    return None
+
+
+def build_host_sanitized():
+    """libautofp with api.hip's host code under AddressSanitizer and
+    UndefinedBehaviorSanitizer, linked with the other objects of build()
+    (run build() first): _build/libautofp_hostsan.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    obj = os.path.join(BUILD, "api_hostsan.o")
+    cmd = [hipcc(), *[c for c in COMMON if c != "-O3"], "-O1", "-g", *DEVICE_FLAGS, *HOST_SANITIZE, "-c",
+           os.path.join(CSRC, "api.hip"), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on api.hip (host sanitizers):\n{res.stdout}\n{res.stderr}")
+    objs = [os.path.join(BUILD, os.path.splitext(src)[0] + ".o") for src in SOURCES if src != "api.hip"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"run build() first: missing {missing}")
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-shared-libasan", obj, *objs, "-o", SANITIZED_LIB]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed (host sanitizers):\n{res.stdout}\n{res.stderr}")
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)
