@@ -20,8 +20,10 @@
  *  - Shapes. A tensor is [rows x k] row-major with k the reduction dimension;
  *    k must be a positive multiple of 16 (one NVFP4 group, [AE] App. B.1).
  *  - Non-finite inputs (inf / NaN) give unspecified results.
- *  - Thread safety: no global mutable state; concurrent calls on different
- *    buffers are safe.
+ *  - Thread safety: concurrent calls on different buffers are safe. The only
+ *    process-wide state is a cache of device properties (each entry set once,
+ *    atomically) and the static scratch of autofp_quantize_noalloc (calls of
+ *    it that overlap on one GPU race; see there).
  */
 #ifndef AUTOFP_H
 #define AUTOFP_H

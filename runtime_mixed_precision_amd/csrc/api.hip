@@ -180,6 +180,22 @@ autofp_status launch_variant(const LinearArgs &a, hipStream_t s) {
   return from_hip(launch_gemm_fmt(a, s));
 }
 
+// autofp_gemv's launches for arguments that linear_common accepted.
+autofp_status gemv_launches(LinearArgs &a, const autofp_packed *w, const autofp_packed *x, int32_t bits,
+                            const int32_t *bits_dev, hipStream_t s) {
+  if (variant_route(a)) return launch_variant(a, s);
+  if ((bits_dev || bits == 6) && x->rows <= 16 && x->k > 65536) return AUTOFP_ERR_SHAPE;
+  if (gemv_needs_panel(a)) {
+    const hipError_t e = launch_act_dequant(a, s);
+    if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  }
+  if ((gemv_small_m_route(a) || (a.b > 16 && gemv_batch_ok(a))) && w->mask && (bits_dev || bits == 6)) {
+    const hipError_t e = launch_mask_prefix(w->mask, mask_bytes(w->k), a.prefix, s);
+    if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  }
+  return from_hip(launch_gemv(a, s));
+}
+
 
 autofp_status check_quantize(const void *x, int32_t x_dtype, int32_t refine, const uint8_t *exclude_mask,
                              const autofp_packed *out) {
@@ -205,20 +221,14 @@ autofp_status check_quantize(const void *x, int32_t x_dtype, int32_t refine, con
   return AUTOFP_OK;
 }
 
-// The encode's launches on scratch `ws` (ws_quantize bytes: amax partials,
+// The encode's arguments on scratch `ws` (ws_quantize bytes: amax partials,
 // then the weight-mask prefix table); arguments already checked. `epi`
 // (op != 0) encodes the producer epilogue's v instead of x.
-autofp_status launch_quantize(const void *x, int32_t x_dtype, int32_t refine, const uint8_t *exclude_mask,
-                              const autofp_params *p, const autofp_packed *out, void *ws, hipStream_t s,
-                              const EncodeArgs *epi = nullptr) {
+EncodeArgs encode_args(const void *x, int32_t x_dtype, int32_t refine, const uint8_t *exclude_mask,
+                       const autofp_params *p, const autofp_packed *out, void *ws, const EncodeArgs *epi) {
   const autofp_params pp = params_or_default(p);
   const bool act_refine = out->kind == AUTOFP_ACTIVATION && refine;
   const bool w_refine = out->kind == AUTOFP_WEIGHT && out->mask != nullptr;
-  float *partial = (float *)ws;
-  int32_t *prefix = (int32_t *)((char *)ws + align_up(sizeof(float) * kAmaxBlocks));
-  const int64_t n = out->rows * out->k;
-  const bool small = encode_is_small(out->rows, out->k);
-  const int np = amax_partial_count(n);
   EncodeArgs a{};
   if (epi) {
     a.op = epi->op;
@@ -229,19 +239,10 @@ autofp_status launch_quantize(const void *x, int32_t x_dtype, int32_t refine, co
   }
   a.rows = out->rows;
   a.k = out->k;
-  hipError_t e = hipSuccess;
-  if (!small) {
-    e = a.op ? launch_amax_partial_op(a, partial, np, s) : launch_amax_partial(x, x_dtype, n, partial, np, s);
-    if (e != hipSuccess) return AUTOFP_ERR_HIP;
-  }
-  if (w_refine) {
-    e = launch_mask_prefix(out->mask, mask_bytes(out->k), prefix, s);
-    if (e != hipSuccess) return AUTOFP_ERR_HIP;
-  }
   a.x = x;
   a.dtype = x_dtype;
-  a.partial = partial;
-  a.n_partial = np;
+  a.partial = (float *)ws;
+  a.n_partial = amax_partial_count(out->rows * out->k);
   a.codes = out->codes;
   a.scales = out->scales;
   a.tensor_scale = out->tensor_scale;
@@ -251,10 +252,30 @@ autofp_status launch_quantize(const void *x, int32_t x_dtype, int32_t refine, co
   a.act_mask = act_refine ? out->mask : nullptr;
   a.act_offsets = act_refine ? out->offsets : nullptr;
   a.w_mask = w_refine ? out->mask : nullptr;
-  a.w_prefix = prefix;
+  a.w_prefix = (int32_t *)((char *)ws + align_up(sizeof(float) * kAmaxBlocks));
   a.n_refined = out->n_refined;
   a.w_offsets = out->offsets;
   a.fmt = out->format;
+  return a;
+}
+
+// The encode's launches (see encode_args).
+autofp_status launch_quantize(const void *x, int32_t x_dtype, int32_t refine, const uint8_t *exclude_mask,
+                              const autofp_params *p, const autofp_packed *out, void *ws, hipStream_t s,
+                              const EncodeArgs *epi = nullptr) {
+  const EncodeArgs a = encode_args(x, x_dtype, refine, exclude_mask, p, out, ws, epi);
+  float *partial = (float *)ws;
+  int32_t *prefix = (int32_t *)((char *)ws + align_up(sizeof(float) * kAmaxBlocks));
+  hipError_t e = hipSuccess;
+  if (!encode_is_small(out->rows, out->k)) {
+    e = a.op ? launch_amax_partial_op(a, partial, a.n_partial, s)
+             : launch_amax_partial(x, x_dtype, out->rows * out->k, partial, a.n_partial, s);
+    if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  }
+  if (a.w_mask) {
+    e = launch_mask_prefix(out->mask, mask_bytes(out->k), prefix, s);
+    if (e != hipSuccess) return AUTOFP_ERR_HIP;
+  }
   return from_hip(launch_encode(a, s));
 }
 
@@ -488,18 +509,7 @@ autofp_status autofp_gemv(const autofp_packed *w, const autofp_packed *x, int32_
   const autofp_status st =
       linear_common(w, x, bits, bits_dev, y, y_dtype, p, workspace, workspace_bytes, a);
   if (st != AUTOFP_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  if (variant_route(a)) return launch_variant(a, s);
-  if ((bits_dev || bits == 6) && x->rows <= 16 && x->k > 65536) return AUTOFP_ERR_SHAPE;
-  if (gemv_needs_panel(a)) {
-    const hipError_t e = launch_act_dequant(a, s);
-    if (e != hipSuccess) return AUTOFP_ERR_HIP;
-  }
-  if ((gemv_small_m_route(a) || (a.b > 16 && gemv_batch_ok(a))) && w->mask && (bits_dev || bits == 6)) {
-    const hipError_t e = launch_mask_prefix(w->mask, mask_bytes(w->k), a.prefix, s);
-    if (e != hipSuccess) return AUTOFP_ERR_HIP;
-  }
-  return from_hip(launch_gemv(a, s));
+  return gemv_launches(a, w, x, bits, bits_dev, (hipStream_t)stream);
 }
 
 autofp_status autofp_gemv_rows(const autofp_packed *w, const autofp_packed *x, const int32_t *bits_rows,
