@@ -118,6 +118,32 @@ def pmc_pass(A, S, device):
     log("pmc pass done: 36 GEMV launches, one 64 MiB copy")
 
 
+def pmc_batch_pass(A, S, device):
+    """Workload of the batched-decode counter runs: the 12 GEMV launches at
+    64 tokens (4 shapes x levels 2/4/6) and the 28672 x 8192 projection at 64
+    tokens, level 4, three times each, eagerly, then the 64 MiB copy that
+    calibrates the traffic counters."""
+    import torch
+    pool = build_pool(A, S, 3, device)
+    bench = DecodeBench(A, S, pool, 64, device)
+    n, k = 28672, 8192
+    w70 = A.quantize_weight(S.weights(n, k, seed=700, tensor_id=0, device=device))
+    x70 = A.quantize_activation(S.activations(64, k, seed=700, tensor_id=1, outlier_frac=0.0, device=device))
+    y70 = torch.empty(64, n, dtype=torch.float32, device=device)
+    ws70 = torch.empty(A.workspace_bytes(2, 64, k), dtype=torch.uint8, device=device)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        bench.gemv_only(0)
+        A.gemv(w70, x70, bits=4, out=y70, workspace=ws70)
+    torch.cuda.synchronize()
+    src = torch.ones(64 << 18, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log("pmc batch pass done: 3 x (12 GEMV launches at 64 tokens + the 70B projection), one 64 MiB copy")
+
+
 def build_pool(A, S, n_layers, device):
     pool = []
     for i in range(n_layers):
@@ -709,6 +735,8 @@ def main():
     ap.add_argument("--kv-only", action="store_true", help="run only the KV-cache attention (no JSON line)")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run only the workload of the HBM-counter runs (no JSON line)")
+    ap.add_argument("--pmc-batch", action="store_true",
+                    help="run only the workload of the 64-token counter runs (no JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path, so --gpus must be 1",
@@ -728,11 +756,14 @@ def main():
     # touches the GPU
     cpu = None
     profiled = any(k.startswith("ROCPROF") for k in os.environ)
-    if not args.no_cpu_baseline and not args.pmc_pass and not args.kv_only and not profiled:
+    if not args.no_cpu_baseline and not args.pmc_pass and not args.pmc_batch and not args.kv_only and not profiled:
         cpu = cpu_baseline(args.batch)
     log(f"device: {torch.cuda.get_device_name(0)}")
     if args.pmc_pass:
         pmc_pass(A, S, device)
+        return
+    if args.pmc_batch:
+        pmc_batch_pass(A, S, device)
         return
     if args.kv_only:
         log(json.dumps(kv_bench(A, S, device, reps=max(args.steps, 5))))
