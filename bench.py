@@ -144,6 +144,36 @@ def pmc_batch_pass(A, S, device):
     log("pmc batch pass done: 3 x (12 GEMV launches at 64 tokens + the 70B projection), one 64 MiB copy")
 
 
+def pmc_prefill_pass(A, S, device):
+    """Workload of the prefill counter runs: the GEMMs of 2048 tokens against
+    Wup (14336 x 4096) and Wdown (4096 x 14336) at levels 4 and 6, three
+    times each, eagerly, then the 64 MiB copy that calibrates the traffic
+    counters."""
+    import torch
+    M = 2048
+    for name, n, k, tid in (("wup", 14336, 4096, 1), ("wdown", 4096, 14336, 3)):
+        w = S.weights(n, k, seed=200, tensor_id=tid, device=device)
+        wp = A.quantize_weight(w, refine=True)
+        del w
+        x = S.activations(M, k, seed=200, tensor_id=10 + tid, outlier_frac=0.005, outlier_scale=30.0,
+                          device=device)
+        ws = torch.empty(A.workspace_bytes(3, M, k), dtype=torch.uint8, device=device)
+        y = torch.empty(M, n, dtype=torch.bfloat16, device=device)
+        for level in (4, 6):
+            xp = A.quantize_activation(x, refine=(level == 6), exclude_mask=wp.mask if level == 6 else None)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                A.gemm(wp, xp, bits=level, out=y, workspace=ws)
+            torch.cuda.synchronize()
+        del wp, x, ws, y
+    src = torch.ones(64 << 18, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log("pmc prefill pass done: 3 x (Wup, Wdown) x levels 4, 6 at 2048 tokens, one 64 MiB copy")
+
+
 def build_pool(A, S, n_layers, device):
     pool = []
     for i in range(n_layers):
@@ -737,6 +767,8 @@ def main():
                     help="run only the workload of the HBM-counter runs (no JSON line)")
     ap.add_argument("--pmc-batch", action="store_true",
                     help="run only the workload of the 64-token counter runs (no JSON line)")
+    ap.add_argument("--pmc-prefill", action="store_true",
+                    help="run only the prefill GEMM counter workload (no JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path, so --gpus must be 1",
@@ -756,7 +788,7 @@ def main():
     # touches the GPU
     cpu = None
     profiled = any(k.startswith("ROCPROF") for k in os.environ)
-    if not args.no_cpu_baseline and not args.pmc_pass and not args.pmc_batch and not args.kv_only and not profiled:
+    if not args.no_cpu_baseline and not args.pmc_pass and not args.pmc_batch and not args.pmc_prefill and not args.kv_only and not profiled:
         cpu = cpu_baseline(args.batch)
     log(f"device: {torch.cuda.get_device_name(0)}")
     if args.pmc_pass:
@@ -764,6 +796,9 @@ def main():
         return
     if args.pmc_batch:
         pmc_batch_pass(A, S, device)
+        return
+    if args.pmc_prefill:
+        pmc_prefill_pass(A, S, device)
         return
     if args.kv_only:
         log(json.dumps(kv_bench(A, S, device, reps=max(args.steps, 5))))

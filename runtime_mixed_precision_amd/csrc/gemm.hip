@@ -16,10 +16,14 @@
 //    or 256 x 128 for prefill, 64 x 64..256 for 17-64 decode tokens) in K steps
 //    of 64 with two LDS stages; the fp16 activation panel goes memory -> LDS
 //    with buffer_load ... lds, the packed weight tile is decoded in registers
-//    and written to LDS (description above the kernel).
+//    and written to LDS (description above the kernel). The prefill tiles
+//    (K <= 32768) let the two halves of the block load the weight steps in
+//    turn, two steps ahead.
 //  - gemm_kernel (any K % 16 == 0): 4 wavefronts on a 128 x 128 tile, both
 //    operands through registers; the fallback for K % 64 != 0.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "afp_device.h"
 #include "afp_launch.h"
@@ -224,6 +228,7 @@ constexpr int kGemmWaves = 16;  // wavefronts per prefill block (four per SIMD, 
 constexpr int kDecodeWaves = 8; // wavefronts per 64-token block
 constexpr int kBK2 = 64;
 constexpr size_t kTabBytes = 2 * 256 * 8;   // level-6 decode tables of gemm_lds_kernel
+constexpr int64_t kAltMaxK = 32768;         // K bound of the alternating-group prefill tiles (mask in LDS)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
@@ -234,6 +239,124 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t
 // XORed with (r / 2) % 8, so the 16 rows at one chunk that a b128 LDS access
 // serves per cycle fall on 16 distinct 16-byte bank groups (64 banks)
 __device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * 128u + ((c ^ ((r >> 1) & 7u)) << 4); }
+
+// One weight item, 32 elements of one row, to fp16: c (16 bytes of E2M1
+// codes; FP6G: c and cx, 24 bytes of E2M3 codes), s2 (the two E4M3 scale
+// bytes of its 16-element groups, low byte first) and, when refine, the offset
+// window of its refined subgroups (AUTOFP6 / AUTOFP6E: o, 12 bytes; AUTOFP8:
+// o4 and o5, 20 bytes) whose first offset starts sh bytes in, with m the
+// item's mask byte. h[p] = elements 8p .. 8p + 7, times their group scale.
+// Tables: dtab / stab (AUTOFP6, AUTOFP6E) or t8 (AUTOFP8), as filled by the
+// kernels below.
+template <int FMT>
+__device__ __forceinline__ void decode_w32(const u32x4v c, const u32x2v cx, uint32_t s2, const u32x3v o,
+                                           const u32x4v o4, uint32_t o5, uint32_t m, uint32_t sh, int L,
+                                           bool refine, const uint2 *dtab, const uint2 *stab, const uint32_t *t8,
+                                           half8v h[4]) {
+  constexpr bool F8 = FMT == AUTOFP_FMT_AUTOFP8;
+  constexpr bool G6 = FMT == AUTOFP_FMT_FP6G;
+  if constexpr (G6) {
+    // 32 six-bit codes in 24 bytes: 8 codes (48 bits) per fragment, at
+    // bits 0, 48, 96 and 144 of the six dwords
+    const uint64_t win4[4] = {((uint64_t)c[1] << 32) | c[0], (((uint64_t)c[2] << 32) | c[1]) >> 16,
+                              ((uint64_t)cx[0] << 32) | c[3], (((uint64_t)cx[1] << 32) | cx[0]) >> 16};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint64_t win = win4[j];
+      half2v p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        p[e] = e2m3x2_to_half2((uint32_t)(win >> (12 * e)) & 63u, (uint32_t)(win >> (12 * e + 6)) & 63u);
+      h[j] = half8v{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+    }
+  } else {
+    uint32_t w4[4] = {c[0], c[1], c[2], c[3]};
+    if (L == 2) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w4[j] = autofp2_codes(w4[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) h[j] = fp4x8_to_half8(w4[j]);
+  }
+  if (F8 && refine) {
+    // the (at most 8) two-byte offset words of these 32 elements, in
+    // subgroup order, from the 20 loaded bytes shifted by the misalignment
+    const uint32_t W0 = __builtin_amdgcn_alignbyte(o4[1], o4[0], sh);
+    const uint32_t W1 = __builtin_amdgcn_alignbyte(o4[2], o4[1], sh);
+    const uint32_t W2 = __builtin_amdgcn_alignbyte(o4[3], o4[2], sh);
+    const uint32_t W3 = __builtin_amdgcn_alignbyte(o5, o4[3], sh);
+    const uint64_t lo = (uint64_t)W0 | ((uint64_t)W1 << 32), hi = (uint64_t)W2 | ((uint64_t)W3 << 32);
+    uint32_t wd[8];
+    uint32_t j = 0;
+#pragma unroll
+    for (int sg = 0; sg < 8; ++sg) {
+      const uint32_t on = (m >> sg) & 1u;
+      const uint64_t src = j < 4 ? lo : hi;
+      wd[sg] = on ? (uint32_t)(src >> (16 * (j & 3))) & 0xFFFFu : 0u;
+      j += on;
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t a0 = wd[2 * p], a1 = wd[2 * p + 1];
+      h[p] += __builtin_bit_cast(half8v, make_uint4(t8[a0 & 0xFFu], t8[a0 >> 8], t8[a1 & 0xFFu], t8[a1 >> 8]));
+    }
+  } else if (!G6 && refine) {
+    // the (at most 8) offset bytes of these 32 elements, in subgroup order;
+    // one byte per subgroup (0 where not refined) via a byte permute
+    const uint32_t lo = __builtin_amdgcn_alignbyte(o[1], o[0], sh);
+    const uint32_t hi = __builtin_amdgcn_alignbyte(o[2], o[1], sh);
+    const uint2 sel = stab[m & 0xFFu];
+    const uint32_t E[2] = {__builtin_amdgcn_perm(hi, lo, sel.x), __builtin_amdgcn_perm(hi, lo, sel.y)};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint2 de = dtab[(E[p >> 1] >> (16 * (p & 1))) & 0xFFu];
+      const uint2 dd = dtab[(E[p >> 1] >> (16 * (p & 1) + 8)) & 0xFFu];
+      const half8v dl = __builtin_bit_cast(half8v, make_uint4(de.x, de.y, dd.x, dd.y));
+      if constexpr (FMT == AUTOFP_FMT_AUTOFP6E) {
+        // delta = d/8 * 2^e of each element's E2M1 value
+        const uint4 hv = __builtin_bit_cast(uint4, h[p]);
+        const uint4 fv = make_uint4(__builtin_bit_cast(uint32_t, pow2e_h2(__builtin_bit_cast(half2v, hv.x))),
+                                    __builtin_bit_cast(uint32_t, pow2e_h2(__builtin_bit_cast(half2v, hv.y))),
+                                    __builtin_bit_cast(uint32_t, pow2e_h2(__builtin_bit_cast(half2v, hv.z))),
+                                    __builtin_bit_cast(uint32_t, pow2e_h2(__builtin_bit_cast(half2v, hv.w))));
+        h[p] += dl * __builtin_bit_cast(half8v, fv);
+      } else {
+        h[p] += dl;
+      }
+    }
+  }
+  const _Float16 b0 = (_Float16)e4m3_value(s2 & 0xFFu);
+  const _Float16 b1 = (_Float16)e4m3_value((s2 >> 8) & 0xFFu);
+  h[0] *= b0;
+  h[1] *= b0;
+  h[2] *= b1;
+  h[3] *= b1;
+}
+
+// Level-6 decode tables in LDS (block-wide fill; the caller synchronizes):
+// AUTOFP8: t8[byte] = the two fp16 offsets d/8 of a byte of two 4-bit
+// offsets; otherwise dtab[byte] = the four fp16 offsets d/8 of an offset byte
+// and stab[mask byte] = the byte selectors that spread a row's compacted
+// offset bytes over the 8 subgroups of 32 elements (0x0C: no offset).
+template <int FMT>
+__device__ __forceinline__ void fill_decode_tables(uint2 *dtab, uint2 *stab, int L) {
+  if constexpr (FMT == AUTOFP_FMT_AUTOFP8) {
+    uint32_t *t8 = (uint32_t *)dtab;
+    for (int i = (int)threadIdx.x; i < 256; i += (int)blockDim.x)
+      t8[i] = __builtin_bit_cast(uint32_t, half2v{delta8_h((uint32_t)i, L == 6), delta8_h((uint32_t)i >> 4, L == 6)});
+  } else {
+    for (int i = (int)threadIdx.x; i < 256; i += (int)blockDim.x) {
+      dtab[i] = delta_words((uint32_t)i);
+      uint32_t sel[2] = {0, 0}, j = 0;
+      for (int sg = 0; sg < 8; ++sg) {
+        const uint32_t on = ((uint32_t)i >> sg) & 1u;
+        sel[sg >> 2] |= (on ? j : 0x0Cu) << (8 * (sg & 3));
+        j += on;
+      }
+      stab[i] = make_uint2(sel[0], sel[1]);
+    }
+  }
+}
 
 // NW wavefronts (8 or 16: two or four per SIMD, so one wavefront's decode
 // and waits overlap the others' MFMAs) in a WGM x NW/WGM grid over the
@@ -246,12 +369,15 @@ __device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * 128
 // range (or past K) loads zeros. At the end the groups' accumulators are
 // summed through LDS in group order (deterministic) by group 0.
 //
+// ALT (prefill tiles, K <= kAltMaxK): the weight steps alternate between the
+// two halves of the wavefronts (the schedule is described at the loop).
+//
 // FMT (autofp_format) selects the weight decode: AUTOFP6 (the default) and
 // AUTOFP6E (its offsets scaled by 2^e of each element's E2M1 value) read one
 // offset byte per refined subgroup; AUTOFP8 two (4-bit d, clamped to
 // [-2, +1] at level 6); FP6G reads 24 bytes of E2M3 codes per 32 elements and
 // no offsets.
-template <int BM, int BN, int NW, int KG = 1, int FMT = AUTOFP_FMT_AUTOFP6>
+template <int BM, int BN, int NW, int KG = 1, int FMT = AUTOFP_FMT_AUTOFP6, bool ALT = false>
 __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
   constexpr int WGM = (NW >= 16 && BM >= 256) ? 4 : 2;   // wavefronts along M
   constexpr int WGN = NW / WGM;                         // wavefronts along N
@@ -267,6 +393,7 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
   constexpr int APW = BM / 8 / NW;            // activation copy instructions per wavefront and step
   static_assert(APW >= 1, "at least one activation copy per wavefront");
   static_assert(WITEMS == 64 * NW * HPT || (HPT == 1 && WITEMS < 64 * NW), "weight items per thread");
+  static_assert(!ALT || (KG == 1 && WITEMS <= 32 * NW), "alternating weight groups: one item per thread of a half");
   extern __shared__ __align__(16) unsigned char lds[];
 
   const int kg = KG > 1 ? (int)(threadIdx.x / (64 * NW)) : 0;   // K group
@@ -295,23 +422,21 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
   // elements (0x0C: no offset). A lookup replaces a few dozen bit operations
   // per 32 decoded weights. AUTOFP8: t8[byte] = the two fp16 offsets d/8 of
   // a byte of two 4-bit offsets.
-  uint2 *dtab = (uint2 *)(lds + KG * 2 * STAGE);
+  // (ALT: in an array of their own, which no copy into the stages can touch,
+  // so reading them waits for no copy in flight)
+  __shared__ uint2 tabs_alt[ALT ? 512 : 1];
+  uint2 *dtab = ALT ? tabs_alt : (uint2 *)(lds + KG * 2 * STAGE);
   uint2 *stab = dtab + 256;
   uint32_t *t8 = (uint32_t *)dtab;
-  if (refine_w && F8) {
-    for (int i = (int)threadIdx.x; i < 256; i += (int)blockDim.x)
-      t8[i] = __builtin_bit_cast(uint32_t, half2v{delta8_h((uint32_t)i, L == 6), delta8_h((uint32_t)i >> 4, L == 6)});
-    __syncthreads();
-  } else if (refine_w) {
-    for (int i = (int)threadIdx.x; i < 256; i += (int)blockDim.x) {
-      dtab[i] = delta_words((uint32_t)i);
-      uint32_t sel[2] = {0, 0}, j = 0;
-      for (int sg = 0; sg < 8; ++sg) {
-        const uint32_t on = ((uint32_t)i >> sg) & 1u;
-        sel[sg >> 2] |= (on ? j : 0x0Cu) << (8 * (sg & 3));
-        j += on;
-      }
-      stab[i] = make_uint2(sel[0], sel[1]);
+  // ALT: the weight mask and its prefix table in LDS (K <= kAltMaxK), so a
+  // step's offset loads depend on no other load
+  __shared__ uint8_t mask_l[ALT ? kAltMaxK / 32 : 1];
+  __shared__ int32_t pref_l[ALT ? kAltMaxK / 32 + 1 : 1];
+  if (refine_w) {
+    fill_decode_tables<FMT>(dtab, stab, L);
+    if constexpr (ALT) {
+      for (int64_t i = threadIdx.x; i < K / 32; i += blockDim.x) mask_l[i] = a.w_mask[i];
+      for (int64_t i = threadIdx.x; i <= K / 32; i += blockDim.x) pref_l[i] = a.prefix[i];
     }
     __syncthreads();
   }
@@ -343,9 +468,13 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
   };
 
   // weight rows of this thread: halves h0 .. h0 + HPT - 1 of row wr
-  const int wr = (HPT == 2) ? tid : (tid >> 1);
-  const int h0 = (HPT == 2) ? 0 : (tid & 1);
-  const bool w_thread = tid < WITEMS / HPT;   // whole wavefronts: WITEMS is a multiple of 64
+  // ALT: the two halves of the block's wavefronts (wg = 0, 1) take the
+  // weight steps in turn, each thread of a half one item
+  const int wg = ALT ? wave / (NW / 2) : 0;
+  const int tw = ALT ? tid % (32 * NW) : tid;
+  const int wr = (HPT == 2) ? tw : (tw >> 1);
+  const int h0 = (HPT == 2) ? 0 : (tw & 1);
+  const bool w_thread = tw < WITEMS / HPT;   // whole wavefronts: WITEMS is a multiple of 64
   struct WRegs {
     u32x4v c[HPT];
     u32x2v cx[HPT];   // FP6G: the last 8 of the 24 code bytes
@@ -372,7 +501,9 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
                                                        0, 0);
       }
     }
-    if (HPT == 2) {
+    if (HPT == 2 || ALT) {
+      // ALT: the dword of the step's four scale bytes (both halves), so no
+      // sub-dword result is widened after the load
       w.s = __builtin_amdgcn_raw_buffer_load_b32(rs, kin ? (int)(wr * (K >> 4) + (k0 >> 4)) : (int)0x80000000u, 0, 0);
     } else {
       w.s = __builtin_amdgcn_raw_buffer_load_b16(
@@ -382,8 +513,14 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
 #pragma unroll
       for (int i = 0; i < HPT; ++i) {
         const int64_t mi = kin ? (k0 >> 5) + h0 + i : 0;   // mask byte (32 elements)
-        w.mb[i] = kin ? a.w_mask[mi] : 0u;
-        w.pos[i] = a.prefix[mi];
+        if constexpr (ALT) {
+          // mask byte and prefix are read again from LDS at the decode, so
+          // they are not held in registers between the two steps
+          w.pos[i] = pref_l[mi];
+        } else {
+          w.mb[i] = kin ? a.w_mask[mi] : 0u;
+          w.pos[i] = a.prefix[mi];
+        }
         if constexpr (F8) {
           const uint32_t al = (uint32_t)(((wr * R + w.pos[i]) * 2) & ~(int64_t)3);
           w.o4[i] = __builtin_amdgcn_raw_buffer_load_b128(ro, (int)al, 0, 0);
@@ -395,94 +532,26 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
       }
     }
   };
-  auto store_w = [&](const WRegs &w, int stage) {
+  // k0: the step's first element (read by ALT, which takes the item's mask
+  // byte and prefix from LDS here)
+  auto store_w = [&](const WRegs &w, int stage, int64_t k0) {
     unsigned char *base = glds + stage * STAGE + A_BYTES;
 #pragma unroll
     for (int i = 0; i < HPT; ++i) {
       half8v h[4];
-      if constexpr (G6) {
-        // 32 six-bit codes in 24 bytes: 8 codes (48 bits) per fragment, at
-        // bits 0, 48, 96 and 144 of the six dwords
-        const uint64_t win4[4] = {
-            ((uint64_t)w.c[i][1] << 32) | w.c[i][0], (((uint64_t)w.c[i][2] << 32) | w.c[i][1]) >> 16,
-            ((uint64_t)w.cx[i][0] << 32) | w.c[i][3], (((uint64_t)w.cx[i][1] << 32) | w.cx[i][0]) >> 16};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint64_t win = win4[j];
-          half2v p[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            p[e] = e2m3x2_to_half2((uint32_t)(win >> (12 * e)) & 63u, (uint32_t)(win >> (12 * e + 6)) & 63u);
-          h[j] = half8v{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
-        }
-      } else {
-        uint32_t w4[4] = {w.c[i][0], w.c[i][1], w.c[i][2], w.c[i][3]};
-        if (L == 2) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) w4[j] = autofp2_codes(w4[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) h[j] = fp4x8_to_half8(w4[j]);
-      }
-      if (F8 && refine_w) {
-        // the (at most 8) two-byte offset words of these 32 elements, in
-        // subgroup order, from the 20 loaded bytes shifted by the misalignment
-        const uint32_t m = w.mb[i];
-        const uint32_t sh = (uint32_t)(((wr * R + w.pos[i]) * 2) & 3);
-        const uint32_t W0 = __builtin_amdgcn_alignbyte(w.o4[i][1], w.o4[i][0], sh);
-        const uint32_t W1 = __builtin_amdgcn_alignbyte(w.o4[i][2], w.o4[i][1], sh);
-        const uint32_t W2 = __builtin_amdgcn_alignbyte(w.o4[i][3], w.o4[i][2], sh);
-        const uint32_t W3 = __builtin_amdgcn_alignbyte(w.o5[i], w.o4[i][3], sh);
-        const uint64_t lo = (uint64_t)W0 | ((uint64_t)W1 << 32), hi = (uint64_t)W2 | ((uint64_t)W3 << 32);
-        uint32_t wd[8];
-        uint32_t j = 0;
-#pragma unroll
-        for (int sg = 0; sg < 8; ++sg) {
-          const uint32_t on = (m >> sg) & 1u;
-          const uint64_t src = j < 4 ? lo : hi;
-          wd[sg] = on ? (uint32_t)(src >> (16 * (j & 3))) & 0xFFFFu : 0u;
-          j += on;
-        }
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t a0 = wd[2 * p], a1 = wd[2 * p + 1];
-          h[p] += __builtin_bit_cast(half8v, make_uint4(t8[a0 & 0xFFu], t8[a0 >> 8], t8[a1 & 0xFFu], t8[a1 >> 8]));
-        }
-      } else if (refine_w) {
-        // the (at most 8) offset bytes of these 32 elements, in subgroup order;
-        // one byte per subgroup (0 where not refined) via a byte permute
-        const uint32_t m = w.mb[i];
-        const uint32_t sh = (uint32_t)((wr * R + w.pos[i]) & 3);
-        const uint32_t lo = __builtin_amdgcn_alignbyte(w.o[i][1], w.o[i][0], sh);
-        const uint32_t hi = __builtin_amdgcn_alignbyte(w.o[i][2], w.o[i][1], sh);
-        const uint2 sel = stab[m & 0xFFu];
-        const uint32_t E[2] = {__builtin_amdgcn_perm(hi, lo, sel.x), __builtin_amdgcn_perm(hi, lo, sel.y)};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint2 de = dtab[(E[p >> 1] >> (16 * (p & 1))) & 0xFFu];
-          const uint2 dd = dtab[(E[p >> 1] >> (16 * (p & 1) + 8)) & 0xFFu];
-          const half8v dl = __builtin_bit_cast(half8v, make_uint4(de.x, de.y, dd.x, dd.y));
-          if constexpr (FMT == AUTOFP_FMT_AUTOFP6E) {
-            // delta = d/8 * 2^e of each element's E2M1 value
-            const uint4 hv = __builtin_bit_cast(uint4, h[p]);
-            const uint4 fv = make_uint4(
-                __builtin_bit_cast(uint32_t, pow2e_h2(__builtin_bit_cast(half2v, hv.x))),
-                __builtin_bit_cast(uint32_t, pow2e_h2(__builtin_bit_cast(half2v, hv.y))),
-                __builtin_bit_cast(uint32_t, pow2e_h2(__builtin_bit_cast(half2v, hv.z))),
-                __builtin_bit_cast(uint32_t, pow2e_h2(__builtin_bit_cast(half2v, hv.w))));
-            h[p] += dl * __builtin_bit_cast(half8v, fv);
-          } else {
-            h[p] += dl;
-          }
+      const uint32_t sbytes = (HPT == 2) ? (w.s >> (16 * i)) : ALT ? (w.s >> (16 * h0)) : w.s;
+      uint32_t mb = 0, sh = 0;
+      if (refine_w) {
+        if constexpr (ALT) {
+          const int64_t mi = (k0 >> 5) + h0 + i;
+          mb = mask_l[mi];
+          sh = (uint32_t)(((wr * R + pref_l[mi]) * OW) & 3);
+        } else {
+          mb = w.mb[i];
+          sh = (uint32_t)(((wr * R + w.pos[i]) * OW) & 3);
         }
       }
-      const uint32_t sbytes = (HPT == 2) ? (w.s >> (16 * i)) : w.s;
-      const _Float16 b0 = (_Float16)e4m3_value(sbytes & 0xFFu);
-      const _Float16 b1 = (_Float16)e4m3_value((sbytes >> 8) & 0xFFu);
-      h[0] *= b0;
-      h[1] *= b0;
-      h[2] *= b1;
-      h[3] *= b1;
+      decode_w32<FMT>(w.c[i], w.cx[i], sbytes, w.o[i], w.o4[i], w.o5[i], mb, sh, L, refine_w, dtab, stab, t8, h);
 #pragma unroll
       for (int j = 0; j < 4; ++j) *(half8v *)(base + swz((uint32_t)wr, (uint32_t)(4 * (h0 + i) + j))) = h[j];
     }
@@ -500,10 +569,87 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
   const int64_t nkt = (K / kBK2 + KG - 1) / KG;
   const int64_t kb = nkt * kg;
   WRegs wreg;
+  if constexpr (ALT) {
+    // Weight step s is loaded by half s % 2 at the top of step s - 2 and
+    // decoded into its LDS stage at the end of step s - 1: two steps for the
+    // loads, one register set per thread. At the end of a step the half
+    // that loaded waits for all but its own new loads (issued after the
+    // activation copy, and the counter retires loads in issue order), the
+    // other half for everything; then one barrier.
+    constexpr int NWL = (G6 ? 2 : 1) + 1;            // weight loads per step: codes, scales
+    constexpr int NWR = NWL + (F8 ? 2 : 1);          // and the offset window
+    static_assert(NWR <= 15, "vmcnt field");
+    auto wait_step = [&](bool keep_w) {
+      if (!keep_w) __builtin_amdgcn_s_waitcnt((7 << 4));                 // vmcnt(0) lgkmcnt(0)
+      else if (refine_w) __builtin_amdgcn_s_waitcnt(NWR | (7 << 4));     // vmcnt(NWR) lgkmcnt(0)
+      else __builtin_amdgcn_s_waitcnt(NWL | (7 << 4));                   // vmcnt(NWL) lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    issue_a(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (w_thread) load_w((int64_t)wg * kBK2, wreg);
+    __builtin_amdgcn_sched_barrier(0);
+    if (wg == 0 && w_thread) store_w(wreg, 0, 0);
+    wait_step(wg == 1 && w_thread);
+    // one step; LOAD / STORE: this half's role in it (compile-time, so the
+    // compiler's own wait counts see which loads are in flight)
+    auto step = [&](int64_t kt, auto load_role, auto store_role) {
+      constexpr bool LOAD = decltype(load_role)::value, STORE = decltype(store_role)::value;
+      // the stage index stays a run-time value, so the unrolled steps share one
+      // set of LDS fragment addresses instead of holding one per stage
+      int st = (int)(kt & 1);
+      asm volatile("" : "+s"(st));
+      const bool more = kt + 1 < nkt;
+      if (more) issue_a((kt + 1) * kBK2, st ^ 1);
+      __builtin_amdgcn_sched_barrier(0);   // the weight loads after the copy (the wait count relies on it)
+      if (LOAD && w_thread) load_w((kt + 2) * kBK2, wreg);
+      __builtin_amdgcn_sched_barrier(0);
+      const unsigned char *As = glds + st * STAGE;
+      const unsigned char *Wsb = As + A_BYTES;
+#pragma unroll
+      for (int kk = 0; kk < kBK2 / 16; ++kk) {
+        const uint32_t ch = (uint32_t)(2 * kk + (lane >> 5));
+        half8v af[TI], bf[TJ];
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+          af[i] = *(const half8v *)(As + swz((uint32_t)(wm * WM + 32 * i + (lane & 31)), ch));
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          bf[j] = *(const half8v *)(Wsb + swz((uint32_t)(wn * WN + 32 * j + (lane & 31)), ch));
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      }
+      if (STORE && more && w_thread) store_w(wreg, st ^ 1, (kt + 1) * kBK2);
+      wait_step(LOAD && w_thread);
+    };
+    using T_ = std::integral_constant<bool, true>;
+    using F_ = std::integral_constant<bool, false>;
+    // half 0 loads on even steps and stores on odd ones, half 1 the reverse
+    int64_t kt = 0;
+    if (wg == 0) {
+      for (; kt + 1 < nkt; kt += 2) {
+        step(kt, T_{}, F_{});
+        step(kt + 1, F_{}, T_{});
+      }
+      if (kt < nkt) step(kt, T_{}, F_{});
+    } else {
+      for (; kt + 1 < nkt; kt += 2) {
+        step(kt, F_{}, T_{});
+        step(kt + 1, T_{}, F_{});
+      }
+      if (kt < nkt) step(kt, F_{}, T_{});
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the loads past K (which return zeros) have retired
+  } else {
   issue_a(kb * kBK2, 0);
   if (w_thread) {
     load_w(kb * kBK2, wreg);
-    store_w(wreg, 0);
+    store_w(wreg, 0, kb * kBK2);
   }
   __builtin_amdgcn_s_waitcnt(0);   // every load of step 0 (the activation copy included) has landed
   __syncthreads();
@@ -531,9 +677,10 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
         for (int j = 0; j < TJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    if (more && w_thread) store_w(wreg, st ^ 1);
+    if (more && w_thread) store_w(wreg, st ^ 1, (kb + kt + 1) * kBK2);
     __builtin_amdgcn_s_waitcnt(0);   // the next step's activation copy has landed
     __syncthreads();
+  }
   }
 
   if (KG > 1) {
@@ -627,17 +774,26 @@ hipError_t launch_gemm_fmt_t(const LinearArgs &a, hipStream_t s) {
   if (a.b >= 128) {
     const int64_t mtiles = (a.b + kBM2 - 1) / kBM2;
     // AUTOFP8 decodes on 128-row tiles (256 rows would exceed 128 VGPRs)
+    const bool alt = a.k <= kAltMaxK;
     if constexpr (FMT != AUTOFP_FMT_AUTOFP8) {
       if (mtiles * nt256 >= 256) {
         const size_t lds = 2 * (size_t)(kBM2 * kBK2 * 2 + 256 * kBK2 * 2) + kTabBytes;
-        hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 256, kGemmWaves, 1, FMT>), dim3((unsigned)(mtiles * nt256)),
-                           dim3(64 * kGemmWaves), lds, s, a);
+        if (alt)
+          hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 256, kGemmWaves, 1, FMT, true>), dim3((unsigned)(mtiles * nt256)),
+                             dim3(64 * kGemmWaves), lds, s, a);
+        else
+          hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 256, kGemmWaves, 1, FMT>), dim3((unsigned)(mtiles * nt256)),
+                             dim3(64 * kGemmWaves), lds, s, a);
         return hipGetLastError();
       }
     }
     const size_t lds = 2 * (size_t)(kBM2 * kBK2 * 2 + 128 * kBK2 * 2) + kTabBytes;
-    hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 128, kGemmWaves, 1, FMT>),
-                       dim3((unsigned)(mtiles * ((a.n + 127) / 128))), dim3(64 * kGemmWaves), lds, s, a);
+    if (alt)
+      hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 128, kGemmWaves, 1, FMT, true>),
+                         dim3((unsigned)(mtiles * ((a.n + 127) / 128))), dim3(64 * kGemmWaves), lds, s, a);
+    else
+      hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 128, kGemmWaves, 1, FMT>),
+                         dim3((unsigned)(mtiles * ((a.n + 127) / 128))), dim3(64 * kGemmWaves), lds, s, a);
     return hipGetLastError();
   }
   const int64_t mtiles = (a.b + 63) / 64;
@@ -667,14 +823,23 @@ hipError_t launch_gemm(const LinearArgs &a, hipStream_t s) {
     // 256 x 256 tiles when they still give every CU a block, else 256 x 128
     const int64_t mtiles = (a.b + kBM2 - 1) / kBM2;
     const int64_t big = mtiles * ((a.n + 255) / 256);
+    const bool alt = a.k <= kAltMaxK;
     if (big >= 256) {
       const size_t lds = 2 * (size_t)(kBM2 * kBK2 * 2 + 256 * kBK2 * 2) + kTabBytes;
-      hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 256, kGemmWaves>), dim3((unsigned)big), dim3(64 * kGemmWaves), lds, s,
-                         a);
+      if (alt)
+        hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 256, kGemmWaves, 1, AUTOFP_FMT_AUTOFP6, true>), dim3((unsigned)big),
+                           dim3(64 * kGemmWaves), lds, s, a);
+      else
+        hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 256, kGemmWaves>), dim3((unsigned)big), dim3(64 * kGemmWaves), lds,
+                           s, a);
     } else {
       const size_t lds = 2 * (size_t)(kBM2 * kBK2 * 2 + 128 * kBK2 * 2) + kTabBytes;
-      hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 128, kGemmWaves>), dim3((unsigned)(mtiles * ((a.n + 127) / 128))),
-                         dim3(64 * kGemmWaves), lds, s, a);
+      if (alt)
+        hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 128, kGemmWaves, 1, AUTOFP_FMT_AUTOFP6, true>),
+                           dim3((unsigned)(mtiles * ((a.n + 127) / 128))), dim3(64 * kGemmWaves), lds, s, a);
+      else
+        hipLaunchKernelGGL((gemm_lds_kernel<kBM2, 128, kGemmWaves>), dim3((unsigned)(mtiles * ((a.n + 127) / 128))),
+                           dim3(64 * kGemmWaves), lds, s, a);
     }
     return hipGetLastError();
   }

@@ -97,14 +97,17 @@ def test_gemv_shapes(n, b, k, level):
 
 
 GEMM_SHAPES = [(200, 130, 272), (384, 512, 1024), (128, 1, 64), (260, 129, 4096 + 16), (64, 300, 96),
-               (1000, 300, 512), (72, 257, 192), (8200, 2000, 128)]   # the last three: large-tile kernel
+               (1000, 300, 512), (72, 257, 192), (8200, 2000, 128), (300, 256, 64), (520, 1000, 2048),
+               (64, 130, 32768), (40, 129, 32768 + 64)]
 
 
 @pytest.mark.parametrize("n,m,k", GEMM_SHAPES)
 @pytest.mark.parametrize("level", [2, 4, 6])
 def test_gemm_shapes(n, m, k, level):
     """Ragged tiles in M and N for both GEMM kernels; 8200 x 2000 x 128 takes
-    the 256 x 256 tiles (264 blocks), 1000 x 300 and 72 x 257 the 256 x 128."""
+    the 256 x 256 tiles (264 blocks), the other 128+ token shapes with
+    K % 64 == 0 the 256 x 128 (K = 64: a single step; K = 192: an odd step
+    count; K = 32768 and 32832: long K loops)."""
     say(f"case: gemm N={n} M={m} K={k} level {level}")
     w, x = operands(n, m, k, seed=n + m + k, outliers=0.005)
     wp, xp4, xp6 = gpu_pack(w, x)
@@ -116,7 +119,8 @@ def test_gemm_shapes(n, m, k, level):
         assert torch.equal(yb, y.to(torch.bfloat16)), "bf16 output is not the RNE of the fp32 result"
 
 
-@pytest.mark.parametrize("op,n,b", [("gemv", 96, 12), ("gemm", 96, 12), ("gemv", 200, 40), ("gemv", 8200, 40)])
+@pytest.mark.parametrize("op,n,b", [("gemv", 96, 12), ("gemm", 96, 12), ("gemv", 200, 40), ("gemv", 8200, 40),
+                                    ("gemm", 300, 200)])
 def test_bf16_output_and_device_level(op, n, b):
     """bf16 outputs are the fp32 results rounded; a level read on the device
     gives the host-level result, bit for bit (40 tokens: the panel kernel,
