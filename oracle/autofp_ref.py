@@ -41,7 +41,7 @@ __all__ = [
     "quantize_activation", "quantize_weight", "select_weight_mask",
     "decode_activation", "decode_weight", "linear",
     "topk_entropy", "update_norm", "PolicyState", "policy_prefill", "policy_decode_step",
-    "silu", "epilogue",
+    "silu", "epilogue", "RMS_EPS", "rmsnorm_residual",
 ]
 
 # [AE] App. B.1: 16 contiguous elements along the reduction dimension share one
@@ -510,6 +510,7 @@ def epilogue(op, z, k, residual=None):
       "copy"     v = z[:, :k]
       "residual" v = residual + z[:, :k]
       "swiglu"   v = silu(z[:, :k]) * z[:, k:2k]
+      "residual_rmsnorm"  v = RMSNorm(residual + z[:, :k]) (rmsnorm_residual)
     Reading: the pages name no model; these are the residual stream and the
     gated MLP of the Llama-shaped layers the workloads use."""
     z = np.asarray(z, dtype=np.float64)
@@ -519,7 +520,32 @@ def epilogue(op, z, k, residual=None):
         return np.asarray(residual, dtype=np.float64) + z[:, :k]
     if op == "swiglu":
         return silu(z[:, :k]) * z[:, k:2 * k]
+    if op == "residual_rmsnorm":
+        return rmsnorm_residual(z, k, residual)[0].astype(np.float64)
     raise ValueError(op)
+
+
+RMS_EPS = 1e-5   # RMSNorm epsilon of the Llama-3 layers the workloads are shaped after
+
+
+def rmsnorm_residual(z, k, residual, eps=RMS_EPS):
+    """The residual add of a pre-norm block followed by the RMSNorm that
+    forms the next linear layer's input, as one post-processing step ([AE]
+    §6.4: the PPU turns completed outputs into the next layer's input
+    activations, non-linear operations included):
+      u = residual + z[:, :k]                  (the new hidden state; fp32, as an fp32 sum)
+      c = 1 / sqrt(sum_j u_j^2 / k + eps)      (per row; the squares summed in fp64, c rounded to fp32)
+      v = u * c                                (one fp32 product per element)
+    Reading: the pages name no model; RMSNorm with unit gain and Llama-3's
+    eps = 1e-5. The squares of fp32 values are exact in fp64, so the row sum
+    is fixed up to fp64 rounding and c to its fp32 rounding. Returns (v, u),
+    both fp32."""
+    z = np.asarray(z, dtype=np.float64)
+    u = (np.asarray(residual, dtype=np.float64) + z[:, :k]).astype(np.float32)
+    u64 = u.astype(np.float64)
+    c = (1.0 / np.sqrt(np.sum(u64 * u64, axis=1) / k + eps)).astype(np.float32)
+    v = u * c[:, None]          # float32 x float32 -> float32, round to nearest even
+    return v.astype(np.float32), u
 
 
 # ----------------------------------------------------------------------------

@@ -35,3 +35,44 @@ def test_epilogue_ops_select_and_combine_the_right_columns():
     # gate = first half (ln 3, 1), up = second half (2, 5)
     assert abs(v[0, 0] - 0.75 * math.log(3.0) * 2.0) < 1e-15
     assert abs(v[0, 1] - 5.0 / (1.0 + math.exp(-1.0))) < 1e-15
+
+
+def test_rmsnorm_residual_closed_forms():
+    """The residual RMSNorm step (oracle.rmsnorm_residual), pinned by facts
+    that hold whatever the implementation: a row with squares summing to 25
+    over k = 2 has RMS sqrt(12.5); scaling a row by a power of two leaves the
+    normalized row unchanged bit for bit when eps = 0 (sqrt and fp32
+    rounding commute with it); a zero row stays zero; each row is normalized
+    by its own RMS; u is the fp32 residual sum and only the first k columns of
+    z count."""
+    z = np.array([[1.0, 4.0, 99.0]])
+    r = np.array([[2.0, 0.0]])
+    v, u = O.rmsnorm_residual(z, 2, r, eps=0.0)            # u = (3, 4)
+    assert u.dtype == np.float32 and np.array_equal(u, np.array([[3.0, 4.0]], np.float32))
+    c = np.float32(1.0 / math.sqrt(12.5))
+    assert np.array_equal(v, np.array([[np.float32(3.0) * c, np.float32(4.0) * c]], np.float32))
+    # u is rounded as an fp32 sum: 1 + 2^-30 is 1 in fp32
+    _, u2 = O.rmsnorm_residual(np.array([[2.0 ** -30]]), 1, np.array([[1.0]]))
+    assert u2[0, 0] == np.float32(1.0)
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 64)).astype(np.float32)
+    zero = np.zeros_like(x)
+    v1, _ = O.rmsnorm_residual(zero, 64, x, eps=0.0)
+    v4, _ = O.rmsnorm_residual(zero, 64, 4.0 * x, eps=0.0)
+    v_small, _ = O.rmsnorm_residual(zero, 64, x / 1024.0, eps=0.0)
+    assert np.array_equal(v1, v4) and np.array_equal(v1, v_small)
+    # each row is normalized by its own RMS: rms(v) = sqrt(m / (m + eps)),
+    # m = mean(u^2), for rows of very different scale
+    y = np.concatenate([x[:1] * 1e-2, x[1:2] * 1e3, x[2:]], axis=0).astype(np.float32)
+    vy, _ = O.rmsnorm_residual(zero, 64, y)
+    m = (y.astype(np.float64) ** 2).mean(axis=1)
+    rms = np.sqrt((vy.astype(np.float64) ** 2).mean(axis=1))
+    assert np.all(np.abs(rms - np.sqrt(m / (m + O.RMS_EPS))) < 1e-6), rms
+    assert abs(rms[1] - 1.0) < 1e-6 and rms[0] < 0.96
+    # eps enters as mean + eps: a row of constant 1e-3 gives 1e-3 / sqrt(1e-6 + 1e-5)
+    vc, _ = O.rmsnorm_residual(np.zeros((1, 8)), 8, np.full((1, 8), 1e-3))
+    assert abs(float(vc[0, 0]) - 1e-3 / math.sqrt(1e-6 + 1e-5)) < 1e-6
+    vz, _ = O.rmsnorm_residual(np.zeros((1, 16)), 16, np.zeros((1, 16)))
+    assert not vz.any()
+    # the epilogue dispatcher returns the same v
+    assert np.array_equal(O.epilogue("residual_rmsnorm", z, 2, r), O.rmsnorm_residual(z, 2, r)[0])
