@@ -199,7 +199,8 @@ class DecodeBench:
         self.xq = {name: A.alloc_activation(batch, k, refine=True, device=device) for name, n, k in SHAPES}
         self.y = {name: torch.empty(batch, n, dtype=torch.float32, device=device) for name, n, k in SHAPES}
         ks = sorted({k for _, _, k in SHAPES})
-        self.qws = {k: torch.empty(A.workspace_bytes(0, batch, k), dtype=torch.uint8, device=device) for k in ks}
+        # encode / epilogue workspaces (AUTOFP_OP_EPILOGUE: the encode's plus the RMSNorm row scales)
+        self.qws = {k: torch.empty(A.workspace_bytes(8, batch, k), dtype=torch.uint8, device=device) for k in ks}
         self.gws = {k: torch.empty(A.workspace_bytes(2, batch, k), dtype=torch.uint8, device=device) for k in ks}
         self.logits = S.logits(batch, S.VOCAB, seed=7, device=device)
         self.sws = torch.empty(A.workspace_bytes(4, batch, S.VOCAB), dtype=torch.uint8, device=device)
@@ -237,15 +238,16 @@ class DecodeBench:
         self.z = {name: torch.empty(b, n, dtype=torch.float32, device=dev) for name, n, k in SHAPES}
         self.f = torch.empty(b, S.FFN, device=dev)
         self.a = torch.empty(b, H, device=dev)
+        self.nrm = torch.empty(b, H, device=dev)
 
     def step(self, s):
         """One decode step with the layers chained and each linear's output
         post-processed into the next linear's input in one call
-        (autofp_epilogue_quantize: copy / residual add / SwiGLU, then the
-        encode): G_E, then per layer GEMV Wqkv -> copy of the first 4096
-        outputs -> GEMV Wo -> h1 = h + o -> GEMV Wgate|Wup -> silu(g) * u ->
-        GEMV Wdown -> h2 = h1 + d, encoded for the next layer -> L_A and the
-        policy update."""
+        (autofp_epilogue_quantize: copy / residual add + RMSNorm / SwiGLU,
+        then the encode): G_E, then per layer GEMV Wqkv -> copy of the first
+        4096 outputs -> GEMV Wo -> h1 = h + o, RMSNorm(h1) encoded -> GEMV
+        Wgate|Wup -> silu(g) * u -> GEMV Wdown -> h2 = h1 + d, RMSNorm(h2)
+        encoded for the next layer -> L_A(h, h2) and the policy update."""
         A, p = self.A, self.p
         A.policy_signals(logits=self.logits, out_entropy=self.g_e, params=p, workspace=self.sws)
         layers = self.layers_of(s)
@@ -261,13 +263,13 @@ class DecodeBench:
             A.epilogue_quantize("copy", self.z["wqkv"], self.xq["wo"], refine=True, exclude_mask=layer["wo"].mask,
                                 workspace=self.qws[4096], params=p)
             g("wo", 4096)
-            A.epilogue_quantize("residual", self.z["wo"], self.xq["wgateup"], residual=h_in, v_out=self.h1,
+            A.epilogue_quantize("residual_rmsnorm", self.z["wo"], self.xq["wgateup"], residual=h_in, v_out=self.h1,
                                 refine=True, exclude_mask=layer["wgateup"].mask, workspace=self.qws[4096], params=p)
             g("wgateup", 4096)
             A.epilogue_quantize("swiglu", self.z["wgateup"], self.xq["wdown"], refine=True,
                                 exclude_mask=layer["wdown"].mask, workspace=self.qws[14336], params=p)
             g("wdown", 14336)
-            A.epilogue_quantize("residual", self.z["wdown"], self.xq["wqkv"], residual=self.h1, v_out=h_out,
+            A.epilogue_quantize("residual_rmsnorm", self.z["wdown"], self.xq["wqkv"], residual=self.h1, v_out=h_out,
                                 refine=True, exclude_mask=nxt["wqkv"].mask, workspace=self.qws[4096], params=p)
             A.policy_layer(1, j, h_in, h_out, self.state, g_e=self.g_e, l_a=self.l_a,
                            bits_rows=self.bits_rows, bits_layer=self.bits_layer, params=p)
@@ -295,7 +297,8 @@ class DecodeBench:
                             workspace=self.qws[4096], params=p)
             g("wo", 4096)
             torch.add(h_in, self.z["wo"], out=self.h1)
-            A.quantize_into(self.h1, self.xq["wgateup"], refine=True, exclude_mask=layer["wgateup"].mask,
+            rmsnorm_into(self.h1, self.nrm)
+            A.quantize_into(self.nrm, self.xq["wgateup"], refine=True, exclude_mask=layer["wgateup"].mask,
                             workspace=self.qws[4096], params=p)
             g("wgateup", 4096)
             silu_mul(self.z["wgateup"], 14336, self.f)
@@ -303,7 +306,8 @@ class DecodeBench:
                             workspace=self.qws[14336], params=p)
             g("wdown", 14336)
             torch.add(self.h1, self.z["wdown"], out=h_out)
-            A.quantize_into(h_out, self.xq["wqkv"], refine=True, exclude_mask=nxt["wqkv"].mask,
+            rmsnorm_into(h_out, self.nrm)
+            A.quantize_into(self.nrm, self.xq["wqkv"], refine=True, exclude_mask=nxt["wqkv"].mask,
                             workspace=self.qws[4096], params=p)
             A.policy_layer(1, j, h_in, h_out, self.state, g_e=self.g_e, l_a=self.l_a,
                            bits_rows=self.bits_rows, bits_layer=self.bits_layer, params=p)
@@ -345,10 +349,12 @@ class DecodeBench:
 class Step32:
     """The full decode step of a 32-layer Llama-3-8B-shaped model under the
     device-side policy: G_E of the step's logits, then per layer
-    a = Wqkv h (first 4096 outputs as the attention stand-in), o = Wo a,
-    h1 = h + o, [g|u] = Wgate|Wup h1, f = silu(g) * u, h2 = h1 + Wdown f, each
-    linear's output turned into the next linear's encoded input by one
-    producer-epilogue call, then L_A(h, h2) and the policy update, whose level
+    a = Wqkv RMSNorm(h) (first 4096 outputs as the attention stand-in),
+    o = Wo a, h1 = h + o, [g|u] = Wgate|Wup RMSNorm(h1), f = silu(g) * u,
+    h2 = h1 + Wdown f, each linear's output turned into the next linear's
+    encoded input by one producer-epilogue call (the residual adds with the
+    following RMSNorm, unit gain, so the hidden state stays finite over 32
+    layers of random weights), then L_A(h, h2) and the policy update, whose level
     the next layer's GEMVs read on the device. Several consecutive steps
     (logits drawn per step) form one HIP graph; the levels chosen are logged
     on the device and read back after timing."""
@@ -366,7 +372,7 @@ class Step32:
         for s in range(1, steps, 2):
             self.logits[s][:, 17] += 25.0
         self.xq = {name: A.alloc_activation(batch, k, refine=True, device=device) for name, n, k in SHAPES}
-        self.qws = {k: torch.empty(A.workspace_bytes(0, batch, k), dtype=torch.uint8, device=device) for k in (H, F)}
+        self.qws = {k: torch.empty(A.workspace_bytes(8, batch, k), dtype=torch.uint8, device=device) for k in (H, F)}
         self.gws = {k: torch.empty(A.workspace_bytes(2, batch, k), dtype=torch.uint8, device=device) for k in (H, F)}
         self.sws = torch.empty(A.workspace_bytes(4, batch, V), dtype=torch.uint8, device=device)
         self.y = {"wqkv": torch.empty(batch, 3 * 2048, device=device), "wo": torch.empty(batch, H, device=device),
@@ -396,15 +402,17 @@ class Step32:
                 A.epilogue_quantize("copy", self.y["wqkv"], self.xq["wo"], refine=True, exclude_mask=w["wo"].mask,
                                     workspace=self.qws[self.H])
                 A.gemv(w["wo"], self.xq["wo"], bits_dev=bits, out=self.y["wo"], workspace=self.gws[self.H])
-                A.epilogue_quantize("residual", self.y["wo"], self.xq["wgateup"], residual=h_in, v_out=self.h1,
-                                    refine=True, exclude_mask=w["wgateup"].mask, workspace=self.qws[self.H])
+                A.epilogue_quantize("residual_rmsnorm", self.y["wo"], self.xq["wgateup"], residual=h_in,
+                                    v_out=self.h1, refine=True, exclude_mask=w["wgateup"].mask,
+                                    workspace=self.qws[self.H])
                 A.gemv(w["wgateup"], self.xq["wgateup"], bits_dev=bits, out=self.y["wgateup"],
                        workspace=self.gws[self.H])
                 A.epilogue_quantize("swiglu", self.y["wgateup"], self.xq["wdown"], refine=True,
                                     exclude_mask=w["wdown"].mask, workspace=self.qws[self.F])
                 A.gemv(w["wdown"], self.xq["wdown"], bits_dev=bits, out=self.y["wdown"], workspace=self.gws[self.F])
-                A.epilogue_quantize("residual", self.y["wdown"], self.xq["wqkv"], residual=self.h1, v_out=h_out,
-                                    refine=True, exclude_mask=nxt["wqkv"].mask, workspace=self.qws[self.H])
+                A.epilogue_quantize("residual_rmsnorm", self.y["wdown"], self.xq["wqkv"], residual=self.h1,
+                                    v_out=h_out, refine=True, exclude_mask=nxt["wqkv"].mask,
+                                    workspace=self.qws[self.H])
                 A.policy_layer(1, i, h_in, h_out, self.state, g_e=self.g_e, new_sequence=(s == 0 and i == 0),
                                l_a=self.l_a, bits_rows=self.rows, bits_layer=lay[i + 1:i + 2])
                 h_in = h_out
@@ -430,6 +438,13 @@ class Step32:
 def torch_add(x, y, out):
     import torch
     torch.add(x, y, out=out)
+
+
+def rmsnorm_into(h, out):
+    """RMSNorm with unit gain and eps 1e-5 in torch ops (the unfused step's
+    counterpart of the residual_rmsnorm epilogue)."""
+    import torch
+    torch.mul(h, torch.rsqrt(h.pow(2).mean(dim=1, keepdim=True) + 1e-5), out=out)
 
 
 def silu_mul(gu, F, out):
@@ -904,7 +919,7 @@ def main():
             "workload": "AutoFP decode step over Llama-3-8B-shaped layers (Wqkv 6144x4096, Wo 4096x4096, "
                         "Wgate|Wup 28672x4096, Wdown 4096x14336): G_E over 128256 logits, then 3 chained layers "
                         "at levels 2/4/6, each: 4 GEMVs, each output post-processed into the next input by one "
-                        "producer-epilogue call (copy / residual / SwiGLU + AutoFP encode), L_A and the policy "
+                        "producer-epilogue call (copy / residual add + RMSNorm / SwiGLU + AutoFP encode), L_A and the policy "
                         "update",
             "batch": args.batch,
             "pool_layers": args.pool_layers,

@@ -171,7 +171,8 @@ typedef enum {
   AUTOFP_OP_SIGNALS = 4,      /* rows = batch, k = vocab (any vocab >= 1)       */
   AUTOFP_OP_KV_WRITE = 5,     /* rows = tokens * KV heads, k = head_dim         */
   AUTOFP_OP_KV_ATTENTION = 6, /* rows = batch * query heads, k = max_pages      */
-  AUTOFP_OP_GPTQ = 7          /* rows, k of the weight                          */
+  AUTOFP_OP_GPTQ = 7,         /* rows, k of the weight                          */
+  AUTOFP_OP_EPILOGUE = 8      /* rows, k of the epilogue's output               */
 } autofp_op;
 
 /* Fills *p with the paper's hyperparameters. Errors: NULL. */
@@ -286,7 +287,9 @@ autofp_status autofp_gptq_quantize(const float *w, int64_t rows, int64_t k, cons
 typedef enum {
   AUTOFP_EPI_COPY = 1,      /* v = z[:, :k]                                   */
   AUTOFP_EPI_RESIDUAL = 2,  /* v = residual + z[:, :k]                        */
-  AUTOFP_EPI_SWIGLU = 3     /* v = silu(z[:, :k]) * z[:, k:2k], silu(g) = g / (1 + e^-g) */
+  AUTOFP_EPI_SWIGLU = 3,    /* v = silu(z[:, :k]) * z[:, k:2k], silu(g) = g / (1 + e^-g) */
+  AUTOFP_EPI_RESIDUAL_RMSNORM = 4  /* u = residual + z[:, :k]; v = u * c, per row
+                                      c = 1 / sqrt(sum u^2 / k + 1e-5)  (RMSNorm, unit gain) */
 } autofp_epilogue_op;
 
 /*
@@ -300,8 +303,17 @@ typedef enum {
  * (same arguments refine / exclude_mask / p, same results bit for bit). One
  * launch for out->rows * out->k <= 16384 elements, two above. COPY and
  * RESIDUAL need ldz >= k, SWIGLU ldz >= 2k; residual [rows][k] fp32 (RESIDUAL
- * only). z, residual, v_out 16-byte aligned, ldz % 4 == 0. Workspace as
- * autofp_quantize (AUTOFP_OP_QUANTIZE, rows, k); out->kind ACTIVATION.
+ * and RESIDUAL_RMSNORM). z, residual, v_out 16-byte aligned, ldz % 4 == 0.
+ * Workspace as autofp_quantize (AUTOFP_OP_QUANTIZE, rows, k); out->kind
+ * ACTIVATION.
+ * RESIDUAL_RMSNORM is a pre-norm block's residual add and the RMSNorm of the
+ * next linear's input in one step: v_out (if not NULL) receives the residual
+ * sum u (the new hidden state, fp32), and the normalized v is what gets
+ * encoded. Per row the squares of u are summed in fp64 (each square exact) and
+ * c = 1 / sqrt(sum / k + 1e-5) is rounded to fp32; v = u * c in fp32. Its
+ * workspace is autofp_workspace_bytes(AUTOFP_OP_EPILOGUE, rows, k) (the
+ * encode's plus one fp32 scale per row); one launch for the same small sizes,
+ * four above (row scales, partial maxima, mask prefix, encode).
  * Errors: NULL, SHAPE, KIND, ARG, WORKSPACE, MISSING_REFINEMENT, HIP.
  */
 autofp_status autofp_epilogue_quantize(int32_t op, const float *z, int64_t ldz, const float *residual,

@@ -214,15 +214,18 @@ def epilogue_quantize(op, z: torch.Tensor, out: AutoFPTensor, residual=None, v_o
                       exclude_mask=None, workspace=None, params=None, stream=None) -> AutoFPTensor:
     """autofp_epilogue_quantize: v = op(z) (``"copy"``: the first out.k columns
     of z; ``"residual"``: residual + z; ``"swiglu"``: silu(z[:, :k]) *
-    z[:, k:2k]) in fp32, written to ``v_out`` when given, and encoded into
-    ``out`` as autofp_quantize encodes v."""
-    ops = {"copy": N.EPI_COPY, "residual": N.EPI_RESIDUAL, "swiglu": N.EPI_SWIGLU}
+    z[:, k:2k]; ``"residual_rmsnorm"``: RMSNorm(residual + z), with v_out
+    receiving the residual sum itself) in fp32, written to ``v_out`` when
+    given, and encoded into ``out`` as autofp_quantize encodes v. A given
+    ``workspace`` holds workspace_bytes(OP_EPILOGUE, out.rows, out.k) bytes."""
+    ops = {"copy": N.EPI_COPY, "residual": N.EPI_RESIDUAL, "swiglu": N.EPI_SWIGLU,
+           "residual_rmsnorm": N.EPI_RESIDUAL_RMSNORM}
     _dev_check(residual, v_out, exclude_mask)
     if z.dtype != torch.float32 or z.dim() != 2 or z.stride(1) != 1 or z.shape[0] != out.rows:
         raise ValueError("z must be a 2-D float32 tensor with unit column stride and out.rows rows")
     p = params or default_params()
     if workspace is None:
-        workspace = _workspace(N.OP_QUANTIZE, out.rows, out.k, z.device)
+        workspace = _workspace(N.OP_EPILOGUE, out.rows, out.k, z.device)
     st = out.struct()
     N.check(N.lib().autofp_epilogue_quantize(ops[op], _ptr(z), z.stride(0), _ptr(residual), _ptr(v_out),
                                              int(bool(refine)), _ptr(exclude_mask), C.byref(p), C.byref(st),

@@ -21,9 +21,9 @@ STATUS_NAMES = {
 F32, BF16 = 0, 1
 WEIGHT, ACTIVATION = 0, 1
 OP_QUANTIZE, OP_SELECT_MASK, OP_GEMV, OP_GEMM, OP_SIGNALS = 0, 1, 2, 3, 4
-OP_KV_WRITE, OP_KV_ATTENTION, OP_GPTQ = 5, 6, 7
+OP_KV_WRITE, OP_KV_ATTENTION, OP_GPTQ, OP_EPILOGUE = 5, 6, 7, 8
 KV_PAGE_TOKENS, KV_HEAD_DIM, KV_PAGE_BYTES = 64, 128, 4608
-EPI_COPY, EPI_RESIDUAL, EPI_SWIGLU = 1, 2, 3
+EPI_COPY, EPI_RESIDUAL, EPI_SWIGLU, EPI_RESIDUAL_RMSNORM = 1, 2, 3, 4
 FMT_AUTOFP6, FMT_AUTOFP6E, FMT_AUTOFP8, FMT_FP6G = 0, 1, 2, 3
 FORMATS = {"autofp6": FMT_AUTOFP6, "autofp6e": FMT_AUTOFP6E, "autofp8": FMT_AUTOFP8, "fp6g": FMT_FP6G}
 

@@ -230,4 +230,39 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+// Sum of the wavefront's fp64 values through DPP row moves and the gfx950
+// row swaps (ALU latency only: no LDS permutes). Every lane ends with a sum of
+// all 64 values; lane 0's is formed in one fixed order (quad pairs, quads,
+// half rows, rows, row pairs, halves), so it does not vary between runs.
+__device__ __forceinline__ double wave_sum_d_dpp(double v) {
+  auto move = [](double x, int ctrl) -> double {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+    switch (ctrl) {   // the DPP control must be a constant
+      case 0: lo = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, false); hi = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, false); break;
+      case 1: lo = __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, false); hi = __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, false); break;
+      case 2: lo = __builtin_amdgcn_mov_dpp(lo, 0x141, 0xF, 0xF, false); hi = __builtin_amdgcn_mov_dpp(hi, 0x141, 0xF, 0xF, false); break;
+      default: lo = __builtin_amdgcn_mov_dpp(lo, 0x140, 0xF, 0xF, false); hi = __builtin_amdgcn_mov_dpp(hi, 0x140, 0xF, 0xF, false); break;
+    }
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+  };
+  v += move(v, 0);   // quad xor 1
+  v += move(v, 1);   // quad xor 2: the quad's sum
+  v += move(v, 2);   // half-row mirror: 8 lanes
+  v += move(v, 3);   // row mirror: 16 lanes
+  auto swap_add = [](double x, bool rows32) -> double {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+    const auto l = rows32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                          : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h = rows32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                          : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    // the pair holds this lane's value and its partner's; fp addition commutes
+    return __builtin_bit_cast(double, ((uint64_t)h[0] << 32) | l[0]) +
+           __builtin_bit_cast(double, ((uint64_t)h[1] << 32) | l[1]);
+  };
+  v = swap_add(v, false);   // rows (0, 1) and (2, 3)
+  return swap_add(v, true); // halves
+}
+
 }  // namespace afp

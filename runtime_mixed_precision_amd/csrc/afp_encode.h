@@ -21,6 +21,7 @@ namespace afp {
 //   COPY      v = z[r][j]                         (the first k columns of z)
 //   RESIDUAL  v = resid[r][j] + z[r][j]
 //   SWIGLU    v = silu(z[r][j]) * z[r][k + j],    silu(g) = g / (1 + e^-g)
+//   RESIDUAL_RMSNORM  v = (resid[r][j] + z[r][j]) * c[r]   (c: the row's RMSNorm scale)
 // in fp32 (expf, one IEEE division, one product).
 // ---------------------------------------------------------------------------
 
@@ -29,8 +30,22 @@ __device__ __forceinline__ float silu_f32(float g) {
   return g / (1.0f + expf(-g));
 }
 
+// u = resid + z of the residual ops (the RESIDUAL_RMSNORM hidden state)
+__device__ __forceinline__ float4 resid_sum4(const EncodeArgs &a, int64_t r, int64_t j) {
+#pragma clang fp contract(off)
+  const float4 zz = *(const float4 *)(a.z + r * a.ldz + j);
+  const float4 rr = *(const float4 *)(a.resid + r * a.k + j);
+  return make_float4(rr.x + zz.x, rr.y + zz.y, rr.z + zz.z, rr.w + zz.w);
+}
+
+__device__ __forceinline__ float4 scale4(float4 u, float c) {
+#pragma clang fp contract(off)
+  return make_float4(u.x * c, u.y * c, u.z * c, u.w * c);
+}
+
 __device__ __forceinline__ float4 epilogue4(const EncodeArgs &a, int64_t r, int64_t j) {
 #pragma clang fp contract(off)
+  if (a.op == AUTOFP_EPI_RESIDUAL_RMSNORM) return scale4(resid_sum4(a, r, j), a.rowscale[r]);
   const float4 zz = *(const float4 *)(a.z + r * a.ldz + j);
   if (a.op == AUTOFP_EPI_RESIDUAL) {
     const float4 rr = *(const float4 *)(a.resid + r * a.k + j);
@@ -176,7 +191,8 @@ __device__ __forceinline__ float4 load_quad(const EncodeArgs &a, int64_t row, in
 }
 
 // The same with the source fixed at compile time: 0 x fp32, 1 x bf16, or
-// 1 + the epilogue op (2 copy, 3 residual, 4 SwiGLU).
+// 1 + the epilogue op (2 copy, 3 residual, 4 SwiGLU, 5 residual + RMSNorm
+// with the row scales in a.rowscale).
 template <int SRC>
 __device__ __forceinline__ float4 load_quad_t(const EncodeArgs &a, int64_t row, int64_t s) {
   if constexpr (SRC >= 2) {

@@ -54,8 +54,9 @@ struct EncodeArgs {
   int op;
   const float *z;
   int64_t ldz;
-  const float *resid;           // [rows][k] (residual op)
-  float *v_out;                 // [rows][k] or null
+  const float *resid;           // [rows][k] (residual ops)
+  float *v_out;                 // [rows][k] or null (RESIDUAL_RMSNORM: the residual sum u)
+  float *rowscale;              // RESIDUAL_RMSNORM, large tensors: the per-row scales c [rows]
 };
 // Small tensors (encode_is_small: rows * roundup(k/4, 64) <= 4096) are
 // encoded in one launch that takes the amax itself (a.partial is not read);
@@ -64,6 +65,10 @@ bool encode_is_small(int64_t rows, int64_t k);
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s);
 // The partial maxima of the epilogue tensor v = op(z, resid) of a.
 hipError_t launch_amax_partial_op(const EncodeArgs &a, float *partial, int n_partial, hipStream_t s);
+// RESIDUAL_RMSNORM: the per-row scales c = 1 / sqrt(sum u^2 / k + eps) of
+// u = resid + z into a.rowscale (fixed-order fp64 sums).
+hipError_t launch_rowscale(const EncodeArgs &a, hipStream_t s);
+constexpr double kRmsEps = 1e-5;   // RMSNorm epsilon of the RESIDUAL_RMSNORM epilogue
 
 // Weight-mask selection ([AE] App. E, Alg. 1 allocation with H = I).
 hipError_t launch_select_mask(const float *w, int64_t rows, int64_t k, int32_t budget,

@@ -60,6 +60,9 @@ size_t ws_quantize(int64_t rows, int64_t k) {
   return align_up(sizeof(float) * kAmaxBlocks) + align_up(sizeof(int32_t) * (mask_bytes(k) + 1));
 }
 
+// the epilogue's: the encode's, then one fp32 RMSNorm scale per row
+size_t ws_epilogue(int64_t rows, int64_t k) { return ws_quantize(rows, k) + align_up(sizeof(float) * (size_t)rows); }
+
 size_t ws_select(int64_t rows, int64_t k) {
   const size_t ncol = (size_t)(k / 4), ng = (size_t)(k / 16);
   return align_up(sizeof(float) * kAmaxBlocks) + align_up(sizeof(double) * (size_t)rows * ncol) +
@@ -236,6 +239,7 @@ EncodeArgs encode_args(const void *x, int32_t x_dtype, int32_t refine, const uin
     a.ldz = epi->ldz;
     a.resid = epi->resid;
     a.v_out = epi->v_out;
+    a.rowscale = epi->rowscale;
   }
   a.rows = out->rows;
   a.k = out->k;
@@ -268,6 +272,10 @@ autofp_status launch_quantize(const void *x, int32_t x_dtype, int32_t refine, co
   int32_t *prefix = (int32_t *)((char *)ws + align_up(sizeof(float) * kAmaxBlocks));
   hipError_t e = hipSuccess;
   if (!encode_is_small(out->rows, out->k)) {
+    if (a.op == AUTOFP_EPI_RESIDUAL_RMSNORM) {
+      e = launch_rowscale(a, s);
+      if (e != hipSuccess) return AUTOFP_ERR_HIP;
+    }
     e = a.op ? launch_amax_partial_op(a, partial, a.n_partial, s)
              : launch_amax_partial(x, x_dtype, out->rows * out->k, partial, a.n_partial, s);
     if (e != hipSuccess) return AUTOFP_ERR_HIP;
@@ -405,6 +413,7 @@ autofp_status autofp_workspace_bytes(int32_t op, int64_t rows, int64_t k, size_t
       if (k > 65536 || rows > kMaxGptqRows) return AUTOFP_ERR_SHAPE;
       *bytes = gptq_workspace_bytes(rows, k);
       return AUTOFP_OK;
+    case AUTOFP_OP_EPILOGUE: *bytes = ws_epilogue(rows, k); return AUTOFP_OK;
     default: return AUTOFP_ERR_ARG;
   }
 }
@@ -470,22 +479,29 @@ autofp_status autofp_epilogue_quantize(int32_t op, const float *z, int64_t ldz, 
                                        const autofp_params *p, autofp_packed *out, void *workspace,
                                        size_t workspace_bytes, void *stream) {
   if (!z) return AUTOFP_ERR_NULL;
-  if (op != AUTOFP_EPI_COPY && op != AUTOFP_EPI_RESIDUAL && op != AUTOFP_EPI_SWIGLU) return AUTOFP_ERR_ARG;
-  if (op == AUTOFP_EPI_RESIDUAL && !residual) return AUTOFP_ERR_NULL;
+  if (op != AUTOFP_EPI_COPY && op != AUTOFP_EPI_RESIDUAL && op != AUTOFP_EPI_SWIGLU &&
+      op != AUTOFP_EPI_RESIDUAL_RMSNORM)
+    return AUTOFP_ERR_ARG;
+  const bool resid_op = op == AUTOFP_EPI_RESIDUAL || op == AUTOFP_EPI_RESIDUAL_RMSNORM;
+  if (resid_op && !residual) return AUTOFP_ERR_NULL;
   // the encode's own checks, with z standing in for the input pointer
   const autofp_status st = check_quantize(z, AUTOFP_F32, refine, exclude_mask, out);
   if (st != AUTOFP_OK) return st;
   if (out->kind != AUTOFP_ACTIVATION) return AUTOFP_ERR_KIND;
   if (ldz < (op == AUTOFP_EPI_SWIGLU ? 2 : 1) * out->k || (ldz & 3) != 0) return AUTOFP_ERR_SHAPE;
   if ((residual && !aligned16(residual)) || (v_out && !aligned16(v_out))) return AUTOFP_ERR_ARG;
-  if (!workspace || workspace_bytes < ws_quantize(out->rows, out->k)) return AUTOFP_ERR_WORKSPACE;
+  const size_t need = op == AUTOFP_EPI_RESIDUAL_RMSNORM ? ws_epilogue(out->rows, out->k) : ws_quantize(out->rows, out->k);
+  if (!workspace || workspace_bytes < need) return AUTOFP_ERR_WORKSPACE;
   if (!aligned16(workspace)) return AUTOFP_ERR_ARG;
   EncodeArgs epi{};
   epi.op = op;
   epi.z = z;
   epi.ldz = ldz;
-  epi.resid = op == AUTOFP_EPI_RESIDUAL ? residual : nullptr;
+  epi.resid = resid_op ? residual : nullptr;
   epi.v_out = v_out;
+  epi.rowscale = op == AUTOFP_EPI_RESIDUAL_RMSNORM
+                     ? (float *)((char *)workspace + ws_quantize(out->rows, out->k))
+                     : nullptr;
   return launch_quantize(z, AUTOFP_F32, refine, exclude_mask, p, out, workspace, (hipStream_t)stream, &epi);
 }
 

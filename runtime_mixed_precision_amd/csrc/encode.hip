@@ -49,6 +49,32 @@ __global__ __launch_bounds__(kThreads) void amax_partial_op_kernel(EncodeArgs a,
   }
 }
 
+// RESIDUAL_RMSNORM row scales: block r sums the squares of u = resid + z of
+// row r in fp64 (each square exact; thread t takes quads t, t + 256, ...,
+// then the wavefronts' butterfly sums and the four wavefront sums in order:
+// one fixed order) and writes c = 1 / sqrt(sum / k + eps) rounded to fp32.
+__global__ __launch_bounds__(kThreads) void rowscale_kernel(EncodeArgs a) {
+#pragma clang fp contract(off)
+  const int64_t r = blockIdx.x;
+  double acc = 0.0;
+  for (int64_t q = threadIdx.x; q < a.k / 4; q += kThreads) {
+    const float4 u = resid_sum4(a, r, 4 * q);
+    acc += (double)u.x * (double)u.x;
+    acc += (double)u.y * (double)u.y;
+    acc += (double)u.z * (double)u.z;
+    acc += (double)u.w * (double)u.w;
+  }
+  acc = wave_sum_d_dpp(acc);
+  __shared__ double red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = red[0];
+    for (int w = 1; w < kThreads / 64; ++w) t += red[w];
+    a.rowscale[r] = (float)(1.0 / sqrt(t / (double)a.k + kRmsEps));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Tensor scale: partial maxima, then every encode block folds them (no atomics,
 // no zero-initialised scratch, identical T in every block).
@@ -233,8 +259,14 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(EncodeArgs a) {
   for (int64_t row = blockIdx.y; row < a.rows; row += gridDim.y) {
     float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
     if (live) {
-      v4 = load_quad(a, row, s);
-      if (a.op && a.v_out) *(float4 *)(a.v_out + row * a.k + 4 * s) = v4;
+      if (a.op == AUTOFP_EPI_RESIDUAL_RMSNORM) {
+        const float4 u4 = resid_sum4(a, row, 4 * s);
+        v4 = scale4(u4, a.rowscale[row]);
+        if (a.v_out) *(float4 *)(a.v_out + row * a.k + 4 * s) = u4;   // the hidden state
+      } else {
+        v4 = load_quad(a, row, s);
+        if (a.op && a.v_out) *(float4 *)(a.v_out + row * a.k + 4 * s) = v4;
+      }
     }
     if (fp6g) encode_subgroup_fp6g(a, T, row, s, live, v4);
     else encode_subgroup(a, T, row, s, live, v4, ex, wbyte, wpos);
@@ -276,15 +308,58 @@ __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t
   // block's own
   float m = 0.0f;
   float4 own = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 own_u = own;   // RESIDUAL_RMSNORM: the residual sum of the own slot
+  if constexpr (SRC == 1 + AUTOFP_EPI_RESIDUAL_RMSNORM) {
+    // u of every slot; per 64-slot chunk (one row: nqp is a multiple of 64)
+    // the fp64 sum of the exact squares, lane order fixed by the butterfly;
+    // then per row the chunk sums in order and c = 1 / sqrt(sum / k + eps)
+    __shared__ double chunk[kSmallSlots / 64];
+    __shared__ float rsc[kSmallSlots / 64];   // at most 64 rows: nqp >= 64
+    float4 uu[SPT];
 #pragma unroll
-  for (int j = 0; j < SPT; ++j) {
-    const int32_t uj = ((bx + j) & (SPT - 1)) * TPB + (int32_t)threadIdx.x;
-    const int32_t r = uj / nqp, sq = uj - r * nqp;
-    const bool ok = uj < tot && sq < nq;
-    float4 v = load_quad_t<SRC>(a, ok ? r : 0, ok ? sq : 0);   // slot 0 stands in for absent slots
-    v = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
-    m = fmaxf(m, max4(v));
-    if (j == 0) own = v;
+    for (int j = 0; j < SPT; ++j) {
+      const int32_t uj = ((bx + j) & (SPT - 1)) * TPB + (int32_t)threadIdx.x;
+      const int32_t r = uj / nqp, sq = uj - r * nqp;
+      const bool ok = uj < tot && sq < nq;
+      const float4 u = resid_sum4(a, ok ? r : 0, ok ? 4 * sq : 0);
+      uu[j] = ok ? u : make_float4(0.f, 0.f, 0.f, 0.f);
+      double d = (double)uu[j].x * (double)uu[j].x;
+      d += (double)uu[j].y * (double)uu[j].y;
+      d += (double)uu[j].z * (double)uu[j].z;
+      d += (double)uu[j].w * (double)uu[j].w;
+      d = wave_sum_d_dpp(d);
+      if ((threadIdx.x & 63) == 0 && uj < tot) chunk[uj / 64] = d;
+    }
+    __syncthreads();
+    const int32_t cpr = nqp / 64;   // chunks per row
+    if ((int32_t)threadIdx.x < (int32_t)a.rows) {
+      double t = 0.0;
+      for (int32_t c = 0; c < cpr; ++c) t += chunk[(int32_t)threadIdx.x * cpr + c];
+      rsc[threadIdx.x] = (float)(1.0 / sqrt(t / (double)a.k + kRmsEps));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int32_t uj = ((bx + j) & (SPT - 1)) * TPB + (int32_t)threadIdx.x;
+      const int32_t r = uj / nqp;
+      const float4 v = uj < tot ? scale4(uu[j], rsc[r]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      m = fmaxf(m, max4(v));
+      if (j == 0) {
+        own = v;
+        own_u = uu[0];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int32_t uj = ((bx + j) & (SPT - 1)) * TPB + (int32_t)threadIdx.x;
+      const int32_t r = uj / nqp, sq = uj - r * nqp;
+      const bool ok = uj < tot && sq < nq;
+      float4 v = load_quad_t<SRC>(a, ok ? r : 0, ok ? sq : 0);   // slot 0 stands in for absent slots
+      v = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+      m = fmaxf(m, max4(v));
+      if (j == 0) own = v;
+    }
   }
   m = wave_max(m);
   __shared__ float red[TPB / 64];
@@ -296,7 +371,8 @@ __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t
   const float T = tensor_scale_of(a, amax);
   if (bx == 0 && threadIdx.x == 0) *a.tensor_scale = T;
 
-  if (SRC >= 2 && live && a.v_out) *(float4 *)(a.v_out + (int64_t)row * a.k + 4 * s) = own;
+  if (SRC >= 2 && live && a.v_out)
+    *(float4 *)(a.v_out + (int64_t)row * a.k + 4 * s) = SRC == 1 + AUTOFP_EPI_RESIDUAL_RMSNORM ? own_u : own;
   if (fp6g) encode_subgroup_fp6g(a, T, row, s, live, own);
   else encode_subgroup(a, T, row, s, live, own, ex, wbyte, wpos);
 }
@@ -478,6 +554,11 @@ hipError_t launch_amax_partial_op(const EncodeArgs &a, float *partial, int n_par
   return hipGetLastError();
 }
 
+hipError_t launch_rowscale(const EncodeArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(rowscale_kernel, dim3((unsigned)a.rows), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_mask_prefix(const uint8_t *mask, int64_t nbytes, int32_t *prefix, hipStream_t s) {
   hipLaunchKernelGGL(mask_prefix_kernel, dim3(1), dim3(1024), 0, s, mask, nbytes, prefix);
   return hipGetLastError();
@@ -496,6 +577,7 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t s) {
       AFP_SMALL(2);
       AFP_SMALL(3);
       AFP_SMALL(4);
+      AFP_SMALL(5);
 #undef AFP_SMALL
       default: return hipErrorInvalidValue;
     }

@@ -328,3 +328,26 @@ def test_kv_attention_rejects_bad_arguments(N):
     assert a(FAKE, 2, 32, C.byref(nt)) == 1
     big = kv_cache(N, max_pages=64 * 64 + 1)
     assert a(FAKE, 2, 32, C.byref(big)) == 2
+
+
+def test_epilogue_rejects_bad_arguments_and_sizes_its_workspace(N):
+    """autofp_epilogue_quantize's checks (no launch is reached): unknown op,
+    a residual op without its residual, z narrower than k, and a workspace
+    of autofp_quantize's size for RESIDUAL_RMSNORM, which needs one more fp32
+    per row (AUTOFP_OP_EPILOGUE)."""
+    L = N.lib()
+    p = params(N)
+    rows, k = 4, 64
+    wq, we = C.c_size_t(), C.c_size_t()
+    assert L.autofp_workspace_bytes(N.OP_QUANTIZE, rows, k, C.byref(wq)) == 0
+    assert L.autofp_workspace_bytes(N.OP_EPILOGUE, rows, k, C.byref(we)) == 0
+    assert we.value >= wq.value + 4 * rows
+    out = packed(N, N.ACTIVATION, rows=rows, k=k)
+    e = lambda op, resid, ldz, wsz: L.autofp_epilogue_quantize(op, FAKE, ldz, resid, None, 0, None, C.byref(p),
+                                                               C.byref(out), FAKE, wsz, None)
+    big = we.value
+    assert e(5, FAKE, k, big) == 8                                  # unknown op
+    assert e(N.EPI_RESIDUAL_RMSNORM, None, k, big) == 1             # residual missing
+    assert e(N.EPI_RESIDUAL, None, k, big) == 1
+    assert e(N.EPI_RESIDUAL_RMSNORM, FAKE, k - 4, big) == 2         # ldz < k
+    assert e(N.EPI_RESIDUAL_RMSNORM, FAKE, k, wq.value) == 5        # the encode's workspace is short

@@ -88,3 +88,44 @@ def test_epilogue_without_v_out_and_arguments():
         A.epilogue_quantize("swiglu", z[:, :k + 16].contiguous(), out)      # ldz < 2k
     with pytest.raises(A.AutofpError):
         A.epilogue_quantize("residual", z, out)                             # residual missing
+
+
+@pytest.mark.parametrize("rows,k", [(1, 4096), (4, 4096), (1, 14336), (3, 272), (64, 1024), (64, 4096), (16, 14336)])
+@pytest.mark.parametrize("refine", [False, True])
+def test_epilogue_residual_rmsnorm(rows, k, refine):
+    """Residual add + RMSNorm (one launch up to 4096 subgroup slots: 1 x 4096,
+    4 x 4096, 1 x 14336, 3 x 272; the row-scale pass above: 64 x 1024,
+    64 x 4096, 16 x 14336): v_out holds u = residual + z bit for bit; the
+    packed output equals the oracle's encode of the oracle's normalized v
+    (whose row scales are fp32 roundings of fp64 sums) bit for bit, and the
+    device encode of that same v byte for byte. The rows carry different
+    scales (one of them 1e3 larger, one small enough for eps to matter)."""
+    say(f"case: epilogue residual_rmsnorm rows={rows} k={k} refine={refine}")
+    ldz = k + 256
+    z = S.hidden(rows, ldz, seed=rows + k, tensor_id=5, device=DEV) * 3.0
+    resid = S.hidden(rows, k, seed=rows + k, tensor_id=6, device=DEV)
+    if rows > 1:
+        resid[0] *= 1e3
+        z[0] *= 1e3
+        resid[-1] *= 1e-3
+        z[-1] *= 1e-3
+    wm, _ = A.select_weight_mask(S.weights(64, k, seed=3, tensor_id=3, device=DEV))
+    ex = wm if refine else None
+    out = A.alloc_activation(rows, k, refine=refine, device=DEV)
+    u = torch.empty(rows, k, dtype=torch.float32, device=DEV)
+    A.epilogue_quantize("residual_rmsnorm", z, out, residual=resid, v_out=u, refine=refine, exclude_mask=ex)
+    torch.cuda.synchronize()
+    v_ref, u_ref = O.rmsnorm_residual(z.cpu().numpy(), k, resid.cpu().numpy())
+    assert np.array_equal(u.cpu().numpy(), u_ref)
+    exn = None if ex is None else ex.cpu().numpy()
+    ref = O.quantize_activation(v_ref, refine=refine, exclude_mask=exn)
+    same_packed(out, ref, refine)
+    q = A.quantize_activation(torch.from_numpy(v_ref).to(DEV), refine=refine, exclude_mask=ex)
+    torch.cuda.synchronize()
+    for key in ("codes", "scales", "tensor_scale") + (("mask", "offsets") if refine else ()):
+        assert torch.equal(getattr(q, key), getattr(out, key)), key
+    # deterministic: a second call gives the same bytes
+    out2 = A.alloc_activation(rows, k, refine=refine, device=DEV)
+    A.epilogue_quantize("residual_rmsnorm", z, out2, residual=resid, refine=refine, exclude_mask=ex)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.codes, out.codes) and torch.equal(out2.tensor_scale, out.tensor_scale)
