@@ -22,12 +22,25 @@ namespace afp {
 //   RESIDUAL  v = resid[r][j] + z[r][j]
 //   SWIGLU    v = silu(z[r][j]) * z[r][k + j],    silu(g) = g / (1 + e^-g)
 //   RESIDUAL_RMSNORM  v = (resid[r][j] + z[r][j]) * c[r]   (c: the row's RMSNorm scale)
-// in fp32 (expf, one IEEE division, one product).
+// in fp32; silu within a few units in the last place (below).
 // ---------------------------------------------------------------------------
 
+// silu(g) = g / (1 + e^-g): e^-g = 2^t with t = -g log2(e) carried as
+// t_hi + t_lo (log2(e) split into two fp32 parts, the product's rounding
+// error recovered by an fma), 2^t_hi from the hardware exp2 (1 ulp) times the
+// first-order correction (1 + t_lo ln 2), then the hardware reciprocal
+// (1 ulp) and one product: relative error below 4 * 2^-23. Past t_hi = 128
+// (g < -88.7) e^-g overflows and the result is -0, as with expf.
 __device__ __forceinline__ float silu_f32(float g) {
 #pragma clang fp contract(off)
-  return g / (1.0f + expf(-g));
+  constexpr float kL2eHi = 1.44269502162933349609375f;   // fp32(log2 e)
+  constexpr float kL2eLo = 1.9259629912e-08f;            // log2 e - kL2eHi
+  constexpr float kLn2 = 0.693147180559945309f;
+  const float th = -g * kL2eHi;
+  const float tl = fmaf(-g, kL2eHi, -th) + (-g) * kL2eLo;
+  const float eh = __builtin_amdgcn_exp2f(th);
+  const float e = th < 128.0f ? fmaf(eh, tl * kLn2, eh) : eh;
+  return g * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // u = resid + z of the residual ops (the RESIDUAL_RMSNORM hidden state)

@@ -278,18 +278,57 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(EncodeArgs a) {
 // subgroup slots): slot u holds subgroup s = u mod nqp of row u / nqp, nqp =
 // k/4 rounded up to 64 (so a wavefront never spans two rows). Block bx of TPB
 // threads encodes slots [TPB bx, TPB bx + TPB); every block loads all slots
-// (thread t: slots j TPB + t, j < 4096 / TPB) with every load in flight at
-// once, takes the amax of the whole tensor from them and encodes its own slot
-// from the registers: one round trip to memory, no second launch. The mask
-// bytes the encode needs are loaded before the reduction.
+// (thread t: slots j TPB + t, j < SPT, SPT the block count rounded up to a
+// power of two), takes the amax of the whole tensor from them and encodes
+// its own slot from the registers: one round trip to memory, no second
+// launch. 256 threads a block (one wavefront per SIMD: the per-slot encode
+// is a chain of dependent instructions), 512 for SwiGLU (each block
+// evaluates every element's silu, so fewer, larger blocks). The source is fixed at compile time and
+// every load of a thread (its slots' inputs, then the mask bytes the encode
+// needs) is issued before the first use of any, so the loads of a thread
+// overlap instead of waiting one after another.
 // ---------------------------------------------------------------------------
 constexpr int kSmallSlots = 4096;
-constexpr int kSmallTPB = 512;
 
-template <int TPB, int SRC>
+// The raw inputs of the four elements of subgroup s of row `row`: p = x (SRC
+// 0 fp32, 1 bf16) or z (the epilogue ops, SRC = 1 + op); q = the residual
+// (residual ops) or the up half z[k + j] (SwiGLU). Loads only.
+template <int SRC>
+__device__ __forceinline__ void src_load(const EncodeArgs &a, int32_t row, int32_t s, float4 &p, float4 &q) {
+  if constexpr (SRC == 0) {
+    p = *(const float4 *)((const float *)a.x + (int64_t)row * a.k + 4 * s);
+  } else if constexpr (SRC == 1) {
+    const uint2 v = *(const uint2 *)((const uint16_t *)a.x + (int64_t)row * a.k + 4 * s);
+    p = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                    __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+  } else {
+    p = *(const float4 *)(a.z + (int64_t)row * a.ldz + 4 * s);
+    if constexpr (SRC == 1 + AUTOFP_EPI_RESIDUAL || SRC == 1 + AUTOFP_EPI_RESIDUAL_RMSNORM)
+      q = *(const float4 *)(a.resid + (int64_t)row * a.k + 4 * s);
+    else if constexpr (SRC == 1 + AUTOFP_EPI_SWIGLU)
+      q = *(const float4 *)(a.z + (int64_t)row * a.ldz + a.k + 4 * s);
+  }
+}
+
+// The tensor value from the raw inputs (epilogue4's arithmetic, the op fixed
+// at compile time): x or z; resid + z; silu(z) * up; RESIDUAL_RMSNORM: the
+// residual sum u (the row scale applies later).
+template <int SRC>
+__device__ __forceinline__ float4 src_value(float4 p, float4 q) {
+#pragma clang fp contract(off)
+  if constexpr (SRC == 1 + AUTOFP_EPI_RESIDUAL || SRC == 1 + AUTOFP_EPI_RESIDUAL_RMSNORM) {
+    return make_float4(q.x + p.x, q.y + p.y, q.z + p.z, q.w + p.w);
+  } else if constexpr (SRC == 1 + AUTOFP_EPI_SWIGLU) {
+    return make_float4(silu_f32(p.x) * q.x, silu_f32(p.y) * q.y, silu_f32(p.z) * q.z, silu_f32(p.w) * q.w);
+  } else {
+    return p;
+  }
+}
+
+template <int TPB, int SPT, int SRC>
 __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t nqp) {
-  constexpr int SPT = kSmallSlots / TPB;
-  static_assert((SPT & (SPT - 1)) == 0, "slot groups per thread: a power of two");
+  static_assert((SPT & (SPT - 1)) == 0 && TPB * SPT <= kSmallSlots, "slot groups per thread: a power of two");
+  constexpr bool NORM = SRC == 1 + AUTOFP_EPI_RESIDUAL_RMSNORM;
   const int32_t nq = (int32_t)(a.k / 4);
   const int32_t tot = (int32_t)a.rows * nqp;
   const int bx = (int)blockIdx.x;
@@ -297,19 +336,36 @@ __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t
   const int32_t row = u / nqp, s = u - row * nqp;
   const bool live = u < tot && s < nq;
   const bool fp6g = a.fmt == AUTOFP_FMT_FP6G;
-  uint32_t ex = 0, wbyte = 0;
-  int32_t wpos = 0;
-  if (!fp6g && a.act_refine && a.exclude_mask && live) ex = ((uint32_t)a.exclude_mask[s >> 3] >> (s & 7)) & 1u;
-  if (!fp6g && a.w_mask && live) {
-    wbyte = a.w_mask[s >> 3];
-    wpos = a.w_prefix[s >> 3] + __popc(wbyte & ((1u << (s & 7)) - 1u));
-  }
+  // row of slot uj < 4096 without an integer division: (uj + 1/2) / nqp lies
+  // at least 1/(2 nqp) >= 2^-13 (nqp <= 4096) inside its integer interval,
+  // far above the rounding error of the fp32 product (at most 2^-17 for
+  // quotients up to 64)
+  const float inv_nqp = 1.0f / (float)nqp;
+  auto row_of = [&](int32_t uj) { return (int32_t)(((float)uj + 0.5f) * inv_nqp); };
   // slot groups in the order bx, bx + 1, ... (mod SPT): the first is the
-  // block's own
+  // block's own; an absent slot reads slot 0 and counts as zero
+  float4 p[SPT], q[SPT];
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int32_t uj = ((bx + j) & (SPT - 1)) * TPB + (int32_t)threadIdx.x;
+    const int32_t r = row_of(uj), sq = uj - r * nqp;
+    const bool ok = uj < tot && sq < nq;
+    src_load<SRC>(a, ok ? r : 0, ok ? sq : 0, p[j], q[j]);
+  }
+  // mask bytes of the own slot (read at slot 0 when absent, unused then)
+  const int32_t sl = live ? s : 0;
+  uint32_t exb = 0, wb = 0;
+  int32_t wp = 0;
+  if (!fp6g && a.act_refine && a.exclude_mask) exb = a.exclude_mask[sl >> 3];
+  if (!fp6g && a.w_mask) {
+    wb = a.w_mask[sl >> 3];
+    wp = a.w_prefix[sl >> 3];
+  }
+
   float m = 0.0f;
   float4 own = make_float4(0.f, 0.f, 0.f, 0.f);
   float4 own_u = own;   // RESIDUAL_RMSNORM: the residual sum of the own slot
-  if constexpr (SRC == 1 + AUTOFP_EPI_RESIDUAL_RMSNORM) {
+  if constexpr (NORM) {
     // u of every slot; per 64-slot chunk (one row: nqp is a multiple of 64)
     // the fp64 sum of the exact squares, lane order fixed by the butterfly;
     // then per row the chunk sums in order and c = 1 / sqrt(sum / k + eps)
@@ -319,10 +375,9 @@ __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
       const int32_t uj = ((bx + j) & (SPT - 1)) * TPB + (int32_t)threadIdx.x;
-      const int32_t r = uj / nqp, sq = uj - r * nqp;
+      const int32_t r = row_of(uj), sq = uj - r * nqp;
       const bool ok = uj < tot && sq < nq;
-      const float4 u = resid_sum4(a, ok ? r : 0, ok ? 4 * sq : 0);
-      uu[j] = ok ? u : make_float4(0.f, 0.f, 0.f, 0.f);
+      uu[j] = ok ? src_value<SRC>(p[j], q[j]) : make_float4(0.f, 0.f, 0.f, 0.f);
       double d = (double)uu[j].x * (double)uu[j].x;
       d += (double)uu[j].y * (double)uu[j].y;
       d += (double)uu[j].z * (double)uu[j].z;
@@ -341,7 +396,7 @@ __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
       const int32_t uj = ((bx + j) & (SPT - 1)) * TPB + (int32_t)threadIdx.x;
-      const int32_t r = uj / nqp;
+      const int32_t r = row_of(uj);
       const float4 v = uj < tot ? scale4(uu[j], rsc[r]) : make_float4(0.f, 0.f, 0.f, 0.f);
       m = fmaxf(m, max4(v));
       if (j == 0) {
@@ -353,10 +408,9 @@ __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
       const int32_t uj = ((bx + j) & (SPT - 1)) * TPB + (int32_t)threadIdx.x;
-      const int32_t r = uj / nqp, sq = uj - r * nqp;
+      const int32_t r = row_of(uj), sq = uj - r * nqp;
       const bool ok = uj < tot && sq < nq;
-      float4 v = load_quad_t<SRC>(a, ok ? r : 0, ok ? sq : 0);   // slot 0 stands in for absent slots
-      v = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 v = ok ? src_value<SRC>(p[j], q[j]) : make_float4(0.f, 0.f, 0.f, 0.f);
       m = fmaxf(m, max4(v));
       if (j == 0) own = v;
     }
@@ -372,9 +426,14 @@ __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t
   if (bx == 0 && threadIdx.x == 0) *a.tensor_scale = T;
 
   if (SRC >= 2 && live && a.v_out)
-    *(float4 *)(a.v_out + (int64_t)row * a.k + 4 * s) = SRC == 1 + AUTOFP_EPI_RESIDUAL_RMSNORM ? own_u : own;
-  if (fp6g) encode_subgroup_fp6g(a, T, row, s, live, own);
-  else encode_subgroup(a, T, row, s, live, own, ex, wbyte, wpos);
+    *(float4 *)(a.v_out + (int64_t)row * a.k + 4 * s) = NORM ? own_u : own;
+  if (fp6g) {
+    encode_subgroup_fp6g(a, T, row, s, live, own);
+  } else {
+    const uint32_t ex = (a.act_refine && a.exclude_mask && live) ? (exb >> (s & 7)) & 1u : 0u;
+    const int32_t wpos = wp + __popc(wb & ((1u << (s & 7)) - 1u));
+    encode_subgroup(a, T, row, s, live, own, ex, live ? wb : 0u, live ? wpos : 0);
+  }
 }
 
 }  // namespace
@@ -564,24 +623,45 @@ hipError_t launch_mask_prefix(const uint8_t *mask, int64_t nbytes, int32_t *pref
   return hipGetLastError();
 }
 
+// blocks of TPB threads over rows * nqp slots; SPT = the block count rounded
+// up to a power of two
+template <int TPB, int SRC>
+hipError_t launch_small(const EncodeArgs &a, int32_t nqp, hipStream_t s) {
+  const int64_t gx = (a.rows * nqp + TPB - 1) / TPB;
+  int spt = 1;
+  while (spt < gx) spt *= 2;
+#define AFP_SMALL(P)                                                                               \
+  case P:                                                                                          \
+    if constexpr (TPB * P <= kSmallSlots)                                                          \
+      hipLaunchKernelGGL((encode_small_kernel<TPB, P, SRC>), dim3((unsigned)gx), dim3(TPB), 0, s, a, nqp); \
+    else                                                                                           \
+      return hipErrorInvalidValue;                                                                 \
+    break
+  switch (spt) {
+    AFP_SMALL(1);
+    AFP_SMALL(2);
+    AFP_SMALL(4);
+    AFP_SMALL(8);
+    AFP_SMALL(16);
+    default: return hipErrorInvalidValue;
+  }
+#undef AFP_SMALL
+  return hipGetLastError();
+}
+
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s) {
   if (encode_is_small(a.rows, a.k)) {
     const int64_t nqp = encode_slots_per_row(a.k);
-    const unsigned gx = (unsigned)((a.rows * nqp + kSmallTPB - 1) / kSmallTPB);
     const int src = a.op ? 1 + a.op : (a.dtype == AUTOFP_BF16 ? 1 : 0);
     switch (src) {
-#define AFP_SMALL(S) \
-  case S: hipLaunchKernelGGL((encode_small_kernel<kSmallTPB, S>), dim3(gx), dim3(kSmallTPB), 0, s, a, (int32_t)nqp); break
-      AFP_SMALL(0);
-      AFP_SMALL(1);
-      AFP_SMALL(2);
-      AFP_SMALL(3);
-      AFP_SMALL(4);
-      AFP_SMALL(5);
-#undef AFP_SMALL
+      case 0: return launch_small<256, 0>(a, (int32_t)nqp, s);
+      case 1: return launch_small<256, 1>(a, (int32_t)nqp, s);
+      case 2: return launch_small<256, 2>(a, (int32_t)nqp, s);
+      case 3: return launch_small<256, 3>(a, (int32_t)nqp, s);
+      case 4: return launch_small<512, 4>(a, (int32_t)nqp, s);
+      case 5: return launch_small<256, 5>(a, (int32_t)nqp, s);
       default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
   }
   const int64_t ns = a.k / 4;
   const int64_t gx = (ns + kEncThreads - 1) / kEncThreads;
