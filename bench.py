@@ -6,9 +6,10 @@ Workload: the decode hot path over Llama-3-8B-shaped layers
 batch 1 by default, synthetic seeded data. One step =
   G_E of the next-token logits (128256 wide)                 (signal)
   three layers, at levels 2, 4 and 6, each:
-    online AutoFP encode of each linear input (amax, NVFP4, 6-bit refinement)
-    AutoFP GEMV against the packed weight
-    L_A of the layer update and the device-side policy update (one call)
+    AutoFP GEMV against the packed weight, four per layer
+    each output turned into the next input by one producer-epilogue call
+    (copy / residual add + RMSNorm / SwiGLU, then the AutoFP encode); the
+    layer's last one also takes L_A and the device-side policy update
 Layers rotate through a pool larger than the 256 MB Infinity Cache, so the
 weights stream from HBM. Everything is captured once per pool position in a
 HIP graph and replayed.
@@ -247,7 +248,8 @@ class DecodeBench:
         then the encode): G_E, then per layer GEMV Wqkv -> copy of the first
         4096 outputs -> GEMV Wo -> h1 = h + o, RMSNorm(h1) encoded -> GEMV
         Wgate|Wup -> silu(g) * u -> GEMV Wdown -> h2 = h1 + d, RMSNorm(h2)
-        encoded for the next layer -> L_A(h, h2) and the policy update."""
+        encoded for the next layer, with L_A(h, h2) and the policy update in
+        the same call (autofp_layer_epilogue)."""
         A, p = self.A, self.p
         A.policy_signals(logits=self.logits, out_entropy=self.g_e, params=p, workspace=self.sws)
         layers = self.layers_of(s)
@@ -269,10 +271,9 @@ class DecodeBench:
             A.epilogue_quantize("swiglu", self.z["wgateup"], self.xq["wdown"], refine=True,
                                 exclude_mask=layer["wdown"].mask, workspace=self.qws[14336], params=p)
             g("wdown", 14336)
-            A.epilogue_quantize("residual_rmsnorm", self.z["wdown"], self.xq["wqkv"], residual=self.h1, v_out=h_out,
-                                refine=True, exclude_mask=nxt["wqkv"].mask, workspace=self.qws[4096], params=p)
-            A.policy_layer(1, j, h_in, h_out, self.state, g_e=self.g_e, l_a=self.l_a,
-                           bits_rows=self.bits_rows, bits_layer=self.bits_layer, params=p)
+            A.layer_epilogue(self.z["wdown"], self.xq["wqkv"], self.h1, h_out, h_in, 1, j, self.state, g_e=self.g_e,
+                             l_a=self.l_a, bits_rows=self.bits_rows, bits_layer=self.bits_layer, refine=True,
+                             exclude_mask=nxt["wqkv"].mask, workspace=self.qws[4096], params=p)
             h_in = h_out
 
     def step_unfused(self, s):
@@ -354,8 +355,8 @@ class Step32:
     h2 = h1 + Wdown f, each linear's output turned into the next linear's
     encoded input by one producer-epilogue call (the residual adds with the
     following RMSNorm, unit gain, so the hidden state stays finite over 32
-    layers of random weights), then L_A(h, h2) and the policy update, whose level
-    the next layer's GEMVs read on the device. Several consecutive steps
+    layers of random weights), the last with L_A(h, h2) and the policy update,
+    whose level the next layer's GEMVs read on the device. Several consecutive steps
     (logits drawn per step) form one HIP graph; the levels chosen are logged
     on the device and read back after timing."""
 
@@ -410,11 +411,10 @@ class Step32:
                 A.epilogue_quantize("swiglu", self.y["wgateup"], self.xq["wdown"], refine=True,
                                     exclude_mask=w["wdown"].mask, workspace=self.qws[self.F])
                 A.gemv(w["wdown"], self.xq["wdown"], bits_dev=bits, out=self.y["wdown"], workspace=self.gws[self.F])
-                A.epilogue_quantize("residual_rmsnorm", self.y["wdown"], self.xq["wqkv"], residual=self.h1,
-                                    v_out=h_out, refine=True, exclude_mask=nxt["wqkv"].mask,
-                                    workspace=self.qws[self.H])
-                A.policy_layer(1, i, h_in, h_out, self.state, g_e=self.g_e, new_sequence=(s == 0 and i == 0),
-                               l_a=self.l_a, bits_rows=self.rows, bits_layer=lay[i + 1:i + 2])
+                A.layer_epilogue(self.y["wdown"], self.xq["wqkv"], self.h1, h_out, h_in, 1, i, self.state,
+                                 g_e=self.g_e, new_sequence=(s == 0 and i == 0), l_a=self.l_a, bits_rows=self.rows,
+                                 bits_layer=lay[i + 1:i + 2], refine=True, exclude_mask=nxt["wqkv"].mask,
+                                 workspace=self.qws[self.H])
                 h_in = h_out
 
     def bytes_of(self, lay):
@@ -919,8 +919,8 @@ def main():
             "workload": "AutoFP decode step over Llama-3-8B-shaped layers (Wqkv 6144x4096, Wo 4096x4096, "
                         "Wgate|Wup 28672x4096, Wdown 4096x14336): G_E over 128256 logits, then 3 chained layers "
                         "at levels 2/4/6, each: 4 GEMVs, each output post-processed into the next input by one "
-                        "producer-epilogue call (copy / residual add + RMSNorm / SwiGLU + AutoFP encode), L_A and the policy "
-                        "update",
+                        "producer-epilogue call (copy / residual add + RMSNorm / SwiGLU + AutoFP encode), the last "
+                        "one with L_A and the policy update",
             "batch": args.batch,
             "pool_layers": args.pool_layers,
             "pool_bytes": int(pool_bytes),

@@ -322,6 +322,35 @@ autofp_status autofp_epilogue_quantize(int32_t op, const float *z, int64_t ldz, 
                                        size_t workspace_bytes, void *stream);
 
 /*
+ * The last producer epilogue of a decoder layer together with the layer's
+ * policy step ([AE] §6.4, the post-processing unit forming the next layer's
+ * input; §3.1, Eq. 1 and Table 1, the runtime policy at the layer boundary):
+ * autofp_epilogue_quantize(AUTOFP_EPI_RESIDUAL_RMSNORM, z, ldz, residual,
+ * v_out, refine, exclude_mask, p, out, ...) followed by
+ * autofp_policy_layer(phase, layer, new_sequence, h_prev, v_out, AUTOFP_F32,
+ * out->k, g_e, out->rows, p, state, l_a_out, bits_rows, bits_layer, ...).
+ * The same results: v_out (the new hidden state u = residual + z) and the
+ * encoded bytes bit for bit; L_A per row from fp64 sums of the exact
+ * differences and squares, equal to autofp_policy_layer's up to the order of
+ * the fp64 additions; the levels, bits_layer and state as the Table 1 step
+ * with that L_A. One launch for out->rows * out->k <= 16384 elements; above,
+ * the epilogue's launches and then the policy's.
+ * z [rows][ldz], residual, v_out (required) and h_prev (the layer's input
+ * hidden state) [rows][k], all fp32, 16-byte aligned; v_out must not overlap
+ * z, residual or h_prev (equal pointers are rejected). The policy arguments
+ * as autofp_policy_layer (g_e [rows] fp32, state [rows], l_a_out [rows] fp32,
+ * bits_rows [rows] int32, bits_layer [1] or NULL). Workspace
+ * autofp_workspace_bytes(AUTOFP_OP_EPILOGUE, rows, k).
+ * Errors: NULL, SHAPE, KIND, ARG, WORKSPACE, MISSING_REFINEMENT, HIP.
+ */
+autofp_status autofp_layer_epilogue(const float *z, int64_t ldz, const float *residual, float *v_out,
+                                    const float *h_prev, int32_t refine, const uint8_t *exclude_mask,
+                                    int32_t phase, int32_t layer, int32_t new_sequence, const float *g_e,
+                                    const autofp_params *p, autofp_policy_state *state, float *l_a_out,
+                                    int32_t *bits_rows, int32_t *bits_layer, autofp_packed *out,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * autofp_quantize for callers that cannot allocate memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same arguments, checks and results, but no workspace argument. Its scratch

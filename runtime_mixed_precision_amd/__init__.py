@@ -234,6 +234,40 @@ def epilogue_quantize(op, z: torch.Tensor, out: AutoFPTensor, residual=None, v_o
     return out
 
 
+def layer_epilogue(z: torch.Tensor, out: AutoFPTensor, residual, v_out, h_prev, phase, layer, state,
+                   g_e=None, new_sequence=False, l_a=None, bits_rows=None, bits_layer=None, refine=False,
+                   exclude_mask=None, workspace=None, params=None, stream=None):
+    """autofp_layer_epilogue: the layer's last producer epilogue (residual add
+    into ``v_out``, its RMSNorm encoded into ``out``) and the layer's policy
+    step (L_A from ``h_prev`` and the new hidden state, then Table 1) in one
+    call. Returns (l_a [rows] fp32, bits_rows [rows] int32, bits_layer [1]
+    int32). A given ``workspace`` holds workspace_bytes(OP_EPILOGUE, rows, k)."""
+    _dev_check(residual, v_out, h_prev, g_e, state, exclude_mask)
+    if z.dtype != torch.float32 or z.dim() != 2 or z.stride(1) != 1 or z.shape[0] != out.rows:
+        raise ValueError("z must be a 2-D float32 tensor with unit column stride and out.rows rows")
+    for t in (residual, v_out, h_prev):
+        if t is None or t.dtype != torch.float32 or tuple(t.shape) != (out.rows, out.k) or not t.is_contiguous():
+            raise ValueError("residual, v_out and h_prev must be contiguous float32 [rows, k] tensors")
+    dev = z.device
+    if l_a is None:
+        l_a = torch.empty(out.rows, dtype=torch.float32, device=dev)
+    if bits_rows is None:
+        bits_rows = torch.empty(out.rows, dtype=torch.int32, device=dev)
+    if bits_layer is None:
+        bits_layer = torch.empty(1, dtype=torch.int32, device=dev)
+    p = params or default_params()
+    if workspace is None:
+        workspace = _workspace(N.OP_EPILOGUE, out.rows, out.k, dev)
+    st = out.struct()
+    N.check(N.lib().autofp_layer_epilogue(_ptr(z), z.stride(0), _ptr(residual), _ptr(v_out), _ptr(h_prev),
+                                          int(bool(refine)), _ptr(exclude_mask), int(phase), int(layer),
+                                          int(bool(new_sequence)), _ptr(g_e), C.byref(p), _ptr(state), _ptr(l_a),
+                                          _ptr(bits_rows), _ptr(bits_layer), C.byref(st), _ptr(workspace),
+                                          workspace.numel(), _stream(stream)),
+            "autofp_layer_epilogue")
+    return l_a, bits_rows, bits_layer
+
+
 def quantize_noalloc(x: torch.Tensor, out: AutoFPTensor, refine=False, exclude_mask=None, params=None,
                      stream=None) -> AutoFPTensor:
     """autofp_quantize_noalloc into preallocated buffers: no workspace, the

@@ -31,7 +31,8 @@ FORMATS = {"autofp6": FMT_AUTOFP6, "autofp6e": FMT_AUTOFP6E, "autofp8": FMT_AUTO
 EXPORTS = (
     "autofp_default_params", "autofp_status_string", "autofp_packed_bytes",
     "autofp_weight_refined_count", "autofp_workspace_bytes", "autofp_select_weight_mask",
-    "autofp_quantize", "autofp_quantize_noalloc", "autofp_gptq_quantize", "autofp_epilogue_quantize", "autofp_gemv", "autofp_gemv_rows", "autofp_gemm", "autofp_policy_signals",
+    "autofp_quantize", "autofp_quantize_noalloc", "autofp_gptq_quantize", "autofp_epilogue_quantize",
+    "autofp_layer_epilogue", "autofp_gemv", "autofp_gemv_rows", "autofp_gemm", "autofp_policy_signals",
     "autofp_policy_update", "autofp_policy_layer", "autofp_kv_write", "autofp_kv_attention",
 )
 
@@ -108,6 +109,9 @@ def lib():
         "autofp_gptq_quantize": (C.c_int, [vp, C.c_int64, C.c_int64, vp, vp, P(Params), P(Packed), vp, C.c_size_t, vp]),
         "autofp_epilogue_quantize": (C.c_int, [C.c_int32, vp, C.c_int64, vp, vp, C.c_int32, vp, P(Params),
                                                P(Packed), vp, C.c_size_t, vp]),
+        "autofp_layer_epilogue": (C.c_int, [vp, C.c_int64, vp, vp, vp, C.c_int32, vp, C.c_int32, C.c_int32,
+                                            C.c_int32, vp, P(Params), vp, vp, vp, vp, P(Packed), vp,
+                                            C.c_size_t, vp]),
         "autofp_gemv": (C.c_int, [P(Packed), P(Packed), C.c_int32, vp, vp, C.c_int32, P(Params), vp,
                                   C.c_size_t, vp]),
         "autofp_gemv_rows": (C.c_int, [P(Packed), P(Packed), vp, vp, C.c_int32, P(Params), vp, C.c_size_t, vp]),

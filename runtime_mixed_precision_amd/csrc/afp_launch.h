@@ -27,6 +27,24 @@ int amax_partial_count(int64_t n);
 // subgroups in bytes [0, i); prefix has nbytes + 1 entries.
 hipError_t launch_mask_prefix(const uint8_t *mask, int64_t nbytes, int32_t *prefix, hipStream_t s);
 
+// Arguments of the policy step (signals.hip; also the fused tail of the
+// RESIDUAL_RMSNORM epilogue in encode.hip).
+struct PolicyArgs {
+  int phase, layer, new_sequence;
+  const float *l_a, *g_e;
+  int64_t batch;
+  double tau, lambda_d;
+  int alpha, beta, n_p;
+  autofp_policy_state *state;
+  int32_t *bits_rows, *bits_layer;
+  // launch_policy_layer: L_A computed from the hidden states into l_a_out
+  const void *h_prev, *h_cur;
+  int h_dtype;
+  int64_t hidden;
+  float eps;
+  float *l_a_out;
+};
+
 struct EncodeArgs {
   const void *x;
   int dtype;
@@ -57,6 +75,11 @@ struct EncodeArgs {
   const float *resid;           // [rows][k] (residual ops)
   float *v_out;                 // [rows][k] or null (RESIDUAL_RMSNORM: the residual sum u)
   float *rowscale;              // RESIDUAL_RMSNORM, large tensors: the per-row scales c [rows]
+  // RESIDUAL_RMSNORM of small tensors with policy != 0: the layer's policy
+  // step in the same launch (L_A of each row from pol.h_prev and the residual
+  // sum, then the Table 1 update; pol.h_cur is not read)
+  int policy;
+  PolicyArgs pol;
 };
 // Small tensors (encode_is_small: rows * roundup(k/4, 64) <= 4096) are
 // encoded in one launch that takes the amax itself (a.partial is not read);
@@ -147,21 +170,6 @@ int64_t entropy_slices(int64_t vocab);                        // vocabulary slic
 size_t entropy_workspace_bytes(int64_t batch, int64_t vocab);  // per-slice candidates / partials
 hipError_t launch_entropy(const float *logits, int64_t batch, int64_t vocab, int top_k,
                           float *out, void *workspace, hipStream_t s);
-struct PolicyArgs {
-  int phase, layer, new_sequence;
-  const float *l_a, *g_e;
-  int64_t batch;
-  double tau, lambda_d;
-  int alpha, beta, n_p;
-  autofp_policy_state *state;
-  int32_t *bits_rows, *bits_layer;
-  // launch_policy_layer: L_A computed from the hidden states into l_a_out
-  const void *h_prev, *h_cur;
-  int h_dtype;
-  int64_t hidden;
-  float eps;
-  float *l_a_out;
-};
 hipError_t launch_policy_update(const PolicyArgs &a, hipStream_t s);
 hipError_t launch_policy_layer(const PolicyArgs &a, hipStream_t s);
 hipError_t launch_update_norm(const void *h_prev, const void *h_cur, int dtype, int64_t batch,

@@ -240,6 +240,8 @@ EncodeArgs encode_args(const void *x, int32_t x_dtype, int32_t refine, const uin
     a.resid = epi->resid;
     a.v_out = epi->v_out;
     a.rowscale = epi->rowscale;
+    a.policy = epi->policy;
+    a.pol = epi->pol;
   }
   a.rows = out->rows;
   a.k = out->k;
@@ -503,6 +505,67 @@ autofp_status autofp_epilogue_quantize(int32_t op, const float *z, int64_t ldz, 
                      ? (float *)((char *)workspace + ws_quantize(out->rows, out->k))
                      : nullptr;
   return launch_quantize(z, AUTOFP_F32, refine, exclude_mask, p, out, workspace, (hipStream_t)stream, &epi);
+}
+
+autofp_status autofp_layer_epilogue(const float *z, int64_t ldz, const float *residual, float *v_out,
+                                    const float *h_prev, int32_t refine, const uint8_t *exclude_mask,
+                                    int32_t phase, int32_t layer, int32_t new_sequence, const float *g_e,
+                                    const autofp_params *p, autofp_policy_state *state, float *l_a_out,
+                                    int32_t *bits_rows, int32_t *bits_layer, autofp_packed *out,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+  if (!z || !residual || !v_out || !h_prev || !l_a_out || !state || !bits_rows) return AUTOFP_ERR_NULL;
+  const autofp_params pp = params_or_default(p);
+  if (phase != 0 && phase != 1) return AUTOFP_ERR_ARG;
+  if (phase == 1 && !g_e) return AUTOFP_ERR_NULL;
+  if (layer < 0 || pp.alpha < 1 || pp.beta < 1 || pp.n_p < 1 ||
+      !(pp.lambda_d >= 0.0 && pp.lambda_d <= 1.0) || !(pp.eps >= 0.0f))
+    return AUTOFP_ERR_ARG;
+  // the checks of autofp_epilogue_quantize with RESIDUAL_RMSNORM
+  const autofp_status st = check_quantize(z, AUTOFP_F32, refine, exclude_mask, out);
+  if (st != AUTOFP_OK) return st;
+  if (out->kind != AUTOFP_ACTIVATION) return AUTOFP_ERR_KIND;
+  if (ldz < out->k || (ldz & 3) != 0) return AUTOFP_ERR_SHAPE;
+  if (!aligned16(residual) || !aligned16(v_out) || !aligned16(h_prev)) return AUTOFP_ERR_ARG;
+  if ((const void *)h_prev == (const void *)v_out || (const void *)residual == (const void *)v_out)
+    return AUTOFP_ERR_ARG;
+  if (!workspace || workspace_bytes < ws_epilogue(out->rows, out->k)) return AUTOFP_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return AUTOFP_ERR_ARG;
+  PolicyArgs pa{};
+  pa.phase = phase;
+  pa.layer = layer;
+  pa.new_sequence = new_sequence;
+  pa.g_e = g_e;
+  pa.batch = out->rows;
+  pa.tau = pp.tau;
+  pa.lambda_d = pp.lambda_d;
+  pa.alpha = pp.alpha;
+  pa.beta = pp.beta;
+  pa.n_p = pp.n_p;
+  pa.state = state;
+  pa.bits_rows = bits_rows;
+  pa.bits_layer = bits_layer;
+  pa.h_prev = h_prev;
+  pa.h_cur = v_out;
+  pa.h_dtype = AUTOFP_F32;
+  pa.hidden = out->k;
+  pa.eps = pp.eps;
+  pa.l_a_out = l_a_out;
+  EncodeArgs epi{};
+  epi.op = AUTOFP_EPI_RESIDUAL_RMSNORM;
+  epi.z = z;
+  epi.ldz = ldz;
+  epi.resid = residual;
+  epi.v_out = v_out;
+  epi.rowscale = (float *)((char *)workspace + ws_quantize(out->rows, out->k));
+  hipStream_t s = (hipStream_t)stream;
+  if (encode_is_small(out->rows, out->k)) {
+    epi.policy = 1;
+    epi.pol = pa;
+    return launch_quantize(z, AUTOFP_F32, refine, exclude_mask, p, out, workspace, s, &epi);
+  }
+  const autofp_status e = launch_quantize(z, AUTOFP_F32, refine, exclude_mask, p, out, workspace, s, &epi);
+  if (e != AUTOFP_OK) return e;
+  return from_hip(launch_policy_layer(pa, s));
 }
 
 autofp_status autofp_quantize_noalloc(const void *x, int32_t x_dtype, int32_t refine,

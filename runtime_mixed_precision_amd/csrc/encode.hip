@@ -17,6 +17,7 @@
 
 #include "afp_device.h"
 #include "afp_encode.h"
+#include "afp_policy.h"
 #include "afp_launch.h"
 
 namespace afp {
@@ -291,8 +292,9 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(EncodeArgs a) {
 constexpr int kSmallSlots = 4096;
 
 // The raw inputs of the four elements of subgroup s of row `row`: p = x (SRC
-// 0 fp32, 1 bf16) or z (the epilogue ops, SRC = 1 + op); q = the residual
-// (residual ops) or the up half z[k + j] (SwiGLU). Loads only.
+// 0 fp32, 1 bf16) or z (the epilogue ops, SRC = 1 + op; 6: RESIDUAL_RMSNORM
+// with the layer's policy step); q = the residual (residual ops) or the up
+// half z[k + j] (SwiGLU). Loads only.
 template <int SRC>
 __device__ __forceinline__ void src_load(const EncodeArgs &a, int32_t row, int32_t s, float4 &p, float4 &q) {
   if constexpr (SRC == 0) {
@@ -303,7 +305,7 @@ __device__ __forceinline__ void src_load(const EncodeArgs &a, int32_t row, int32
                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
   } else {
     p = *(const float4 *)(a.z + (int64_t)row * a.ldz + 4 * s);
-    if constexpr (SRC == 1 + AUTOFP_EPI_RESIDUAL || SRC == 1 + AUTOFP_EPI_RESIDUAL_RMSNORM)
+    if constexpr (SRC == 1 + AUTOFP_EPI_RESIDUAL || SRC >= 1 + AUTOFP_EPI_RESIDUAL_RMSNORM)
       q = *(const float4 *)(a.resid + (int64_t)row * a.k + 4 * s);
     else if constexpr (SRC == 1 + AUTOFP_EPI_SWIGLU)
       q = *(const float4 *)(a.z + (int64_t)row * a.ldz + a.k + 4 * s);
@@ -316,7 +318,7 @@ __device__ __forceinline__ void src_load(const EncodeArgs &a, int32_t row, int32
 template <int SRC>
 __device__ __forceinline__ float4 src_value(float4 p, float4 q) {
 #pragma clang fp contract(off)
-  if constexpr (SRC == 1 + AUTOFP_EPI_RESIDUAL || SRC == 1 + AUTOFP_EPI_RESIDUAL_RMSNORM) {
+  if constexpr (SRC == 1 + AUTOFP_EPI_RESIDUAL || SRC >= 1 + AUTOFP_EPI_RESIDUAL_RMSNORM) {
     return make_float4(q.x + p.x, q.y + p.y, q.z + p.z, q.w + p.w);
   } else if constexpr (SRC == 1 + AUTOFP_EPI_SWIGLU) {
     return make_float4(silu_f32(p.x) * q.x, silu_f32(p.y) * q.y, silu_f32(p.z) * q.z, silu_f32(p.w) * q.w);
@@ -328,7 +330,8 @@ __device__ __forceinline__ float4 src_value(float4 p, float4 q) {
 template <int TPB, int SPT, int SRC>
 __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t nqp) {
   static_assert((SPT & (SPT - 1)) == 0 && TPB * SPT <= kSmallSlots, "slot groups per thread: a power of two");
-  constexpr bool NORM = SRC == 1 + AUTOFP_EPI_RESIDUAL_RMSNORM;
+  constexpr bool NORM = SRC >= 1 + AUTOFP_EPI_RESIDUAL_RMSNORM;
+  constexpr bool POL = SRC == 2 + AUTOFP_EPI_RESIDUAL_RMSNORM;   // with the policy step (block 0)
   const int32_t nq = (int32_t)(a.k / 4);
   const int32_t tot = (int32_t)a.rows * nqp;
   const int bx = (int)blockIdx.x;
@@ -361,6 +364,20 @@ __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t
     wb = a.w_mask[sl >> 3];
     wp = a.w_prefix[sl >> 3];
   }
+  // POL: block 0 (which holds every slot) also reads the layer's input
+  // hidden state for L_A
+  float4 hp[POL ? SPT : 1];
+  if constexpr (POL) {
+    if (bx == 0) {
+#pragma unroll
+      for (int j = 0; j < SPT; ++j) {
+        const int32_t uj = j * TPB + (int32_t)threadIdx.x;
+        const int32_t r = row_of(uj), sq = uj - r * nqp;
+        const bool ok = uj < tot && sq < nq;
+        hp[j] = *(const float4 *)((const float *)a.pol.h_prev + (int64_t)(ok ? r : 0) * a.k + 4 * (ok ? sq : 0));
+      }
+    }
+  }
 
   float m = 0.0f;
   float4 own = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -371,6 +388,10 @@ __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t
     // then per row the chunk sums in order and c = 1 / sqrt(sum / k + eps)
     __shared__ double chunk[kSmallSlots / 64];
     __shared__ float rsc[kSmallSlots / 64];   // at most 64 rows: nqp >= 64
+    // POL: per chunk the fp64 sums of (u - h_prev)^2 and h_prev^2 (Eq. 1;
+    // differences and squares exact in fp64), the same fixed order
+    __shared__ double cnum[POL ? kSmallSlots / 64 : 1], cden[POL ? kSmallSlots / 64 : 1];
+    __shared__ float la_s[POL ? kSmallSlots / 64 : 1];
     float4 uu[SPT];
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
@@ -385,14 +406,64 @@ __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t
       d = wave_sum_d_dpp(d);
       if ((threadIdx.x & 63) == 0 && uj < tot) chunk[uj / 64] = d;
     }
+    if constexpr (POL) {
+      if (bx == 0) {
+        // block 0's slot groups are in the order j (bx = 0: no rotation)
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+          const int32_t uj = j * TPB + (int32_t)threadIdx.x;
+          const int32_t r = row_of(uj), sq = uj - r * nqp;
+          const bool ok = uj < tot && sq < nq;
+          const float4 h = ok ? hp[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+          const float c[4] = {uu[j].x, uu[j].y, uu[j].z, uu[j].w};
+          const float pv[4] = {h.x, h.y, h.z, h.w};
+          double nm = 0.0, dn = 0.0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const double df = (double)c[e] - (double)pv[e];
+            nm += df * df;
+            dn += (double)pv[e] * (double)pv[e];
+          }
+          nm = wave_sum_d_dpp(nm);
+          dn = wave_sum_d_dpp(dn);
+          if ((threadIdx.x & 63) == 0 && uj < tot) {
+            cnum[uj / 64] = nm;
+            cden[uj / 64] = dn;
+          }
+        }
+      }
+    }
     __syncthreads();
     const int32_t cpr = nqp / 64;   // chunks per row
     if ((int32_t)threadIdx.x < (int32_t)a.rows) {
       double t = 0.0;
       for (int32_t c = 0; c < cpr; ++c) t += chunk[(int32_t)threadIdx.x * cpr + c];
       rsc[threadIdx.x] = (float)(1.0 / sqrt(t / (double)a.k + kRmsEps));
+      if constexpr (POL) {
+        if (bx == 0) {
+          double n = 0.0, dd = 0.0;
+          for (int32_t c = 0; c < cpr; ++c) {
+            n += cnum[(int32_t)threadIdx.x * cpr + c];
+            dd += cden[(int32_t)threadIdx.x * cpr + c];
+          }
+          const float la = (float)(sqrt(n) / (sqrt(dd) + (double)a.pol.eps));
+          la_s[threadIdx.x] = la;
+          a.pol.l_a_out[threadIdx.x] = la;
+        }
+      }
     }
     __syncthreads();
+    if constexpr (POL) {
+      // the Table 1 step of every row in order, the highest level -> bits_layer
+      if (bx == 0 && threadIdx.x == 0) {
+        int mx = 0;
+        for (int64_t b = 0; b < a.rows; ++b) {
+          const int lv = policy_row(a.pol, b, (double)la_s[b]);
+          mx = lv > mx ? lv : mx;
+        }
+        if (a.pol.bits_layer) *a.pol.bits_layer = mx;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
       const int32_t uj = ((bx + j) & (SPT - 1)) * TPB + (int32_t)threadIdx.x;
@@ -659,7 +730,7 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t s) {
       case 2: return launch_small<256, 2>(a, (int32_t)nqp, s);
       case 3: return launch_small<256, 3>(a, (int32_t)nqp, s);
       case 4: return launch_small<512, 4>(a, (int32_t)nqp, s);
-      case 5: return launch_small<256, 5>(a, (int32_t)nqp, s);
+      case 5: return a.policy ? launch_small<256, 6>(a, (int32_t)nqp, s) : launch_small<256, 5>(a, (int32_t)nqp, s);
       default: return hipErrorInvalidValue;
     }
   }

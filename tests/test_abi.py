@@ -351,3 +351,32 @@ def test_epilogue_rejects_bad_arguments_and_sizes_its_workspace(N):
     assert e(N.EPI_RESIDUAL, None, k, big) == 1
     assert e(N.EPI_RESIDUAL_RMSNORM, FAKE, k - 4, big) == 2         # ldz < k
     assert e(N.EPI_RESIDUAL_RMSNORM, FAKE, k, wq.value) == 5        # the encode's workspace is short
+
+
+def test_layer_epilogue_rejects_bad_arguments(N):
+    """autofp_layer_epilogue's checks (no launch is reached): the required
+    pointers, the policy arguments (phase, decode without g_e), v_out equal to
+    h_prev or to the residual, z narrower than k, a workspace of the
+    encode's size (AUTOFP_OP_EPILOGUE needs one more fp32 per row)."""
+    L = N.lib()
+    p = params(N)
+    rows, k = 2, 64
+    wq, we = C.c_size_t(), C.c_size_t()
+    assert L.autofp_workspace_bytes(N.OP_QUANTIZE, rows, k, C.byref(wq)) == 0
+    assert L.autofp_workspace_bytes(N.OP_EPILOGUE, rows, k, C.byref(we)) == 0
+    out = packed(N, N.ACTIVATION, rows=rows, k=k)
+    F2, F3, F4 = FAKE + 4096, FAKE + 8192, FAKE + 12288
+
+    def e(z=FAKE, ldz=k, resid=F2, v_out=F3, h_prev=F4, phase=1, g_e=FAKE, state=FAKE, l_a=FAKE, bits=FAKE,
+          wsz=None):
+        return L.autofp_layer_epilogue(z, ldz, resid, v_out, h_prev, 0, None, phase, 0, 0, g_e, C.byref(p),
+                                       state, l_a, bits, None, C.byref(out), FAKE,
+                                       we.value if wsz is None else wsz, None)
+    for kw in ("z", "resid", "v_out", "h_prev", "state", "l_a", "bits"):
+        assert e(**{kw: None}) == 1, kw                    # AUTOFP_ERR_NULL
+    assert e(g_e=None) == 1                                # decode needs G_E
+    assert e(phase=2) == 8                                 # AUTOFP_ERR_ARG
+    assert e(v_out=F4) == 8                                # v_out is h_prev
+    assert e(v_out=F2) == 8                                # v_out is the residual
+    assert e(ldz=k - 4) == 2                               # AUTOFP_ERR_SHAPE
+    assert e(wsz=wq.value) == 5                            # AUTOFP_ERR_WORKSPACE

@@ -9,7 +9,11 @@ next layer's activation ([AE] §6.4).
   - the packed output bit for bit against the oracle's encode of that same v
     (the encode of a given fp32 tensor is exact), at 1 token (one launch), 4
     and 64 tokens, with and without refinement and an exclusion mask;
-  - and against autofp_quantize of v, byte for byte.
+  - and against autofp_quantize of v, byte for byte;
+  - autofp_layer_epilogue (the residual RMSNorm epilogue with the layer's L_A
+    and policy step in the same launch) against the epilogue followed by
+    autofp_policy_layer: hidden state, bytes, L_A, levels and state equal
+    over a sequence of layers and steps.
 """
 
 import sys
@@ -129,3 +133,47 @@ def test_epilogue_residual_rmsnorm(rows, k, refine):
     A.epilogue_quantize("residual_rmsnorm", z, out2, residual=resid, refine=refine, exclude_mask=ex)
     torch.cuda.synchronize()
     assert torch.equal(out2.codes, out.codes) and torch.equal(out2.tensor_scale, out.tensor_scale)
+
+
+@pytest.mark.parametrize("rows,k", [(1, 4096), (4, 4096), (3, 1024), (16, 4096)])
+@pytest.mark.parametrize("phase", [1, 0])
+def test_layer_epilogue_equals_epilogue_then_policy_layer(rows, k, phase):
+    """autofp_layer_epilogue (the residual RMSNorm epilogue with the layer's
+    L_A and Table 1 step fused: one launch up to 16384 elements, the two
+    calls above) against autofp_epilogue_quantize("residual_rmsnorm")
+    followed by autofp_policy_layer, over 3 steps x 6 layers of a sequence
+    with two policy states evolving side by side: v_out and the encoded bytes
+    bit for bit, L_A, the levels, the layer maximum and the whole state equal
+    after every layer. The update sizes vary by layer and step so the trend
+    counters move both ways; G_E straddles tau = 0.1 in decode."""
+    say(f"case: layer epilogue rows={rows} k={k} phase={phase}")
+    wm, _ = A.select_weight_mask(S.weights(64, k, seed=5, tensor_id=3, device=DEV))
+    st_a, st_b = A.policy_state(rows, DEV), A.policy_state(rows, DEV)
+    ws_a = torch.empty(A.workspace_bytes(A.N.OP_EPILOGUE, rows, k), dtype=torch.uint8, device=DEV)
+    ws_b = torch.empty_like(ws_a)
+    h_prev = S.hidden(rows, k, seed=11, tensor_id=0, device=DEV)
+    for step in range(3):
+        g_e = torch.tensor([0.05 + 0.1 * ((r + step) % 3) for r in range(rows)], dtype=torch.float32, device=DEV)
+        for layer in range(6):
+            scale = 0.02 * (1 + ((layer * 7 + step * 3) % 5))
+            z = S.hidden(rows, k + 64, seed=100 * step + layer, tensor_id=1, device=DEV) * scale
+            resid = (h_prev + S.hidden(rows, k, seed=100 * step + layer, tensor_id=2, device=DEV) * scale).contiguous()
+            out_a = A.alloc_activation(rows, k, refine=True, device=DEV)
+            out_b = A.alloc_activation(rows, k, refine=True, device=DEV)
+            v_a = torch.empty(rows, k, dtype=torch.float32, device=DEV)
+            v_b = torch.empty_like(v_a)
+            new_seq = step == 0 and layer == 0
+            ge = g_e if phase == 1 else None
+            A.epilogue_quantize("residual_rmsnorm", z, out_a, residual=resid, v_out=v_a, refine=True,
+                                exclude_mask=wm, workspace=ws_a)
+            la_a, br_a, bl_a = A.policy_layer(phase, layer, h_prev, v_a, st_a, g_e=ge, new_sequence=new_seq)
+            la_b, br_b, bl_b = A.layer_epilogue(z, out_b, resid, v_b, h_prev, phase, layer, st_b, g_e=ge,
+                                                new_sequence=new_seq, refine=True, exclude_mask=wm, workspace=ws_b)
+            torch.cuda.synchronize()
+            assert torch.equal(v_a, v_b)
+            for key in ("codes", "scales", "tensor_scale", "mask", "offsets"):
+                assert torch.equal(getattr(out_a, key), getattr(out_b, key)), key
+            assert torch.equal(la_a, la_b), (step, layer, la_a, la_b)
+            assert torch.equal(br_a, br_b) and torch.equal(bl_a, bl_b), (step, layer)
+            assert torch.equal(st_a, st_b), (step, layer)
+            h_prev = v_a.clone()
