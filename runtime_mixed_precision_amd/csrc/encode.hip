@@ -327,11 +327,82 @@ __device__ __forceinline__ float4 src_value(float4 p, float4 q) {
   }
 }
 
+// The layer's policy step beside the RESIDUAL_RMSNORM encode (one extra block
+// of the launch): the new hidden state u = resid + z (the same fp32 sums the
+// encode blocks write to v_out), per 64-slot chunk the fp64 sums of
+// (u - h_prev)^2 and h_prev^2 (Eq. 1; differences and squares exact in fp64,
+// lane order fixed by the butterfly), per row the chunks in order, L_A, then
+// the Table 1 step of every row in order with the highest level to
+// bits_layer.
+template <int TPB, int SPT>
+__device__ __forceinline__ void policy_tail(const EncodeArgs &a, int32_t nqp) {
+  __shared__ double cnum[kSmallSlots / 64], cden[kSmallSlots / 64];
+  __shared__ float la_s[kSmallSlots / 64];
+  const int32_t nq = (int32_t)(a.k / 4);
+  const int32_t tot = (int32_t)a.rows * nqp;
+  const float inv_nqp = 1.0f / (float)nqp;
+  float4 z[SPT], rr[SPT], hp[SPT];
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int32_t uj = j * TPB + (int32_t)threadIdx.x;
+    const int32_t r = (int32_t)(((float)uj + 0.5f) * inv_nqp), sq = uj - r * nqp;
+    const bool ok = uj < tot && sq < nq;
+    const int64_t e = (int64_t)(ok ? r : 0) * a.k + 4 * (ok ? sq : 0);
+    z[j] = *(const float4 *)(a.z + (int64_t)(ok ? r : 0) * a.ldz + 4 * (ok ? sq : 0));
+    rr[j] = *(const float4 *)(a.resid + e);
+    hp[j] = *(const float4 *)((const float *)a.pol.h_prev + e);
+  }
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+#pragma clang fp contract(off)
+    const int32_t uj = j * TPB + (int32_t)threadIdx.x;
+    const int32_t r = (int32_t)(((float)uj + 0.5f) * inv_nqp), sq = uj - r * nqp;
+    const bool ok = uj < tot && sq < nq;
+    const float c[4] = {rr[j].x + z[j].x, rr[j].y + z[j].y, rr[j].z + z[j].z, rr[j].w + z[j].w};
+    const float pv[4] = {hp[j].x, hp[j].y, hp[j].z, hp[j].w};
+    double nm = 0.0, dn = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double df = ok ? (double)c[e] - (double)pv[e] : 0.0;
+      const double pd = ok ? (double)pv[e] : 0.0;
+      nm += df * df;
+      dn += pd * pd;
+    }
+    nm = wave_sum_d_dpp(nm);
+    dn = wave_sum_d_dpp(dn);
+    if ((threadIdx.x & 63) == 0 && uj < tot) {
+      cnum[uj / 64] = nm;
+      cden[uj / 64] = dn;
+    }
+  }
+  __syncthreads();
+  const int32_t cpr = nqp / 64;
+  if ((int32_t)threadIdx.x < (int32_t)a.rows) {
+    double n = 0.0, d = 0.0;
+    for (int32_t c = 0; c < cpr; ++c) {
+      n += cnum[(int32_t)threadIdx.x * cpr + c];
+      d += cden[(int32_t)threadIdx.x * cpr + c];
+    }
+    const float la = (float)(sqrt(n) / (sqrt(d) + (double)a.pol.eps));
+    la_s[threadIdx.x] = la;
+    a.pol.l_a_out[threadIdx.x] = la;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int mx = 0;
+    for (int64_t b = 0; b < a.rows; ++b) {
+      const int lv = policy_row(a.pol, b, (double)la_s[b]);
+      mx = lv > mx ? lv : mx;
+    }
+    if (a.pol.bits_layer) *a.pol.bits_layer = mx;
+  }
+}
+
 template <int TPB, int SPT, int SRC>
 __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t nqp) {
   static_assert((SPT & (SPT - 1)) == 0 && TPB * SPT <= kSmallSlots, "slot groups per thread: a power of two");
   constexpr bool NORM = SRC >= 1 + AUTOFP_EPI_RESIDUAL_RMSNORM;
-  constexpr bool POL = SRC == 2 + AUTOFP_EPI_RESIDUAL_RMSNORM;   // with the policy step (block 0)
+  constexpr bool POL = SRC == 2 + AUTOFP_EPI_RESIDUAL_RMSNORM;   // with the policy step
   const int32_t nq = (int32_t)(a.k / 4);
   const int32_t tot = (int32_t)a.rows * nqp;
   const int bx = (int)blockIdx.x;
@@ -339,6 +410,13 @@ __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t
   const int32_t row = u / nqp, s = u - row * nqp;
   const bool live = u < tot && s < nq;
   const bool fp6g = a.fmt == AUTOFP_FMT_FP6G;
+  if constexpr (POL) {
+    // the last block runs the layer's policy step beside the encode blocks
+    if (bx == (int)gridDim.x - 1) {
+      policy_tail<TPB, SPT>(a, nqp);
+      return;
+    }
+  }
   // row of slot uj < 4096 without an integer division: (uj + 1/2) / nqp lies
   // at least 1/(2 nqp) >= 2^-13 (nqp <= 4096) inside its integer interval,
   // far above the rounding error of the fp32 product (at most 2^-17 for
@@ -364,21 +442,6 @@ __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t
     wb = a.w_mask[sl >> 3];
     wp = a.w_prefix[sl >> 3];
   }
-  // POL: block 0 (which holds every slot) also reads the layer's input
-  // hidden state for L_A
-  float4 hp[POL ? SPT : 1];
-  if constexpr (POL) {
-    if (bx == 0) {
-#pragma unroll
-      for (int j = 0; j < SPT; ++j) {
-        const int32_t uj = j * TPB + (int32_t)threadIdx.x;
-        const int32_t r = row_of(uj), sq = uj - r * nqp;
-        const bool ok = uj < tot && sq < nq;
-        hp[j] = *(const float4 *)((const float *)a.pol.h_prev + (int64_t)(ok ? r : 0) * a.k + 4 * (ok ? sq : 0));
-      }
-    }
-  }
-
   float m = 0.0f;
   float4 own = make_float4(0.f, 0.f, 0.f, 0.f);
   float4 own_u = own;   // RESIDUAL_RMSNORM: the residual sum of the own slot
@@ -388,10 +451,6 @@ __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t
     // then per row the chunk sums in order and c = 1 / sqrt(sum / k + eps)
     __shared__ double chunk[kSmallSlots / 64];
     __shared__ float rsc[kSmallSlots / 64];   // at most 64 rows: nqp >= 64
-    // POL: per chunk the fp64 sums of (u - h_prev)^2 and h_prev^2 (Eq. 1;
-    // differences and squares exact in fp64), the same fixed order
-    __shared__ double cnum[POL ? kSmallSlots / 64 : 1], cden[POL ? kSmallSlots / 64 : 1];
-    __shared__ float la_s[POL ? kSmallSlots / 64 : 1];
     float4 uu[SPT];
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
@@ -406,64 +465,14 @@ __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t
       d = wave_sum_d_dpp(d);
       if ((threadIdx.x & 63) == 0 && uj < tot) chunk[uj / 64] = d;
     }
-    if constexpr (POL) {
-      if (bx == 0) {
-        // block 0's slot groups are in the order j (bx = 0: no rotation)
-#pragma unroll
-        for (int j = 0; j < SPT; ++j) {
-          const int32_t uj = j * TPB + (int32_t)threadIdx.x;
-          const int32_t r = row_of(uj), sq = uj - r * nqp;
-          const bool ok = uj < tot && sq < nq;
-          const float4 h = ok ? hp[j] : make_float4(0.f, 0.f, 0.f, 0.f);
-          const float c[4] = {uu[j].x, uu[j].y, uu[j].z, uu[j].w};
-          const float pv[4] = {h.x, h.y, h.z, h.w};
-          double nm = 0.0, dn = 0.0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const double df = (double)c[e] - (double)pv[e];
-            nm += df * df;
-            dn += (double)pv[e] * (double)pv[e];
-          }
-          nm = wave_sum_d_dpp(nm);
-          dn = wave_sum_d_dpp(dn);
-          if ((threadIdx.x & 63) == 0 && uj < tot) {
-            cnum[uj / 64] = nm;
-            cden[uj / 64] = dn;
-          }
-        }
-      }
-    }
     __syncthreads();
     const int32_t cpr = nqp / 64;   // chunks per row
     if ((int32_t)threadIdx.x < (int32_t)a.rows) {
       double t = 0.0;
       for (int32_t c = 0; c < cpr; ++c) t += chunk[(int32_t)threadIdx.x * cpr + c];
       rsc[threadIdx.x] = (float)(1.0 / sqrt(t / (double)a.k + kRmsEps));
-      if constexpr (POL) {
-        if (bx == 0) {
-          double n = 0.0, dd = 0.0;
-          for (int32_t c = 0; c < cpr; ++c) {
-            n += cnum[(int32_t)threadIdx.x * cpr + c];
-            dd += cden[(int32_t)threadIdx.x * cpr + c];
-          }
-          const float la = (float)(sqrt(n) / (sqrt(dd) + (double)a.pol.eps));
-          la_s[threadIdx.x] = la;
-          a.pol.l_a_out[threadIdx.x] = la;
-        }
-      }
     }
     __syncthreads();
-    if constexpr (POL) {
-      // the Table 1 step of every row in order, the highest level -> bits_layer
-      if (bx == 0 && threadIdx.x == 0) {
-        int mx = 0;
-        for (int64_t b = 0; b < a.rows; ++b) {
-          const int lv = policy_row(a.pol, b, (double)la_s[b]);
-          mx = lv > mx ? lv : mx;
-        }
-        if (a.pol.bits_layer) *a.pol.bits_layer = mx;
-      }
-    }
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
       const int32_t uj = ((bx + j) & (SPT - 1)) * TPB + (int32_t)threadIdx.x;
@@ -698,9 +707,11 @@ hipError_t launch_mask_prefix(const uint8_t *mask, int64_t nbytes, int32_t *pref
 // up to a power of two
 template <int TPB, int SRC>
 hipError_t launch_small(const EncodeArgs &a, int32_t nqp, hipStream_t s) {
-  const int64_t gx = (a.rows * nqp + TPB - 1) / TPB;
+  const int64_t ge = (a.rows * nqp + TPB - 1) / TPB;   // encode blocks
   int spt = 1;
-  while (spt < gx) spt *= 2;
+  while (spt < ge) spt *= 2;
+  // with the policy step: one more block, beside the encode blocks
+  const int64_t gx = ge + (SRC == 2 + AUTOFP_EPI_RESIDUAL_RMSNORM ? 1 : 0);
 #define AFP_SMALL(P)                                                                               \
   case P:                                                                                          \
     if constexpr (TPB * P <= kSmallSlots)                                                          \
