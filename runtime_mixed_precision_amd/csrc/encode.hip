@@ -516,6 +516,194 @@ __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t
   }
 }
 
+// ---------------------------------------------------------------------------
+// Element-parallel one-launch encoder (AutoFP6 activations; every source but
+// SwiGLU): one thread per element instead of per four-element subgroup, so
+// each thread's encode is about a quarter of the work. The decisions a
+// subgroup or group shares come from DPP moves among its lanes (lanes 16g ..
+// 16g + 15 hold group g of a wavefront, four lanes a subgroup): the group
+// maximum, the subgroup's NMSE sums in element order, its offset byte and the
+// code byte of an element pair. Every block still loads every slot of the
+// tensor for the maximum (and the RMSNorm row sums); the own element is one
+// more load. Rows are padded to 4 nqp elements (a multiple of 256), so a
+// wavefront (64 consecutive elements of one row) holds 4 whole groups.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+// The raw inputs of element `col` of row `row` (src_load for one element).
+template <int SRC>
+__device__ __forceinline__ void src_load1(const EncodeArgs &a, int32_t row, int32_t col, float &p, float &q) {
+  if constexpr (SRC == 0) {
+    p = ((const float *)a.x)[(int64_t)row * a.k + col];
+  } else if constexpr (SRC == 1) {
+    p = __uint_as_float((uint32_t)((const uint16_t *)a.x)[(int64_t)row * a.k + col] << 16);
+  } else {
+    p = a.z[(int64_t)row * a.ldz + col];
+    if constexpr (SRC == 1 + AUTOFP_EPI_RESIDUAL || SRC >= 1 + AUTOFP_EPI_RESIDUAL_RMSNORM)
+      q = a.resid[(int64_t)row * a.k + col];
+  }
+}
+
+// encode_subgroup's arithmetic for the AutoFP6 format, one element per lane
+// (the same values and bytes): E2M1 code and E4M3 group scale; with
+// act_refine the subgroup's offsets and its refinement decision outside the
+// exclusion mask (exb: the mask byte of the lane's subgroup).
+__device__ __forceinline__ void encode_element(const EncodeArgs &a, float T, int32_t row, int32_t col, bool live,
+                                               float x, uint32_t exb) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  const int32_t k = (int32_t)a.k;
+  const float sixT = 6.0f * T;
+  // the group's maximum: quads, then the half rows and rows of 16 lanes
+  float gm = fabsf(x);
+  gm = fmaxf(gm, dppf<0xB1>(gm));
+  gm = fmaxf(gm, dppf<0x4E>(gm));
+  gm = fmaxf(gm, dppf<0x141>(gm));
+  gm = fmaxf(gm, dppf<0x140>(gm));
+  const float b = sixT > 0.0f ? gm / sixT : 0.0f;
+  const uint32_t B = e4m3_encode(b);
+  const float sc = T * e4m3_value(B);
+  const float v = (sc != 0.0f) ? x / sc : 0.0f;
+  const uint32_t q = e2m1_encode(v);
+  const uint32_t qn = dppu<0xF5>(q);   // the odd neighbour's code (quad lanes 1, 1, 3, 3)
+  if (live && !(col & 1)) a.codes[(int64_t)row * (k / 2) + (col >> 1)] = (uint8_t)(q | (qn << 4));
+  if (live && !(col & 15)) a.scales[(int64_t)row * (k / 16) + (col >> 4)] = (uint8_t)B;
+  if (!a.act_refine) return;
+  const float r = v - e2m1_value(q);
+  const uint32_t oc = offset_code(r);
+  const float rr = r * r;
+  const float vv = v * v;
+  // the subgroup's sums in element order, ((e0 + e1) + e2) + e3, in all 4 lanes
+  const float num = ((dppf<0x00>(rr) + dppf<0x55>(rr)) + dppf<0xAA>(rr)) + dppf<0xFF>(rr);
+  const float den = ((dppf<0x00>(vv) + dppf<0x55>(vv)) + dppf<0xAA>(vv)) + dppf<0xFF>(vv);
+  const uint32_t ob = dppu<0x00>(oc) | (dppu<0x55>(oc) << 2) | (dppu<0xAA>(oc) << 4) | (dppu<0xFF>(oc) << 6);
+  const uint32_t s = (uint32_t)col >> 2;
+  const bool ex = a.exclude_mask != nullptr && ((exb >> (s & 7)) & 1u);
+  const bool refine = live && den > 0.0f && num > a.thresh * den && !ex;
+  const uint64_t bits = __ballot(refine);
+  if (live && !(col & 3)) a.act_offsets[(int64_t)row * (k / 4) + s] = (uint8_t)(refine ? ob : 0u);
+  if (live && !(col & 31)) {
+    // 8 subgroups' bits (every fourth lane of the lane's half wavefront) -> one mask byte
+    uint32_t w = (uint32_t)(bits >> (lane & 32)) & 0x11111111u;
+    w = (w | (w >> 3)) & 0x03030303u;
+    w = (w | (w >> 6)) & 0x000F000Fu;
+    w = (w | (w >> 12)) & 0xFFu;
+    a.act_mask[(int64_t)row * ((k + 31) / 32) + (s >> 3)] = (uint8_t)w;
+  }
+}
+
+template <int TPB, int SPT, int SRC>
+__global__ __launch_bounds__(TPB) void encode_elem_kernel(EncodeArgs a, int32_t nqp) {
+  static_assert((SPT & (SPT - 1)) == 0 && TPB * SPT <= kSmallSlots, "slot groups per thread: a power of two");
+  static_assert(SRC != 1 + AUTOFP_EPI_SWIGLU, "SwiGLU keeps the per-subgroup kernel");
+  constexpr bool NORM = SRC >= 1 + AUTOFP_EPI_RESIDUAL_RMSNORM;
+  constexpr bool POL = SRC == 2 + AUTOFP_EPI_RESIDUAL_RMSNORM;
+  const int bx = (int)blockIdx.x;
+  if constexpr (POL) {
+    if (bx == (int)gridDim.x - 1) {
+      policy_tail<TPB, SPT>(a, nqp);
+      return;
+    }
+  }
+  const int32_t nq = (int32_t)(a.k / 4);
+  const int32_t tot = (int32_t)a.rows * nqp;
+  const int32_t kp = 4 * nqp;
+  // rows without integer division: (u + 1/2) / d lies at least 1/(2 d) >= 2^-15
+  // (d <= 16384) inside its integer interval, far above the fp32 rounding
+  // error of the product (at most 2^-16.9 for quotients below 65)
+  const float inv_nqp = 1.0f / (float)nqp;
+  auto row_of = [&](int32_t uj) { return (int32_t)(((float)uj + 0.5f) * inv_nqp); };
+  const int32_t e = bx * TPB + (int32_t)threadIdx.x;
+  const int32_t erow = (int32_t)(((float)e + 0.5f) * (0.25f * inv_nqp));
+  const int32_t ecol = e - erow * kp;
+  const bool live = erow < a.rows && ecol < a.k;
+  // every load first: the own element, every slot, the own subgroup's mask byte
+  float op = 0.0f, oq = 0.0f;
+  src_load1<SRC>(a, live ? erow : 0, live ? ecol : 0, op, oq);
+  float4 p[SPT], q[SPT];
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int32_t uj = j * TPB + (int32_t)threadIdx.x;
+    const int32_t r = row_of(uj), sq = uj - r * nqp;
+    const bool ok = uj < tot && sq < nq;
+    src_load<SRC>(a, ok ? r : 0, ok ? sq : 0, p[j], q[j]);
+  }
+  uint32_t exb = 0;
+  if (a.act_refine && a.exclude_mask) exb = a.exclude_mask[(live ? ecol : 0) >> 5];
+
+  float m = 0.0f;
+  float rs = 1.0f;   // RESIDUAL_RMSNORM: the own row's scale
+  if constexpr (NORM) {
+    __shared__ double chunk[kSmallSlots / 64];
+    __shared__ float rsc[kSmallSlots / 64];
+    float4 uu[SPT];
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int32_t uj = j * TPB + (int32_t)threadIdx.x;
+      const int32_t r = row_of(uj), sq = uj - r * nqp;
+      const bool ok = uj < tot && sq < nq;
+      uu[j] = ok ? src_value<SRC>(p[j], q[j]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      double d = (double)uu[j].x * (double)uu[j].x;
+      d += (double)uu[j].y * (double)uu[j].y;
+      d += (double)uu[j].z * (double)uu[j].z;
+      d += (double)uu[j].w * (double)uu[j].w;
+      d = wave_sum_d_dpp(d);
+      if ((threadIdx.x & 63) == 0 && uj < tot) chunk[uj / 64] = d;
+    }
+    __syncthreads();
+    const int32_t cpr = nqp / 64;
+    if ((int32_t)threadIdx.x < (int32_t)a.rows) {
+      double t = 0.0;
+      for (int32_t c = 0; c < cpr; ++c) t += chunk[(int32_t)threadIdx.x * cpr + c];
+      rsc[threadIdx.x] = (float)(1.0 / sqrt(t / (double)a.k + kRmsEps));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int32_t uj = j * TPB + (int32_t)threadIdx.x;
+      const float4 v = uj < tot ? scale4(uu[j], rsc[row_of(uj)]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      m = fmaxf(m, max4(v));
+    }
+    rs = rsc[live ? erow : 0];
+  } else {
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int32_t uj = j * TPB + (int32_t)threadIdx.x;
+      const int32_t r = row_of(uj), sq = uj - r * nqp;
+      const bool ok = uj < tot && sq < nq;
+      const float4 v = ok ? src_value<SRC>(p[j], q[j]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      m = fmaxf(m, max4(v));
+    }
+  }
+  m = wave_max(m);
+  __shared__ float red[TPB / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float amax = red[0];
+#pragma unroll
+  for (int w = 1; w < TPB / 64; ++w) amax = fmaxf(amax, red[w]);
+  const float T = tensor_scale_of(a, amax);
+  if (bx == 0 && threadIdx.x == 0) *a.tensor_scale = T;
+
+  // the own element: v (RESIDUAL_RMSNORM: u times the row scale)
+  float u1, x;
+  {
+#pragma clang fp contract(off)
+    u1 = (SRC == 1 + AUTOFP_EPI_RESIDUAL || NORM) ? oq + op : op;
+    x = NORM ? u1 * rs : u1;
+  }
+  x = live ? x : 0.0f;
+  if (SRC >= 2 && live && a.v_out) a.v_out[(int64_t)erow * a.k + ecol] = u1;
+  encode_element(a, T, erow, ecol, live, x, exb);
+}
+
 }  // namespace
 
 int64_t encode_slots_per_row(int64_t k) { return (k / 4 + 63) / 64 * 64; }
@@ -731,10 +919,50 @@ hipError_t launch_small(const EncodeArgs &a, int32_t nqp, hipStream_t s) {
   return hipGetLastError();
 }
 
+// the element-parallel encoder: rows * 4 nqp elements over blocks of TPB,
+// SPT slot groups per thread (the slot count over TPB rounded up to a power of
+// two); with the policy step one more block
+template <int TPB, int SRC>
+hipError_t launch_elem(const EncodeArgs &a, int32_t nqp, hipStream_t s) {
+  const int64_t ge = (a.rows * 4 * (int64_t)nqp + TPB - 1) / TPB;
+  const int64_t gs = (a.rows * (int64_t)nqp + TPB - 1) / TPB;
+  int spt = 1;
+  while (spt < gs) spt *= 2;
+  const int64_t gx = ge + (SRC == 2 + AUTOFP_EPI_RESIDUAL_RMSNORM ? 1 : 0);
+#define AFP_ELEM(P)                                                                                \
+  case P:                                                                                          \
+    if constexpr (TPB * P <= kSmallSlots)                                                          \
+      hipLaunchKernelGGL((encode_elem_kernel<TPB, P, SRC>), dim3((unsigned)gx), dim3(TPB), 0, s, a, nqp); \
+    else                                                                                           \
+      return hipErrorInvalidValue;                                                                 \
+    break
+  switch (spt) {
+    AFP_ELEM(1);
+    AFP_ELEM(2);
+    AFP_ELEM(4);
+    AFP_ELEM(8);
+    AFP_ELEM(16);
+    default: return hipErrorInvalidValue;
+  }
+#undef AFP_ELEM
+  return hipGetLastError();
+}
+
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s) {
   if (encode_is_small(a.rows, a.k)) {
     const int64_t nqp = encode_slots_per_row(a.k);
     const int src = a.op ? 1 + a.op : (a.dtype == AUTOFP_BF16 ? 1 : 0);
+    if (a.fmt == AUTOFP_FMT_AUTOFP6 && a.w_mask == nullptr) {
+      // activations: the element-parallel encoder (SwiGLU excepted)
+      switch (src) {
+        case 0: return launch_elem<256, 0>(a, (int32_t)nqp, s);
+        case 1: return launch_elem<256, 1>(a, (int32_t)nqp, s);
+        case 2: return launch_elem<256, 2>(a, (int32_t)nqp, s);
+        case 3: return launch_elem<256, 3>(a, (int32_t)nqp, s);
+        case 5: return a.policy ? launch_elem<256, 6>(a, (int32_t)nqp, s) : launch_elem<256, 5>(a, (int32_t)nqp, s);
+        default: break;
+      }
+    }
     switch (src) {
       case 0: return launch_small<256, 0>(a, (int32_t)nqp, s);
       case 1: return launch_small<256, 1>(a, (int32_t)nqp, s);
