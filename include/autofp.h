@@ -301,7 +301,7 @@ typedef enum {
  * it forms v [out->rows][out->k] in fp32 with `op`, writes v to v_out (may be
  * NULL) and encodes v into `out` exactly as autofp_quantize would encode v
  * (same arguments refine / exclude_mask / p, same results bit for bit). One
- * launch for out->rows * out->k <= 16384 elements, two above. COPY and
+ * launch for out->rows * roundup(out->k, 256) <= 32768, two above. COPY and
  * RESIDUAL need ldz >= k, SWIGLU ldz >= 2k; residual [rows][k] fp32 (RESIDUAL
  * and RESIDUAL_RMSNORM). z, residual, v_out 16-byte aligned, ldz % 4 == 0.
  * Workspace as autofp_quantize (AUTOFP_OP_QUANTIZE, rows, k); out->kind
@@ -333,7 +333,7 @@ autofp_status autofp_epilogue_quantize(int32_t op, const float *z, int64_t ldz, 
  * encoded bytes bit for bit; L_A per row from fp64 sums of the exact
  * differences and squares, equal to autofp_policy_layer's up to the order of
  * the fp64 additions; the levels, bits_layer and state as the Table 1 step
- * with that L_A. One launch for out->rows * out->k <= 16384 elements; above,
+ * with that L_A. One launch for out->rows * roundup(out->k, 256) <= 32768; above,
  * the epilogue's launches and then the policy's.
  * z [rows][ldz], residual, v_out (required) and h_prev (the layer's input
  * hidden state) [rows][k], all fp32, 16-byte aligned; v_out must not overlap

@@ -275,21 +275,22 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(EncodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// One-launch encoder of small tensors (rows * roundup(k/4, 64) <= 4096
+// One-launch encoder of small tensors (rows * roundup(k/4, 64) <= 8192
 // subgroup slots): slot u holds subgroup s = u mod nqp of row u / nqp, nqp =
 // k/4 rounded up to 64 (so a wavefront never spans two rows). Block bx of TPB
 // threads encodes slots [TPB bx, TPB bx + TPB); every block loads all slots
 // (thread t: slots j TPB + t, j < SPT, SPT the block count rounded up to a
 // power of two), takes the amax of the whole tensor from them and encodes
 // its own slot from the registers: one round trip to memory, no second
-// launch. 256 threads a block (one wavefront per SIMD: the per-slot encode
-// is a chain of dependent instructions), 512 for SwiGLU (each block
-// evaluates every element's silu, so fewer, larger blocks). The source is fixed at compile time and
+// launch. 256 threads a block up to 4096 slots (one wavefront per SIMD: the
+// per-slot encode is a chain of dependent instructions), 512 above and for
+// SwiGLU (every block reads the whole tensor, so fewer, larger blocks). The source is fixed at compile time and
 // every load of a thread (its slots' inputs, then the mask bytes the encode
 // needs) is issued before the first use of any, so the loads of a thread
 // overlap instead of waiting one after another.
 // ---------------------------------------------------------------------------
-constexpr int kSmallSlots = 4096;
+constexpr int kSmallSlots = 8192;
+constexpr int kSmallSlots256 = 4096;   // up to here 256-thread blocks, above 512
 
 // The raw inputs of the four elements of subgroup s of row `row`: p = x (SRC
 // 0 fp32, 1 bf16) or z (the epilogue ops, SRC = 1 + op; 6: RESIDUAL_RMSNORM
@@ -417,10 +418,10 @@ __global__ __launch_bounds__(TPB) void encode_small_kernel(EncodeArgs a, int32_t
       return;
     }
   }
-  // row of slot uj < 4096 without an integer division: (uj + 1/2) / nqp lies
-  // at least 1/(2 nqp) >= 2^-13 (nqp <= 4096) inside its integer interval,
-  // far above the rounding error of the fp32 product (at most 2^-17 for
-  // quotients up to 64)
+  // row of slot uj without an integer division: (uj + 1/2) / nqp lies at
+  // least 1/(2 nqp) inside its integer interval, and the fp32 product errs by
+  // at most (rows + 1) 2^-23 (uj < (rows + 1) nqp), below 2^-8 of that margin
+  // since rows nqp <= 8192
   const float inv_nqp = 1.0f / (float)nqp;
   auto row_of = [&](int32_t uj) { return (int32_t)(((float)uj + 0.5f) * inv_nqp); };
   // slot groups in the order bx, bx + 1, ... (mod SPT): the first is the
@@ -615,9 +616,10 @@ __global__ __launch_bounds__(TPB) void encode_elem_kernel(EncodeArgs a, int32_t 
   const int32_t nq = (int32_t)(a.k / 4);
   const int32_t tot = (int32_t)a.rows * nqp;
   const int32_t kp = 4 * nqp;
-  // rows without integer division: (u + 1/2) / d lies at least 1/(2 d) >= 2^-15
-  // (d <= 16384) inside its integer interval, far above the fp32 rounding
-  // error of the product (at most 2^-16.9 for quotients below 65)
+  // rows without integer division: (u + 1/2) / d lies at least 1/(2 d) inside
+  // its integer interval, and the fp32 product errs by at most (rows + 2)
+  // 2^-23 (u < (rows + 2) d), below a fortieth of that margin since
+  // rows 4 nqp <= 32768 and 4 nqp <= 32768
   const float inv_nqp = 1.0f / (float)nqp;
   auto row_of = [&](int32_t uj) { return (int32_t)(((float)uj + 0.5f) * inv_nqp); };
   const int32_t e = bx * TPB + (int32_t)threadIdx.x;
@@ -952,24 +954,30 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t s) {
   if (encode_is_small(a.rows, a.k)) {
     const int64_t nqp = encode_slots_per_row(a.k);
     const int src = a.op ? 1 + a.op : (a.dtype == AUTOFP_BF16 ? 1 : 0);
+    const int32_t q = (int32_t)nqp;
+    const bool big = a.rows * nqp > kSmallSlots256;   // 512-thread blocks
     if (a.fmt == AUTOFP_FMT_AUTOFP6 && a.w_mask == nullptr) {
       // activations: the element-parallel encoder (SwiGLU excepted)
       switch (src) {
-        case 0: return launch_elem<256, 0>(a, (int32_t)nqp, s);
-        case 1: return launch_elem<256, 1>(a, (int32_t)nqp, s);
-        case 2: return launch_elem<256, 2>(a, (int32_t)nqp, s);
-        case 3: return launch_elem<256, 3>(a, (int32_t)nqp, s);
-        case 5: return a.policy ? launch_elem<256, 6>(a, (int32_t)nqp, s) : launch_elem<256, 5>(a, (int32_t)nqp, s);
+        case 0: return big ? launch_elem<512, 0>(a, q, s) : launch_elem<256, 0>(a, q, s);
+        case 1: return big ? launch_elem<512, 1>(a, q, s) : launch_elem<256, 1>(a, q, s);
+        case 2: return big ? launch_elem<512, 2>(a, q, s) : launch_elem<256, 2>(a, q, s);
+        case 3: return big ? launch_elem<512, 3>(a, q, s) : launch_elem<256, 3>(a, q, s);
+        case 5:
+          if (a.policy) return big ? launch_elem<512, 6>(a, q, s) : launch_elem<256, 6>(a, q, s);
+          return big ? launch_elem<512, 5>(a, q, s) : launch_elem<256, 5>(a, q, s);
         default: break;
       }
     }
     switch (src) {
-      case 0: return launch_small<256, 0>(a, (int32_t)nqp, s);
-      case 1: return launch_small<256, 1>(a, (int32_t)nqp, s);
-      case 2: return launch_small<256, 2>(a, (int32_t)nqp, s);
-      case 3: return launch_small<256, 3>(a, (int32_t)nqp, s);
-      case 4: return launch_small<512, 4>(a, (int32_t)nqp, s);
-      case 5: return a.policy ? launch_small<256, 6>(a, (int32_t)nqp, s) : launch_small<256, 5>(a, (int32_t)nqp, s);
+      case 0: return big ? launch_small<512, 0>(a, q, s) : launch_small<256, 0>(a, q, s);
+      case 1: return big ? launch_small<512, 1>(a, q, s) : launch_small<256, 1>(a, q, s);
+      case 2: return big ? launch_small<512, 2>(a, q, s) : launch_small<256, 2>(a, q, s);
+      case 3: return big ? launch_small<512, 3>(a, q, s) : launch_small<256, 3>(a, q, s);
+      case 4: return launch_small<512, 4>(a, q, s);
+      case 5:
+        if (a.policy) return big ? launch_small<512, 6>(a, q, s) : launch_small<256, 6>(a, q, s);
+        return big ? launch_small<512, 5>(a, q, s) : launch_small<256, 5>(a, q, s);
       default: return hipErrorInvalidValue;
     }
   }

@@ -65,13 +65,15 @@ def test_activation_encode_config1(dtype, refine):
     assert_same_packed(pk, ref)
 
 
-@pytest.mark.parametrize("shape", [(1, 4096), (4, 4096), (5, 4096), (1, 14336), (64, 16), (65, 16), (32, 272),
-                                   (33, 272), (8, 14336), (8192, 16), (8193, 16), (16, 14336), (3, 65536)])
+@pytest.mark.parametrize("shape", [(1, 4096), (4, 4096), (5, 4096), (8, 4096), (9, 4096), (1, 14336), (2, 14336),
+                                   (3, 14336), (64, 16), (65, 16), (128, 16), (129, 16), (32, 272), (33, 272),
+                                   (64, 272), (65, 272), (8, 14336), (8192, 16), (8193, 16), (16, 14336), (3, 65536)])
 def test_activation_encode_one_and_two_launch_paths(shape):
-    """Decode-step activation shapes on both sides of the single-launch limit
-    (rows * roundup(k/4, 64) <= 4096 subgroup slots: 4 x 4096, 64 x 16,
-    32 x 272 fit, one row more does not): bit-exact codes, scales, T, mask
-    and offsets."""
+    """Decode-step activation shapes on both sides of the single-launch limits
+    (rows * roundup(k/4, 64) subgroup slots: 256-thread blocks up to 4096 —
+    4 x 4096, 64 x 16, 32 x 272 —, 512-thread blocks up to 8192 — 8 x 4096,
+    2 x 14336, 128 x 16, 64 x 272 —, one row more takes the next form):
+    bit-exact codes, scales, T, mask and offsets."""
     rows, k = shape
     say(f"case: activation encode {rows}x{k} (bf16, refine, exclusion mask)")
     x = S.activations(rows, k, seed=rows + k, tensor_id=3, dtype=torch.bfloat16, device=DEV)

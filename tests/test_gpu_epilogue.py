@@ -44,7 +44,7 @@ def same_packed(gpu, ref, refine):
 
 
 @pytest.mark.parametrize("op", ["copy", "residual", "swiglu"])
-@pytest.mark.parametrize("rows,k", [(1, 4096), (4, 4096), (1, 14336), (64, 1024), (3, 272)])
+@pytest.mark.parametrize("rows,k", [(1, 4096), (4, 4096), (8, 4096), (1, 14336), (2, 14336), (64, 1024), (3, 272)])
 @pytest.mark.parametrize("refine", [False, True])
 def test_epilogue_quantize(op, rows, k, refine):
     say(f"case: epilogue {op} rows={rows} k={k} refine={refine}")
@@ -94,7 +94,7 @@ def test_epilogue_without_v_out_and_arguments():
         A.epilogue_quantize("residual", z, out)                             # residual missing
 
 
-@pytest.mark.parametrize("rows,k", [(1, 4096), (4, 4096), (1, 14336), (3, 272), (64, 1024), (64, 4096), (16, 14336)])
+@pytest.mark.parametrize("rows,k", [(1, 4096), (4, 4096), (8, 4096), (1, 14336), (2, 14336), (3, 272), (64, 1024), (64, 4096), (16, 14336)])
 @pytest.mark.parametrize("refine", [False, True])
 def test_epilogue_residual_rmsnorm(rows, k, refine):
     """Residual add + RMSNorm (one launch up to 4096 subgroup slots: 1 x 4096,
@@ -135,7 +135,7 @@ def test_epilogue_residual_rmsnorm(rows, k, refine):
     assert torch.equal(out2.codes, out.codes) and torch.equal(out2.tensor_scale, out.tensor_scale)
 
 
-@pytest.mark.parametrize("rows,k", [(1, 4096), (4, 4096), (3, 1024), (16, 4096)])
+@pytest.mark.parametrize("rows,k", [(1, 4096), (4, 4096), (8, 4096), (3, 1024), (16, 4096)])
 @pytest.mark.parametrize("phase", [1, 0])
 def test_layer_epilogue_equals_epilogue_then_policy_layer(rows, k, phase):
     """autofp_layer_epilogue (the residual RMSNorm epilogue with the layer's
