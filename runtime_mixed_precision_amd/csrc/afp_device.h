@@ -186,10 +186,27 @@ __device__ __forceinline__ half2v e2m3x2_to_half2(uint32_t c0, uint32_t c1) {
 // Wave reductions (64-wide wavefronts)
 // ---------------------------------------------------------------------------
 
+// Largest value of the wavefront in every lane (fmaxf: NaNs are skipped),
+// through DPP row moves and the gfx950 row swaps (no LDS permutes).
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  auto dmax = [](float x, int ctrl) -> float {
+    int y = 0;
+    switch (ctrl) {   // the DPP control must be a constant
+      case 0: y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false); break;   // quad xor 1
+      case 1: y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false); break;   // quad xor 2
+      case 2: y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false); break;  // row half mirror
+      default: y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false); break; // row mirror
+    }
+    return fmaxf(x, __int_as_float(y));
+  };
+  v = dmax(v, 0);
+  v = dmax(v, 1);
+  v = dmax(v, 2);
+  v = dmax(v, 3);   // every lane: max of its row of 16
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));   // rows (0, 1) and (2, 3)
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Largest value of the wavefront in every lane, through DPP row moves and the
