@@ -1354,7 +1354,10 @@ StreamCfg stream_cfg(const LinearArgs &a) {
 // more wavefronts: every wavefront's prologue costs the same few loads, so
 // short ranges make the launch instruction-bound (measured at one token:
 // Wqkv 6.4 us at one wavefront per tile, 7.7 at four; Wo 4.9 at two, 5.3 at
-// four). Level 6 (or a device-side level) takes the streaming kernel's
+// four). A host-side level 2 with K up to 4096 (the digit remap adds to
+// every chunk's arithmetic) takes about 1536 wavefronts, and two per tile on
+// evenly split wide weights (one token, graphs of 9 launches: Wqkv 8.5 -> 7.4 us, Wo 6.1
+// -> 5.9, Wgate|Wup 16.2 -> 15.8). Level 6 (or a device-side level) takes the streaming kernel's
 // shape, about 1536 wavefronts. When the row tiles split evenly over the
 // compute units, 256 blocks of tiles / 256 tiles each. Ranges are capped at
 // the LDS staging capacity (16 chunks at one token, 32 / bt above).
@@ -1385,17 +1388,20 @@ Fp4Cfg fp4_cfg(const LinearArgs &a, bool six, int bt) {
   const size_t wave_lds = fp4_wave_lds(bt, six);
   int wk = a.waves > 0 ? a.waves : 1;
   while ((nch + wk - 1) / wk > cap) ++wk;
+  const bool two = !six && a.bits == 2 && a.bits_dev == nullptr;   // host-side level 2
   if (tiles % kCUs == 0 && per_cu >= 2 && per_cu * wk <= kMaxWaves &&
       (size_t)(per_cu * wk) * wave_lds <= (size_t)max_lds_per_block()) {
     c.rt = (int)per_cu;
-    if (a.waves == 0 && six) {
+    if (a.waves == 0 && (six || two)) {
       while (c.rt * wk * 2 <= kMaxWaves && nch / (2 * wk) >= 8 &&
-             (size_t)(c.rt * wk * 2) * wave_lds <= (size_t)max_lds_per_block())
+             (size_t)(c.rt * wk * 2) * wave_lds <= (size_t)max_lds_per_block()) {
         wk *= 2;
+        if (two) break;   // level 2: two wavefronts per tile
+      }
     }
     c.wk = wk;
   } else if (!six && a.waves == 0) {
-    while (tiles * wk < 384 && nch / (2 * wk) >= 4) wk <<= 1;
+    while (tiles * wk < (two && nch <= kFp4Chunks ? 1536 : 384) && nch / (2 * wk) >= 4) wk <<= 1;
     c.wk = wk;
     c.rt = 1;
   } else {
