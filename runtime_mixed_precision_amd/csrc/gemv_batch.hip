@@ -15,7 +15,7 @@
 // is applied once per output.
 //
 // Work split. A block of 4 wavefronts owns 16 NF weight rows (NF = 4, or 2
-// above 32 tokens with level-6 operands) and 16 TT tokens (TT = 1, 2 or 4
+// above 32 tokens with per-token levels) and 16 TT tokens (TT = 1, 2 or 4
 // tiles of 16); the wavefronts split the block's K range into four contiguous
 // parts, and the blocks of one row tile split K into S parts (S > 1 only
 // when the row tiles alone leave compute units idle). Per 128-element K step
@@ -448,9 +448,11 @@ int batch_splits(int64_t n, int64_t k, int rows) {
   return s;
 }
 
-// 16-row fragments per wavefront: 4 (64 rows per block), 2 for 64 tokens
-// with refinement (register budget of two wavefronts per SIMD)
-int batch_frags(int64_t tokens, bool ref) { return (tokens > 32 && ref) ? 2 : 4; }
+// 16-row fragments per wavefront: 4 (64 rows per block), 2 above 32 tokens
+// with per-token levels (the mixed kernel's registers: two wavefronts per
+// SIMD). A single level 6 keeps 4 (64 tokens: Wgate|Wup 81 -> 62 us, Wdown
+// 50 -> 45 us against 2).
+int batch_frags(int64_t tokens, bool mixed) { return (tokens > 32 && mixed) ? 2 : 4; }
 
 }  // namespace
 
@@ -458,10 +460,10 @@ int64_t gemv_batch_part_floats(int64_t tokens) { return (int64_t)kPartFloats * (
 
 bool gemv_batch_ok(const LinearArgs &a) {
   if (a.k % kStep != 0) return false;
-  const bool ref = a.bits_rows != nullptr || a.bits_dev != nullptr || a.bits == 6;
+  const bool mixed = a.bits_rows != nullptr;
   for (int64_t b : {a.b < 64 ? a.b : (int64_t)64, a.b % 64}) {
     if (b == 0) continue;
-    const int s = batch_splits(a.n, a.k, 16 * batch_frags(b, ref));
+    const int s = batch_splits(a.n, a.k, 16 * batch_frags(b, mixed));
     if (s > 1 && (int64_t)s * a.n > kPartFloats) return false;
   }
   return true;
@@ -478,7 +480,7 @@ hipError_t launch_gemv_batch(const LinearArgs &a0, hipStream_t st) {
     a.x_offsets = a0.x_offsets ? a0.x_offsets + t0 * (a0.k / 4) : nullptr;
     a.bits_rows = a0.bits_rows ? a0.bits_rows + t0 : nullptr;
     a.y = (char *)a0.y + t0 * a0.n * (a0.y_dtype == AUTOFP_BF16 ? 2 : 4);
-    const int nf = batch_frags(a.b, ref);
+    const int nf = batch_frags(a.b, mixed);
     const int S = batch_splits(a.n, a.k, 16 * nf);
     const int64_t nrb = (a.n + 16 * nf - 1) / (16 * nf);
     a.splits = S;
@@ -494,7 +496,8 @@ hipError_t launch_gemv_batch(const LinearArgs &a0, hipStream_t st) {
     else AFP_BATCH(TT, NF, false, false)
     if (tt == 1) { AFP_BATCH_TT(1, 4); }
     else if (tt == 2) { AFP_BATCH_TT(2, 4); }
-    else if (nf == 2) { AFP_BATCH_TT(4, 2); }
+    else if (nf == 2) { AFP_BATCH(4, 2, true, true); }
+    else if (ref) { AFP_BATCH(4, 4, false, true); }
     else { AFP_BATCH(4, 4, false, false); }
 #undef AFP_BATCH_TT
 #undef AFP_BATCH
