@@ -144,6 +144,8 @@ hipError_t launch_gemv(const LinearArgs &a, hipStream_t s);
 // levels): K % 128 == 0. Reads a.prefix at level 6 (or a device/per-token
 // level) and a.part when the K range is split.
 bool gemv_batch_ok(const LinearArgs &a);
+// 9-64 tokens served by the batched kernel (gemv_batch_ok and the 9-16-token shape rule)
+bool gemv_batch_route(const LinearArgs &a);
 int64_t gemv_batch_part_floats(int64_t tokens);   // floats of a.part the launcher may use
 hipError_t launch_gemv_batch(const LinearArgs &a, hipStream_t s);
 

@@ -192,7 +192,7 @@ autofp_status gemv_launches(LinearArgs &a, const autofp_packed *w, const autofp_
     const hipError_t e = launch_act_dequant(a, s);
     if (e != hipSuccess) return AUTOFP_ERR_HIP;
   }
-  if ((gemv_small_m_route(a) || (a.b > 16 && gemv_batch_ok(a))) && w->mask && (bits_dev || bits == 6)) {
+  if ((gemv_small_m_route(a) || gemv_batch_route(a)) && w->mask && (bits_dev || bits == 6)) {
     const hipError_t e = launch_mask_prefix(w->mask, mask_bytes(w->k), a.prefix, s);
     if (e != hipSuccess) return AUTOFP_ERR_HIP;
   }

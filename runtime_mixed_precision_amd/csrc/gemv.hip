@@ -1438,8 +1438,17 @@ bool gemv_panel_packed(const LinearArgs &a) {
          a.bits != 6;
 }
 
+// 9-16 tokens take the batched kernel on the larger weights (measured at 16
+// tokens, graphs of 9 launches, levels 2/4/6: Wqkv 19.0/18.1/28.8 ->
+// 14.9/13.6/20.5 us, Wgate|Wup 30.5/29.4/44.8 -> 27.2/23.1/40.6, Wdown
+// 27.4/26.0/30.4 -> 19.6/17.1/30.8) and the streaming kernel on the smaller
+// ones (Wo 10.4/10.1/16.1 against 12.1/11.3/17.6 us)
+bool gemv_batch_route(const LinearArgs &a) {
+  return a.b > 16 ? gemv_batch_ok(a) : (a.b > 8 && (a.n >= 6144 || a.k > 4096) && gemv_batch_ok(a));
+}
+
 bool gemv_needs_panel(const LinearArgs &a) {
-  if (a.b > 16 && gemv_batch_ok(a)) return false;
+  if (gemv_batch_route(a)) return false;
   if (a.b > 16) return !gemv_panel_packed(a);
   return !stream_cfg(a).xlds;
 }
@@ -1480,6 +1489,7 @@ hipError_t launch_gemv(const LinearArgs &a0, hipStream_t s) {
       return hipGetLastError();
     }
   }
+  if (a0.b <= 16 && gemv_batch_route(a0)) return launch_gemv_batch(a0, s);
   if (a0.b <= 16) {
     const StreamCfg c = stream_cfg(a0);
     LinearArgs a1 = a0;
