@@ -23,7 +23,8 @@ __all__ = [
     "select_weight_mask", "quantize", "quantize_weight", "quantize_activation",
     "alloc_activation", "quantize_into", "quantize_noalloc", "epilogue_quantize", "gptq_quantize",
     "gemv", "gemv_rows", "gemm", "policy_signals", "policy_state", "policy_update", "AutofpError",
-    "NativeLibraryError", "KVCache", "kv_write", "kv_attention",
+    "NativeLibraryError", "KVCache", "kv_write", "kv_attention", "layer_epilogue", "policy_layer",
+    "save_packed", "load_packed",
 ]
 
 _DT = {torch.float32: N.F32, torch.bfloat16: N.BF16}
@@ -149,6 +150,78 @@ def _alloc_packed(rows, k, kind, refine, n_refined, device, format=0):
         mask = buf(nb[3], (rows, mb))
         offs = buf(nb[4], (rows, (k // 4) * ow))
     return AutoFPTensor(rows, k, kind, codes, scales, ts, mask, offs, n_refined if kind == N.WEIGHT else 0, fmt)
+
+
+_SAVE_VERSION = "1"
+_SAVE_FIELDS = ("codes", "scales", "tensor_scale", "mask", "offsets")
+
+
+def save_packed(path, tensors: dict) -> None:
+    """Write packed tensors (name -> AutoFPTensor) to a safetensors file.
+
+    Each buffer is stored as-is (byte codes, E4M3 scale bytes, the fp32 tensor
+    scale, mask and offset bytes) under ``<name>.<field>``; rows, k, kind,
+    n_refined and the format go into the file's string metadata. Nothing is
+    re-encoded, so a loaded tensor gives bit-identical GEMV/GEMM outputs.
+    """
+    from safetensors.torch import save_file
+    blobs, meta = {}, {"autofp_packed_version": _SAVE_VERSION}
+    for name, t in tensors.items():
+        if "." in name:
+            raise ValueError(f"tensor name {name!r} may not contain '.'")
+        meta[name] = f"{t.rows},{t.k},{t.kind},{t.n_refined},{t.format}"
+        for f in _SAVE_FIELDS:
+            b = getattr(t, f)
+            if b is not None:
+                blobs[f"{name}.{f}"] = b.detach().contiguous().cpu()
+    save_file(blobs, str(path), metadata=meta)
+
+
+def load_packed(path, device="cuda:0") -> dict:
+    """Read a file written by ``save_packed``: name -> AutoFPTensor on ``device``.
+
+    The buffers are allocated as the quantizers allocate them (including the
+    padding after a weight's offsets that the GEMV may read) and filled from
+    the file; a buffer whose size or dtype differs from what the metadata
+    implies, or a file safetensors cannot parse, raises ``ValueError``. The
+    file is parsed by safetensors, which executes nothing from it.
+    """
+    from safetensors import SafetensorError, safe_open
+    try:
+        return _load_packed(safe_open(str(path), framework="pt", device="cpu"), path, device)
+    except SafetensorError as e:
+        raise ValueError(f"{path}: {e}") from None
+
+
+def _load_packed(handle, path, device):
+    out = {}
+    with handle as f:
+        meta = f.metadata() or {}
+        if meta.get("autofp_packed_version") != _SAVE_VERSION:
+            raise ValueError(f"{path}: not an AutoFP packed file (version {meta.get('autofp_packed_version')!r})")
+        keys = set(f.keys())
+        for name, desc in meta.items():
+            if name == "autofp_packed_version":
+                continue
+            try:
+                rows, k, kind, n_ref, fmt = (int(v) for v in desc.split(","))
+            except ValueError:
+                raise ValueError(f"{path}: bad metadata for {name!r}: {desc!r}") from None
+            refine = f"{name}.offsets" in keys
+            t = _alloc_packed(rows, k, kind, refine, n_ref, device, fmt)
+            for fld in _SAVE_FIELDS:
+                dst, key = getattr(t, fld), f"{name}.{fld}"
+                if (dst is None) != (key not in keys):
+                    raise ValueError(f"{path}: {key} is {'missing' if dst is not None else 'unexpected'}")
+                if dst is None:
+                    continue
+                src = f.get_tensor(key)
+                if src.dtype != dst.dtype or tuple(src.shape) != tuple(dst.shape):
+                    raise ValueError(f"{path}: {key} has {src.dtype} {tuple(src.shape)}, "
+                                     f"expected {dst.dtype} {tuple(dst.shape)}")
+                dst.copy_(src)
+            out[name] = t
+    return out
 
 
 def select_weight_mask(w: torch.Tensor, params=None, stream=None, format="autofp6"):

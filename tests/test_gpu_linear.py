@@ -154,6 +154,21 @@ def test_gemv_equals_gemm():
         assert np.abs(a - b).max() <= 1e-5 * np.abs(b).max()
 
 
+def test_saved_and_loaded_operands_give_identical_outputs(tmp_path):
+    say("case: save/load round trip 4096x4096, 1 and 40 tokens")
+    w, x = operands(4096, 40, 4096, seed=21)
+    wp, xp4, xp6 = gpu_pack(w, x)
+    path = tmp_path / "layer.safetensors"
+    A.save_packed(path, {"w": wp, "x4": xp4, "x6": xp6})
+    got = A.load_packed(path, device=DEV)
+    for level in (2, 4, 6):
+        xa, xb = (xp6, got["x6"]) if level == 6 else (xp4, got["x4"])
+        for fn in (A.gemv, A.gemm):
+            assert torch.equal(fn(wp, xa, bits=level), fn(got["w"], xb, bits=level)), (fn.__name__, level)
+    x1 = A.quantize_activation(x[:1].contiguous(), refine=True, exclude_mask=wp.mask)
+    assert torch.equal(A.gemv(wp, x1, bits=6), A.gemv(got["w"], x1, bits=6))
+
+
 @pytest.mark.parametrize("name,b", [("wgate", 1), ("wgate", 8), ("wdown", 8), ("wqkv", 1), ("wqkv", 8), ("wqkv", 16),
                                     ("wdown", 64), ("wqkv", 64), ("wgate", 64)])
 def test_full_size_decode_sampled(name, b):
