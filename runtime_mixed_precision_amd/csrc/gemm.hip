@@ -10,7 +10,7 @@
 // B*(q + d/8) (up to 10 significant bits) exactly. The operands are therefore
 // decoded into fp16 - exact - and multiplied at the fp16 MFMA rate.
 //
-// Two kernels:
+// Three kernels:
 //  - gemm_lds_kernel (K % 64 == 0, the prefill and batched-decode path): a
 //    block of 8 or 16 wavefronts computes BM tokens x BN weight rows (256 x 256
 //    or 256 x 128 for prefill, 64 x 64..256 for 17-64 decode tokens) in K steps
@@ -21,6 +21,8 @@
 //    turn, two steps ahead.
 //  - gemm_kernel (any K % 16 == 0): 4 wavefronts on a 128 x 128 tile, both
 //    operands through registers; the fallback for K % 64 != 0.
+//  - gemv_fmt_kernel (the variant formats at 1-4 tokens): a vector GEMV over
+//    the same weight decode, one wavefront per two weight rows.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -221,6 +223,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a) {
 
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3v __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x6v __attribute__((ext_vector_type(6)));
+typedef _Float16 half32v __attribute__((ext_vector_type(32)));
 #define AFP_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 constexpr int kBM2 = 256;
@@ -247,17 +251,27 @@ __device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * 128
 // o4 and o5, 20 bytes) whose first offset starts sh bytes in, with m the
 // item's mask byte. h[p] = elements 8p .. 8p + 7, times their group scale.
 // Tables: dtab / stab (AUTOFP6, AUTOFP6E) or t8 (AUTOFP8), as filled by the
-// kernels below.
-template <int FMT>
+// kernels below. PK6: FP6G codes through the 32-element fp6 conversion.
+template <int FMT, bool PK6 = false>
 __device__ __forceinline__ void decode_w32(const u32x4v c, const u32x2v cx, uint32_t s2, const u32x3v o,
                                            const u32x4v o4, uint32_t o5, uint32_t m, uint32_t sh, int L,
                                            bool refine, const uint2 *dtab, const uint2 *stab, const uint32_t *t8,
                                            half8v h[4]) {
   constexpr bool F8 = FMT == AUTOFP_FMT_AUTOFP8;
   constexpr bool G6 = FMT == AUTOFP_FMT_FP6G;
-  if constexpr (G6) {
-    // 32 six-bit codes in 24 bytes: 8 codes (48 bits) per fragment, at
-    // bits 0, 48, 96 and 144 of the six dwords
+  if constexpr (G6 && PK6) {
+    // 32 six-bit E2M3 codes in 24 bytes (code i at bits [6i+5:6i] of the
+    // six little-endian dwords) to fp16 in one conversion (exact; scale 1)
+    const u32x6v src = {c[0], c[1], c[2], c[3], cx[0], cx[1]};
+    const half32v v = __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(src, 1.0f);
+    h[0] = __builtin_shufflevector(v, v, 0, 1, 2, 3, 4, 5, 6, 7);
+    h[1] = __builtin_shufflevector(v, v, 8, 9, 10, 11, 12, 13, 14, 15);
+    h[2] = __builtin_shufflevector(v, v, 16, 17, 18, 19, 20, 21, 22, 23);
+    h[3] = __builtin_shufflevector(v, v, 24, 25, 26, 27, 28, 29, 30, 31);
+  } else if constexpr (G6) {
+    // the same bits field by field: 8 codes (48 bits) per fragment, at bits
+    // 0, 48, 96 and 144 of the six dwords (no 32-register result, for the
+    // GEMM tiles whose register budget it would exceed)
     const uint64_t win4[4] = {((uint64_t)c[1] << 32) | c[0], (((uint64_t)c[2] << 32) | c[1]) >> 16,
                               ((uint64_t)cx[0] << 32) | c[3], (((uint64_t)cx[1] << 32) | cx[0]) >> 16};
 #pragma unroll
@@ -735,6 +749,219 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Variant formats at 1-4 tokens: vector GEMV
+// ---------------------------------------------------------------------------
+//
+// A variant weight element B (q + delta) or an E2M3 code needs more than the
+// four significant bits the fp4 matrix cores take, and a 64-token GEMM tile
+// at one token leaves most of the chip idle ([AE] App. I Table 10, App. B.2:
+// the formats; the product is the one the GEMM tiles compute). Here a wavefront owns RPW weight
+// rows and its lanes split K into 32-element items: lane l takes items l,
+// l + 64, ... of each row, decodes them with decode_w32 (the GEMM tiles' own
+// weight decode: fp16, exact, group scales applied) and accumulates their
+// dot products with the fp16 activation panel in fp32 (v_dot2_f32_f16,
+// products exact in fp32); the lanes' sums are added across the wavefront at
+// the end in one fixed order. TB >= b tokens (absent tokens read as zero).
+// The time is mostly the decode's vector ALU (a wave64 instruction per four
+// cycles on each SIMD), so FP6G takes its codes through the 32-element fp6
+// conversion.
+
+// Sum of the wavefront's values, the same in every lane, through DPP row
+// moves and the row swaps (quad pairs, quads, half rows, rows, row pairs,
+// halves: one fixed order).
+__device__ __forceinline__ float wave_sum_f(float v) {
+  auto dadd = [](float x, int ctrl) -> float {
+    int y = 0;
+    switch (ctrl) {   // the DPP control must be a constant
+      case 0: y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false); break;   // quad xor 1
+      case 1: y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false); break;   // quad xor 2
+      case 2: y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false); break;  // row half mirror
+      default: y = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false); break; // row mirror
+    }
+    return x + __int_as_float(y);
+  };
+  v = dadd(v, 0);
+  v = dadd(v, 1);
+  v = dadd(v, 2);
+  v = dadd(v, 3);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ float dot8(half8v w, half8v x, float acc) {
+  acc = __builtin_amdgcn_fdot2(half2v{w[0], w[1]}, half2v{x[0], x[1]}, acc, false);
+  acc = __builtin_amdgcn_fdot2(half2v{w[2], w[3]}, half2v{x[2], x[3]}, acc, false);
+  acc = __builtin_amdgcn_fdot2(half2v{w[4], w[5]}, half2v{x[4], x[5]}, acc, false);
+  return __builtin_amdgcn_fdot2(half2v{w[6], w[7]}, half2v{x[6], x[7]}, acc, false);
+}
+
+constexpr int kFmtGemvWaves = 4;    // wavefronts per block
+// Largest token count routed here (Wup 14336 x 4096, one token: FP6G 51 ->
+// 21 us, AUTOFP8 58 -> 28 us, AUTOFP6E 56 -> 33 us against the 64-token GEMM
+// tile; still ahead at 4 tokens, behind at 8, where the tile's decode of each
+// weight serves every token)
+constexpr int kFmtGemvTokens = 4;
+
+template <int FMT, int TB, int RPW, int U>
+__global__ __launch_bounds__(64 * kFmtGemvWaves) void gemv_fmt_kernel(LinearArgs a) {
+  constexpr bool F8 = FMT == AUTOFP_FMT_AUTOFP8;
+  constexpr bool G6 = FMT == AUTOFP_FMT_FP6G;
+  constexpr int64_t OW = F8 ? 2 : 1;   // offset bytes per refined subgroup
+  constexpr uint32_t OOB = 0x80000000u;
+  __shared__ uint2 tabs[512];
+  uint2 *dtab = tabs, *stab = tabs + 256;
+  uint32_t *t8 = (uint32_t *)tabs;
+  const int L = run_level(a);
+  const bool refine_w = !G6 && (L == 6 || (F8 && L == 8)) && a.w_mask != nullptr && a.w_offsets != nullptr &&
+                        a.n_refined > 0;
+  if (refine_w) fill_decode_tables<FMT>(dtab, stab, L);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t K = a.k, R = a.n_refined;
+  const int64_t CB = G6 ? 3 * K / 4 : K / 2;   // code bytes per weight row
+  const int64_t items = K >> 5;                 // 32-element items per row
+  const int64_t n0 = ((int64_t)blockIdx.x * kFmtGemvWaves + wave) * RPW;
+  if (n0 >= a.n) return;
+  const int64_t nrows = (a.n - n0) < RPW ? (a.n - n0) : RPW;
+  // this wavefront's rows only, so offsets stay 32-bit; rows past n, and
+  // items past K, read as zero
+  const __amdgpu_buffer_rsrc_t rc = rsrc(a.w_codes + n0 * CB, nrows * CB);
+  const __amdgpu_buffer_rsrc_t rs = rsrc(a.w_scales + n0 * (K >> 4), nrows * (K >> 4));
+  const __amdgpu_buffer_rsrc_t ro =
+      rsrc(refine_w ? a.w_offsets + n0 * R * OW : a.w_codes, refine_w ? nrows * R * OW + 16 : 0);
+  const __amdgpu_buffer_rsrc_t rm = rsrc(refine_w ? a.w_mask : a.w_codes, refine_w ? items : 0);
+  const __amdgpu_buffer_rsrc_t rp = rsrc(refine_w ? (const void *)a.prefix : a.w_codes, refine_w ? 4 * items : 0);
+  // activation panel [b][kpad] fp16 (b <= TB <= 4): tokens past b read as zero
+  const __amdgpu_buffer_rsrc_t rx = rsrc(a.xh, a.b * a.kpad * 2);
+
+  float acc[RPW][TB];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[r][t] = 0.0f;
+
+  // U items per lane per pass (items jb, jb + 64, ...), every load of the
+  // pass issued before the first use: mask bytes and prefixes first (the
+  // offsets' positions), then activations, codes and scales, then offsets
+  for (int64_t jb = lane; jb < items; jb += 64 * U) {
+    uint32_t mb[U], joff[U];
+    int32_t pos[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = jb + 64 * u;
+      joff[u] = j < items ? (uint32_t)j : OOB;
+      mb[u] = 0;
+      pos[u] = 0;
+      if (refine_w) {
+        mb[u] = __builtin_amdgcn_raw_buffer_load_b8(rm, (int)joff[u], 0, 0);
+        pos[u] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rp, (int)(j < items ? 4 * joff[u] : OOB), 0, 0);
+      }
+    }
+    half8v xv[U][TB][4];
+    u32x4v c[U][RPW];
+    u32x2v cx[U][RPW];
+    uint32_t s2[U][RPW];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool live = joff[u] != OOB;
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t off = live && t < a.b ? (uint32_t)((t * a.kpad + 32 * joff[u] + 8 * q) * 2) : OOB;
+          xv[u][t][q] = __builtin_bit_cast(half8v, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0));
+        }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        if constexpr (G6) {
+          const uint32_t off = live ? (uint32_t)(r * CB + 24 * joff[u]) : OOB;
+          c[u][r] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)off, 0, 0);
+          cx[u][r] = __builtin_amdgcn_raw_buffer_load_b64(rc, (int)(live ? off + 16 : OOB), 0, 0);
+        } else {
+          c[u][r] = __builtin_amdgcn_raw_buffer_load_b128(
+              rc, (int)(live ? (uint32_t)(r * (K >> 1) + 16 * joff[u]) : OOB), 0, 0);
+          cx[u][r] = u32x2v{0u, 0u};
+        }
+        s2[u][r] = __builtin_amdgcn_raw_buffer_load_b16(
+            rs, (int)(live ? (uint32_t)(r * (K >> 4) + 2 * joff[u]) : OOB), 0, 0);
+      }
+    }
+    u32x3v o[U][RPW];
+    u32x4v o4[U][RPW];
+    uint32_t o5[U][RPW], sh[U][RPW];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        o[u][r] = u32x3v{0u, 0u, 0u};
+        o4[u][r] = u32x4v{0u, 0u, 0u, 0u};
+        o5[u][r] = 0;
+        sh[u][r] = 0;
+        if (refine_w) {
+          const int64_t p = (r * R + pos[u]) * OW;   // byte of the item's first offset
+          const uint32_t al = (uint32_t)(p & ~(int64_t)3);
+          sh[u][r] = (uint32_t)(p & 3);
+          if constexpr (F8) {
+            o4[u][r] = __builtin_amdgcn_raw_buffer_load_b128(ro, (int)al, 0, 0);
+            o5[u][r] = __builtin_amdgcn_raw_buffer_load_b32(ro, (int)(al + 16), 0, 0);
+          } else {
+            o[u][r] = __builtin_amdgcn_raw_buffer_load_b96(ro, (int)al, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        half8v h[4];
+        decode_w32<FMT, true>(c[u][r], cx[u][r], s2[u][r], o[u][r], o4[u][r], o5[u][r], mb[u], sh[u][r], L,
+                              refine_w, dtab, stab, t8, h);
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[r][t] = dot8(h[q], xv[u][t][q], acc[r][t]);
+      }
+  }
+
+  float scale = (*a.w_T) * (*a.x_T);
+  if (L == 2) scale *= a.c2;
+  const bool out_bf16 = a.y_dtype == AUTOFP_BF16;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      const float v = wave_sum_f(acc[r][t]) * scale;
+      if (lane == r * TB + t && r < nrows && t < a.b) {
+        const int64_t i = (int64_t)t * a.n + n0 + r;
+        if (out_bf16) ((uint16_t *)a.y)[i] = f32_to_bf16_rne(v);
+        else ((float *)a.y)[i] = v;
+      }
+    }
+}
+
+template <int FMT, int TB>
+hipError_t launch_gemv_fmt_t(const LinearArgs &a, hipStream_t s) {
+  constexpr int RPW = TB <= 2 ? 2 : 1;   // weight rows per wavefront
+  constexpr int U = 1;                   // items per lane per pass
+  const int64_t rows_per_block = (int64_t)kFmtGemvWaves * RPW;
+  hipLaunchKernelGGL((gemv_fmt_kernel<FMT, TB, RPW, U>),
+                     dim3((unsigned)((a.n + rows_per_block - 1) / rows_per_block)), dim3(64 * kFmtGemvWaves), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_gemv_fmt(const LinearArgs &a, hipStream_t s) {
+  if (a.b <= 1) return launch_gemv_fmt_t<FMT, 1>(a, s);
+  if (a.b <= 2) return launch_gemv_fmt_t<FMT, 2>(a, s);
+  return launch_gemv_fmt_t<FMT, 4>(a, s);
+}
+
 }  // namespace
 
 bool gemm_small_m_ok(const LinearArgs &a) { return a.k % kBK2 == 0; }
@@ -770,6 +997,7 @@ hipError_t launch_gemm_small_m(const LinearArgs &a, hipStream_t s) {
 
 template <int FMT>
 hipError_t launch_gemm_fmt_t(const LinearArgs &a, hipStream_t s) {
+  if (a.b <= kFmtGemvTokens) return launch_gemv_fmt<FMT>(a, s);
   const int64_t nt256 = (a.n + 255) / 256;
   if (a.b >= 128) {
     const int64_t mtiles = (a.b + kBM2 - 1) / kBM2;

@@ -139,10 +139,12 @@ def oracle_linear(fmt, wq, xq4, xq6, level):
 
 @pytest.mark.parametrize("fmt", ("autofp6e", "autofp8", "fp6g"))
 @pytest.mark.parametrize("n,b,k", [(300, 1, 1024), (130, 5, 512), (520, 64, 2048), (200, 40, 64),
-                                   (1000, 300, 1024)])
+                                   (1000, 300, 1024), (301, 2, 4160), (77, 8, 64), (64, 3, 14336),
+                                   (9, 1, 256), (45, 4, 256)])
 def test_linear_formats(fmt, n, b, k):
     """Every level of the format on the decode entry point (and the prefill
-    one at the same shape): ragged weight rows, 1-300 tokens."""
+    one at the same shape): ragged weight rows, 1-300 tokens (1-4 on the
+    vector GEMV, K from 64 (fewer items than lanes) to 14336)."""
     say(f"case: linear {fmt} n={n} b={b} k={k}")
     wp, xp4, xp6, wq, xq4, xq6 = packs(fmt, n, b, k, seed=n + b + k)
     for level in levels_of(fmt):
@@ -177,6 +179,25 @@ def test_linear_formats_shape_rules():
     with pytest.raises(A.AutofpError):
         A.gemv(wp, xp6, bits=8)
     check_close(A.gemv(wp, xp4, bits=4).cpu().numpy(), oracle_linear("autofp8", wq, xq4, xq6, 4))
+
+
+@pytest.mark.parametrize("fmt", ("autofp6e", "autofp8", "fp6g"))
+@pytest.mark.parametrize("b", [1, 4])
+def test_decode_formats_full_width_sampled(fmt, b):
+    """The one-token decode the benchmark times (Wup 14336 x 4096) and 4
+    tokens (the vector GEMV's widest case), at the format's top level: every output of 48 sampled weight
+    rows (the first and last among them), fp32 and bf16 outputs."""
+    n, k = 14336, 4096
+    rows = np.concatenate([[0, n - 1], np.random.default_rng(8).choice(np.arange(1, n - 1), 46, replace=False)])
+    say(f"case: decode {fmt} {n}x{k} at {b} tokens, sampled rows")
+    wp, xp4, xp6, wq, xq4, xq6 = packs(fmt, n, b, k, seed=33, rows=rows)
+    level = 8 if fmt == "autofp8" else 6
+    ref = oracle_linear(fmt, wq, xq4, xq6, level)
+    y = A.gemv(wp, xp6, bits=level, out_dtype=torch.float32).cpu().numpy()
+    e = check_close(y[:, rows], ref)
+    yb = A.gemv(wp, xp6, bits=level, out_dtype=torch.bfloat16).float().cpu().numpy()
+    assert np.abs(yb[:, rows] - y[:, rows]).max() <= 2.0 ** -8 * np.abs(y[:, rows]).max()
+    say(f"max rel err {e:.2e}")
 
 
 @pytest.mark.parametrize("fmt", ("autofp6e", "autofp8", "fp6g"))
