@@ -37,7 +37,7 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_decode_b1_pmc_traffic.md")
 GEMV_SOURCES = ("runtime_mixed_precision_amd/csrc/gemv.hip", "runtime_mixed_precision_amd/csrc/afp_device.h",
-                "runtime_mixed_precision_amd/csrc/afp_launch.h")
+                "runtime_mixed_precision_amd/csrc/afp_launch.h", "runtime_mixed_precision_amd/csrc/afp_act.h")
 PEAK_FP16_TFLOPS = 2500.0      # dense fp16/bf16 MFMA
 PEAK_FP4_TFLOPS = 10100.0      # dense fp4/fp6 MFMA
 LEVELS = (2, 4, 6)

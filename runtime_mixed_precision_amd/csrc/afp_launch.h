@@ -153,9 +153,9 @@ hipError_t launch_gemv_batch(const LinearArgs &a, hipStream_t s);
 hipError_t launch_gemm(const LinearArgs &a, hipStream_t s);
 bool gemm_small_m_ok(const LinearArgs &a);   // the 64-token GEMM tile applies (K % 64 == 0)
 hipError_t launch_gemm_small_m(const LinearArgs &a, hipStream_t s);   // reads a.xh and, at level 6, a.prefix
-// The variant formats (a.fmt != AUTOFP6) at any level, K % 64 == 0: reads the
-// fp16 panel a.xh that launch_act_dequant wrote for a.fmt and (offset
-// formats) a.prefix.
+// The variant formats (a.fmt != AUTOFP6) at any level, K % 64 == 0: writes
+// the fp16 activation panel a.xh and (offset formats) the mask prefix
+// a.prefix into the workspace when its kernels read them, then Y.
 hipError_t launch_gemm_fmt(const LinearArgs &a, hipStream_t s);
 
 // ---- gptq.hip ----

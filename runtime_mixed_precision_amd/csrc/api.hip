@@ -174,12 +174,6 @@ bool variant_route(const LinearArgs &a) { return a.fmt != AUTOFP_FMT_AUTOFP6 && 
 
 autofp_status launch_variant(const LinearArgs &a, hipStream_t s) {
   if (a.k % 64 != 0) return AUTOFP_ERR_SHAPE;
-  hipError_t e = launch_act_dequant(a, s);
-  if (e != hipSuccess) return AUTOFP_ERR_HIP;
-  if (a.fmt != AUTOFP_FMT_FP6G && a.w_mask) {
-    e = launch_mask_prefix(a.w_mask, mask_bytes(a.k), a.prefix, s);
-    if (e != hipSuccess) return AUTOFP_ERR_HIP;
-  }
   return from_hip(launch_gemm_fmt(a, s));
 }
 

@@ -27,6 +27,7 @@
 
 #include <type_traits>
 
+#include "afp_act.h"
 #include "afp_device.h"
 #include "afp_launch.h"
 
@@ -805,13 +806,18 @@ constexpr int kFmtGemvWaves = 4;    // wavefronts per block
 // tile; still ahead at 4 tokens, behind at 8, where the tile's decode of each
 // weight serves every token)
 constexpr int kFmtGemvTokens = 4;
+// Largest b * K whose activations the variant GEMV decodes into LDS itself
+// (32 KB of fp16; K <= 16384, so at most 512 mask bytes); above it, and at 3-4
+// tokens, a panel pass writes them first.
+constexpr int64_t kFmtXlElems = 16384;
 
-template <int FMT, int TB, int RPW, int U>
+template <int FMT, int TB, int RPW, int U, bool XL>
 __global__ __launch_bounds__(64 * kFmtGemvWaves) void gemv_fmt_kernel(LinearArgs a) {
   constexpr bool F8 = FMT == AUTOFP_FMT_AUTOFP8;
   constexpr bool G6 = FMT == AUTOFP_FMT_FP6G;
   constexpr int64_t OW = F8 ? 2 : 1;   // offset bytes per refined subgroup
   constexpr uint32_t OOB = 0x80000000u;
+  constexpr int NT = 64 * kFmtGemvWaves;
   __shared__ uint2 tabs[512];
   uint2 *dtab = tabs, *stab = tabs + 256;
   uint32_t *t8 = (uint32_t *)tabs;
@@ -819,13 +825,59 @@ __global__ __launch_bounds__(64 * kFmtGemvWaves) void gemv_fmt_kernel(LinearArgs
   const bool refine_w = !G6 && (L == 6 || (F8 && L == 8)) && a.w_mask != nullptr && a.w_offsets != nullptr &&
                         a.n_refined > 0;
   if (refine_w) fill_decode_tables<FMT>(dtab, stab, L);
-  __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t K = a.k, R = a.n_refined;
   const int64_t CB = G6 ? 3 * K / 4 : K / 2;   // code bytes per weight row
   const int64_t items = K >> 5;                 // 32-element items per row
+
+  // XL (b * K <= kFmtXlElems): the block decodes the activations into LDS
+  // itself, quad-major ([token][quad q of an item][item], 16 bytes each, so
+  // the lanes' reads of one quad are consecutive), and forms the weight
+  // mask's exclusive popcount prefix there (pref[j]: refined subgroups before
+  // item j) - no activation panel, no prefix pass.
+  extern __shared__ __align__(16) unsigned char xl_lds[];
+  uint4 *xs = (uint4 *)xl_lds;
+  int32_t *pref = (int32_t *)(xl_lds + (XL ? a.b * K * 2 : 0));
+  if constexpr (XL) {
+    constexpr int PER = kFmtXlElems / 8 / NT;   // 8-element activation items per thread
+    const bool refine_x = !G6 && (L == 6 || (F8 && L == 8)) && a.x_offsets != nullptr;
+    const uint32_t per_row = (uint32_t)(K >> 3), nx = (uint32_t)a.b * per_row;
+    uint4 v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t e = threadIdx.x + (uint32_t)(i * NT);
+      const uint32_t t = e / per_row, k0 = (e - t * per_row) * 8;
+      v[i] = e < nx ? act_decode8_fmt(a, t, k0, refine_x, L) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t e = threadIdx.x + (uint32_t)(i * NT);
+      const uint32_t t = e / per_row, k0 = (e - t * per_row) * 8;
+      if (e < nx) xs[(t * 4 + ((k0 >> 3) & 3)) * items + (k0 >> 5)] = v[i];
+    }
+    if (refine_w) {
+      // items <= 512: thread t takes mask bytes 2t and 2t + 1
+      const uint32_t m0 = 2 * threadIdx.x < items ? a.w_mask[2 * threadIdx.x] : 0u;
+      const uint32_t m1 = 2 * threadIdx.x + 1 < items ? a.w_mask[2 * threadIdx.x + 1] : 0u;
+      const int32_t own = __popc(m0) + __popc(m1);
+      int32_t inc = own;   // inclusive scan over the wavefront
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int32_t y = __shfl_up(inc, o, 64);
+        inc += lane >= o ? y : 0;
+      }
+      __shared__ int32_t wsum[kFmtGemvWaves];
+      if (lane == 63) wsum[wave] = inc;
+      __syncthreads();
+      int32_t ex = inc - own;
+      for (int w = 0; w < wave; ++w) ex += wsum[w];
+      if (2 * threadIdx.x < items) pref[2 * threadIdx.x] = ex;
+      if (2 * threadIdx.x + 1 < items) pref[2 * threadIdx.x + 1] = ex + __popc(m0);
+    }
+  }
+  __syncthreads();
   const int64_t n0 = ((int64_t)blockIdx.x * kFmtGemvWaves + wave) * RPW;
   if (n0 >= a.n) return;
   const int64_t nrows = (a.n - n0) < RPW ? (a.n - n0) : RPW;
@@ -836,9 +888,10 @@ __global__ __launch_bounds__(64 * kFmtGemvWaves) void gemv_fmt_kernel(LinearArgs
   const __amdgpu_buffer_rsrc_t ro =
       rsrc(refine_w ? a.w_offsets + n0 * R * OW : a.w_codes, refine_w ? nrows * R * OW + 16 : 0);
   const __amdgpu_buffer_rsrc_t rm = rsrc(refine_w ? a.w_mask : a.w_codes, refine_w ? items : 0);
-  const __amdgpu_buffer_rsrc_t rp = rsrc(refine_w ? (const void *)a.prefix : a.w_codes, refine_w ? 4 * items : 0);
-  // activation panel [b][kpad] fp16 (b <= TB <= 4): tokens past b read as zero
-  const __amdgpu_buffer_rsrc_t rx = rsrc(a.xh, a.b * a.kpad * 2);
+  const __amdgpu_buffer_rsrc_t rp =
+      rsrc(refine_w && !XL ? (const void *)a.prefix : a.w_codes, refine_w && !XL ? 4 * items : 0);
+  // !XL: activation panel [b][kpad] fp16 (b <= TB <= 4): tokens past b read as zero
+  const __amdgpu_buffer_rsrc_t rx = rsrc(XL ? (const void *)a.w_codes : (const void *)a.xh, XL ? 0 : a.b * a.kpad * 2);
 
   float acc[RPW][TB];
 #pragma unroll
@@ -860,7 +913,8 @@ __global__ __launch_bounds__(64 * kFmtGemvWaves) void gemv_fmt_kernel(LinearArgs
       pos[u] = 0;
       if (refine_w) {
         mb[u] = __builtin_amdgcn_raw_buffer_load_b8(rm, (int)joff[u], 0, 0);
-        pos[u] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rp, (int)(j < items ? 4 * joff[u] : OOB), 0, 0);
+        if constexpr (XL) pos[u] = j < items ? pref[j] : 0;
+        else pos[u] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rp, (int)(j < items ? 4 * joff[u] : OOB), 0, 0);
       }
     }
     half8v xv[U][TB][4];
@@ -874,8 +928,13 @@ __global__ __launch_bounds__(64 * kFmtGemvWaves) void gemv_fmt_kernel(LinearArgs
       for (int t = 0; t < TB; ++t)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t off = live && t < a.b ? (uint32_t)((t * a.kpad + 32 * joff[u] + 8 * q) * 2) : OOB;
-          xv[u][t][q] = __builtin_bit_cast(half8v, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0));
+          if constexpr (XL) {
+            xv[u][t][q] = live && t < a.b ? __builtin_bit_cast(half8v, xs[(t * 4 + q) * items + joff[u]])
+                                          : half8v{};
+          } else {
+            const uint32_t off = live && t < a.b ? (uint32_t)((t * a.kpad + 32 * joff[u] + 8 * q) * 2) : OOB;
+            xv[u][t][q] = __builtin_bit_cast(half8v, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0));
+          }
         }
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
@@ -945,13 +1004,25 @@ __global__ __launch_bounds__(64 * kFmtGemvWaves) void gemv_fmt_kernel(LinearArgs
     }
 }
 
+// The variant GEMV stages the activations and the mask prefix in LDS itself
+// at 1-2 tokens, where each block's redundant activation decode is at most a
+// quarter of its weight decode (4 wavefronts x 2 rows; Wup one token: FP6G
+// 21.8 -> 18.6 us, AUTOFP8 30.1 -> 25.9 us). At 4 tokens (one row per
+// wavefront) it would match the weight decode: 53 -> 71 us.
+bool fmt_gemv_xl(const LinearArgs &a) { return a.b <= 2 && a.b * a.k <= kFmtXlElems; }
+
 template <int FMT, int TB>
 hipError_t launch_gemv_fmt_t(const LinearArgs &a, hipStream_t s) {
   constexpr int RPW = TB <= 2 ? 2 : 1;   // weight rows per wavefront
   constexpr int U = 1;                   // items per lane per pass
   const int64_t rows_per_block = (int64_t)kFmtGemvWaves * RPW;
-  hipLaunchKernelGGL((gemv_fmt_kernel<FMT, TB, RPW, U>),
-                     dim3((unsigned)((a.n + rows_per_block - 1) / rows_per_block)), dim3(64 * kFmtGemvWaves), 0, s, a);
+  const dim3 grid((unsigned)((a.n + rows_per_block - 1) / rows_per_block)), block(64 * kFmtGemvWaves);
+  if (fmt_gemv_xl(a)) {
+    const size_t lds = (size_t)(a.b * a.k * 2 + 4 * (a.k / 32 + 1));
+    hipLaunchKernelGGL((gemv_fmt_kernel<FMT, TB, RPW, U, true>), grid, block, lds, s, a);
+  } else {
+    hipLaunchKernelGGL((gemv_fmt_kernel<FMT, TB, RPW, U, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -1038,6 +1109,16 @@ hipError_t launch_gemm_fmt_t(const LinearArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_gemm_fmt(const LinearArgs &a, hipStream_t s) {
+  if (a.fmt != AUTOFP_FMT_AUTOFP6 && !fmt_gemv_xl(a)) {
+    // the fp16 activation panel and (offset formats, refined weight) the
+    // mask prefix the tiles and the panel GEMV read
+    hipError_t e = launch_act_dequant(a, s);
+    if (e != hipSuccess) return e;
+    if (a.fmt != AUTOFP_FMT_FP6G && a.w_mask) {
+      e = launch_mask_prefix(a.w_mask, mask_bytes(a.k), a.prefix, s);
+      if (e != hipSuccess) return e;
+    }
+  }
   switch (a.fmt) {
     case AUTOFP_FMT_AUTOFP6E: return launch_gemm_fmt_t<AUTOFP_FMT_AUTOFP6E>(a, s);
     case AUTOFP_FMT_AUTOFP8: return launch_gemm_fmt_t<AUTOFP_FMT_AUTOFP8>(a, s);

@@ -140,11 +140,13 @@ def oracle_linear(fmt, wq, xq4, xq6, level):
 @pytest.mark.parametrize("fmt", ("autofp6e", "autofp8", "fp6g"))
 @pytest.mark.parametrize("n,b,k", [(300, 1, 1024), (130, 5, 512), (520, 64, 2048), (200, 40, 64),
                                    (1000, 300, 1024), (301, 2, 4160), (77, 8, 64), (64, 3, 14336),
-                                   (9, 1, 256), (45, 4, 256)])
+                                   (9, 1, 256), (45, 4, 256), (33, 2, 14336), (50, 1, 16448)])
 def test_linear_formats(fmt, n, b, k):
     """Every level of the format on the decode entry point (and the prefill
     one at the same shape): ragged weight rows, 1-300 tokens (1-4 on the
-    vector GEMV, K from 64 (fewer items than lanes) to 14336)."""
+    vector GEMV, K from 64 (fewer items than lanes) to 16448; tokens x K up
+    to 16384 with the activations decoded in the kernel, beyond it and at 3-4
+    tokens from the panel)."""
     say(f"case: linear {fmt} n={n} b={b} k={k}")
     wp, xp4, xp6, wq, xq4, xq6 = packs(fmt, n, b, k, seed=n + b + k)
     for level in levels_of(fmt):
