@@ -26,10 +26,6 @@ constexpr size_t kOffsetPad = 16;
 constexpr int64_t kMaxGptqRows = 65535 * 16;
 // largest reduction dimension of autofp_gemv / autofp_gemm
 constexpr int64_t kMaxLinearK = (int64_t)1 << 22;
-// Largest K for which the batched GEMV forms the weight mask's prefix entries
-// in each block (up to 2048 mask bytes: at most two dwords per thread); above
-// it a prefix pass writes the table first.
-constexpr int64_t kBatchScanMaxK = 65536;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -190,15 +186,11 @@ autofp_status gemv_launches(LinearArgs &a, const autofp_packed *w, const autofp_
     const hipError_t e = launch_act_dequant(a, s);
     if (e != hipSuccess) return AUTOFP_ERR_HIP;
   }
-  // the weight mask's prefix table: for the 64-token GEMM tile, and for the
-  // batched kernel when K > kBatchScanMaxK; otherwise the batched kernel forms
-  // its slice of it in each block (no prefix pass)
-  if (w->mask && (bits_dev || bits == 6) &&
-      (gemv_small_m_route(a) || (gemv_batch_route(a) && a.k > kBatchScanMaxK))) {
+  // the weight mask's prefix table, read by the 64-token GEMM tile (the
+  // batched kernel forms its slice of it in each block)
+  if (w->mask && (bits_dev || bits == 6) && gemv_small_m_route(a)) {
     const hipError_t e = launch_mask_prefix(w->mask, mask_bytes(w->k), a.prefix, s);
     if (e != hipSuccess) return AUTOFP_ERR_HIP;
-  } else {
-    a.prefix = nullptr;
   }
   return from_hip(launch_gemv(a, s));
 }
@@ -611,13 +603,7 @@ autofp_status autofp_gemv_rows(const autofp_packed *w, const autofp_packed *x, c
   a.bits_rows = bits_rows;
   if (!gemv_batch_ok(a)) return AUTOFP_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
-  if (w->mask && a.k > kBatchScanMaxK) {
-    const hipError_t e = launch_mask_prefix(w->mask, mask_bytes(w->k), a.prefix, s);
-    if (e != hipSuccess) return AUTOFP_ERR_HIP;
-  } else {
-    a.prefix = nullptr;   // the batched kernel forms the prefix entries itself
-  }
-  return from_hip(launch_gemv_batch(a, s));
+  return from_hip(launch_gemv_batch(a, s));   // the kernel forms the mask prefix itself
 }
 
 autofp_status autofp_gemm(const autofp_packed *w, const autofp_packed *x, int32_t bits,

@@ -173,48 +173,42 @@ __global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(2))) v
       }
       stab[i] = make_uint2(sel[0], sel[1]);
     }
-    if (a.prefix != nullptr) {
-      for (int64_t i = threadIdx.x; i < 4 * nsb; i += blockDim.x) {
-        const int64_t mi = 4 * bs0 + i;   // mask byte of elements 32 mi .. 32 mi + 31
-        pl_mask[i] = a.w_mask[mi];
-        pl_pos[i] = a.prefix[mi];
-      }
-    } else {
-      // no prefix table: the slice's entries are formed here. Mask dword d
-      // holds the 4 mask bytes of step d (128 elements); thread t counts the
-      // refined subgroups of a contiguous run of the dwords before the
-      // slice's end, the counts are scanned across the block (wavefront
-      // scans, then the wavefront totals in order) and each thread writes
-      // the slice entries of its run.
-      const uint32_t *m32 = (const uint32_t *)a.w_mask;
-      const int64_t nd = bs0 + nsb;
-      const int64_t rd = (nd + 64 * kBW - 1) / (64 * kBW);
-      const int64_t d0 = (int64_t)threadIdx.x * rd;
-      const int64_t d1 = (d0 + rd) < nd ? (d0 + rd) : nd;
-      int32_t own = 0;
-      for (int64_t d = d0; d < d1; ++d) own += __popc(m32[d]);
-      int32_t inc = own;
+    // the slice's mask bytes and their exclusive popcount prefix (refined
+    // subgroups before each byte), formed here: mask dword d holds the 4 mask
+    // bytes of step d (128 elements); thread t counts the refined subgroups of
+    // a contiguous run of the dwords before the slice's end (at most two per
+    // thread for K <= 65536, the largest K whose masks the library selects),
+    // the counts are scanned across the block (wavefront scans, then the
+    // wavefront totals in order) and each thread writes the slice entries of
+    // its run.
+    const uint32_t *m32 = (const uint32_t *)a.w_mask;
+    const int64_t nd = bs0 + nsb;
+    const int64_t rd = (nd + 64 * kBW - 1) / (64 * kBW);
+    const int64_t d0 = (int64_t)threadIdx.x * rd;
+    const int64_t d1 = (d0 + rd) < nd ? (d0 + rd) : nd;
+    int32_t own = 0;
+    for (int64_t d = d0; d < d1; ++d) own += __popc(m32[d]);
+    int32_t inc = own;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int32_t y = __shfl_up(inc, o, 64);
-        inc += lane >= o ? y : 0;
-      }
-      __shared__ int32_t wtot[kBW];
-      if (lane == 63) wtot[wave] = inc;
-      __syncthreads();
-      int32_t pos = inc - own;
-      for (int w = 0; w < wave; ++w) pos += wtot[w];
-      for (int64_t d = d0; d < d1; ++d) {
-        const uint32_t m = m32[d];
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t y = __shfl_up(inc, o, 64);
+      inc += lane >= o ? y : 0;
+    }
+    __shared__ int32_t wtot[kBW];
+    if (lane == 63) wtot[wave] = inc;
+    __syncthreads();
+    int32_t pos = inc - own;
+    for (int w = 0; w < wave; ++w) pos += wtot[w];
+    for (int64_t d = d0; d < d1; ++d) {
+      const uint32_t m = m32[d];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t mb = (m >> (8 * e)) & 0xFFu;
-          if (d >= bs0) {
-            pl_mask[4 * (d - bs0) + e] = (uint8_t)mb;
-            pl_pos[4 * (d - bs0) + e] = pos;
-          }
-          pos += __popc(mb);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t mb = (m >> (8 * e)) & 0xFFu;
+        if (d >= bs0) {
+          pl_mask[4 * (d - bs0) + e] = (uint8_t)mb;
+          pl_pos[4 * (d - bs0) + e] = pos;
         }
+        pos += __popc(mb);
       }
     }
   }

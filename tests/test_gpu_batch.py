@@ -58,13 +58,15 @@ def packs(n, b, k, seed, rows=None):
 
 @pytest.mark.parametrize("n,b,k", [(200, 17, 256), (64, 33, 512), (300, 64, 1024), (130, 64, 4096),
                                    (1000, 48, 384), (257, 100, 4096), (70, 32, 128), (50, 20, 192),
-                                   (70, 12, 4224), (130, 16, 4352), (6150, 9, 256)])
+                                   (70, 12, 4224), (130, 16, 4352), (6150, 9, 256), (48, 24, 65536)])
 @pytest.mark.parametrize("level", [2, 4, 6])
 def test_batched_gemv_shapes(n, b, k, level):
     """Ragged row tiles (n not a multiple of 64), 9-100 tokens (16-token tiles
     1, 2 and 4, two 64-token slices; 9-16 tokens on weights with K above 4096
-    or 6144+ rows), K of 1 to 34 steps of 128, K split over blocks (small n,
-    long K), and K % 128 != 0 (the other batched routes)."""
+    or 6144+ rows), K of 1 to 512 steps of 128, K split over blocks (small n,
+    long K), and K % 128 != 0 (the other batched routes). Each block forms
+    its slice of the weight mask's prefix itself (at K = 65536, the largest
+    K whose masks are selected, two mask dwords per thread)."""
     say(f"case: batched GEMV n={n} b={b} k={k} level {level}")
     wp, xp4, xp6, wq, xq4, xq6 = packs(n, b, k, seed=n + b + k)
     y = A.gemv(wp, xp6 if level == 6 else xp4, bits=level).cpu().numpy()
@@ -86,7 +88,8 @@ def oracle_rows(wq, xq4, xq6, levels):
     return np.stack([out[int(l)][t] for t, l in enumerate(levels)])
 
 
-@pytest.mark.parametrize("n,b,k", [(300, 40, 1024), (130, 3, 512), (64, 70, 4096), (1000, 64, 256)])
+@pytest.mark.parametrize("n,b,k", [(300, 40, 1024), (130, 3, 512), (64, 70, 4096), (1000, 64, 256),
+                                   (40, 20, 65536)])
 def test_gemv_rows_mixed_levels(n, b, k):
     """Tokens at levels drawn from {2, 4, 6}: each output row equals the
     oracle's product at that row's level."""
