@@ -758,13 +758,15 @@ __global__ __launch_bounds__(64 * NW * KG) void gemm_lds_kernel(LinearArgs a) {
 // A variant weight element B (q + delta) or an E2M3 code needs more than the
 // four significant bits the fp4 matrix cores take, and a 64-token GEMM tile
 // at one token leaves most of the chip idle ([AE] App. I Table 10, App. B.2:
-// the formats; the product is the one the GEMM tiles compute). Here a wavefront owns RPW weight
-// rows and its lanes split K into 32-element items: lane l takes items l,
-// l + 64, ... of each row, decodes them with decode_w32 (the GEMM tiles' own
-// weight decode: fp16, exact, group scales applied) and accumulates their
-// dot products with the fp16 activation panel in fp32 (v_dot2_f32_f16,
-// products exact in fp32); the lanes' sums are added across the wavefront at
-// the end in one fixed order. TB >= b tokens (absent tokens read as zero).
+// the formats; the product is the one the GEMM tiles compute). Here a
+// wavefront owns RPW weight rows and its lanes split K into 32-element items:
+// lane l takes items l, l + 64, ... of each row, decodes them with decode_w32
+// (the GEMM tiles' own weight decode: fp16, exact, group scales applied) and
+// accumulates their dot products with the fp16 activations in fp32
+// (v_dot2_f32_f16, products exact in fp32); the lanes' sums are added across
+// the wavefront at the end in one fixed order. The activations come from LDS,
+// decoded there by the block (1-2 tokens), or from the fp16 panel of the
+// workspace. TB >= b tokens (absent tokens read as zero).
 // The time is mostly the decode's vector ALU (a wave64 instruction per four
 // cycles on each SIMD), so FP6G takes its codes through the 32-element fp6
 // conversion.
